@@ -1,0 +1,158 @@
+/*
+ * oracle.h -- plain CPU oracle for the MoE layer forward pass
+ * (route + pack + compute + combine).
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only the test suite, the smoke check and the
+ * CPU-baseline leg of the benchmark may load this library.  The product path
+ * (the HIP library and its Python binding) never calls it and shares no code,
+ * header, table or helper with it.
+ *
+ * Sources (the pages this follows; every function below cites its passage):
+ *   [MML]  "271,104 Routes: What I Missed About Mixture-of-Experts"
+ *          (michaelml.dev), sections 1 "The MoE Block", 2 "The Router",
+ *          3 "Dispatch: Turning Routes Into GPU Work".
+ *   [INT8] "Mixture of Experts: Routing, Dispatch, and Load Balancing"
+ *          (int8ai.pages.dev), section 1 (router), section 3 (minimal
+ *          example), section 4 (capacity, overflow, load imbalance).
+ *   [BEA]  "MoE Inference Visualized" (infra.bea.ai), "The Router" and
+ *          "Expert Execution: Gather -> Compute -> Scale -> Scatter".
+ *   [SPK]  "Session 19: Mixture-of-Experts: routing and capacity"
+ *          (cours.spawnkit.ai), slides "Top-k and mixture", "Capacity",
+ *          "Worked case -- full trace".
+ *   [UD]   "Mixture-of-experts routing" (understandingdata.com),
+ *          "The maths": the gate, capacity and load-imbalance formulas.
+ *
+ * Precision.  Router logits are fp32 (the [MML] Granite experiment casts the
+ * router logits to float before top-k), accumulated by a plain sequential
+ * fused multiply-add over the hidden dimension in increasing index order;
+ * that order is a reading of ours, because the pages leave it open and the
+ * selected expert ids depend on it at near ties.  Gates, expert FFNs and the
+ * combine are computed in double precision.
+ *
+ * Element types: dtype 0 = IEEE binary32, dtype 1 = bfloat16 (raw 16-bit
+ * patterns, the upper half of a binary32).  All arrays are row-major and
+ * contiguous.  Weights use the [out, in] storage of a linear layer:
+ * w_router[E][d], w_gate[E][d_ff][d], w_up[E][d_ff][d], w_down[E][d][d_ff].
+ *
+ * Parity status per function is stated beside each declaration.
+ */
+#ifndef MOE_ORACLE_H
+#define MOE_ORACLE_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define ORACLE_F32 0
+#define ORACLE_BF16 1
+
+/* Expert capacity C = ceil(phi * T * k / E) ([UD] "Capacity"; [SPK]
+ * "Capacity" and the full trace).  Evaluated in IEEE double as
+ * ceil(phi * (double)(T*k) / (double)E).  phi <= 0 means "no capacity
+ * limit" and returns -1.  Pinned by the [SPK] trace (C = 5, 4, 8, 6, 3) and
+ * the [INT8] overflow case (C = 2). */
+int64_t oracle_capacity(int64_t T, int64_t E, int64_t k, double phi);
+
+/* Router logits, fp32: logits[t][e] = sum_i x[t][i] * w[e][i] (+ b[e]),
+ * accumulated with fmaf in increasing i, bias added after the sum
+ * ([INT8] section 1: x @ W_router + b_router; [BEA] "The Router": one
+ * 768-wide dot product per expert row).  b may be NULL.
+ * Pinned against fp64 dot products within the fp32 error bound. */
+void oracle_router_logits(int64_t T, int64_t d, int64_t E, int dtype,
+                          const void* x, const void* w, const float* b,
+                          float* logits);
+
+/* The same dot products in double precision (exact products, double sums),
+ * for the near-tie report.  Not used for decisions. */
+void oracle_router_logits_f64(int64_t T, int64_t d, int64_t E, int dtype,
+                              const void* x, const void* w, const float* b,
+                              double* logits);
+
+/* Top-k selection and gates ([MML] section 2: logits.topk then softmax over
+ * the selected logits; [UD] "The gate"; [SPK] "Top-k and mixture":
+ * renormalise the selected probabilities by their sum; [BEA] "Expert
+ * Execution": top-1 scaled by its softmax probability).
+ * Selection: the k largest logits, slot j = j-th largest; equal logits are
+ * ordered by lower expert index first.
+ * renorm = 1: g_j = exp(l_j - m) / sum_{selected} exp(l_i - m)
+ * renorm = 0: g_j = exp(l_j - m) / sum_{all e} exp(l_e - m)
+ * with m the largest logit; computed in double, rounded once to float.
+ * Pinned by the [SPK] worked example, the gate-sum invariant and brute-force
+ * sorting. */
+void oracle_topk_gates(int64_t T, int64_t E, int64_t k, int renorm,
+                       const float* logits, int32_t* expert_ids, float* gates);
+
+/* Counting-sort dispatch with optional capacity ([MML] section 3: flatten
+ * routes r = t*k + j, stable argsort by expert, bincount + cumsum;
+ * [SPK] "Capacity" and trace: arrivals beyond C are dropped in arrival
+ * order; [INT8] section 4 overflow case).
+ *   counts[e]      demand n_e (routes choosing e, before capacity)
+ *   kept[e]        m_e = min(n_e, C)
+ *   offsets[E+1]   exclusive prefix of m_e
+ *   route_pos[r]   row of route r in the expert-grouped layout, -1 if dropped
+ *   row_token[p]   source token of packed row p, p < offsets[E]
+ * C < 0 means no capacity limit.  Pinned by the [MML] and [SPK]/[INT8]
+ * worked cases. */
+void oracle_dispatch(int64_t T, int64_t E, int64_t k, int64_t C,
+                     const int32_t* expert_ids, int32_t* counts, int32_t* kept,
+                     int32_t* offsets, int32_t* route_pos, int32_t* row_token);
+
+/* Row duplication: packed[p][:] = x[row_token[p]][:] for p < n_rows, a bit
+ * copy of elem_bytes-sized elements ([MML] section 3: index_select). */
+void oracle_gather_rows(int64_t n_rows, int64_t d, int64_t elem_bytes,
+                        const void* x, const int32_t* row_token, void* packed);
+
+/* Expert SwiGLU FFN of one expert on n rows, in double:
+ *   a = x Wg^T, b = x Wu^T, h = SiLU(a) * b, y = h Wd^T
+ * ([BEA] "Expert Execution": down_proj(SiLU(gate_proj(x)) * up_proj(x))).
+ * x: [n][d] (dtype), wg, wu: [d_ff][d], wd: [d][d_ff] (dtype), y: [n][d].
+ * Pinned against a torch fp64 dense MLP. */
+void oracle_swiglu_rows(int64_t n, int64_t d, int64_t d_ff, int dtype,
+                        const void* x, const void* wg, const void* wu,
+                        const void* wd, double* y);
+
+/* Expert FFN over expert-grouped rows: rows [offsets[e], offsets[e+1]) of
+ * x_packed run through expert e ([MML] section 3: grouped expert matmuls).
+ * y_packed: [offsets[E]][d] double. */
+void oracle_expert_ffn(int64_t E, int64_t d, int64_t d_ff, int dtype,
+                       const int32_t* offsets, const void* x_packed,
+                       const void* w_gate, const void* w_up,
+                       const void* w_down, double* y_packed);
+
+/* Gate-weighted combine ([MML] section 1: y = sum_i p_i E_i(x), section 3:
+ * restore token order; [SPK] "Top-k and mixture": + shared expert outside
+ * the renormalisation; [SPK] trace: a dropped route contributes nothing and
+ * the remaining gates are not renormalised).
+ * y[t] = sum_{j < k, route_pos[t*k+j] >= 0} g[t][j] * y_packed[route_pos]
+ *        + y_shared[t]
+ * y_packed and y_shared are given in ypdtype (0 f32, 1 bf16, 2 f64);
+ * y_shared may be NULL.  Output in double. */
+void oracle_combine(int64_t T, int64_t k, int64_t d, int ypdtype,
+                    const void* y_packed, const int32_t* route_pos,
+                    const float* gates, const void* y_shared, double* y);
+
+/* Whole layer forward: logits -> top-k gates -> dispatch with capacity ->
+ * expert FFN per kept route -> gate-weighted sum (+ shared expert).
+ * Routing (ids, gates, counts, route_pos) is computed for all T tokens;
+ * the output rows are computed for the n_sel tokens listed in sel (all T
+ * tokens in order when sel is NULL), y: [n_sel][d] double.
+ * d_ff_shared = 0 means no shared expert (ws_* may be NULL).
+ * Any of ids/gates/counts/route_pos may be NULL.
+ * Returns 0, or -1 on bad arguments. */
+int oracle_layer_forward(int64_t T, int64_t d, int64_t E, int64_t k,
+                         int64_t d_ff, int64_t d_ff_shared, int dtype,
+                         int renorm, double phi, const void* x,
+                         const void* w_router, const float* b_router,
+                         const void* w_gate, const void* w_up,
+                         const void* w_down, const void* ws_gate,
+                         const void* ws_up, const void* ws_down,
+                         int64_t n_sel, const int32_t* sel, double* y,
+                         int32_t* ids, float* gates, int32_t* counts,
+                         int32_t* route_pos);
+
+#ifdef __cplusplus
+}
+#endif
+#endif

@@ -1,0 +1,439 @@
+"""Pins of the CPU oracle against what the pages and mathematics fix.
+
+Each test names the passage or the closed form it checks.  None of them
+compares the oracle with itself: the references are the pages' printed
+values (tests/golden/), library routines (numpy / scipy / torch fp64),
+brute force and exact invariants.
+"""
+import math
+
+import numpy as np
+import pytest
+import scipy.special
+import torch
+
+import oracle
+from tests import _golden as G
+from tests.bruteforce import dense_mask_layer, swiglu_dense
+from workloads import WORKLOADS, Workload, make_inputs
+
+
+def onehot_router(logit_rows, d=8):
+    """x[t] = unit vector e_t, W_r[e][t] = logit -> the router's dot product
+    returns the logit itself (one exact product, all other terms zero)."""
+    L = np.asarray(logit_rows, dtype=np.float32)
+    T, E = L.shape
+    assert T <= d
+    x = np.zeros((T, d), np.float32)
+    x[np.arange(T), np.arange(T)] = 1.0
+    w = np.zeros((E, d), np.float32)
+    w[:, :T] = L.T
+    return x, w
+
+
+# ---------------------------------------------------------------- router ---
+
+def test_worked_router_softmax_spk():
+    g = G.load("spk_worked_router.txt")
+    logits = G.nums(g["logits"])
+    x, w = onehot_router([logits])
+    L = oracle.router_logits(x, w)
+    assert np.array_equal(L[0], np.float32(logits))
+    # full softmax (k = E, no renormalisation) in descending order
+    ids, gates = oracle.topk_gates(L, k=3, renorm=0)
+    assert ids[0].tolist() == [0, 1, 2]
+    assert np.allclose(gates[0], G.nums(g["softmax"]), atol=5e-4)
+    # the printed exponentials: gate * sum(exp) = exp(l)
+    assert np.allclose(gates[0] * float(g["exp_sum"]), G.nums(g["exp"]), atol=2e-3)
+    # top-2 renormalised over the selected mass 0.921
+    ids2, g2 = oracle.topk_gates(L, k=2, renorm=1)
+    assert ids2[0].tolist() == G.nums(g["top2_ids"], int)
+    assert np.allclose(g2[0], G.nums(g["top2_renorm"]), atol=5e-4)
+    assert abs(gates[0][:2].sum() - float(g["selected_mass"])) < 1e-3
+    assert np.allclose(g2[0], gates[0][:2] / gates[0][:2].sum(), atol=1e-7)
+    # flipped third logit: E3 replaces E2 in the top-2
+    fl = G.nums(g["flipped_logits"])
+    x, w = onehot_router([fl])
+    Lf = oracle.router_logits(x, w)
+    idsf, gf = oracle.topk_gates(Lf, k=3, renorm=0)
+    assert idsf[0].tolist() == [0, 2, 1]
+    want = G.nums(g["flipped_softmax"])
+    assert np.allclose(gf[0], [want[0], want[2], want[1]], atol=5e-4)
+    ids2f, _ = oracle.topk_gates(Lf, k=2, renorm=1)
+    assert sorted(ids2f[0].tolist()) == G.nums(g["flipped_top2_ids"], int)
+
+
+def test_renormalised_equals_softmax_of_selected_logits():
+    # 0.529/0.921 = 0.574 = 1/(1+exp(-0.3)): renormalising selected
+    # probabilities is the softmax of the selected logits
+    _, g2 = oracle.topk_gates(np.array([[2.1, 1.8, 0.2]], np.float32), 2, 1)
+    l0, l1 = np.float32(2.1), np.float32(1.8)
+    assert abs(g2[0, 0] - 1.0 / (1.0 + math.exp(float(l1) - float(l0)))) < 1e-7
+
+
+@pytest.mark.parametrize("k", [1, 2, 8])
+def test_gate_sum_invariant(k):
+    # Granite check: renormalised gates sum to one within atol 1e-6
+    rng = np.random.default_rng(1)
+    L = rng.standard_normal((500, 32)).astype(np.float32) * 3
+    ids, g = oracle.topk_gates(L, k, 1)
+    assert np.max(np.abs(g.astype(np.float64).sum(-1) - 1.0)) <= 1e-6
+    if k == 1:
+        assert np.all(g == 1.0)
+
+
+def test_k_equals_E_renorm_is_full_softmax():
+    rng = np.random.default_rng(2)
+    L = rng.standard_normal((64, 6)).astype(np.float32)
+    ids, g = oracle.topk_gates(L, 6, 1)
+    ref = scipy.special.softmax(L.astype(np.float64), axis=-1)
+    assert np.allclose(g, np.take_along_axis(ref, ids, -1), atol=1e-7)
+    ids0, g0 = oracle.topk_gates(L, 6, 0)
+    assert np.array_equal(ids, ids0) and np.allclose(g, g0, atol=1e-7)
+
+
+def test_top1_no_renorm_is_max_probability():
+    rng = np.random.default_rng(3)
+    L = rng.standard_normal((200, 8)).astype(np.float32)
+    ids, g = oracle.topk_gates(L, 1, 0)
+    ref = scipy.special.softmax(L.astype(np.float64), axis=-1)
+    assert np.array_equal(ids[:, 0], ref.argmax(-1))
+    assert np.allclose(g[:, 0], ref.max(-1), atol=1e-7)
+
+
+@pytest.mark.parametrize("ties", [False, True])
+def test_topk_against_full_sort(ties):
+    rng = np.random.default_rng(4 + ties)
+    E, k = 16, 5
+    if ties:
+        L = rng.integers(-2, 3, size=(400, E)).astype(np.float32)
+    else:
+        L = rng.standard_normal((400, E)).astype(np.float32)
+    ids, _ = oracle.topk_gates(L, k, 1)
+    for t in range(L.shape[0]):
+        # order by (logit descending, index ascending)
+        ref = np.lexsort((np.arange(E), -L[t]))[:k]
+        assert ids[t].tolist() == ref.tolist()
+
+
+def test_all_equal_logits_lowest_index():
+    ids, g = oracle.topk_gates(np.zeros((3, 8), np.float32), 4, 1)
+    assert np.all(ids == np.arange(4))
+    assert np.allclose(g, 0.25)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_router_logits_within_fp32_bound(dtype):
+    w = Workload("r", T=40, E=8, k=2, d=1000, d_ff=8, dtype=dtype, bias="normal")
+    inp = make_inputs(w, seed=5)
+    L = oracle.router_logits(inp["x"], inp["w_router"], inp["b_router"])
+    L64 = oracle.router_logits(inp["x"], inp["w_router"], inp["b_router"], f64=True)
+    # independent fp64 reference by library matmul
+    X = inp["x"].double().numpy()
+    Wr = inp["w_router"].double().numpy()
+    ref = X @ Wr.T + inp["b_router"].double().numpy()
+    assert np.allclose(L64, ref, rtol=0, atol=1e-12)
+    # sequential fp32 summation: |err| <= gamma_d * sum|x_i w_i| + bias rounding
+    u = 2.0 ** -24
+    gam = w.d * u / (1 - w.d * u)
+    bound = gam * (np.abs(X) @ np.abs(Wr).T) + 2 * u * (np.abs(ref) + 1)
+    assert np.all(np.abs(L.astype(np.float64) - ref) <= bound)
+
+
+# -------------------------------------------------------------- dispatch ---
+
+def test_permute_mml_example():
+    g = G.load("mml_permute.txt")
+    E = int(g["num_experts"])
+    ids = np.array(G.rows(g["expert_ids"], int), np.int32)
+    out = oracle.dispatch(ids, E, -1)
+    ends = np.cumsum(out["counts"])
+    assert ends.tolist() == G.nums(g["expert_ends"], int)
+    assert out["offsets"].tolist() == [0] + G.nums(g["expert_ends"], int)
+    for e in (2, 4, 7):
+        lo, hi = out["offsets"][e], out["offsets"][e + 1]
+        assert out["row_token"][lo:hi].tolist() == G.nums(g[f"group_{e}"], int)
+    # round trip: packed rows restored to route order equal x[token_ids]
+    x = np.array(G.rows(g["x"]), np.float32)
+    packed = oracle.gather_rows(x, out["row_token"])
+    restored = packed[out["route_pos"].reshape(-1)]
+    assert np.array_equal(restored, x[np.repeat(np.arange(3), 2)])
+
+
+def test_dispatch_matches_stable_argsort():
+    # the page's formulation: stable argsort of the flat ids + bincount.cumsum
+    rng = np.random.default_rng(6)
+    T, E, k = 300, 12, 3
+    ids = np.stack([rng.permutation(E)[:k] for _ in range(T)]).astype(np.int32)
+    out = oracle.dispatch(ids, E, -1)
+    flat = ids.reshape(-1)
+    order = np.argsort(flat, kind="stable")
+    tok = np.repeat(np.arange(T), k)
+    assert np.array_equal(out["row_token"], tok[order])
+    assert np.array_equal(out["offsets"][1:], np.cumsum(np.bincount(flat, minlength=E)))
+    inv = np.empty_like(order)
+    inv[order] = np.arange(order.size)
+    assert np.array_equal(out["route_pos"].reshape(-1), inv)
+
+
+def _trace_variant(assign, E, phi, k):
+    ids = np.array(assign, np.int32)[:, :k].copy()
+    T = ids.shape[0]
+    C = oracle.capacity(T, E, k, phi)
+    return C, ids, oracle.dispatch(ids, E, C)
+
+
+def test_capacity_trace_spk():
+    g = G.load("spk_capacity_trace.txt")
+    E, k = int(g["E"]), int(g["k"])
+    assign = G.rows(g["assign"], int)
+    variants = g["variant"]
+    for v in variants:
+        phi, C_want, dropped, used, reserved = v.split()
+        C, ids, out = _trace_variant(assign, E, float(phi), k)
+        assert C == int(C_want)
+        assert out["counts"].tolist() == G.nums(g["counts"], int)
+        assert int(out["counts"].sum()) == int(g["T"]) * k          # 16 = 8 x 2
+        drops = sorted(f"{r // k}@{ids[r // k, r % k]}"
+                       for r in np.flatnonzero(out["route_pos"].reshape(-1) < 0))
+        want = [] if dropped == "-" else sorted(dropped.split(","))
+        assert drops == want
+        assert int(out["kept"].sum()) == int(used)
+        assert E * C == int(reserved)
+        if phi == "1.25":
+            for e in range(E):
+                lo, hi = out["offsets"][e], out["offsets"][e + 1]
+                assert out["row_token"][lo:hi].tolist() == G.nums(g[f"slots_E{e}"], int)
+    # k = 1: first choice of each pair, phi = 1.25
+    C, ids, out = _trace_variant(assign, E, 1.25, 1)
+    assert C == int(g["k1_C"])
+    assert out["counts"].tolist() == G.nums(g["k1_loads"], int)
+    assert np.flatnonzero(out["route_pos"].reshape(-1) < 0).tolist() == G.nums(g["k1_dropped"], int)
+
+
+def test_capacity_trace_end_to_end_t6_keeps_only_second_gate():
+    """Trace driven through the whole layer: each token's logits put its pair
+    first (t6 shares t1's logits); with C = 5 t6 loses E1 and its output is
+    the second gate (0.426) times E2's FFN output, not renormalised."""
+    g = G.load("spk_capacity_trace.txt")
+    assign = G.rows(g["assign"], int)
+    T, E, k, d, d_ff = 8, 4, 2, 16, 24
+    L = np.full((T, E), 0.2, np.float32)
+    for t, (a, b) in enumerate(assign):
+        L[t, a], L[t, b] = 2.1, 1.8
+    x = np.zeros((T, d), np.float32)
+    x[np.arange(T), np.arange(T)] = 1.0
+    x += np.random.default_rng(7).standard_normal((T, d)).astype(np.float32) * 0  # keep one-hot
+    wr = np.zeros((E, d), np.float32)
+    wr[:, :T] = L.T
+    rng = np.random.default_rng(8)
+    wg = rng.standard_normal((E, d_ff, d)).astype(np.float32)
+    wu = rng.standard_normal((E, d_ff, d)).astype(np.float32)
+    wd = rng.standard_normal((E, d, d_ff)).astype(np.float32)
+    out = oracle.layer_forward(x, wr, None, wg, wu, wd, k=k, renorm=1, phi=1.25)
+    assert out["route_pos"][5, 0] == -1 and out["route_pos"][5, 1] >= 0
+    X = torch.from_numpy(x).double()
+    ffn_e2 = swiglu_dense(X[5:6], *(torch.from_numpy(w[1]).double() for w in (wg, wu, wd)))[0]
+    gate = out["gates"][5, 1]
+    assert abs(gate - float(g["t6_kept_gate"])) < 5e-4
+    assert np.allclose(out["y"][5], gate * ffn_e2.numpy(), rtol=1e-12, atol=1e-12)
+
+
+def test_overflow_int8():
+    g = G.load("int8_overflow.txt")
+    T, E, k, phi = int(g["T"]), int(g["E"]), int(g["k"]), float(g["phi"])
+    ids = np.array(G.nums(g["assign"], int), np.int32).reshape(T, k)
+    C = oracle.capacity(T, E, k, phi)
+    assert C == int(g["C"])
+    out = oracle.dispatch(ids, E, C)
+    assert out["counts"].tolist() == G.nums(g["loads"], int)
+    dropped = np.flatnonzero(out["route_pos"].reshape(-1) < 0)
+    assert len(dropped) == int(g["dropped"])
+    # arrival order: the last three arrivals at expert 0 are the dropped ones
+    e0 = np.flatnonzero(ids[:, 0] == 0)
+    assert dropped.tolist() == e0[2:].tolist()
+
+
+def test_capacity_formula():
+    assert oracle.capacity(8, 4, 2, 1.25) == 5
+    assert oracle.capacity(8, 4, 1, 1.25) == 3
+    assert oracle.capacity(4096, 8, 1, 1.0) == 512
+    assert oracle.capacity(4096, 8, 1, 1.25) == 640
+    assert oracle.capacity(10, 4, 1, 0.01) == 1
+    assert oracle.capacity(8, 4, 2, 0.0) == -1
+    assert oracle.capacity(8, 4, 2, -1.0) == -1
+
+
+def test_route_count_granite_271104():
+    """1,412 tokens x 24 layers x top-8 of 32 = 271,104 routes: the demand
+    counts of 24 independently seeded router layers sum to that."""
+    w = WORKLOADS["granite_1412"].with_(d_ff=8)
+    total = 0
+    for layer in range(24):
+        inp = make_inputs(w.with_(E=32), seed=100 + layer)
+        L = oracle.router_logits(inp["x"], inp["w_router"])
+        ids, _ = oracle.topk_gates(L, w.k, 1)
+        out = oracle.dispatch(ids, w.E, -1)
+        assert int(out["counts"].sum()) == w.T * w.k == 11296
+        assert int(out["offsets"][-1]) == 11296
+        total += int(out["counts"].sum())
+    assert total == 271104
+
+
+def test_forced_expert_imbalance_reaches_E_over_k():
+    """One expert in every token's top-k gives max/mean demand = E/k, the
+    worst case (4 for 32 experts, top-8)."""
+    w = Workload("imb", T=256, E=32, k=8, d=64, d_ff=8)
+    inp = make_inputs(w, seed=9)
+    b = np.zeros(32, np.float32)
+    b[17] = 1e3
+    L = oracle.router_logits(inp["x"], inp["w_router"], b)
+    ids, _ = oracle.topk_gates(L, w.k, 1)
+    counts = oracle.dispatch(ids, w.E, -1)["counts"]
+    I = counts.max() / counts.mean()
+    assert counts[17] == w.T and I == w.E / w.k == 4.0
+
+
+# ------------------------------------------------------- FFN and layer ---
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_single_expert_is_dense_swiglu(dtype):
+    w = Workload("dense", T=24, E=1, k=1, d=40, d_ff=56, dtype=dtype)
+    inp = make_inputs(w, seed=10)
+    out = oracle.layer_forward(inp["x"], inp["w_router"], None, inp["w_gate"], inp["w_up"],
+                               inp["w_down"], k=1, renorm=1, phi=0)
+    ref = swiglu_dense(inp["x"].double(), inp["w_gate"][0].double(), inp["w_up"][0].double(),
+                       inp["w_down"][0].double())
+    assert np.all(out["gates"] == 1.0)
+    assert np.allclose(out["y"], ref.numpy(), rtol=1e-12, atol=1e-12)
+    rows = oracle.swiglu_rows(inp["x"], inp["w_gate"][0], inp["w_up"][0], inp["w_down"][0])
+    assert np.allclose(rows, ref.numpy(), rtol=1e-12, atol=1e-12)
+
+
+def test_shared_expert_alone_when_routed_outputs_zero():
+    w = Workload("sh", T=16, E=4, k=2, d=32, d_ff=24, d_ff_shared=40, dtype="bf16")
+    inp = make_inputs(w, seed=11, zero_routed=True)
+    out = oracle.layer_forward(inp["x"], inp["w_router"], None, inp["w_gate"], inp["w_up"],
+                               inp["w_down"], k=2, renorm=1, phi=0, ws_gate=inp["ws_gate"],
+                               ws_up=inp["ws_up"], ws_down=inp["ws_down"])
+    ref = swiglu_dense(inp["x"].double(), inp["ws_gate"].double(), inp["ws_up"].double(),
+                       inp["ws_down"].double())
+    assert np.allclose(out["y"], ref.numpy(), rtol=1e-12, atol=1e-12)
+
+
+CASES = [
+    dict(T=48, E=4, k=2, d=32, d_ff=48, dtype="f32", renorm=1, phi=0.0, bias=None),
+    dict(T=40, E=8, k=1, d=24, d_ff=40, dtype="bf16", renorm=0, phi=1.0, bias="normal"),
+    dict(T=40, E=8, k=1, d=24, d_ff=40, dtype="bf16", renorm=0, phi=1.25, bias="normal"),
+    dict(T=30, E=6, k=3, d=16, d_ff=24, dtype="bf16", renorm=1, phi=0.75, bias=None),
+    dict(T=32, E=16, k=2, d=32, d_ff=16, d_ff_shared=40, dtype="bf16", renorm=1, phi=0.0,
+         bias="zipf"),
+    dict(T=20, E=5, k=5, d=16, d_ff=16, dtype="f32", renorm=1, phi=0.0, bias=None),
+]
+
+
+@pytest.mark.parametrize("case", range(len(CASES)))
+def test_layer_matches_dense_mask_bruteforce(case):
+    w = Workload("bf", **CASES[case])
+    inp = make_inputs(w, seed=20 + case)
+    sh = dict(ws_gate=inp["ws_gate"], ws_up=inp["ws_up"], ws_down=inp["ws_down"])
+    out = oracle.layer_forward(inp["x"], inp["w_router"], inp["b_router"], inp["w_gate"],
+                               inp["w_up"], inp["w_down"], k=w.k, renorm=w.renorm, phi=w.phi, **sh)
+    ref = dense_mask_layer(inp["x"], inp["w_router"], inp["b_router"], inp["w_gate"],
+                           inp["w_up"], inp["w_down"], w.k, w.renorm, w.phi, **sh)
+    if ref["gap"] is not None:
+        assert float(ref["gap"].min()) > 1e-4   # no near tie at these seeds
+    assert np.array_equal(out["ids"], ref["ids"].numpy())
+    scale = np.abs(ref["y"].numpy()).max()
+    assert np.max(np.abs(out["y"] - ref["y"].numpy())) <= 1e-5 * scale
+    # gates agree with the brute-force weights of the selected experts
+    wsel = torch.gather(ref["weights"], 1, ref["ids"].long()).numpy()
+    kept = out["route_pos"] >= 0
+    assert np.allclose(out["gates"][kept], wsel[kept], atol=1e-6)
+
+
+def test_token_permutation_equivariance_dropless():
+    w = Workload("perm", T=32, E=8, k=2, d=32, d_ff=24, dtype="bf16")
+    inp = make_inputs(w, seed=30)
+    args = lambda x: (x, inp["w_router"], None, inp["w_gate"], inp["w_up"], inp["w_down"])
+    y = oracle.layer_forward(*args(inp["x"]), k=2, renorm=1, phi=0)["y"]
+    perm = torch.randperm(w.T, generator=torch.Generator().manual_seed(1))
+    yp = oracle.layer_forward(*args(inp["x"][perm].contiguous()), k=2, renorm=1, phi=0)["y"]
+    assert np.array_equal(yp, y[perm.numpy()])
+
+
+def test_expert_relabelling_invariance():
+    w = Workload("relab", T=32, E=8, k=2, d=32, d_ff=24, dtype="bf16", bias="normal")
+    inp = make_inputs(w, seed=31)
+    perm = torch.tensor([3, 7, 0, 5, 1, 6, 2, 4])
+    base = oracle.layer_forward(inp["x"], inp["w_router"], inp["b_router"], inp["w_gate"],
+                                inp["w_up"], inp["w_down"], k=2, renorm=1, phi=0)
+    rel = oracle.layer_forward(inp["x"], inp["w_router"][perm].contiguous(),
+                               inp["b_router"][perm].contiguous(), inp["w_gate"][perm].contiguous(),
+                               inp["w_up"][perm].contiguous(), inp["w_down"][perm].contiguous(),
+                               k=2, renorm=1, phi=0)
+    assert np.array_equal(perm.numpy()[rel["ids"]], base["ids"])
+    assert np.allclose(rel["y"], base["y"], rtol=1e-12, atol=1e-12)
+
+
+def test_down_projection_scaling_is_exact():
+    w = Workload("sc", T=16, E=4, k=2, d=32, d_ff=24, dtype="bf16")
+    inp = make_inputs(w, seed=32)
+    a = oracle.layer_forward(inp["x"], inp["w_router"], None, inp["w_gate"], inp["w_up"],
+                             inp["w_down"], k=2, renorm=1, phi=0)["y"]
+    b = oracle.layer_forward(inp["x"], inp["w_router"], None, inp["w_gate"], inp["w_up"],
+                             inp["w_down"] * 2, k=2, renorm=1, phi=0)["y"]
+    assert np.array_equal(b, 2 * a)
+
+
+def test_combine_round_trip_with_uniform_gates():
+    """Gates 1/k over packed copies of x return x exactly (k a power of
+    two): checks that combine reads each route's own packed row."""
+    for k in (1, 2, 4):
+        w = Workload("rt", T=50, E=8, k=k, d=16, d_ff=8, dtype="bf16")
+        inp = make_inputs(w, seed=33)
+        L = oracle.router_logits(inp["x"], inp["w_router"])
+        ids, _ = oracle.topk_gates(L, k, 1)
+        disp = oracle.dispatch(ids, 8, -1)
+        packed = oracle.gather_rows(inp["x"], disp["row_token"])
+        gates = np.full((w.T, k), 1.0 / k, np.float32)
+        y = oracle.combine(packed, disp["route_pos"], gates)
+        assert np.array_equal(y, inp["x"].double().numpy())
+
+
+def test_expert_ffn_and_combine_compose_to_layer():
+    w = Workload("cmp", T=40, E=6, k=2, d=24, d_ff=32, d_ff_shared=16, dtype="bf16",
+                 phi=1.0, bias="normal")
+    inp = make_inputs(w, seed=34)
+    out = oracle.layer_forward(inp["x"], inp["w_router"], inp["b_router"], inp["w_gate"],
+                               inp["w_up"], inp["w_down"], k=2, renorm=1, phi=1.0,
+                               ws_gate=inp["ws_gate"], ws_up=inp["ws_up"], ws_down=inp["ws_down"])
+    C = oracle.capacity(w.T, w.E, w.k, 1.0)
+    disp = oracle.dispatch(out["ids"], w.E, C)
+    assert np.array_equal(disp["route_pos"], out["route_pos"])
+    packed = oracle.gather_rows(inp["x"], disp["row_token"])
+    yp = oracle.expert_ffn(packed, disp["offsets"], inp["w_gate"], inp["w_up"], inp["w_down"])
+    ysh = oracle.swiglu_rows(inp["x"], inp["ws_gate"], inp["ws_up"], inp["ws_down"])
+    y = oracle.combine(yp, disp["route_pos"], out["gates"], ysh)
+    assert np.allclose(y, out["y"], rtol=1e-12, atol=1e-12)
+
+
+def test_sampled_tokens_match_full_run_and_determinism():
+    w = Workload("sel", T=30, E=4, k=2, d=16, d_ff=16, dtype="bf16", phi=1.0)
+    inp = make_inputs(w, seed=35)
+    args = (inp["x"], inp["w_router"], None, inp["w_gate"], inp["w_up"], inp["w_down"])
+    full = oracle.layer_forward(*args, k=2, renorm=1, phi=1.0)
+    again = oracle.layer_forward(*args, k=2, renorm=1, phi=1.0)
+    for key in full:
+        assert np.array_equal(full[key], again[key])
+    sel = np.array([29, 0, 7, 7], np.int32)
+    part = oracle.layer_forward(*args, k=2, renorm=1, phi=1.0, sel=sel)
+    assert np.array_equal(part["y"], full["y"][sel])
+
+
+def test_empty_batch():
+    w = Workload("empty", T=0, E=4, k=2, d=16, d_ff=16, dtype="bf16")
+    inp = make_inputs(w, seed=36)
+    out = oracle.layer_forward(inp["x"], inp["w_router"], None, inp["w_gate"], inp["w_up"],
+                               inp["w_down"], k=2, renorm=1, phi=1.0)
+    assert out["y"].shape == (0, 16) and out["counts"].tolist() == [0, 0, 0, 0]
