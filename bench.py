@@ -1,0 +1,236 @@
+"""Benchmark of the MoE layer forward (route + pack + compute + combine) on one
+MI355X.
+
+A step is one moe_layer_forward call over one batch of seeded synthetic
+input, inputs resident in HBM.  By default each step uses the next of
+several device copies of the expert weights (enough copies to exceed the
+256 MB last-level cache), as consecutive MoE layers of a model would: the
+weights are read cold from HBM every step.
+
+Prints ONE JSON line:
+  value          whole-step tokens/s (T / step time)
+  roofline       dominant kernel (grouped GEMM 1, gate+up+SwiGLU) against
+                 the MI355X bf16 dense MFMA peak or the HBM peak, timed with
+                 hipEvents recorded on the library's stream around it
+  cpu_baseline   the CPU oracle on a bounded sample of the same workload
+  stages_us      mean per-stage times of the timed-variant pass
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+"""
+import argparse
+import ctypes
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_F32_TFLOPS = 157.3     # MI355X fp32 (vector)
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+MALL_BYTES = 256 << 20
+DEFAULT_WORKLOAD = "switch_phi125"
+STAGES = ["route", "permute", "gemm1_gate_up_swiglu", "gemm2_down", "shared_expert", "combine"]
+
+
+def _hip():
+    lib = ctypes.CDLL("libamdhip64.so")
+    lib.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+    lib.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                        ctypes.c_void_p]
+    lib.hipEventDestroy.argtypes = [ctypes.c_void_p]
+    return lib
+
+
+def gemm1_model(w, kept_rows, active_experts):
+    """Algorithmic flops and bytes of grouped GEMM 1 (gate + up + SwiGLU):
+    flops = kept * 4*d*d_ff; bytes = active experts' gate+up weights + the
+    kept token rows read + the hidden rows written."""
+    eb = 2 if w.dtype == "bf16" else 4
+    flops = kept_rows * 4.0 * w.d * w.d_ff
+    byts = active_experts * 2.0 * w.d * w.d_ff * eb + kept_rows * (w.d + w.d_ff) * eb
+    return flops, byts
+
+
+def traffic_from_profile(workload):
+    """HBM bytes per GEMM-1 launch from the committed rocprofv3 counter
+    summary, or None when absent or taken on a different gemm.hip."""
+    path = os.path.join(ROOT, "profiles", f"gemm1_{workload}_traffic.json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path))
+    src = open(os.path.join(ROOT, "routing_dispatch_expert_route_amd", "csrc", "gemm.hip"), "rb").read()
+    if rec.get("gemm_hip_sha256") != hashlib.sha256(src).hexdigest():
+        return None
+    return (rec["fetch_kib"] * rec["fetch_scale"] + rec["write_kib"] * rec["write_scale"]) * 1024.0
+
+
+def cpu_baseline(w, inp, seconds):
+    import numpy as np
+    import oracle
+    cores = int(os.environ.get("OMP_NUM_THREADS") or len(os.sched_getaffinity(0)))
+
+    def run(n):
+        sel = np.arange(n, dtype=np.int32)
+        t0 = time.perf_counter()
+        oracle.layer_forward(inp["x"], inp["w_router"], inp["b_router"], inp["w_gate"],
+                             inp["w_up"], inp["w_down"], w.k, w.renorm, w.phi, inp["ws_gate"],
+                             inp["ws_up"], inp["ws_down"], sel=sel)
+        return time.perf_counter() - t0
+
+    n0 = min(w.T, max(1, cores))
+    t_route = run(1)                      # routing of all T tokens + one token's FFN
+    t0 = max(run(n0) - t_route, 1e-3)     # per-token FFN cost from n0 tokens
+    n = int(min(w.T, max(n0, n0 * (seconds - t_route) / t0)))
+    t = run(n)
+    return {"value": n / t, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sample": f"first {n} of {w.T} tokens of {w.name} (routing of all {w.T} tokens, "
+                      f"expert FFN + combine of the {n}), {t:.1f} s wall"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--weight-sets", type=int, default=0,
+                    help="device copies of the weights cycled per step (0 = enough to exceed the LLC)")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--no-stages", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import routing_dispatch_expert_route_amd as moe
+    from workloads import WORKLOADS, make_inputs
+
+    w = WORKLOADS[args.workload]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    inp = make_inputs(w, seed=0)
+    d = {k: (None if v is None else v.to(dev)) for k, v in inp.items()}
+    s = moe.shape_of(w)
+    eb = 2 if w.dtype == "bf16" else 4
+    wbytes = (w.E * 3 * w.d * w.d_ff + 3 * w.d * w.d_ff_shared) * eb
+    nsets = args.weight_sets or max(1, -(-2 * MALL_BYTES // max(wbytes, 1)))
+    nsets = min(nsets, max(1, int(torch.cuda.mem_get_info()[0] * 0.6 // max(wbytes, 1))))
+    sets = [d] + [{k: (v.clone() if (v is not None and k.startswith("w")) else v)
+                   for k, v in d.items()} for _ in range(nsets - 1)]
+    ws = moe.workspace(s, dev)
+    y = torch.empty(w.T, w.d, dtype=w.torch_dtype, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step(i):
+        p = sets[i % nsets]
+        moe.layer_forward(s, p["x"], p["w_router"], p["b_router"], p["w_gate"], p["w_up"],
+                          p["w_down"], p["ws_gate"], p["ws_up"], p["ws_down"], y=y, ws=ws)
+
+    # routing statistics for the work model
+    _, rt = moe.layer_forward(s, d["x"], d["w_router"], d["b_router"], d["w_gate"], d["w_up"],
+                              d["w_down"], d["ws_gate"], d["ws_up"], d["ws_down"],
+                              return_routing=True)
+    counts = rt["counts"].cpu().long()
+    C, _ = moe.capacity(s)
+    kept = counts.clamp(max=C) if C >= 0 else counts
+    kept_rows = int(kept.sum())
+    active = int((kept > 0).sum())
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms = (t1 - t0) * 1e3 / args.steps
+    value = w.T / (ms / 1e3)
+
+    # per-stage times with hipEvents on the library's stream
+    stages = None
+    g1_us = None
+    if not args.no_stages:
+        hip = _hip()
+        K = args.steps
+        evs = []
+        for _ in range(K * 7):
+            e = ctypes.c_void_p()
+            assert hip.hipEventCreate(ctypes.byref(e)) == 0
+            evs.append(e.value)
+        torch.cuda.synchronize()
+        for i in range(K):
+            p = sets[i % nsets]
+            moe.layer_forward_timed(s, p["x"], p["w_router"], p["b_router"], p["w_gate"],
+                                    p["w_up"], p["w_down"], p["ws_gate"], p["ws_up"],
+                                    p["ws_down"], y, ws, evs[7 * i:7 * i + 7], stream=stream)
+        torch.cuda.synchronize()
+        acc = [0.0] * 6
+        f = ctypes.c_float()
+        for i in range(K):
+            for j in range(6):
+                assert hip.hipEventElapsedTime(ctypes.byref(f), evs[7 * i + j], evs[7 * i + j + 1]) == 0
+                acc[j] += f.value * 1e3
+        for e in evs:
+            hip.hipEventDestroy(e)
+        stages = {n: round(a / K, 2) for n, a in zip(STAGES, acc)}
+        g1_us = acc[2] / K
+
+    roof = None
+    if g1_us:
+        flops, byts = gemm1_model(w, kept_rows, active)
+        peak_c = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_F32_TFLOPS
+        t_c = flops / (peak_c * 1e12)
+        t_m = byts / (PEAK_HBM_GBS * 1e9)
+        if t_c >= t_m:
+            ach = flops / (g1_us * 1e-6) / 1e12
+            roof = {"bound": "mfma" if w.dtype == "bf16" else "alu", "achieved": round(ach, 1),
+                    "peak": peak_c, "unit": "TFLOP/s", "frac": round(ach / peak_c, 4)}
+        else:
+            ach = byts / (g1_us * 1e-6) / 1e9
+            roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBS,
+                    "unit": "GB/s", "frac": round(ach / PEAK_HBM_GBS, 4)}
+        roof["kernel"] = "gemm_bf16_kernel (grouped GEMM 1: gate+up+SwiGLU)"
+        roof["us_per_launch"] = round(g1_us, 2)
+        roof["algorithmic_flops"] = flops
+        roof["algorithmic_bytes"] = byts
+        roof["traffic"] = traffic_from_profile(w.name)
+
+    cpu = None
+    if not args.no_cpu:
+        cpu = cpu_baseline(w, inp, args.cpu_seconds)
+
+    out = {
+        "metric": "MoE layer forward tokens/s at 1 GPU",
+        "value": round(value, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if w.dtype == "bf16" else "f32",
+        "data": "synthetic (seeded randn, no checkpoint)",
+        "config": {"workload": w.name, "T": w.T, "E": w.E, "k": w.k, "d": w.d, "d_ff": w.d_ff,
+                   "d_ff_shared": w.d_ff_shared, "phi": w.phi, "renormalize": w.renorm,
+                   "kept_routes": kept_rows, "weight_sets": nsets,
+                   "parallelism": "single GPU"},
+        "roofline": roof,
+        "cpu_baseline": cpu,
+        "stages_us": stages,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,217 @@
+/*
+ * moe.h -- C ABI of the MI355X (gfx950) MoE layer forward library, libmoe.so.
+ *
+ * The layer is route + pack + compute + combine:
+ *   route    router projection, softmax, top-k (optionally renormalised over
+ *            the k selected experts), lowest expert index first on ties;
+ *   pack     counting-sort permute that duplicates token rows and groups them
+ *            by expert, with optional capacity C = ceil(phi*T*k/E) and
+ *            dropping of overflow routes in arrival (token) order;
+ *   compute  per-expert SwiGLU FFN, run as variable-size grouped GEMMs;
+ *   combine  gate-weighted un-permute that restores token order, plus an
+ *            optional always-on shared expert.
+ * Definitions follow these pages:
+ *   "271,104 Routes: What I Missed About Mixture-of-Experts" (michaelml.dev),
+ *      section 1 "The MoE Block" (y = sum_i p_i(x) E_i(x)), section 2
+ *      "The Router" (topk then softmax of the selected logits), section 3
+ *      "Dispatch: Turning Routes Into GPU Work" (stable argsort, bincount +
+ *      cumsum, index_select, restore).
+ *   "Mixture of Experts: Routing, Dispatch, and Load Balancing"
+ *      (int8ai.pages.dev), section 1 (router x W + b), sections 2-4.
+ *   "MoE Inference Visualized" (infra.bea.ai), "The Router" and
+ *      "Expert Execution" (gate/up/down SwiGLU expert; top-1 output scaled by
+ *      its softmax probability).
+ *   "Session 19: Mixture-of-Experts: routing and capacity"
+ *      (cours.spawnkit.ai), "Top-k and mixture" (renormalisation, shared
+ *      expert), "Capacity" and "Worked case -- full trace" (C, drops).
+ *   "Mixture-of-experts routing" (understandingdata.com), "The maths"
+ *      (gate, capacity and imbalance formulas).
+ *
+ * Conventions for every entry point:
+ *  - Pointers are DEVICE pointers unless marked "host".  Tensors are
+ *    row-major and contiguous; x, weights, packed rows and outputs must be
+ *    16-byte aligned.  Weights use the [out, in] storage of a linear layer.
+ *  - Element type of x, weights, packed rows, hidden rows and y is the
+ *    shape's dtype (fp32 or bf16).  Accumulation is always fp32.  Router
+ *    bias, logits and gates are fp32; ids, counts and indices int32.
+ *  - Ownership: the caller allocates and owns every buffer, including the
+ *    workspace (moe_workspace_bytes).  The library never allocates or frees
+ *    device memory, keeps no state between calls and is reentrant.
+ *  - Every call is asynchronous on the given HIP stream (NULL = the null
+ *    stream); none synchronises or reads device memory on the host.
+ *  - Errors: every call validates its arguments on the host before any
+ *    launch and returns a moe_status.  On error nothing is launched and no
+ *    output is touched.  A failed launch returns MOE_ERR_HIP; faults inside
+ *    kernels surface at the caller's next synchronisation.  No C++
+ *    exception crosses this interface.
+ *  - Supported range: T >= 0, T*k < 2^31, 1 <= E <= 256, 1 <= k <= min(E, 8),
+ *    d, d_ff (and d_ff_shared when non-zero) positive multiples of 8.
+ *    NaN or infinite inputs give unspecified (but memory-safe) results.
+ */
+#ifndef MOE_H
+#define MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum moe_status {
+  MOE_OK = 0,
+  MOE_ERR_INVALID_ARG = 1, /* null required pointer, bad size, misalignment */
+  MOE_ERR_UNSUPPORTED = 2, /* outside the supported range or unknown mode  */
+  MOE_ERR_WORKSPACE = 3,   /* workspace missing or smaller than required   */
+  MOE_ERR_HIP = 4          /* a kernel launch failed                       */
+} moe_status;
+
+#define MOE_DTYPE_F32 0
+#define MOE_DTYPE_BF16 1
+#define MOE_TIE_LOWEST_INDEX 0
+
+/* Problem description (host struct, passed by pointer). */
+typedef struct moe_shape {
+  int64_t T;           /* tokens                                           */
+  int64_t d;           /* model width                                      */
+  int64_t E;           /* routed experts                                   */
+  int64_t k;           /* experts selected per token                       */
+  int64_t d_ff;        /* routed-expert SwiGLU hidden width                */
+  int64_t d_ff_shared; /* shared-expert hidden width, 0 = no shared expert */
+  int32_t dtype;       /* MOE_DTYPE_F32 or MOE_DTYPE_BF16                  */
+  int32_t renormalize; /* 1: gates = softmax over the k selected logits;
+                          0: gates = full softmax probabilities over all E */
+  int32_t tie_break;   /* MOE_TIE_LOWEST_INDEX (only supported rule)       */
+  int32_t reserved;    /* must be 0                                        */
+  double phi;          /* capacity factor; <= 0 means no capacity limit    */
+} moe_shape;
+
+/* Human-readable name of a status code (static string). */
+const char* moe_status_string(int status);
+
+/* Host only.  Capacity and packed-row bound.
+ * C = ceil(phi * (double)(T*k) / (double)E) when phi > 0, else -1 (no
+ * limit) -- "Mixture-of-experts routing", "Capacity"; the spawnkit trace
+ * gives C = ceil(8*2/4*1.25) = 5.  R_max = T*k without a limit, else
+ * min(T*k, E*C): the number of rows every packed buffer must hold.
+ * Either output pointer may be NULL. */
+int moe_capacity(const moe_shape* s, int64_t* C_out /*host*/, int64_t* R_max_out /*host*/);
+
+/* Host only.  Bytes of device workspace that moe_route, moe_permute,
+ * moe_expert_ffn and moe_layer_forward need for shape s (one size serves
+ * all of them; 0 is never returned for a valid shape).  The workspace must be 256-byte
+ * aligned. */
+int moe_workspace_bytes(const moe_shape* s, size_t* bytes_out /*host*/);
+
+/* Route: logits = x W_router^T + b ("Mixture of Experts: Routing, Dispatch,
+ * and Load Balancing", section 1), fp32, each dot product accumulated by a
+ * sequential fused multiply-add in increasing hidden index, bias added
+ * after; top-k by (logit descending, expert index ascending) ("271,104
+ * Routes", section 2); gates per shape->renormalize (see moe_shape).
+ *   x           [T, d]   dtype
+ *   w_router    [E, d]   dtype
+ *   b_router    [E]      fp32, may be NULL (no bias)
+ *   logits      [T, E]   fp32 output, may be NULL (not written)
+ *   expert_ids  [T, k]   int32 output, slot j = j-th largest logit
+ *   gates       [T, k]   fp32 output
+ * Workspace: moe_workspace_bytes (holds the logits when logits is NULL). */
+int moe_route(const moe_shape* s, const void* x, const void* w_router, const float* b_router,
+              float* logits, int32_t* expert_ids, float* gates, void* ws, size_t ws_bytes,
+              hipStream_t stream);
+
+/* Pack: stable counting sort of the T*k routes r = t*k + j by expert
+ * ("271,104 Routes", section 3: argsort(stable) + bincount.cumsum), with
+ * capacity: route r is kept iff its arrival slot (number of earlier routes
+ * to the same expert) is < C; overflow routes are dropped ("Session 19",
+ * "Capacity" and the full trace).
+ *   x           [T, d]     dtype
+ *   expert_ids  [T, k]     int32, each in [0, E); a token lists an expert at
+ *                          most once (as moe_route produces)
+ *   counts      [E]        int32 output: demand n_e before capacity
+ *   kept_counts [E]        int32 output: m_e = min(n_e, C)
+ *   offsets     [E+1]      int32 output: exclusive prefix of m_e
+ *   route_pos   [T, k]     int32 output: packed row of route r, -1 if dropped
+ *   row_token   [R_max]    int32 output: source token of packed row p
+ *   x_packed    [R_max, d] dtype output: x_packed[p] = x[row_token[p]]
+ * Rows at or past offsets[E] of row_token / x_packed are left unwritten.
+ * Workspace: moe_workspace_bytes. */
+int moe_permute(const moe_shape* s, const void* x, const int32_t* expert_ids, int32_t* counts,
+                int32_t* kept_counts, int32_t* offsets, int32_t* route_pos, int32_t* row_token,
+                void* x_packed, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* Compute: for every expert e and packed row p in [offsets[e], offsets[e+1]):
+ *   y_packed[p] = W_down[e] (SiLU(W_gate[e] x_p) * (W_up[e] x_p))
+ * ("MoE Inference Visualized", "Expert Execution"), as two grouped GEMMs on
+ * bf16 MFMA (fp32 accumulation; the hidden activations are rounded to dtype
+ * between the two GEMMs).
+ *   x_packed    [R_max, d]       dtype
+ *   offsets     [E+1]            int32 (device; never read on the host)
+ *   w_gate      [E, d_ff, d]     dtype
+ *   w_up        [E, d_ff, d]     dtype
+ *   w_down      [E, d, d_ff]     dtype
+ *   y_packed    [R_max, d]       dtype output (rows past offsets[E] unwritten)
+ * offsets[E] must be <= R_max of the shape.  A dense FFN (such as a shared
+ * expert) is the case E = 1, k = 1 with offsets = {0, T}.
+ * Workspace: moe_workspace_bytes. */
+int moe_expert_ffn(const moe_shape* s, const void* x_packed, const int32_t* offsets,
+                   const void* w_gate, const void* w_up, const void* w_down, void* y_packed,
+                   void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* Combine: y[t] = sum_{j<k, route_pos[t,j] >= 0} gates[t,j] * y_packed[route_pos[t,j]]
+ *                 (+ y_shared[t])
+ * summed in fp32 with j ascending, shared output added last, rounded once to
+ * dtype ("271,104 Routes", sections 1 and 3; "Session 19", "Top-k and
+ * mixture": the shared expert is outside the gate normalisation; dropped
+ * routes contribute nothing and the other gates are not renormalised).
+ *   y_packed  [R_max, d]  dtype
+ *   route_pos [T, k]      int32
+ *   gates     [T, k]      fp32
+ *   y_shared  [T, d]      dtype, may be NULL
+ *   y         [T, d]      dtype output
+ * No workspace. */
+int moe_combine(const moe_shape* s, const void* y_packed, const int32_t* route_pos,
+                const float* gates, const void* y_shared, void* y, hipStream_t stream);
+
+/* The whole layer: route -> pack -> compute (routed experts, and the shared
+ * expert when d_ff_shared > 0) -> combine, all stream-ordered with no host
+ * synchronisation.  The packed copy of x is not materialised: the first
+ * grouped GEMM reads token rows through the route table.  No residual add
+ * (the caller adds x).
+ *   x, w_router, b_router (nullable)       as in moe_route
+ *   w_gate, w_up, w_down                   as in moe_expert_ffn
+ *   ws_gate [d_ff_shared, d], ws_up [d_ff_shared, d], ws_down [d, d_ff_shared]
+ *                                          dtype; required iff d_ff_shared > 0
+ *   y          [T, d]  dtype output
+ *   expert_ids [T, k], gates [T, k], counts [E], route_pos [T, k]:
+ *              optional outputs (NULL = not returned)
+ * Workspace: moe_workspace_bytes. */
+int moe_layer_forward(const moe_shape* s, const void* x, const void* w_router,
+                      const float* b_router, const void* w_gate, const void* w_up,
+                      const void* w_down, const void* ws_gate, const void* ws_up,
+                      const void* ws_down, void* y, int32_t* expert_ids, float* gates,
+                      int32_t* counts, int32_t* route_pos, void* ws, size_t ws_bytes,
+                      hipStream_t stream);
+
+/* Measurement variant of moe_layer_forward (same arguments without the
+ * optional routing outputs): additionally records events[i] on the stream at
+ * the stage boundaries, so that elapsed times between them are the stage
+ * times ("271,104 Routes", "The next experiment": one trace that lines up
+ * router, permutation and packing, expert matmuls and combine):
+ *   events[0] before route          events[1] before the permute
+ *   events[2] before grouped GEMM 1 events[3] before grouped GEMM 2
+ *   events[4] before the shared expert (equal to events[5] without one)
+ *   events[5] before combine        events[6] after combine
+ *   events     host array of 7 hipEvent_t created by the caller; a NULL
+ *              entry is skipped.  The array itself must not be NULL. */
+int moe_layer_forward_timed(const moe_shape* s, const void* x, const void* w_router,
+                            const float* b_router, const void* w_gate, const void* w_up,
+                            const void* w_down, const void* ws_gate, const void* ws_up,
+                            const void* ws_down, void* y, void* ws, size_t ws_bytes,
+                            hipStream_t stream, hipEvent_t* events /*host*/);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOE_H */

@@ -1,0 +1,270 @@
+"""MI355X (gfx950) MoE layer forward: route + pack + compute + combine.
+
+Thin Python binding over the C ABI of libmoe.so (include/moe.h).  Every step
+of the layer runs in the library's HIP kernels; this module only checks
+tensor arguments, allocates outputs with torch (device memory and streams are
+torch's) and passes pointers.  There is no fallback: importing this package
+fails when libmoe.so has not been built.
+
+Entry points (same names as the C ABI, without the moe_ prefix):
+    capacity, workspace_bytes, route, permute, expert_ffn, combine,
+    layer_forward
+"""
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmoe.so")
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(
+        f"libmoe.so is not built ({LIB_PATH}); run "
+        "`python routing_dispatch_expert_route_amd/build.py` or __graft_entry__.build()")
+
+_lib = ctypes.CDLL(LIB_PATH)
+
+DTYPE_F32, DTYPE_BF16 = 0, 1
+MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = range(5)
+
+EXPORTS = ("moe_status_string", "moe_capacity", "moe_workspace_bytes", "moe_route",
+           "moe_permute", "moe_expert_ffn", "moe_combine", "moe_layer_forward",
+           "moe_layer_forward_timed")
+
+
+class MoeShape(ctypes.Structure):
+    _fields_ = [("T", ctypes.c_int64), ("d", ctypes.c_int64), ("E", ctypes.c_int64),
+                ("k", ctypes.c_int64), ("d_ff", ctypes.c_int64), ("d_ff_shared", ctypes.c_int64),
+                ("dtype", ctypes.c_int32), ("renormalize", ctypes.c_int32),
+                ("tie_break", ctypes.c_int32), ("reserved", ctypes.c_int32),
+                ("phi", ctypes.c_double)]
+
+
+class MoeError(RuntimeError):
+    def __init__(self, status, where):
+        self.status = status
+        super().__init__(f"{where}: {_lib.moe_status_string(status).decode()}")
+
+
+_vp, _sz, _i64p = ctypes.c_void_p, ctypes.c_size_t, ctypes.POINTER(ctypes.c_int64)
+_SP = ctypes.POINTER(MoeShape)
+_lib.moe_status_string.restype = ctypes.c_char_p
+_lib.moe_status_string.argtypes = [ctypes.c_int]
+_lib.moe_capacity.argtypes = [_SP, _i64p, _i64p]
+_lib.moe_workspace_bytes.argtypes = [_SP, ctypes.POINTER(_sz)]
+_lib.moe_route.argtypes = [_SP] + [_vp] * 6 + [_vp, _sz, _vp]
+_lib.moe_permute.argtypes = [_SP] + [_vp] * 8 + [_vp, _sz, _vp]
+_lib.moe_expert_ffn.argtypes = [_SP] + [_vp] * 6 + [_vp, _sz, _vp]
+_lib.moe_combine.argtypes = [_SP] + [_vp] * 5 + [_vp]
+_lib.moe_layer_forward.argtypes = [_SP] + [_vp] * 14 + [_vp, _sz, _vp]
+_lib.moe_layer_forward_timed.argtypes = [_SP] + [_vp] * 10 + [_vp, _sz, _vp, _vp]
+for _n in EXPORTS[1:]:
+    getattr(_lib, _n).restype = ctypes.c_int
+
+
+def shape(T, d, E, k, d_ff, d_ff_shared=0, dtype="bf16", renorm=1, phi=0.0):
+    """Build the C moe_shape struct."""
+    dt = {"bf16": DTYPE_BF16, torch.bfloat16: DTYPE_BF16, "f32": DTYPE_F32,
+          torch.float32: DTYPE_F32}[dtype]
+    return MoeShape(int(T), int(d), int(E), int(k), int(d_ff), int(d_ff_shared), dt,
+                    int(renorm), 0, 0, float(phi))
+
+
+def shape_of(w):
+    """moe_shape of a workloads.Workload."""
+    return shape(w.T, w.d, w.E, w.k, w.d_ff, w.d_ff_shared, w.dtype, w.renorm, w.phi)
+
+
+def _tdtype(s):
+    return torch.bfloat16 if s.dtype == DTYPE_BF16 else torch.float32
+
+
+def _check(status, where):
+    if status != MOE_OK:
+        raise MoeError(status, where)
+
+
+def _ptr(t, name, shp=None, dtype=None, device=None, optional=False):
+    if t is None:
+        if optional:
+            return None
+        raise ValueError(f"{name} is required")
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if shp is not None and tuple(t.shape) != tuple(shp):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shp)}")
+    if t.numel() == 0:
+        return None
+    return t.data_ptr()
+
+
+def _stream(stream):
+    s = torch.cuda.current_stream() if stream is None else stream
+    return s.cuda_stream
+
+
+def capacity(s):
+    """(C, R_max): C = -1 without a capacity limit."""
+    C, R = ctypes.c_int64(), ctypes.c_int64()
+    _check(_lib.moe_capacity(ctypes.byref(s), ctypes.byref(C), ctypes.byref(R)), "moe_capacity")
+    return C.value, R.value
+
+
+def workspace_bytes(s):
+    n = _sz()
+    _check(_lib.moe_workspace_bytes(ctypes.byref(s), ctypes.byref(n)), "moe_workspace_bytes")
+    return n.value
+
+
+def workspace(s, device="cuda"):
+    """A device byte tensor of moe_workspace_bytes (torch allocations are 256-byte aligned)."""
+    return torch.empty(workspace_bytes(s), dtype=torch.uint8, device=device)
+
+
+def _ws(s, ws, device):
+    if ws is None:
+        ws = workspace(s, device)
+    _ptr(ws, "ws", dtype=torch.uint8)
+    return ws
+
+
+def route(s, x, w_router, b_router=None, logits=None, ws=None, stream=None, want_logits=False):
+    """Router logits, top-k ids and gates.  Returns (expert_ids, gates, logits-or-None)."""
+    dt = _tdtype(s)
+    dev = x.device
+    xp = _ptr(x, "x", (s.T, s.d), dt)
+    wp = _ptr(w_router, "w_router", (s.E, s.d), dt)
+    bp = _ptr(b_router, "b_router", (s.E,), torch.float32, optional=True)
+    if logits is None and want_logits:
+        logits = torch.empty(s.T, s.E, dtype=torch.float32, device=dev)
+    lp = _ptr(logits, "logits", (s.T, s.E), torch.float32, optional=True)
+    ids = torch.empty(s.T, s.k, dtype=torch.int32, device=dev)
+    gates = torch.empty(s.T, s.k, dtype=torch.float32, device=dev)
+    ws = _ws(s, ws, dev)
+    _check(_lib.moe_route(ctypes.byref(s), xp, wp, bp, lp, ids.data_ptr() if ids.numel() else None,
+                          gates.data_ptr() if gates.numel() else None, ws.data_ptr(), ws.numel(),
+                          _stream(stream)), "moe_route")
+    return ids, gates, logits
+
+
+def permute(s, x, expert_ids, ws=None, stream=None):
+    """Counting-sort dispatch.  Returns dict(counts, kept_counts, offsets,
+    route_pos, row_token, x_packed); row_token / x_packed have R_max rows, of
+    which the first offsets[E] are written."""
+    dt = _tdtype(s)
+    dev = x.device
+    _, R_max = capacity(s)
+    xp = _ptr(x, "x", (s.T, s.d), dt)
+    ip = _ptr(expert_ids, "expert_ids", (s.T, s.k), torch.int32)
+    out = dict(counts=torch.empty(s.E, dtype=torch.int32, device=dev),
+               kept_counts=torch.empty(s.E, dtype=torch.int32, device=dev),
+               offsets=torch.empty(s.E + 1, dtype=torch.int32, device=dev),
+               route_pos=torch.empty(s.T, s.k, dtype=torch.int32, device=dev),
+               row_token=torch.empty(max(R_max, 1), dtype=torch.int32, device=dev),
+               x_packed=torch.empty(max(R_max, 1), s.d, dtype=dt, device=dev))
+    ws = _ws(s, ws, dev)
+    _check(_lib.moe_permute(ctypes.byref(s), xp, ip, out["counts"].data_ptr(),
+                            out["kept_counts"].data_ptr(), out["offsets"].data_ptr(),
+                            _ptr(out["route_pos"], "route_pos"), out["row_token"].data_ptr(),
+                            out["x_packed"].data_ptr(), ws.data_ptr(), ws.numel(),
+                            _stream(stream)), "moe_permute")
+    return out
+
+
+def expert_ffn(s, x_packed, offsets, w_gate, w_up, w_down, y_packed=None, ws=None, stream=None):
+    """Grouped SwiGLU expert FFN over packed rows.  Returns y_packed [R_max, d]."""
+    dt = _tdtype(s)
+    dev = x_packed.device
+    xp = _ptr(x_packed, "x_packed", dtype=dt)
+    if x_packed.dim() != 2 or x_packed.shape[1] != s.d:
+        raise ValueError("x_packed must be [rows, d]")
+    op = _ptr(offsets, "offsets", (s.E + 1,), torch.int32)
+    gp = _ptr(w_gate, "w_gate", (s.E, s.d_ff, s.d), dt)
+    up = _ptr(w_up, "w_up", (s.E, s.d_ff, s.d), dt)
+    dp = _ptr(w_down, "w_down", (s.E, s.d, s.d_ff), dt)
+    if y_packed is None:
+        y_packed = torch.empty(x_packed.shape[0], s.d, dtype=dt, device=dev)
+    yp = _ptr(y_packed, "y_packed", (x_packed.shape[0], s.d), dt)
+    ws = _ws(s, ws, dev)
+    _check(_lib.moe_expert_ffn(ctypes.byref(s), xp, op, gp, up, dp, yp, ws.data_ptr(), ws.numel(),
+                               _stream(stream)), "moe_expert_ffn")
+    return y_packed
+
+
+def combine(s, y_packed, route_pos, gates, y_shared=None, y=None, stream=None):
+    """Gate-weighted un-permute (+ shared expert rows).  Returns y [T, d]."""
+    dt = _tdtype(s)
+    dev = y_packed.device
+    yp = _ptr(y_packed, "y_packed", dtype=dt)
+    rp = _ptr(route_pos, "route_pos", (s.T, s.k), torch.int32)
+    gp = _ptr(gates, "gates", (s.T, s.k), torch.float32)
+    sp = _ptr(y_shared, "y_shared", (s.T, s.d), dt, optional=True)
+    if y is None:
+        y = torch.empty(s.T, s.d, dtype=dt, device=dev)
+    op = _ptr(y, "y", (s.T, s.d), dt)
+    _check(_lib.moe_combine(ctypes.byref(s), yp, rp, gp, sp, op, _stream(stream)), "moe_combine")
+    return y
+
+
+def layer_forward(s, x, w_router, b_router, w_gate, w_up, w_down, ws_gate=None, ws_up=None,
+                  ws_down=None, y=None, ws=None, stream=None, return_routing=False):
+    """Whole MoE layer.  Returns y, or (y, dict(expert_ids, gates, counts,
+    route_pos)) with return_routing."""
+    dt = _tdtype(s)
+    dev = x.device
+    xp = _ptr(x, "x", (s.T, s.d), dt)
+    rp = _ptr(w_router, "w_router", (s.E, s.d), dt)
+    bp = _ptr(b_router, "b_router", (s.E,), torch.float32, optional=True)
+    gp = _ptr(w_gate, "w_gate", (s.E, s.d_ff, s.d), dt)
+    up = _ptr(w_up, "w_up", (s.E, s.d_ff, s.d), dt)
+    dp = _ptr(w_down, "w_down", (s.E, s.d, s.d_ff), dt)
+    shp = s.d_ff_shared > 0
+    sg = _ptr(ws_gate, "ws_gate", (s.d_ff_shared, s.d), dt, optional=not shp)
+    su = _ptr(ws_up, "ws_up", (s.d_ff_shared, s.d), dt, optional=not shp)
+    sd = _ptr(ws_down, "ws_down", (s.d, s.d_ff_shared), dt, optional=not shp)
+    if y is None:
+        y = torch.empty(s.T, s.d, dtype=dt, device=dev)
+    yo = _ptr(y, "y", (s.T, s.d), dt)
+    routing = None
+    ip = gtp = cp = rpp = None
+    if return_routing:
+        routing = dict(expert_ids=torch.empty(s.T, s.k, dtype=torch.int32, device=dev),
+                       gates=torch.empty(s.T, s.k, dtype=torch.float32, device=dev),
+                       counts=torch.empty(s.E, dtype=torch.int32, device=dev),
+                       route_pos=torch.empty(s.T, s.k, dtype=torch.int32, device=dev))
+        ip = _ptr(routing["expert_ids"], "expert_ids")
+        gtp = _ptr(routing["gates"], "gates")
+        cp = _ptr(routing["counts"], "counts")
+        rpp = _ptr(routing["route_pos"], "route_pos")
+    ws = _ws(s, ws, dev)
+    _check(_lib.moe_layer_forward(ctypes.byref(s), xp, rp, bp, gp, up, dp, sg, su, sd, yo, ip, gtp,
+                                  cp, rpp, ws.data_ptr(), ws.numel(), _stream(stream)),
+           "moe_layer_forward")
+    return (y, routing) if return_routing else y
+
+
+def layer_forward_timed(s, x, w_router, b_router, w_gate, w_up, w_down, ws_gate, ws_up, ws_down,
+                        y, ws, events, stream=None):
+    """moe_layer_forward_timed: records the 7 stage-boundary hipEvents
+    (`events`: sequence of raw hipEvent_t handles as ints)."""
+    dt = _tdtype(s)
+    arr = (ctypes.c_void_p * 7)(*[ctypes.c_void_p(e) for e in events])
+    shp = s.d_ff_shared > 0
+    _check(_lib.moe_layer_forward_timed(
+        ctypes.byref(s), _ptr(x, "x", (s.T, s.d), dt), _ptr(w_router, "w_router", (s.E, s.d), dt),
+        _ptr(b_router, "b_router", (s.E,), torch.float32, optional=True),
+        _ptr(w_gate, "w_gate", (s.E, s.d_ff, s.d), dt), _ptr(w_up, "w_up", (s.E, s.d_ff, s.d), dt),
+        _ptr(w_down, "w_down", (s.E, s.d, s.d_ff), dt),
+        _ptr(ws_gate, "ws_gate", (s.d_ff_shared, s.d), dt, optional=not shp),
+        _ptr(ws_up, "ws_up", (s.d_ff_shared, s.d), dt, optional=not shp),
+        _ptr(ws_down, "ws_down", (s.d, s.d_ff_shared), dt, optional=not shp),
+        _ptr(y, "y", (s.T, s.d), dt), ws.data_ptr(), ws.numel(), _stream(stream), arr),
+        "moe_layer_forward_timed")
+    return y

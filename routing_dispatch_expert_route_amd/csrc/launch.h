@@ -1,0 +1,42 @@
+// launch.h -- host-side launchers of the HIP kernels (internal to libmoe).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+// router_logits_kernel + topk_gates_kernel
+hipError_t launch_route(bool bf16, const void* x, const void* w, const float* b, int T, int d,
+                        int E, int k, int renorm, float* logits, int32_t* ids, float* gates,
+                        hipStream_t st);
+
+// hist + scan + scatter.  cnt_ws holds E * permute_nchunks(T*k) ints.
+int permute_nchunks(long R);
+hipError_t launch_permute_index(const int32_t* ids, int T, int k, int E, int C, int32_t* cnt_ws,
+                                int32_t* counts, int32_t* kept, int32_t* offsets,
+                                int32_t* route_pos, int32_t* row_token, hipStream_t st);
+hipError_t launch_gather_rows(const void* x, const int32_t* row_token, const int32_t* offsets,
+                              int E, long R_max, long row_bytes, void* x_packed, hipStream_t st);
+
+// Row groups of a grouped GEMM: device offsets[E+1] (never read on the
+// host), or one dense group of M_dense rows when offsets is null.
+struct GemmPlan {
+  bool bf16;
+  const int32_t* offsets;
+  int E;
+  int M_dense;
+  long R_max;  // bound on offsets[E]
+  long m_cap;  // bound on any one group's rows
+};
+hipError_t launch_gemm_swiglu(const GemmPlan& pl, const void* A, const int32_t* a_rows,
+                              const void* Wg, const void* Wu, int N, int K, void* H,
+                              hipStream_t st);
+hipError_t launch_gemm_down(const GemmPlan& pl, const void* H, const void* Wd, int N, int K,
+                            void* Y, hipStream_t st);
+
+hipError_t launch_combine(bool bf16, const void* y_packed, const int32_t* route_pos,
+                          const float* gates, const void* y_shared, int T, int k, int d, void* y,
+                          hipStream_t st);
+
+}  // namespace moe

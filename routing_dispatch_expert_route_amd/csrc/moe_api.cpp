@@ -1,0 +1,309 @@
+// moe_api.cpp -- the C ABI of libmoe (include/moe.h): argument validation,
+// capacity and workspace arithmetic, and stream-ordered kernel launches.
+// No allocation, no host synchronisation, no state.
+#include "moe.h"
+
+#include <math.h>
+#include <stdint.h>
+
+#include "launch.h"
+
+namespace {
+
+constexpr int64_t kMaxE = 256;
+constexpr int64_t kMaxK = 8;
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int elem_bytes(const moe_shape* s) { return s->dtype == MOE_DTYPE_BF16 ? 2 : 4; }
+
+int validate(const moe_shape* s) {
+  if (!s) return MOE_ERR_INVALID_ARG;
+  if (s->reserved != 0) return MOE_ERR_INVALID_ARG;
+  if (s->T < 0 || s->d <= 0 || s->E <= 0 || s->k <= 0 || s->d_ff <= 0 || s->d_ff_shared < 0)
+    return MOE_ERR_INVALID_ARG;
+  if (s->d % 8 || s->d_ff % 8 || s->d_ff_shared % 8) return MOE_ERR_INVALID_ARG;
+  if (s->k > s->E) return MOE_ERR_INVALID_ARG;
+  if (isnan(s->phi)) return MOE_ERR_INVALID_ARG;
+  if (s->renormalize != 0 && s->renormalize != 1) return MOE_ERR_INVALID_ARG;
+  if (s->dtype != MOE_DTYPE_F32 && s->dtype != MOE_DTYPE_BF16) return MOE_ERR_UNSUPPORTED;
+  if (s->tie_break != MOE_TIE_LOWEST_INDEX) return MOE_ERR_UNSUPPORTED;
+  if (s->E > kMaxE || s->k > kMaxK) return MOE_ERR_UNSUPPORTED;
+  if (s->T * s->k >= (int64_t(1) << 31)) return MOE_ERR_UNSUPPORTED;
+  if (s->d >= (int64_t(1) << 24) || s->d_ff >= (int64_t(1) << 24) ||
+      s->d_ff_shared >= (int64_t(1) << 24))
+    return MOE_ERR_UNSUPPORTED;
+  return MOE_OK;
+}
+
+// C = ceil(phi * (double)(T*k) / (double)E), -1 without a limit; clamped to T*k.
+int64_t capacity_of(const moe_shape* s) {
+  if (!(s->phi > 0.0)) return -1;
+  const double c = ceil(s->phi * (double)(s->T * s->k) / (double)s->E);
+  const double lim = (double)(s->T * s->k);
+  return (int64_t)(c < lim ? c : lim);
+}
+
+int64_t rmax_of(const moe_shape* s, int64_t C) {
+  const int64_t R = s->T * s->k;
+  if (C < 0) return R;
+  const int64_t ec = s->E * C;
+  return ec < R ? ec : R;
+}
+
+struct Layout {
+  size_t logits, ids, gates, cnt, counts, kept, offsets, route_pos, row_token, h, yp, hs, ys;
+  size_t total;
+};
+
+Layout layout_of(const moe_shape* s) {
+  const int64_t C = capacity_of(s);
+  const int64_t Rmax = rmax_of(s, C);
+  const size_t R = (size_t)(s->T * s->k);
+  const size_t eb = (size_t)elem_bytes(s);
+  const size_t nch = (size_t)moe::permute_nchunks((long)R);
+  Layout L{};
+  size_t o = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = o;
+    o += align_up(bytes > 0 ? bytes : 1);
+    return at;
+  };
+  L.logits = take((size_t)s->T * s->E * sizeof(float));
+  L.ids = take(R * sizeof(int32_t));
+  L.gates = take(R * sizeof(float));
+  L.cnt = take((size_t)s->E * nch * sizeof(int32_t));
+  L.counts = take((size_t)s->E * sizeof(int32_t));
+  L.kept = take((size_t)s->E * sizeof(int32_t));
+  L.offsets = take((size_t)(s->E + 1) * sizeof(int32_t));
+  L.route_pos = take(R * sizeof(int32_t));
+  L.row_token = take((size_t)Rmax * sizeof(int32_t));
+  L.h = take((size_t)Rmax * s->d_ff * eb);
+  L.yp = take((size_t)Rmax * s->d * eb);
+  L.hs = take((size_t)s->T * s->d_ff_shared * eb);
+  L.ys = take(s->d_ff_shared > 0 ? (size_t)s->T * s->d * eb : 0);
+  L.total = o;
+  return L;
+}
+
+int check_ws(const moe_shape* s, void* ws, size_t ws_bytes) {
+  if (!ws) return MOE_ERR_WORKSPACE;
+  if (reinterpret_cast<uintptr_t>(ws) % kAlign) return MOE_ERR_WORKSPACE;
+  if (ws_bytes < layout_of(s).total) return MOE_ERR_WORKSPACE;
+  return MOE_OK;
+}
+
+template <typename T>
+T* at(void* ws, size_t off) {
+  return reinterpret_cast<T*>(reinterpret_cast<char*>(ws) + off);
+}
+
+int hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+const char* moe_status_string(int status) {
+  switch (status) {
+    case MOE_OK: return "MOE_OK";
+    case MOE_ERR_INVALID_ARG: return "MOE_ERR_INVALID_ARG: invalid argument";
+    case MOE_ERR_UNSUPPORTED: return "MOE_ERR_UNSUPPORTED: outside the supported range";
+    case MOE_ERR_WORKSPACE: return "MOE_ERR_WORKSPACE: workspace missing, misaligned or too small";
+    case MOE_ERR_HIP: return "MOE_ERR_HIP: kernel launch failed";
+    default: return "unknown moe status";
+  }
+}
+
+int moe_capacity(const moe_shape* s, int64_t* C_out, int64_t* R_max_out) {
+  const int v = validate(s);
+  if (v != MOE_OK) return v;
+  const int64_t C = capacity_of(s);
+  if (C_out) *C_out = C;
+  if (R_max_out) *R_max_out = rmax_of(s, C);
+  return MOE_OK;
+}
+
+int moe_workspace_bytes(const moe_shape* s, size_t* bytes_out) {
+  const int v = validate(s);
+  if (v != MOE_OK) return v;
+  if (!bytes_out) return MOE_ERR_INVALID_ARG;
+  *bytes_out = layout_of(s).total;
+  return MOE_OK;
+}
+
+int moe_route(const moe_shape* s, const void* x, const void* w_router, const float* b_router,
+              float* logits, int32_t* expert_ids, float* gates, void* ws, size_t ws_bytes,
+              hipStream_t stream) {
+  int v = validate(s);
+  if (v != MOE_OK) return v;
+  const bool tok = s->T > 0;  // token-sized buffers may be NULL when T == 0
+  if (!w_router || (tok && (!x || !expert_ids || !gates))) return MOE_ERR_INVALID_ARG;
+  if (!aligned16(x) || !aligned16(w_router)) return MOE_ERR_INVALID_ARG;
+  if (!logits) {
+    v = check_ws(s, ws, ws_bytes);
+    if (v != MOE_OK) return v;
+    logits = at<float>(ws, layout_of(s).logits);
+  }
+  return hip_status(moe::launch_route(s->dtype == MOE_DTYPE_BF16, x, w_router, b_router, (int)s->T,
+                                      (int)s->d, (int)s->E, (int)s->k, s->renormalize, logits,
+                                      expert_ids, gates, stream));
+}
+
+int moe_permute(const moe_shape* s, const void* x, const int32_t* expert_ids, int32_t* counts,
+                int32_t* kept_counts, int32_t* offsets, int32_t* route_pos, int32_t* row_token,
+                void* x_packed, void* ws, size_t ws_bytes, hipStream_t stream) {
+  int v = validate(s);
+  if (v != MOE_OK) return v;
+  const bool tok = s->T > 0;  // token- and row-sized buffers may be NULL when T == 0
+  if (!counts || !kept_counts || !offsets ||
+      (tok && (!x || !expert_ids || !route_pos || !row_token || !x_packed)))
+    return MOE_ERR_INVALID_ARG;
+  if (!aligned16(x) || !aligned16(x_packed)) return MOE_ERR_INVALID_ARG;
+  v = check_ws(s, ws, ws_bytes);
+  if (v != MOE_OK) return v;
+  const Layout L = layout_of(s);
+  const int64_t C = capacity_of(s);
+  hipError_t e = moe::launch_permute_index(expert_ids, (int)s->T, (int)s->k, (int)s->E, (int)C,
+                                           at<int32_t>(ws, L.cnt), counts, kept_counts, offsets,
+                                           route_pos, row_token, stream);
+  if (e != hipSuccess) return MOE_ERR_HIP;
+  return hip_status(moe::launch_gather_rows(x, row_token, offsets, (int)s->E, rmax_of(s, C),
+                                            s->d * elem_bytes(s), x_packed, stream));
+}
+
+int moe_expert_ffn(const moe_shape* s, const void* x_packed, const int32_t* offsets,
+                   const void* w_gate, const void* w_up, const void* w_down, void* y_packed,
+                   void* ws, size_t ws_bytes, hipStream_t stream) {
+  int v = validate(s);
+  if (v != MOE_OK) return v;
+  const bool tok = s->T > 0;  // row-sized buffers may be NULL when T == 0
+  if (!offsets || !w_gate || !w_up || !w_down || (tok && (!x_packed || !y_packed)))
+    return MOE_ERR_INVALID_ARG;
+  if (!aligned16(x_packed) || !aligned16(w_gate) || !aligned16(w_up) || !aligned16(w_down) ||
+      !aligned16(y_packed))
+    return MOE_ERR_INVALID_ARG;
+  v = check_ws(s, ws, ws_bytes);
+  if (v != MOE_OK) return v;
+  const Layout L = layout_of(s);
+  const int64_t Rmax = rmax_of(s, capacity_of(s));
+  moe::GemmPlan pl{s->dtype == MOE_DTYPE_BF16, offsets, (int)s->E, 0, (long)Rmax, (long)Rmax};
+  void* h = at<void>(ws, L.h);
+  hipError_t e = moe::launch_gemm_swiglu(pl, x_packed, nullptr, w_gate, w_up, (int)s->d_ff,
+                                         (int)s->d, h, stream);
+  if (e != hipSuccess) return MOE_ERR_HIP;
+  return hip_status(
+      moe::launch_gemm_down(pl, h, w_down, (int)s->d, (int)s->d_ff, y_packed, stream));
+}
+
+int moe_combine(const moe_shape* s, const void* y_packed, const int32_t* route_pos,
+                const float* gates, const void* y_shared, void* y, hipStream_t stream) {
+  int v = validate(s);
+  if (v != MOE_OK) return v;
+  if (s->T > 0 && (!y_packed || !route_pos || !gates || !y)) return MOE_ERR_INVALID_ARG;
+  if (!aligned16(y_packed) || !aligned16(y) || (y_shared && !aligned16(y_shared)))
+    return MOE_ERR_INVALID_ARG;
+  return hip_status(moe::launch_combine(s->dtype == MOE_DTYPE_BF16, y_packed, route_pos, gates,
+                                        y_shared, (int)s->T, (int)s->k, (int)s->d, y, stream));
+}
+
+static int layer_forward_impl(const moe_shape* s, const void* x, const void* w_router,
+                              const float* b_router, const void* w_gate, const void* w_up,
+                              const void* w_down, const void* ws_gate, const void* ws_up,
+                              const void* ws_down, void* y, int32_t* expert_ids, float* gates,
+                              int32_t* counts, int32_t* route_pos, void* ws, size_t ws_bytes,
+                              hipStream_t stream, hipEvent_t* ev) {
+  int v = validate(s);
+  if (v != MOE_OK) return v;
+  if (!w_router || !w_gate || !w_up || !w_down || (s->T > 0 && (!x || !y)))
+    return MOE_ERR_INVALID_ARG;
+  const bool shared = s->d_ff_shared > 0;
+  if (shared && (!ws_gate || !ws_up || !ws_down)) return MOE_ERR_INVALID_ARG;
+  if (!aligned16(x) || !aligned16(w_router) || !aligned16(w_gate) || !aligned16(w_up) ||
+      !aligned16(w_down) || !aligned16(y))
+    return MOE_ERR_INVALID_ARG;
+  if (shared && (!aligned16(ws_gate) || !aligned16(ws_up) || !aligned16(ws_down)))
+    return MOE_ERR_INVALID_ARG;
+  v = check_ws(s, ws, ws_bytes);
+  if (v != MOE_OK) return v;
+
+  const Layout L = layout_of(s);
+  const bool bf16 = s->dtype == MOE_DTYPE_BF16;
+  const int T = (int)s->T, d = (int)s->d, E = (int)s->E, k = (int)s->k, dff = (int)s->d_ff;
+  const int64_t C = capacity_of(s);
+  const int64_t Rmax = rmax_of(s, C);
+  int32_t* ids = expert_ids ? expert_ids : at<int32_t>(ws, L.ids);
+  float* g = gates ? gates : at<float>(ws, L.gates);
+  int32_t* cnts = counts ? counts : at<int32_t>(ws, L.counts);
+  int32_t* rpos = route_pos ? route_pos : at<int32_t>(ws, L.route_pos);
+  int32_t* offsets = at<int32_t>(ws, L.offsets);
+  int32_t* row_token = at<int32_t>(ws, L.row_token);
+  void* h = at<void>(ws, L.h);
+  void* yp = at<void>(ws, L.yp);
+
+  auto mark = [&](int i) {
+    if (ev && ev[i]) hipEventRecord(ev[i], stream);
+  };
+  mark(0);
+  hipError_t e = moe::launch_route(bf16, x, w_router, b_router, T, d, E, k, s->renormalize,
+                                   at<float>(ws, L.logits), ids, g, stream);
+  if (e != hipSuccess) return MOE_ERR_HIP;
+  mark(1);
+  e = moe::launch_permute_index(ids, T, k, E, (int)C, at<int32_t>(ws, L.cnt), cnts,
+                                at<int32_t>(ws, L.kept), offsets, rpos, row_token, stream);
+  if (e != hipSuccess) return MOE_ERR_HIP;
+  // each token picks an expert at most once, so no group exceeds min(T, C) rows
+  const long mcap = (C >= 0 && C < T) ? (long)C : (long)T;
+  moe::GemmPlan pl{bf16, offsets, E, 0, (long)Rmax, mcap};
+  mark(2);
+  e = moe::launch_gemm_swiglu(pl, x, row_token, w_gate, w_up, dff, d, h, stream);
+  if (e != hipSuccess) return MOE_ERR_HIP;
+  mark(3);
+  e = moe::launch_gemm_down(pl, h, w_down, d, dff, yp, stream);
+  if (e != hipSuccess) return MOE_ERR_HIP;
+  mark(4);
+  const void* ysh = nullptr;
+  if (shared) {
+    moe::GemmPlan ps{bf16, nullptr, 1, T, (long)T, (long)T};
+    void* hs = at<void>(ws, L.hs);
+    void* ys = at<void>(ws, L.ys);
+    e = moe::launch_gemm_swiglu(ps, x, nullptr, ws_gate, ws_up, (int)s->d_ff_shared, d, hs,
+                                stream);
+    if (e != hipSuccess) return MOE_ERR_HIP;
+    e = moe::launch_gemm_down(ps, hs, ws_down, d, (int)s->d_ff_shared, ys, stream);
+    if (e != hipSuccess) return MOE_ERR_HIP;
+    ysh = ys;
+  }
+  mark(5);
+  e = moe::launch_combine(bf16, yp, rpos, g, ysh, T, k, d, y, stream);
+  if (e != hipSuccess) return MOE_ERR_HIP;
+  mark(6);
+  return MOE_OK;
+}
+
+int moe_layer_forward(const moe_shape* s, const void* x, const void* w_router,
+                      const float* b_router, const void* w_gate, const void* w_up,
+                      const void* w_down, const void* ws_gate, const void* ws_up,
+                      const void* ws_down, void* y, int32_t* expert_ids, float* gates,
+                      int32_t* counts, int32_t* route_pos, void* ws, size_t ws_bytes,
+                      hipStream_t stream) {
+  return layer_forward_impl(s, x, w_router, b_router, w_gate, w_up, w_down, ws_gate, ws_up,
+                            ws_down, y, expert_ids, gates, counts, route_pos, ws, ws_bytes,
+                            stream, nullptr);
+}
+
+int moe_layer_forward_timed(const moe_shape* s, const void* x, const void* w_router,
+                            const float* b_router, const void* w_gate, const void* w_up,
+                            const void* w_down, const void* ws_gate, const void* ws_up,
+                            const void* ws_down, void* y, void* ws, size_t ws_bytes,
+                            hipStream_t stream, hipEvent_t* events) {
+  if (!events) return MOE_ERR_INVALID_ARG;
+  return layer_forward_impl(s, x, w_router, b_router, w_gate, w_up, w_down, ws_gate, ws_up,
+                            ws_down, y, nullptr, nullptr, nullptr, nullptr, ws, ws_bytes, stream,
+                            events);
+}
+
+}  // extern "C"

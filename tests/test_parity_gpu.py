@@ -1,0 +1,383 @@
+"""GPU parity of every C-ABI entry point against the CPU oracle.
+
+Integer outputs (expert ids, counts, offsets, route positions, row tokens,
+drop masks) and byte copies (packed rows) must match bit for bit; router
+logits too (both sides accumulate each dot product by sequential fp32
+fused multiply-add).  Floating outputs are held to 1e-4 absolute (fp32) or
+2e-2 relative (bf16).  Full-size workloads compare every routing output in
+full and the layer output on sampled tokens (first/last token, a seeded
+random set, and the owners of every expert's first and last packed row).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from tests._gpu import bits, check_y, host_inputs, sample_tokens, say, to_dev
+from workloads import WORKLOADS, Workload, make_inputs
+
+pytestmark = pytest.mark.gpu
+
+ALL = list(WORKLOADS)
+SMALL = ["tiny", "switch_phi1", "switch_phi125", "granite_1412"]
+
+
+@pytest.fixture(scope="module")
+def moe():
+    assert torch.cuda.is_available(), "GPU parity tests need a GPU"
+    import routing_dispatch_expert_route_amd as m
+    return m
+
+
+def _np(t):
+    return t.detach().cpu().numpy()
+
+
+def oracle_route(inp, w):
+    L = oracle.router_logits(inp["x"], inp["w_router"], inp["b_router"])
+    ids, gates = oracle.topk_gates(L, w.k, w.renorm)
+    return L, ids, gates
+
+
+# ------------------------------------------------------------------ route ---
+
+@pytest.mark.parametrize("name", ALL)
+def test_route_parity(moe, name):
+    w = WORKLOADS[name]
+    say(f"[route] {name}")
+    inp = host_inputs(name, routing_only=True)
+    dev = to_dev(inp)
+    s = moe.shape_of(w)
+    ids, gates, logits = moe.route(s, dev["x"], dev["w_router"], dev["b_router"], want_logits=True)
+    torch.cuda.synchronize()
+    L, oids, og = oracle_route(inp, w)
+    assert np.array_equal(bits(logits), L.view(np.int32)), "logits differ"
+    assert np.array_equal(_np(ids), oids)
+    assert np.max(np.abs(_np(gates) - og)) <= 1e-6
+    if w.renorm:
+        assert np.max(np.abs(_np(gates).astype(np.float64).sum(-1) - 1.0)) <= 1e-6
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_route_worked_example(moe, dtype):
+    """Router logits [2.1, 1.8, 0.2] -> softmax [0.529, 0.392, 0.079], top-2
+    renormalised [0.574, 0.426] ("Session 19", worked case)."""
+    say(f"[route worked] {dtype}")
+    dt = torch.float32 if dtype == "f32" else torch.bfloat16
+    x = torch.zeros(2, 8, dtype=dt)
+    x[0, 0] = x[1, 1] = 1.0
+    wr = torch.zeros(3, 8, dtype=dt)
+    wr[:, 0] = torch.tensor([2.1, 1.8, 0.2])
+    wr[:, 1] = torch.tensor([2.1, 1.8, 1.9])
+    s3 = moe.shape(2, 8, 3, 3, 8, dtype=dtype, renorm=0)
+    ids, g, _ = moe.route(s3, x.cuda(), wr.cuda())
+    gl = _np(g)
+    assert _np(ids)[0].tolist() == [0, 1, 2] and _np(ids)[1].tolist() == [0, 2, 1]
+    tol = 5e-4 if dtype == "f32" else 5e-3   # bf16 stores 2.1 as 2.09375
+    assert np.allclose(gl[0], [0.529, 0.392, 0.079], atol=tol)
+    assert np.allclose(gl[1], [0.391, 0.320, 0.289], atol=tol)
+    s2 = moe.shape(2, 8, 3, 2, 8, dtype=dtype, renorm=1)
+    ids2, g2, _ = moe.route(s2, x.cuda(), wr.cuda())
+    assert np.allclose(_np(g2)[0], [0.574, 0.426], atol=tol)
+    assert sorted(_np(ids2)[1].tolist()) == [0, 2]
+
+
+def test_route_ties_take_lowest_index(moe):
+    say("[route ties]")
+    w = Workload("ties", T=300, E=16, k=5, d=64, d_ff=8, dtype="bf16")
+    g = torch.Generator().manual_seed(3)
+    x = torch.randint(-1, 2, (w.T, w.d), generator=g).to(torch.bfloat16)
+    wr = torch.randint(-1, 2, (w.E, w.d), generator=g).to(torch.bfloat16)
+    ids, gates, logits = moe.route(moe.shape_of(w), x.cuda(), wr.cuda(), want_logits=True)
+    L = oracle.router_logits(x, wr)
+    oids, og = oracle.topk_gates(L, w.k, 1)
+    assert np.array_equal(_np(logits), L)
+    assert np.array_equal(_np(ids), oids)
+    for t in range(w.T):  # integer logits: many exact ties
+        assert oids[t].tolist() == np.lexsort((np.arange(w.E), -L[t]))[:w.k].tolist()
+    z = moe.route(moe.shape(5, 64, 8, 3, 8), torch.zeros(5, 64, dtype=torch.bfloat16).cuda(),
+                  torch.zeros(8, 64, dtype=torch.bfloat16).cuda())[0]
+    assert np.all(_np(z) == np.arange(3))
+
+
+# ---------------------------------------------------------------- permute ---
+
+PERMUTE_CASES = ALL + ["e256_k8", "ragged_cap"]
+
+
+def _permute_case(name):
+    if name == "e256_k8":
+        return Workload(name, T=777, E=256, k=8, d=72, d_ff=40, phi=1.0)
+    if name == "ragged_cap":
+        return Workload(name, T=1001, E=7, k=3, d=24, d_ff=16, phi=0.6, bias="normal")
+    return WORKLOADS[name]
+
+
+@pytest.mark.parametrize("name", PERMUTE_CASES)
+def test_permute_parity(moe, name):
+    w = _permute_case(name)
+    say(f"[permute] {name}")
+    inp = host_inputs(name, routing_only=True) if name in WORKLOADS else \
+        make_inputs(w, seed=1, routing_only=True)
+    _, oids, _ = oracle_route(inp, w)
+    C = oracle.capacity(w.T, w.E, w.k, w.phi)
+    ref = oracle.dispatch(oids, w.E, C)
+    s = moe.shape_of(w)
+    out = moe.permute(s, inp["x"].cuda(), torch.from_numpy(oids).cuda())
+    torch.cuda.synchronize()
+    assert np.array_equal(_np(out["counts"]), ref["counts"])
+    assert np.array_equal(_np(out["kept_counts"]), ref["kept"])
+    assert np.array_equal(_np(out["offsets"]), ref["offsets"])
+    assert np.array_equal(_np(out["route_pos"]), ref["route_pos"])
+    n = int(ref["offsets"][-1])
+    assert np.array_equal(_np(out["row_token"])[:n], ref["row_token"])
+    packed = oracle.gather_rows(inp["x"], ref["row_token"])
+    assert np.array_equal(bits(out["x_packed"][:n]), packed.view(bits(out["x_packed"][:1]).dtype))
+    assert int(ref["counts"].sum()) == w.T * w.k
+
+
+def test_permute_capacity_trace(moe):
+    """The "Session 19" trace: C = 5, E1 demand 6, t6 dropped; slot table."""
+    say("[permute trace]")
+    assign = np.array([[0, 1], [0, 2], [0, 1], [0, 3], [0, 2], [0, 1], [1, 3], [2, 3]], np.int32)
+    x = torch.arange(8 * 8, dtype=torch.float32).reshape(8, 8)
+    for phi, C, drops in ((1.25, 5, [10]), (1.0, 4, [8, 10]), (2.0, 8, []), (1.5, 6, [])):
+        s = moe.shape(8, 8, 4, 2, 8, dtype="f32", phi=phi)
+        assert moe.capacity(s)[0] == C
+        out = moe.permute(s, x.cuda(), torch.from_numpy(assign).cuda())
+        rp = _np(out["route_pos"]).reshape(-1)
+        assert np.flatnonzero(rp < 0).tolist() == drops
+        assert _np(out["counts"]).tolist() == [6, 4, 3, 3]
+        if phi == 1.25:
+            off = _np(out["offsets"])
+            rt = _np(out["row_token"])
+            assert rt[off[0]:off[1]].tolist() == [0, 1, 2, 3, 4]
+            assert rt[off[1]:off[2]].tolist() == [0, 2, 5, 6]
+            assert rt[off[2]:off[3]].tolist() == [1, 4, 7]
+            assert rt[off[3]:off[4]].tolist() == [3, 6, 7]
+
+
+def test_permute_out_of_range_ids_are_dropped(moe):
+    say("[permute bad ids]")
+    ids = torch.tensor([[0, 1], [9, 2], [-3, 1], [3, 0]], dtype=torch.int32)
+    s = moe.shape(4, 8, 4, 2, 8, dtype="f32")
+    out = moe.permute(s, torch.ones(4, 8).cuda(), ids.cuda())
+    assert _np(out["counts"]).tolist() == [2, 2, 1, 1]
+    rp = _np(out["route_pos"])
+    assert rp[1, 0] == -1 and rp[2, 0] == -1 and np.all(rp[[0, 3]] >= 0)
+
+
+# ---------------------------------------------------------------- combine ---
+
+@pytest.mark.parametrize("dtype,k", [("f32", 1), ("f32", 2), ("bf16", 1), ("bf16", 2),
+                                     ("bf16", 4), ("bf16", 8)])
+def test_combine_round_trip_exact(moe, dtype, k):
+    """permute then combine with gates 1/k returns x bit for bit ("271,104
+    Routes", section 3: restored rows equal x[token_ids])."""
+    say(f"[combine round trip] {dtype} k={k}")
+    w = Workload("rt", T=333, E=16, k=k, d=200, d_ff=8, dtype=dtype)
+    inp = make_inputs(w, seed=4, routing_only=True)
+    s = moe.shape_of(w)
+    x = inp["x"].cuda()
+    ids, _, _ = moe.route(s, x, inp["w_router"].cuda())
+    out = moe.permute(s, x, ids)
+    gates = torch.full((w.T, k), 1.0 / k, dtype=torch.float32, device="cuda")
+    y = moe.combine(s, out["x_packed"], out["route_pos"], gates)
+    assert np.array_equal(bits(y), bits(inp["x"]))
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_combine_parity_with_drops_and_shared(moe, dtype):
+    say(f"[combine parity] {dtype}")
+    w = Workload("cmb", T=500, E=8, k=3, d=136, d_ff=8, dtype=dtype, phi=0.7, bias="normal")
+    inp = make_inputs(w, seed=5, routing_only=True)
+    s = moe.shape_of(w)
+    _, oids, og = oracle_route(inp, w)
+    ref = oracle.dispatch(oids, w.E, oracle.capacity(w.T, w.E, w.k, w.phi))
+    assert np.any(ref["route_pos"] < 0)
+    g = torch.Generator().manual_seed(6)
+    n = int(ref["offsets"][-1])
+    yp = torch.randn(n, w.d, generator=g).to(w.torch_dtype)
+    ysh = torch.randn(w.T, w.d, generator=g).to(w.torch_dtype)
+    y = moe.combine(s, yp.cuda(), torch.from_numpy(ref["route_pos"]).cuda(),
+                    torch.from_numpy(og).cuda(), ysh.cuda())
+    yref = oracle.combine(yp, ref["route_pos"], og, ysh)
+    check_y(y, yref, dtype, "combine")
+    if dtype == "bf16":  # one rounding of an fp32 sum: within 2 bf16 ulps
+        assert np.max(np.abs(_np(y.float()) - yref) / (np.abs(yref) + 1e-3)) < 2 ** -7
+
+
+# ------------------------------------------------------------- expert FFN ---
+
+FFN_CASES = SMALL + ["ragged_ffn", "single_row_experts", "mixtral_decode", "shared64"]
+
+
+def _ffn_case(name):
+    if name == "ragged_ffn":
+        return Workload(name, T=301, E=5, k=2, d=200, d_ff=72, phi=0.0, bias="normal")
+    if name == "single_row_experts":
+        return Workload(name, T=5, E=8, k=1, d=64, d_ff=96)
+    return WORKLOADS[name]
+
+
+@pytest.mark.parametrize("name", FFN_CASES)
+def test_expert_ffn_parity(moe, name):
+    w = _ffn_case(name)
+    say(f"[expert_ffn] {name}")
+    inp = host_inputs(name) if name in WORKLOADS else make_inputs(w, seed=2)
+    _, oids, _ = oracle_route(inp, w)
+    ref = oracle.dispatch(oids, w.E, oracle.capacity(w.T, w.E, w.k, w.phi))
+    packed = oracle.gather_rows(inp["x"], ref["row_token"])
+    n = int(ref["offsets"][-1])
+    s = moe.shape_of(w)
+    _, R_max = moe.capacity(s)
+    xp = torch.zeros(max(R_max, 1), w.d, dtype=w.torch_dtype)
+    xp[:n] = inp["x"][torch.from_numpy(ref["row_token"]).long()]
+    assert np.array_equal(bits(xp[:n]), packed.view(bits(xp[:1]).dtype))
+    d = to_dev(inp)
+    yp = moe.expert_ffn(s, xp.cuda(), torch.from_numpy(ref["offsets"]).cuda(), d["w_gate"],
+                        d["w_up"], d["w_down"])
+    torch.cuda.synchronize()
+    offs = ref["offsets"]
+    if n <= 2048:
+        rows = np.arange(n)
+    else:
+        rng = np.random.default_rng(0)
+        rows = set(rng.choice(n, 256, replace=False).tolist())
+        for e in range(w.E):
+            if offs[e + 1] > offs[e]:
+                rows.update([int(offs[e]), int(offs[e + 1] - 1)])
+        rows = np.array(sorted(rows))
+    yref = np.empty((len(rows), w.d))
+    for e in range(w.E):
+        m = (rows >= offs[e]) & (rows < offs[e + 1])
+        if m.any():
+            yref[m] = oracle.swiglu_rows(xp[torch.from_numpy(rows[m]).long()], inp["w_gate"][e],
+                                         inp["w_up"][e],
+                                         inp["w_down"][e])
+    check_y(yp[torch.from_numpy(rows).long().cuda()], yref, w.dtype, "y_packed")
+
+
+def test_expert_ffn_dense_group(moe):
+    """A dense SwiGLU MLP is the E = 1 case with offsets {0, T} (the shared
+    expert's form); checked against torch fp64 matmuls."""
+    say("[expert_ffn dense]")
+    w = Workload("dense", T=257, E=1, k=1, d=256, d_ff=384)
+    inp = make_inputs(w, seed=7)
+    s = moe.shape_of(w)
+    d = to_dev(inp)
+    yp = moe.expert_ffn(s, d["x"], torch.tensor([0, w.T], dtype=torch.int32).cuda(), d["w_gate"],
+                        d["w_up"], d["w_down"])
+    X = inp["x"].double()
+    ref = (torch.nn.functional.silu(X @ inp["w_gate"][0].double().T) *
+           (X @ inp["w_up"][0].double().T)) @ inp["w_down"][0].double().T
+    check_y(yp, ref.numpy(), "bf16", "dense")
+
+
+# ------------------------------------------------------------ whole layer ---
+
+def _layer_check(moe, w, inp, seed=0, n_random=96):
+    d = to_dev(inp)
+    s = moe.shape_of(w)
+    y, rt = moe.layer_forward(s, d["x"], d["w_router"], d["b_router"], d["w_gate"], d["w_up"],
+                              d["w_down"], d["ws_gate"], d["ws_up"], d["ws_down"],
+                              return_routing=True)
+    torch.cuda.synchronize()
+    _, oids, og = oracle_route(inp, w)
+    C = oracle.capacity(w.T, w.E, w.k, w.phi)
+    disp = oracle.dispatch(oids, w.E, C)
+    assert np.array_equal(_np(rt["expert_ids"]), oids)
+    assert np.max(np.abs(_np(rt["gates"]) - og), initial=0.0) <= 1e-6
+    assert np.array_equal(_np(rt["counts"]), disp["counts"])
+    assert np.array_equal(_np(rt["route_pos"]), disp["route_pos"])
+    if w.T == 0:
+        return y
+    sel = None
+    if w.T > 256:
+        sel = sample_tokens(w.T, disp["route_pos"], disp["offsets"], disp["row_token"],
+                            n_random=n_random, seed=seed)
+    ref = oracle.layer_forward(inp["x"], inp["w_router"], inp["b_router"], inp["w_gate"],
+                               inp["w_up"], inp["w_down"], w.k, w.renorm, w.phi,
+                               inp["ws_gate"], inp["ws_up"], inp["ws_down"], sel=sel)
+    got = y if sel is None else y[torch.from_numpy(sel).long().cuda()]
+    errs = check_y(got, ref["y"], w.dtype, f"layer {w.name}")
+    say(f"   {w.name}: err {errs[0]:.3e} / {errs[1]:.3e}, kept {int(disp['kept'].sum())}"
+        f" of {w.T * w.k} routes")
+    return y
+
+
+@pytest.mark.parametrize("name", ALL)
+def test_layer_forward_parity(moe, name):
+    w = WORKLOADS[name]
+    say(f"[layer] {name}")
+    _layer_check(moe, w, host_inputs(name))
+
+
+EDGE = {
+    "empty": Workload("empty", T=0, E=4, k=2, d=64, d_ff=64),
+    "one_token": Workload("one_token", T=1, E=8, k=2, d=64, d_ff=64),
+    "ragged_tails": Workload("ragged_tails", T=515, E=6, k=2, d=72, d_ff=40, bias="normal"),
+    "e256_k8": Workload("e256_k8", T=300, E=256, k=8, d=64, d_ff=32),
+    "cap_one": Workload("cap_one", T=64, E=16, k=2, d=64, d_ff=64, phi=0.01),
+    "k_equals_E": Workload("k_equals_E", T=100, E=4, k=4, d=64, d_ff=64),
+    "f32_ragged": Workload("f32_ragged", T=77, E=5, k=3, d=40, d_ff=24, dtype="f32",
+                           phi=0.8, bias="normal"),
+    "shared_small": Workload("shared_small", T=130, E=4, k=1, d=128, d_ff=64, d_ff_shared=96,
+                             renorm=0, phi=1.0, bias="zipf"),
+}
+
+
+@pytest.mark.parametrize("name", list(EDGE))
+def test_layer_forward_edge_cases(moe, name):
+    w = EDGE[name]
+    say(f"[layer edge] {name}")
+    _layer_check(moe, w, make_inputs(w, seed=11))
+
+
+def test_forced_hot_expert_reaches_E_over_k(moe):
+    say("[layer hot expert]")
+    w = Workload("hot", T=512, E=32, k=8, d=64, d_ff=32, bias="normal")
+    inp = make_inputs(w, seed=12)
+    inp["b_router"] = torch.zeros(32)
+    inp["b_router"][5] = 1e3
+    _layer_check(moe, w, inp)
+    s = moe.shape_of(w)
+    d = to_dev(inp)
+    _, rt = moe.layer_forward(s, d["x"], d["w_router"], d["b_router"], d["w_gate"], d["w_up"],
+                              d["w_down"], return_routing=True)
+    c = _np(rt["counts"]).astype(np.float64)
+    assert c[5] == w.T and c.max() / c.mean() == w.E / w.k
+
+
+def test_layer_forward_deterministic(moe):
+    say("[layer determinism]")
+    w = WORKLOADS["granite_1412"]
+    d = to_dev(host_inputs("granite_1412"))
+    s = moe.shape_of(w)
+    runs = []
+    for _ in range(2):
+        y, rt = moe.layer_forward(s, d["x"], d["w_router"], d["b_router"], d["w_gate"], d["w_up"],
+                                  d["w_down"], return_routing=True)
+        runs.append((bits(y), {k_: _np(v) for k_, v in rt.items()}))
+    assert np.array_equal(runs[0][0], runs[1][0])
+    for k_ in runs[0][1]:
+        assert np.array_equal(runs[0][1][k_], runs[1][1][k_])
+
+
+def test_layer_dropped_route_keeps_only_other_gate(moe):
+    """"Session 19" trace through the whole layer: t6 (logits equal to t1's)
+    loses E1 at C = 5 and keeps 0.426 times E2's output."""
+    say("[layer trace t6]")
+    assign = [[0, 1], [0, 2], [0, 1], [0, 3], [0, 2], [0, 1], [1, 3], [2, 3]]
+    w = Workload("trace", T=8, E=4, k=2, d=16, d_ff=24, dtype="f32", phi=1.25)
+    inp = make_inputs(w, seed=13)
+    x = torch.zeros(8, 16)
+    x[torch.arange(8), torch.arange(8)] = 1.0
+    wr = torch.full((4, 16), 0.0)
+    wr[:, :8] = 0.2
+    for t, (a, b) in enumerate(assign):
+        wr[a, t], wr[b, t] = 2.1, 1.8
+    inp["x"], inp["w_router"] = x, wr
+    y = _layer_check(moe, w, inp)
+    e2 = oracle.swiglu_rows(x[5:6], inp["w_gate"][1], inp["w_up"][1], inp["w_down"][1])[0]
+    assert np.allclose(_np(y[5]), 0.4256 * e2, rtol=2e-3, atol=1e-6)

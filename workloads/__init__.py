@@ -70,11 +70,14 @@ WORKLOADS = {
 }
 
 
-def make_inputs(w: Workload, seed: int = 0, device: str = "cpu", zero_routed: bool = False):
+def make_inputs(w: Workload, seed: int = 0, device: str = "cpu", zero_routed: bool = False,
+                routing_only: bool = False):
     """Draw the workload's inputs on the CPU (then move them to `device`).
 
     Returns a dict with x, w_router, b_router (or None), w_gate, w_up,
     w_down, ws_gate, ws_up, ws_down (None without a shared expert).
+    routing_only stops after the router tensors (the same x, W_router and
+    bias as a full draw, since those come first); expert weights are None.
     """
     g = torch.Generator(device="cpu")
     g.manual_seed(seed)
@@ -95,6 +98,12 @@ def make_inputs(w: Workload, seed: int = 0, device: str = "cpu", zero_routed: bo
     elif w.bias == "zipf":
         # log-prior proportional to 1/rank: expert 0 most popular
         b_router = -torch.log(torch.arange(1, w.E + 1, dtype=torch.float64)).to(torch.float32)
+    if routing_only:
+        out = dict(x=x, w_router=w_router, b_router=b_router, w_gate=None, w_up=None,
+                   w_down=None, ws_gate=None, ws_up=None, ws_down=None)
+        if device != "cpu":
+            out = {k_: (None if v is None else v.to(device)) for k_, v in out.items()}
+        return out
     w_gate = torch.empty(w.E, w.d_ff, w.d, dtype=dt)
     w_up = torch.empty(w.E, w.d_ff, w.d, dtype=dt)
     w_down = torch.empty(w.E, w.d, w.d_ff, dtype=dt)
