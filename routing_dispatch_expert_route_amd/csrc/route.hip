@@ -126,16 +126,16 @@ __global__ __launch_bounds__(64) void topk_gates_kernel(const float* __restrict_
   for (int e = 0; e < E; ++e) {
     float cv = row[e];
     int ci = e;
+    // branch-free insertion: the displaced entry moves one slot down
 #pragma unroll
     for (int j = 0; j < KMAX; ++j) {
-      if (j < k && (j >= filled || precedes(cv, ci, bv[j], bi[j]))) {
-        float tv = bv[j];
-        int ti = bi[j];
-        bv[j] = cv;
-        bi[j] = ci;
-        cv = tv;
-        ci = ti;
-      }
+      const bool take = (j < k) & ((j >= filled) | precedes(cv, ci, bv[j], bi[j]));
+      const float ov = bv[j];
+      const int oi = bi[j];
+      bv[j] = take ? cv : ov;
+      bi[j] = take ? ci : oi;
+      cv = take ? ov : cv;
+      ci = take ? oi : ci;
     }
     filled = filled < k ? filled + 1 : k;
   }
