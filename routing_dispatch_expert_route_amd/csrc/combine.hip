@@ -6,26 +6,73 @@
 // shared expert is added outside the gate normalisation; the full trace: a
 // dropped route contributes nothing and the kept gates stay as they are.
 //
-// One wave per token; each lane owns 16-byte column chunks.  The k rows of a
-// token are gathered with vector loads, summed in fp32 in slot order j = 0..k-1
-// (fused multiply-add by the gate), the shared row added last, and the sum
-// rounded once to the output type.  No atomics: the order is fixed.
+// One wave per token; each lane owns chunks of 8 (bf16) or 4 (fp32) output
+// columns.  The k rows of a token are gathered with vector loads, summed in
+// fp32 in slot order j = 0..k-1 (fused multiply-add by the gate), the shared
+// row added last, and the sum rounded once to the output type.  When the
+// down GEMM split K, a row is first the sum of its fp32 partial planes in
+// plane order.  No atomics: every order is fixed.
 #include "common.h"
 #include "launch.h"
 
 namespace moe {
 
+// Load G consecutive values of row p starting at column col as fp32.
+template <bool BF16, bool PARTIAL, int G>
+__device__ __forceinline__ void load_row(const void* yp, int splits, long stride, size_t p,
+                                         int d, int col, float* v) {
+  if constexpr (PARTIAL) {
+    const float* P = reinterpret_cast<const float*>(yp) + p * d + col;
+#pragma unroll
+    for (int q = 0; q < G; q += 4) {
+      f32x4_t s4 = *reinterpret_cast<const f32x4_t*>(P + q);
+      for (int s = 1; s < splits; ++s) {
+        const f32x4_t t4 = *reinterpret_cast<const f32x4_t*>(P + (size_t)s * stride + q);
+        s4 += t4;
+      }
+#pragma unroll
+      for (int t = 0; t < 4; ++t) v[q + t] = s4[t];
+    }
+  } else if constexpr (BF16) {
+    const u32x4_t u = *reinterpret_cast<const u32x4_t*>(reinterpret_cast<const bf16_t*>(yp) +
+                                                       p * d + col);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      v[2 * q] = bf16lo(u[q]);
+      v[2 * q + 1] = bf16hi(u[q]);
+    }
+  } else {
+    const f32x4_t u = *reinterpret_cast<const f32x4_t*>(reinterpret_cast<const float*>(yp) +
+                                                       p * d + col);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) v[q] = u[q];
+  }
+}
+
 template <bool BF16>
-__global__ __launch_bounds__(256) void combine_kernel(const void* __restrict__ yp,
+__device__ __forceinline__ void store_out(void* y, size_t idx, const float* acc) {
+  if constexpr (BF16) {
+    u32x4_t o;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) o[q] = pack_bf16x2(acc[2 * q], acc[2 * q + 1]);
+    *reinterpret_cast<u32x4_t*>(reinterpret_cast<bf16_t*>(y) + idx) = o;
+  } else {
+    f32x4_t o = {acc[0], acc[1], acc[2], acc[3]};
+    *reinterpret_cast<f32x4_t*>(reinterpret_cast<float*>(y) + idx) = o;
+  }
+}
+
+template <bool BF16, bool PARTIAL>
+__global__ __launch_bounds__(256) void combine_kernel(const void* __restrict__ yp, int splits,
+                                                      long split_stride,
                                                       const int32_t* __restrict__ route_pos,
                                                       const float* __restrict__ gates,
                                                       const void* __restrict__ ysh, int T, int k,
                                                       int d, void* __restrict__ y) {
-  constexpr int G = BF16 ? 8 : 4;  // elements per 16-byte chunk
+  constexpr int G = BF16 ? 8 : 4;  // output elements per 16-byte chunk
   const int lane = threadIdx.x & 63;
   const int t = blockIdx.x * (blockDim.x / 64) + (threadIdx.x >> 6);
   if (t >= T) return;
-  const int nch = d / G;
   int pos[8];
   float g[8];
 #pragma unroll
@@ -33,64 +80,82 @@ __global__ __launch_bounds__(256) void combine_kernel(const void* __restrict__ y
     pos[j] = j < k ? route_pos[(size_t)t * k + j] : -1;
     g[j] = j < k ? gates[(size_t)t * k + j] : 0.0f;
   }
-  const u32x4_t* Y = reinterpret_cast<const u32x4_t*>(yp);
-  const u32x4_t* S = reinterpret_cast<const u32x4_t*>(ysh);
-  u32x4_t* O = reinterpret_cast<u32x4_t*>(y);
-  for (int c = lane; c < nch; c += 64) {
+  for (int col = lane * G; col < d; col += 64 * G) {
     float acc[G];
 #pragma unroll
     for (int q = 0; q < G; ++q) acc[q] = 0.0f;
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       if (pos[j] < 0) continue;
-      const u32x4_t v = Y[(size_t)pos[j] * nch + c];
-      if constexpr (BF16) {
+      float v[G];
+      load_row<BF16, PARTIAL, G>(yp, splits, split_stride, (size_t)pos[j], d, col, v);
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          acc[2 * q] = __builtin_fmaf(g[j], bf16lo(v[q]), acc[2 * q]);
-          acc[2 * q + 1] = __builtin_fmaf(g[j], bf16hi(v[q]), acc[2 * q + 1]);
-        }
-      } else {
-#pragma unroll
-        for (int q = 0; q < 4; ++q) acc[q] = __builtin_fmaf(g[j], __uint_as_float(v[q]), acc[q]);
-      }
+      for (int q = 0; q < G; ++q) acc[q] = __builtin_fmaf(g[j], v[q], acc[q]);
     }
     if (ysh) {
-      const u32x4_t v = S[(size_t)t * nch + c];
-      if constexpr (BF16) {
+      float v[G];
+      load_row<BF16, false, G>(ysh, 1, 0, (size_t)t, d, col, v);
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          acc[2 * q] += bf16lo(v[q]);
-          acc[2 * q + 1] += bf16hi(v[q]);
-        }
-      } else {
-#pragma unroll
-        for (int q = 0; q < 4; ++q) acc[q] += __uint_as_float(v[q]);
-      }
+      for (int q = 0; q < G; ++q) acc[q] += v[q];
     }
-    u32x4_t o;
-    if constexpr (BF16) {
-#pragma unroll
-      for (int q = 0; q < 4; ++q) o[q] = pack_bf16x2(acc[2 * q], acc[2 * q + 1]);
-    } else {
-#pragma unroll
-      for (int q = 0; q < 4; ++q) o[q] = __float_as_uint(acc[q]);
-    }
-    O[(size_t)t * nch + c] = o;
+    store_out<BF16>(y, (size_t)t * d + col, acc);
   }
 }
 
-hipError_t launch_combine(bool bf16, const void* y_packed, const int32_t* route_pos,
-                          const float* gates, const void* y_shared, int T, int k, int d, void* y,
-                          hipStream_t st) {
+// y[p][:] = sum_s parts[s][p][:] for the valid rows, rounded once.
+template <bool BF16>
+__global__ __launch_bounds__(256) void reduce_splits_kernel(const float* __restrict__ parts,
+                                                            int splits, long stride,
+                                                            const int32_t* __restrict__ offsets,
+                                                            int E, long R_max, int N,
+                                                            void* __restrict__ y) {
+  constexpr int G = BF16 ? 8 : 4;
+  const long rows = offsets ? (long)offsets[E] : R_max;
+  const long per_row = N / G;
+  const long total = (rows < R_max ? rows : R_max) * per_row;
+  for (long g = (long)blockIdx.x * blockDim.x + threadIdx.x; g < total;
+       g += (long)gridDim.x * blockDim.x) {
+    const long p = g / per_row;
+    const int col = (int)(g - p * per_row) * G;
+    float v[G];
+    load_row<BF16, true, G>(parts, splits, stride, (size_t)p, N, col, v);
+    store_out<BF16>(y, (size_t)p * N + col, v);
+  }
+}
+
+hipError_t launch_combine(bool bf16, const void* y_packed, int splits, long split_stride,
+                          const int32_t* route_pos, const float* gates, const void* y_shared,
+                          int T, int k, int d, void* y, hipStream_t st) {
   if (T == 0) return hipSuccess;
   dim3 grid(ceil_div(T, 4)), block(256);
+  const bool part = splits > 1;
+#define CB(B, P)                                                                           \
+  hipLaunchKernelGGL((combine_kernel<B, P>), grid, block, 0, st, y_packed, splits, split_stride, \
+                     route_pos, gates, y_shared, T, k, d, y)
+  if (bf16) {
+    if (part) CB(true, true);
+    else CB(true, false);
+  } else {
+    if (part) CB(false, true);
+    else CB(false, false);
+  }
+#undef CB
+  return hipGetLastError();
+}
+
+hipError_t launch_reduce_splits(bool bf16, const float* parts, int splits, long split_stride,
+                                const int32_t* offsets, int E, long R_max, int N, void* y,
+                                hipStream_t st) {
+  const long total = R_max * (N / (bf16 ? 8 : 4));
+  if (total == 0) return hipSuccess;
+  long blocks = (total + 255) / 256;
+  if (blocks > 4096) blocks = 4096;
   if (bf16)
-    hipLaunchKernelGGL(combine_kernel<true>, grid, block, 0, st, y_packed, route_pos, gates,
-                       y_shared, T, k, d, y);
+    hipLaunchKernelGGL(reduce_splits_kernel<true>, dim3((unsigned)blocks), dim3(256), 0, st, parts,
+                       splits, split_stride, offsets, E, R_max, N, y);
   else
-    hipLaunchKernelGGL(combine_kernel<false>, grid, block, 0, st, y_packed, route_pos, gates,
-                       y_shared, T, k, d, y);
+    hipLaunchKernelGGL(reduce_splits_kernel<false>, dim3((unsigned)blocks), dim3(256), 0, st,
+                       parts, splits, split_stride, offsets, E, R_max, N, y);
   return hipGetLastError();
 }
 

@@ -33,12 +33,16 @@ struct GemmArgs {
   const void* B1;  // up weights [E][N][K] (SwiGLU only)
   int N;
   int K;
-  void* C;  // [rows][N]
-  int n_tiles;
+  void* C;            // [rows][N] in dtype, or fp32 partial planes [splits][R_max][N]
+  long split_stride;  // elements between partial planes
+  int n_tiles;        // column tiles
+  int m_tiles;        // row tiles (an upper bound; tiles past the last group exit)
+  int splits;         // K splits (partial-plane output when > 1)
+  int k_chunk;        // K elements per split, a multiple of 64
 };
 
 // Find the (expert, first row, row count) of row-tile mt.  Executed by one
-// wave; lane 0 of the finding lane group writes the result to info[0..2]
+// wave; the lane that owns the tile writes the result to info[0..2]
 // (info[0] stays -1 when mt is past the last tile).
 template <int BM>
 __device__ __forceinline__ void find_row_tile(const GemmArgs& a, int mt, int lane, int* info) {
@@ -82,35 +86,80 @@ __device__ __forceinline__ void find_row_tile(const GemmArgs& a, int mt, int lan
   }
 }
 
-// ---------------------------------------------------------------------------
-// bf16 MFMA kernel.  256 threads = WGM x WGN waves; block tile BM x BNO
-// outputs; BK = 64 per LDS stage, two stages.  LDS rows hold 8 chunks of 16
-// bytes; chunk c of row r is stored at c ^ (r & 7) so that the 8 lanes that
-// read one column chunk of 8 consecutive rows hit 8 different bank groups.
-// ---------------------------------------------------------------------------
-template <int BM, int BNO, int WGM, int WGN, bool SWIGLU, bool GATHER>
-__global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmArgs a) {
-  constexpr int BK = 64;
-  constexpr int CH = BK / 8;  // 16-byte chunks per LDS row
-  constexpr int NREG = SWIGLU ? 2 : 1;
-  constexpr int BNB = BNO * NREG;  // weight rows in the B tile
-  constexpr int WTM = BM / WGM, WTN = BNO / WGN;
-  constexpr int TM = WTM / 32, TN = WTN / 32;
-  constexpr int A_LD = BM * CH / 256;   // A chunks per thread per stage
-  constexpr int B_LD = BNB * CH / 256;  // B chunks per thread per stage
-  static_assert(WGM * WGN == 4, "four waves");
-  static_assert(TM >= 1 && TN >= 1 && A_LD >= 1 && B_LD >= 1, "tile shape");
+// Block -> (row tile, column tile, K split).  Workgroups are dispatched
+// round-robin over the 8 XCDs (each with its own L2), so consecutive logical
+// tiles are first gathered per XCD; tiles are then walked in groups of
+// GM row tiles, column tile slowest inside a group, so the workgroups that
+// run together on one XCD share both their weight and activation tiles.
+__device__ __forceinline__ void tile_of_block(const GemmArgs& a, int& mt, int& nt, int& ks) {
+  constexpr int NXCD = 8, GM = 8;
+  const int nb = gridDim.x, bid = blockIdx.x;
+  const int xcd = bid % NXCD, local = bid / NXCD;
+  const int per = nb / NXCD, rem = nb % NXCD;
+  int l = (xcd < rem ? xcd * (per + 1) : rem * (per + 1) + (xcd - rem) * per) + local;
+  const int tiles = a.m_tiles * a.n_tiles;
+  ks = l / tiles;
+  l -= ks * tiles;
+  const int group = l / (GM * a.n_tiles);
+  const int first = group * GM;
+  const int gsize = min(GM, a.m_tiles - first);
+  const int within = l - group * GM * a.n_tiles;
+  mt = first + within % gsize;
+  nt = within / gsize;
+}
 
-  __shared__ __attribute__((aligned(16))) u32x4_t sA[2][BM * CH];
-  __shared__ __attribute__((aligned(16))) u32x4_t sB[2][BNB * CH];
+// ---------------------------------------------------------------------------
+// bf16 MFMA kernel, NT threads = WM x WN waves (NT = 256 or 512).
+//
+// Operand roles.  The MFMA A operand is the weight tile (rows n), the B
+// operand the activation tile (rows m), so the accumulator holds D[n][m]:
+// lane l of a 32x32 tile owns column m = l%32 and rows n = 8*(v/4) +
+// 4*(l/32) + v%4 -- four consecutive output columns of one token row per
+// group of four accumulator registers, written as one 8-byte store.
+//
+// Pipeline.  K advances in stages of BK = 64 through two LDS buffers.  Each
+// thread stages its share of a stage in registers; with two register sets
+// the loads of stage t+2 are in flight while stage t feeds the MFMAs and
+// stage t+1 waits in the other set.  With 512 threads (two waves per SIMD)
+// one wave's MFMAs run while the other waits on LDS or memory.
+//
+// LDS layout.  A row holds 8 chunks of 16 bytes; logical chunk c of row r
+// sits at c ^ f(r), f(r) = (r & 7) ^ ((r >> 3) & 1): the 8 or 16 lanes that
+// read one chunk column of consecutive rows visit distinct bank groups
+// whether the LDS has 32 or 64 four-byte banks.
+//
+// SWIGLU: the weight tile stacks BNW/2 gate rows over the matching BNW/2 up
+// rows; the epilogue writes SiLU(gate) * up.  PARTIAL: fp32 output into the
+// K split's partial plane (summed later in a fixed order).
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ int swz(int r) { return (r & 7) ^ ((r >> 3) & 1); }
+
+template <int BM, int BNW, int WM, int WN, int NSET, bool SWIGLU, bool GATHER, bool PARTIAL>
+__global__ __launch_bounds__(WM * WN * 64) void gemm_bf16_kernel(GemmArgs a) {
+  constexpr int NT = WM * WN * 64;
+  constexpr int BK = 64;
+  constexpr int CH = BK / 8;       // 16-byte chunks per row
+  constexpr int NREG = SWIGLU ? 2 : 1;
+  constexpr int BNO = BNW / NREG;  // output columns per block
+  constexpr int WTM = BM / WM, WTN = BNO / WN;
+  constexpr int TM = WTM / 32, TN = WTN / 32;
+  constexpr int X_LD = BM * CH / NT;   // chunks per thread per stage
+  constexpr int W_LD = BNW * CH / NT;
+  constexpr int RSTEP = NT / CH;       // rows between a thread's chunks
+  static_assert(TM >= 1 && TN >= 1 && X_LD >= 1 && W_LD >= 1, "tile shape");
+  static_assert(RSTEP % 16 == 0, "swizzle period");
+  static_assert(!(SWIGLU && PARTIAL), "SwiGLU needs the full K sum");
+
+  __shared__ __attribute__((aligned(16))) u32x4_t sX[2][BM * CH];
+  __shared__ __attribute__((aligned(16))) u32x4_t sW[2][BNW * CH];
   __shared__ int s_info[3];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int wm = wave / WGN, wn = wave % WGN;
-  const int mt = blockIdx.x / a.n_tiles;
-  const int nt = blockIdx.x % a.n_tiles;
+  const int wm = wave / WN, wn = wave % WN;
+  int mt, nt, ks;
+  tile_of_block(a, mt, nt, ks);
 
   if (wave == 0) find_row_tile<BM>(a, mt, lane, s_info);
   __syncthreads();
@@ -119,117 +168,176 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmArgs a) {
   const int row0 = s_info[1];
   const int rows = s_info[2];
   const int K = a.K, N = a.N;
+  const int kb = ks * a.k_chunk;
+  const int klen = min(K, kb + a.k_chunk) - kb;
 
-  // per-thread global sources (fixed over the K loop)
-  const bf16_t* a_src[A_LD];
-  int a_lds[A_LD];
-  int a_k[A_LD];
+  // Thread tid stages chunk c = tid % 8 of rows tid/8 + q*RSTEP.  RSTEP is a
+  // multiple of 16, so the swizzled LDS slot has the same in-row position
+  // for every q: one base slot plus q * RSTEP * 8.
+  const int c = tid % CH;
+  const int r0 = tid / CH;
+  const int lds0 = r0 * CH + (c ^ swz(r0));
+  int xo[X_LD];
 #pragma unroll
-  for (int q = 0; q < A_LD; ++q) {
-    const int idx = q * 256 + tid;
-    const int r = idx / CH, c = idx % CH;
+  for (int q = 0; q < X_LD; ++q) {
+    const int r = r0 + q * RSTEP;
     const int p = row0 + (r < rows ? r : rows - 1);
     const int src = GATHER ? a.a_rows[p] : p;
-    a_src[q] = reinterpret_cast<const bf16_t*>(a.A) + (size_t)src * K + c * 8;
-    a_k[q] = c * 8;
-    a_lds[q] = r * CH + (c ^ (r & 7));
+    xo[q] = src * K + kb + c * 8;
   }
-  const bf16_t* b_src[B_LD];
-  int b_lds[B_LD];
-  int b_k[B_LD];
+  const bf16_t* xbase = reinterpret_cast<const bf16_t*>(a.A);
+  const bf16_t* wbase[NREG];
+  wbase[0] = reinterpret_cast<const bf16_t*>(a.B0) + (size_t)e * N * K;
+  if constexpr (SWIGLU) wbase[NREG - 1] = reinterpret_cast<const bf16_t*>(a.B1) + (size_t)e * N * K;
+  int wo[W_LD];
 #pragma unroll
-  for (int q = 0; q < B_LD; ++q) {
-    const int idx = q * 256 + tid;
-    const int r = idx / CH, c = idx % CH;
-    const int reg = r / BNO;
+  for (int q = 0; q < W_LD; ++q) {
+    const int r = r0 + q * RSTEP;
     int n = nt * BNO + (r % BNO);
     n = n < N ? n : N - 1;
-    const bf16_t* base = reinterpret_cast<const bf16_t*>(reg == 0 ? a.B0 : a.B1);
-    b_src[q] = base + ((size_t)e * N + n) * K + c * 8;
-    b_k[q] = c * 8;
-    b_lds[q] = r * CH + (c ^ (r & 7));
+    wo[q] = n * K + kb + c * 8;
   }
 
-  f32x16_t acc[NREG][TM][TN];
+  f32x16_t acc[NREG][TN][TM];
 #pragma unroll
   for (int g = 0; g < NREG; ++g)
 #pragma unroll
-    for (int i = 0; i < TM; ++i)
+    for (int j = 0; j < TN; ++j)
 #pragma unroll
-      for (int j = 0; j < TN; ++j)
+      for (int i = 0; i < TM; ++i)
 #pragma unroll
-        for (int v = 0; v < 16; ++v) acc[g][i][j][v] = 0.0f;
+        for (int v = 0; v < 16; ++v) acc[g][j][i][v] = 0.0f;
 
-  u32x4_t ra[A_LD], rb[B_LD];
-  const u32x4_t zero = {0u, 0u, 0u, 0u};
-  auto gload = [&](int k0) {
+  u32x4_t rx0[X_LD], rw0[W_LD], rx1[X_LD], rw1[W_LD];
+  auto gload = [&](u32x4_t* rx, u32x4_t* rw, int kt) {
+    const int k0 = kt * BK;
+    // K tail: a chunk past the end (possible in every stage when K < 64)
+    // reads its row start instead -- always in bounds -- and is zeroed
+    const bool ok = c * 8 < klen - k0;
+    const int ko = ok ? k0 : -(kb + c * 8);
 #pragma unroll
-    for (int q = 0; q < A_LD; ++q)
-      ra[q] = (k0 + a_k[q] < K) ? *reinterpret_cast<const u32x4_t*>(a_src[q] + k0) : zero;
+    for (int q = 0; q < X_LD; ++q) {
+      const u32x4_t v = *reinterpret_cast<const u32x4_t*>(xbase + xo[q] + ko);
+      rx[q] = ok ? v : u32x4_t{0u, 0u, 0u, 0u};
+    }
 #pragma unroll
-    for (int q = 0; q < B_LD; ++q)
-      rb[q] = (k0 + b_k[q] < K) ? *reinterpret_cast<const u32x4_t*>(b_src[q] + k0) : zero;
+    for (int q = 0; q < W_LD; ++q) {
+      const int reg = (r0 + q * RSTEP) / BNO;
+      const u32x4_t v = *reinterpret_cast<const u32x4_t*>(wbase[reg] + wo[q] + ko);
+      rw[q] = ok ? v : u32x4_t{0u, 0u, 0u, 0u};
+    }
   };
-  auto sstore = [&](int buf) {
+  auto sstore = [&](const u32x4_t* rx, const u32x4_t* rw, int buf) {
 #pragma unroll
-    for (int q = 0; q < A_LD; ++q) sA[buf][a_lds[q]] = ra[q];
+    for (int q = 0; q < X_LD; ++q) sX[buf][lds0 + q * RSTEP * CH] = rx[q];
 #pragma unroll
-    for (int q = 0; q < B_LD; ++q) sB[buf][b_lds[q]] = rb[q];
+    for (int q = 0; q < W_LD; ++q) sW[buf][lds0 + q * RSTEP * CH] = rw[q];
   };
-
-  const int nk = (K + BK - 1) / BK;
-  gload(0);
-  sstore(0);
-  __syncthreads();
   const int lrow = lane & 31;
   const int lk = lane >> 5;
-  for (int kt = 0; kt < nk; ++kt) {
-    const int buf = kt & 1;
-    if (kt + 1 < nk) gload((kt + 1) * BK);
+  auto compute = [&](int buf) {
 #pragma unroll
-    for (int ks = 0; ks < BK / 16; ++ks) {
-      const int ch = ks * 2 + lk;
-      bf16x8_t af[TM];
+    for (int kk = 0; kk < BK / 16; ++kk) {
+      const int ch = kk * 2 + lk;
+      bf16x8_t bx[TM];
 #pragma unroll
       for (int i = 0; i < TM; ++i) {
         const int r = wm * WTM + i * 32 + lrow;
-        af[i] = __builtin_bit_cast(bf16x8_t, sA[buf][r * CH + (ch ^ (r & 7))]);
+        bx[i] = __builtin_bit_cast(bf16x8_t, sX[buf][r * CH + (ch ^ swz(r))]);
       }
 #pragma unroll
       for (int g = 0; g < NREG; ++g) {
 #pragma unroll
         for (int j = 0; j < TN; ++j) {
           const int r = g * BNO + wn * WTN + j * 32 + lrow;
-          const bf16x8_t bf = __builtin_bit_cast(bf16x8_t, sB[buf][r * CH + (ch ^ (r & 7))]);
+          const bf16x8_t aw = __builtin_bit_cast(bf16x8_t, sW[buf][r * CH + (ch ^ swz(r))]);
 #pragma unroll
           for (int i = 0; i < TM; ++i)
-            acc[g][i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bf, acc[g][i][j], 0, 0, 0);
+            acc[g][j][i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aw, bx[i], acc[g][j][i], 0, 0, 0);
         }
       }
     }
-    if (kt + 1 < nk) sstore(buf ^ 1);
+  };
+
+  const int nk = (klen + BK - 1) / BK;
+  if constexpr (NSET == 2) {
+    if (nk > 0) {
+      gload(rx0, rw0, 0);
+      if (nk > 1) gload(rx1, rw1, 1);
+      sstore(rx0, rw0, 0);
+      if (nk > 2) gload(rx0, rw0, 2);
+    }
     __syncthreads();
+    for (int kt = 0; kt < nk; kt += 2) {
+      compute(0);
+      if (kt + 1 < nk) {
+        sstore(rx1, rw1, 1);
+        if (kt + 3 < nk) gload(rx1, rw1, kt + 3);
+      }
+      __syncthreads();
+      if (kt + 1 >= nk) break;
+      compute(1);
+      if (kt + 2 < nk) {
+        sstore(rx0, rw0, 0);
+        if (kt + 4 < nk) gload(rx0, rw0, kt + 4);
+      }
+      __syncthreads();
+    }
+  } else {
+    // one staging set: stage t+1 is in flight while stage t computes
+    (void)rx1;
+    (void)rw1;
+    if (nk > 0) {
+      gload(rx0, rw0, 0);
+      sstore(rx0, rw0, 0);
+      if (nk > 1) gload(rx0, rw0, 1);
+    }
+    __syncthreads();
+    for (int kt = 0; kt < nk; ++kt) {
+      const int buf = kt & 1;
+      compute(buf);
+      if (kt + 1 < nk) {
+        sstore(rx0, rw0, buf ^ 1);
+        if (kt + 2 < nk) gload(rx0, rw0, kt + 2);
+      }
+      __syncthreads();
+    }
   }
 
-  // epilogue: accumulator element v of lane l is (row 8*(v/4) + 4*(l/32) + v%4, col l%32)
-  bf16_t* Cp = reinterpret_cast<bf16_t*>(a.C);
+  // epilogue: four consecutive columns per store
 #pragma unroll
-  for (int i = 0; i < TM; ++i) {
+  for (int j = 0; j < TN; ++j) {
 #pragma unroll
-    for (int j = 0; j < TN; ++j) {
-      const int col = nt * BNO + wn * WTN + j * 32 + lrow;
+    for (int i = 0; i < TM; ++i) {
+      const int m = wm * WTM + i * 32 + lrow;
+      if (m >= rows) continue;
+      const size_t p = (size_t)(row0 + m);
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int r = wm * WTM + i * 32 + 8 * (v >> 2) + 4 * lk + (v & 3);
-        float o;
-        if constexpr (SWIGLU) {
-          const float gv = acc[0][i][j][v];
-          const float uv = acc[1][i][j][v];
-          o = gv / (1.0f + expf(-gv)) * uv;
-        } else {
-          o = acc[0][i][j][v];
+      for (int q = 0; q < 4; ++q) {
+        const int n = nt * BNO + wn * WTN + j * 32 + 8 * q + 4 * lk;
+        if (n >= N) continue;
+        float o[4];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          if constexpr (SWIGLU) {
+            const float gv = acc[0][j][i][4 * q + t];
+            const float uv = acc[1][j][i][4 * q + t];
+            o[t] = __fdividef(gv, 1.0f + __expf(-gv)) * uv;
+          } else {
+            o[t] = acc[0][j][i][4 * q + t];
+          }
         }
-        if (r < rows && col < N) Cp[(size_t)(row0 + r) * N + col] = (bf16_t)f32_to_bf16(o);
+        if constexpr (PARTIAL) {
+          float* Cp = reinterpret_cast<float*>(a.C) + (size_t)ks * a.split_stride;
+          f32x4_t v = {o[0], o[1], o[2], o[3]};
+          *reinterpret_cast<f32x4_t*>(Cp + p * N + n) = v;
+        } else {
+          bf16_t* Cp = reinterpret_cast<bf16_t*>(a.C);
+          uint2 v;
+          v.x = pack_bf16x2(o[0], o[1]);
+          v.y = pack_bf16x2(o[2], o[3]);
+          *reinterpret_cast<uint2*>(Cp + p * N + n) = v;
+        }
       }
     }
   }
@@ -274,25 +382,52 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs a) {
 
 // Upper bound on the number of row tiles of size BM over all groups.
 static long row_tile_bound(const GemmPlan& pl, int BM) {
-  if (pl.offsets == nullptr) return (pl.M_dense + BM - 1) / BM;
+  if (!pl.grouped) return (pl.M_dense + BM - 1) / BM;
   const long by_rows = (pl.R_max + (long)pl.E * (BM - 1)) / BM;
   const long by_cap = (long)pl.E * ((pl.m_cap + BM - 1) / BM);
   return by_rows < by_cap ? by_rows : by_cap;
 }
 
-template <int BM, int BNO, int WGM, int WGN, bool SWIGLU>
+// Tile shape: the largest row tile that still gives every CU work.  Tile
+// counts are estimated from the row bound (each group wastes half a tile on
+// average): 256-row tiles (128x128 per wave) when there are at least two
+// per CU, else 128-row tiles when there is at least one, else 64.
+enum TileCfg { TILE_L, TILE_M, TILE_S };
+static long est_tiles(const GemmPlan& pl, int bm, int bno, int N) {
+  const long mt = pl.grouped ? pl.R_max / bm + (pl.E + 1) / 2 : (pl.M_dense + bm - 1) / bm;
+  return mt * ((N + bno - 1) / bno);
+}
+static TileCfg tile_cfg(const GemmPlan& pl, int N, bool swiglu) {
+  const int bno = swiglu ? 128 : 256;
+  if (est_tiles(pl, 256, bno, N) >= 512) return TILE_L;
+  if (est_tiles(pl, 128, bno, N) >= 256) return TILE_M;
+  return TILE_S;
+}
+static int cfg_bm(TileCfg c) { return c == TILE_L ? 256 : c == TILE_M ? 128 : 64; }
+
+template <int BM, int BNW, int WM, int WN, int NSET, bool SWIGLU, bool PARTIAL>
 static hipError_t run_bf16(const GemmPlan& pl, GemmArgs a, hipStream_t st) {
+  constexpr int BNO = SWIGLU ? BNW / 2 : BNW;
   a.n_tiles = (a.N + BNO - 1) / BNO;
-  const long mtb = row_tile_bound(pl, BM);
-  const long blocks = mtb * a.n_tiles;
+  a.m_tiles = (int)row_tile_bound(pl, BM);
+  const long blocks = (long)a.m_tiles * a.n_tiles * a.splits;
   if (blocks == 0) return hipSuccess;
   if (a.a_rows)
-    hipLaunchKernelGGL((gemm_bf16_kernel<BM, BNO, WGM, WGN, SWIGLU, true>), dim3((unsigned)blocks),
-                       dim3(256), 0, st, a);
+    hipLaunchKernelGGL((gemm_bf16_kernel<BM, BNW, WM, WN, NSET, SWIGLU, true, PARTIAL>),
+                       dim3((unsigned)blocks), dim3(WM * WN * 64), 0, st, a);
   else
-    hipLaunchKernelGGL((gemm_bf16_kernel<BM, BNO, WGM, WGN, SWIGLU, false>),
-                       dim3((unsigned)blocks), dim3(256), 0, st, a);
+    hipLaunchKernelGGL((gemm_bf16_kernel<BM, BNW, WM, WN, NSET, SWIGLU, false, PARTIAL>),
+                       dim3((unsigned)blocks), dim3(WM * WN * 64), 0, st, a);
   return hipGetLastError();
+}
+
+template <bool SWIGLU, bool PARTIAL>
+static hipError_t run_cfg(const GemmPlan& pl, GemmArgs a, hipStream_t st) {
+  switch (tile_cfg(pl, a.N, SWIGLU)) {
+    case TILE_L: return run_bf16<256, 256, 2, 4, 1, SWIGLU, PARTIAL>(pl, a, st);
+    case TILE_M: return run_bf16<128, 256, 2, 4, 2, SWIGLU, PARTIAL>(pl, a, st);
+    default: return run_bf16<64, 256, 2, 2, 2, SWIGLU, PARTIAL>(pl, a, st);
+  }
 }
 
 template <bool SWIGLU>
@@ -308,19 +443,41 @@ static hipError_t run_f32(const GemmPlan& pl, GemmArgs a, hipStream_t st) {
   return hipGetLastError();
 }
 
+int gemm_down_splits(const GemmPlan& pl, int N, int K) {
+  if (!pl.bf16) return 1;
+  const TileCfg c = tile_cfg(pl, N, false);
+  const int bm = cfg_bm(c);
+  const long mt = pl.grouped ? (pl.R_max + bm - 1) / bm + (pl.E + 1) / 2
+                             : (pl.M_dense + bm - 1) / bm;
+  const long blocks = mt * ((N + 255) / 256);
+  const long want = 512;  // two workgroups per CU
+  if (blocks == 0 || blocks >= want || K < 512) return 1;
+  long s = (want + blocks - 1) / blocks;
+  if (s > 8) s = 8;
+  if (s > K / 256) s = K / 256;
+  if (s < 1) s = 1;
+  const int chunk = (int)(((K + s - 1) / s + 63) / 64 * 64);
+  return (K + chunk - 1) / chunk;
+}
+
 hipError_t launch_gemm_swiglu(const GemmPlan& pl, const void* A, const int32_t* a_rows,
                               const void* Wg, const void* Wu, int N, int K, void* H,
                               hipStream_t st) {
-  GemmArgs a{A, a_rows, pl.offsets, pl.E, pl.M_dense, Wg, Wu, N, K, H, 0};
+  GemmArgs a{A, a_rows, pl.offsets, pl.E, pl.M_dense, Wg, Wu, N, K, H, 0, 0, 0, 1, K};
   if (!pl.bf16) return run_f32<true>(pl, a, st);
-  return run_bf16<128, 128, 2, 2, true>(pl, a, st);
+  return run_cfg<true, false>(pl, a, st);
 }
 
 hipError_t launch_gemm_down(const GemmPlan& pl, const void* H, const void* Wd, int N, int K,
-                            void* Y, hipStream_t st) {
-  GemmArgs a{H, nullptr, pl.offsets, pl.E, pl.M_dense, Wd, nullptr, N, K, Y, 0};
+                            void* Y, int splits, long split_stride, hipStream_t st) {
+  GemmArgs a{H, nullptr, pl.offsets, pl.E, pl.M_dense, Wd, nullptr, N, K, Y, split_stride, 0, 0,
+             1, K};
   if (!pl.bf16) return run_f32<false>(pl, a, st);
-  return run_bf16<128, 128, 2, 2, false>(pl, a, st);
+  if (splits <= 1) return run_cfg<false, false>(pl, a, st);
+  a.splits = splits;
+  a.k_chunk = (K + splits - 1) / splits;
+  a.k_chunk = (a.k_chunk + 63) / 64 * 64;
+  return run_cfg<false, true>(pl, a, st);
 }
 
 }  // namespace moe

@@ -23,6 +23,7 @@ hipError_t launch_gather_rows(const void* x, const int32_t* row_token, const int
 // host), or one dense group of M_dense rows when offsets is null.
 struct GemmPlan {
   bool bf16;
+  bool grouped;  // rows come in E groups given by offsets (else one dense group)
   const int32_t* offsets;
   int E;
   int M_dense;
@@ -32,11 +33,23 @@ struct GemmPlan {
 hipError_t launch_gemm_swiglu(const GemmPlan& pl, const void* A, const int32_t* a_rows,
                               const void* Wg, const void* Wu, int N, int K, void* H,
                               hipStream_t st);
+// K splits the down GEMM uses for this plan (1 = direct dtype output;
+// more = fp32 partial planes [splits][R_max][N] summed in a fixed order by
+// the consumer).  A pure function of the plan, so workspace sizing and the
+// launch agree.
+int gemm_down_splits(const GemmPlan& pl, int N, int K);
 hipError_t launch_gemm_down(const GemmPlan& pl, const void* H, const void* Wd, int N, int K,
-                            void* Y, hipStream_t st);
+                            void* Y, int splits, long split_stride, hipStream_t st);
 
-hipError_t launch_combine(bool bf16, const void* y_packed, const int32_t* route_pos,
-                          const float* gates, const void* y_shared, int T, int k, int d, void* y,
-                          hipStream_t st);
+// y_packed is dtype rows (splits == 1) or fp32 partial planes (splits > 1,
+// plane stride split_stride elements).
+hipError_t launch_combine(bool bf16, const void* y_packed, int splits, long split_stride,
+                          const int32_t* route_pos, const float* gates, const void* y_shared,
+                          int T, int k, int d, void* y, hipStream_t st);
+// y[p] = sum over planes of parts[s][p] for p < offsets[E] (or M_dense rows
+// when offsets is null), rounded once to dtype.
+hipError_t launch_reduce_splits(bool bf16, const float* parts, int splits, long split_stride,
+                                const int32_t* offsets, int E, long R_max, int N, void* y,
+                                hipStream_t st);
 
 }  // namespace moe

@@ -55,9 +55,22 @@ int64_t rmax_of(const moe_shape* s, int64_t C) {
 }
 
 struct Layout {
-  size_t logits, ids, gates, cnt, counts, kept, offsets, route_pos, row_token, h, yp, hs, ys;
+  size_t logits, ids, gates, cnt, counts, kept, offsets, route_pos, row_token, h, yp, part, hs,
+      ys;
+  int splits;  // K splits of the routed down GEMM (fp32 partial planes when > 1)
   size_t total;
 };
+
+// Plan of the routed-expert grouped GEMMs.  Each token picks an expert at
+// most once, so with routes from moe_route no group exceeds min(T, C) rows;
+// moe_expert_ffn takes caller offsets and only assumes offsets[E] <= R_max.
+moe::GemmPlan routed_plan(const moe_shape* s, const int32_t* offsets, bool own_routes) {
+  const int64_t C = capacity_of(s);
+  const int64_t Rmax = rmax_of(s, C);
+  long cap = (long)Rmax;
+  if (own_routes) cap = (C >= 0 && C < s->T) ? (long)C : (long)s->T;
+  return moe::GemmPlan{s->dtype == MOE_DTYPE_BF16, true, offsets, (int)s->E, 0, (long)Rmax, cap};
+}
 
 Layout layout_of(const moe_shape* s) {
   const int64_t C = capacity_of(s);
@@ -83,6 +96,8 @@ Layout layout_of(const moe_shape* s) {
   L.row_token = take((size_t)Rmax * sizeof(int32_t));
   L.h = take((size_t)Rmax * s->d_ff * eb);
   L.yp = take((size_t)Rmax * s->d * eb);
+  L.splits = moe::gemm_down_splits(routed_plan(s, nullptr, false), (int)s->d, (int)s->d_ff);
+  L.part = take(L.splits > 1 ? (size_t)L.splits * Rmax * s->d * sizeof(float) : 0);
   L.hs = take((size_t)s->T * s->d_ff_shared * eb);
   L.ys = take(s->d_ff_shared > 0 ? (size_t)s->T * s->d * eb : 0);
   L.total = o;
@@ -189,14 +204,22 @@ int moe_expert_ffn(const moe_shape* s, const void* x_packed, const int32_t* offs
   v = check_ws(s, ws, ws_bytes);
   if (v != MOE_OK) return v;
   const Layout L = layout_of(s);
-  const int64_t Rmax = rmax_of(s, capacity_of(s));
-  moe::GemmPlan pl{s->dtype == MOE_DTYPE_BF16, offsets, (int)s->E, 0, (long)Rmax, (long)Rmax};
+  const moe::GemmPlan pl = routed_plan(s, offsets, false);
+  const bool bf16 = s->dtype == MOE_DTYPE_BF16;
   void* h = at<void>(ws, L.h);
   hipError_t e = moe::launch_gemm_swiglu(pl, x_packed, nullptr, w_gate, w_up, (int)s->d_ff,
                                          (int)s->d, h, stream);
   if (e != hipSuccess) return MOE_ERR_HIP;
-  return hip_status(
-      moe::launch_gemm_down(pl, h, w_down, (int)s->d, (int)s->d_ff, y_packed, stream));
+  if (L.splits <= 1)
+    return hip_status(moe::launch_gemm_down(pl, h, w_down, (int)s->d, (int)s->d_ff, y_packed, 1,
+                                            0, stream));
+  float* part = at<float>(ws, L.part);
+  const long stride = pl.R_max * s->d;
+  e = moe::launch_gemm_down(pl, h, w_down, (int)s->d, (int)s->d_ff, part, L.splits, stride,
+                            stream);
+  if (e != hipSuccess) return MOE_ERR_HIP;
+  return hip_status(moe::launch_reduce_splits(bf16, part, L.splits, stride, offsets, (int)s->E,
+                                              pl.R_max, (int)s->d, y_packed, stream));
 }
 
 int moe_combine(const moe_shape* s, const void* y_packed, const int32_t* route_pos,
@@ -206,8 +229,9 @@ int moe_combine(const moe_shape* s, const void* y_packed, const int32_t* route_p
   if (s->T > 0 && (!y_packed || !route_pos || !gates || !y)) return MOE_ERR_INVALID_ARG;
   if (!aligned16(y_packed) || !aligned16(y) || (y_shared && !aligned16(y_shared)))
     return MOE_ERR_INVALID_ARG;
-  return hip_status(moe::launch_combine(s->dtype == MOE_DTYPE_BF16, y_packed, route_pos, gates,
-                                        y_shared, (int)s->T, (int)s->k, (int)s->d, y, stream));
+  return hip_status(moe::launch_combine(s->dtype == MOE_DTYPE_BF16, y_packed, 1, 0, route_pos,
+                                        gates, y_shared, (int)s->T, (int)s->k, (int)s->d, y,
+                                        stream));
 }
 
 static int layer_forward_impl(const moe_shape* s, const void* x, const void* w_router,
@@ -255,30 +279,37 @@ static int layer_forward_impl(const moe_shape* s, const void* x, const void* w_r
   e = moe::launch_permute_index(ids, T, k, E, (int)C, at<int32_t>(ws, L.cnt), cnts,
                                 at<int32_t>(ws, L.kept), offsets, rpos, row_token, stream);
   if (e != hipSuccess) return MOE_ERR_HIP;
-  // each token picks an expert at most once, so no group exceeds min(T, C) rows
-  const long mcap = (C >= 0 && C < T) ? (long)C : (long)T;
-  moe::GemmPlan pl{bf16, offsets, E, 0, (long)Rmax, mcap};
+  const moe::GemmPlan pl = routed_plan(s, offsets, true);
   mark(2);
   e = moe::launch_gemm_swiglu(pl, x, row_token, w_gate, w_up, dff, d, h, stream);
   if (e != hipSuccess) return MOE_ERR_HIP;
   mark(3);
-  e = moe::launch_gemm_down(pl, h, w_down, d, dff, yp, stream);
+  // the split decision depends on the shape only (same as the workspace)
+  const void* yrows = yp;
+  const long stride = (long)Rmax * d;
+  if (L.splits > 1) {
+    yrows = at<float>(ws, L.part);
+    e = moe::launch_gemm_down(pl, h, w_down, d, dff, at<float>(ws, L.part), L.splits, stride,
+                              stream);
+  } else {
+    e = moe::launch_gemm_down(pl, h, w_down, d, dff, yp, 1, 0, stream);
+  }
   if (e != hipSuccess) return MOE_ERR_HIP;
   mark(4);
   const void* ysh = nullptr;
   if (shared) {
-    moe::GemmPlan ps{bf16, nullptr, 1, T, (long)T, (long)T};
+    moe::GemmPlan ps{bf16, false, nullptr, 1, T, (long)T, (long)T};
     void* hs = at<void>(ws, L.hs);
     void* ys = at<void>(ws, L.ys);
     e = moe::launch_gemm_swiglu(ps, x, nullptr, ws_gate, ws_up, (int)s->d_ff_shared, d, hs,
                                 stream);
     if (e != hipSuccess) return MOE_ERR_HIP;
-    e = moe::launch_gemm_down(ps, hs, ws_down, d, (int)s->d_ff_shared, ys, stream);
+    e = moe::launch_gemm_down(ps, hs, ws_down, d, (int)s->d_ff_shared, ys, 1, 0, stream);
     if (e != hipSuccess) return MOE_ERR_HIP;
     ysh = ys;
   }
   mark(5);
-  e = moe::launch_combine(bf16, yp, rpos, g, ysh, T, k, d, y, stream);
+  e = moe::launch_combine(bf16, yrows, L.splits, stride, rpos, g, ysh, T, k, d, y, stream);
   if (e != hipSuccess) return MOE_ERR_HIP;
   mark(6);
   return MOE_OK;

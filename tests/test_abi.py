@@ -134,3 +134,13 @@ def test_python_binding_rejects_host_tensors():
     with pytest.raises(ValueError):
         moe.route(s, torch.zeros(4, 64, dtype=torch.bfloat16),
                   torch.zeros(4, 64, dtype=torch.bfloat16))
+
+
+def test_capacity_and_workspace_for_every_workload():
+    from workloads import WORKLOADS
+    moe = _moe()
+    for name, w in WORKLOADS.items():
+        s = moe.shape_of(w)
+        C, R = moe.capacity(s)
+        assert R <= w.T * w.k
+        assert moe.workspace_bytes(s) >= R * (w.d + w.d_ff) * (2 if w.dtype == "bf16" else 4)
