@@ -39,6 +39,7 @@ struct GemmArgs {
   int m_tiles;        // row tiles (an upper bound; tiles past the last group exit)
   int splits;         // K splits (partial-plane output when > 1)
   int k_chunk;        // K elements per split, a multiple of 64
+  unsigned a_bytes;   // extent of A in bytes (< 2^31; buffer range of the activation loads)
 };
 
 // Find the (expert, first row, row count) of row-tile mt.  Executed by one
@@ -109,7 +110,7 @@ __device__ __forceinline__ void tile_of_block(const GemmArgs& a, int& mt, int& n
 }
 
 // ---------------------------------------------------------------------------
-// bf16 MFMA kernel, NT threads = WM x WN waves (NT = 256 or 512).
+// bf16 MFMA kernel, 256 threads = WM x WN waves.
 //
 // Operand roles.  The MFMA A operand is the weight tile (rows n), the B
 // operand the activation tile (rows m), so the accumulator holds D[n][m]:
@@ -117,86 +118,137 @@ __device__ __forceinline__ void tile_of_block(const GemmArgs& a, int& mt, int& n
 // 4*(l/32) + v%4 -- four consecutive output columns of one token row per
 // group of four accumulator registers, written as one 8-byte store.
 //
-// Pipeline.  K advances in stages of BK = 64 through two LDS buffers.  Each
-// thread stages its share of a stage in registers; with two register sets
-// the loads of stage t+2 are in flight while stage t feeds the MFMAs and
-// stage t+1 waits in the other set.  With 512 threads (two waves per SIMD)
-// one wave's MFMAs run while the other waits on LDS or memory.
+// Pipeline.  K advances in stages of BK = 32 through a ring of four LDS
+// stages filled by direct buffer->LDS loads (buffer_load_dwordx4 ... lds:
+// each wave-level load writes 1 KB = 16 rows of 64 bytes; no staging
+// registers; the K position is the scalar offset, so a lane's vector
+// offset never changes).  Three stages are in flight while one feeds the
+// MFMAs; a stage costs one s_waitcnt on the wave's own loads and one
+// workgroup barrier.  Each ring slot is its own LDS object and every access
+// names its slot statically (switch on kt % 4), so the compiler can tell a
+// load into one slot from a read of another and inserts no extra waits.
 //
-// LDS layout.  A row holds 8 chunks of 16 bytes; logical chunk c of row r
-// sits at c ^ f(r), f(r) = (r & 7) ^ ((r >> 3) & 1): the 8 or 16 lanes that
+// LDS layout.  A row holds 4 chunks of 16 bytes; logical chunk c of row r
+// sits at c ^ f(r), f(r) = ((r >> 1) ^ (r >> 3)) & 3: the 8 or 16 lanes that
 // read one chunk column of consecutive rows visit distinct bank groups
 // whether the LDS has 32 or 64 four-byte banks.
+//
+// K tail (K not a multiple of 32): a chunk past the end gets a vector
+// offset beyond the buffer, which the buffer unit returns as zero.
 //
 // SWIGLU: the weight tile stacks BNW/2 gate rows over the matching BNW/2 up
 // rows; the epilogue writes SiLU(gate) * up.  PARTIAL: fp32 output into the
 // K split's partial plane (summed later in a fixed order).
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ int swz(int r) { return (r & 7) ^ ((r >> 3) & 1); }
+__device__ __forceinline__ int swz(int r) { return ((r >> 1) ^ (r >> 3)) & 3; }
 
-template <int BM, int BNW, int WM, int WN, int NSET, bool SWIGLU, bool GATHER, bool PARTIAL>
-__global__ __launch_bounds__(WM * WN * 64) void gemm_bf16_kernel(GemmArgs a) {
-  constexpr int NT = WM * WN * 64;
-  constexpr int BK = 64;
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+constexpr int kBufFlags = 0x00020000;  // raw buffer, 32-bit data format
+
+template <int BM, int BNW, int WM, int WN, bool SWIGLU, bool GATHER, bool PARTIAL>
+__global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmArgs a) {
+#if defined(__HIP_DEVICE_COMPILE__)  // the host pass only emits the launch stub
+  constexpr int BK = 32;
   constexpr int CH = BK / 8;       // 16-byte chunks per row
+  constexpr int RPS = 64 / CH;     // rows per 1 KB wave-level load
+  constexpr int NS = 4;            // ring slots
   constexpr int NREG = SWIGLU ? 2 : 1;
   constexpr int BNO = BNW / NREG;  // output columns per block
   constexpr int WTM = BM / WM, WTN = BNO / WN;
   constexpr int TM = WTM / 32, TN = WTN / 32;
-  constexpr int X_LD = BM * CH / NT;   // chunks per thread per stage
-  constexpr int W_LD = BNW * CH / NT;
-  constexpr int RSTEP = NT / CH;       // rows between a thread's chunks
-  static_assert(TM >= 1 && TN >= 1 && X_LD >= 1 && W_LD >= 1, "tile shape");
-  static_assert(RSTEP % 16 == 0, "swizzle period");
+  constexpr int XS = BM / RPS / 4;   // activation loads per wave per stage
+  constexpr int WS = BNW / RPS / 4;  // weight loads per wave per stage
+  constexpr int PER = XS + WS;
+  constexpr int STAGE = (BM + BNW) * CH;  // 16-byte units per stage
+  static_assert(WM * WN == 4, "four waves");
+  static_assert(TM >= 1 && TN >= 1 && XS >= 1 && WS >= 1, "tile shape");
   static_assert(!(SWIGLU && PARTIAL), "SwiGLU needs the full K sum");
+  static_assert(PER * (NS - 1) < 64, "vmcnt range");
 
-  __shared__ __attribute__((aligned(16))) u32x4_t sX[2][BM * CH];
-  __shared__ __attribute__((aligned(16))) u32x4_t sW[2][BNW * CH];
+  __shared__ __attribute__((aligned(1024))) u32x4_t st0[STAGE];
+  __shared__ __attribute__((aligned(1024))) u32x4_t st1[STAGE];
+  __shared__ __attribute__((aligned(1024))) u32x4_t st2[STAGE];
+  __shared__ __attribute__((aligned(1024))) u32x4_t st3[STAGE];
   __shared__ int s_info[3];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  // wave-uniform values the compiler cannot prove uniform on its own (the
+  // wave index, and the tile found by wave 0 and read back from LDS): they
+  // feed buffer descriptors and LDS load destinations, which must be scalar
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave / WN, wn = wave % WN;
   int mt, nt, ks;
   tile_of_block(a, mt, nt, ks);
 
   if (wave == 0) find_row_tile<BM>(a, mt, lane, s_info);
   __syncthreads();
-  const int e = s_info[0];
+  const int e = __builtin_amdgcn_readfirstlane(s_info[0]);
   if (e < 0) return;
-  const int row0 = s_info[1];
-  const int rows = s_info[2];
+  const int row0 = __builtin_amdgcn_readfirstlane(s_info[1]);
+  const int rows = __builtin_amdgcn_readfirstlane(s_info[2]);
   const int K = a.K, N = a.N;
   const int kb = ks * a.k_chunk;
   const int klen = min(K, kb + a.k_chunk) - kb;
 
-  // Thread tid stages chunk c = tid % 8 of rows tid/8 + q*RSTEP.  RSTEP is a
-  // multiple of 16, so the swizzled LDS slot has the same in-row position
-  // for every q: one base slot plus q * RSTEP * 8.
-  const int c = tid % CH;
-  const int r0 = tid / CH;
-  const int lds0 = r0 * CH + (c ^ swz(r0));
-  int xo[X_LD];
+  // Buffer resources: activations, and the expert's gate/up or down rows.
+  const __amdgpu_buffer_rsrc_t rx =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(a.A), (short)0, (int)a.a_bytes, kBufFlags);
+  __amdgpu_buffer_rsrc_t rw[NREG];
+  const size_t wexp = (size_t)e * N * K * 2;
+  rw[0] = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<char*>(reinterpret_cast<const char*>(a.B0) + wexp), (short)0, N * K * 2,
+      kBufFlags);
+  if constexpr (SWIGLU)
+    rw[NREG - 1] = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<char*>(reinterpret_cast<const char*>(a.B1) + wexp), (short)0, N * K * 2,
+        kBufFlags);
+
+  // Lane i of wave-level load q writes row seg*RPS + i/CH (seg = wave*XS+q
+  // for activations) at physical chunk i%CH, so it fetches logical chunk
+  // (i%CH) ^ f(row).  Byte offsets, fixed for the whole K loop.
+  unsigned xo[XS];
+  int xc[XS];
 #pragma unroll
-  for (int q = 0; q < X_LD; ++q) {
-    const int r = r0 + q * RSTEP;
+  for (int q = 0; q < XS; ++q) {
+    const int r = (wave * XS + q) * RPS + lane / CH;
+    xc[q] = (lane % CH) ^ swz(r);
     const int p = row0 + (r < rows ? r : rows - 1);
     const int src = GATHER ? a.a_rows[p] : p;
-    xo[q] = src * K + kb + c * 8;
+    xo[q] = ((unsigned)src * (unsigned)K + (unsigned)(kb + xc[q] * 8)) * 2u;
   }
-  const bf16_t* xbase = reinterpret_cast<const bf16_t*>(a.A);
-  const bf16_t* wbase[NREG];
-  wbase[0] = reinterpret_cast<const bf16_t*>(a.B0) + (size_t)e * N * K;
-  if constexpr (SWIGLU) wbase[NREG - 1] = reinterpret_cast<const bf16_t*>(a.B1) + (size_t)e * N * K;
-  int wo[W_LD];
+  unsigned wo[WS];
+  int wc[WS];
 #pragma unroll
-  for (int q = 0; q < W_LD; ++q) {
-    const int r = r0 + q * RSTEP;
+  for (int q = 0; q < WS; ++q) {
+    const int r = (wave * WS + q) * RPS + lane / CH;
+    wc[q] = (lane % CH) ^ swz(r);
     int n = nt * BNO + (r % BNO);
     n = n < N ? n : N - 1;
-    wo[q] = n * K + kb + c * 8;
+    wo[q] = ((unsigned)n * (unsigned)K + (unsigned)(kb + wc[q] * 8)) * 2u;
   }
+
+  // stage layout: BM activation rows, then BNW weight rows
+  auto issue = [&](u32x4_t* stg, int kt) {
+    const int k0 = kt * BK;
+    const int soff = k0 * 2;
+    const bool tail = k0 + BK > klen;  // includes padding stages past K
+#pragma unroll
+    for (int q = 0; q < XS; ++q) {
+      // past-K chunk: an offset past every buffer extent reads zero
+      const unsigned vo = (tail && xc[q] * 8 >= klen - k0) ? 0x80000000u : xo[q];
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (lds_ptr_t)(stg + (wave * XS + q) * 64), 16, vo,
+                                               soff, 0, 0);
+    }
+#pragma unroll
+    for (int q = 0; q < WS; ++q) {
+      const int reg = ((wave * WS + q) * RPS) / BNO;
+      const unsigned vo = (tail && wc[q] * 8 >= klen - k0) ? 0x80000000u : wo[q];
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rw[reg],
+                                               (lds_ptr_t)(stg + BM * CH + (wave * WS + q) * 64),
+                                               16, vo, soff, 0, 0);
+    }
+  };
 
   f32x16_t acc[NREG][TN][TM];
 #pragma unroll
@@ -208,49 +260,39 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_bf16_kernel(GemmArgs a) {
 #pragma unroll
         for (int v = 0; v < 16; ++v) acc[g][j][i][v] = 0.0f;
 
-  u32x4_t rx0[X_LD], rw0[W_LD], rx1[X_LD], rw1[W_LD];
-  auto gload = [&](u32x4_t* rx, u32x4_t* rw, int kt) {
-    const int k0 = kt * BK;
-    // K tail: a chunk past the end (possible in every stage when K < 64)
-    // reads its row start instead -- always in bounds -- and is zeroed
-    const bool ok = c * 8 < klen - k0;
-    const int ko = ok ? k0 : -(kb + c * 8);
-#pragma unroll
-    for (int q = 0; q < X_LD; ++q) {
-      const u32x4_t v = *reinterpret_cast<const u32x4_t*>(xbase + xo[q] + ko);
-      rx[q] = ok ? v : u32x4_t{0u, 0u, 0u, 0u};
-    }
-#pragma unroll
-    for (int q = 0; q < W_LD; ++q) {
-      const int reg = (r0 + q * RSTEP) / BNO;
-      const u32x4_t v = *reinterpret_cast<const u32x4_t*>(wbase[reg] + wo[q] + ko);
-      rw[q] = ok ? v : u32x4_t{0u, 0u, 0u, 0u};
-    }
-  };
-  auto sstore = [&](const u32x4_t* rx, const u32x4_t* rw, int buf) {
-#pragma unroll
-    for (int q = 0; q < X_LD; ++q) sX[buf][lds0 + q * RSTEP * CH] = rx[q];
-#pragma unroll
-    for (int q = 0; q < W_LD; ++q) sW[buf][lds0 + q * RSTEP * CH] = rw[q];
-  };
+  // Fragment byte offsets inside a stage.  Row bases are multiples of 32,
+  // so the swizzle of a fragment row depends on the lane's row (lane % 32)
+  // only: one offset per (operand, 16-wide k step) covers every fragment,
+  // the rest is a compile-time displacement.
   const int lrow = lane & 31;
   const int lk = lane >> 5;
-  auto compute = [&](int buf) {
+  int xoff[2], woff[2];
+#pragma unroll
+  for (int kk = 0; kk < 2; ++kk) {
+    const int chunk = ((kk * 2 + lk) ^ swz(lrow)) * 16;
+    xoff[kk] = (wm * WTM + lrow) * CH * 16 + chunk;
+    woff[kk] = BM * CH * 16 + (wn * WTN + lrow) * CH * 16 + chunk;
+  }
+  auto compute = [&](const u32x4_t* stg) {
+    // opaque copies: keeps the compiler from hoisting one set of addresses
+    // per ring slot out of the loop (which would not fit in registers)
+    int xo0 = xoff[0], xo1 = xoff[1], wo0 = woff[0], wo1 = woff[1];
+    asm volatile("" : "+v"(xo0), "+v"(xo1), "+v"(wo0), "+v"(wo1));
+    const char* base = reinterpret_cast<const char*>(stg);
 #pragma unroll
     for (int kk = 0; kk < BK / 16; ++kk) {
-      const int ch = kk * 2 + lk;
+      const int xo = kk ? xo1 : xo0;
+      const int wo = kk ? wo1 : wo0;
       bf16x8_t bx[TM];
 #pragma unroll
-      for (int i = 0; i < TM; ++i) {
-        const int r = wm * WTM + i * 32 + lrow;
-        bx[i] = __builtin_bit_cast(bf16x8_t, sX[buf][r * CH + (ch ^ swz(r))]);
-      }
+      for (int i = 0; i < TM; ++i)
+        bx[i] = *reinterpret_cast<const bf16x8_t*>(base + xo + i * 32 * CH * 16);
 #pragma unroll
       for (int g = 0; g < NREG; ++g) {
 #pragma unroll
         for (int j = 0; j < TN; ++j) {
-          const int r = g * BNO + wn * WTN + j * 32 + lrow;
-          const bf16x8_t aw = __builtin_bit_cast(bf16x8_t, sW[buf][r * CH + (ch ^ swz(r))]);
+          const bf16x8_t aw =
+              *reinterpret_cast<const bf16x8_t*>(base + wo + (g * BNO + j * 32) * CH * 16);
 #pragma unroll
           for (int i = 0; i < TM; ++i)
             acc[g][j][i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aw, bx[i], acc[g][j][i], 0, 0, 0);
@@ -259,50 +301,34 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_bf16_kernel(GemmArgs a) {
     }
   };
 
-  const int nk = (klen + BK - 1) / BK;
-  if constexpr (NSET == 2) {
-    if (nk > 0) {
-      gload(rx0, rw0, 0);
-      if (nk > 1) gload(rx1, rw1, 1);
-      sstore(rx0, rw0, 0);
-      if (nk > 2) gload(rx0, rw0, 2);
-    }
-    __syncthreads();
-    for (int kt = 0; kt < nk; kt += 2) {
-      compute(0);
-      if (kt + 1 < nk) {
-        sstore(rx1, rw1, 1);
-        if (kt + 3 < nk) gload(rx1, rw1, kt + 3);
-      }
-      __syncthreads();
-      if (kt + 1 >= nk) break;
-      compute(1);
-      if (kt + 2 < nk) {
-        sstore(rx0, rw0, 0);
-        if (kt + 4 < nk) gload(rx0, rw0, kt + 4);
-      }
-      __syncthreads();
-    }
-  } else {
-    // one staging set: stage t+1 is in flight while stage t computes
-    (void)rx1;
-    (void)rw1;
-    if (nk > 0) {
-      gload(rx0, rw0, 0);
-      sstore(rx0, rw0, 0);
-      if (nk > 1) gload(rx0, rw0, 1);
-    }
-    __syncthreads();
-    for (int kt = 0; kt < nk; ++kt) {
-      const int buf = kt & 1;
-      compute(buf);
-      if (kt + 1 < nk) {
-        sstore(rx0, rw0, buf ^ 1);
-        if (kt + 2 < nk) gload(rx0, rw0, kt + 2);
-      }
-      __syncthreads();
-    }
+  // Stage count padded to a multiple of the ring size; stages past K (the
+  // padding, and the refills issued during the last three stages) read
+  // zeros -- every chunk offset is past the buffer -- so the loop body is
+  // four straight-line steps and every refill is unconditional.  (A
+  // conditional refill makes the compiler wait for all loads in flight
+  // before the next LDS read, which would serialise the ring.)
+  const int nk = ((klen + BK - 1) / BK + NS - 1) / NS * NS;
+  constexpr int WAIT = 0x0F70 | ((2 * PER) & 15) | (((2 * PER) >> 4) << 14);  // vmcnt(2*PER)
+  // stage kt: wait until only this wave's loads of stages kt+1, kt+2 are in
+  // flight, barrier, refill the slot stage kt-1 used with stage kt+3, compute
+  auto step = [&](u32x4_t* cur, u32x4_t* refill, int kt) {
+    __builtin_amdgcn_s_waitcnt(WAIT);
+    __builtin_amdgcn_s_barrier();
+    issue(refill, kt + NS - 1);
+    compute(cur);
+  };
+  issue(st0, 0);
+  issue(st1, 1);
+  issue(st2, 2);
+  for (int kt = 0; kt < nk; kt += NS) {
+    step(st0, st3, kt);
+    step(st1, st0, kt + 1);
+    step(st2, st1, kt + 2);
+    step(st3, st2, kt + 3);
   }
+  // the zero-reading refills past the end must land before the workgroup's
+  // LDS is released
+  __builtin_amdgcn_s_waitcnt(0x0F70);
 
   // epilogue: four consecutive columns per store
 #pragma unroll
@@ -341,6 +367,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_bf16_kernel(GemmArgs a) {
       }
     }
   }
+#endif
 }
 
 // ---------------------------------------------------------------------------
@@ -405,7 +432,7 @@ static TileCfg tile_cfg(const GemmPlan& pl, int N, bool swiglu) {
 }
 static int cfg_bm(TileCfg c) { return c == TILE_L ? 256 : c == TILE_M ? 128 : 64; }
 
-template <int BM, int BNW, int WM, int WN, int NSET, bool SWIGLU, bool PARTIAL>
+template <int BM, int BNW, int WM, int WN, bool SWIGLU, bool PARTIAL>
 static hipError_t run_bf16(const GemmPlan& pl, GemmArgs a, hipStream_t st) {
   constexpr int BNO = SWIGLU ? BNW / 2 : BNW;
   a.n_tiles = (a.N + BNO - 1) / BNO;
@@ -413,20 +440,20 @@ static hipError_t run_bf16(const GemmPlan& pl, GemmArgs a, hipStream_t st) {
   const long blocks = (long)a.m_tiles * a.n_tiles * a.splits;
   if (blocks == 0) return hipSuccess;
   if (a.a_rows)
-    hipLaunchKernelGGL((gemm_bf16_kernel<BM, BNW, WM, WN, NSET, SWIGLU, true, PARTIAL>),
-                       dim3((unsigned)blocks), dim3(WM * WN * 64), 0, st, a);
+    hipLaunchKernelGGL((gemm_bf16_kernel<BM, BNW, WM, WN, SWIGLU, true, PARTIAL>),
+                       dim3((unsigned)blocks), dim3(256), 0, st, a);
   else
-    hipLaunchKernelGGL((gemm_bf16_kernel<BM, BNW, WM, WN, NSET, SWIGLU, false, PARTIAL>),
-                       dim3((unsigned)blocks), dim3(WM * WN * 64), 0, st, a);
+    hipLaunchKernelGGL((gemm_bf16_kernel<BM, BNW, WM, WN, SWIGLU, false, PARTIAL>),
+                       dim3((unsigned)blocks), dim3(256), 0, st, a);
   return hipGetLastError();
 }
 
 template <bool SWIGLU, bool PARTIAL>
 static hipError_t run_cfg(const GemmPlan& pl, GemmArgs a, hipStream_t st) {
   switch (tile_cfg(pl, a.N, SWIGLU)) {
-    case TILE_L: return run_bf16<256, 256, 2, 4, 1, SWIGLU, PARTIAL>(pl, a, st);
-    case TILE_M: return run_bf16<128, 256, 2, 4, 2, SWIGLU, PARTIAL>(pl, a, st);
-    default: return run_bf16<64, 256, 2, 2, 2, SWIGLU, PARTIAL>(pl, a, st);
+    case TILE_L: return run_bf16<256, 256, 2, 2, SWIGLU, PARTIAL>(pl, a, st);
+    case TILE_M: return run_bf16<128, 256, 2, 2, SWIGLU, PARTIAL>(pl, a, st);
+    default: return run_bf16<64, 256, 1, 4, SWIGLU, PARTIAL>(pl, a, st);
   }
 }
 
@@ -461,17 +488,19 @@ int gemm_down_splits(const GemmPlan& pl, int N, int K) {
 }
 
 hipError_t launch_gemm_swiglu(const GemmPlan& pl, const void* A, const int32_t* a_rows,
-                              const void* Wg, const void* Wu, int N, int K, void* H,
+                              long a_nrows, const void* Wg, const void* Wu, int N, int K, void* H,
                               hipStream_t st) {
-  GemmArgs a{A, a_rows, pl.offsets, pl.E, pl.M_dense, Wg, Wu, N, K, H, 0, 0, 0, 1, K};
+  GemmArgs a{A, a_rows, pl.offsets, pl.E, pl.M_dense, Wg, Wu, N, K, H, 0, 0, 0, 1, K,
+             (unsigned)(a_nrows * K * 2)};
   if (!pl.bf16) return run_f32<true>(pl, a, st);
   return run_cfg<true, false>(pl, a, st);
 }
 
 hipError_t launch_gemm_down(const GemmPlan& pl, const void* H, const void* Wd, int N, int K,
                             void* Y, int splits, long split_stride, hipStream_t st) {
+  const long h_rows = pl.grouped ? pl.R_max : pl.M_dense;
   GemmArgs a{H, nullptr, pl.offsets, pl.E, pl.M_dense, Wd, nullptr, N, K, Y, split_stride, 0, 0,
-             1, K};
+             1, K, (unsigned)(h_rows * K * 2)};
   if (!pl.bf16) return run_f32<false>(pl, a, st);
   if (splits <= 1) return run_cfg<false, false>(pl, a, st);
   a.splits = splits;

@@ -30,8 +30,9 @@ struct GemmPlan {
   long R_max;  // bound on offsets[E]
   long m_cap;  // bound on any one group's rows
 };
+// a_nrows: rows of A (its byte extent bounds the activation loads)
 hipError_t launch_gemm_swiglu(const GemmPlan& pl, const void* A, const int32_t* a_rows,
-                              const void* Wg, const void* Wu, int N, int K, void* H,
+                              long a_nrows, const void* Wg, const void* Wu, int N, int K, void* H,
                               hipStream_t st);
 // K splits the down GEMM uses for this plan (1 = direct dtype output;
 // more = fp32 partial planes [splits][R_max][N] summed in a fixed order by

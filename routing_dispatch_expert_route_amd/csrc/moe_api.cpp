@@ -36,6 +36,15 @@ int validate(const moe_shape* s) {
   if (s->d >= (int64_t(1) << 24) || s->d_ff >= (int64_t(1) << 24) ||
       s->d_ff_shared >= (int64_t(1) << 24))
     return MOE_ERR_UNSUPPORTED;
+  // every activation, hidden and per-expert weight buffer the GEMMs read
+  // must span less than 2^31 bytes (32-bit buffer offsets)
+  const int64_t eb = s->dtype == MOE_DTYPE_BF16 ? 2 : 4;
+  const int64_t lim = int64_t(1) << 31;
+  const int64_t R = s->T * s->k;
+  const int64_t wide = s->d > s->d_ff ? s->d : s->d_ff;
+  if (s->T * s->d * eb >= lim || R * wide * eb >= lim || s->d * s->d_ff * eb >= lim ||
+      s->T * s->d_ff_shared * eb >= lim || s->d * s->d_ff_shared * eb >= lim)
+    return MOE_ERR_UNSUPPORTED;
   return MOE_OK;
 }
 
@@ -207,8 +216,8 @@ int moe_expert_ffn(const moe_shape* s, const void* x_packed, const int32_t* offs
   const moe::GemmPlan pl = routed_plan(s, offsets, false);
   const bool bf16 = s->dtype == MOE_DTYPE_BF16;
   void* h = at<void>(ws, L.h);
-  hipError_t e = moe::launch_gemm_swiglu(pl, x_packed, nullptr, w_gate, w_up, (int)s->d_ff,
-                                         (int)s->d, h, stream);
+  hipError_t e = moe::launch_gemm_swiglu(pl, x_packed, nullptr, pl.R_max, w_gate, w_up,
+                                         (int)s->d_ff, (int)s->d, h, stream);
   if (e != hipSuccess) return MOE_ERR_HIP;
   if (L.splits <= 1)
     return hip_status(moe::launch_gemm_down(pl, h, w_down, (int)s->d, (int)s->d_ff, y_packed, 1,
@@ -281,7 +290,7 @@ static int layer_forward_impl(const moe_shape* s, const void* x, const void* w_r
   if (e != hipSuccess) return MOE_ERR_HIP;
   const moe::GemmPlan pl = routed_plan(s, offsets, true);
   mark(2);
-  e = moe::launch_gemm_swiglu(pl, x, row_token, w_gate, w_up, dff, d, h, stream);
+  e = moe::launch_gemm_swiglu(pl, x, row_token, T, w_gate, w_up, dff, d, h, stream);
   if (e != hipSuccess) return MOE_ERR_HIP;
   mark(3);
   // the split decision depends on the shape only (same as the workspace)
@@ -301,7 +310,7 @@ static int layer_forward_impl(const moe_shape* s, const void* x, const void* w_r
     moe::GemmPlan ps{bf16, false, nullptr, 1, T, (long)T, (long)T};
     void* hs = at<void>(ws, L.hs);
     void* ys = at<void>(ws, L.ys);
-    e = moe::launch_gemm_swiglu(ps, x, nullptr, ws_gate, ws_up, (int)s->d_ff_shared, d, hs,
+    e = moe::launch_gemm_swiglu(ps, x, nullptr, T, ws_gate, ws_up, (int)s->d_ff_shared, d, hs,
                                 stream);
     if (e != hipSuccess) return MOE_ERR_HIP;
     e = moe::launch_gemm_down(ps, hs, ws_down, d, (int)s->d_ff_shared, ys, 1, 0, stream);

@@ -144,3 +144,12 @@ def test_capacity_and_workspace_for_every_workload():
         C, R = moe.capacity(s)
         assert R <= w.T * w.k
         assert moe.workspace_bytes(s) >= R * (w.d + w.d_ff) * (2 if w.dtype == "bf16" else 4)
+
+
+def test_library_has_no_unresolved_internal_symbols():
+    """Every kernel launch stub the host code references is defined (a kernel
+    whose body the host pass rejects would leave one undefined)."""
+    moe = _moe()
+    out = subprocess.run(["nm", "-D", "--undefined-only", moe.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    assert not [l for l in out.splitlines() if "_ZN3moe" in l]
