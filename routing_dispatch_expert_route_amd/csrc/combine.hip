@@ -6,8 +6,8 @@
 // shared expert is added outside the gate normalisation; the full trace: a
 // dropped route contributes nothing and the kept gates stay as they are.
 //
-// One wave per token; each lane owns chunks of 8 (bf16) or 4 (fp32) output
-// columns.  The k rows of a token are gathered with vector loads, summed in
+// One wave per (token, slice of 64 column chunks); each lane owns one chunk
+// of 8 (bf16) or 4 (fp32) output columns.  The k rows of a token are gathered with vector loads, summed in
 // fp32 in slot order j = 0..k-1 (fused multiply-add by the gate), the shared
 // row added last, and the sum rounded once to the output type.  When the
 // down GEMM split K, a row is first the sum of its fp32 partial planes in
@@ -18,20 +18,28 @@
 namespace moe {
 
 // Load G consecutive values of row p starting at column col as fp32.
+// Partial planes (at most 8) are summed in plane order; the loop is fully
+// unrolled so the loads of all planes are in flight together.
 template <bool BF16, bool PARTIAL, int G>
 __device__ __forceinline__ void load_row(const void* yp, int splits, long stride, size_t p,
                                          int d, int col, float* v) {
   if constexpr (PARTIAL) {
     const float* P = reinterpret_cast<const float*>(yp) + p * d + col;
+    f32x4_t part[8][G / 4];
 #pragma unroll
-    for (int q = 0; q < G; q += 4) {
-      f32x4_t s4 = *reinterpret_cast<const f32x4_t*>(P + q);
-      for (int s = 1; s < splits; ++s) {
-        const f32x4_t t4 = *reinterpret_cast<const f32x4_t*>(P + (size_t)s * stride + q);
-        s4 += t4;
-      }
+    for (int s = 0; s < 8; ++s)
 #pragma unroll
-      for (int t = 0; t < 4; ++t) v[q + t] = s4[t];
+      for (int q = 0; q < G / 4; ++q)
+        part[s][q] = s < splits ? *reinterpret_cast<const f32x4_t*>(P + (size_t)s * stride + 4 * q)
+                                : f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int q = 0; q < G / 4; ++q) {
+      f32x4_t s4 = part[0][q];
+#pragma unroll
+      for (int s = 1; s < 8; ++s)
+        if (s < splits) s4 += part[s][q];
+#pragma unroll
+      for (int t = 0; t < 4; ++t) v[4 * q + t] = s4[t];
     }
   } else if constexpr (BF16) {
     const u32x4_t u = *reinterpret_cast<const u32x4_t*>(reinterpret_cast<const bf16_t*>(yp) +
@@ -62,6 +70,8 @@ __device__ __forceinline__ void store_out(void* y, size_t idx, const float* acc)
   }
 }
 
+// grid: (token groups of 4, column slices of 64 chunks); one wave per
+// (token, slice), one chunk per lane
 template <bool BF16, bool PARTIAL>
 __global__ __launch_bounds__(256) void combine_kernel(const void* __restrict__ yp, int splits,
                                                       long split_stride,
@@ -72,7 +82,8 @@ __global__ __launch_bounds__(256) void combine_kernel(const void* __restrict__ y
   constexpr int G = BF16 ? 8 : 4;  // output elements per 16-byte chunk
   const int lane = threadIdx.x & 63;
   const int t = blockIdx.x * (blockDim.x / 64) + (threadIdx.x >> 6);
-  if (t >= T) return;
+  const int col = (blockIdx.y * 64 + lane) * G;
+  if (t >= T || col >= d) return;
   int pos[8];
   float g[8];
 #pragma unroll
@@ -80,26 +91,24 @@ __global__ __launch_bounds__(256) void combine_kernel(const void* __restrict__ y
     pos[j] = j < k ? route_pos[(size_t)t * k + j] : -1;
     g[j] = j < k ? gates[(size_t)t * k + j] : 0.0f;
   }
-  for (int col = lane * G; col < d; col += 64 * G) {
-    float acc[G];
+  float acc[G];
 #pragma unroll
-    for (int q = 0; q < G; ++q) acc[q] = 0.0f;
+  for (int q = 0; q < G; ++q) acc[q] = 0.0f;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      if (pos[j] < 0) continue;
-      float v[G];
-      load_row<BF16, PARTIAL, G>(yp, splits, split_stride, (size_t)pos[j], d, col, v);
+  for (int j = 0; j < 8; ++j) {
+    if (pos[j] < 0) continue;
+    float v[G];
+    load_row<BF16, PARTIAL, G>(yp, splits, split_stride, (size_t)pos[j], d, col, v);
 #pragma unroll
-      for (int q = 0; q < G; ++q) acc[q] = __builtin_fmaf(g[j], v[q], acc[q]);
-    }
-    if (ysh) {
-      float v[G];
-      load_row<BF16, false, G>(ysh, 1, 0, (size_t)t, d, col, v);
-#pragma unroll
-      for (int q = 0; q < G; ++q) acc[q] += v[q];
-    }
-    store_out<BF16>(y, (size_t)t * d + col, acc);
+    for (int q = 0; q < G; ++q) acc[q] = __builtin_fmaf(g[j], v[q], acc[q]);
   }
+  if (ysh) {
+    float v[G];
+    load_row<BF16, false, G>(ysh, 1, 0, (size_t)t, d, col, v);
+#pragma unroll
+    for (int q = 0; q < G; ++q) acc[q] += v[q];
+  }
+  store_out<BF16>(y, (size_t)t * d + col, acc);
 }
 
 // y[p][:] = sum_s parts[s][p][:] for the valid rows, rounded once.
@@ -127,7 +136,7 @@ hipError_t launch_combine(bool bf16, const void* y_packed, int splits, long spli
                           const int32_t* route_pos, const float* gates, const void* y_shared,
                           int T, int k, int d, void* y, hipStream_t st) {
   if (T == 0) return hipSuccess;
-  dim3 grid(ceil_div(T, 4)), block(256);
+  dim3 grid(ceil_div(T, 4), ceil_div(d, 64 * (bf16 ? 8 : 4))), block(256);
   const bool part = splits > 1;
 #define CB(B, P)                                                                           \
   hipLaunchKernelGGL((combine_kernel<B, P>), grid, block, 0, st, y_packed, splits, split_stride, \

@@ -34,13 +34,16 @@ __global__ __launch_bounds__(64) void hist_kernel(const int32_t* __restrict__ id
   for (int e = lane; e < E; e += kWave) s_cnt[e] = 0;
   __syncthreads();
   const int r0 = c * kChunk;
-  for (int it = 0; it < kChunk / kWave; ++it) {
+  constexpr int NIT = kChunk / kWave;
+  int ev[NIT];  // all of the lane's ids in flight together
+#pragma unroll
+  for (int it = 0; it < NIT; ++it) {
     const int r = r0 + it * kWave + lane;
-    if (r < R) {
-      const int e = ids[r];
-      if (e >= 0 && e < E) atomicAdd(&s_cnt[e], 1);
-    }
+    ev[it] = r < R ? ids[r] : -1;
   }
+#pragma unroll
+  for (int it = 0; it < NIT; ++it)
+    if (ev[it] >= 0 && ev[it] < E) atomicAdd(&s_cnt[ev[it]], 1);
   __syncthreads();
   for (int e = lane; e < E; e += kWave) cnt[(size_t)e * nchunks + c] = s_cnt[e];
 }
@@ -66,12 +69,21 @@ __global__ __launch_bounds__(1024) void scan_kernel(int32_t* __restrict__ cnt, i
   for (int e = wave; e < E; e += nwaves) {
     int32_t* row = cnt + (size_t)e * nchunks;
     int carry = 0;
-    for (int c0 = 0; c0 < nchunks; c0 += kWave) {
-      const int c = c0 + lane;
-      const int v = c < nchunks ? row[c] : 0;
-      const int incl = wave_incl_scan(v, lane);
-      if (c < nchunks) row[c] = carry + incl - v;
-      carry += __shfl(incl, kWave - 1, kWave);
+    constexpr int NB = 8;  // groups of 64 chunks loaded together
+    for (int c1 = 0; c1 < nchunks; c1 += NB * kWave) {
+      int v[NB];
+#pragma unroll
+      for (int q = 0; q < NB; ++q) {
+        const int c = c1 + q * kWave + lane;
+        v[q] = c < nchunks ? row[c] : 0;
+      }
+#pragma unroll
+      for (int q = 0; q < NB; ++q) {
+        const int c = c1 + q * kWave + lane;
+        const int incl = wave_incl_scan(v[q], lane);
+        if (c < nchunks) row[c] = carry + incl - v[q];
+        carry += __shfl(incl, kWave - 1, kWave);
+      }
     }
     if (lane == 0) {
       const int m = (C < 0 || carry <= C) ? carry : C;
@@ -111,10 +123,17 @@ __global__ __launch_bounds__(64) void scatter_kernel(const int32_t* __restrict__
   __syncthreads();
   const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (kWave - lane));
   const int r0 = c * kChunk;
-  for (int it = 0; it < kChunk / kWave; ++it) {
+  constexpr int NIT = kChunk / kWave;
+  int ev[NIT];  // all of the lane's ids in flight together
+#pragma unroll
+  for (int it = 0; it < NIT; ++it) {
     const int r = r0 + it * kWave + lane;
-    int e = -1;
-    if (r < R) e = ids[r];
+    ev[it] = r < R ? ids[r] : -1;
+  }
+#pragma unroll
+  for (int it = 0; it < NIT; ++it) {
+    const int r = r0 + it * kWave + lane;
+    const int e = ev[it];
     const bool valid = r < R && e >= 0 && e < E;
     // lanes holding the same expert id: match on all 8 bits (E <= 256)
     uint64_t m = __ballot(valid);

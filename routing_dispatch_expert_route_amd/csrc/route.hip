@@ -8,13 +8,12 @@
 // softmax probability (no renormalisation).
 //
 // Two kernels:
-//   router_logits_kernel  one lane per (token, group of EL experts): each
-//       logit is a sequential fp32 fused multiply-add over the hidden index
-//       in increasing order, bias added after the sum.  That fixed order is
-//       what makes the logits -- and so the selected expert ids at near
-//       ties -- bit-reproducible.  The lane's token row streams through
-//       16-byte vector loads; the expert rows are wave-uniform, so the
-//       compiler fetches them with scalar loads shared by the 64 lanes.
+//   router_logits_kernel  one lane per (token, expert) chain: each logit is a
+//       sequential fp32 fused multiply-add over the hidden index in
+//       increasing order, bias added after the sum.  That fixed order is what
+//       makes the logits -- and so the selected expert ids at near ties --
+//       bit-reproducible.  Token and expert rows are staged through LDS as
+//       fp32 tiles (see the kernel).
 //   topk_gates_kernel  one lane per token over an LDS copy of its logits:
 //       a single insertion pass keeps the k best by (logit desc, index asc),
 //       then the gates.
@@ -23,67 +22,126 @@
 
 namespace moe {
 
-template <bool BF16>
-struct Granule;
-template <>
-struct Granule<true> {
-  static constexpr int N = 8;  // 8 bf16 per 16 bytes
-  __device__ __forceinline__ static void load(const void* p, float* v) {
-    u32x4_t u = *reinterpret_cast<const u32x4_t*>(p);
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      v[2 * q] = bf16lo(u[q]);
-      v[2 * q + 1] = bf16hi(u[q]);
-    }
-  }
-};
-template <>
-struct Granule<false> {
-  static constexpr int N = 4;  // 4 fp32 per 16 bytes
-  __device__ __forceinline__ static void load(const void* p, float* v) {
-    f32x4_t u = *reinterpret_cast<const f32x4_t*>(p);
-#pragma unroll
-    for (int q = 0; q < 4; ++q) v[q] = u[q];
-  }
-};
-
-template <bool BF16, int EL>
+// Router logits.  Block = 64 tokens x (4 * EPW) experts; lane = token, wave
+// w owns experts e0 + w*EPW + j.  The hidden dimension advances in chunks of
+// RKC (128 when the chains are few and latency-bound, 64 when many blocks
+// share a CU): the block stages the x tile [64][RKC] and the W tile
+// [4*EPW][RKC] in LDS as fp32 (converted once per element), then every lane
+// runs its EPW fused-multiply-add chains in increasing hidden index, reading
+// its own x row and broadcast W rows.  Chunks are prefetched two ahead into
+// two register sets while the current one is consumed.
+template <bool BF16, int EPW, int RKC>
 __global__ __launch_bounds__(256) void router_logits_kernel(
     const void* __restrict__ x, const void* __restrict__ w, const float* __restrict__ b, int T,
     int d, int E, float* __restrict__ logits) {
-  using G = Granule<BF16>;
+  constexpr int EB = 4 * EPW;             // experts per block
+  constexpr int G = BF16 ? 8 : 4;         // elements per 16-byte chunk
+  constexpr int CPR = RKC / G;            // 16-byte chunks per tile row
+  constexpr int XPT = 64 * CPR / 256;     // x chunks per thread
+  constexpr int WPT = (EB * CPR + 255) / 256;  // W chunks per thread (upper bound)
+  constexpr int XS = RKC + 4;             // padded fp32 row (conflict-free b128 reads)
+  __shared__ __attribute__((aligned(16))) float sx[64 * XS];
+  __shared__ __attribute__((aligned(16))) float sw[EB * RKC];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int t0 = blockIdx.x * 64;
+  const int e0 = blockIdx.y * EB;
+  const char* xb = reinterpret_cast<const char*>(x);
+  const char* wb = reinterpret_cast<const char*>(w);
   constexpr int esz = BF16 ? 2 : 4;
-  const int lane = threadIdx.x & (kWave - 1);
-  const int wave = threadIdx.x / kWave;
-  const int t = blockIdx.x * kWave + lane;
-  const int e0 = (blockIdx.y * (blockDim.x / kWave) + wave) * EL;
-  if (e0 >= E) return;  // whole wave
-  const int tc = t < T ? t : T - 1;  // clamped row: loads stay in bounds
-  const char* xr = reinterpret_cast<const char*>(x) + (size_t)tc * d * esz;
-  const char* wr[EL];
+  const u32x4_t zero = {0u, 0u, 0u, 0u};
+
+  u32x4_t rx[2][XPT], rw[2][WPT];
+  auto fetch = [&](int set, int k0) {
 #pragma unroll
-  for (int j = 0; j < EL; ++j) {
-    const int e = e0 + j < E ? e0 + j : E - 1;
-    wr[j] = reinterpret_cast<const char*>(w) + (size_t)e * d * esz;
-  }
-  float acc[EL];
-#pragma unroll
-  for (int j = 0; j < EL; ++j) acc[j] = 0.0f;
-  for (int i = 0; i < d; i += G::N) {
-    float xv[G::N];
-    G::load(xr + (size_t)i * esz, xv);
-#pragma unroll
-    for (int j = 0; j < EL; ++j) {
-      float wv[G::N];
-      G::load(wr[j] + (size_t)i * esz, wv);
-#pragma unroll
-      for (int q = 0; q < G::N; ++q) acc[j] = __builtin_fmaf(xv[q], wv[q], acc[j]);
+    for (int q = 0; q < XPT; ++q) {
+      const int c = q * 256 + tid;
+      const int row = c / CPR, col = (c % CPR) * G;
+      const int t = min(t0 + row, T - 1);
+      rx[set][q] = (k0 + col < d)
+                       ? *reinterpret_cast<const u32x4_t*>(xb + ((size_t)t * d + k0 + col) * esz)
+                       : zero;
     }
+#pragma unroll
+    for (int q = 0; q < WPT; ++q) {
+      const int c = q * 256 + tid;
+      const int row = c / CPR, col = (c % CPR) * G;
+      const int e = min(e0 + row, E - 1);
+      rw[set][q] = (c < EB * CPR && k0 + col < d)
+                       ? *reinterpret_cast<const u32x4_t*>(wb + ((size_t)e * d + k0 + col) * esz)
+                       : zero;
+    }
+  };
+  auto put = [&](float* dst, const u32x4_t v) {
+    if constexpr (BF16) {
+      f32x4_t lo = {bf16lo(v[0]), bf16hi(v[0]), bf16lo(v[1]), bf16hi(v[1])};
+      f32x4_t hi = {bf16lo(v[2]), bf16hi(v[2]), bf16lo(v[3]), bf16hi(v[3])};
+      *reinterpret_cast<f32x4_t*>(dst) = lo;
+      *reinterpret_cast<f32x4_t*>(dst + 4) = hi;
+    } else {
+      *reinterpret_cast<u32x4_t*>(dst) = v;
+    }
+  };
+  auto stage = [&](int set) {
+#pragma unroll
+    for (int q = 0; q < XPT; ++q) {
+      const int c = q * 256 + tid;
+      put(sx + (c / CPR) * XS + (c % CPR) * G, rx[set][q]);
+    }
+#pragma unroll
+    for (int q = 0; q < WPT; ++q) {
+      const int c = q * 256 + tid;
+      if (c < EB * CPR) put(sw + (c / CPR) * RKC + (c % CPR) * G, rw[set][q]);
+    }
+  };
+
+  float acc[EPW];
+#pragma unroll
+  for (int j = 0; j < EPW; ++j) acc[j] = 0.0f;
+  const float* xr = sx + lane * XS;
+  auto chain4 = [&](int kk) {
+    const f32x4_t xv = *reinterpret_cast<const f32x4_t*>(xr + kk);
+#pragma unroll
+    for (int j = 0; j < EPW; ++j) {
+      const f32x4_t wv = *reinterpret_cast<const f32x4_t*>(sw + (wave * EPW + j) * RKC + kk);
+      acc[j] = __builtin_fmaf(xv[0], wv[0], acc[j]);
+      acc[j] = __builtin_fmaf(xv[1], wv[1], acc[j]);
+      acc[j] = __builtin_fmaf(xv[2], wv[2], acc[j]);
+      acc[j] = __builtin_fmaf(xv[3], wv[3], acc[j]);
+    }
+  };
+  auto consume = [&](int k0) {
+    const int kc = min(RKC, d - k0);  // a multiple of 8
+    if (kc == RKC) {
+#pragma unroll 8
+      for (int kk = 0; kk < RKC; kk += 4) chain4(kk);
+    } else {
+      for (int kk = 0; kk < kc; kk += 4) chain4(kk);
+    }
+  };
+  const int nc = (d + RKC - 1) / RKC;
+  fetch(0, 0);
+  if (nc > 1) fetch(1, RKC);
+  for (int c = 0; c < nc; c += 2) {
+    __syncthreads();  // previous chunk fully consumed
+    stage(0);
+    if (c + 2 < nc) fetch(0, (c + 2) * RKC);
+    __syncthreads();
+    consume(c * RKC);
+    if (c + 1 >= nc) break;
+    __syncthreads();
+    stage(1);
+    if (c + 3 < nc) fetch(1, (c + 3) * RKC);
+    __syncthreads();
+    consume((c + 1) * RKC);
   }
+  const int t = t0 + lane;
   if (t >= T) return;
 #pragma unroll
-  for (int j = 0; j < EL; ++j) {
-    const int e = e0 + j;
+  for (int j = 0; j < EPW; ++j) {
+    const int e = e0 + wave * EPW + j;
     if (e < E) {
       float v = acc[j];
       if (b) v = v + b[e];
@@ -98,6 +156,8 @@ __device__ __forceinline__ bool precedes(float a, int ia, float b, int ib) {
   return a > b || (a == b && ia < ib);
 }
 
+// KMAX: slots kept by the insertion pass, the smallest power of two >= k
+template <int KMAX>
 __global__ __launch_bounds__(64) void topk_gates_kernel(const float* __restrict__ logits, int T,
                                                          int E, int k, int renorm,
                                                          int32_t* __restrict__ ids,
@@ -108,13 +168,24 @@ __global__ __launch_bounds__(64) void topk_gates_kernel(const float* __restrict_
   const int t0 = blockIdx.x * tpb;
   const int nt = min(tpb, T - t0);
   const int stride = E + 1;
-  for (int idx = lane; idx < nt * E; idx += tpb) {
-    s_log[(idx / E) * stride + idx % E] = logits[(size_t)t0 * E + idx];
+  // coalesced staging, eight loads in flight per lane
+  const int n = nt * E;
+  for (int base = 0; base < n; base += 8 * tpb) {
+    float v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int idx = base + u * tpb + lane;
+      v[u] = idx < n ? logits[(size_t)t0 * E + idx] : 0.0f;
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int idx = base + u * tpb + lane;
+      if (idx < n) s_log[(idx / E) * stride + idx % E] = v[u];
+    }
   }
   __syncthreads();
   if (lane >= nt) return;
   const float* row = s_log + lane * stride;
-  constexpr int KMAX = 8;
   float bv[KMAX];
   int bi[KMAX];
 #pragma unroll
@@ -164,33 +235,40 @@ hipError_t launch_route(bool bf16, const void* x, const void* w, const float* b,
                         int E, int k, int renorm, float* logits, int32_t* ids, float* gates,
                         hipStream_t st) {
   if (T == 0) return hipSuccess;
-  // experts per lane: enough waves to cover the chip when T*E is small,
-  // more register reuse of the token row when it is large
-  const long pairs = (long)T * E;
-  int EL = 8;
-  if (pairs <= 64L * 1024) EL = 1;
-  else if (pairs <= 256L * 1024) EL = 4;
-  dim3 grid(ceil_div(T, kWave), ceil_div(E, EL * 4));
+  // experts per wave: the most register reuse that still leaves about
+  // 2048 waves (two per SIMD) of independent chains
+  const long waves_at1 = (long)ceil_div(T, kWave) * E;
+  int EPW = 1;
+  if (waves_at1 >= 8192) EPW = 4;
+  else if (waves_at1 >= 4096) EPW = 2;
+  dim3 grid(ceil_div(T, kWave), ceil_div(E, 4 * EPW));
   dim3 block(256);
-#define RL(BF, EL_)                                                                     \
-  hipLaunchKernelGGL((router_logits_kernel<BF, EL_>), grid, block, 0, st, x, w, b, T, d, E, \
-                     logits)
+#define RL(BF, EPW_)                                                                            \
+  hipLaunchKernelGGL((router_logits_kernel<BF, EPW_, (EPW_ == 4 ? 64 : 128)>), grid, block, 0, st, \
+                     x, w, b, T, d, E, logits)
   if (bf16) {
-    if (EL == 1) RL(true, 1);
-    else if (EL == 4) RL(true, 4);
-    else RL(true, 8);
+    if (EPW == 1) RL(true, 1);
+    else if (EPW == 2) RL(true, 2);
+    else RL(true, 4);
   } else {
-    if (EL == 1) RL(false, 1);
-    else if (EL == 4) RL(false, 4);
-    else RL(false, 8);
+    if (EPW == 1) RL(false, 1);
+    else if (EPW == 2) RL(false, 2);
+    else RL(false, 4);
   }
 #undef RL
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   const int tpb = (E + 1) * 64 * (int)sizeof(float) <= 48 * 1024 ? 64 : 32;
   const size_t lds = (size_t)tpb * (E + 1) * sizeof(float);
-  hipLaunchKernelGGL(topk_gates_kernel, dim3(ceil_div(T, tpb)), dim3(tpb), lds, st, logits, T, E,
-                     k, renorm, ids, gates);
+  const dim3 tg(ceil_div(T, tpb)), tb(tpb);
+  if (k <= 1)
+    hipLaunchKernelGGL(topk_gates_kernel<1>, tg, tb, lds, st, logits, T, E, k, renorm, ids, gates);
+  else if (k <= 2)
+    hipLaunchKernelGGL(topk_gates_kernel<2>, tg, tb, lds, st, logits, T, E, k, renorm, ids, gates);
+  else if (k <= 4)
+    hipLaunchKernelGGL(topk_gates_kernel<4>, tg, tb, lds, st, logits, T, E, k, renorm, ids, gates);
+  else
+    hipLaunchKernelGGL(topk_gates_kernel<8>, tg, tb, lds, st, logits, T, E, k, renorm, ids, gates);
   return hipGetLastError();
 }
 
