@@ -11,11 +11,23 @@ Prints ONE JSON line:
   value          whole-step tokens/s (T / step time)
   roofline       dominant kernel (grouped GEMM 1, gate+up+SwiGLU) against
                  the MI355X bf16 dense MFMA peak or the HBM peak, timed with
-                 hipEvents recorded on the library's stream around it
+                 hipEvents recorded on the library's stream around it in
+                 every timed step; traffic = HBM bytes per launch from the
+                 committed rocprofv3 counter summary (null when absent or
+                 taken on another version of the GEMM source)
   cpu_baseline   the CPU oracle on a bounded sample of the same workload
-  stages_us      mean per-stage times of the timed-variant pass
+  stages_us      mean per-stage times of a second, fully event-marked pass
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+Counter support (HBM traffic of GEMM 1):
+  --copy-calibration MIB   after the run, copy a MIB-MiB device buffer
+                           three times (plain blit copies of known size, the
+                           scale for FETCH_SIZE / WRITE_SIZE)
+  --traffic-from F W       read two rocprofv3 --pmc csv output folders (F:
+                           FETCH_SIZE pass, W: WRITE_SIZE pass, both of
+                           `bench.py --copy-calibration ...`) and write the
+                           per-launch traffic summary of GEMM 1 (no GPU use)
 """
 import argparse
 import ctypes
@@ -55,17 +67,72 @@ def gemm1_model(w, kept_rows, active_experts):
     return flops, byts
 
 
+GEMM_SRC = os.path.join(ROOT, "routing_dispatch_expert_route_amd", "csrc", "gemm.hip")
+N_CAL = 3  # calibration copies at the end of a --copy-calibration run
+
+
+def _gemm_sha():
+    return hashlib.sha256(open(GEMM_SRC, "rb").read()).hexdigest()
+
+
+def traffic_path(workload):
+    return os.path.join(ROOT, "profiles", f"gemm1_{workload}_traffic.json")
+
+
 def traffic_from_profile(workload):
     """HBM bytes per GEMM-1 launch from the committed rocprofv3 counter
     summary, or None when absent or taken on a different gemm.hip."""
-    path = os.path.join(ROOT, "profiles", f"gemm1_{workload}_traffic.json")
+    path = traffic_path(workload)
     if not os.path.exists(path):
         return None
     rec = json.load(open(path))
-    src = open(os.path.join(ROOT, "routing_dispatch_expert_route_amd", "csrc", "gemm.hip"), "rb").read()
-    if rec.get("gemm_hip_sha256") != hashlib.sha256(src).hexdigest():
+    if rec.get("gemm_hip_sha256") != _gemm_sha():
         return None
-    return (rec["fetch_kib"] * rec["fetch_scale"] + rec["write_kib"] * rec["write_scale"]) * 1024.0
+    return rec["traffic_bytes_per_launch"]
+
+
+def _is_gemm1(name):
+    # gemm_bf16_kernel<BM, BNW, WM, WN, SWIGLU, GATHER, PARTIAL>: GEMM 1 of
+    # the whole-layer path is the SwiGLU instance that gathers token rows
+    if "gemm_bf16_kernel<" not in name:
+        return False
+    args = [a.strip() for a in name.split("<", 1)[1].split(">", 1)[0].split(",")]
+    return len(args) == 7 and args[4] == "true" and args[5] == "true"
+
+
+def _counter_rows(folder, counter):
+    import csv
+    import glob
+    rows = []
+    for f in sorted(glob.glob(os.path.join(folder, "**", "*counter_collection.csv"), recursive=True)):
+        rows += [r for r in csv.DictReader(open(f)) if r["Counter_Name"] == counter]
+    rows.sort(key=lambda r: int(r["Dispatch_Id"]))
+    if not rows:
+        raise SystemExit(f"no {counter} rows under {folder}")
+    return rows
+
+
+def traffic_summary(fetch_dir, write_dir, workload, cal_mib, out_path):
+    """Per-launch HBM bytes of GEMM 1 from two counter passes, each counter
+    scaled by what it reads for the calibration copies (known bytes)."""
+    res = {"workload": workload, "gemm_hip_sha256": _gemm_sha(), "calibration_mib": cal_mib}
+    known = cal_mib * 1024.0  # KiB read (and written) by one calibration copy
+    for key, folder, counter in (("fetch", fetch_dir, "FETCH_SIZE"), ("write", write_dir, "WRITE_SIZE")):
+        rows = _counter_rows(folder, counter)
+        g1 = [float(r["Counter_Value"]) for r in rows if _is_gemm1(r["Kernel_Name"])]
+        cal = [float(r["Counter_Value"]) for r in rows if "copyBuffer" in r["Kernel_Name"]][-N_CAL:]
+        if not g1 or len(cal) < N_CAL:
+            raise SystemExit(f"{counter}: {len(g1)} GEMM-1 and {len(cal)} calibration dispatches")
+        res[f"{key}_kib"] = sum(g1) / len(g1)
+        res[f"{key}_dispatches"] = len(g1)
+        res[f"{key}_copy_kib"] = sum(cal) / len(cal)
+        res[f"{key}_scale"] = known / res[f"{key}_copy_kib"]
+    res["traffic_bytes_per_launch"] = 1024.0 * (res["fetch_kib"] * res["fetch_scale"]
+                                                 + res["write_kib"] * res["write_scale"])
+    with open(out_path, "w") as f:
+        json.dump(res, f, indent=1)
+        f.write("\n")
+    print(json.dumps(res))
 
 
 def cpu_baseline(w, inp, seconds):
@@ -86,9 +153,16 @@ def cpu_baseline(w, inp, seconds):
     t0 = max(run(n0) - t_route, 1e-3)     # per-token FFN cost from n0 tokens
     n = int(min(w.T, max(n0, n0 * (seconds - t_route) / t0)))
     t = run(n)
-    return {"value": n / t, "unit": "tokens/s", "cores": cores, "kind": "oracle",
-            "sample": f"first {n} of {w.T} tokens of {w.name} (routing of all {w.T} tokens, "
-                      f"expert FFN + combine of the {n}), {t:.1f} s wall"}
+    reps = 1
+    if n == w.T:                          # the whole workload fits: repeat it
+        while t < seconds:
+            t += run(n)
+            reps += 1
+    what = (f"all {w.T} tokens of {w.name} (full layer), {reps} passes" if n == w.T else
+            f"first {n} of {w.T} tokens of {w.name} (routing of all {w.T} tokens, "
+            f"expert FFN + combine of the {n})")
+    return {"value": n * reps / t, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sample": f"{what}, {t:.1f} s wall"}
 
 
 def main():
@@ -102,7 +176,16 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-stages", action="store_true")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB")
+    ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
+    ap.add_argument("--traffic-out", default=None)
     args = ap.parse_args()
+
+    if args.traffic_from:
+        traffic_summary(args.traffic_from[0], args.traffic_from[1], args.workload,
+                        args.copy_calibration or 256,
+                        args.traffic_out or traffic_path(args.workload))
+        return
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -144,28 +227,47 @@ def main():
     kept_rows = int(kept.sum())
     active = int((kept > 0).sum())
 
+    hip = _hip()
+
+    def new_events(n):
+        evs = []
+        for _ in range(n):
+            e = ctypes.c_void_p()
+            assert hip.hipEventCreate(ctypes.byref(e)) == 0
+            evs.append(e.value)
+        return evs
+
+    def elapsed_us(a, b):
+        f = ctypes.c_float()
+        assert hip.hipEventElapsedTime(ctypes.byref(f), a, b) == 0
+        return f.value * 1e3
+
+    # timed region: K steps, GEMM 1 bracketed by hipEvents on the library's
+    # stream in every step (the other stage boundaries are not marked here)
+    K = args.steps
+    g1_ev = new_events(2 * K)
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for i in range(args.steps):
-        step(i)
+    for i in range(K):
+        p = sets[i % nsets]
+        moe.layer_forward_timed(s, p["x"], p["w_router"], p["b_router"], p["w_gate"], p["w_up"],
+                                p["w_down"], p["ws_gate"], p["ws_up"], p["ws_down"], y, ws,
+                                [None, None, g1_ev[2 * i], g1_ev[2 * i + 1], None, None, None],
+                                stream=stream)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
-    ms = (t1 - t0) * 1e3 / args.steps
+    ms = (t1 - t0) * 1e3 / K
     value = w.T / (ms / 1e3)
+    g1_us = sum(elapsed_us(g1_ev[2 * i], g1_ev[2 * i + 1]) for i in range(K)) / K
+    for e in g1_ev:
+        hip.hipEventDestroy(e)
 
-    # per-stage times with hipEvents on the library's stream
+    # per-stage times: a second pass with every stage boundary marked
     stages = None
-    g1_us = None
     if not args.no_stages:
-        hip = _hip()
-        K = args.steps
-        evs = []
-        for _ in range(K * 7):
-            e = ctypes.c_void_p()
-            assert hip.hipEventCreate(ctypes.byref(e)) == 0
-            evs.append(e.value)
+        evs = new_events(K * 7)
         torch.cuda.synchronize()
         for i in range(K):
             p = sets[i % nsets]
@@ -174,18 +276,25 @@ def main():
                                     p["ws_down"], y, ws, evs[7 * i:7 * i + 7], stream=stream)
         torch.cuda.synchronize()
         acc = [0.0] * 6
-        f = ctypes.c_float()
         for i in range(K):
             for j in range(6):
-                assert hip.hipEventElapsedTime(ctypes.byref(f), evs[7 * i + j], evs[7 * i + j + 1]) == 0
-                acc[j] += f.value * 1e3
+                acc[j] += elapsed_us(evs[7 * i + j], evs[7 * i + j + 1])
         for e in evs:
             hip.hipEventDestroy(e)
         stages = {n: round(a / K, 2) for n, a in zip(STAGES, acc)}
-        g1_us = acc[2] / K
+
+    if args.copy_calibration:
+        n = args.copy_calibration << 20
+        src = torch.ones(n, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        for _ in range(N_CAL):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     roof = None
-    if g1_us:
+    if g1_us > 0:
         flops, byts = gemm1_model(w, kept_rows, active)
         peak_c = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_F32_TFLOPS
         t_c = flops / (peak_c * 1e12)
