@@ -36,7 +36,7 @@ struct GemmArgs {
   void* C;            // [rows][N] in dtype, or fp32 partial planes [splits][R_max][N]
   long split_stride;  // elements between partial planes
   int n_tiles;        // column tiles
-  int m_tiles;        // row tiles (an upper bound; tiles past the last group exit)
+  int m_tiles;        // row tiles (an upper bound, host side; the kernel counts the real ones)
   int splits;         // K splits (partial-plane output when > 1)
   int k_chunk;        // K elements per split, a multiple of 64
   unsigned a_bytes;   // extent of A in bytes (< 2^31; buffer range of the activation loads)
@@ -87,26 +87,52 @@ __device__ __forceinline__ void find_row_tile(const GemmArgs& a, int mt, int lan
   }
 }
 
-// Block -> (row tile, column tile, K split).  Workgroups are dispatched
-// round-robin over the 8 XCDs (each with its own L2), so consecutive logical
-// tiles are first gathered per XCD; tiles are then walked in groups of
-// GM row tiles, column tile slowest inside a group, so the workgroups that
-// run together on one XCD share both their weight and activation tiles.
-__device__ __forceinline__ void tile_of_block(const GemmArgs& a, int& mt, int& nt, int& ks) {
+// Row tiles of size BM over all groups, from the device offsets (every lane
+// of the calling wave gets the total).
+template <int BM>
+__device__ __forceinline__ int count_row_tiles(const GemmArgs& a, int lane) {
+  if (a.offsets == nullptr) return (a.M_dense + BM - 1) / BM;
+  int total = 0;
+  for (int e0 = 0; e0 < a.E; e0 += kWave) {
+    const int e = e0 + lane;
+    int t = 0;
+    if (e < a.E) t = (a.offsets[e + 1] - a.offsets[e] + BM - 1) / BM;
+#pragma unroll
+    for (int s = kWave / 2; s >= 1; s >>= 1) t += __shfl_xor(t, s, kWave);
+    total += t;
+  }
+  return total;
+}
+
+// Block -> (row tile, column tile, K split) over the tiles that exist.  The
+// grid is an upper bound (a multiple of 8) on the tile count; the real count
+// comes from the device offsets.  Workgroups are dispatched round-robin over
+// the 8 XCDs (each with its own L2), so XCD x takes the x-th contiguous
+// eighth of the real tiles -- the work is spread evenly whatever the routing
+// -- and blocks past its share exit.  Inside a share, tiles are walked in
+// groups of GM row tiles, column tile slowest inside a group, so the
+// workgroups that run together on one XCD share their weight and activation
+// tiles.  Returns false for a block with no tile.
+__device__ __forceinline__ bool tile_of_block(const GemmArgs& a, int m_real, int& mt, int& nt,
+                                              int& ks) {
   constexpr int NXCD = 8, GM = 8;
-  const int nb = gridDim.x, bid = blockIdx.x;
+  const int bid = blockIdx.x;
   const int xcd = bid % NXCD, local = bid / NXCD;
-  const int per = nb / NXCD, rem = nb % NXCD;
-  int l = (xcd < rem ? xcd * (per + 1) : rem * (per + 1) + (xcd - rem) * per) + local;
-  const int tiles = a.m_tiles * a.n_tiles;
+  const int tiles = m_real * a.n_tiles;
+  const int n_real = tiles * a.splits;
+  const int chunk = (n_real + NXCD - 1) / NXCD;
+  if (local >= chunk) return false;
+  int l = xcd * chunk + local;
+  if (l >= n_real) return false;
   ks = l / tiles;
   l -= ks * tiles;
   const int group = l / (GM * a.n_tiles);
   const int first = group * GM;
-  const int gsize = min(GM, a.m_tiles - first);
+  const int gsize = min(GM, m_real - first);
   const int within = l - group * GM * a.n_tiles;
   mt = first + within % gsize;
   nt = within / gsize;
+  return true;
 }
 
 // ---------------------------------------------------------------------------
@@ -140,18 +166,29 @@ __device__ __forceinline__ void tile_of_block(const GemmArgs& a, int& mt, int& n
 // rows; the epilogue writes SiLU(gate) * up.  PARTIAL: fp32 output into the
 // K split's partial plane (summed later in a fixed order).
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ int swz(int r) { return ((r >> 1) ^ (r >> 3)) & 3; }
+// CH = 4 (64-byte rows): f(r) = (r ^ (r >> 2)) & 3, measured free of bank
+// conflicts for the fragment reads below (the variant ((r >> 1) ^ (r >> 3))
+// & 3 costs one conflict cycle per access cycle on gfx950).
+// CH = 8 (128-byte rows): a 3-bit f that is a bijection on the low three
+// row bits for any aligned 8 rows and on bits 1..3 for each row parity in
+// any aligned 16 rows (also measured conflict-free).
+template <int CH>
+__device__ __forceinline__ int swz(int r) {
+  if constexpr (CH == 4) return (r ^ (r >> 2)) & 3;
+  return ((((r >> 2) ^ (r >> 3)) & 1) << 2) | (r & 2) | ((r ^ (r >> 3)) & 1);
+}
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 constexpr int kBufFlags = 0x00020000;  // raw buffer, 32-bit data format
 
-template <int BM, int BNW, int WM, int WN, bool SWIGLU, bool GATHER, bool PARTIAL>
-__global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmArgs a) {
+template <int BM, int BNW, int WM, int WN, int BK, int NS, int OCC, bool SWIGLU, bool GATHER,
+          bool PARTIAL>
+__global__ __launch_bounds__(256, OCC) void gemm_bf16_kernel(GemmArgs a) {
 #if defined(__HIP_DEVICE_COMPILE__)  // the host pass only emits the launch stub
-  constexpr int BK = 32;
+  // BK: K elements per stage (32 or 64); NS: ring slots (2, 3 or 4); OCC:
+  // waves per SIMD the register budget must allow (2 = two workgroups per CU)
   constexpr int CH = BK / 8;       // 16-byte chunks per row
   constexpr int RPS = 64 / CH;     // rows per 1 KB wave-level load
-  constexpr int NS = 4;            // ring slots
   constexpr int NREG = SWIGLU ? 2 : 1;
   constexpr int BNO = BNW / NREG;  // output columns per block
   constexpr int WTM = BM / WM, WTN = BNO / WN;
@@ -164,12 +201,13 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmArgs a) {
   static_assert(TM >= 1 && TN >= 1 && XS >= 1 && WS >= 1, "tile shape");
   static_assert(!(SWIGLU && PARTIAL), "SwiGLU needs the full K sum");
   static_assert(PER * (NS - 1) < 64, "vmcnt range");
+  static_assert((BK == 32 || BK == 64) && NS >= 2 && NS <= 4, "pipeline shape");
 
   __shared__ __attribute__((aligned(1024))) u32x4_t st0[STAGE];
   __shared__ __attribute__((aligned(1024))) u32x4_t st1[STAGE];
-  __shared__ __attribute__((aligned(1024))) u32x4_t st2[STAGE];
-  __shared__ __attribute__((aligned(1024))) u32x4_t st3[STAGE];
-  __shared__ int s_info[3];
+  __shared__ __attribute__((aligned(1024))) u32x4_t st2[NS > 2 ? STAGE : 1];  // NS >= 3
+  __shared__ __attribute__((aligned(1024))) u32x4_t st3[NS > 2 ? STAGE : 1];
+  __shared__ int s_info[5];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -178,15 +216,25 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmArgs a) {
   // feed buffer descriptors and LDS load destinations, which must be scalar
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave / WN, wn = wave % WN;
-  int mt, nt, ks;
-  tile_of_block(a, mt, nt, ks);
-
-  if (wave == 0) find_row_tile<BM>(a, mt, lane, s_info);
+  if (wave == 0) {
+    int mt0 = 0, nt0 = 0, ks0 = 0;
+    if (tile_of_block(a, count_row_tiles<BM>(a, lane), mt0, nt0, ks0)) {
+      find_row_tile<BM>(a, mt0, lane, s_info);
+      if (lane == 0) {
+        s_info[3] = nt0;
+        s_info[4] = ks0;
+      }
+    } else if (lane == 0) {
+      s_info[0] = -1;
+    }
+  }
   __syncthreads();
   const int e = __builtin_amdgcn_readfirstlane(s_info[0]);
   if (e < 0) return;
   const int row0 = __builtin_amdgcn_readfirstlane(s_info[1]);
   const int rows = __builtin_amdgcn_readfirstlane(s_info[2]);
+  const int nt = __builtin_amdgcn_readfirstlane(s_info[3]);
+  const int ks = __builtin_amdgcn_readfirstlane(s_info[4]);
   const int K = a.K, N = a.N;
   const int kb = ks * a.k_chunk;
   const int klen = min(K, kb + a.k_chunk) - kb;
@@ -212,7 +260,7 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmArgs a) {
 #pragma unroll
   for (int q = 0; q < XS; ++q) {
     const int r = (wave * XS + q) * RPS + lane / CH;
-    xc[q] = (lane % CH) ^ swz(r);
+    xc[q] = (lane % CH) ^ swz<CH>(r);
     const int p = row0 + (r < rows ? r : rows - 1);
     const int src = GATHER ? a.a_rows[p] : p;
     xo[q] = ((unsigned)src * (unsigned)K + (unsigned)(kb + xc[q] * 8)) * 2u;
@@ -222,7 +270,7 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmArgs a) {
 #pragma unroll
   for (int q = 0; q < WS; ++q) {
     const int r = (wave * WS + q) * RPS + lane / CH;
-    wc[q] = (lane % CH) ^ swz(r);
+    wc[q] = (lane % CH) ^ swz<CH>(r);
     int n = nt * BNO + (r % BNO);
     n = n < N ? n : N - 1;
     wo[q] = ((unsigned)n * (unsigned)K + (unsigned)(kb + wc[q] * 8)) * 2u;
@@ -266,65 +314,143 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmArgs a) {
   // the rest is a compile-time displacement.
   const int lrow = lane & 31;
   const int lk = lane >> 5;
-  int xoff[2], woff[2];
+  constexpr int KS = BK / 16;  // 16-wide MFMA k steps per stage
+  int xoff[KS], woff[KS];
 #pragma unroll
-  for (int kk = 0; kk < 2; ++kk) {
-    const int chunk = ((kk * 2 + lk) ^ swz(lrow)) * 16;
+  for (int kk = 0; kk < KS; ++kk) {
+    const int chunk = ((kk * 2 + lk) ^ swz<CH>(lrow)) * 16;
     xoff[kk] = (wm * WTM + lrow) * CH * 16 + chunk;
     woff[kk] = BM * CH * 16 + (wn * WTN + lrow) * CH * 16 + chunk;
   }
-  auto compute = [&](const u32x4_t* stg) {
+  // Fragments of one 16-wide k step, double-buffered in registers: the
+  // reads of step kk+1 are issued before the MFMAs of step kk, so the LDS
+  // latency hides behind them.
+  struct Frag {
+    bf16x8_t bx[TM];
+    bf16x8_t aw[NREG][TN];
+  };
+  auto read_frags = [&](const u32x4_t* stg, int kk, Frag& F) {
     // opaque copies: keeps the compiler from hoisting one set of addresses
-    // per ring slot out of the loop (which would not fit in registers)
-    int xo0 = xoff[0], xo1 = xoff[1], wo0 = woff[0], wo1 = woff[1];
-    asm volatile("" : "+v"(xo0), "+v"(xo1), "+v"(wo0), "+v"(wo1));
+    // per (ring slot, k step) out of the loop (which would not fit in
+    // registers)
+    int xo = xoff[kk], wo = woff[kk];
+    asm volatile("" : "+v"(xo), "+v"(wo));
     const char* base = reinterpret_cast<const char*>(stg);
 #pragma unroll
-    for (int kk = 0; kk < BK / 16; ++kk) {
-      const int xo = kk ? xo1 : xo0;
-      const int wo = kk ? wo1 : wo0;
-      bf16x8_t bx[TM];
+    for (int i = 0; i < TM; ++i)
+      F.bx[i] = *reinterpret_cast<const bf16x8_t*>(base + xo + i * 32 * CH * 16);
 #pragma unroll
-      for (int i = 0; i < TM; ++i)
-        bx[i] = *reinterpret_cast<const bf16x8_t*>(base + xo + i * 32 * CH * 16);
+    for (int g = 0; g < NREG; ++g)
 #pragma unroll
-      for (int g = 0; g < NREG; ++g) {
+      for (int j = 0; j < TN; ++j)
+        F.aw[g][j] = *reinterpret_cast<const bf16x8_t*>(base + wo + (g * BNO + j * 32) * CH * 16);
+  };
+  auto mma = [&](const Frag& F) {
 #pragma unroll
-        for (int j = 0; j < TN; ++j) {
-          const bf16x8_t aw =
-              *reinterpret_cast<const bf16x8_t*>(base + wo + (g * BNO + j * 32) * CH * 16);
+    for (int g = 0; g < NREG; ++g)
 #pragma unroll
-          for (int i = 0; i < TM; ++i)
-            acc[g][j][i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aw, bx[i], acc[g][j][i], 0, 0, 0);
-        }
-      }
-    }
+      for (int j = 0; j < TN; ++j)
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+          acc[g][j][i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(F.aw[g][j], F.bx[i], acc[g][j][i], 0, 0, 0);
   };
 
   // Stage count padded to a multiple of the ring size; stages past K (the
-  // padding, and the refills issued during the last three stages) read
-  // zeros -- every chunk offset is past the buffer -- so the loop body is
-  // four straight-line steps and every refill is unconditional.  (A
-  // conditional refill makes the compiler wait for all loads in flight
-  // before the next LDS read, which would serialise the ring.)
+  // padding, and the refills issued during the last stages) read zeros --
+  // every chunk offset is past the buffer -- so the loop body is straight
+  // line and every refill is unconditional.  (A conditional refill makes
+  // the compiler wait for all loads in flight before the next LDS read,
+  // which would serialise the ring.)
   const int nk = ((klen + BK - 1) / BK + NS - 1) / NS * NS;
-  constexpr int WAIT = 0x0F70 | ((2 * PER) & 15) | (((2 * PER) >> 4) << 14);  // vmcnt(2*PER)
-  // stage kt: wait until only this wave's loads of stages kt+1, kt+2 are in
-  // flight, barrier, refill the slot stage kt-1 used with stage kt+3, compute
-  auto step = [&](u32x4_t* cur, u32x4_t* refill, int kt) {
+  // Entering stage kt: wait until only this wave's loads of stages kt+1 ..
+  // kt+NS-2 are in flight and its LDS reads have returned, barrier (every
+  // wave's loads of stage kt have landed, and every wave has read all it
+  // needs of stage kt-1), refill the slot of stage kt-1 with stage kt+NS-1.
+  constexpr int VM = (NS - 2) * PER;
+  constexpr int WAIT = 0x0070 | (VM & 15) | ((VM >> 4) << 14);  // vmcnt(VM) lgkmcnt(0)
+  Frag F0, F1;
+  // one stage: k steps 0 .. KS-2 read the next step's fragments first; the
+  // last step moves to the next stage (slot nxt) before its MFMAs, which
+  // only need registers
+  // Instruction order (the scheduler otherwise sinks each LDS read to its
+  // first use, which exposes the LDS latency on every k step): one LDS
+  // read of the next step per MFMA of the current one, and after a barrier
+  // one refill load per MFMA as well.
+  constexpr int NDS = TM + NREG * TN;  // LDS reads per k step
+  constexpr int NMF = NREG * TN * TM;  // MFMAs per k step
+  auto order_kstep = [&]() {
+#pragma unroll
+    for (int u = 0; u < NMF; ++u) {
+      if (u < NDS) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);               // MFMA
+    }
+  };
+  auto order_transition = [&]() {
+#pragma unroll
+    for (int u = 0; u < (NMF > PER ? NMF : PER); ++u) {
+      if (u < PER) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // global load
+      if (u < NDS) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read
+      if (u < NMF) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+    }
+  };
+  auto stage = [&](u32x4_t* cur, const u32x4_t* nxt, int kt) {
+#pragma unroll
+    for (int kk = 0; kk < KS - 1; ++kk) {
+      if (kk % 2 == 0) {
+        read_frags(cur, kk + 1, F1);
+        mma(F0);
+      } else {
+        read_frags(cur, kk + 1, F0);
+        mma(F1);
+      }
+      order_kstep();
+    }
     __builtin_amdgcn_s_waitcnt(WAIT);
     __builtin_amdgcn_s_barrier();
-    issue(refill, kt + NS - 1);
-    compute(cur);
+    issue(cur, kt + NS);
+    // KS is even: the last step used F1, the next stage starts in F0
+    read_frags(nxt, 0, F0);
+    mma(F1);
+    order_transition();
   };
-  issue(st0, 0);
-  issue(st1, 1);
-  issue(st2, 2);
-  for (int kt = 0; kt < nk; kt += NS) {
-    step(st0, st3, kt);
-    step(st1, st0, kt + 1);
-    step(st2, st1, kt + 2);
-    step(st3, st2, kt + 3);
+  static_assert(BK / 16 % 2 == 0, "even number of k steps per stage");
+  constexpr int WAIT0 = 0x0F70 | (VM & 15) | ((VM >> 4) << 14);
+  if constexpr (NS == 4) {
+    issue(st0, 0);
+    issue(st1, 1);
+    issue(st2, 2);
+    __builtin_amdgcn_s_waitcnt(WAIT0);
+    __builtin_amdgcn_s_barrier();
+    issue(st3, 3);
+    read_frags(st0, 0, F0);
+    for (int kt = 0; kt < nk; kt += NS) {
+      stage(st0, st1, kt);
+      stage(st1, st2, kt + 1);
+      stage(st2, st3, kt + 2);
+      stage(st3, st0, kt + 3);
+    }
+  } else if constexpr (NS == 3) {
+    issue(st0, 0);
+    issue(st1, 1);
+    __builtin_amdgcn_s_waitcnt(WAIT0);
+    __builtin_amdgcn_s_barrier();
+    issue(st2, 2);
+    read_frags(st0, 0, F0);
+    for (int kt = 0; kt < nk; kt += NS) {
+      stage(st0, st1, kt);
+      stage(st1, st2, kt + 1);
+      stage(st2, st0, kt + 2);
+    }
+  } else {
+    issue(st0, 0);
+    __builtin_amdgcn_s_waitcnt(WAIT0);
+    __builtin_amdgcn_s_barrier();
+    issue(st1, 1);
+    read_frags(st0, 0, F0);
+    for (int kt = 0; kt < nk; kt += NS) {
+      stage(st0, st1, kt);
+      stage(st1, st0, kt + 1);
+    }
   }
   // the zero-reading refills past the end must land before the workgroup's
   // LDS is released
@@ -432,18 +558,19 @@ static TileCfg tile_cfg(const GemmPlan& pl, int N, bool swiglu) {
 }
 static int cfg_bm(TileCfg c) { return c == TILE_L ? 256 : c == TILE_M ? 128 : 64; }
 
-template <int BM, int BNW, int WM, int WN, bool SWIGLU, bool PARTIAL>
+template <int BM, int BNW, int WM, int WN, int BK, int NS, int OCC, bool SWIGLU, bool PARTIAL>
 static hipError_t run_bf16(const GemmPlan& pl, GemmArgs a, hipStream_t st) {
   constexpr int BNO = SWIGLU ? BNW / 2 : BNW;
   a.n_tiles = (a.N + BNO - 1) / BNO;
   a.m_tiles = (int)row_tile_bound(pl, BM);
-  const long blocks = (long)a.m_tiles * a.n_tiles * a.splits;
+  // an upper bound on the tiles, rounded up to whole rounds of the 8 XCDs
+  const long blocks = ((long)a.m_tiles * a.n_tiles * a.splits + 7) / 8 * 8;
   if (blocks == 0) return hipSuccess;
   if (a.a_rows)
-    hipLaunchKernelGGL((gemm_bf16_kernel<BM, BNW, WM, WN, SWIGLU, true, PARTIAL>),
+    hipLaunchKernelGGL((gemm_bf16_kernel<BM, BNW, WM, WN, BK, NS, OCC, SWIGLU, true, PARTIAL>),
                        dim3((unsigned)blocks), dim3(256), 0, st, a);
   else
-    hipLaunchKernelGGL((gemm_bf16_kernel<BM, BNW, WM, WN, SWIGLU, false, PARTIAL>),
+    hipLaunchKernelGGL((gemm_bf16_kernel<BM, BNW, WM, WN, BK, NS, OCC, SWIGLU, false, PARTIAL>),
                        dim3((unsigned)blocks), dim3(256), 0, st, a);
   return hipGetLastError();
 }
@@ -451,9 +578,9 @@ static hipError_t run_bf16(const GemmPlan& pl, GemmArgs a, hipStream_t st) {
 template <bool SWIGLU, bool PARTIAL>
 static hipError_t run_cfg(const GemmPlan& pl, GemmArgs a, hipStream_t st) {
   switch (tile_cfg(pl, a.N, SWIGLU)) {
-    case TILE_L: return run_bf16<256, 256, 2, 2, SWIGLU, PARTIAL>(pl, a, st);
-    case TILE_M: return run_bf16<128, 256, 2, 2, SWIGLU, PARTIAL>(pl, a, st);
-    default: return run_bf16<64, 256, 1, 4, SWIGLU, PARTIAL>(pl, a, st);
+    case TILE_L: return run_bf16<256, 256, 2, 2, 64, 2, 1, SWIGLU, PARTIAL>(pl, a, st);
+    case TILE_M: return run_bf16<128, 256, 2, 2, 32, 3, 2, SWIGLU, PARTIAL>(pl, a, st);
+    default: return run_bf16<64, 256, 1, 4, 64, 3, 1, SWIGLU, PARTIAL>(pl, a, st);
   }
 }
 
