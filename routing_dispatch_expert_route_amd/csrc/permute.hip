@@ -162,6 +162,99 @@ __global__ __launch_bounds__(64) void scatter_kernel(const int32_t* __restrict__
   }
 }
 
+// Whole permute in one workgroup of 1024 threads (16 waves), for route counts
+// small enough that one CU finishes them faster than three dependent
+// launches: histogram by LDS atomics, capacity and the exclusive prefix by
+// one wave, then the routes in chunks of 1024 in route order -- the rank of
+// a route is the running count of its expert before the chunk, plus the
+// routes of the same expert in earlier waves of the chunk, plus its rank
+// among the lanes of its own wave (ballots).  Same result as the chunked
+// kernels above, bit for bit.
+constexpr int kSmallThreads = 1024;
+constexpr int kSmallWaves = kSmallThreads / kWave;
+constexpr long kSmallMaxRoutes = 4096;
+
+__global__ __launch_bounds__(kSmallThreads) void permute_small_kernel(
+    const int32_t* __restrict__ ids, int R, int k, int E, int C, int32_t* __restrict__ counts,
+    int32_t* __restrict__ kept, int32_t* __restrict__ offsets, int32_t* __restrict__ route_pos,
+    int32_t* __restrict__ row_token) {
+  __shared__ int s_cnt[256];
+  __shared__ int s_off[256];
+  __shared__ int s_run[256];
+  __shared__ int s_w[kSmallWaves][256];  // per-wave counts of the chunk, then their prefix
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int wave = tid / kWave;
+  for (int e = tid; e < E; e += kSmallThreads) {
+    s_cnt[e] = 0;
+    s_run[e] = 0;
+  }
+  __syncthreads();
+  for (int r = tid; r < R; r += kSmallThreads) {
+    const int e = ids[r];
+    if (e >= 0 && e < E) atomicAdd(&s_cnt[e], 1);
+  }
+  __syncthreads();
+  if (wave == 0) {
+    int carry = 0;
+    if (lane == 0) offsets[0] = 0;
+    for (int e0 = 0; e0 < E; e0 += kWave) {
+      const int e = e0 + lane;
+      const int n = e < E ? s_cnt[e] : 0;
+      const int m = (C < 0 || n <= C) ? n : C;
+      const int incl = wave_incl_scan(m, lane);
+      if (e < E) {
+        counts[e] = n;
+        kept[e] = m;
+        s_off[e] = carry + incl - m;
+        offsets[e + 1] = carry + incl;
+      }
+      carry += __shfl(incl, kWave - 1, kWave);
+    }
+  }
+  const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (kWave - lane));
+  for (int base = 0; base < R; base += kSmallThreads) {
+    for (int e = lane; e < E; e += kWave) s_w[wave][e] = 0;
+    const int r = base + tid;
+    const int e = r < R ? ids[r] : -1;
+    const bool valid = r < R && e >= 0 && e < E;
+    uint64_t m = __ballot(valid);
+#pragma unroll
+    for (int bit = 0; bit < 8; ++bit) {
+      const bool on = (e >> bit) & 1;
+      const uint64_t bb = __ballot(on);
+      m &= on ? bb : ~bb;
+    }
+    const int rank = __popcll(m & lt_mask);
+    __syncthreads();  // s_w cleared (and s_off written, first chunk)
+    // the first lane of each expert group records the group's size
+    if (valid && rank == 0) s_w[wave][e] = __popcll(m);
+    __syncthreads();
+    // per expert: exclusive prefix over the waves, and the running count
+    for (int x = tid; x < E; x += kSmallThreads) {
+      int acc = s_run[x];
+      for (int w = 0; w < kSmallWaves; ++w) {
+        const int c = s_w[w][x];
+        s_w[w][x] = acc;
+        acc += c;
+      }
+      s_run[x] = acc;
+    }
+    __syncthreads();
+    if (r < R) {
+      const int slot = valid ? s_w[wave][e] + rank : 0;
+      if (valid && (C < 0 || slot < C)) {
+        const int p = s_off[e] + slot;
+        route_pos[r] = p;
+        row_token[p] = r / k;
+      } else {
+        route_pos[r] = -1;
+      }
+    }
+    __syncthreads();  // s_w is reused by the next chunk
+  }
+}
+
 // x_packed[p][:] = x[row_token[p]][:] for p < offsets[E]; 16-byte chunks.
 __global__ __launch_bounds__(256) void gather_rows_kernel(const u32x4_t* __restrict__ x,
                                                           const int32_t* __restrict__ row_token,
@@ -184,6 +277,11 @@ hipError_t launch_permute_index(const int32_t* ids, int T, int k, int E, int C, 
                                 int32_t* counts, int32_t* kept, int32_t* offsets,
                                 int32_t* route_pos, int32_t* row_token, hipStream_t st) {
   const int R = T * k;
+  if (R <= kSmallMaxRoutes) {
+    hipLaunchKernelGGL(permute_small_kernel, dim3(1), dim3(kSmallThreads), 0, st, ids, R, k, E, C,
+                       counts, kept, offsets, route_pos, row_token);
+    return hipGetLastError();
+  }
   const int nch = permute_nchunks(R);
   if (nch > 0) {
     hipLaunchKernelGGL(hist_kernel, dim3(nch), dim3(kWave), 0, st, ids, R, E, nch, cnt_ws);
