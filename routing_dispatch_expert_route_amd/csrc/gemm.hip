@@ -207,7 +207,9 @@ __global__ __launch_bounds__(256, OCC) void gemm_bf16_kernel(GemmArgs a) {
   __shared__ __attribute__((aligned(1024))) u32x4_t st1[STAGE];
   __shared__ __attribute__((aligned(1024))) u32x4_t st2[NS > 2 ? STAGE : 1];  // NS >= 3
   __shared__ __attribute__((aligned(1024))) u32x4_t st3[NS > 2 ? STAGE : 1];
-  __shared__ int s_info[5];
+  // the tile found by wave 0 is passed through the first ring slot, before
+  // any load into it (a barrier separates the reads from the first refill)
+  int* s_info = reinterpret_cast<int*>(st0);
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -235,6 +237,7 @@ __global__ __launch_bounds__(256, OCC) void gemm_bf16_kernel(GemmArgs a) {
   const int rows = __builtin_amdgcn_readfirstlane(s_info[2]);
   const int nt = __builtin_amdgcn_readfirstlane(s_info[3]);
   const int ks = __builtin_amdgcn_readfirstlane(s_info[4]);
+  __syncthreads();  // every wave has its tile before st0 is refilled
   const int K = a.K, N = a.N;
   const int kb = ks * a.k_chunk;
   const int klen = min(K, kb + a.k_chunk) - kb;
@@ -541,19 +544,28 @@ static long row_tile_bound(const GemmPlan& pl, int BM) {
   return by_rows < by_cap ? by_rows : by_cap;
 }
 
-// Tile shape: the largest row tile that still gives every CU work.  Tile
-// counts are estimated from the row bound (each group wastes half a tile on
-// average): 256-row tiles (128x128 per wave) when there are at least two
-// per CU, else 128-row tiles when there is at least one, else 64.
+// Tile shape, from the shape alone (the routing is not known on the host;
+// the row counts are bounded by R_max).  Measured on MI355X:
+//   L  256-row tiles, one workgroup per CU: best when K is long and every
+//      group has many rows (the K loop amortises the pipeline fill);
+//   M  128-row tiles, two per CU: the default;
+//   S  64-row tiles: fewer idle slots in the last round for small problems
+//      (the down projection below about two rounds of 128-row tiles, the
+//      gate/up projection only for a few hundred rows in all).
+// Tile counts are estimated from the row bound (each group wastes half a
+// tile on average).
 enum TileCfg { TILE_L, TILE_M, TILE_S };
 static long est_tiles(const GemmPlan& pl, int bm, int bno, int N) {
   const long mt = pl.grouped ? pl.R_max / bm + (pl.E + 1) / 2 : (pl.M_dense + bm - 1) / bm;
   return mt * ((N + bno - 1) / bno);
 }
-static TileCfg tile_cfg(const GemmPlan& pl, int N, bool swiglu) {
+static TileCfg tile_cfg(const GemmPlan& pl, int N, int K, bool swiglu) {
   const int bno = swiglu ? 128 : 256;
-  if (est_tiles(pl, 256, bno, N) >= 512) return TILE_L;
-  if (est_tiles(pl, 128, bno, N) >= 256) return TILE_M;
+  const long per_group = pl.grouped ? pl.R_max / (pl.E > 0 ? pl.E : 1) : pl.M_dense;
+  if (K >= 2048 && per_group >= 1024 && est_tiles(pl, 256, bno, N) >= 256) return TILE_L;
+  // GEMM 1 keeps 128-row tiles unless the rows are very few (decode); the
+  // down projection takes 64-row tiles below about two rounds
+  if (est_tiles(pl, 128, bno, N) > (swiglu ? 256 : 1024)) return TILE_M;
   return TILE_S;
 }
 static int cfg_bm(TileCfg c) { return c == TILE_L ? 256 : c == TILE_M ? 128 : 64; }
@@ -577,10 +589,14 @@ static hipError_t run_bf16(const GemmPlan& pl, GemmArgs a, hipStream_t st) {
 
 template <bool SWIGLU, bool PARTIAL>
 static hipError_t run_cfg(const GemmPlan& pl, GemmArgs a, hipStream_t st) {
-  switch (tile_cfg(pl, a.N, SWIGLU)) {
+  switch (tile_cfg(pl, a.N, a.K, SWIGLU)) {
     case TILE_L: return run_bf16<256, 256, 2, 2, 64, 2, 1, SWIGLU, PARTIAL>(pl, a, st);
     case TILE_M: return run_bf16<128, 256, 2, 2, 32, 3, 2, SWIGLU, PARTIAL>(pl, a, st);
-    default: return run_bf16<64, 256, 1, 4, 64, 3, 1, SWIGLU, PARTIAL>(pl, a, st);
+    default:
+      // a long K loop per tile wants the deeper ring; short ones two
+      // workgroups per CU
+      if (!SWIGLU && a.k_chunk >= 2048) return run_bf16<64, 256, 1, 4, 64, 3, 1, SWIGLU, PARTIAL>(pl, a, st);
+      return run_bf16<64, 256, 1, 4, 64, 2, 2, SWIGLU, PARTIAL>(pl, a, st);
   }
 }
 
@@ -599,7 +615,7 @@ static hipError_t run_f32(const GemmPlan& pl, GemmArgs a, hipStream_t st) {
 
 int gemm_down_splits(const GemmPlan& pl, int N, int K) {
   if (!pl.bf16) return 1;
-  const TileCfg c = tile_cfg(pl, N, false);
+  const TileCfg c = tile_cfg(pl, N, K, false);
   const int bm = cfg_bm(c);
   const long mt = pl.grouped ? (pl.R_max + bm - 1) / bm + (pl.E + 1) / 2
                              : (pl.M_dense + bm - 1) / bm;
