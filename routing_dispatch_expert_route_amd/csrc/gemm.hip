@@ -18,6 +18,8 @@
 //
 // GEMM 1 can read its A rows through an index (a_rows[p] = source token), so
 // the whole-layer path never materialises the packed copy of x.
+#include <type_traits>
+
 #include "common.h"
 #include "launch.h"
 
@@ -178,15 +180,34 @@ __device__ __forceinline__ int swz(int r) {
   return ((((r >> 2) ^ (r >> 3)) & 1) << 2) | (r & 2) | ((r ^ (r >> 3)) & 1);
 }
 
+// Calls f(integral_constant<int, I>) for I = B .. E-1 (compile-time unrolled).
+template <int B, int E, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (B < E) {
+    f(std::integral_constant<int, B>{});
+    static_for<B + 1, E>(f);
+  }
+}
+
+// LDS ring slot TAG of SIZE 16-byte units: one distinct LDS object per
+// (TAG, SIZE), allocated in the kernels that use it.
+template <int TAG, int SIZE>
+__device__ __forceinline__ u32x4_t* lds_slot() {
+  __shared__ __attribute__((aligned(1024))) u32x4_t buf[SIZE];
+  return buf;
+}
+
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 constexpr int kBufFlags = 0x00020000;  // raw buffer, 32-bit data format
 
-template <int BM, int BNW, int WM, int WN, int BK, int NS, int OCC, bool SWIGLU, bool GATHER,
-          bool PARTIAL>
+template <int BM, int BNW, int WM, int WN, int BK, int NSX, int NSW, int OCC, bool SWIGLU,
+          bool GATHER, bool PARTIAL>
 __global__ __launch_bounds__(256, OCC) void gemm_bf16_kernel(GemmArgs a) {
 #if defined(__HIP_DEVICE_COMPILE__)  // the host pass only emits the launch stub
-  // BK: K elements per stage (32 or 64); NS: ring slots (2, 3 or 4); OCC:
-  // waves per SIMD the register budget must allow (2 = two workgroups per CU)
+  // BK: K elements per stage (32 or 64); NSX / NSW: ring slots of the
+  // activation / weight tiles (2 to 4 each, NSW >= NSX: the weights, first
+  // touched in HBM, may be fetched further ahead); OCC: waves per SIMD the
+  // register budget must allow (2 = two workgroups per CU)
   constexpr int CH = BK / 8;       // 16-byte chunks per row
   constexpr int RPS = 64 / CH;     // rows per 1 KB wave-level load
   constexpr int NREG = SWIGLU ? 2 : 1;
@@ -196,20 +217,21 @@ __global__ __launch_bounds__(256, OCC) void gemm_bf16_kernel(GemmArgs a) {
   constexpr int XS = BM / RPS / 4;   // activation loads per wave per stage
   constexpr int WS = BNW / RPS / 4;  // weight loads per wave per stage
   constexpr int PER = XS + WS;
-  constexpr int STAGE = (BM + BNW) * CH;  // 16-byte units per stage
+  constexpr int XSTAGE = BM * CH;   // 16-byte units per activation stage
+  constexpr int WSTAGE = BNW * CH;  // 16-byte units per weight stage
   static_assert(WM * WN == 4, "four waves");
   static_assert(TM >= 1 && TN >= 1 && XS >= 1 && WS >= 1, "tile shape");
   static_assert(!(SWIGLU && PARTIAL), "SwiGLU needs the full K sum");
-  static_assert(PER * (NS - 1) < 64, "vmcnt range");
-  static_assert((BK == 32 || BK == 64) && NS >= 2 && NS <= 4, "pipeline shape");
+  static_assert(XS * (NSX - 1) + WS * (NSW - 1) < 64, "vmcnt range");
+  static_assert((BK == 32 || BK == 64) && NSX >= 2 && NSX <= NSW && NSW <= 4, "pipeline shape");
 
-  __shared__ __attribute__((aligned(1024))) u32x4_t st0[STAGE];
-  __shared__ __attribute__((aligned(1024))) u32x4_t st1[STAGE];
-  __shared__ __attribute__((aligned(1024))) u32x4_t st2[NS > 2 ? STAGE : 1];  // NS >= 3
-  __shared__ __attribute__((aligned(1024))) u32x4_t st3[NS > 2 ? STAGE : 1];
+  // every ring slot is its own LDS object (only the slots in use exist), so
+  // the compiler can tell a load into one slot from a read of another
+  u32x4_t* const X0 = lds_slot<0, XSTAGE>();
+  u32x4_t* const W0 = lds_slot<4, WSTAGE>();
   // the tile found by wave 0 is passed through the first ring slot, before
   // any load into it (a barrier separates the reads from the first refill)
-  int* s_info = reinterpret_cast<int*>(st0);
+  int* s_info = reinterpret_cast<int*>(X0);
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -237,7 +259,7 @@ __global__ __launch_bounds__(256, OCC) void gemm_bf16_kernel(GemmArgs a) {
   const int rows = __builtin_amdgcn_readfirstlane(s_info[2]);
   const int nt = __builtin_amdgcn_readfirstlane(s_info[3]);
   const int ks = __builtin_amdgcn_readfirstlane(s_info[4]);
-  __syncthreads();  // every wave has its tile before st0 is refilled
+  __syncthreads();  // every wave has its tile before X0 is refilled
   const int K = a.K, N = a.N;
   const int kb = ks * a.k_chunk;
   const int klen = min(K, kb + a.k_chunk) - kb;
@@ -279,8 +301,8 @@ __global__ __launch_bounds__(256, OCC) void gemm_bf16_kernel(GemmArgs a) {
     wo[q] = ((unsigned)n * (unsigned)K + (unsigned)(kb + wc[q] * 8)) * 2u;
   }
 
-  // stage layout: BM activation rows, then BNW weight rows
-  auto issue = [&](u32x4_t* stg, int kt) {
+  // one stage of the activation tile (BM rows) / of the weight tile (BNW rows)
+  auto issue_x = [&](u32x4_t* xs, int kt) {
     const int k0 = kt * BK;
     const int soff = k0 * 2;
     const bool tail = k0 + BK > klen;  // includes padding stages past K
@@ -288,16 +310,20 @@ __global__ __launch_bounds__(256, OCC) void gemm_bf16_kernel(GemmArgs a) {
     for (int q = 0; q < XS; ++q) {
       // past-K chunk: an offset past every buffer extent reads zero
       const unsigned vo = (tail && xc[q] * 8 >= klen - k0) ? 0x80000000u : xo[q];
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (lds_ptr_t)(stg + (wave * XS + q) * 64), 16, vo,
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (lds_ptr_t)(xs + (wave * XS + q) * 64), 16, vo,
                                                soff, 0, 0);
     }
+  };
+  auto issue_w = [&](u32x4_t* wsl, int kt) {
+    const int k0 = kt * BK;
+    const int soff = k0 * 2;
+    const bool tail = k0 + BK > klen;
 #pragma unroll
     for (int q = 0; q < WS; ++q) {
       const int reg = ((wave * WS + q) * RPS) / BNO;
       const unsigned vo = (tail && wc[q] * 8 >= klen - k0) ? 0x80000000u : wo[q];
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rw[reg],
-                                               (lds_ptr_t)(stg + BM * CH + (wave * WS + q) * 64),
-                                               16, vo, soff, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rw[reg], (lds_ptr_t)(wsl + (wave * WS + q) * 64), 16,
+                                               vo, soff, 0, 0);
     }
   };
 
@@ -323,7 +349,7 @@ __global__ __launch_bounds__(256, OCC) void gemm_bf16_kernel(GemmArgs a) {
   for (int kk = 0; kk < KS; ++kk) {
     const int chunk = ((kk * 2 + lk) ^ swz<CH>(lrow)) * 16;
     xoff[kk] = (wm * WTM + lrow) * CH * 16 + chunk;
-    woff[kk] = BM * CH * 16 + (wn * WTN + lrow) * CH * 16 + chunk;
+    woff[kk] = (wn * WTN + lrow) * CH * 16 + chunk;
   }
   // Fragments of one 16-wide k step, double-buffered in registers: the
   // reads of step kk+1 are issued before the MFMAs of step kk, so the LDS
@@ -332,21 +358,22 @@ __global__ __launch_bounds__(256, OCC) void gemm_bf16_kernel(GemmArgs a) {
     bf16x8_t bx[TM];
     bf16x8_t aw[NREG][TN];
   };
-  auto read_frags = [&](const u32x4_t* stg, int kk, Frag& F) {
+  auto read_frags = [&](const u32x4_t* xs, const u32x4_t* wsl, int kk, Frag& F) {
     // opaque copies: keeps the compiler from hoisting one set of addresses
     // per (ring slot, k step) out of the loop (which would not fit in
     // registers)
     int xo = xoff[kk], wo = woff[kk];
     asm volatile("" : "+v"(xo), "+v"(wo));
-    const char* base = reinterpret_cast<const char*>(stg);
+    const char* xb = reinterpret_cast<const char*>(xs);
+    const char* wb = reinterpret_cast<const char*>(wsl);
 #pragma unroll
     for (int i = 0; i < TM; ++i)
-      F.bx[i] = *reinterpret_cast<const bf16x8_t*>(base + xo + i * 32 * CH * 16);
+      F.bx[i] = *reinterpret_cast<const bf16x8_t*>(xb + xo + i * 32 * CH * 16);
 #pragma unroll
     for (int g = 0; g < NREG; ++g)
 #pragma unroll
       for (int j = 0; j < TN; ++j)
-        F.aw[g][j] = *reinterpret_cast<const bf16x8_t*>(base + wo + (g * BNO + j * 32) * CH * 16);
+        F.aw[g][j] = *reinterpret_cast<const bf16x8_t*>(wb + wo + (g * BNO + j * 32) * CH * 16);
   };
   auto mma = [&](const Frag& F) {
 #pragma unroll
@@ -358,23 +385,32 @@ __global__ __launch_bounds__(256, OCC) void gemm_bf16_kernel(GemmArgs a) {
           acc[g][j][i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(F.aw[g][j], F.bx[i], acc[g][j][i], 0, 0, 0);
   };
 
-  // Stage count padded to a multiple of the ring size; stages past K (the
-  // padding, and the refills issued during the last stages) read zeros --
-  // every chunk offset is past the buffer -- so the loop body is straight
-  // line and every refill is unconditional.  (A conditional refill makes
-  // the compiler wait for all loads in flight before the next LDS read,
-  // which would serialise the ring.)
-  const int nk = ((klen + BK - 1) / BK + NS - 1) / NS * NS;
-  // Entering stage kt: wait until only this wave's loads of stages kt+1 ..
-  // kt+NS-2 are in flight and its LDS reads have returned, barrier (every
-  // wave's loads of stage kt have landed, and every wave has read all it
-  // needs of stage kt-1), refill the slot of stage kt-1 with stage kt+NS-1.
-  constexpr int VM = (NS - 2) * PER;
-  constexpr int WAIT = 0x0070 | (VM & 15) | ((VM >> 4) << 14);  // vmcnt(VM) lgkmcnt(0)
+  // Stage count padded to a whole number of loop bodies (every combination
+  // of the two rings' slots); stages past K (the padding, and the refills
+  // issued during the last stages) read zeros -- every chunk offset is past
+  // the buffer -- so the loop body is straight line and every refill is
+  // unconditional.  (A conditional refill makes the compiler wait for all
+  // loads in flight before the next LDS read, which would serialise the
+  // ring.)
+  constexpr int LB = NSX * NSW / (NSX == NSW ? NSX : (NSW % NSX == 0 ? NSX : 1));  // lcm
+  const int nk = ((klen + BK - 1) / BK + LB - 1) / LB * LB;
+  // The transition into stage t+1 (at the end of stage t) refills the
+  // slots of stage t with x(t+NSX) and w(t+NSW), in that order.  Entering
+  // it, x(t+1) and w(t+1) must have landed: the loads issued after x(t+1)
+  // are w(t+NSX-1+...) of the same transition (when the weight ring is
+  // deeper) and the NSX-2 transitions since.  Then its LDS reads must have
+  // returned and every wave must be past the barrier (every wave's loads of
+  // stage t+1 have landed, and every wave has read all it needs of stage t).
+  constexpr int VM = (NSW > NSX ? WS : 0) + (NSX - 2) * PER;
+  constexpr int WAIT = 0x0070 | (VM & 15) | ((VM >> 4) << 14);   // vmcnt(VM) lgkmcnt(0)
+  constexpr int WAIT0 = 0x0F70 | (VM & 15) | ((VM >> 4) << 14);  // vmcnt(VM)
+  auto xslot = [&](auto i) -> u32x4_t* {
+    return lds_slot<decltype(i)::value % NSX, XSTAGE>();
+  };
+  auto wslot = [&](auto i) -> u32x4_t* {
+    return lds_slot<4 + decltype(i)::value % NSW, WSTAGE>();
+  };
   Frag F0, F1;
-  // one stage: k steps 0 .. KS-2 read the next step's fragments first; the
-  // last step moves to the next stage (slot nxt) before its MFMAs, which
-  // only need registers
   // Instruction order (the scheduler otherwise sinks each LDS read to its
   // first use, which exposes the LDS latency on every k step): one LDS
   // read of the next step per MFMA of the current one, and after a barrier
@@ -396,65 +432,49 @@ __global__ __launch_bounds__(256, OCC) void gemm_bf16_kernel(GemmArgs a) {
       if (u < NMF) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
     }
   };
-  auto stage = [&](u32x4_t* cur, const u32x4_t* nxt, int kt) {
+  // Stage S of the loop body (kt = its stage index): k steps 0 .. KS-2 read
+  // the next step's fragments first; the last step moves to the next stage
+  // before its MFMAs, which only need registers.
+  auto stage = [&](auto S, int kt) {
+    constexpr int s = decltype(S)::value;
+    u32x4_t* xc_ = xslot(std::integral_constant<int, s>{});
+    u32x4_t* wc_ = wslot(std::integral_constant<int, s>{});
 #pragma unroll
     for (int kk = 0; kk < KS - 1; ++kk) {
       if (kk % 2 == 0) {
-        read_frags(cur, kk + 1, F1);
+        read_frags(xc_, wc_, kk + 1, F1);
         mma(F0);
       } else {
-        read_frags(cur, kk + 1, F0);
+        read_frags(xc_, wc_, kk + 1, F0);
         mma(F1);
       }
       order_kstep();
     }
     __builtin_amdgcn_s_waitcnt(WAIT);
     __builtin_amdgcn_s_barrier();
-    issue(cur, kt + NS);
+    issue_x(xc_, kt + NSX);
+    issue_w(wc_, kt + NSW);
     // KS is even: the last step used F1, the next stage starts in F0
-    read_frags(nxt, 0, F0);
+    read_frags(xslot(std::integral_constant<int, s + 1>{}), wslot(std::integral_constant<int, s + 1>{}),
+               0, F0);
     mma(F1);
     order_transition();
   };
   static_assert(BK / 16 % 2 == 0, "even number of k steps per stage");
-  constexpr int WAIT0 = 0x0F70 | (VM & 15) | ((VM >> 4) << 14);
-  if constexpr (NS == 4) {
-    issue(st0, 0);
-    issue(st1, 1);
-    issue(st2, 2);
-    __builtin_amdgcn_s_waitcnt(WAIT0);
-    __builtin_amdgcn_s_barrier();
-    issue(st3, 3);
-    read_frags(st0, 0, F0);
-    for (int kt = 0; kt < nk; kt += NS) {
-      stage(st0, st1, kt);
-      stage(st1, st2, kt + 1);
-      stage(st2, st3, kt + 2);
-      stage(st3, st0, kt + 3);
-    }
-  } else if constexpr (NS == 3) {
-    issue(st0, 0);
-    issue(st1, 1);
-    __builtin_amdgcn_s_waitcnt(WAIT0);
-    __builtin_amdgcn_s_barrier();
-    issue(st2, 2);
-    read_frags(st0, 0, F0);
-    for (int kt = 0; kt < nk; kt += NS) {
-      stage(st0, st1, kt);
-      stage(st1, st2, kt + 1);
-      stage(st2, st0, kt + 2);
-    }
-  } else {
-    issue(st0, 0);
-    __builtin_amdgcn_s_waitcnt(WAIT0);
-    __builtin_amdgcn_s_barrier();
-    issue(st1, 1);
-    read_frags(st0, 0, F0);
-    for (int kt = 0; kt < nk; kt += NS) {
-      stage(st0, st1, kt);
-      stage(st1, st0, kt + 1);
-    }
-  }
+  // prologue: the transitions before stage 0 (t = -NSW .. -1), the wait of
+  // the last one in between
+  static_for<0, NSW - 1>([&](auto tt) {
+    constexpr int t = decltype(tt)::value - NSW;
+    if constexpr (t + NSX >= 0) issue_x(xslot(std::integral_constant<int, t + NSX>{}), t + NSX);
+    issue_w(wslot(std::integral_constant<int, t + NSW>{}), t + NSW);
+  });
+  __builtin_amdgcn_s_waitcnt(WAIT0);
+  __builtin_amdgcn_s_barrier();
+  issue_x(xslot(std::integral_constant<int, NSX - 1>{}), NSX - 1);
+  issue_w(wslot(std::integral_constant<int, NSW - 1>{}), NSW - 1);
+  read_frags(X0, W0, 0, F0);
+  for (int kt = 0; kt < nk; kt += LB)
+    static_for<0, LB>([&](auto S) { stage(S, kt + decltype(S)::value); });
   // the zero-reading refills past the end must land before the workgroup's
   // LDS is released
   __builtin_amdgcn_s_waitcnt(0x0F70);
@@ -570,7 +590,8 @@ static TileCfg tile_cfg(const GemmPlan& pl, int N, int K, bool swiglu) {
 }
 static int cfg_bm(TileCfg c) { return c == TILE_L ? 256 : c == TILE_M ? 128 : 64; }
 
-template <int BM, int BNW, int WM, int WN, int BK, int NS, int OCC, bool SWIGLU, bool PARTIAL>
+template <int BM, int BNW, int WM, int WN, int BK, int NSX, int NSW, int OCC, bool SWIGLU,
+          bool PARTIAL>
 static hipError_t run_bf16(const GemmPlan& pl, GemmArgs a, hipStream_t st) {
   constexpr int BNO = SWIGLU ? BNW / 2 : BNW;
   a.n_tiles = (a.N + BNO - 1) / BNO;
@@ -579,10 +600,10 @@ static hipError_t run_bf16(const GemmPlan& pl, GemmArgs a, hipStream_t st) {
   const long blocks = ((long)a.m_tiles * a.n_tiles * a.splits + 7) / 8 * 8;
   if (blocks == 0) return hipSuccess;
   if (a.a_rows)
-    hipLaunchKernelGGL((gemm_bf16_kernel<BM, BNW, WM, WN, BK, NS, OCC, SWIGLU, true, PARTIAL>),
+    hipLaunchKernelGGL((gemm_bf16_kernel<BM, BNW, WM, WN, BK, NSX, NSW, OCC, SWIGLU, true, PARTIAL>),
                        dim3((unsigned)blocks), dim3(256), 0, st, a);
   else
-    hipLaunchKernelGGL((gemm_bf16_kernel<BM, BNW, WM, WN, BK, NS, OCC, SWIGLU, false, PARTIAL>),
+    hipLaunchKernelGGL((gemm_bf16_kernel<BM, BNW, WM, WN, BK, NSX, NSW, OCC, SWIGLU, false, PARTIAL>),
                        dim3((unsigned)blocks), dim3(256), 0, st, a);
   return hipGetLastError();
 }
@@ -590,13 +611,13 @@ static hipError_t run_bf16(const GemmPlan& pl, GemmArgs a, hipStream_t st) {
 template <bool SWIGLU, bool PARTIAL>
 static hipError_t run_cfg(const GemmPlan& pl, GemmArgs a, hipStream_t st) {
   switch (tile_cfg(pl, a.N, a.K, SWIGLU)) {
-    case TILE_L: return run_bf16<256, 256, 2, 2, 64, 2, 1, SWIGLU, PARTIAL>(pl, a, st);
-    case TILE_M: return run_bf16<128, 256, 2, 2, 32, 3, 2, SWIGLU, PARTIAL>(pl, a, st);
+    case TILE_L: return run_bf16<256, 256, 2, 2, 64, 2, 3, 1, SWIGLU, PARTIAL>(pl, a, st);
+    case TILE_M: return run_bf16<128, 256, 2, 2, 32, 3, 3, 2, SWIGLU, PARTIAL>(pl, a, st);
     default:
       // a long K loop per tile wants the deeper ring; short ones two
       // workgroups per CU
-      if (!SWIGLU && a.k_chunk >= 2048) return run_bf16<64, 256, 1, 4, 64, 3, 1, SWIGLU, PARTIAL>(pl, a, st);
-      return run_bf16<64, 256, 1, 4, 64, 2, 2, SWIGLU, PARTIAL>(pl, a, st);
+      if (!SWIGLU && a.k_chunk >= 2048) return run_bf16<64, 256, 1, 4, 64, 3, 3, 1, SWIGLU, PARTIAL>(pl, a, st);
+      return run_bf16<64, 256, 1, 4, 64, 2, 2, 2, SWIGLU, PARTIAL>(pl, a, st);
   }
 }
 
