@@ -92,12 +92,13 @@ def traffic_from_profile(workload):
 
 
 def _is_gemm1(name):
-    # gemm_bf16_kernel<BM, BNW, WM, WN, SWIGLU, GATHER, PARTIAL>: GEMM 1 of
-    # the whole-layer path is the SwiGLU instance that gathers token rows
+    # gemm_bf16_kernel<tile and pipeline sizes..., SWIGLU, GATHER, PARTIAL>:
+    # GEMM 1 of the whole-layer path is the SwiGLU instance that gathers
+    # token rows
     if "gemm_bf16_kernel<" not in name:
         return False
     args = [a.strip() for a in name.split("<", 1)[1].split(">", 1)[0].split(",")]
-    return len(args) == 7 and args[4] == "true" and args[5] == "true"
+    return len(args) >= 3 and args[-3] == "true" and args[-2] == "true"
 
 
 def _counter_rows(folder, counter):
