@@ -55,6 +55,9 @@ def lib():
         L.oracle_expert_ffn.argtypes = [_i64, _i64, _i64, _int, _vp, _vp, _vp, _vp, _vp, _vp]
         L.oracle_combine.restype = None
         L.oracle_combine.argtypes = [_i64, _i64, _i64, _int, _vp, _vp, _vp, _vp, _vp]
+        L.oracle_routing_stats.restype = None
+        L.oracle_routing_stats.argtypes = [_i64, _i64, _i64, _vp, _vp, _vp, _dbl, ctypes.c_int32,
+                                           _vp, _vp, _vp, _vp]
         L.oracle_layer_forward.restype = _int
         L.oracle_layer_forward.argtypes = [_i64] * 6 + [_int, _int, _dbl] + [_vp] * 9 + \
             [_i64, _vp, _vp, _vp, _vp, _vp, _vp]
@@ -179,6 +182,29 @@ def combine(y_packed, route_pos, gates, y_shared=None):
     y = np.empty((T, d), np.float64)
     lib().oracle_combine(T, k, d, dt, _p(ya), _p(rp), _p(g), _p(sa), _p(y))
     return y
+
+
+STAT_NAMES = ("aux_loss", "load_imbalance", "mean_max_gate", "mean_norm_entropy",
+              "js_to_uniform", "mean_confidence")
+
+
+def routing_stats(logits, gates, counts, alpha=1e-2, n_bins=20):
+    """Forward-only routing statistics (see oracle_routing_stats).  Returns
+    dict with the six scalars by name, share[E], mean_prob[E], hist[n_bins]."""
+    la = np.ascontiguousarray(logits, dtype=np.float32)
+    T, E = la.shape
+    ga = np.ascontiguousarray(gates, dtype=np.float32)
+    k = ga.shape[1] if ga.ndim == 2 else max(1, ga.size // max(T, 1))
+    ca = np.ascontiguousarray(counts, dtype=np.int32)
+    out = np.zeros(6)
+    share = np.zeros(E)
+    mean_prob = np.zeros(E)
+    hist = np.zeros(n_bins, np.int64)
+    lib().oracle_routing_stats(T, E, k, _p(la), _p(ga), _p(ca), float(alpha), int(n_bins),
+                               _p(out), _p(share), _p(mean_prob), _p(hist))
+    res = dict(zip(STAT_NAMES, out.tolist()))
+    res.update(share=share, mean_prob=mean_prob, hist=hist)
+    return res
 
 
 def layer_forward(x, w_router, b_router, w_gate, w_up, w_down, k, renorm, phi,

@@ -240,6 +240,74 @@ void oracle_combine(int64_t T, int64_t k, int64_t d, int ypdtype,
   }
 }
 
+void oracle_routing_stats(int64_t T, int64_t E, int64_t k, const float* logits,
+                          const float* gates, const int32_t* counts,
+                          double alpha, int32_t n_bins, double* out,
+                          double* share, double* mean_prob, int64_t* hist) {
+  for (int i = 0; i < 6; i++) out[i] = 0.0;
+  for (int64_t e = 0; e < E; e++) {
+    share[e] = 0.0;
+    mean_prob[e] = 0.0;
+  }
+  for (int32_t b = 0; b < n_bins; b++) hist[b] = 0;
+  if (T <= 0) return;
+  /* route shares f_e and the demand imbalance */
+  double R = (double)T * (double)k;
+  double cmax = 0.0;
+  for (int64_t e = 0; e < E; e++) {
+    share[e] = (double)counts[e] / R;
+    if ((double)counts[e] > cmax) cmax = (double)counts[e];
+  }
+  out[1] = cmax / (R / (double)E);
+  /* per token: softmax over all experts, confidence, gates */
+  double sum_max_gate = 0.0, sum_entropy = 0.0, sum_conf = 0.0;
+  for (int64_t t = 0; t < T; t++) {
+    const float* l = logits + t * E;
+    double m = (double)l[0];
+    for (int64_t e = 1; e < E; e++)
+      if ((double)l[e] > m) m = (double)l[e];
+    double z = 0.0;
+    for (int64_t e = 0; e < E; e++) z += exp((double)l[e] - m);
+    for (int64_t e = 0; e < E; e++) mean_prob[e] += exp((double)l[e] - m) / z;
+    double conf = 1.0 / z; /* probability of the largest logit */
+    sum_conf += conf;
+    int32_t b = (int32_t)floor(conf * (double)n_bins);
+    if (b >= n_bins) b = n_bins - 1;
+    if (b < 0) b = 0;
+    hist[b] += 1;
+    const float* g = gates + t * k;
+    double gmax = (double)g[0], gsum = 0.0;
+    for (int64_t j = 0; j < k; j++) {
+      if ((double)g[j] > gmax) gmax = (double)g[j];
+      gsum += (double)g[j];
+    }
+    sum_max_gate += gmax;
+    if (k > 1 && gsum > 0.0) {
+      double h = 0.0;
+      for (int64_t j = 0; j < k; j++) {
+        double q = (double)g[j] / gsum;
+        if (q > 0.0) h -= q * log(q);
+      }
+      sum_entropy += h / log((double)k);
+    }
+  }
+  for (int64_t e = 0; e < E; e++) mean_prob[e] /= (double)T;
+  double aux = 0.0;
+  for (int64_t e = 0; e < E; e++) aux += share[e] * mean_prob[e];
+  out[0] = alpha * (double)E * aux;
+  out[2] = sum_max_gate / (double)T;
+  out[3] = sum_entropy / (double)T;
+  /* Jensen-Shannon divergence (base 2) of f and the uniform load */
+  double js = 0.0, u = 1.0 / (double)E;
+  for (int64_t e = 0; e < E; e++) {
+    double mid = 0.5 * (share[e] + u);
+    if (share[e] > 0.0) js += 0.5 * share[e] * log2(share[e] / mid);
+    js += 0.5 * u * log2(u / mid);
+  }
+  out[4] = sqrt(js > 0.0 ? js : 0.0);
+  out[5] = sum_conf / (double)T;
+}
+
 int oracle_layer_forward(int64_t T, int64_t d, int64_t E, int64_t k,
                          int64_t d_ff, int64_t d_ff_shared, int dtype,
                          int renorm, double phi, const void* x,

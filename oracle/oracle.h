@@ -133,6 +133,37 @@ void oracle_combine(int64_t T, int64_t k, int64_t d, int ypdtype,
                     const void* y_packed, const int32_t* route_pos,
                     const float* gates, const void* y_shared, double* y);
 
+/* Forward-only routing statistics of one batch of routes.
+ *   out[0]  aux     Switch auxiliary load-balancing loss value
+ *                   alpha * E * sum_e f_e * P_e ([INT8] section 4, after
+ *                   Switch Transformer), f_e = counts[e] / (T*k) the share of
+ *                   routes sent to e (demand, before capacity), P_e the mean
+ *                   over tokens of the full softmax probability of e
+ *   out[1]  imbalance  max_e counts[e] / (T*k/E) ([UD] load imbalance,
+ *                   measured on demand)
+ *   out[2]  mean over tokens of the largest selected gate ([MML] section 4
+ *                   "largest selected weight")
+ *   out[3]  mean over tokens of the normalised routing entropy: the k
+ *                   selected gates normalised to sum 1, entropy / ln k
+ *                   (0 when k = 1) ([MML] section 4)
+ *   out[4]  Jensen-Shannon distance, base 2, between the route shares f and
+ *                   the uniform load 1/E ([MML] section 4 compares load
+ *                   vectors with it)
+ *   out[5]  mean over tokens of the router confidence: the softmax
+ *                   probability of the chosen (largest-logit) expert ([BEA]
+ *                   "Router Confidence")
+ *   share[E] = f, mean_prob[E] = P
+ *   hist[n_bins]: tokens by router confidence in n_bins equal bins on
+ *                   [0, 1] (bin b holds [b/n_bins, (b+1)/n_bins); 1.0 goes
+ *                   to the last bin)
+ * Everything in double from the fp32 logits; T = 0 gives zeros.  Pinned by
+ * closed forms (uniform logits, balanced routing gives aux = alpha, a hot
+ * expert gives E/k) and scipy's entropy and Jensen-Shannon routines. */
+void oracle_routing_stats(int64_t T, int64_t E, int64_t k, const float* logits,
+                          const float* gates, const int32_t* counts,
+                          double alpha, int32_t n_bins, double* out,
+                          double* share, double* mean_prob, int64_t* hist);
+
 /* Whole layer forward: logits -> top-k gates -> dispatch with capacity ->
  * expert FFN per kept route -> gate-weighted sum (+ shared expert).
  * Routing (ids, gates, counts, route_pos) is computed for all T tokens;

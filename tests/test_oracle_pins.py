@@ -437,3 +437,91 @@ def test_empty_batch():
     out = oracle.layer_forward(inp["x"], inp["w_router"], None, inp["w_gate"], inp["w_up"],
                                inp["w_down"], k=2, renorm=1, phi=1.0)
     assert out["y"].shape == (0, 16) and out["counts"].tolist() == [0, 0, 0, 0]
+
+
+# ---------------------------------------------------------------------------
+# Forward-only routing statistics ([INT8] section 4 aux loss; [UD] load
+# imbalance; [MML] section 4 shares, largest weight, entropy, JS distance;
+# [BEA] "Router Confidence").
+
+def _routing(T, E, k, renorm, seed, scale=1.0, bias=None):
+    rng = np.random.default_rng(seed)
+    logits = (rng.standard_normal((T, E)) * scale).astype(np.float32)
+    if bias is not None:
+        logits = (logits + bias).astype(np.float32)
+    ids, gates = oracle.topk_gates(logits, k, renorm)
+    counts = np.bincount(ids.ravel(), minlength=E).astype(np.int32)
+    return logits, ids, gates, counts
+
+
+def test_stats_balanced_routing_gives_alpha():
+    # f_e = 1/E for every expert => aux = alpha * E * sum_e P_e / E = alpha
+    # whatever the probabilities (they sum to 1)
+    T, E, k = 64, 8, 2
+    rng = np.random.default_rng(3)
+    logits = rng.standard_normal((T, E)).astype(np.float32)
+    _, gates = oracle.topk_gates(logits, k, 1)
+    counts = np.full(E, T * k // E, np.int32)
+    st = oracle.routing_stats(logits, gates, counts, alpha=1e-2)
+    assert st["aux_loss"] == pytest.approx(1e-2, rel=1e-12)
+    assert st["load_imbalance"] == pytest.approx(1.0, rel=1e-12)
+    assert st["js_to_uniform"] == pytest.approx(0.0, abs=1e-7)
+
+
+def test_stats_uniform_logits():
+    T, E, k, nb = 32, 8, 2, 20
+    logits = np.zeros((T, E), np.float32)
+    ids, gates = oracle.topk_gates(logits, k, 1)
+    counts = np.bincount(ids.ravel(), minlength=E).astype(np.int32)
+    st = oracle.routing_stats(logits, gates, counts, n_bins=nb)
+    assert np.allclose(st["mean_prob"], 1.0 / E, rtol=0, atol=1e-15)
+    assert st["mean_confidence"] == pytest.approx(1.0 / E, rel=1e-12)
+    assert st["hist"][int(nb / E)] == T and st["hist"].sum() == T
+    # all ties go to experts 0..k-1 ([UD]: the worst case is E/k)
+    assert st["load_imbalance"] == pytest.approx(E / k, rel=1e-12)
+    assert st["mean_norm_entropy"] == pytest.approx(1.0, rel=1e-12)
+    assert st["mean_max_gate"] == pytest.approx(1.0 / k, rel=1e-7)
+
+
+def test_stats_hot_expert_imbalance_is_E_over_k():
+    T, E, k = 128, 32, 8
+    bias = np.zeros(E, np.float32)
+    bias[5] = 1e3
+    logits, ids, gates, counts = _routing(T, E, k, 1, seed=4, bias=bias)
+    st = oracle.routing_stats(logits, gates, counts)
+    assert st["load_imbalance"] == pytest.approx(E / k, rel=1e-12)
+
+
+@pytest.mark.parametrize("T,E,k,renorm", [(300, 8, 2, 1), (257, 32, 8, 1), (100, 8, 1, 0), (64, 64, 2, 1)])
+def test_stats_against_scipy(T, E, k, renorm):
+    from scipy.spatial.distance import jensenshannon
+    from scipy.special import softmax
+    from scipy.stats import entropy
+    nb = 16
+    logits, ids, gates, counts = _routing(T, E, k, renorm, seed=T + E, scale=2.0)
+    st = oracle.routing_stats(logits, gates, counts, alpha=1e-2, n_bins=nb)
+    p = softmax(logits.astype(np.float64), axis=1)
+    share = counts / (T * k)
+    assert np.allclose(st["share"], share, rtol=1e-14)
+    assert np.allclose(st["mean_prob"], p.mean(axis=0), rtol=1e-12, atol=1e-15)
+    assert st["aux_loss"] == pytest.approx(1e-2 * E * float(np.dot(share, p.mean(axis=0))), rel=1e-12)
+    assert st["js_to_uniform"] == pytest.approx(float(jensenshannon(share, np.full(E, 1.0 / E), base=2)),
+                                                rel=1e-9, abs=1e-12)
+    g = gates.astype(np.float64)
+    assert st["mean_max_gate"] == pytest.approx(float(g.max(axis=1).mean()), rel=1e-12)
+    if k > 1:
+        h = entropy(g / g.sum(axis=1, keepdims=True), axis=1) / np.log(k)
+        assert st["mean_norm_entropy"] == pytest.approx(float(h.mean()), rel=1e-10)
+    else:
+        assert st["mean_norm_entropy"] == 0.0
+    conf = p.max(axis=1)
+    assert st["mean_confidence"] == pytest.approx(float(conf.mean()), rel=1e-12)
+    ref_hist, _ = np.histogram(conf, bins=nb, range=(0.0, 1.0))
+    assert np.array_equal(st["hist"], ref_hist)
+
+
+def test_stats_empty_batch():
+    st = oracle.routing_stats(np.zeros((0, 4), np.float32), np.zeros((0, 2), np.float32),
+                              np.zeros(4, np.int32), n_bins=8)
+    assert all(st[n] == 0.0 for n in oracle.STAT_NAMES)
+    assert st["hist"].sum() == 0
