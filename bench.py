@@ -17,6 +17,9 @@ Prints ONE JSON line:
                  taken on another version of the GEMM source)
   cpu_baseline   the CPU oracle on a bounded sample of the same workload
   stages_us      mean per-stage times of a second, fully event-marked pass
+  routing_stats  forward-only routing statistics of the batch (Switch
+                 aux-loss value with alpha 1e-2, demand imbalance, ...) and
+                 the time of one moe_routing_stats call
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 
@@ -284,6 +287,32 @@ def main():
             hip.hipEventDestroy(e)
         stages = {n: round(a / K, 2) for n, a in zip(STAGES, acc)}
 
+    # forward-only routing statistics of the bench batch: one extra pass over
+    # the route outputs (router logits requested from moe_route)
+    rstats = None
+    if not args.no_stages:
+        ids_, gates_, logits_ = moe.route(s, d["x"], d["w_router"], d["b_router"], ws=ws,
+                                          want_logits=True)
+        counts_ = moe.permute(s, d["x"], ids_, ws=ws)["counts"]
+        outs = moe.routing_stats(s, logits_, gates_, counts_, alpha=1e-2, n_bins=20, ws=ws)
+        ev = new_events(2)
+        torch.cuda.synchronize()
+        hip_rec = hip.hipEventRecord
+        hip_rec.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+        # the calls are short next to their host-side marshalling: keep the
+        # GPU busy while they are queued, so the events time the GPU only
+        torch.cuda._sleep(int(K * 2e5))
+        hip_rec(ev[0], ctypes.c_void_p(stream.cuda_stream))
+        for _ in range(K):
+            moe.routing_stats(s, logits_, gates_, counts_, alpha=1e-2, n_bins=20, ws=ws, out=outs)
+        hip_rec(ev[1], ctypes.c_void_p(stream.cuda_stream))
+        torch.cuda.synchronize()
+        named = moe.stats_dict(s, *outs)
+        rstats = {n: round(float(named[n]), 6) for n in moe.STAT_NAMES}
+        rstats["us_per_call"] = round(elapsed_us(ev[0], ev[1]) / K, 2)
+        for e in ev:
+            hip.hipEventDestroy(e)
+
     if args.copy_calibration:
         n = args.copy_calibration << 20
         src = torch.ones(n, dtype=torch.uint8, device=dev)
@@ -338,6 +367,7 @@ def main():
         "roofline": roof,
         "cpu_baseline": cpu,
         "stages_us": stages,
+        "routing_stats": rstats,
     }
     print(json.dumps(out), flush=True)
 

@@ -194,6 +194,37 @@ int moe_layer_forward(const moe_shape* s, const void* x, const void* w_router,
                       int32_t* counts, int32_t* route_pos, void* ws, size_t ws_bytes,
                       hipStream_t stream);
 
+/* Forward-only routing statistics of one batch of routes, from the outputs
+ * of moe_route (logits must have been requested) and moe_permute (counts).
+ *   "Mixture of Experts: Routing, Dispatch, and Load Balancing", section 4:
+ *     the Switch auxiliary load-balancing loss alpha * N * sum_i f_i P_i,
+ *     f_i the share of routes sent to expert i (before capacity), P_i the
+ *     mean over tokens of its full softmax probability (N = E).
+ *   "Mixture-of-experts routing", load imbalance: max_e D_e / mean D, D the
+ *     demand before capacity.
+ *   "271,104 Routes", section 4: selection share, largest selected weight,
+ *     normalised routing entropy, Jensen-Shannon distance of load vectors.
+ *   "MoE Inference Visualized", "Router Confidence": the softmax probability
+ *     of the chosen expert.
+ * Inputs (device): logits [T][E] fp32, gates [T][k] fp32, counts [E] int32
+ * (demand, as moe_permute writes it).  alpha: loss coefficient (the Switch
+ * Transformer value is 1e-2).  n_bins in [1, 256].
+ * Outputs (device):
+ *   stats [6 + 2E] fp32:
+ *     [0] aux loss  [1] load imbalance  [2] mean largest selected gate
+ *     [3] mean normalised entropy of the selected gates (each token's k
+ *         gates normalised to sum 1, entropy / ln k; 0 when k = 1)
+ *     [4] Jensen-Shannon distance (base 2) of the route shares to the
+ *         uniform load  [5] mean router confidence
+ *     [6, 6+E) route shares f  [6+E, 6+2E) mean probabilities P
+ *   hist [n_bins] int32: tokens by router confidence (the largest softmax
+ *     probability) in equal bins on [0, 1].
+ * Sums run in a fixed order in fp32 (repeat calls give identical results).
+ * T = 0 gives zeros.  Uses the workspace of moe_workspace_bytes. */
+int moe_routing_stats(const moe_shape* s, const float* logits, const float* gates,
+                      const int32_t* counts, double alpha, int32_t n_bins, float* stats,
+                      int32_t* hist, void* ws, size_t ws_bytes, hipStream_t stream);
+
 /* Measurement variant of moe_layer_forward (same arguments without the
  * optional routing outputs): additionally records events[i] on the stream at
  * the stage boundaries, so that elapsed times between them are the stage

@@ -30,7 +30,7 @@ MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP
 
 EXPORTS = ("moe_status_string", "moe_capacity", "moe_workspace_bytes", "moe_route",
            "moe_permute", "moe_expert_ffn", "moe_combine", "moe_layer_forward",
-           "moe_layer_forward_timed")
+           "moe_layer_forward_timed", "moe_routing_stats")
 
 
 class MoeShape(ctypes.Structure):
@@ -59,6 +59,8 @@ _lib.moe_expert_ffn.argtypes = [_SP] + [_vp] * 6 + [_vp, _sz, _vp]
 _lib.moe_combine.argtypes = [_SP] + [_vp] * 5 + [_vp]
 _lib.moe_layer_forward.argtypes = [_SP] + [_vp] * 14 + [_vp, _sz, _vp]
 _lib.moe_layer_forward_timed.argtypes = [_SP] + [_vp] * 10 + [_vp, _sz, _vp, _vp]
+_lib.moe_routing_stats.argtypes = [_SP, _vp, _vp, _vp, ctypes.c_double, ctypes.c_int32, _vp, _vp,
+                                   _vp, _sz, _vp]
 for _n in EXPORTS[1:]:
     getattr(_lib, _n).restype = ctypes.c_int
 
@@ -211,6 +213,39 @@ def combine(s, y_packed, route_pos, gates, y_shared=None, y=None, stream=None):
     op = _ptr(y, "y", (s.T, s.d), dt)
     _check(_lib.moe_combine(ctypes.byref(s), yp, rp, gp, sp, op, _stream(stream)), "moe_combine")
     return y
+
+
+STAT_NAMES = ("aux_loss", "load_imbalance", "mean_max_gate", "mean_norm_entropy",
+              "js_to_uniform", "mean_confidence")
+
+
+def routing_stats(s, logits, gates, counts, alpha=1e-2, n_bins=20, ws=None, stream=None,
+                  out=None):
+    """moe_routing_stats.  Returns (stats [6 + 2E] fp32, hist [n_bins] int32)
+    device tensors; stats_dict() turns them into named values."""
+    dev = counts.device
+    lp = _ptr(logits, "logits", (s.T, s.E), torch.float32, optional=s.T == 0)
+    gp = _ptr(gates, "gates", (s.T, s.k), torch.float32, optional=s.T == 0)
+    cp = _ptr(counts, "counts", (s.E,), torch.int32)
+    if out is None:
+        out = (torch.empty(6 + 2 * s.E, dtype=torch.float32, device=dev),
+               torch.empty(int(n_bins), dtype=torch.int32, device=dev))
+    st, hist = out
+    ws = _ws(s, ws, dev)
+    _check(_lib.moe_routing_stats(ctypes.byref(s), lp, gp, cp, float(alpha), int(n_bins),
+                                  _ptr(st, "stats", (6 + 2 * s.E,), torch.float32),
+                                  _ptr(hist, "hist", (int(n_bins),), torch.int32),
+                                  ws.data_ptr(), ws.numel(), _stream(stream)), "moe_routing_stats")
+    return st, hist
+
+
+def stats_dict(s, stats, hist):
+    """Named host copies of the routing_stats outputs."""
+    v = stats.detach().cpu().double().numpy()
+    res = dict(zip(STAT_NAMES, v[:6].tolist()))
+    res.update(share=v[6:6 + s.E], mean_prob=v[6 + s.E:6 + 2 * s.E],
+               hist=hist.detach().cpu().numpy().astype("int64"))
+    return res
 
 
 def layer_forward(s, x, w_router, b_router, w_gate, w_up, w_down, ws_gate=None, ws_up=None,

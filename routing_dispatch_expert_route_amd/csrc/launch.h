@@ -53,4 +53,13 @@ hipError_t launch_reduce_splits(bool bf16, const float* parts, int splits, long 
                                 const int32_t* offsets, int E, long R_max, int N, void* y,
                                 hipStream_t st);
 
+// stats_partial_kernel + stats_final_kernel.  part holds
+// stats_blocks(T) * (E + 3) floats, hpart stats_blocks(T) * n_bins ints;
+// n_bins <= kMaxStatBins.
+constexpr int kMaxStatBins = 256;
+int stats_blocks(long T);
+hipError_t launch_routing_stats(const float* logits, const float* gates, const int32_t* counts,
+                                int T, int E, int k, int n_bins, float alpha, float* part,
+                                int32_t* hpart, float* stats, int32_t* hist, hipStream_t st);
+
 }  // namespace moe

@@ -65,7 +65,7 @@ int64_t rmax_of(const moe_shape* s, int64_t C) {
 
 struct Layout {
   size_t logits, ids, gates, cnt, counts, kept, offsets, route_pos, row_token, h, yp, part, hs,
-      ys;
+      ys, spart, shist;
   int splits;  // K splits of the routed down GEMM (fp32 partial planes when > 1)
   size_t total;
 };
@@ -109,6 +109,10 @@ Layout layout_of(const moe_shape* s) {
   L.part = take(L.splits > 1 ? (size_t)L.splits * Rmax * s->d * sizeof(float) : 0);
   L.hs = take((size_t)s->T * s->d_ff_shared * eb);
   L.ys = take(s->d_ff_shared > 0 ? (size_t)s->T * s->d * eb : 0);
+  // routing statistics: one partial row per 64 tokens
+  const size_t sblk = (size_t)moe::stats_blocks((long)s->T);
+  L.spart = take(sblk * (size_t)(s->E + 3) * sizeof(float));
+  L.shist = take(sblk * (size_t)moe::kMaxStatBins * sizeof(int32_t));
   L.total = o;
   return L;
 }
@@ -241,6 +245,22 @@ int moe_combine(const moe_shape* s, const void* y_packed, const int32_t* route_p
   return hip_status(moe::launch_combine(s->dtype == MOE_DTYPE_BF16, y_packed, 1, 0, route_pos,
                                         gates, y_shared, (int)s->T, (int)s->k, (int)s->d, y,
                                         stream));
+}
+
+int moe_routing_stats(const moe_shape* s, const float* logits, const float* gates,
+                      const int32_t* counts, double alpha, int32_t n_bins, float* stats,
+                      int32_t* hist, void* ws, size_t ws_bytes, hipStream_t stream) {
+  int v = validate(s);
+  if (v != MOE_OK) return v;
+  if (!counts || !stats || !hist || (s->T > 0 && (!logits || !gates))) return MOE_ERR_INVALID_ARG;
+  if (n_bins < 1 || n_bins > moe::kMaxStatBins || isnan(alpha)) return MOE_ERR_INVALID_ARG;
+  v = check_ws(s, ws, ws_bytes);
+  if (v != MOE_OK) return v;
+  const Layout L = layout_of(s);
+  return hip_status(moe::launch_routing_stats(logits, gates, counts, (int)s->T, (int)s->E,
+                                              (int)s->k, n_bins, (float)alpha,
+                                              at<float>(ws, L.spart), at<int32_t>(ws, L.shist),
+                                              stats, hist, stream));
 }
 
 static int layer_forward_impl(const moe_shape* s, const void* x, const void* w_router,

@@ -1,0 +1,169 @@
+// stats.hip -- forward-only routing statistics of one batch of routes.
+//
+// "Mixture of Experts: Routing, Dispatch, and Load Balancing", section 4:
+// the Switch auxiliary load-balancing loss alpha * N * sum_i f_i P_i (f_i the
+// share of tokens dispatched to expert i, P_i its mean routing probability).
+// "Mixture-of-experts routing", load imbalance: max demand over mean demand,
+// measured before capacity.  "271,104 Routes", section 4: selection share,
+// largest selected weight, normalised routing entropy, Jensen-Shannon
+// distance between load vectors.  "MoE Inference Visualized", "Router
+// Confidence": the softmax probability of the chosen expert.
+//
+// Two kernels, no atomics on floating point (every sum has a fixed order):
+//   stats_partial_kernel  64 tokens per block: softmax of each token's
+//       logits (sequential over experts), its confidence bin, largest gate
+//       and gate entropy; then per expert the block's sum of probabilities
+//       over its tokens in token order.  Writes one partial row per block.
+//   stats_final_kernel    one block: sums the partial rows in block order
+//       and forms the statistics.
+#include "common.h"
+#include "launch.h"
+
+namespace moe {
+
+constexpr int kStatTok = 64;  // tokens per block
+
+__global__ __launch_bounds__(256) void stats_partial_kernel(const float* __restrict__ logits,
+                                                            const float* __restrict__ gates,
+                                                            int T, int E, int k, int n_bins,
+                                                            float* __restrict__ part,
+                                                            int32_t* __restrict__ hpart) {
+  __shared__ float s_l[kStatTok * 257];  // the block's logits, row stride E + 1
+  __shared__ float s_m[kStatTok], s_iz[kStatTok];
+  __shared__ float s_tok[3][kStatTok];
+  __shared__ int s_hist[kMaxStatBins];
+  const int tid = threadIdx.x;
+  const int t0 = blockIdx.x * kStatTok;
+  const int nt = min(kStatTok, T - t0);
+  const int ls = E + 1;
+  for (int i = tid; i < nt * E; i += 256) s_l[(i / E) * ls + i % E] = logits[(size_t)t0 * E + i];
+  for (int b = tid; b < n_bins; b += 256) s_hist[b] = 0;
+  __syncthreads();
+  if (tid < kStatTok) {
+    float gmax = 0.0f, ent = 0.0f, conf = 0.0f;
+    if (tid < nt) {
+      const float* l = s_l + tid * ls;
+      float m = l[0];
+      for (int e = 1; e < E; ++e) m = fmaxf(m, l[e]);
+      float z = 0.0f;
+      for (int e = 0; e < E; ++e) z += __expf(l[e] - m);
+      const float iz = 1.0f / z;
+      s_m[tid] = m;
+      s_iz[tid] = iz;
+      conf = iz;  // probability of the largest logit
+      int b = (int)(conf * (float)n_bins);
+      b = b < n_bins ? b : n_bins - 1;
+      atomicAdd(&s_hist[b], 1);  // integer counts: any order gives the same result
+      const float* g = gates + (size_t)(t0 + tid) * k;
+      float gs = 0.0f;
+      gmax = g[0];
+      for (int j = 0; j < k; ++j) {
+        gmax = fmaxf(gmax, g[j]);
+        gs += g[j];
+      }
+      if (k > 1 && gs > 0.0f) {
+        float h = 0.0f;
+        for (int j = 0; j < k; ++j) {
+          const float q = g[j] / gs;
+          if (q > 0.0f) h -= q * __logf(q);
+        }
+        ent = h / __logf((float)k);
+      }
+    }
+    s_tok[0][tid] = gmax;
+    s_tok[1][tid] = ent;
+    s_tok[2][tid] = conf;
+  }
+  __syncthreads();
+  const size_t row = (size_t)blockIdx.x * (E + 3);
+  for (int e = tid; e < E; e += 256) {
+    float acc = 0.0f;
+    for (int t = 0; t < nt; ++t) acc += __expf(s_l[t * ls + e] - s_m[t]) * s_iz[t];
+    part[row + e] = acc;
+  }
+  if (tid < 3) {
+    float acc = 0.0f;
+    for (int t = 0; t < kStatTok; ++t) acc += s_tok[tid][t];
+    part[row + E + tid] = acc;
+  }
+  for (int b = tid; b < n_bins; b += 256) hpart[(size_t)blockIdx.x * n_bins + b] = s_hist[b];
+}
+
+// Sum of column c over nblk rows of a row-major [nblk][ld] array, rows in
+// order, sixteen loads in flight (a fixed order: repeat calls agree).
+template <typename V>
+__device__ __forceinline__ V column_sum(const V* __restrict__ a, int nblk, int ld, int c) {
+  V acc = 0;
+  for (int b0 = 0; b0 < nblk; b0 += 16) {
+    V v[16];
+#pragma unroll
+    for (int u = 0; u < 16; ++u) v[u] = b0 + u < nblk ? a[(size_t)(b0 + u) * ld + c] : V(0);
+#pragma unroll
+    for (int u = 0; u < 16; ++u) acc += v[u];
+  }
+  return acc;
+}
+
+// stats: [0] aux loss, [1] load imbalance, [2] mean largest gate, [3] mean
+// normalised entropy, [4] JS distance of the shares to uniform (base 2),
+// [5] mean confidence, [6, 6+E) shares, [6+E, 6+2E) mean probabilities.
+__global__ __launch_bounds__(256) void stats_final_kernel(const float* __restrict__ part,
+                                                          const int32_t* __restrict__ hpart,
+                                                          int nblk, const int32_t* __restrict__ counts,
+                                                          int T, int E, int k, int n_bins,
+                                                          float alpha, float* __restrict__ stats,
+                                                          int32_t* __restrict__ hist) {
+  __shared__ float s_f[256], s_p[256];
+  __shared__ float s_tok[3];
+  const int tid = threadIdx.x;
+  const float inv_t = T > 0 ? 1.0f / (float)T : 0.0f;
+  const float R = (float)T * (float)k;
+  for (int e = tid; e < E; e += 256) {
+    const float p = column_sum(part, nblk, E + 3, e) * inv_t;
+    const float f = T > 0 ? (float)counts[e] / R : 0.0f;
+    s_f[e] = f;
+    s_p[e] = p;
+    stats[6 + e] = f;
+    stats[6 + E + e] = p;
+  }
+  if (tid < 3) s_tok[tid] = column_sum(part, nblk, E + 3, E + tid) * inv_t;
+  for (int b = tid; b < n_bins; b += 256) hist[b] = column_sum(hpart, nblk, n_bins, b);
+  __syncthreads();
+  if (tid == 0) {
+    float aux = 0.0f, cmax = 0.0f, js = 0.0f;
+    const float u = 1.0f / (float)E;
+    for (int e = 0; e < E; ++e) {
+      aux += s_f[e] * s_p[e];
+      cmax = fmaxf(cmax, (float)counts[e]);
+      const float mid = 0.5f * (s_f[e] + u);
+      if (s_f[e] > 0.0f) js += 0.5f * s_f[e] * __log2f(s_f[e] / mid);
+      js += 0.5f * u * __log2f(u / mid);
+    }
+    const bool any = T > 0;
+    stats[0] = any ? alpha * (float)E * aux : 0.0f;
+    stats[1] = any ? cmax / (R / (float)E) : 0.0f;
+    stats[2] = s_tok[0];
+    stats[3] = s_tok[1];
+    stats[4] = any ? sqrtf(fmaxf(js, 0.0f)) : 0.0f;
+    stats[5] = s_tok[2];
+  }
+}
+
+int stats_blocks(long T) { return (int)((T + kStatTok - 1) / kStatTok); }
+
+hipError_t launch_routing_stats(const float* logits, const float* gates, const int32_t* counts,
+                                int T, int E, int k, int n_bins, float alpha, float* part,
+                                int32_t* hpart, float* stats, int32_t* hist, hipStream_t st) {
+  const int nblk = stats_blocks(T);
+  if (nblk > 0) {
+    hipLaunchKernelGGL(stats_partial_kernel, dim3(nblk), dim3(256), 0, st, logits, gates, T, E, k,
+                       n_bins, part, hpart);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+  }
+  hipLaunchKernelGGL(stats_final_kernel, dim3(1), dim3(256), 0, st, part, hpart, nblk, counts, T, E,
+                     k, n_bins, alpha, stats, hist);
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -153,3 +153,29 @@ def test_library_has_no_unresolved_internal_symbols():
     out = subprocess.run(["nm", "-D", "--undefined-only", moe.LIB_PATH], capture_output=True,
                          text=True, check=True).stdout
     assert not [l for l in out.splitlines() if "_ZN3moe" in l]
+
+
+def test_routing_stats_rejected_before_launch():
+    moe = _moe()
+    s = moe.shape(16, 64, 4, 2, 64)
+    by = ctypes.byref(s)
+    L = moe._lib
+    fake = 4096  # never dereferenced: validation fails first
+    need = moe.workspace_bytes(s)
+    ok_ws = 1 << 20  # 256-byte aligned stand-in
+    # missing counts / stats / hist / inputs
+    assert L.moe_routing_stats(by, fake, fake, None, 0.01, 8, fake, fake, ok_ws, need, None) \
+        == moe.MOE_ERR_INVALID_ARG
+    assert L.moe_routing_stats(by, None, fake, fake, 0.01, 8, fake, fake, ok_ws, need, None) \
+        == moe.MOE_ERR_INVALID_ARG
+    assert L.moe_routing_stats(by, fake, fake, fake, 0.01, 8, fake, None, ok_ws, need, None) \
+        == moe.MOE_ERR_INVALID_ARG
+    # bin count out of range, NaN alpha
+    for nb in (0, -3, 257):
+        assert L.moe_routing_stats(by, fake, fake, fake, 0.01, nb, fake, fake, ok_ws, need, None) \
+            == moe.MOE_ERR_INVALID_ARG
+    assert L.moe_routing_stats(by, fake, fake, fake, float("nan"), 8, fake, fake, ok_ws, need, None) \
+        == moe.MOE_ERR_INVALID_ARG
+    # workspace too small
+    assert L.moe_routing_stats(by, fake, fake, fake, 0.01, 8, fake, fake, ok_ws, need - 1, None) \
+        == moe.MOE_ERR_WORKSPACE
