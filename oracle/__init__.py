@@ -55,6 +55,8 @@ def lib():
         L.oracle_expert_ffn.argtypes = [_i64, _i64, _i64, _int, _vp, _vp, _vp, _vp, _vp, _vp]
         L.oracle_combine.restype = None
         L.oracle_combine.argtypes = [_i64, _i64, _i64, _int, _vp, _vp, _vp, _vp, _vp]
+        L.oracle_dispatch_padded.restype = None
+        L.oracle_dispatch_padded.argtypes = [_i64, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _vp]
         L.oracle_routing_stats.restype = None
         L.oracle_routing_stats.argtypes = [_i64, _i64, _i64, _vp, _vp, _vp, _dbl, ctypes.c_int32,
                                            _vp, _vp, _vp, _vp]
@@ -135,6 +137,21 @@ def dispatch(expert_ids, E, C):
     n = int(offsets[E])
     return dict(counts=counts, kept=kept, offsets=offsets,
                 route_pos=route_pos.reshape(T, k), row_token=row_token[:n].copy())
+
+
+def dispatch_padded(expert_ids, E, C):
+    """Dispatch into the fixed [E, C] slot buffer.  Returns dict(pad_pos [T, k],
+    slot_token [E, C] (-1 = empty slot)) plus the packed dispatch's fields."""
+    ids = np.ascontiguousarray(expert_ids, dtype=np.int32)
+    T, k = ids.shape
+    d = dispatch(ids, E, C)
+    pad_pos = np.empty(T * k, np.int32)
+    slot_token = np.empty(max(E * C, 1), np.int32)
+    rp = np.ascontiguousarray(d["route_pos"].reshape(-1), dtype=np.int32)
+    lib().oracle_dispatch_padded(T, E, k, int(C), _p(ids), _p(rp), _p(d["offsets"]),
+                                 _p(pad_pos), _p(slot_token))
+    d.update(pad_pos=pad_pos.reshape(T, k), slot_token=slot_token[:E * C].reshape(E, C))
+    return d
 
 
 def gather_rows(x, row_token):

@@ -157,6 +157,23 @@ void oracle_dispatch(int64_t T, int64_t E, int64_t k, int64_t C,
   free(slot);
 }
 
+void oracle_dispatch_padded(int64_t T, int64_t E, int64_t k, int64_t C,
+                            const int32_t* expert_ids, const int32_t* route_pos,
+                            const int32_t* offsets, int32_t* pad_pos,
+                            int32_t* slot_token) {
+  for (int64_t p = 0; p < E * C; p++) slot_token[p] = -1;
+  for (int64_t r = 0; r < T * k; r++) {
+    if (route_pos[r] < 0) {
+      pad_pos[r] = -1;
+      continue;
+    }
+    int32_t e = expert_ids[r];
+    int64_t slot = route_pos[r] - offsets[e]; /* arrival rank among kept */
+    pad_pos[r] = (int32_t)(e * C + slot);
+    slot_token[e * C + slot] = (int32_t)(r / k);
+  }
+}
+
 void oracle_gather_rows(int64_t n_rows, int64_t d, int64_t elem_bytes,
                         const void* x, const int32_t* row_token,
                         void* packed) {

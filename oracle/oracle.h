@@ -99,6 +99,20 @@ void oracle_dispatch(int64_t T, int64_t E, int64_t k, int64_t C,
                      const int32_t* expert_ids, int32_t* counts, int32_t* kept,
                      int32_t* offsets, int32_t* route_pos, int32_t* row_token);
 
+/* The fixed-shape dispatch buffer [E, C, d] ("Session 19", "Capacity":
+ * capacity is a tensor dimension; "Visual support -- Capacity" slot table;
+ * "271,104 Routes", section 3 "When one expert gets too many tokens": fixed
+ * expert buffers).  From a dispatch with capacity C >= 1 (route_pos and
+ * offsets of oracle_dispatch):
+ *   pad_pos[r]       e*C + slot of route r (slot = its arrival rank at e),
+ *                    -1 if dropped
+ *   slot_token[e*C + c]  token seated in slot c of expert e, -1 if empty
+ * Pinned by the slot table of the "Session 19" trace (15 filled, 5 empty). */
+void oracle_dispatch_padded(int64_t T, int64_t E, int64_t k, int64_t C,
+                            const int32_t* expert_ids, const int32_t* route_pos,
+                            const int32_t* offsets, int32_t* pad_pos,
+                            int32_t* slot_token);
+
 /* Row duplication: packed[p][:] = x[row_token[p]][:] for p < n_rows, a bit
  * copy of elem_bytes-sized elements ([MML] section 3: index_select). */
 void oracle_gather_rows(int64_t n_rows, int64_t d, int64_t elem_bytes,

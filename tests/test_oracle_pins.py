@@ -525,3 +525,47 @@ def test_stats_empty_batch():
                               np.zeros(4, np.int32), n_bins=8)
     assert all(st[n] == 0.0 for n in oracle.STAT_NAMES)
     assert st["hist"].sum() == 0
+
+
+def test_padded_slot_table_spk():
+    """"Session 19", "Visual support -- Capacity": the [E, C, d] dispatch
+    buffer for the trace with C = 5 -- slots in arrival order per expert,
+    15 filled, 5 empty, t6 dropped at E1."""
+    g = G.load("spk_capacity_trace.txt")
+    E, k = int(g["E"]), int(g["k"])
+    ids = np.array(G.rows(g["assign"], int), np.int32)
+    C = oracle.capacity(int(g["T"]), E, k, 1.25)
+    out = oracle.dispatch_padded(ids, E, C)
+    st = out["slot_token"]
+    assert st.shape == (E, 5)
+    for e in range(E):
+        seated = G.nums(g[f"slots_E{e}"], int)
+        assert st[e, :len(seated)].tolist() == seated
+        assert (st[e, len(seated):] == -1).all()
+    assert int((st >= 0).sum()) == 15 and int((st < 0).sum()) == 5
+    pp = out["pad_pos"]
+    assert pp[5, 0] == -1                                  # t6 at E1 dropped
+    for t in range(ids.shape[0]):
+        for j in range(k):
+            if pp[t, j] >= 0:
+                e, c = divmod(int(pp[t, j]), C)
+                assert e == ids[t, j] and st[e, c] == t
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_padded_positions_follow_arrival_order(seed):
+    # brute force: slot = number of earlier kept routes to the same expert
+    rng = np.random.default_rng(seed)
+    T, E, k = 50, 6, 2
+    ids = np.array([rng.choice(E, size=k, replace=False) for _ in range(T)], np.int32)
+    C = oracle.capacity(T, E, k, 1.0)
+    out = oracle.dispatch_padded(ids, E, C)
+    seen = np.zeros(E, int)
+    for r in range(T * k):
+        t, j = divmod(r, k)
+        e = ids[t, j]
+        if seen[e] < C:
+            assert out["pad_pos"][t, j] == e * C + seen[e]
+            seen[e] += 1
+        else:
+            assert out["pad_pos"][t, j] == -1
