@@ -180,6 +180,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-stages", action="store_true")
+    ap.add_argument("--padded", action="store_true",
+                    help="fixed-shape [E, C, d] dispatch buffer instead of packed rows")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB")
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
     ap.add_argument("--traffic-out", default=None)
@@ -219,7 +221,8 @@ def main():
     def step(i):
         p = sets[i % nsets]
         moe.layer_forward(s, p["x"], p["w_router"], p["b_router"], p["w_gate"], p["w_up"],
-                          p["w_down"], p["ws_gate"], p["ws_up"], p["ws_down"], y=y, ws=ws)
+                          p["w_down"], p["ws_gate"], p["ws_up"], p["ws_down"], y=y, ws=ws,
+                          padded=args.padded)
 
     # routing statistics for the work model
     _, rt = moe.layer_forward(s, d["x"], d["w_router"], d["b_router"], d["w_gate"], d["w_up"],
@@ -259,7 +262,7 @@ def main():
         moe.layer_forward_timed(s, p["x"], p["w_router"], p["b_router"], p["w_gate"], p["w_up"],
                                 p["w_down"], p["ws_gate"], p["ws_up"], p["ws_down"], y, ws,
                                 [None, None, g1_ev[2 * i], g1_ev[2 * i + 1], None, None, None],
-                                stream=stream)
+                                stream=stream, padded=args.padded)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms = (t1 - t0) * 1e3 / K
@@ -277,7 +280,8 @@ def main():
             p = sets[i % nsets]
             moe.layer_forward_timed(s, p["x"], p["w_router"], p["b_router"], p["w_gate"],
                                     p["w_up"], p["w_down"], p["ws_gate"], p["ws_up"],
-                                    p["ws_down"], y, ws, evs[7 * i:7 * i + 7], stream=stream)
+                                    p["ws_down"], y, ws, evs[7 * i:7 * i + 7], stream=stream,
+                                    padded=args.padded)
         torch.cuda.synchronize()
         acc = [0.0] * 6
         for i in range(K):
@@ -341,7 +345,7 @@ def main():
         roof["us_per_launch"] = round(g1_us, 2)
         roof["algorithmic_flops"] = flops
         roof["algorithmic_bytes"] = byts
-        roof["traffic"] = traffic_from_profile(w.name)
+        roof["traffic"] = None if args.padded else traffic_from_profile(w.name)
 
     cpu = None
     if not args.no_cpu:
@@ -363,6 +367,8 @@ def main():
         "config": {"workload": w.name, "T": w.T, "E": w.E, "k": w.k, "d": w.d, "d_ff": w.d_ff,
                    "d_ff_shared": w.d_ff_shared, "phi": w.phi, "renormalize": w.renorm,
                    "kept_routes": kept_rows, "weight_sets": nsets,
+                   "layout": "padded [E, C, d]" if args.padded else "packed",
+                   "padded_rows": (w.E * C) if (args.padded and C > 0) else None,
                    "parallelism": "single GPU"},
         "roofline": roof,
         "cpu_baseline": cpu,

@@ -194,6 +194,37 @@ int moe_layer_forward(const moe_shape* s, const void* x, const void* w_router,
                       int32_t* counts, int32_t* route_pos, void* ws, size_t ws_bytes,
                       hipStream_t stream);
 
+/* Fixed-shape dispatch buffer [E, C, d] ("Session 19: Mixture-of-Experts:
+ * routing and capacity", "Capacity": capacity is a tensor dimension, and the
+ * slot table of "Visual support -- Capacity"; "271,104 Routes", section 3
+ * "When one expert gets too many tokens": fixed expert buffers make shapes
+ * regular at the cost of padding).  The same counting-sort dispatch as
+ * moe_permute, written into the fixed buffer instead of packed rows:
+ *   route_pos[T*k]     row e*C + slot of the buffer for a kept route (slot =
+ *                      its arrival rank at expert e), -1 if dropped
+ *   x_padded[E*C][d]   x_padded[e*C + c] = x[token seated in slot c of e];
+ *                      empty slots are zero rows
+ *   counts, kept_counts as in moe_permute.
+ * Needs a capacity (phi > 0): otherwise MOE_ERR_INVALID_ARG.  E*C rows must
+ * fit 32-bit buffer offsets (else MOE_ERR_UNSUPPORTED). */
+int moe_permute_padded(const moe_shape* s, const void* x, const int32_t* expert_ids,
+                       int32_t* counts, int32_t* kept_counts, int32_t* route_pos, void* x_padded,
+                       void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* moe_layer_forward over the fixed-shape buffer: the expert FFNs run on all
+ * E*C rows of [E, C, d] (empty slots included -- the padding the pages
+ * price: E*C - sum_e m_e rows of work), then the same combine.  The output
+ * equals moe_layer_forward's for every kept route (padding rows are zero
+ * and never read back).  The optional route_pos output receives the
+ * buffer's rows e*C + slot.  Same arguments and errors as moe_layer_forward,
+ * plus those of moe_permute_padded. */
+int moe_layer_forward_padded(const moe_shape* s, const void* x, const void* w_router,
+                             const float* b_router, const void* w_gate, const void* w_up,
+                             const void* w_down, const void* ws_gate, const void* ws_up,
+                             const void* ws_down, void* y, int32_t* expert_ids, float* gates,
+                             int32_t* counts, int32_t* route_pos, void* ws, size_t ws_bytes,
+                             hipStream_t stream);
+
 /* Forward-only routing statistics of one batch of routes, from the outputs
  * of moe_route (logits must have been requested) and moe_permute (counts).
  *   "Mixture of Experts: Routing, Dispatch, and Load Balancing", section 4:
@@ -235,12 +266,14 @@ int moe_routing_stats(const moe_shape* s, const float* logits, const float* gate
  *   events[4] before the shared expert (equal to events[5] without one)
  *   events[5] before combine        events[6] after combine
  *   events     host array of 7 hipEvent_t created by the caller; a NULL
- *              entry is skipped.  The array itself must not be NULL. */
+ *              entry is skipped.  The array itself must not be NULL.
+ *   layout     0: packed rows (moe_layer_forward); 1: the fixed-shape
+ *              [E, C, d] buffer (moe_layer_forward_padded). */
 int moe_layer_forward_timed(const moe_shape* s, const void* x, const void* w_router,
                             const float* b_router, const void* w_gate, const void* w_up,
                             const void* w_down, const void* ws_gate, const void* ws_up,
                             const void* ws_down, void* y, void* ws, size_t ws_bytes,
-                            hipStream_t stream, hipEvent_t* events /*host*/);
+                            hipStream_t stream, hipEvent_t* events /*host*/, int32_t layout);
 
 #ifdef __cplusplus
 }

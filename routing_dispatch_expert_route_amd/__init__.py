@@ -30,7 +30,8 @@ MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP
 
 EXPORTS = ("moe_status_string", "moe_capacity", "moe_workspace_bytes", "moe_route",
            "moe_permute", "moe_expert_ffn", "moe_combine", "moe_layer_forward",
-           "moe_layer_forward_timed", "moe_routing_stats")
+           "moe_layer_forward_timed", "moe_routing_stats", "moe_permute_padded",
+           "moe_layer_forward_padded")
 
 
 class MoeShape(ctypes.Structure):
@@ -58,7 +59,9 @@ _lib.moe_permute.argtypes = [_SP] + [_vp] * 8 + [_vp, _sz, _vp]
 _lib.moe_expert_ffn.argtypes = [_SP] + [_vp] * 6 + [_vp, _sz, _vp]
 _lib.moe_combine.argtypes = [_SP] + [_vp] * 5 + [_vp]
 _lib.moe_layer_forward.argtypes = [_SP] + [_vp] * 14 + [_vp, _sz, _vp]
-_lib.moe_layer_forward_timed.argtypes = [_SP] + [_vp] * 10 + [_vp, _sz, _vp, _vp]
+_lib.moe_layer_forward_timed.argtypes = [_SP] + [_vp] * 10 + [_vp, _sz, _vp, _vp, ctypes.c_int32]
+_lib.moe_permute_padded.argtypes = [_SP] + [_vp] * 6 + [_vp, _sz, _vp]
+_lib.moe_layer_forward_padded.argtypes = [_SP] + [_vp] * 14 + [_vp, _sz, _vp]
 _lib.moe_routing_stats.argtypes = [_SP, _vp, _vp, _vp, ctypes.c_double, ctypes.c_int32, _vp, _vp,
                                    _vp, _sz, _vp]
 for _n in EXPORTS[1:]:
@@ -180,6 +183,28 @@ def permute(s, x, expert_ids, ws=None, stream=None):
     return out
 
 
+def permute_padded(s, x, expert_ids, ws=None, stream=None):
+    """Dispatch into the fixed-shape buffer [E, C, d].  Returns dict(counts,
+    kept_counts, route_pos (rows e*C + slot, -1 dropped), x_padded [E*C, d])."""
+    dt = _tdtype(s)
+    dev = x.device
+    C, _ = capacity(s)
+    if C <= 0:
+        raise ValueError("the fixed-shape buffer needs a capacity (phi > 0)")
+    xp = _ptr(x, "x", (s.T, s.d), dt)
+    ip = _ptr(expert_ids, "expert_ids", (s.T, s.k), torch.int32)
+    out = dict(counts=torch.empty(s.E, dtype=torch.int32, device=dev),
+               kept_counts=torch.empty(s.E, dtype=torch.int32, device=dev),
+               route_pos=torch.empty(s.T, s.k, dtype=torch.int32, device=dev),
+               x_padded=torch.empty(s.E * C, s.d, dtype=dt, device=dev))
+    ws = _ws(s, ws, dev)
+    _check(_lib.moe_permute_padded(ctypes.byref(s), xp, ip, out["counts"].data_ptr(),
+                                   out["kept_counts"].data_ptr(), _ptr(out["route_pos"], "route_pos"),
+                                   out["x_padded"].data_ptr(), ws.data_ptr(), ws.numel(),
+                                   _stream(stream)), "moe_permute_padded")
+    return out
+
+
 def expert_ffn(s, x_packed, offsets, w_gate, w_up, w_down, y_packed=None, ws=None, stream=None):
     """Grouped SwiGLU expert FFN over packed rows.  Returns y_packed [R_max, d]."""
     dt = _tdtype(s)
@@ -249,9 +274,10 @@ def stats_dict(s, stats, hist):
 
 
 def layer_forward(s, x, w_router, b_router, w_gate, w_up, w_down, ws_gate=None, ws_up=None,
-                  ws_down=None, y=None, ws=None, stream=None, return_routing=False):
+                  ws_down=None, y=None, ws=None, stream=None, return_routing=False, padded=False):
     """Whole MoE layer.  Returns y, or (y, dict(expert_ids, gates, counts,
-    route_pos)) with return_routing."""
+    route_pos)) with return_routing.  padded=True runs moe_layer_forward_padded
+    (fixed-shape [E, C, d] buffer; route_pos then holds its rows e*C + slot)."""
     dt = _tdtype(s)
     dev = x.device
     xp = _ptr(x, "x", (s.T, s.d), dt)
@@ -279,14 +305,15 @@ def layer_forward(s, x, w_router, b_router, w_gate, w_up, w_down, ws_gate=None, 
         cp = _ptr(routing["counts"], "counts")
         rpp = _ptr(routing["route_pos"], "route_pos")
     ws = _ws(s, ws, dev)
-    _check(_lib.moe_layer_forward(ctypes.byref(s), xp, rp, bp, gp, up, dp, sg, su, sd, yo, ip, gtp,
-                                  cp, rpp, ws.data_ptr(), ws.numel(), _stream(stream)),
-           "moe_layer_forward")
+    fn = _lib.moe_layer_forward_padded if padded else _lib.moe_layer_forward
+    _check(fn(ctypes.byref(s), xp, rp, bp, gp, up, dp, sg, su, sd, yo, ip, gtp, cp, rpp,
+              ws.data_ptr(), ws.numel(), _stream(stream)),
+           "moe_layer_forward_padded" if padded else "moe_layer_forward")
     return (y, routing) if return_routing else y
 
 
 def layer_forward_timed(s, x, w_router, b_router, w_gate, w_up, w_down, ws_gate, ws_up, ws_down,
-                        y, ws, events, stream=None):
+                        y, ws, events, stream=None, padded=False):
     """moe_layer_forward_timed: records the 7 stage-boundary hipEvents
     (`events`: sequence of raw hipEvent_t handles as ints)."""
     dt = _tdtype(s)
@@ -300,6 +327,7 @@ def layer_forward_timed(s, x, w_router, b_router, w_gate, w_up, w_down, ws_gate,
         _ptr(ws_gate, "ws_gate", (s.d_ff_shared, s.d), dt, optional=not shp),
         _ptr(ws_up, "ws_up", (s.d_ff_shared, s.d), dt, optional=not shp),
         _ptr(ws_down, "ws_down", (s.d, s.d_ff_shared), dt, optional=not shp),
-        _ptr(y, "y", (s.T, s.d), dt), ws.data_ptr(), ws.numel(), _stream(stream), arr),
+        _ptr(y, "y", (s.T, s.d), dt), ws.data_ptr(), ws.numel(), _stream(stream), arr,
+        1 if padded else 0),
         "moe_layer_forward_timed")
     return y

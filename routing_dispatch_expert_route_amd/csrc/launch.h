@@ -18,6 +18,13 @@ hipError_t launch_permute_index(const int32_t* ids, int T, int k, int E, int C, 
                                 int32_t* route_pos, int32_t* row_token, hipStream_t st);
 hipError_t launch_gather_rows(const void* x, const int32_t* row_token, const int32_t* offsets,
                               int E, long R_max, long row_bytes, void* x_packed, hipStream_t st);
+// Fixed-shape [E, C, d] buffer from a packed dispatch (needs C >= 1): padded
+// route positions, the buffer's rows (zero for empty slots) and its row
+// groups offsets_pad[e] = e*C.
+hipError_t launch_padded(const void* x, const int32_t* ids, const int32_t* route_pos,
+                         const int32_t* offsets, const int32_t* kept, const int32_t* row_token,
+                         int T, int k, int E, int C, long row_bytes, int32_t* pad_pos,
+                         void* x_pad, int32_t* offsets_pad, hipStream_t st);
 
 // Row groups of a grouped GEMM: device offsets[E+1] (never read on the
 // host), or one dense group of M_dense rows when offsets is null.

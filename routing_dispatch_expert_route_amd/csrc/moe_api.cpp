@@ -65,8 +65,9 @@ int64_t rmax_of(const moe_shape* s, int64_t C) {
 
 struct Layout {
   size_t logits, ids, gates, cnt, counts, kept, offsets, route_pos, row_token, h, yp, part, hs,
-      ys, spart, shist;
-  int splits;  // K splits of the routed down GEMM (fp32 partial planes when > 1)
+      ys, spart, shist, xpad, opad, ppos;
+  int splits;      // K splits of the routed down GEMM (fp32 partial planes when > 1)
+  int splits_pad;  // the same for the fixed-shape [E, C] layout
   size_t total;
 };
 
@@ -79,6 +80,30 @@ moe::GemmPlan routed_plan(const moe_shape* s, const int32_t* offsets, bool own_r
   long cap = (long)Rmax;
   if (own_routes) cap = (C >= 0 && C < s->T) ? (long)C : (long)s->T;
   return moe::GemmPlan{s->dtype == MOE_DTYPE_BF16, true, offsets, (int)s->E, 0, (long)Rmax, cap};
+}
+
+// Rows of the fixed-shape dispatch buffer [E, C, d] (0 without a capacity).
+int64_t rpad_of(const moe_shape* s) {
+  const int64_t C = capacity_of(s);
+  return C > 0 ? s->E * C : 0;
+}
+
+// The fixed-shape [E, C, d] buffer needs a capacity, and its rows must stay
+// within 32-bit buffer offsets like every other expert buffer.
+int validate_padded(const moe_shape* s) {
+  if (capacity_of(s) <= 0) return MOE_ERR_INVALID_ARG;
+  const int64_t eb = elem_bytes(s);
+  const int64_t wide = s->d > s->d_ff ? s->d : s->d_ff;
+  if (rpad_of(s) * wide * eb >= (int64_t(1) << 31)) return MOE_ERR_UNSUPPORTED;
+  return MOE_OK;
+}
+
+// Plan of the expert GEMMs over the fixed-shape buffer: E groups of C rows
+// (device offsets e*C), every row computed, empty slots included.
+moe::GemmPlan padded_plan(const moe_shape* s, const int32_t* offsets_pad) {
+  const int64_t C = capacity_of(s);
+  return moe::GemmPlan{s->dtype == MOE_DTYPE_BF16, true, offsets_pad, (int)s->E, 0,
+                       (long)rpad_of(s), (long)(C > 0 ? C : 0)};
 }
 
 Layout layout_of(const moe_shape* s) {
@@ -103,10 +128,21 @@ Layout layout_of(const moe_shape* s) {
   L.offsets = take((size_t)(s->E + 1) * sizeof(int32_t));
   L.route_pos = take(R * sizeof(int32_t));
   L.row_token = take((size_t)Rmax * sizeof(int32_t));
-  L.h = take((size_t)Rmax * s->d_ff * eb);
-  L.yp = take((size_t)Rmax * s->d * eb);
+  // expert rows: the packed layout's R_max rows, or the fixed-shape
+  // buffer's E*C rows when there is a capacity (the larger of the two)
+  const int64_t Rpad = rpad_of(s);
+  const size_t Rbig = (size_t)(Rpad > Rmax ? Rpad : Rmax);
+  L.h = take(Rbig * s->d_ff * eb);
+  L.yp = take(Rbig * s->d * eb);
   L.splits = moe::gemm_down_splits(routed_plan(s, nullptr, false), (int)s->d, (int)s->d_ff);
-  L.part = take(L.splits > 1 ? (size_t)L.splits * Rmax * s->d * sizeof(float) : 0);
+  L.splits_pad = Rpad > 0 ? moe::gemm_down_splits(padded_plan(s, nullptr), (int)s->d, (int)s->d_ff)
+                          : 1;
+  const size_t part_rows = (size_t)(L.splits > 1 ? L.splits * Rmax : 0);
+  const size_t part_rows_pad = (size_t)(L.splits_pad > 1 ? L.splits_pad * Rpad : 0);
+  L.part = take((part_rows > part_rows_pad ? part_rows : part_rows_pad) * s->d * sizeof(float));
+  L.xpad = take((size_t)Rpad * s->d * eb);
+  L.opad = take((size_t)(s->E + 1) * sizeof(int32_t));
+  L.ppos = take(R * sizeof(int32_t));
   L.hs = take((size_t)s->T * s->d_ff_shared * eb);
   L.ys = take(s->d_ff_shared > 0 ? (size_t)s->T * s->d * eb : 0);
   // routing statistics: one partial row per 64 tokens
@@ -203,6 +239,33 @@ int moe_permute(const moe_shape* s, const void* x, const int32_t* expert_ids, in
                                             s->d * elem_bytes(s), x_packed, stream));
 }
 
+int moe_permute_padded(const moe_shape* s, const void* x, const int32_t* expert_ids,
+                       int32_t* counts, int32_t* kept_counts, int32_t* route_pos, void* x_padded,
+                       void* ws, size_t ws_bytes, hipStream_t stream) {
+  int v = validate(s);
+  if (v != MOE_OK) return v;
+  if ((v = validate_padded(s)) != MOE_OK) return v;
+  const bool tok = s->T > 0;
+  if (!counts || !kept_counts || !x_padded || (tok && (!x || !expert_ids || !route_pos)))
+    return MOE_ERR_INVALID_ARG;
+  if (!aligned16(x) || !aligned16(x_padded)) return MOE_ERR_INVALID_ARG;
+  v = check_ws(s, ws, ws_bytes);
+  if (v != MOE_OK) return v;
+  const Layout L = layout_of(s);
+  const int64_t C = capacity_of(s);
+  int32_t* offsets = at<int32_t>(ws, L.offsets);
+  int32_t* rpos = at<int32_t>(ws, L.route_pos);
+  int32_t* row_token = at<int32_t>(ws, L.row_token);
+  hipError_t e = moe::launch_permute_index(expert_ids, (int)s->T, (int)s->k, (int)s->E, (int)C,
+                                           at<int32_t>(ws, L.cnt), counts, kept_counts, offsets,
+                                           rpos, row_token, stream);
+  if (e != hipSuccess) return MOE_ERR_HIP;
+  return hip_status(moe::launch_padded(x, expert_ids, rpos, offsets, kept_counts, row_token,
+                                       (int)s->T, (int)s->k, (int)s->E, (int)C,
+                                       s->d * elem_bytes(s), route_pos, x_padded,
+                                       at<int32_t>(ws, L.opad), stream));
+}
+
 int moe_expert_ffn(const moe_shape* s, const void* x_packed, const int32_t* offsets,
                    const void* w_gate, const void* w_up, const void* w_down, void* y_packed,
                    void* ws, size_t ws_bytes, hipStream_t stream) {
@@ -268,9 +331,10 @@ static int layer_forward_impl(const moe_shape* s, const void* x, const void* w_r
                               const void* w_down, const void* ws_gate, const void* ws_up,
                               const void* ws_down, void* y, int32_t* expert_ids, float* gates,
                               int32_t* counts, int32_t* route_pos, void* ws, size_t ws_bytes,
-                              hipStream_t stream, hipEvent_t* ev) {
+                              hipStream_t stream, hipEvent_t* ev, bool padded) {
   int v = validate(s);
   if (v != MOE_OK) return v;
+  if (padded && (v = validate_padded(s)) != MOE_OK) return v;
   if (!w_router || !w_gate || !w_up || !w_down || (s->T > 0 && (!x || !y)))
     return MOE_ERR_INVALID_ARG;
   const bool shared = s->d_ff_shared > 0;
@@ -291,7 +355,11 @@ static int layer_forward_impl(const moe_shape* s, const void* x, const void* w_r
   int32_t* ids = expert_ids ? expert_ids : at<int32_t>(ws, L.ids);
   float* g = gates ? gates : at<float>(ws, L.gates);
   int32_t* cnts = counts ? counts : at<int32_t>(ws, L.counts);
-  int32_t* rpos = route_pos ? route_pos : at<int32_t>(ws, L.route_pos);
+  // route positions: the caller's array receives the packed rows, or the
+  // fixed-shape buffer's rows e*C + slot (the packed ones then stay internal)
+  int32_t* rpos = (route_pos && !padded) ? route_pos : at<int32_t>(ws, L.route_pos);
+  int32_t* ppos = route_pos ? route_pos : at<int32_t>(ws, L.ppos);
+  const int64_t Rpad = rpad_of(s);
   int32_t* offsets = at<int32_t>(ws, L.offsets);
   int32_t* row_token = at<int32_t>(ws, L.row_token);
   void* h = at<void>(ws, L.h);
@@ -308,17 +376,29 @@ static int layer_forward_impl(const moe_shape* s, const void* x, const void* w_r
   e = moe::launch_permute_index(ids, T, k, E, (int)C, at<int32_t>(ws, L.cnt), cnts,
                                 at<int32_t>(ws, L.kept), offsets, rpos, row_token, stream);
   if (e != hipSuccess) return MOE_ERR_HIP;
-  const moe::GemmPlan pl = routed_plan(s, offsets, true);
+  if (padded) {
+    e = moe::launch_padded(x, ids, rpos, offsets, at<int32_t>(ws, L.kept), row_token, T, k, E,
+                           (int)C, (long)d * elem_bytes(s), ppos, at<void>(ws, L.xpad),
+                           at<int32_t>(ws, L.opad), stream);
+    if (e != hipSuccess) return MOE_ERR_HIP;
+  }
+  const moe::GemmPlan pl =
+      padded ? padded_plan(s, at<int32_t>(ws, L.opad)) : routed_plan(s, offsets, true);
   mark(2);
-  e = moe::launch_gemm_swiglu(pl, x, row_token, T, w_gate, w_up, dff, d, h, stream);
+  if (padded)
+    e = moe::launch_gemm_swiglu(pl, at<void>(ws, L.xpad), nullptr, Rpad, w_gate, w_up, dff, d, h,
+                                stream);
+  else
+    e = moe::launch_gemm_swiglu(pl, x, row_token, T, w_gate, w_up, dff, d, h, stream);
   if (e != hipSuccess) return MOE_ERR_HIP;
   mark(3);
   // the split decision depends on the shape only (same as the workspace)
+  const int splits = padded ? L.splits_pad : L.splits;
   const void* yrows = yp;
-  const long stride = (long)Rmax * d;
-  if (L.splits > 1) {
+  const long stride = (long)(padded ? Rpad : Rmax) * d;
+  if (splits > 1) {
     yrows = at<float>(ws, L.part);
-    e = moe::launch_gemm_down(pl, h, w_down, d, dff, at<float>(ws, L.part), L.splits, stride,
+    e = moe::launch_gemm_down(pl, h, w_down, d, dff, at<float>(ws, L.part), splits, stride,
                               stream);
   } else {
     e = moe::launch_gemm_down(pl, h, w_down, d, dff, yp, 1, 0, stream);
@@ -338,7 +418,8 @@ static int layer_forward_impl(const moe_shape* s, const void* x, const void* w_r
     ysh = ys;
   }
   mark(5);
-  e = moe::launch_combine(bf16, yrows, L.splits, stride, rpos, g, ysh, T, k, d, y, stream);
+  e = moe::launch_combine(bf16, yrows, splits, stride, padded ? ppos : rpos, g, ysh, T, k, d, y,
+                         stream);
   if (e != hipSuccess) return MOE_ERR_HIP;
   mark(6);
   return MOE_OK;
@@ -352,18 +433,30 @@ int moe_layer_forward(const moe_shape* s, const void* x, const void* w_router,
                       hipStream_t stream) {
   return layer_forward_impl(s, x, w_router, b_router, w_gate, w_up, w_down, ws_gate, ws_up,
                             ws_down, y, expert_ids, gates, counts, route_pos, ws, ws_bytes,
-                            stream, nullptr);
+                            stream, nullptr, false);
+}
+
+int moe_layer_forward_padded(const moe_shape* s, const void* x, const void* w_router,
+                             const float* b_router, const void* w_gate, const void* w_up,
+                             const void* w_down, const void* ws_gate, const void* ws_up,
+                             const void* ws_down, void* y, int32_t* expert_ids, float* gates,
+                             int32_t* counts, int32_t* route_pos, void* ws, size_t ws_bytes,
+                             hipStream_t stream) {
+  return layer_forward_impl(s, x, w_router, b_router, w_gate, w_up, w_down, ws_gate, ws_up,
+                            ws_down, y, expert_ids, gates, counts, route_pos, ws, ws_bytes,
+                            stream, nullptr, true);
 }
 
 int moe_layer_forward_timed(const moe_shape* s, const void* x, const void* w_router,
                             const float* b_router, const void* w_gate, const void* w_up,
                             const void* w_down, const void* ws_gate, const void* ws_up,
                             const void* ws_down, void* y, void* ws, size_t ws_bytes,
-                            hipStream_t stream, hipEvent_t* events) {
+                            hipStream_t stream, hipEvent_t* events, int32_t layout) {
   if (!events) return MOE_ERR_INVALID_ARG;
+  if (layout != 0 && layout != 1) return MOE_ERR_INVALID_ARG;
   return layer_forward_impl(s, x, w_router, b_router, w_gate, w_up, w_down, ws_gate, ws_up,
                             ws_down, y, nullptr, nullptr, nullptr, nullptr, ws, ws_bytes, stream,
-                            events);
+                            events, layout == 1);
 }
 
 }  // extern "C"

@@ -271,6 +271,71 @@ __global__ __launch_bounds__(256) void gather_rows_kernel(const u32x4_t* __restr
   }
 }
 
+// Fixed-shape dispatch buffer [E, C, d] ("Session 19", "Capacity": capacity
+// is a tensor dimension; slot table of "Visual support -- Capacity").  From
+// the packed dispatch: a kept route r of expert e at packed row p sits in
+// slot p - offsets[e] of e, i.e. row e*C + slot of the buffer.
+__global__ __launch_bounds__(256) void padded_index_kernel(const int32_t* __restrict__ route_pos,
+                                                           const int32_t* __restrict__ ids,
+                                                           const int32_t* __restrict__ offsets,
+                                                           int R, int C,
+                                                           int32_t* __restrict__ pad_pos) {
+  const int r = blockIdx.x * blockDim.x + threadIdx.x;
+  if (r >= R) return;
+  const int p = route_pos[r];
+  if (p < 0) {
+    pad_pos[r] = -1;
+    return;
+  }
+  const int e = ids[r];
+  pad_pos[r] = e * C + (p - offsets[e]);
+}
+
+// x_pad[e*C + c] = x[row_token[offsets[e] + c]] for c < kept[e], zero rows
+// for the empty slots; offsets_pad[e] = e*C (the buffer's row groups).
+__global__ __launch_bounds__(256) void fill_padded_kernel(const u32x4_t* __restrict__ x,
+                                                          const int32_t* __restrict__ row_token,
+                                                          const int32_t* __restrict__ offsets,
+                                                          const int32_t* __restrict__ kept, int E,
+                                                          int C, int cpr, long total,
+                                                          u32x4_t* __restrict__ x_pad,
+                                                          int32_t* __restrict__ offsets_pad) {
+  const long g0 = (long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (g0 <= E) offsets_pad[g0] = (int32_t)(g0 * C);
+  const u32x4_t zero = {0u, 0u, 0u, 0u};
+  for (long g = g0; g < total; g += (long)gridDim.x * blockDim.x) {
+    const long p = g / cpr;
+    const int ch = (int)(g - p * cpr);
+    const int e = (int)(p / C);
+    const int c = (int)(p - (long)e * C);
+    x_pad[g] = c < kept[e] ? x[(long)row_token[offsets[e] + c] * cpr + ch] : zero;
+  }
+}
+
+hipError_t launch_padded(const void* x, const int32_t* ids, const int32_t* route_pos,
+                         const int32_t* offsets, const int32_t* kept, const int32_t* row_token,
+                         int T, int k, int E, int C, long row_bytes, int32_t* pad_pos,
+                         void* x_pad, int32_t* offsets_pad, hipStream_t st) {
+  const int R = T * k;
+  if (R > 0) {
+    hipLaunchKernelGGL(padded_index_kernel, dim3(ceil_div(R, 256)), dim3(256), 0, st, route_pos,
+                       ids, offsets, R, C, pad_pos);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+  }
+  const int cpr = (int)(row_bytes / 16);
+  const long total = (long)E * C * cpr;
+  long blocks = (total + 255) / 256;
+  if (blocks > 8192) blocks = 8192;
+  // offsets_pad (E + 1 entries) is written by the first threads, even when
+  // the buffer has no rows
+  if (blocks < (E + 256) / 256) blocks = (E + 256) / 256;
+  hipLaunchKernelGGL(fill_padded_kernel, dim3((unsigned)blocks), dim3(256), 0, st,
+                     reinterpret_cast<const u32x4_t*>(x), row_token, offsets, kept, E, C, cpr, total,
+                     reinterpret_cast<u32x4_t*>(x_pad), offsets_pad);
+  return hipGetLastError();
+}
+
 int permute_nchunks(long R) { return (int)((R + kChunk - 1) / kChunk); }
 
 hipError_t launch_permute_index(const int32_t* ids, int T, int k, int E, int C, int32_t* cnt_ws,

@@ -179,3 +179,22 @@ def test_routing_stats_rejected_before_launch():
     # workspace too small
     assert L.moe_routing_stats(by, fake, fake, fake, 0.01, 8, fake, fake, ok_ws, need - 1, None) \
         == moe.MOE_ERR_WORKSPACE
+
+
+def test_padded_entry_points_need_a_capacity():
+    moe = _moe()
+    s = moe.shape(16, 64, 4, 2, 64)  # phi = 0: dropless, no fixed buffer
+    by = ctypes.byref(s)
+    L = moe._lib
+    fake, ws = 4096, 1 << 20
+    need = moe.workspace_bytes(s)
+    assert L.moe_permute_padded(by, fake, fake, fake, fake, fake, fake, ws, need, None) \
+        == moe.MOE_ERR_INVALID_ARG
+    assert L.moe_layer_forward_padded(by, fake, fake, None, fake, fake, fake, None, None, None,
+                                      fake, None, None, None, None, ws, need, None) \
+        == moe.MOE_ERR_INVALID_ARG
+    # with a capacity the buffer's rows enter the workspace: E*C >= R_max
+    sc = moe.shape(16, 64, 4, 2, 64, phi=2.0)
+    C, R = moe.capacity(sc)
+    assert 4 * C >= R
+    assert moe.workspace_bytes(sc) >= moe.workspace_bytes(s)
