@@ -57,6 +57,8 @@ def lib():
         L.oracle_combine.argtypes = [_i64, _i64, _i64, _int, _vp, _vp, _vp, _vp, _vp]
         L.oracle_dispatch_padded.restype = None
         L.oracle_dispatch_padded.argtypes = [_i64, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _vp]
+        L.oracle_dispatch_reroute.restype = None
+        L.oracle_dispatch_reroute.argtypes = [_i64, _i64, _i64, _i64] + [_vp] * 9
         L.oracle_routing_stats.restype = None
         L.oracle_routing_stats.argtypes = [_i64, _i64, _i64, _vp, _vp, _vp, _dbl, ctypes.c_int32,
                                            _vp, _vp, _vp, _vp]
@@ -152,6 +154,28 @@ def dispatch_padded(expert_ids, E, C):
                                  _p(pad_pos), _p(slot_token))
     d.update(pad_pos=pad_pos.reshape(T, k), slot_token=slot_token[:E * C].reshape(E, C))
     return d
+
+
+def dispatch_reroute(logits, expert_ids, E, C):
+    """Drop-then-reroute dispatch.  Returns dict(ids, counts, filled, offsets,
+    route_pos [T, k], row_token, n_rerouted)."""
+    la = np.ascontiguousarray(logits, dtype=np.float32)
+    ids = np.ascontiguousarray(expert_ids, dtype=np.int32)
+    T, k = ids.shape
+    ids_out = np.empty_like(ids)
+    counts = np.empty(E, np.int32)
+    filled = np.empty(E, np.int32)
+    offsets = np.empty(E + 1, np.int32)
+    route_pos = np.empty(T * k, np.int32)
+    row_token = np.full(max(T * k, 1), -1, np.int32)
+    moved = np.zeros(1, np.int64)
+    lib().oracle_dispatch_reroute(T, E, k, int(C), _p(la), _p(ids), _p(ids_out), _p(counts),
+                                  _p(filled), _p(offsets), _p(route_pos), _p(row_token),
+                                  _p(moved))
+    n = int(offsets[E])
+    return dict(ids=ids_out, counts=counts, filled=filled, offsets=offsets,
+                route_pos=route_pos.reshape(T, k), row_token=row_token[:n].copy(),
+                n_rerouted=int(moved[0]))
 
 
 def gather_rows(x, row_token):

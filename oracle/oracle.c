@@ -174,6 +174,62 @@ void oracle_dispatch_padded(int64_t T, int64_t E, int64_t k, int64_t C,
   }
 }
 
+void oracle_dispatch_reroute(int64_t T, int64_t E, int64_t k, int64_t C,
+                             const float* logits, const int32_t* ids_in,
+                             int32_t* ids_out, int32_t* counts, int32_t* filled,
+                             int32_t* offsets, int32_t* route_pos,
+                             int32_t* row_token, int64_t* n_rerouted) {
+  int64_t R = T * k;
+  size_t nR = (size_t)(R > 0 ? R : 1);
+  int32_t* kept = (int32_t*)malloc((size_t)E * sizeof(int32_t));
+  int32_t* offs0 = (int32_t*)malloc((size_t)(E + 1) * sizeof(int32_t));
+  int32_t* pos0 = (int32_t*)malloc(nR * sizeof(int32_t));
+  int64_t* slot = (int64_t*)malloc(nR * sizeof(int64_t));
+  /* pass 1: the drop policy */
+  oracle_dispatch(T, E, k, C, ids_in, counts, kept, offs0, pos0, NULL);
+  for (int64_t e = 0; e < E; e++) filled[e] = kept[e];
+  for (int64_t r = 0; r < R; r++) {
+    ids_out[r] = ids_in[r];
+    slot[r] = pos0[r] >= 0 ? pos0[r] - offs0[ids_in[r]] : -1;
+  }
+  /* pass 2: dropped routes in arrival order take the best expert with room */
+  int64_t moved = 0;
+  for (int64_t r = 0; r < R; r++) {
+    if (slot[r] >= 0) continue;
+    int64_t t = r / k;
+    const float* l = logits + t * E;
+    int64_t best = -1;
+    for (int64_t e = 0; e < E; e++) {
+      if (C >= 0 && filled[e] >= C) continue; /* no room */
+      int held = 0;
+      for (int64_t j = 0; j < k; j++) held |= (ids_out[t * k + j] == e);
+      if (held) continue;
+      if (best < 0 || l[e] > l[best]) best = e; /* strict >: lower index on ties */
+    }
+    if (best < 0) continue; /* stays dropped */
+    ids_out[r] = (int32_t)best;
+    slot[r] = filled[best];
+    filled[best] += 1;
+    moved += 1;
+  }
+  offsets[0] = 0;
+  for (int64_t e = 0; e < E; e++) offsets[e + 1] = offsets[e] + filled[e];
+  for (int64_t r = 0; r < R; r++) {
+    if (slot[r] < 0) {
+      route_pos[r] = -1;
+      continue;
+    }
+    int32_t p = (int32_t)(offsets[ids_out[r]] + slot[r]);
+    route_pos[r] = p;
+    if (row_token) row_token[p] = (int32_t)(r / k);
+  }
+  if (n_rerouted) *n_rerouted = moved;
+  free(kept);
+  free(offs0);
+  free(pos0);
+  free(slot);
+}
+
 void oracle_gather_rows(int64_t n_rows, int64_t d, int64_t elem_bytes,
                         const void* x, const int32_t* row_token,
                         void* packed) {

@@ -113,6 +113,32 @@ void oracle_dispatch_padded(int64_t T, int64_t E, int64_t k, int64_t C,
                             const int32_t* offsets, int32_t* pad_pos,
                             int32_t* slot_token);
 
+/* Overflow policy "reroute" ("Session 19", "Overflow policies": the
+ * overflowing route is handled by the token's next-best expert; the router
+ * decision is overridden).  Reading: routes keep the seats the drop policy
+ * gives them (oracle_dispatch); then the dropped routes, in arrival order
+ * r = t*k + j, each move to the best-ranked expert of token t (logit
+ * descending, lower index first on ties) that t does not already hold and
+ * that still has room, taking its next free slot; with no such expert the
+ * route stays dropped.  Its gate is unchanged.
+ *   ids_out[T*k]     the expert of every route after rerouting
+ *   counts[E]        demand of the original choices (before capacity)
+ *   filled[E]        seats used per expert (kept + rerouted, <= C)
+ *   offsets[E+1]     exclusive prefix of filled
+ *   route_pos[T*k]   packed row: kept routes first in each expert (arrival
+ *                    order), then its rerouted routes (arrival order); -1
+ *                    if dropped after all
+ *   row_token[p]     source token of packed row p
+ *   n_rerouted       (out) routes moved
+ * Pinned by the trace (t6 at E1 goes to its third choice) and by invariants
+ * of the greedy order (no expert over C; every expert a rerouted route
+ * preferred, and every expert a dropped route could take, is full). */
+void oracle_dispatch_reroute(int64_t T, int64_t E, int64_t k, int64_t C,
+                             const float* logits, const int32_t* ids_in,
+                             int32_t* ids_out, int32_t* counts, int32_t* filled,
+                             int32_t* offsets, int32_t* route_pos,
+                             int32_t* row_token, int64_t* n_rerouted);
+
 /* Row duplication: packed[p][:] = x[row_token[p]][:] for p < n_rows, a bit
  * copy of elem_bytes-sized elements ([MML] section 3: index_select). */
 void oracle_gather_rows(int64_t n_rows, int64_t d, int64_t elem_bytes,

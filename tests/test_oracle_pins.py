@@ -569,3 +569,102 @@ def test_padded_positions_follow_arrival_order(seed):
             seen[e] += 1
         else:
             assert out["pad_pos"][t, j] == -1
+
+
+def test_reroute_trace_spk():
+    """"Session 19", "Overflow policies": with C = 5, t6 finds E1 full; under
+    the reroute policy its route goes to its third-best expert (it already
+    holds E2) -- E3 here -- and every one of the 16 routes is seated."""
+    g = G.load("spk_capacity_trace.txt")
+    assign = G.rows(g["assign"], int)
+    T, E, k = 8, 4, 2
+    L = np.full((T, E), 0.2, np.float32)
+    for t, (a, b) in enumerate(assign):
+        L[t, a], L[t, b] = 2.1, 1.8
+    third = 2 if 2 not in assign[5] else 3
+    L[5, third] = 0.9   # third-best of t6 (its pair comes first)
+    ids = np.array(assign, np.int32)
+    C = oracle.capacity(T, E, k, 1.25)
+    out = oracle.dispatch_reroute(L, ids, E, C)
+    assert out["n_rerouted"] == 1
+    assert out["ids"][5].tolist() == [third, 1]
+    assert out["filled"].tolist() == [5, 4, 4, 3]
+    assert int(out["offsets"][E]) == 16
+    # E3's seats: t2, t5, t8 kept, then t6 in the fourth slot
+    lo = out["offsets"][third]
+    assert out["row_token"][lo:lo + 4].tolist() == G.nums(g[f"slots_E{third}"], int) + [5]
+
+
+def _reroute_invariants(L, ids, E, C, out, ref):
+    T, k = ids.shape
+    fids, rp = out["ids"], out["route_pos"]
+    filled = out["filled"]
+    assert (filled <= C).all()
+    seated = rp >= 0
+    assert np.array_equal(np.bincount(fids[seated], minlength=E), filled)
+    for t in range(T):
+        assert len(set(fids[t].tolist())) == k, "a token holds an expert twice"
+    order = lambda t: sorted(range(E), key=lambda e: (-float(L[t, e]), e))
+    for t in range(T):
+        for j in range(k):
+            e0, e1 = ids[t, j], fids[t, j]
+            if ref["route_pos"][t, j] >= 0:
+                # kept by the drop policy: same expert, same slot
+                assert e1 == e0 and rp[t, j] - out["offsets"][e1] == ref["route_pos"][t, j] - ref["offsets"][e0]
+                continue
+            others = set(fids[t].tolist()) - {e1}
+            if rp[t, j] >= 0:       # rerouted: every preferred free choice is full now
+                assert e1 != e0
+                for e in order(t):
+                    if e == e1:
+                        break
+                    if e not in others and e != e0:
+                        assert filled[e] == C, (t, j, e)
+            else:                   # still dropped: nothing it could take has room
+                for e in range(E):
+                    if e not in others and e != e0:
+                        assert filled[e] == C
+    # packed rows: kept routes of an expert first, then its rerouted ones,
+    # each group in arrival order
+    for e in range(E):
+        lo, hi = out["offsets"][e], out["offsets"][e + 1]
+        rows = [(int(rp[t, j]), t * k + j, ref["route_pos"][t, j] >= 0)
+                for t in range(T) for j in range(k) if fids[t, j] == e and rp[t, j] >= 0]
+        rows.sort()
+        assert [r[0] for r in rows] == list(range(lo, hi))
+        flags = [r[2] for r in rows]
+        assert flags == sorted(flags, reverse=True)
+        kept_routes = [r[1] for r in rows if r[2]]
+        moved_routes = [r[1] for r in rows if not r[2]]
+        assert kept_routes == sorted(kept_routes) and moved_routes == sorted(moved_routes)
+        for p, r, _ in rows:
+            assert out["row_token"][p] == r // k
+
+
+@pytest.mark.parametrize("T,E,k,phi,seed", [(40, 4, 2, 0.6, 0), (64, 8, 2, 0.5, 1),
+                                            (50, 8, 1, 0.7, 2), (30, 16, 4, 0.3, 3),
+                                            (25, 4, 4, 0.5, 4)])
+def test_reroute_greedy_invariants(T, E, k, phi, seed):
+    rng = np.random.default_rng(seed)
+    L = rng.standard_normal((T, E)).astype(np.float32)
+    L[:, 0] += 1.5                                  # a popular expert: many overflows
+    L[rng.random((T, E)) < 0.1] = 0.25              # and some exact ties
+    ids, _ = oracle.topk_gates(L, k, 1)
+    C = oracle.capacity(T, E, k, phi)
+    ref = oracle.dispatch(ids, E, C)
+    out = oracle.dispatch_reroute(L, ids, E, C)
+    assert np.array_equal(out["counts"], ref["counts"])
+    _reroute_invariants(L, ids, E, C, out, ref)
+    assert out["n_rerouted"] == int((ref["route_pos"] < 0).sum()) - int((out["route_pos"] < 0).sum())
+
+
+def test_reroute_without_overflow_is_the_drop_policy():
+    T, E, k = 32, 8, 2
+    L = np.random.default_rng(9).standard_normal((T, E)).astype(np.float32)
+    ids, _ = oracle.topk_gates(L, k, 1)
+    C = oracle.capacity(T, E, k, 4.0)
+    ref = oracle.dispatch(ids, E, C)
+    out = oracle.dispatch_reroute(L, ids, E, C)
+    assert out["n_rerouted"] == 0
+    assert np.array_equal(out["route_pos"], ref["route_pos"])
+    assert np.array_equal(out["ids"], ids)
