@@ -182,6 +182,8 @@ def main():
     ap.add_argument("--no-stages", action="store_true")
     ap.add_argument("--padded", action="store_true",
                     help="fixed-shape [E, C, d] dispatch buffer instead of packed rows")
+    ap.add_argument("--reroute", action="store_true",
+                    help="reroute overflow policy (dropped routes move to the next-best expert with room)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB")
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
     ap.add_argument("--traffic-out", default=None)
@@ -222,15 +224,22 @@ def main():
         p = sets[i % nsets]
         moe.layer_forward(s, p["x"], p["w_router"], p["b_router"], p["w_gate"], p["w_up"],
                           p["w_down"], p["ws_gate"], p["ws_up"], p["ws_down"], y=y, ws=ws,
-                          padded=args.padded)
+                          padded=args.padded, reroute=args.reroute)
 
     # routing statistics for the work model
     _, rt = moe.layer_forward(s, d["x"], d["w_router"], d["b_router"], d["w_gate"], d["w_up"],
                               d["w_down"], d["ws_gate"], d["ws_up"], d["ws_down"],
                               return_routing=True)
+    if args.reroute:
+        _, rt_r = moe.layer_forward(s, d["x"], d["w_router"], d["b_router"], d["w_gate"],
+                                    d["w_up"], d["w_down"], d["ws_gate"], d["ws_up"],
+                                    d["ws_down"], return_routing=True, reroute=True)
     counts = rt["counts"].cpu().long()
     C, _ = moe.capacity(s)
     kept = counts.clamp(max=C) if C >= 0 else counts
+    if args.reroute:  # seated rows per expert after rerouting
+        seated = rt_r["route_pos"].cpu().flatten() >= 0
+        kept = torch.bincount(rt_r["expert_ids"].cpu().flatten().long()[seated], minlength=w.E)
     kept_rows = int(kept.sum())
     active = int((kept > 0).sum())
 
@@ -262,7 +271,7 @@ def main():
         moe.layer_forward_timed(s, p["x"], p["w_router"], p["b_router"], p["w_gate"], p["w_up"],
                                 p["w_down"], p["ws_gate"], p["ws_up"], p["ws_down"], y, ws,
                                 [None, None, g1_ev[2 * i], g1_ev[2 * i + 1], None, None, None],
-                                stream=stream, padded=args.padded)
+                                stream=stream, padded=args.padded, reroute=args.reroute)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms = (t1 - t0) * 1e3 / K
@@ -281,7 +290,7 @@ def main():
             moe.layer_forward_timed(s, p["x"], p["w_router"], p["b_router"], p["w_gate"],
                                     p["w_up"], p["w_down"], p["ws_gate"], p["ws_up"],
                                     p["ws_down"], y, ws, evs[7 * i:7 * i + 7], stream=stream,
-                                    padded=args.padded)
+                                    padded=args.padded, reroute=args.reroute)
         torch.cuda.synchronize()
         acc = [0.0] * 6
         for i in range(K):
@@ -345,7 +354,7 @@ def main():
         roof["us_per_launch"] = round(g1_us, 2)
         roof["algorithmic_flops"] = flops
         roof["algorithmic_bytes"] = byts
-        roof["traffic"] = None if args.padded else traffic_from_profile(w.name)
+        roof["traffic"] = None if (args.padded or args.reroute) else traffic_from_profile(w.name)
 
     cpu = None
     if not args.no_cpu:
@@ -368,6 +377,7 @@ def main():
                    "d_ff_shared": w.d_ff_shared, "phi": w.phi, "renormalize": w.renorm,
                    "kept_routes": kept_rows, "weight_sets": nsets,
                    "layout": "padded [E, C, d]" if args.padded else "packed",
+                   "overflow": "reroute" if args.reroute else "drop",
                    "padded_rows": (w.E * C) if (args.padded and C > 0) else None,
                    "parallelism": "single GPU"},
         "roofline": roof,

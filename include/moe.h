@@ -225,6 +225,41 @@ int moe_layer_forward_padded(const moe_shape* s, const void* x, const void* w_ro
                              int32_t* counts, int32_t* route_pos, void* ws, size_t ws_bytes,
                              hipStream_t stream);
 
+/* Overflow policy "reroute" ("Session 19: Mixture-of-Experts: routing and
+ * capacity", "Overflow policies": the overflowing route is handled by the
+ * token's next-best expert, the router decision overridden; "271,104
+ * Routes", section 3: an overflowing expert's routes are dropped, rerouted,
+ * given more room or handled dynamically).  Routes keep the seats of the drop
+ * policy (moe_permute); then the dropped routes, in arrival order r = t*k + j,
+ * each take the best-ranked expert of token t (logit descending, lower index
+ * first on ties) that t does not already hold and that still has room (<= C
+ * seats); without one the route stays dropped.  Gates are not changed.
+ * Inputs: logits [T][E] and expert_ids [T][k] from moe_route.
+ * Outputs: expert_ids_out [T][k] the expert of every route after rerouting;
+ *   counts [E] demand of the router's choices (before capacity); filled [E]
+ *   seats used per expert; offsets [E+1] their exclusive prefix; route_pos
+ *   [T][k] packed row (an expert's kept routes first, then its rerouted
+ *   ones, each in arrival order), -1 if dropped; row_token [R_max];
+ *   x_packed [R_max][d] as in moe_permute.
+ * E <= 64 (else MOE_ERR_UNSUPPORTED).  The walk over the dropped routes is
+ * sequential by definition (one wave). */
+int moe_permute_reroute(const moe_shape* s, const void* x, const float* logits,
+                        const int32_t* expert_ids, int32_t* expert_ids_out, int32_t* counts,
+                        int32_t* filled, int32_t* offsets, int32_t* route_pos,
+                        int32_t* row_token, void* x_packed, void* ws, size_t ws_bytes,
+                        hipStream_t stream);
+
+/* moe_layer_forward with the reroute overflow policy (moe_permute_reroute
+ * in place of moe_permute).  expert_ids receives the experts after
+ * rerouting, counts the demand of the router's choices, route_pos the
+ * rerouted packed rows.  E <= 64. */
+int moe_layer_forward_reroute(const moe_shape* s, const void* x, const void* w_router,
+                              const float* b_router, const void* w_gate, const void* w_up,
+                              const void* w_down, const void* ws_gate, const void* ws_up,
+                              const void* ws_down, void* y, int32_t* expert_ids, float* gates,
+                              int32_t* counts, int32_t* route_pos, void* ws, size_t ws_bytes,
+                              hipStream_t stream);
+
 /* Forward-only routing statistics of one batch of routes, from the outputs
  * of moe_route (logits must have been requested) and moe_permute (counts).
  *   "Mixture of Experts: Routing, Dispatch, and Load Balancing", section 4:
@@ -268,7 +303,8 @@ int moe_routing_stats(const moe_shape* s, const float* logits, const float* gate
  *   events     host array of 7 hipEvent_t created by the caller; a NULL
  *              entry is skipped.  The array itself must not be NULL.
  *   layout     0: packed rows (moe_layer_forward); 1: the fixed-shape
- *              [E, C, d] buffer (moe_layer_forward_padded). */
+ *              [E, C, d] buffer (moe_layer_forward_padded); 2: the reroute
+ *              overflow policy (moe_layer_forward_reroute). */
 int moe_layer_forward_timed(const moe_shape* s, const void* x, const void* w_router,
                             const float* b_router, const void* w_gate, const void* w_up,
                             const void* w_down, const void* ws_gate, const void* ws_up,

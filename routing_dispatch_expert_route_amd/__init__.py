@@ -31,7 +31,7 @@ MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP
 EXPORTS = ("moe_status_string", "moe_capacity", "moe_workspace_bytes", "moe_route",
            "moe_permute", "moe_expert_ffn", "moe_combine", "moe_layer_forward",
            "moe_layer_forward_timed", "moe_routing_stats", "moe_permute_padded",
-           "moe_layer_forward_padded")
+           "moe_layer_forward_padded", "moe_permute_reroute", "moe_layer_forward_reroute")
 
 
 class MoeShape(ctypes.Structure):
@@ -62,6 +62,8 @@ _lib.moe_layer_forward.argtypes = [_SP] + [_vp] * 14 + [_vp, _sz, _vp]
 _lib.moe_layer_forward_timed.argtypes = [_SP] + [_vp] * 10 + [_vp, _sz, _vp, _vp, ctypes.c_int32]
 _lib.moe_permute_padded.argtypes = [_SP] + [_vp] * 6 + [_vp, _sz, _vp]
 _lib.moe_layer_forward_padded.argtypes = [_SP] + [_vp] * 14 + [_vp, _sz, _vp]
+_lib.moe_permute_reroute.argtypes = [_SP] + [_vp] * 10 + [_vp, _sz, _vp]
+_lib.moe_layer_forward_reroute.argtypes = [_SP] + [_vp] * 14 + [_vp, _sz, _vp]
 _lib.moe_routing_stats.argtypes = [_SP, _vp, _vp, _vp, ctypes.c_double, ctypes.c_int32, _vp, _vp,
                                    _vp, _sz, _vp]
 for _n in EXPORTS[1:]:
@@ -205,6 +207,34 @@ def permute_padded(s, x, expert_ids, ws=None, stream=None):
     return out
 
 
+def permute_reroute(s, x, logits, expert_ids, ws=None, stream=None):
+    """Dispatch with the reroute overflow policy.  Returns dict(expert_ids
+    (after rerouting), counts (demand), filled, offsets, route_pos, row_token,
+    x_packed)."""
+    dt = _tdtype(s)
+    dev = x.device
+    _, R_max = capacity(s)
+    xp = _ptr(x, "x", (s.T, s.d), dt)
+    lp = _ptr(logits, "logits", (s.T, s.E), torch.float32)
+    ip = _ptr(expert_ids, "expert_ids", (s.T, s.k), torch.int32)
+    out = dict(expert_ids=torch.empty(s.T, s.k, dtype=torch.int32, device=dev),
+               counts=torch.empty(s.E, dtype=torch.int32, device=dev),
+               filled=torch.empty(s.E, dtype=torch.int32, device=dev),
+               offsets=torch.empty(s.E + 1, dtype=torch.int32, device=dev),
+               route_pos=torch.empty(s.T, s.k, dtype=torch.int32, device=dev),
+               row_token=torch.empty(max(R_max, 1), dtype=torch.int32, device=dev),
+               x_packed=torch.empty(max(R_max, 1), s.d, dtype=dt, device=dev))
+    ws = _ws(s, ws, dev)
+    _check(_lib.moe_permute_reroute(ctypes.byref(s), xp, lp, ip,
+                                    _ptr(out["expert_ids"], "expert_ids_out"),
+                                    out["counts"].data_ptr(), out["filled"].data_ptr(),
+                                    out["offsets"].data_ptr(), _ptr(out["route_pos"], "route_pos"),
+                                    out["row_token"].data_ptr(), out["x_packed"].data_ptr(),
+                                    ws.data_ptr(), ws.numel(), _stream(stream)),
+           "moe_permute_reroute")
+    return out
+
+
 def expert_ffn(s, x_packed, offsets, w_gate, w_up, w_down, y_packed=None, ws=None, stream=None):
     """Grouped SwiGLU expert FFN over packed rows.  Returns y_packed [R_max, d]."""
     dt = _tdtype(s)
@@ -274,10 +304,13 @@ def stats_dict(s, stats, hist):
 
 
 def layer_forward(s, x, w_router, b_router, w_gate, w_up, w_down, ws_gate=None, ws_up=None,
-                  ws_down=None, y=None, ws=None, stream=None, return_routing=False, padded=False):
+                  ws_down=None, y=None, ws=None, stream=None, return_routing=False, padded=False,
+                  reroute=False):
     """Whole MoE layer.  Returns y, or (y, dict(expert_ids, gates, counts,
     route_pos)) with return_routing.  padded=True runs moe_layer_forward_padded
-    (fixed-shape [E, C, d] buffer; route_pos then holds its rows e*C + slot)."""
+    (fixed-shape [E, C, d] buffer; route_pos then holds its rows e*C + slot);
+    reroute=True runs moe_layer_forward_reroute (expert_ids then holds the
+    experts after rerouting)."""
     dt = _tdtype(s)
     dev = x.device
     xp = _ptr(x, "x", (s.T, s.d), dt)
@@ -305,15 +338,15 @@ def layer_forward(s, x, w_router, b_router, w_gate, w_up, w_down, ws_gate=None, 
         cp = _ptr(routing["counts"], "counts")
         rpp = _ptr(routing["route_pos"], "route_pos")
     ws = _ws(s, ws, dev)
-    fn = _lib.moe_layer_forward_padded if padded else _lib.moe_layer_forward
-    _check(fn(ctypes.byref(s), xp, rp, bp, gp, up, dp, sg, su, sd, yo, ip, gtp, cp, rpp,
-              ws.data_ptr(), ws.numel(), _stream(stream)),
-           "moe_layer_forward_padded" if padded else "moe_layer_forward")
+    name = ("moe_layer_forward_padded" if padded else
+            "moe_layer_forward_reroute" if reroute else "moe_layer_forward")
+    _check(getattr(_lib, name)(ctypes.byref(s), xp, rp, bp, gp, up, dp, sg, su, sd, yo, ip, gtp,
+                               cp, rpp, ws.data_ptr(), ws.numel(), _stream(stream)), name)
     return (y, routing) if return_routing else y
 
 
 def layer_forward_timed(s, x, w_router, b_router, w_gate, w_up, w_down, ws_gate, ws_up, ws_down,
-                        y, ws, events, stream=None, padded=False):
+                        y, ws, events, stream=None, padded=False, reroute=False):
     """moe_layer_forward_timed: records the 7 stage-boundary hipEvents
     (`events`: sequence of raw hipEvent_t handles as ints)."""
     dt = _tdtype(s)
@@ -328,6 +361,6 @@ def layer_forward_timed(s, x, w_router, b_router, w_gate, w_up, w_down, ws_gate,
         _ptr(ws_up, "ws_up", (s.d_ff_shared, s.d), dt, optional=not shp),
         _ptr(ws_down, "ws_down", (s.d, s.d_ff_shared), dt, optional=not shp),
         _ptr(y, "y", (s.T, s.d), dt), ws.data_ptr(), ws.numel(), _stream(stream), arr,
-        1 if padded else 0),
+        1 if padded else 2 if reroute else 0),
         "moe_layer_forward_timed")
     return y

@@ -18,6 +18,17 @@ hipError_t launch_permute_index(const int32_t* ids, int T, int k, int E, int C, 
                                 int32_t* route_pos, int32_t* row_token, hipStream_t st);
 hipError_t launch_gather_rows(const void* x, const int32_t* row_token, const int32_t* offsets,
                               int E, long R_max, long row_bytes, void* x_packed, hipStream_t st);
+// Overflow policy "reroute" after a drop-policy dispatch (route_pos0,
+// offsets0, kept from launch_permute_index); E <= 64, k <= 8, C >= 0.
+// Writes the final experts, the packed positions and rows of the result.
+// pref: scratch of T*k*64 bytes (preference lists of the dropped routes).
+hipError_t launch_reroute(const float* logits, const int32_t* ids_in, const int32_t* route_pos0,
+                          const int32_t* offsets0, const int32_t* kept, int T, int k, int E,
+                          int C, int32_t* ids_out, int32_t* slot, int32_t* offsets,
+                          int32_t* route_pos, int32_t* row_token, uint8_t* pref,
+                          hipStream_t st);
+// seats[e] = offsets[e+1] - offsets[e]
+hipError_t launch_seats(const int32_t* offsets, int E, int32_t* seats, hipStream_t st);
 // Fixed-shape [E, C, d] buffer from a packed dispatch (needs C >= 1): padded
 // route positions, the buffer's rows (zero for empty slots) and its row
 // groups offsets_pad[e] = e*C.

@@ -12,6 +12,7 @@ namespace {
 
 constexpr int64_t kMaxE = 256;
 constexpr int64_t kMaxK = 8;
+constexpr int64_t kMaxRerouteE = 64;  // the reroute walk keeps one expert per lane
 constexpr size_t kAlign = 256;
 
 size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
@@ -65,7 +66,7 @@ int64_t rmax_of(const moe_shape* s, int64_t C) {
 
 struct Layout {
   size_t logits, ids, gates, cnt, counts, kept, offsets, route_pos, row_token, h, yp, part, hs,
-      ys, spart, shist, xpad, opad, ppos;
+      ys, spart, shist, xpad, opad, ppos, ids2, slot, offs2, rpos0, pref;
   int splits;      // K splits of the routed down GEMM (fp32 partial planes when > 1)
   int splits_pad;  // the same for the fixed-shape [E, C] layout
   size_t total;
@@ -143,6 +144,12 @@ Layout layout_of(const moe_shape* s) {
   L.xpad = take((size_t)Rpad * s->d * eb);
   L.opad = take((size_t)(s->E + 1) * sizeof(int32_t));
   L.ppos = take(R * sizeof(int32_t));
+  // reroute policy: primary positions, final experts and seats
+  L.ids2 = take(R * sizeof(int32_t));
+  L.slot = take(R * sizeof(int32_t));
+  L.offs2 = take((size_t)(s->E + 1) * sizeof(int32_t));
+  L.rpos0 = take(R * sizeof(int32_t));
+  L.pref = take(R * 64);  // preference lists of the dropped routes (E <= 64)
   L.hs = take((size_t)s->T * s->d_ff_shared * eb);
   L.ys = take(s->d_ff_shared > 0 ? (size_t)s->T * s->d * eb : 0);
   // routing statistics: one partial row per 64 tokens
@@ -266,6 +273,41 @@ int moe_permute_padded(const moe_shape* s, const void* x, const int32_t* expert_
                                        at<int32_t>(ws, L.opad), stream));
 }
 
+int moe_permute_reroute(const moe_shape* s, const void* x, const float* logits,
+                        const int32_t* expert_ids, int32_t* expert_ids_out, int32_t* counts,
+                        int32_t* filled, int32_t* offsets, int32_t* route_pos,
+                        int32_t* row_token, void* x_packed, void* ws, size_t ws_bytes,
+                        hipStream_t stream) {
+  int v = validate(s);
+  if (v != MOE_OK) return v;
+  if (s->E > kMaxRerouteE) return MOE_ERR_UNSUPPORTED;
+  const bool tok = s->T > 0;
+  if (!counts || !filled || !offsets ||
+      (tok && (!x || !logits || !expert_ids || !expert_ids_out || !route_pos || !row_token ||
+               !x_packed)))
+    return MOE_ERR_INVALID_ARG;
+  if (!aligned16(x) || !aligned16(x_packed)) return MOE_ERR_INVALID_ARG;
+  v = check_ws(s, ws, ws_bytes);
+  if (v != MOE_OK) return v;
+  const Layout L = layout_of(s);
+  const int64_t C = capacity_of(s);
+  const int T = (int)s->T, k = (int)s->k, E = (int)s->E;
+  int32_t* offs0 = at<int32_t>(ws, L.offsets);
+  hipError_t e = moe::launch_permute_index(expert_ids, T, k, E, (int)C, at<int32_t>(ws, L.cnt),
+                                           counts, filled, offs0, at<int32_t>(ws, L.rpos0),
+                                           row_token, stream);
+  if (e != hipSuccess) return MOE_ERR_HIP;
+  // kept counts (in filled) seed the walk, which turns them into seats
+  e = moe::launch_reroute(logits, expert_ids, at<int32_t>(ws, L.rpos0), offs0, filled, T, k, E,
+                          (int)C, expert_ids_out, at<int32_t>(ws, L.slot), offsets, route_pos,
+                          row_token, at<uint8_t>(ws, L.pref), stream);
+  if (e != hipSuccess) return MOE_ERR_HIP;
+  e = moe::launch_seats(offsets, E, filled, stream);
+  if (e != hipSuccess) return MOE_ERR_HIP;
+  return hip_status(moe::launch_gather_rows(x, row_token, offsets, E, rmax_of(s, C),
+                                            s->d * elem_bytes(s), x_packed, stream));
+}
+
 int moe_expert_ffn(const moe_shape* s, const void* x_packed, const int32_t* offsets,
                    const void* w_gate, const void* w_up, const void* w_down, void* y_packed,
                    void* ws, size_t ws_bytes, hipStream_t stream) {
@@ -331,10 +373,15 @@ static int layer_forward_impl(const moe_shape* s, const void* x, const void* w_r
                               const void* w_down, const void* ws_gate, const void* ws_up,
                               const void* ws_down, void* y, int32_t* expert_ids, float* gates,
                               int32_t* counts, int32_t* route_pos, void* ws, size_t ws_bytes,
-                              hipStream_t stream, hipEvent_t* ev, bool padded) {
+                              hipStream_t stream, hipEvent_t* ev, int layout) {
+  // layout 0: packed rows; 1: fixed-shape [E, C, d] buffer; 2: packed rows
+  // after the reroute overflow policy
+  const bool padded = layout == 1;
+  const bool reroute = layout == 2;
   int v = validate(s);
   if (v != MOE_OK) return v;
   if (padded && (v = validate_padded(s)) != MOE_OK) return v;
+  if (reroute && s->E > kMaxRerouteE) return MOE_ERR_UNSUPPORTED;
   if (!w_router || !w_gate || !w_up || !w_down || (s->T > 0 && (!x || !y)))
     return MOE_ERR_INVALID_ARG;
   const bool shared = s->d_ff_shared > 0;
@@ -352,7 +399,10 @@ static int layer_forward_impl(const moe_shape* s, const void* x, const void* w_r
   const int T = (int)s->T, d = (int)s->d, E = (int)s->E, k = (int)s->k, dff = (int)s->d_ff;
   const int64_t C = capacity_of(s);
   const int64_t Rmax = rmax_of(s, C);
-  int32_t* ids = expert_ids ? expert_ids : at<int32_t>(ws, L.ids);
+  // router choices (rerouting keeps them internal and reports the final
+  // experts in expert_ids)
+  int32_t* ids = (expert_ids && !reroute) ? expert_ids : at<int32_t>(ws, L.ids);
+  int32_t* ids_final = expert_ids ? expert_ids : at<int32_t>(ws, L.ids2);
   float* g = gates ? gates : at<float>(ws, L.gates);
   int32_t* cnts = counts ? counts : at<int32_t>(ws, L.counts);
   // route positions: the caller's array receives the packed rows, or the
@@ -374,8 +424,19 @@ static int layer_forward_impl(const moe_shape* s, const void* x, const void* w_r
   if (e != hipSuccess) return MOE_ERR_HIP;
   mark(1);
   e = moe::launch_permute_index(ids, T, k, E, (int)C, at<int32_t>(ws, L.cnt), cnts,
-                                at<int32_t>(ws, L.kept), offsets, rpos, row_token, stream);
+                                at<int32_t>(ws, L.kept), offsets,
+                                reroute ? at<int32_t>(ws, L.rpos0) : rpos, row_token, stream);
   if (e != hipSuccess) return MOE_ERR_HIP;
+  if (reroute) {
+    // the drop-policy seats stay; dropped routes move; packed rows follow
+    // the final experts (offsets become the rerouted ones)
+    e = moe::launch_reroute(at<float>(ws, L.logits), ids, at<int32_t>(ws, L.rpos0), offsets,
+                            at<int32_t>(ws, L.kept), T, k, E, (int)C, ids_final,
+                            at<int32_t>(ws, L.slot), at<int32_t>(ws, L.offs2), rpos, row_token,
+                            at<uint8_t>(ws, L.pref), stream);
+    if (e != hipSuccess) return MOE_ERR_HIP;
+    offsets = at<int32_t>(ws, L.offs2);
+  }
   if (padded) {
     e = moe::launch_padded(x, ids, rpos, offsets, at<int32_t>(ws, L.kept), row_token, T, k, E,
                            (int)C, (long)d * elem_bytes(s), ppos, at<void>(ws, L.xpad),
@@ -433,7 +494,7 @@ int moe_layer_forward(const moe_shape* s, const void* x, const void* w_router,
                       hipStream_t stream) {
   return layer_forward_impl(s, x, w_router, b_router, w_gate, w_up, w_down, ws_gate, ws_up,
                             ws_down, y, expert_ids, gates, counts, route_pos, ws, ws_bytes,
-                            stream, nullptr, false);
+                            stream, nullptr, 0);
 }
 
 int moe_layer_forward_padded(const moe_shape* s, const void* x, const void* w_router,
@@ -444,7 +505,18 @@ int moe_layer_forward_padded(const moe_shape* s, const void* x, const void* w_ro
                              hipStream_t stream) {
   return layer_forward_impl(s, x, w_router, b_router, w_gate, w_up, w_down, ws_gate, ws_up,
                             ws_down, y, expert_ids, gates, counts, route_pos, ws, ws_bytes,
-                            stream, nullptr, true);
+                            stream, nullptr, 1);
+}
+
+int moe_layer_forward_reroute(const moe_shape* s, const void* x, const void* w_router,
+                              const float* b_router, const void* w_gate, const void* w_up,
+                              const void* w_down, const void* ws_gate, const void* ws_up,
+                              const void* ws_down, void* y, int32_t* expert_ids, float* gates,
+                              int32_t* counts, int32_t* route_pos, void* ws, size_t ws_bytes,
+                              hipStream_t stream) {
+  return layer_forward_impl(s, x, w_router, b_router, w_gate, w_up, w_down, ws_gate, ws_up,
+                            ws_down, y, expert_ids, gates, counts, route_pos, ws, ws_bytes,
+                            stream, nullptr, 2);
 }
 
 int moe_layer_forward_timed(const moe_shape* s, const void* x, const void* w_router,
@@ -453,10 +525,10 @@ int moe_layer_forward_timed(const moe_shape* s, const void* x, const void* w_rou
                             const void* ws_down, void* y, void* ws, size_t ws_bytes,
                             hipStream_t stream, hipEvent_t* events, int32_t layout) {
   if (!events) return MOE_ERR_INVALID_ARG;
-  if (layout != 0 && layout != 1) return MOE_ERR_INVALID_ARG;
+  if (layout < 0 || layout > 2) return MOE_ERR_INVALID_ARG;
   return layer_forward_impl(s, x, w_router, b_router, w_gate, w_up, w_down, ws_gate, ws_up,
                             ws_down, y, nullptr, nullptr, nullptr, nullptr, ws, ws_bytes, stream,
-                            events, layout == 1);
+                            events, layout);
 }
 
 }  // extern "C"

@@ -336,6 +336,198 @@ hipError_t launch_padded(const void* x, const int32_t* ids, const int32_t* route
   return hipGetLastError();
 }
 
+// Overflow policy "reroute" ("Session 19", "Overflow policies": the
+// overflowing route is handled by the token's next-best expert).  Routes
+// keep the seats of the drop policy; then the dropped ones, in arrival
+// order, each take the best-ranked expert of their token (logit descending,
+// lower index first) that the token does not hold and that still has room.
+// That is a greedy in arrival order -- every choice depends on the earlier
+// ones -- so one wave walks the dropped routes one by one, after a parallel
+// kernel has written every dropped route's rank of each expert (one byte
+// each).  The walk stages a 64-route chunk's rank rows in LDS (the next
+// chunk's are loaded while this one is walked); for a route, lane e reads
+// its expert's rank and the choice is the lowest rank among the lanes with
+// room that the token does not hold -- six ballots over the rank bits, no
+// branches; lane e keeps expert e's seat count (E <= 64).
+//   ids_out   final expert of every route; slot  seat at that expert, or -1
+//   offsets   exclusive prefix of the seats used per expert
+constexpr int kRerouteMaxE = 64;
+
+// rank[r][e] = rank of expert e in dropped route r's preference order
+// (experts ahead: larger logit, or equal logit and lower index); one thread
+// per (r, e)
+__global__ __launch_bounds__(256) void reroute_rank_kernel(const float* __restrict__ logits,
+                                                           const int32_t* __restrict__ route_pos0,
+                                                           int R, int k, int E,
+                                                           uint8_t* __restrict__ rank) {
+  const long g = (long)blockIdx.x * blockDim.x + threadIdx.x;
+  const int r = (int)(g / kRerouteMaxE), e = (int)(g % kRerouteMaxE);
+  if (r >= R || e >= E || route_pos0[r] >= 0) return;
+  const float* l = logits + (size_t)(r / k) * E;
+  const float le = l[e];
+  int rk = 0;
+  for (int e2 = 0; e2 < E; ++e2) {
+    const float l2 = l[e2];
+    rk += (l2 > le) | ((l2 == le) & (e2 < e));
+  }
+  rank[(size_t)r * kRerouteMaxE + e] = (uint8_t)rk;
+}
+
+__global__ __launch_bounds__(64) void reroute_kernel(
+    const uint8_t* __restrict__ rank, const int32_t* __restrict__ ids_in,
+    const int32_t* __restrict__ route_pos0, const int32_t* __restrict__ offsets0,
+    const int32_t* __restrict__ kept, int T, int k, int E, int C, int32_t* __restrict__ ids_out,
+    int32_t* __restrict__ slot, int32_t* __restrict__ offsets) {
+  __shared__ __attribute__((aligned(16))) uint8_t s_rank[kWave][kRerouteMaxE];
+  const int lane = threadIdx.x;
+  const int R = T * k;
+  int fill = lane < E ? kept[lane] : 0;  // lane e: seats used at expert e
+  uint64_t avail = __ballot(lane < E && fill < C);  // experts with room
+  int cur_t = -1;
+  uint64_t cur_mask[8];  // final experts of token cur_t's slots, one bit each
+#pragma unroll
+  for (int jj = 0; jj < 8; ++jj) cur_mask[jj] = 0;
+  // chunk data of lane i: its route's drop-policy position and expert, and,
+  // when dropped, its rank row and its token's experts
+  int p0, e0, tid[8];
+  uint4 rw[4];
+  auto load = [&](int base) {
+    const int rr = base + lane;
+    p0 = rr < R ? route_pos0[rr] : 0;
+    e0 = rr < R ? ids_in[rr] : 0;
+    const bool drop = rr < R && p0 < 0;
+    const uint4* src = reinterpret_cast<const uint4*>(rank + (size_t)(drop ? rr : 0) * kRerouteMaxE);
+#pragma unroll
+    for (int w = 0; w < 4; ++w) rw[w] = (drop && 16 * w < E) ? src[w] : uint4{0u, 0u, 0u, 0u};
+    const int t = drop ? rr / k : 0;
+#pragma unroll
+    for (int jj = 0; jj < 8; ++jj) tid[jj] = (drop && jj < k) ? ids_in[t * k + jj] : 0;
+  };
+  load(0);
+  for (int base = 0; base < R; base += kWave) {
+    const int cp0 = p0, ce0 = e0;
+    int ctid[8];
+#pragma unroll
+    for (int jj = 0; jj < 8; ++jj) ctid[jj] = tid[jj];
+    __syncthreads();  // the previous chunk's rank rows are no longer read
+#pragma unroll
+    for (int w = 0; w < 4; ++w) *reinterpret_cast<uint4*>(&s_rank[lane][16 * w]) = rw[w];
+    __syncthreads();
+    if (base + kWave < R) load(base + kWave);  // in flight during this chunk's walk
+    const int rr = base + lane;
+    if (rr < R && cp0 >= 0) {  // kept by the drop policy: same expert, same seat
+      ids_out[rr] = ce0;
+      slot[rr] = cp0 - offsets0[ce0];
+    }
+    uint64_t m = __ballot(rr < R && cp0 < 0);
+    int b = m ? __builtin_amdgcn_readfirstlane(__builtin_ctzll(m)) : 0;
+    int key = s_rank[b][lane & (kRerouteMaxE - 1)];
+    while (m) {
+      m &= m - 1;
+      const int bn = m ? __builtin_amdgcn_readfirstlane(__builtin_ctzll(m)) : b;
+      const int key_next = s_rank[bn][lane & (kRerouteMaxE - 1)];  // issued ahead
+      const int r = base + b;
+      const int t = r / k, j = r - t * k;
+      if (t != cur_t) {
+        cur_t = t;
+#pragma unroll
+        for (int jj = 0; jj < 8; ++jj)
+          cur_mask[jj] = (jj < k) ? (1ull << __builtin_amdgcn_readlane(ctid[jj], b)) : 0ull;
+      }
+      uint64_t held = 0;
+#pragma unroll
+      for (int jj = 0; jj < 8; ++jj) held |= (jj != j) ? cur_mask[jj] : 0ull;
+      // lowest rank among the experts with room the token does not hold:
+      // ranks are distinct, six ballots over their bits leave one lane
+      uint64_t alive = avail & ~held & __ballot(lane < E);
+#pragma unroll
+      for (int bit = 5; bit >= 0; --bit) {
+        const uint64_t zeros = __ballot(((key >> bit) & 1) == 0) & alive;
+        alive = zeros ? zeros : alive;
+      }
+      if (alive) {
+        const int best = __builtin_ctzll(alive);
+        const int seat = __builtin_amdgcn_readlane(fill, best);
+        if (lane == best) fill = seat + 1;
+        if (lane == 0) {
+          slot[r] = seat;
+          ids_out[r] = best;
+        }
+        if (seat + 1 >= C) avail &= ~(1ull << best);
+#pragma unroll
+        for (int jj = 0; jj < 8; ++jj)
+          if (jj == j) cur_mask[jj] = 1ull << best;
+      } else {  // no expert with room: dropped after all (lane b's own expert)
+        const int orig = __builtin_amdgcn_readlane(ce0, b);
+        if (lane == 0) {
+          ids_out[r] = orig;
+          slot[r] = -1;
+        }
+      }
+      b = bn;
+      key = key_next;
+    }
+  }
+  const int f = lane < E ? fill : 0;
+  const int incl = wave_incl_scan(f, lane);
+  if (lane == 0) offsets[0] = 0;
+  if (lane < E) offsets[lane + 1] = incl;
+}
+
+// Packed rows of the rerouted dispatch: route_pos[r] = offsets[ids[r]] +
+// slot[r] (or -1), row_token[route_pos[r]] = r / k.
+__global__ __launch_bounds__(256) void reroute_rows_kernel(const int32_t* __restrict__ ids,
+                                                           const int32_t* __restrict__ slot,
+                                                           const int32_t* __restrict__ offsets,
+                                                           int R, int k,
+                                                           int32_t* __restrict__ route_pos,
+                                                           int32_t* __restrict__ row_token) {
+  const int r = blockIdx.x * blockDim.x + threadIdx.x;
+  if (r >= R) return;
+  const int sl = slot[r];
+  if (sl < 0) {
+    route_pos[r] = -1;
+    return;
+  }
+  const int p = offsets[ids[r]] + sl;
+  route_pos[r] = p;
+  row_token[p] = r / k;
+}
+
+hipError_t launch_reroute(const float* logits, const int32_t* ids_in, const int32_t* route_pos0,
+                          const int32_t* offsets0, const int32_t* kept, int T, int k, int E,
+                          int C, int32_t* ids_out, int32_t* slot, int32_t* offsets,
+                          int32_t* route_pos, int32_t* row_token, uint8_t* pref,
+                          hipStream_t st) {
+  const int R = T * k;
+  if (R > 0) {
+    const long threads = (long)R * kRerouteMaxE;
+    hipLaunchKernelGGL(reroute_rank_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0,
+                       st, logits, route_pos0, R, k, E, pref);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+  }
+  hipLaunchKernelGGL(reroute_kernel, dim3(1), dim3(kWave), 0, st, pref, ids_in, route_pos0,
+                     offsets0, kept, T, k, E, C, ids_out, slot, offsets);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess || R == 0) return err;
+  hipLaunchKernelGGL(reroute_rows_kernel, dim3(ceil_div(R, 256)), dim3(256), 0, st, ids_out, slot,
+                     offsets, R, k, route_pos, row_token);
+  return hipGetLastError();
+}
+
+// seats[e] = offsets[e+1] - offsets[e]
+__global__ __launch_bounds__(256) void seats_kernel(const int32_t* __restrict__ offsets, int E,
+                                                    int32_t* __restrict__ seats) {
+  const int e = blockIdx.x * blockDim.x + threadIdx.x;
+  if (e < E) seats[e] = offsets[e + 1] - offsets[e];
+}
+
+hipError_t launch_seats(const int32_t* offsets, int E, int32_t* seats, hipStream_t st) {
+  hipLaunchKernelGGL(seats_kernel, dim3(ceil_div(E, 256)), dim3(256), 0, st, offsets, E, seats);
+  return hipGetLastError();
+}
+
 int permute_nchunks(long R) { return (int)((R + kChunk - 1) / kChunk); }
 
 hipError_t launch_permute_index(const int32_t* ids, int T, int k, int E, int C, int32_t* cnt_ws,

@@ -198,3 +198,17 @@ def test_padded_entry_points_need_a_capacity():
     C, R = moe.capacity(sc)
     assert 4 * C >= R
     assert moe.workspace_bytes(sc) >= moe.workspace_bytes(s)
+
+
+def test_reroute_needs_at_most_64_experts():
+    moe = _moe()
+    s = moe.shape(16, 64, 65, 2, 64, phi=1.0)
+    by = ctypes.byref(s)
+    L = moe._lib
+    fake, ws = 4096, 1 << 20
+    need = moe.workspace_bytes(s)
+    assert L.moe_permute_reroute(by, fake, fake, fake, fake, fake, fake, fake, fake, fake, fake,
+                                 ws, need, None) == moe.MOE_ERR_UNSUPPORTED
+    assert L.moe_layer_forward_reroute(by, fake, fake, None, fake, fake, fake, None, None, None,
+                                       fake, None, None, None, None, ws, need, None) \
+        == moe.MOE_ERR_UNSUPPORTED

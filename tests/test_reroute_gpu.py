@@ -1,0 +1,96 @@
+"""GPU parity of the reroute overflow policy ("Session 19", "Overflow
+policies") -- moe_permute_reroute and moe_layer_forward_reroute -- against the
+CPU oracle.  Routing outputs (final experts, seats, offsets, packed rows) are
+integers: bit for bit.  The layer output is held to the layer tolerances
+against the oracle composed from its own pieces (rerouted dispatch, expert
+FFN, combine)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from tests._gpu import bits, check_y, host_inputs, say, to_dev
+from workloads import WORKLOADS, Workload, make_inputs
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def moe():
+    assert torch.cuda.is_available(), "GPU parity tests need a GPU"
+    import routing_dispatch_expert_route_amd as m
+    return m
+
+
+def _np(t):
+    return t.detach().cpu().numpy()
+
+
+CASES = {
+    "switch_phi1": WORKLOADS["switch_phi1"],
+    "switch_phi125": WORKLOADS["switch_phi125"],
+    "cap_one": Workload("cap_one", T=64, E=16, k=2, d=64, d_ff=64, phi=0.01),
+    "f32_ragged": Workload("f32_ragged", T=77, E=5, k=3, d=40, d_ff=24, dtype="f32", phi=0.8,
+                           bias="normal"),
+    "shared_small": Workload("shared_small", T=130, E=4, k=1, d=128, d_ff=64, d_ff_shared=96,
+                             renorm=0, phi=1.0, bias="zipf"),
+    "granite_tight": WORKLOADS["granite_1412"].with_(name="granite_tight", phi=0.75, bias="normal"),
+    "e64_k8_zipf": Workload("e64_k8", T=600, E=64, k=8, d=64, d_ff=32, phi=0.9, bias="zipf"),
+}
+
+
+def _inputs(name):
+    w = CASES[name]
+    return w, (host_inputs(name) if name in WORKLOADS else make_inputs(w, seed=17))
+
+
+def _oracle(w, inp):
+    L = oracle.router_logits(inp["x"], inp["w_router"], inp["b_router"])
+    ids, gates = oracle.topk_gates(L, w.k, w.renorm)
+    C = oracle.capacity(w.T, w.E, w.k, w.phi)
+    return L, ids, gates, oracle.dispatch_reroute(L, ids, w.E, C)
+
+
+@pytest.mark.parametrize("name", list(CASES))
+def test_permute_reroute_parity(moe, name):
+    w, inp = _inputs(name)
+    say(f"[permute reroute] {name}")
+    d = to_dev(inp)
+    s = moe.shape_of(w)
+    ids, _, logits = moe.route(s, d["x"], d["w_router"], d["b_router"], want_logits=True)
+    out = moe.permute_reroute(s, d["x"], logits, ids)
+    torch.cuda.synchronize()
+    _, _, _, ref = _oracle(w, inp)
+    assert np.array_equal(_np(out["expert_ids"]), ref["ids"])
+    assert np.array_equal(_np(out["counts"]), ref["counts"])
+    assert np.array_equal(_np(out["filled"]), ref["filled"])
+    assert np.array_equal(_np(out["offsets"]), ref["offsets"])
+    assert np.array_equal(_np(out["route_pos"]), ref["route_pos"])
+    n = int(ref["offsets"][-1])
+    assert np.array_equal(_np(out["row_token"])[:n], ref["row_token"])
+    assert np.array_equal(bits(out["x_packed"])[:n], bits(inp["x"])[ref["row_token"]])
+    say(f"   {name}: {ref['n_rerouted']} routes rerouted, {n} of {w.T * w.k} seated")
+
+
+@pytest.mark.parametrize("name", list(CASES))
+def test_layer_forward_reroute_parity(moe, name):
+    w, inp = _inputs(name)
+    say(f"[layer reroute] {name}")
+    d = to_dev(inp)
+    s = moe.shape_of(w)
+    y, rt = moe.layer_forward(s, d["x"], d["w_router"], d["b_router"], d["w_gate"], d["w_up"],
+                              d["w_down"], d["ws_gate"], d["ws_up"], d["ws_down"],
+                              return_routing=True, reroute=True)
+    torch.cuda.synchronize()
+    _, _, gates, ref = _oracle(w, inp)
+    assert np.array_equal(_np(rt["expert_ids"]), ref["ids"])
+    assert np.array_equal(_np(rt["route_pos"]), ref["route_pos"])
+    assert np.max(np.abs(_np(rt["gates"]) - gates), initial=0.0) <= 1e-6
+    xp = oracle.gather_rows(inp["x"], ref["row_token"])
+    yp = oracle.expert_ffn(xp, ref["offsets"], inp["w_gate"], inp["w_up"], inp["w_down"])
+    ysh = None
+    if w.d_ff_shared > 0:
+        ysh = oracle.swiglu_rows(inp["x"], inp["ws_gate"], inp["ws_up"], inp["ws_down"])
+    yref = oracle.combine(yp, ref["route_pos"], gates, ysh)
+    errs = check_y(y, yref, w.dtype, f"reroute layer {name}")
+    say(f"   {name}: err {errs[0]:.3e} / {errs[1]:.3e}")
