@@ -59,6 +59,11 @@ def lib():
         L.oracle_dispatch_padded.argtypes = [_i64, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _vp]
         L.oracle_dispatch_reroute.restype = None
         L.oracle_dispatch_reroute.argtypes = [_i64, _i64, _i64, _i64] + [_vp] * 9
+        L.oracle_expert_choice.restype = None
+        L.oracle_expert_choice.argtypes = [_i64, _i64, _i64, _vp, _vp, _vp, _vp]
+        L.oracle_layer_forward_expert_choice.restype = _int
+        L.oracle_layer_forward_expert_choice.argtypes = [_i64] * 5 + [_int, _i64] + [_vp] * 9 + \
+            [_i64, _vp, _vp, _vp, _vp]
         L.oracle_routing_stats.restype = None
         L.oracle_routing_stats.argtypes = [_i64, _i64, _i64, _vp, _vp, _vp, _dbl, ctypes.c_int32,
                                            _vp, _vp, _vp, _vp]
@@ -178,6 +183,19 @@ def dispatch_reroute(logits, expert_ids, E, C):
                 n_rerouted=int(moved[0]))
 
 
+def expert_choice(logits, C):
+    """Expert-choice routing (see oracle_expert_choice).  Returns dict(scores
+    [T, E] fp32, route_pos [T, E], row_token [E*Ce], Ce)."""
+    la = np.ascontiguousarray(logits, dtype=np.float32)
+    T, E = la.shape
+    Ce = T if (C < 0 or C > T) else int(C)
+    scores = np.empty((T, E), np.float32)
+    route_pos = np.empty((T, E), np.int32)
+    row_token = np.full(max(E * Ce, 1), -1, np.int32)
+    lib().oracle_expert_choice(T, E, int(C), _p(la), _p(scores), _p(route_pos), _p(row_token))
+    return dict(scores=scores, route_pos=route_pos, row_token=row_token[:E * Ce].copy(), Ce=Ce)
+
+
 def gather_rows(x, row_token):
     xa, dt = as_array(x)
     rt = np.ascontiguousarray(row_token, dtype=np.int32)
@@ -285,3 +303,36 @@ def layer_forward(x, w_router, b_router, w_gate, w_up, w_down, k, renorm, phi,
     if rc != 0:
         raise ValueError("oracle_layer_forward: bad arguments")
     return dict(y=y, ids=ids, gates=gates, counts=counts, route_pos=route_pos)
+
+
+def layer_forward_expert_choice(x, w_router, b_router, w_gate, w_up, w_down, C,
+                                ws_gate=None, ws_up=None, ws_down=None, sel=None):
+    """Whole-layer oracle under expert-choice routing with capacity C (C < 0:
+    every expert takes every token).  Returns dict(y, scores, route_pos)."""
+    xa, dt = as_array(x)
+    T, d = xa.shape
+    ra, _ = as_array(w_router)
+    E = ra.shape[0]
+    ba = None if b_router is None else np.ascontiguousarray(as_array(b_router)[0], np.float32)
+    ga, _ = as_array(w_gate)
+    ua, _ = as_array(w_up)
+    da, _ = as_array(w_down)
+    d_ff = ga.shape[1]
+    d_ffs = 0
+    sga = sua = sda = None
+    if ws_gate is not None:
+        sga, _ = as_array(ws_gate)
+        sua, _ = as_array(ws_up)
+        sda, _ = as_array(ws_down)
+        d_ffs = sga.shape[0]
+    sela = None if sel is None else np.ascontiguousarray(sel, dtype=np.int32)
+    n_sel = T if sela is None else sela.shape[0]
+    y = np.empty((n_sel, d), np.float64)
+    scores = np.empty((T, E), np.float32)
+    route_pos = np.empty((T, E), np.int32)
+    rc = lib().oracle_layer_forward_expert_choice(
+        T, d, E, d_ff, d_ffs, dt, int(C), _p(xa), _p(ra), _p(ba), _p(ga), _p(ua), _p(da),
+        _p(sga), _p(sua), _p(sda), n_sel, _p(sela), _p(y), _p(scores), _p(route_pos))
+    if rc != 0:
+        raise ValueError("oracle_layer_forward_expert_choice: bad arguments")
+    return dict(y=y, scores=scores, route_pos=route_pos)

@@ -230,6 +230,68 @@ void oracle_dispatch_reroute(int64_t T, int64_t E, int64_t k, int64_t C,
   free(slot);
 }
 
+/* Expert-choice routing ("MoE Inference Visualized", "Why MoE Matters for
+ * Infrastructure": against load imbalance the experts can pick the tokens
+ * instead of the tokens picking experts).  The page names the idea only.
+ * Reading: the score of (t, e) is the full softmax probability of the
+ * router logits; each expert takes the Ce = min(C, T) tokens of largest
+ * score (C < 0: no limit, Ce = T); a token's gate for an expert that took it
+ * is that score. */
+typedef struct {
+  float s;
+  int32_t t;
+} ec_item;
+
+/* larger score first; the lower token index first among equal scores */
+static int ec_order(const void* a, const void* b) {
+  const ec_item* x = (const ec_item*)a;
+  const ec_item* y = (const ec_item*)b;
+  if (x->s != y->s) return x->s > y->s ? -1 : 1;
+  return x->t < y->t ? -1 : (x->t > y->t ? 1 : 0);
+}
+
+void oracle_expert_choice(int64_t T, int64_t E, int64_t C, const float* logits,
+                          float* scores, int32_t* route_pos, int32_t* row_token) {
+  const int64_t Ce = (C < 0 || C > T) ? T : C;
+  /* scores: softmax over all E logits of the token, in double, stored as
+   * the fp32 gate (the decision below is taken on this stored value) */
+  for (int64_t t = 0; t < T; t++) {
+    const float* l = logits + t * E;
+    double m = (double)l[0];
+    for (int64_t e = 1; e < E; e++)
+      if ((double)l[e] > m) m = (double)l[e];
+    double denom = 0.0;
+    for (int64_t e = 0; e < E; e++) denom += exp((double)l[e] - m);
+    for (int64_t e = 0; e < E; e++)
+      scores[t * E + e] = (float)(exp((double)l[e] - m) / denom);
+  }
+  ec_item* items = (ec_item*)malloc((size_t)(T > 0 ? T : 1) * sizeof(ec_item));
+  unsigned char* chosen = (unsigned char*)malloc((size_t)(T > 0 ? T : 1));
+  for (int64_t e = 0; e < E; e++) {
+    /* expert e ranks every token by its score and keeps the first Ce */
+    for (int64_t t = 0; t < T; t++) {
+      items[t].s = scores[t * E + e];
+      items[t].t = (int32_t)t;
+    }
+    qsort(items, (size_t)T, sizeof(ec_item), ec_order);
+    memset(chosen, 0, (size_t)(T > 0 ? T : 1));
+    for (int64_t i = 0; i < Ce; i++) chosen[items[i].t] = 1;
+    /* its rows: Ce of them from row e*Ce, its tokens in increasing index */
+    int64_t n = 0;
+    for (int64_t t = 0; t < T; t++) {
+      if (chosen[t]) {
+        route_pos[t * E + e] = (int32_t)(e * Ce + n);
+        if (row_token) row_token[e * Ce + n] = (int32_t)t;
+        n++;
+      } else {
+        route_pos[t * E + e] = -1;
+      }
+    }
+  }
+  free(items);
+  free(chosen);
+}
+
 void oracle_gather_rows(int64_t n_rows, int64_t d, int64_t elem_bytes,
                         const void* x, const int32_t* row_token,
                         void* packed) {
@@ -450,6 +512,60 @@ int oracle_layer_forward(int64_t T, int64_t d, int64_t E, int64_t k,
   free(counts);
   free(kept);
   free(offsets);
+  free(route_pos);
+  return 0;
+}
+
+int oracle_layer_forward_expert_choice(int64_t T, int64_t d, int64_t E,
+                                       int64_t d_ff, int64_t d_ff_shared,
+                                       int dtype, int64_t C, const void* x,
+                                       const void* w_router,
+                                       const float* b_router,
+                                       const void* w_gate, const void* w_up,
+                                       const void* w_down, const void* ws_gate,
+                                       const void* ws_up, const void* ws_down,
+                                       int64_t n_sel, const int32_t* sel,
+                                       double* y, float* scores_out,
+                                       int32_t* route_pos_out) {
+  if (T < 0 || d <= 0 || E <= 0 || d_ff <= 0) return -1;
+  if (d_ff_shared > 0 && (!ws_gate || !ws_up || !ws_down)) return -1;
+  size_t nTE = (size_t)(T > 0 ? T : 1) * (size_t)E;
+  float* logits = (float*)malloc(nTE * sizeof(float));
+  float* scores = (float*)malloc(nTE * sizeof(float));
+  int32_t* route_pos = (int32_t*)malloc(nTE * sizeof(int32_t));
+  oracle_router_logits(T, d, E, dtype, x, w_router, b_router, logits);
+  oracle_expert_choice(T, E, C, logits, scores, route_pos, NULL);
+  /* [MML] section 1: y = sum over the experts that hold the token of
+   * gate * E_e(x), here over the experts that chose it, in expert order */
+  int64_t n_out = sel ? n_sel : T;
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int64_t s = 0; s < n_out; s++) {
+    int64_t t = sel ? sel[s] : s;
+    int64_t hmax = d_ff > d_ff_shared ? d_ff : d_ff_shared;
+    double* h = (double*)malloc((size_t)hmax * sizeof(double));
+    double* ye = (double*)malloc((size_t)d * sizeof(double));
+    double* yt = y + s * d;
+    for (int64_t i = 0; i < d; i++) yt[i] = 0.0;
+    for (int64_t e = 0; e < E; e++) {
+      if (route_pos[t * E + e] < 0) continue; /* expert e did not take t */
+      swiglu_row(d, d_ff, dtype, x, t * d, w_gate, e * d_ff * d, w_up,
+                 e * d_ff * d, w_down, e * d * d_ff, h, ye);
+      double g = (double)scores[t * E + e];
+      for (int64_t i = 0; i < d; i++) yt[i] += g * ye[i];
+    }
+    if (d_ff_shared > 0) {
+      swiglu_row(d, d_ff_shared, dtype, x, t * d, ws_gate, 0, ws_up, 0,
+                 ws_down, 0, h, ye);
+      for (int64_t i = 0; i < d; i++) yt[i] += ye[i];
+    }
+    free(h);
+    free(ye);
+  }
+  if (scores_out) memcpy(scores_out, scores, (size_t)(T * E) * sizeof(float));
+  if (route_pos_out)
+    memcpy(route_pos_out, route_pos, (size_t)(T * E) * sizeof(int32_t));
+  free(logits);
+  free(scores);
   free(route_pos);
   return 0;
 }

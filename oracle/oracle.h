@@ -139,6 +139,24 @@ void oracle_dispatch_reroute(int64_t T, int64_t E, int64_t k, int64_t C,
                              int32_t* offsets, int32_t* route_pos,
                              int32_t* row_token, int64_t* n_rerouted);
 
+/* Expert-choice routing ("MoE Inference Visualized", "Why MoE Matters for
+ * Infrastructure": the experts pick the tokens instead of the tokens picking
+ * experts -- named only).  Reading: score[t][e] = full softmax probability
+ * of the router logits (stored as fp32; the choice is made on that value);
+ * expert e takes the Ce = min(C, T) tokens of largest score, lower token
+ * index first among equal scores (C < 0: Ce = T, every expert takes every
+ * token).  Every expert thus holds exactly Ce rows; a token may be taken by
+ * any number of experts, none included.
+ *   scores[T][E]      the scores = the gates of the chosen pairs
+ *   route_pos[T][E]   row e*Ce + i if expert e took token t as its i-th
+ *                     token in increasing token order, else -1
+ *   row_token[E*Ce]   source token of every row (may be NULL)
+ * Pinned by a worked example with closed-form scores, the tie rule on equal
+ * scores, the ranking invariant on random inputs and the C >= T case (the
+ * full soft mixture). */
+void oracle_expert_choice(int64_t T, int64_t E, int64_t C, const float* logits,
+                          float* scores, int32_t* route_pos, int32_t* row_token);
+
 /* Row duplication: packed[p][:] = x[row_token[p]][:] for p < n_rows, a bit
  * copy of elem_bytes-sized elements ([MML] section 3: index_select). */
 void oracle_gather_rows(int64_t n_rows, int64_t d, int64_t elem_bytes,
@@ -222,6 +240,24 @@ int oracle_layer_forward(int64_t T, int64_t d, int64_t E, int64_t k,
                          int64_t n_sel, const int32_t* sel, double* y,
                          int32_t* ids, float* gates, int32_t* counts,
                          int32_t* route_pos);
+
+/* Whole layer under expert-choice routing: router logits as
+ * oracle_router_logits, choice as oracle_expert_choice with capacity C,
+ * y[t] = sum over the experts e that took t (increasing e) of
+ * score[t][e] * E_e(x_t), plus the shared expert when d_ff_shared > 0.
+ * y holds the tokens in sel (all when sel is NULL), in double.  scores_out
+ * and route_pos_out ([T][E]) may be NULL.  Returns 0, or -1 on bad sizes. */
+int oracle_layer_forward_expert_choice(int64_t T, int64_t d, int64_t E,
+                                       int64_t d_ff, int64_t d_ff_shared,
+                                       int dtype, int64_t C, const void* x,
+                                       const void* w_router,
+                                       const float* b_router,
+                                       const void* w_gate, const void* w_up,
+                                       const void* w_down, const void* ws_gate,
+                                       const void* ws_up, const void* ws_down,
+                                       int64_t n_sel, const int32_t* sel,
+                                       double* y, float* scores_out,
+                                       int32_t* route_pos_out);
 
 #ifdef __cplusplus
 }

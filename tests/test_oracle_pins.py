@@ -668,3 +668,125 @@ def test_reroute_without_overflow_is_the_drop_policy():
     assert out["n_rerouted"] == 0
     assert np.array_equal(out["route_pos"], ref["route_pos"])
     assert np.array_equal(out["ids"], ids)
+
+
+# ---------------------------------------------------------------------------
+# Expert-choice routing ([BEA] "Why MoE Matters for Infrastructure": experts
+# pick tokens).  Reading: score = full softmax probability, expert e keeps
+# its Ce = min(C, T) best tokens (lower index first on equal scores), gate =
+# score.
+
+def _logits_from_p0(p0):
+    """Two experts with softmax probabilities (p0, 1 - p0): logits
+    (0, ln((1 - p0) / p0)) in closed form."""
+    p0 = np.asarray(p0, np.float64)
+    L = np.zeros((p0.size, 2), np.float32)
+    L[:, 1] = np.log((1.0 - p0) / p0)
+    return L
+
+
+def test_expert_choice_closed_form():
+    # expert 0 sees (0.25, 0.5, 0.9, 0.1) -> keeps tokens 2 and 1; expert 1
+    # sees (0.75, 0.5, 0.1, 0.9) -> keeps tokens 3 and 0; rows list each
+    # expert's tokens in increasing index
+    out = oracle.expert_choice(_logits_from_p0([0.25, 0.5, 0.9, 0.1]), 2)
+    assert out["Ce"] == 2
+    np.testing.assert_allclose(out["scores"][:, 0], [0.25, 0.5, 0.9, 0.1], rtol=1e-6)
+    assert out["route_pos"].tolist() == [[-1, 2], [0, -1], [1, -1], [-1, 3]]
+    assert out["row_token"].tolist() == [1, 2, 0, 3]
+
+
+def test_expert_choice_equal_scores_take_lower_tokens():
+    out = oracle.expert_choice(np.zeros((5, 2), np.float32), 3)
+    assert (out["scores"] == 0.5).all()
+    assert out["route_pos"].tolist() == [[0, 3], [1, 4], [2, 5], [-1, -1], [-1, -1]]
+    # one expert: every score is 1, so the first Ce tokens are taken
+    one = oracle.expert_choice(np.random.default_rng(0).standard_normal((10, 1)).astype(np.float32), 4)
+    assert one["route_pos"][:, 0].tolist() == [0, 1, 2, 3, -1, -1, -1, -1, -1, -1]
+
+
+@pytest.mark.parametrize("T,E,C,seed", [(50, 4, 13, 0), (97, 8, 25, 1), (64, 16, 64, 2),
+                                        (33, 3, 40, 3), (200, 32, 7, 4)])
+def test_expert_choice_ranking_invariant(T, E, C, seed):
+    rng = np.random.default_rng(seed)
+    L = (rng.standard_normal((T, E)) * 2.0).astype(np.float32)
+    L[rng.integers(0, T, T // 5), :] = 0.0  # whole rows of equal scores (ties)
+    out = oracle.expert_choice(L, C)
+    S, P = out["scores"], out["route_pos"]
+    ref = torch.softmax(torch.from_numpy(L).double(), dim=-1).numpy()
+    np.testing.assert_allclose(S, ref, rtol=2e-7, atol=1e-12)
+    Ce = min(C, T)
+    assert out["Ce"] == Ce
+    for e in range(E):
+        taken = np.flatnonzero(P[:, e] >= 0)
+        assert taken.size == Ce  # every expert holds exactly Ce tokens
+        # rows e*Ce .. e*Ce+Ce-1 in increasing token order
+        assert P[taken, e].tolist() == list(range(e * Ce, (e + 1) * Ce))
+        assert out["row_token"][e * Ce:(e + 1) * Ce].tolist() == taken.tolist()
+        left = np.flatnonzero(P[:, e] < 0)
+        if taken.size and left.size:
+            s_in, s_out = S[taken, e], S[left, e]
+            worst_in = s_in.min()
+            assert worst_in >= s_out.max()
+            # among tokens at the boundary score, the taken ones come first
+            tie_in = taken[s_in == worst_in]
+            tie_out = left[s_out == worst_in]
+            if tie_out.size:
+                assert tie_in.max() < tie_out.min()
+
+
+def test_expert_choice_full_capacity_is_the_soft_mixture():
+    # C >= T: every expert takes every token, so y = sum_e p_e E_e(x) + shared,
+    # the dense soft mixture -- the brute-force dense-mask layer with k = E
+    # and no renormalisation
+    w = Workload("ec_dense", T=24, E=4, k=4, d=16, d_ff=24, d_ff_shared=8, dtype="f32",
+                 bias="normal")
+    inp = make_inputs(w, seed=41)
+    out = oracle.layer_forward_expert_choice(inp["x"], inp["w_router"], inp["b_router"],
+                                             inp["w_gate"], inp["w_up"], inp["w_down"], C=-1,
+                                             ws_gate=inp["ws_gate"], ws_up=inp["ws_up"],
+                                             ws_down=inp["ws_down"])
+    assert (out["route_pos"] >= 0).all()
+    ref = dense_mask_layer(inp["x"], inp["w_router"], inp["b_router"], inp["w_gate"], inp["w_up"],
+                           inp["w_down"], k=4, renorm=0, phi=0.0, ws_gate=inp["ws_gate"],
+                           ws_up=inp["ws_up"], ws_down=inp["ws_down"])["y"].numpy()
+    scale = np.abs(ref).max()
+    # the oracle's gates are the fp32 scores (relative rounding 2^-24)
+    np.testing.assert_allclose(out["y"], ref, rtol=1e-6, atol=1e-6 * scale)
+
+
+@pytest.mark.parametrize("dtype,phi", [("bf16", 1.0), ("f32", 0.5)])
+def test_expert_choice_layer_against_dense_products(dtype, phi):
+    w = Workload("ec_layer", T=40, E=6, k=2, d=24, d_ff=32, d_ff_shared=16, dtype=dtype,
+                 bias="normal")
+    inp = make_inputs(w, seed=42)
+    C = oracle.capacity(w.T, w.E, w.k, phi)
+    out = oracle.layer_forward_expert_choice(inp["x"], inp["w_router"], inp["b_router"],
+                                             inp["w_gate"], inp["w_up"], inp["w_down"], C,
+                                             ws_gate=inp["ws_gate"], ws_up=inp["ws_up"],
+                                             ws_down=inp["ws_down"])
+    # the choice is the pinned expert_choice of the router logits
+    L = oracle.router_logits(inp["x"], inp["w_router"], inp["b_router"])
+    ch = oracle.expert_choice(L, C)
+    assert np.array_equal(out["route_pos"], ch["route_pos"])
+    assert np.array_equal(out["scores"], ch["scores"])
+    # y from fp64 library matmuls: every expert on every token, masked
+    X = inp["x"].double()
+    mask = torch.from_numpy((ch["route_pos"] >= 0).astype(np.float64))
+    g = torch.from_numpy(ch["scores"].astype(np.float64)) * mask
+    y = swiglu_dense(X, inp["ws_gate"].double(), inp["ws_up"].double(), inp["ws_down"].double())
+    for e in range(w.E):
+        y = y + g[:, e:e + 1] * swiglu_dense(X, inp["w_gate"][e].double(),
+                                             inp["w_up"][e].double(), inp["w_down"][e].double())
+    np.testing.assert_allclose(out["y"], y.numpy(), rtol=1e-10, atol=1e-12)
+    # a token no expert took gets only the shared expert
+    none = np.flatnonzero((ch["route_pos"] < 0).all(axis=1))
+    if none.size:
+        ysh = swiglu_dense(X, inp["ws_gate"].double(), inp["ws_up"].double(),
+                           inp["ws_down"].double()).numpy()
+        np.testing.assert_allclose(out["y"][none], ysh[none], rtol=1e-10, atol=1e-12)
+
+
+def test_expert_choice_empty_batch():
+    out = oracle.expert_choice(np.zeros((0, 4), np.float32), 3)
+    assert out["Ce"] == 0 and out["row_token"].size == 0 and out["route_pos"].shape == (0, 4)
