@@ -139,7 +139,7 @@ def traffic_summary(fetch_dir, write_dir, workload, cal_mib, out_path):
     print(json.dumps(res))
 
 
-def cpu_baseline(w, inp, seconds):
+def cpu_baseline(w, inp, seconds, choice=False):
     import numpy as np
     import oracle
     cores = int(os.environ.get("OMP_NUM_THREADS") or len(os.sched_getaffinity(0)))
@@ -147,9 +147,15 @@ def cpu_baseline(w, inp, seconds):
     def run(n):
         sel = np.arange(n, dtype=np.int32)
         t0 = time.perf_counter()
-        oracle.layer_forward(inp["x"], inp["w_router"], inp["b_router"], inp["w_gate"],
-                             inp["w_up"], inp["w_down"], w.k, w.renorm, w.phi, inp["ws_gate"],
-                             inp["ws_up"], inp["ws_down"], sel=sel)
+        if choice:
+            oracle.layer_forward_expert_choice(
+                inp["x"], inp["w_router"], inp["b_router"], inp["w_gate"], inp["w_up"],
+                inp["w_down"], oracle.capacity(w.T, w.E, w.k, w.phi), inp["ws_gate"],
+                inp["ws_up"], inp["ws_down"], sel=sel)
+        else:
+            oracle.layer_forward(inp["x"], inp["w_router"], inp["b_router"], inp["w_gate"],
+                                 inp["w_up"], inp["w_down"], w.k, w.renorm, w.phi, inp["ws_gate"],
+                                 inp["ws_up"], inp["ws_down"], sel=sel)
         return time.perf_counter() - t0
 
     n0 = min(w.T, max(1, cores))
@@ -184,6 +190,9 @@ def main():
                     help="fixed-shape [E, C, d] dispatch buffer instead of packed rows")
     ap.add_argument("--reroute", action="store_true",
                     help="reroute overflow policy (dropped routes move to the next-best expert with room)")
+    ap.add_argument("--choice", action="store_true",
+                    help="expert-choice routing (each expert keeps its top-C tokens; full softmax "
+                         "gates, capacity factor 1 when the workload has none)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB")
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
     ap.add_argument("--traffic-out", default=None)
@@ -205,6 +214,8 @@ def main():
     from workloads import WORKLOADS, make_inputs
 
     w = WORKLOADS[args.workload]
+    if args.choice:  # expert choice needs a capacity and full softmax gates
+        w = w.with_(renorm=0, phi=w.phi if w.phi > 0 else 1.0)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     inp = make_inputs(w, seed=0)
@@ -222,6 +233,11 @@ def main():
 
     def step(i):
         p = sets[i % nsets]
+        if args.choice:
+            moe.layer_forward_expert_choice(s, p["x"], p["w_router"], p["b_router"], p["w_gate"],
+                                            p["w_up"], p["w_down"], p["ws_gate"], p["ws_up"],
+                                            p["ws_down"], y=y, ws=ws)
+            return
         moe.layer_forward(s, p["x"], p["w_router"], p["b_router"], p["w_gate"], p["w_up"],
                           p["w_down"], p["ws_gate"], p["ws_up"], p["ws_down"], y=y, ws=ws,
                           padded=args.padded, reroute=args.reroute)
@@ -240,6 +256,8 @@ def main():
     if args.reroute:  # seated rows per expert after rerouting
         seated = rt_r["route_pos"].cpu().flatten() >= 0
         kept = torch.bincount(rt_r["expert_ids"].cpu().flatten().long()[seated], minlength=w.E)
+    if args.choice:  # every expert holds exactly Ce rows
+        kept = torch.full((w.E,), moe.choice_capacity(s), dtype=torch.long)
     kept_rows = int(kept.sum())
     active = int((kept > 0).sum())
 
@@ -271,7 +289,8 @@ def main():
         moe.layer_forward_timed(s, p["x"], p["w_router"], p["b_router"], p["w_gate"], p["w_up"],
                                 p["w_down"], p["ws_gate"], p["ws_up"], p["ws_down"], y, ws,
                                 [None, None, g1_ev[2 * i], g1_ev[2 * i + 1], None, None, None],
-                                stream=stream, padded=args.padded, reroute=args.reroute)
+                                stream=stream, padded=args.padded, reroute=args.reroute,
+                                choice=args.choice)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms = (t1 - t0) * 1e3 / K
@@ -290,7 +309,8 @@ def main():
             moe.layer_forward_timed(s, p["x"], p["w_router"], p["b_router"], p["w_gate"],
                                     p["w_up"], p["w_down"], p["ws_gate"], p["ws_up"],
                                     p["ws_down"], y, ws, evs[7 * i:7 * i + 7], stream=stream,
-                                    padded=args.padded, reroute=args.reroute)
+                                    padded=args.padded, reroute=args.reroute,
+                                    choice=args.choice)
         torch.cuda.synchronize()
         acc = [0.0] * 6
         for i in range(K):
@@ -354,11 +374,12 @@ def main():
         roof["us_per_launch"] = round(g1_us, 2)
         roof["algorithmic_flops"] = flops
         roof["algorithmic_bytes"] = byts
-        roof["traffic"] = None if (args.padded or args.reroute) else traffic_from_profile(w.name)
+        roof["traffic"] = (None if (args.padded or args.reroute or args.choice)
+                           else traffic_from_profile(w.name))
 
     cpu = None
     if not args.no_cpu:
-        cpu = cpu_baseline(w, inp, args.cpu_seconds)
+        cpu = cpu_baseline(w, inp, args.cpu_seconds, choice=args.choice)
 
     out = {
         "metric": "MoE layer forward tokens/s at 1 GPU",
@@ -378,6 +399,7 @@ def main():
                    "kept_routes": kept_rows, "weight_sets": nsets,
                    "layout": "padded [E, C, d]" if args.padded else "packed",
                    "overflow": "reroute" if args.reroute else "drop",
+                   "routing": "expert choice" if args.choice else "token choice (top-k)",
                    "padded_rows": (w.E * C) if (args.padded and C > 0) else None,
                    "parallelism": "single GPU"},
         "roofline": roof,

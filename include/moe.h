@@ -291,6 +291,44 @@ int moe_routing_stats(const moe_shape* s, const float* logits, const float* gate
                       const int32_t* counts, double alpha, int32_t n_bins, float* stats,
                       int32_t* hist, void* ws, size_t ws_bytes, hipStream_t stream);
 
+/* Expert-choice routing ("MoE Inference Visualized", "Why MoE Matters for
+ * Infrastructure": against load imbalance the experts pick the tokens
+ * instead of the tokens picking experts; the page names the idea only).
+ * Reading: score[t][e] = softmax of token t's router logits over all E
+ * experts; expert e keeps the Ce = min(C, T) tokens of largest score (C =
+ * moe_capacity's), the lower token index first among equal scores; a kept
+ * pair's gate is its score.  Every expert holds exactly Ce rows; a token may
+ * be kept by any number of experts, none included (it then gets only the
+ * shared expert).  The choice is made on the fp32 scores written out.
+ * Inputs: x [T][d]; logits [T][E] fp32 from moe_route.
+ * Outputs:
+ *   scores      [T][E] fp32
+ *   route_pos   [T][E] int32: row e*Ce + i when expert e kept token t as its
+ *               i-th token in increasing index, else -1
+ *   offsets     [E+1] int32: e*Ce
+ *   row_token   [E*Ce] int32: source token of every row
+ *   x_packed    [E*Ce][d]: x_packed[r] = x[row_token[r]]
+ * shape->k only sets C = ceil(phi*T*k/E).  Needs phi > 0 and renormalize = 0
+ * (else MOE_ERR_INVALID_ARG) and T <= 32768 (else MOE_ERR_UNSUPPORTED).
+ * Uses the workspace of moe_workspace_bytes. */
+int moe_permute_expert_choice(const moe_shape* s, const void* x, const float* logits,
+                              float* scores, int32_t* route_pos, int32_t* offsets,
+                              int32_t* row_token, void* x_packed, void* ws, size_t ws_bytes,
+                              hipStream_t stream);
+
+/* moe_layer_forward under expert-choice routing: router logits, the choice of
+ * moe_permute_expert_choice, the expert FFNs on the E*Ce rows, then
+ * y[t] = sum over the experts e that kept t, in increasing e, of
+ * score[t][e] * E_e(x_t), plus the shared expert.  scores and route_pos
+ * ([T][E]) are optional outputs (NULL: kept in the workspace).  Same
+ * requirements as moe_permute_expert_choice. */
+int moe_layer_forward_expert_choice(const moe_shape* s, const void* x, const void* w_router,
+                                    const float* b_router, const void* w_gate, const void* w_up,
+                                    const void* w_down, const void* ws_gate, const void* ws_up,
+                                    const void* ws_down, void* y, float* scores,
+                                    int32_t* route_pos, void* ws, size_t ws_bytes,
+                                    hipStream_t stream);
+
 /* Measurement variant of moe_layer_forward (same arguments without the
  * optional routing outputs): additionally records events[i] on the stream at
  * the stage boundaries, so that elapsed times between them are the stage
@@ -304,7 +342,9 @@ int moe_routing_stats(const moe_shape* s, const float* logits, const float* gate
  *              entry is skipped.  The array itself must not be NULL.
  *   layout     0: packed rows (moe_layer_forward); 1: the fixed-shape
  *              [E, C, d] buffer (moe_layer_forward_padded); 2: the reroute
- *              overflow policy (moe_layer_forward_reroute). */
+ *              overflow policy (moe_layer_forward_reroute); 3: expert-choice
+ *              routing (moe_layer_forward_expert_choice; events[1] is then
+ *              before the choice). */
 int moe_layer_forward_timed(const moe_shape* s, const void* x, const void* w_router,
                             const float* b_router, const void* w_gate, const void* w_up,
                             const void* w_down, const void* ws_gate, const void* ws_up,

@@ -8,7 +8,9 @@ fails when libmoe.so has not been built.
 
 Entry points (same names as the C ABI, without the moe_ prefix):
     capacity, workspace_bytes, route, permute, expert_ffn, combine,
-    layer_forward
+    layer_forward, layer_forward_timed, routing_stats, permute_padded,
+    permute_reroute, permute_expert_choice, layer_forward_expert_choice
+    (layer_forward takes padded= / reroute= for the other layouts)
 """
 import ctypes
 import os
@@ -31,7 +33,8 @@ MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP
 EXPORTS = ("moe_status_string", "moe_capacity", "moe_workspace_bytes", "moe_route",
            "moe_permute", "moe_expert_ffn", "moe_combine", "moe_layer_forward",
            "moe_layer_forward_timed", "moe_routing_stats", "moe_permute_padded",
-           "moe_layer_forward_padded", "moe_permute_reroute", "moe_layer_forward_reroute")
+           "moe_layer_forward_padded", "moe_permute_reroute", "moe_layer_forward_reroute",
+           "moe_permute_expert_choice", "moe_layer_forward_expert_choice")
 
 
 class MoeShape(ctypes.Structure):
@@ -64,6 +67,8 @@ _lib.moe_permute_padded.argtypes = [_SP] + [_vp] * 6 + [_vp, _sz, _vp]
 _lib.moe_layer_forward_padded.argtypes = [_SP] + [_vp] * 14 + [_vp, _sz, _vp]
 _lib.moe_permute_reroute.argtypes = [_SP] + [_vp] * 10 + [_vp, _sz, _vp]
 _lib.moe_layer_forward_reroute.argtypes = [_SP] + [_vp] * 14 + [_vp, _sz, _vp]
+_lib.moe_permute_expert_choice.argtypes = [_SP] + [_vp] * 7 + [_vp, _sz, _vp]
+_lib.moe_layer_forward_expert_choice.argtypes = [_SP] + [_vp] * 12 + [_vp, _sz, _vp]
 _lib.moe_routing_stats.argtypes = [_SP, _vp, _vp, _vp, ctypes.c_double, ctypes.c_int32, _vp, _vp,
                                    _vp, _sz, _vp]
 for _n in EXPORTS[1:]:
@@ -235,6 +240,69 @@ def permute_reroute(s, x, logits, expert_ids, ws=None, stream=None):
     return out
 
 
+def choice_capacity(s):
+    """Tokens every expert keeps under expert-choice routing: min(C, T)."""
+    C, _ = capacity(s)
+    return max(0, min(C, s.T))
+
+
+def permute_expert_choice(s, x, logits, ws=None, stream=None):
+    """Expert-choice dispatch.  Returns dict(scores [T, E], route_pos [T, E],
+    offsets [E+1], row_token [E*Ce], x_packed [E*Ce, d])."""
+    dt = _tdtype(s)
+    dev = x.device
+    Ce = choice_capacity(s)
+    xp = _ptr(x, "x", (s.T, s.d), dt)
+    lp = _ptr(logits, "logits", (s.T, s.E), torch.float32)
+    out = dict(scores=torch.empty(s.T, s.E, dtype=torch.float32, device=dev),
+               route_pos=torch.empty(s.T, s.E, dtype=torch.int32, device=dev),
+               offsets=torch.empty(s.E + 1, dtype=torch.int32, device=dev),
+               row_token=torch.empty(max(s.E * Ce, 1), dtype=torch.int32, device=dev),
+               x_packed=torch.empty(max(s.E * Ce, 1), s.d, dtype=dt, device=dev))
+    ws = _ws(s, ws, dev)
+    _check(_lib.moe_permute_expert_choice(ctypes.byref(s), xp, lp, _ptr(out["scores"], "scores"),
+                                          _ptr(out["route_pos"], "route_pos"),
+                                          out["offsets"].data_ptr(), out["row_token"].data_ptr(),
+                                          out["x_packed"].data_ptr(), ws.data_ptr(), ws.numel(),
+                                          _stream(stream)), "moe_permute_expert_choice")
+    out["row_token"] = out["row_token"][:s.E * Ce]
+    out["x_packed"] = out["x_packed"][:s.E * Ce]
+    return out
+
+
+def layer_forward_expert_choice(s, x, w_router, b_router, w_gate, w_up, w_down, ws_gate=None,
+                                ws_up=None, ws_down=None, y=None, ws=None, stream=None,
+                                return_routing=False):
+    """Whole MoE layer under expert-choice routing.  Returns y, or (y,
+    dict(scores [T, E], route_pos [T, E])) with return_routing."""
+    dt = _tdtype(s)
+    dev = x.device
+    shp = s.d_ff_shared > 0
+    args = (_ptr(x, "x", (s.T, s.d), dt), _ptr(w_router, "w_router", (s.E, s.d), dt),
+            _ptr(b_router, "b_router", (s.E,), torch.float32, optional=True),
+            _ptr(w_gate, "w_gate", (s.E, s.d_ff, s.d), dt),
+            _ptr(w_up, "w_up", (s.E, s.d_ff, s.d), dt),
+            _ptr(w_down, "w_down", (s.E, s.d, s.d_ff), dt),
+            _ptr(ws_gate, "ws_gate", (s.d_ff_shared, s.d), dt, optional=not shp),
+            _ptr(ws_up, "ws_up", (s.d_ff_shared, s.d), dt, optional=not shp),
+            _ptr(ws_down, "ws_down", (s.d, s.d_ff_shared), dt, optional=not shp))
+    if y is None:
+        y = torch.empty(s.T, s.d, dtype=dt, device=dev)
+    yo = _ptr(y, "y", (s.T, s.d), dt)
+    routing = None
+    scp = rpp = None
+    if return_routing:
+        routing = dict(scores=torch.empty(s.T, s.E, dtype=torch.float32, device=dev),
+                       route_pos=torch.empty(s.T, s.E, dtype=torch.int32, device=dev))
+        scp = _ptr(routing["scores"], "scores")
+        rpp = _ptr(routing["route_pos"], "route_pos")
+    ws = _ws(s, ws, dev)
+    _check(_lib.moe_layer_forward_expert_choice(ctypes.byref(s), *args, yo, scp, rpp,
+                                                ws.data_ptr(), ws.numel(), _stream(stream)),
+           "moe_layer_forward_expert_choice")
+    return (y, routing) if return_routing else y
+
+
 def expert_ffn(s, x_packed, offsets, w_gate, w_up, w_down, y_packed=None, ws=None, stream=None):
     """Grouped SwiGLU expert FFN over packed rows.  Returns y_packed [R_max, d]."""
     dt = _tdtype(s)
@@ -346,9 +414,11 @@ def layer_forward(s, x, w_router, b_router, w_gate, w_up, w_down, ws_gate=None, 
 
 
 def layer_forward_timed(s, x, w_router, b_router, w_gate, w_up, w_down, ws_gate, ws_up, ws_down,
-                        y, ws, events, stream=None, padded=False, reroute=False):
+                        y, ws, events, stream=None, padded=False, reroute=False, choice=False):
     """moe_layer_forward_timed: records the 7 stage-boundary hipEvents
-    (`events`: sequence of raw hipEvent_t handles as ints)."""
+    (`events`: sequence of raw hipEvent_t handles as ints).  padded, reroute
+    and choice select the layout (fixed [E, C, d] buffer, reroute overflow
+    policy, expert-choice routing)."""
     dt = _tdtype(s)
     arr = (ctypes.c_void_p * 7)(*[ctypes.c_void_p(e) for e in events])
     shp = s.d_ff_shared > 0
@@ -361,6 +431,6 @@ def layer_forward_timed(s, x, w_router, b_router, w_gate, w_up, w_down, ws_gate,
         _ptr(ws_up, "ws_up", (s.d_ff_shared, s.d), dt, optional=not shp),
         _ptr(ws_down, "ws_down", (s.d, s.d_ff_shared), dt, optional=not shp),
         _ptr(y, "y", (s.T, s.d), dt), ws.data_ptr(), ws.numel(), _stream(stream), arr,
-        1 if padded else 2 if reroute else 0),
+        1 if padded else 2 if reroute else 3 if choice else 0),
         "moe_layer_forward_timed")
     return y

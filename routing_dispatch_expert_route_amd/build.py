@@ -17,7 +17,8 @@ LIB = os.path.join(PKG, "libmoe.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
-SOURCES = ["route.hip", "permute.hip", "gemm.hip", "combine.hip", "stats.hip", "moe_api.cpp"]
+SOURCES = ["route.hip", "permute.hip", "choice.hip", "gemm.hip", "combine.hip", "stats.hip",
+           "moe_api.cpp"]
 
 COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-I", INC, "-I", CSRC,
           "-Wall", "-Wno-unused-result"]

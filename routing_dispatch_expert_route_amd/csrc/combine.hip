@@ -7,8 +7,9 @@
 // dropped route contributes nothing and the kept gates stay as they are.
 //
 // One wave per (token, slice of 64 column chunks); each lane owns one chunk
-// of 8 (bf16) or 4 (fp32) output columns.  The k rows of a token are gathered with vector loads, summed in
-// fp32 in slot order j = 0..k-1 (fused multiply-add by the gate), the shared
+// of 8 (bf16) or 4 (fp32) output columns.  The k rows of a token (any k;
+// expert choice passes one slot per expert) are gathered with vector loads,
+// summed in fp32 in slot order j = 0..k-1 (fused multiply-add by the gate), the shared
 // row added last, and the sum rounded once to the output type.  When the
 // down GEMM split K, a row is first the sum of its fp32 partial planes in
 // plane order.  No atomics: every order is fixed.
@@ -84,23 +85,27 @@ __global__ __launch_bounds__(256) void combine_kernel(const void* __restrict__ y
   const int t = blockIdx.x * (blockDim.x / 64) + (threadIdx.x >> 6);
   const int col = (blockIdx.y * 64 + lane) * G;
   if (t >= T || col >= d) return;
-  int pos[8];
-  float g[8];
-#pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    pos[j] = j < k ? route_pos[(size_t)t * k + j] : -1;
-    g[j] = j < k ? gates[(size_t)t * k + j] : 0.0f;
-  }
   float acc[G];
 #pragma unroll
   for (int q = 0; q < G; ++q) acc[q] = 0.0f;
+  // slots in groups of eight (one group when k <= 8; expert choice passes
+  // one slot per expert)
+  for (int j0 = 0; j0 < k; j0 += 8) {
+    int pos[8];
+    float g[8];
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    if (pos[j] < 0) continue;
-    float v[G];
-    load_row<BF16, PARTIAL, G>(yp, splits, split_stride, (size_t)pos[j], d, col, v);
+    for (int j = 0; j < 8; ++j) {
+      pos[j] = j0 + j < k ? route_pos[(size_t)t * k + j0 + j] : -1;
+      g[j] = j0 + j < k ? gates[(size_t)t * k + j0 + j] : 0.0f;
+    }
 #pragma unroll
-    for (int q = 0; q < G; ++q) acc[q] = __builtin_fmaf(g[j], v[q], acc[q]);
+    for (int j = 0; j < 8; ++j) {
+      if (pos[j] < 0) continue;
+      float v[G];
+      load_row<BF16, PARTIAL, G>(yp, splits, split_stride, (size_t)pos[j], d, col, v);
+#pragma unroll
+      for (int q = 0; q < G; ++q) acc[q] = __builtin_fmaf(g[j], v[q], acc[q]);
+    }
   }
   if (ysh) {
     float v[G];

@@ -6,7 +6,8 @@
 
 namespace moe {
 
-// router_logits_kernel + topk_gates_kernel
+// router_logits_kernel + topk_gates_kernel (the projection only when ids
+// is null)
 hipError_t launch_route(bool bf16, const void* x, const void* w, const float* b, int T, int d,
                         int E, int k, int renorm, float* logits, int32_t* ids, float* gates,
                         hipStream_t st);
@@ -36,6 +37,14 @@ hipError_t launch_padded(const void* x, const int32_t* ids, const int32_t* route
                          const int32_t* offsets, const int32_t* kept, const int32_t* row_token,
                          int T, int k, int E, int C, long row_bytes, int32_t* pad_pos,
                          void* x_pad, int32_t* offsets_pad, hipStream_t st);
+
+// Expert-choice routing from router logits [T][E]: scores [T][E] (softmax),
+// keys [E][T] scratch, route_pos [T][E] (row e*Ce + i or -1), row_token
+// [E*Ce] and offsets[e] = e*Ce.  Needs T <= 32768 and 1 <= Ce <= T (Ce = 0
+// when T = 0).
+hipError_t launch_expert_choice(const float* logits, int T, int E, int Ce, float* scores,
+                                uint32_t* keys, int32_t* route_pos, int32_t* row_token,
+                                int32_t* offsets, hipStream_t st);
 
 // Row groups of a grouped GEMM: device offsets[E+1] (never read on the
 // host), or one dense group of M_dense rows when offsets is null.

@@ -13,6 +13,7 @@ namespace {
 constexpr int64_t kMaxE = 256;
 constexpr int64_t kMaxK = 8;
 constexpr int64_t kMaxRerouteE = 64;  // the reroute walk keeps one expert per lane
+constexpr int64_t kMaxChoiceT = 32768;  // expert choice keeps a column in registers
 constexpr size_t kAlign = 256;
 
 size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
@@ -66,9 +67,10 @@ int64_t rmax_of(const moe_shape* s, int64_t C) {
 
 struct Layout {
   size_t logits, ids, gates, cnt, counts, kept, offsets, route_pos, row_token, h, yp, part, hs,
-      ys, spart, shist, xpad, opad, ppos, ids2, slot, offs2, rpos0, pref;
+      ys, spart, shist, xpad, opad, ppos, ids2, slot, offs2, rpos0, pref, ecs, eck, ecp, ecoff;
   int splits;      // K splits of the routed down GEMM (fp32 partial planes when > 1)
   int splits_pad;  // the same for the fixed-shape [E, C] layout
+  int splits_ec;   // the same for expert-choice rows
   size_t total;
 };
 
@@ -107,6 +109,34 @@ moe::GemmPlan padded_plan(const moe_shape* s, const int32_t* offsets_pad) {
                        (long)rpad_of(s), (long)(C > 0 ? C : 0)};
 }
 
+// Expert choice: every expert keeps Ce = min(C, T) tokens (C from phi > 0;
+// 0 without a capacity, which validate_choice rejects).
+int64_t ce_of(const moe_shape* s) {
+  const int64_t C = capacity_of(s);
+  if (C < 0) return 0;
+  return C < s->T ? C : s->T;
+}
+
+// Expert choice needs a capacity (its rows are the fixed E*Ce; their extent
+// is bounded like the fixed-shape buffer's), full softmax gates (a token's
+// number of experts is not fixed, so there is no set to renormalise over)
+// and T within the register-resident selection.
+int validate_choice(const moe_shape* s) {
+  if (!(s->phi > 0.0) || s->renormalize != 0) return MOE_ERR_INVALID_ARG;
+  if (s->T > kMaxChoiceT) return MOE_ERR_UNSUPPORTED;
+  const int64_t eb = elem_bytes(s);
+  const int64_t wide = s->d > s->d_ff ? s->d : s->d_ff;
+  if (s->E * ce_of(s) * wide * eb >= (int64_t(1) << 31)) return MOE_ERR_UNSUPPORTED;
+  return MOE_OK;
+}
+
+// E groups of exactly Ce rows (device offsets e*Ce).
+moe::GemmPlan choice_plan(const moe_shape* s, const int32_t* offsets_ec) {
+  const int64_t Ce = ce_of(s);
+  return moe::GemmPlan{s->dtype == MOE_DTYPE_BF16, true, offsets_ec, (int)s->E, 0,
+                       (long)(s->E * Ce), (long)Ce};
+}
+
 Layout layout_of(const moe_shape* s) {
   const int64_t C = capacity_of(s);
   const int64_t Rmax = rmax_of(s, C);
@@ -128,19 +158,26 @@ Layout layout_of(const moe_shape* s) {
   L.kept = take((size_t)s->E * sizeof(int32_t));
   L.offsets = take((size_t)(s->E + 1) * sizeof(int32_t));
   L.route_pos = take(R * sizeof(int32_t));
-  L.row_token = take((size_t)Rmax * sizeof(int32_t));
   // expert rows: the packed layout's R_max rows, or the fixed-shape
-  // buffer's E*C rows when there is a capacity (the larger of the two)
+  // buffer's E*C rows when there is a capacity (the larger of the two;
+  // expert choice's E*Ce rows are at most E*C)
   const int64_t Rpad = rpad_of(s);
   const size_t Rbig = (size_t)(Rpad > Rmax ? Rpad : Rmax);
+  L.row_token = take(Rbig * sizeof(int32_t));
   L.h = take(Rbig * s->d_ff * eb);
   L.yp = take(Rbig * s->d * eb);
   L.splits = moe::gemm_down_splits(routed_plan(s, nullptr, false), (int)s->d, (int)s->d_ff);
   L.splits_pad = Rpad > 0 ? moe::gemm_down_splits(padded_plan(s, nullptr), (int)s->d, (int)s->d_ff)
                           : 1;
+  L.splits_ec = Rpad > 0 ? moe::gemm_down_splits(choice_plan(s, nullptr), (int)s->d, (int)s->d_ff)
+                         : 1;
   const size_t part_rows = (size_t)(L.splits > 1 ? L.splits * Rmax : 0);
   const size_t part_rows_pad = (size_t)(L.splits_pad > 1 ? L.splits_pad * Rpad : 0);
-  L.part = take((part_rows > part_rows_pad ? part_rows : part_rows_pad) * s->d * sizeof(float));
+  const size_t part_rows_ec =
+      (size_t)(L.splits_ec > 1 && Rpad > 0 ? L.splits_ec * s->E * ce_of(s) : 0);
+  size_t part_max = part_rows > part_rows_pad ? part_rows : part_rows_pad;
+  if (part_rows_ec > part_max) part_max = part_rows_ec;
+  L.part = take(part_max * s->d * sizeof(float));
   L.xpad = take((size_t)Rpad * s->d * eb);
   L.opad = take((size_t)(s->E + 1) * sizeof(int32_t));
   L.ppos = take(R * sizeof(int32_t));
@@ -150,6 +187,12 @@ Layout layout_of(const moe_shape* s) {
   L.offs2 = take((size_t)(s->E + 1) * sizeof(int32_t));
   L.rpos0 = take(R * sizeof(int32_t));
   L.pref = take(R * 64);  // preference lists of the dropped routes (E <= 64)
+  // expert choice: scores, expert-major keys, route table [T][E], row groups
+  const size_t TE = (size_t)s->T * s->E;
+  L.ecs = take(TE * sizeof(float));
+  L.eck = take(TE * sizeof(uint32_t));
+  L.ecp = take(TE * sizeof(int32_t));
+  L.ecoff = take((size_t)(s->E + 1) * sizeof(int32_t));
   L.hs = take((size_t)s->T * s->d_ff_shared * eb);
   L.ys = take(s->d_ff_shared > 0 ? (size_t)s->T * s->d * eb : 0);
   // routing statistics: one partial row per 64 tokens
@@ -308,6 +351,29 @@ int moe_permute_reroute(const moe_shape* s, const void* x, const float* logits,
                                             s->d * elem_bytes(s), x_packed, stream));
 }
 
+int moe_permute_expert_choice(const moe_shape* s, const void* x, const float* logits,
+                              float* scores, int32_t* route_pos, int32_t* offsets,
+                              int32_t* row_token, void* x_packed, void* ws, size_t ws_bytes,
+                              hipStream_t stream) {
+  int v = validate(s);
+  if (v != MOE_OK) return v;
+  if ((v = validate_choice(s)) != MOE_OK) return v;
+  const bool tok = s->T > 0;
+  if (!offsets || (tok && (!x || !logits || !scores || !route_pos || !row_token || !x_packed)))
+    return MOE_ERR_INVALID_ARG;
+  if (!aligned16(x) || !aligned16(x_packed)) return MOE_ERR_INVALID_ARG;
+  v = check_ws(s, ws, ws_bytes);
+  if (v != MOE_OK) return v;
+  const Layout L = layout_of(s);
+  const int T = (int)s->T, E = (int)s->E;
+  const int Ce = (int)ce_of(s);
+  hipError_t e = moe::launch_expert_choice(logits, T, E, Ce, scores, at<uint32_t>(ws, L.eck),
+                                           route_pos, row_token, offsets, stream);
+  if (e != hipSuccess) return MOE_ERR_HIP;
+  return hip_status(moe::launch_gather_rows(x, row_token, offsets, E, (long)E * Ce,
+                                            s->d * elem_bytes(s), x_packed, stream));
+}
+
 int moe_expert_ffn(const moe_shape* s, const void* x_packed, const int32_t* offsets,
                    const void* w_gate, const void* w_up, const void* w_down, void* y_packed,
                    void* ws, size_t ws_bytes, hipStream_t stream) {
@@ -368,6 +434,58 @@ int moe_routing_stats(const moe_shape* s, const float* logits, const float* gate
                                               stats, hist, stream));
 }
 
+// Expert GEMMs over the row groups of pl (activations A, gathered through
+// a_rows when non-null; a_nrows rows of A), the shared expert (on x), and the
+// combine over kslots slots per token (route table rpos, gates g, both
+// [T][kslots]).  splits: K splits of the down GEMM, whose fp32 planes hold
+// `rows` rows each.  Records events 2..6 of the timed variant.
+static int experts_and_combine(const moe_shape* s, const Layout& L, const moe::GemmPlan& pl,
+                               const void* x, const void* A, const int32_t* a_rows, long a_nrows,
+                               const void* w_gate, const void* w_up, const void* w_down,
+                               const void* ws_gate, const void* ws_up, const void* ws_down,
+                               int splits, long rows, const int32_t* rpos, const float* g,
+                               int kslots, void* y, void* ws, hipStream_t stream, hipEvent_t* ev) {
+  const bool bf16 = s->dtype == MOE_DTYPE_BF16;
+  const int T = (int)s->T, d = (int)s->d, dff = (int)s->d_ff;
+  void* h = at<void>(ws, L.h);
+  void* yp = at<void>(ws, L.yp);
+  auto mark = [&](int i) {
+    if (ev && ev[i]) hipEventRecord(ev[i], stream);
+  };
+  mark(2);
+  hipError_t e = moe::launch_gemm_swiglu(pl, A, a_rows, a_nrows, w_gate, w_up, dff, d, h, stream);
+  if (e != hipSuccess) return MOE_ERR_HIP;
+  mark(3);
+  const void* yrows = yp;
+  const long stride = rows * d;
+  if (splits > 1) {
+    yrows = at<float>(ws, L.part);
+    e = moe::launch_gemm_down(pl, h, w_down, d, dff, at<float>(ws, L.part), splits, stride,
+                              stream);
+  } else {
+    e = moe::launch_gemm_down(pl, h, w_down, d, dff, yp, 1, 0, stream);
+  }
+  if (e != hipSuccess) return MOE_ERR_HIP;
+  mark(4);
+  const void* ysh = nullptr;
+  if (s->d_ff_shared > 0) {
+    moe::GemmPlan ps{bf16, false, nullptr, 1, T, (long)T, (long)T};
+    void* hs = at<void>(ws, L.hs);
+    void* ys = at<void>(ws, L.ys);
+    e = moe::launch_gemm_swiglu(ps, x, nullptr, T, ws_gate, ws_up, (int)s->d_ff_shared, d, hs,
+                                stream);
+    if (e != hipSuccess) return MOE_ERR_HIP;
+    e = moe::launch_gemm_down(ps, hs, ws_down, d, (int)s->d_ff_shared, ys, 1, 0, stream);
+    if (e != hipSuccess) return MOE_ERR_HIP;
+    ysh = ys;
+  }
+  mark(5);
+  e = moe::launch_combine(bf16, yrows, splits, stride, rpos, g, ysh, T, kslots, d, y, stream);
+  if (e != hipSuccess) return MOE_ERR_HIP;
+  mark(6);
+  return MOE_OK;
+}
+
 static int layer_forward_impl(const moe_shape* s, const void* x, const void* w_router,
                               const float* b_router, const void* w_gate, const void* w_up,
                               const void* w_down, const void* ws_gate, const void* ws_up,
@@ -375,13 +493,16 @@ static int layer_forward_impl(const moe_shape* s, const void* x, const void* w_r
                               int32_t* counts, int32_t* route_pos, void* ws, size_t ws_bytes,
                               hipStream_t stream, hipEvent_t* ev, int layout) {
   // layout 0: packed rows; 1: fixed-shape [E, C, d] buffer; 2: packed rows
-  // after the reroute overflow policy
+  // after the reroute overflow policy; 3: expert-choice rows (gates and
+  // route_pos are then [T][E], expert_ids and counts unused)
   const bool padded = layout == 1;
   const bool reroute = layout == 2;
+  const bool choice = layout == 3;
   int v = validate(s);
   if (v != MOE_OK) return v;
   if (padded && (v = validate_padded(s)) != MOE_OK) return v;
   if (reroute && s->E > kMaxRerouteE) return MOE_ERR_UNSUPPORTED;
+  if (choice && (v = validate_choice(s)) != MOE_OK) return v;
   if (!w_router || !w_gate || !w_up || !w_down || (s->T > 0 && (!x || !y)))
     return MOE_ERR_INVALID_ARG;
   const bool shared = s->d_ff_shared > 0;
@@ -396,7 +517,7 @@ static int layer_forward_impl(const moe_shape* s, const void* x, const void* w_r
 
   const Layout L = layout_of(s);
   const bool bf16 = s->dtype == MOE_DTYPE_BF16;
-  const int T = (int)s->T, d = (int)s->d, E = (int)s->E, k = (int)s->k, dff = (int)s->d_ff;
+  const int T = (int)s->T, d = (int)s->d, E = (int)s->E, k = (int)s->k;
   const int64_t C = capacity_of(s);
   const int64_t Rmax = rmax_of(s, C);
   // router choices (rerouting keeps them internal and reports the final
@@ -412,13 +533,29 @@ static int layer_forward_impl(const moe_shape* s, const void* x, const void* w_r
   const int64_t Rpad = rpad_of(s);
   int32_t* offsets = at<int32_t>(ws, L.offsets);
   int32_t* row_token = at<int32_t>(ws, L.row_token);
-  void* h = at<void>(ws, L.h);
-  void* yp = at<void>(ws, L.yp);
 
   auto mark = [&](int i) {
     if (ev && ev[i]) hipEventRecord(ev[i], stream);
   };
   mark(0);
+  if (choice) {
+    // expert choice: logits, each expert's top-Ce tokens, then the shared
+    // GEMM, shared-expert and combine stages below with one slot per expert
+    const int Ce = (int)ce_of(s);
+    float* sc = gates ? gates : at<float>(ws, L.ecs);
+    int32_t* ecpos = route_pos ? route_pos : at<int32_t>(ws, L.ecp);
+    int32_t* ecoff = at<int32_t>(ws, L.ecoff);
+    hipError_t e = moe::launch_route(bf16, x, w_router, b_router, T, d, E, k, 0,
+                                     at<float>(ws, L.logits), nullptr, nullptr, stream);
+    if (e != hipSuccess) return MOE_ERR_HIP;
+    mark(1);
+    e = moe::launch_expert_choice(at<float>(ws, L.logits), T, E, Ce, sc, at<uint32_t>(ws, L.eck),
+                                  ecpos, row_token, ecoff, stream);
+    if (e != hipSuccess) return MOE_ERR_HIP;
+    return experts_and_combine(s, L, choice_plan(s, ecoff), x, x, row_token, T, w_gate, w_up,
+                               w_down, ws_gate, ws_up, ws_down, L.splits_ec, (long)E * Ce, ecpos,
+                               sc, E, y, ws, stream, ev);
+  }
   hipError_t e = moe::launch_route(bf16, x, w_router, b_router, T, d, E, k, s->renormalize,
                                    at<float>(ws, L.logits), ids, g, stream);
   if (e != hipSuccess) return MOE_ERR_HIP;
@@ -445,45 +582,12 @@ static int layer_forward_impl(const moe_shape* s, const void* x, const void* w_r
   }
   const moe::GemmPlan pl =
       padded ? padded_plan(s, at<int32_t>(ws, L.opad)) : routed_plan(s, offsets, true);
-  mark(2);
   if (padded)
-    e = moe::launch_gemm_swiglu(pl, at<void>(ws, L.xpad), nullptr, Rpad, w_gate, w_up, dff, d, h,
-                                stream);
-  else
-    e = moe::launch_gemm_swiglu(pl, x, row_token, T, w_gate, w_up, dff, d, h, stream);
-  if (e != hipSuccess) return MOE_ERR_HIP;
-  mark(3);
-  // the split decision depends on the shape only (same as the workspace)
-  const int splits = padded ? L.splits_pad : L.splits;
-  const void* yrows = yp;
-  const long stride = (long)(padded ? Rpad : Rmax) * d;
-  if (splits > 1) {
-    yrows = at<float>(ws, L.part);
-    e = moe::launch_gemm_down(pl, h, w_down, d, dff, at<float>(ws, L.part), splits, stride,
-                              stream);
-  } else {
-    e = moe::launch_gemm_down(pl, h, w_down, d, dff, yp, 1, 0, stream);
-  }
-  if (e != hipSuccess) return MOE_ERR_HIP;
-  mark(4);
-  const void* ysh = nullptr;
-  if (shared) {
-    moe::GemmPlan ps{bf16, false, nullptr, 1, T, (long)T, (long)T};
-    void* hs = at<void>(ws, L.hs);
-    void* ys = at<void>(ws, L.ys);
-    e = moe::launch_gemm_swiglu(ps, x, nullptr, T, ws_gate, ws_up, (int)s->d_ff_shared, d, hs,
-                                stream);
-    if (e != hipSuccess) return MOE_ERR_HIP;
-    e = moe::launch_gemm_down(ps, hs, ws_down, d, (int)s->d_ff_shared, ys, 1, 0, stream);
-    if (e != hipSuccess) return MOE_ERR_HIP;
-    ysh = ys;
-  }
-  mark(5);
-  e = moe::launch_combine(bf16, yrows, splits, stride, padded ? ppos : rpos, g, ysh, T, k, d, y,
-                         stream);
-  if (e != hipSuccess) return MOE_ERR_HIP;
-  mark(6);
-  return MOE_OK;
+    return experts_and_combine(s, L, pl, x, at<void>(ws, L.xpad), nullptr, Rpad, w_gate, w_up,
+                               w_down, ws_gate, ws_up, ws_down, L.splits_pad, Rpad, ppos, g, k,
+                               y, ws, stream, ev);
+  return experts_and_combine(s, L, pl, x, x, row_token, T, w_gate, w_up, w_down, ws_gate, ws_up,
+                             ws_down, L.splits, Rmax, rpos, g, k, y, ws, stream, ev);
 }
 
 int moe_layer_forward(const moe_shape* s, const void* x, const void* w_router,
@@ -519,13 +623,24 @@ int moe_layer_forward_reroute(const moe_shape* s, const void* x, const void* w_r
                             stream, nullptr, 2);
 }
 
+int moe_layer_forward_expert_choice(const moe_shape* s, const void* x, const void* w_router,
+                                    const float* b_router, const void* w_gate, const void* w_up,
+                                    const void* w_down, const void* ws_gate, const void* ws_up,
+                                    const void* ws_down, void* y, float* scores,
+                                    int32_t* route_pos, void* ws, size_t ws_bytes,
+                                    hipStream_t stream) {
+  return layer_forward_impl(s, x, w_router, b_router, w_gate, w_up, w_down, ws_gate, ws_up,
+                            ws_down, y, nullptr, scores, nullptr, route_pos, ws, ws_bytes, stream,
+                            nullptr, 3);
+}
+
 int moe_layer_forward_timed(const moe_shape* s, const void* x, const void* w_router,
                             const float* b_router, const void* w_gate, const void* w_up,
                             const void* w_down, const void* ws_gate, const void* ws_up,
                             const void* ws_down, void* y, void* ws, size_t ws_bytes,
                             hipStream_t stream, hipEvent_t* events, int32_t layout) {
   if (!events) return MOE_ERR_INVALID_ARG;
-  if (layout < 0 || layout > 2) return MOE_ERR_INVALID_ARG;
+  if (layout < 0 || layout > 3) return MOE_ERR_INVALID_ARG;
   return layer_forward_impl(s, x, w_router, b_router, w_gate, w_up, w_down, ws_gate, ws_up,
                             ws_down, y, nullptr, nullptr, nullptr, nullptr, ws, ws_bytes, stream,
                             events, layout);

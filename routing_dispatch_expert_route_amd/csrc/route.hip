@@ -257,7 +257,7 @@ hipError_t launch_route(bool bf16, const void* x, const void* w, const float* b,
   }
 #undef RL
   hipError_t err = hipGetLastError();
-  if (err != hipSuccess) return err;
+  if (err != hipSuccess || !ids) return err;  // logits only
   const int tpb = (E + 1) * 64 * (int)sizeof(float) <= 48 * 1024 ? 64 : 32;
   const size_t lds = (size_t)tpb * (E + 1) * sizeof(float);
   const dim3 tg(ceil_div(T, tpb)), tb(tpb);

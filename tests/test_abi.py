@@ -212,3 +212,32 @@ def test_reroute_needs_at_most_64_experts():
     assert L.moe_layer_forward_reroute(by, fake, fake, None, fake, fake, fake, None, None, None,
                                        fake, None, None, None, None, ws, need, None) \
         == moe.MOE_ERR_UNSUPPORTED
+
+
+def test_expert_choice_rejected_before_launch():
+    moe = _moe()
+    L = moe._lib
+    fake, ws = 4096, 1 << 20
+
+    def both(s):
+        by = ctypes.byref(s)
+        need = moe.workspace_bytes(s)
+        a = L.moe_permute_expert_choice(by, fake, fake, fake, fake, fake, fake, fake, ws, need,
+                                        None)
+        b = L.moe_layer_forward_expert_choice(by, fake, fake, None, fake, fake, fake, None, None,
+                                              None, fake, None, None, ws, need, None)
+        return a, b
+
+    # no capacity: an expert's share is undefined
+    assert both(moe.shape(16, 64, 4, 2, 64, renorm=0)) == (moe.MOE_ERR_INVALID_ARG,) * 2
+    # renormalised gates: a token's set of experts is not fixed
+    assert both(moe.shape(16, 64, 4, 2, 64, renorm=1, phi=1.0)) == (moe.MOE_ERR_INVALID_ARG,) * 2
+    # beyond the register-resident selection
+    assert both(moe.shape(32769, 64, 4, 1, 64, renorm=0, phi=1.0)) == \
+        (moe.MOE_ERR_UNSUPPORTED,) * 2
+    # the timed variant knows layouts 0..3 only
+    s = moe.shape(16, 64, 4, 2, 64, renorm=0, phi=1.0)
+    evs = (ctypes.c_void_p * 7)()
+    assert L.moe_layer_forward_timed(ctypes.byref(s), fake, fake, None, fake, fake, fake, None,
+                                     None, None, fake, ws, moe.workspace_bytes(s), None, evs,
+                                     4) == moe.MOE_ERR_INVALID_ARG
