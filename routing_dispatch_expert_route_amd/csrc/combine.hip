@@ -78,6 +78,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const void* __restrict__ y
                                                       long split_stride,
                                                       const int32_t* __restrict__ route_pos,
                                                       const float* __restrict__ gates,
+                                                      long s_tok, long s_slot,
                                                       const void* __restrict__ ysh, int T, int k,
                                                       int d, void* __restrict__ y) {
   constexpr int G = BF16 ? 8 : 4;  // output elements per 16-byte chunk
@@ -95,8 +96,9 @@ __global__ __launch_bounds__(256) void combine_kernel(const void* __restrict__ y
     float g[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      pos[j] = j0 + j < k ? route_pos[(size_t)t * k + j0 + j] : -1;
-      g[j] = j0 + j < k ? gates[(size_t)t * k + j0 + j] : 0.0f;
+      const size_t at = (size_t)t * s_tok + (size_t)(j0 + j) * s_slot;
+      pos[j] = j0 + j < k ? route_pos[at] : -1;
+      g[j] = j0 + j < k ? gates[at] : 0.0f;
     }
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
@@ -137,15 +139,16 @@ __global__ __launch_bounds__(256) void reduce_splits_kernel(const float* __restr
   }
 }
 
-hipError_t launch_combine(bool bf16, const void* y_packed, int splits, long split_stride,
-                          const int32_t* route_pos, const float* gates, const void* y_shared,
-                          int T, int k, int d, void* y, hipStream_t st) {
+static hipError_t combine_strided(bool bf16, const void* y_packed, int splits, long split_stride,
+                                  const int32_t* route_pos, const float* gates, long s_tok,
+                                  long s_slot, const void* y_shared, int T, int k, int d, void* y,
+                                  hipStream_t st) {
   if (T == 0) return hipSuccess;
   dim3 grid(ceil_div(T, 4), ceil_div(d, 64 * (bf16 ? 8 : 4))), block(256);
   const bool part = splits > 1;
 #define CB(B, P)                                                                           \
   hipLaunchKernelGGL((combine_kernel<B, P>), grid, block, 0, st, y_packed, splits, split_stride, \
-                     route_pos, gates, y_shared, T, k, d, y)
+                     route_pos, gates, s_tok, s_slot, y_shared, T, k, d, y)
   if (bf16) {
     if (part) CB(true, true);
     else CB(true, false);
@@ -155,6 +158,21 @@ hipError_t launch_combine(bool bf16, const void* y_packed, int splits, long spli
   }
 #undef CB
   return hipGetLastError();
+}
+
+hipError_t launch_combine(bool bf16, const void* y_packed, int splits, long split_stride,
+                          const int32_t* route_pos, const float* gates, const void* y_shared,
+                          int T, int k, int d, void* y, hipStream_t st) {
+  return combine_strided(bf16, y_packed, splits, split_stride, route_pos, gates, k, 1, y_shared,
+                         T, k, d, y, st);
+}
+
+hipError_t launch_combine_slot_major(bool bf16, const void* y_packed, int splits,
+                                     long split_stride, const int32_t* route_pos,
+                                     const float* gates, const void* y_shared, int T, int k,
+                                     int d, void* y, hipStream_t st) {
+  return combine_strided(bf16, y_packed, splits, split_stride, route_pos, gates, 1, T, y_shared,
+                         T, k, d, y, st);
 }
 
 hipError_t launch_reduce_splits(bool bf16, const float* parts, int splits, long split_stride,

@@ -38,13 +38,14 @@ hipError_t launch_padded(const void* x, const int32_t* ids, const int32_t* route
                          int T, int k, int E, int C, long row_bytes, int32_t* pad_pos,
                          void* x_pad, int32_t* offsets_pad, hipStream_t st);
 
-// Expert-choice routing from router logits [T][E]: scores [T][E] (softmax),
-// keys [E][T] scratch, route_pos [T][E] (row e*Ce + i or -1), row_token
-// [E*Ce] and offsets[e] = e*Ce.  Needs T <= 32768 and 1 <= Ce <= T (Ce = 0
-// when T = 0).
+// Expert-choice routing from router logits [T][E]: scores [T][E] (softmax;
+// may be null), keys [E][T] (the scores' bits, expert-major), pos_et [E][T]
+// (row e*Ce + i or -1), route_pos [T][E] (the same table token-major; may be
+// null), row_token [E*Ce] and offsets[e] = e*Ce.  Needs T <= 32768 and
+// 1 <= Ce <= T (Ce = 0 when T = 0).
 hipError_t launch_expert_choice(const float* logits, int T, int E, int Ce, float* scores,
-                                uint32_t* keys, int32_t* route_pos, int32_t* row_token,
-                                int32_t* offsets, hipStream_t st);
+                                uint32_t* keys, int32_t* pos_et, int32_t* route_pos,
+                                int32_t* row_token, int32_t* offsets, hipStream_t st);
 
 // Row groups of a grouped GEMM: device offsets[E+1] (never read on the
 // host), or one dense group of M_dense rows when offsets is null.
@@ -74,6 +75,12 @@ hipError_t launch_gemm_down(const GemmPlan& pl, const void* H, const void* Wd, i
 hipError_t launch_combine(bool bf16, const void* y_packed, int splits, long split_stride,
                           const int32_t* route_pos, const float* gates, const void* y_shared,
                           int T, int k, int d, void* y, hipStream_t st);
+// The same with the route table and gates expert-major ([k][T]: slot j of
+// token t at j*T + t), as expert choice writes them.
+hipError_t launch_combine_slot_major(bool bf16, const void* y_packed, int splits,
+                                     long split_stride, const int32_t* route_pos,
+                                     const float* gates, const void* y_shared, int T, int k,
+                                     int d, void* y, hipStream_t st);
 // y[p] = sum over planes of parts[s][p] for p < offsets[E] (or M_dense rows
 // when offsets is null), rounded once to dtype.
 hipError_t launch_reduce_splits(bool bf16, const float* parts, int splits, long split_stride,

@@ -67,7 +67,7 @@ int64_t rmax_of(const moe_shape* s, int64_t C) {
 
 struct Layout {
   size_t logits, ids, gates, cnt, counts, kept, offsets, route_pos, row_token, h, yp, part, hs,
-      ys, spart, shist, xpad, opad, ppos, ids2, slot, offs2, rpos0, pref, ecs, eck, ecp, ecoff;
+      ys, spart, shist, xpad, opad, ppos, ids2, slot, offs2, rpos0, pref, eck, ecp, ecoff;
   int splits;      // K splits of the routed down GEMM (fp32 partial planes when > 1)
   int splits_pad;  // the same for the fixed-shape [E, C] layout
   int splits_ec;   // the same for expert-choice rows
@@ -187,9 +187,8 @@ Layout layout_of(const moe_shape* s) {
   L.offs2 = take((size_t)(s->E + 1) * sizeof(int32_t));
   L.rpos0 = take(R * sizeof(int32_t));
   L.pref = take(R * 64);  // preference lists of the dropped routes (E <= 64)
-  // expert choice: scores, expert-major keys, route table [T][E], row groups
+  // expert choice: expert-major keys (score bits) and route table, row groups
   const size_t TE = (size_t)s->T * s->E;
-  L.ecs = take(TE * sizeof(float));
   L.eck = take(TE * sizeof(uint32_t));
   L.ecp = take(TE * sizeof(int32_t));
   L.ecoff = take((size_t)(s->E + 1) * sizeof(int32_t));
@@ -368,7 +367,8 @@ int moe_permute_expert_choice(const moe_shape* s, const void* x, const float* lo
   const int T = (int)s->T, E = (int)s->E;
   const int Ce = (int)ce_of(s);
   hipError_t e = moe::launch_expert_choice(logits, T, E, Ce, scores, at<uint32_t>(ws, L.eck),
-                                           route_pos, row_token, offsets, stream);
+                                           at<int32_t>(ws, L.ecp), route_pos, row_token, offsets,
+                                           stream);
   if (e != hipSuccess) return MOE_ERR_HIP;
   return hip_status(moe::launch_gather_rows(x, row_token, offsets, E, (long)E * Ce,
                                             s->d * elem_bytes(s), x_packed, stream));
@@ -437,14 +437,15 @@ int moe_routing_stats(const moe_shape* s, const float* logits, const float* gate
 // Expert GEMMs over the row groups of pl (activations A, gathered through
 // a_rows when non-null; a_nrows rows of A), the shared expert (on x), and the
 // combine over kslots slots per token (route table rpos, gates g, both
-// [T][kslots]).  splits: K splits of the down GEMM, whose fp32 planes hold
+// [T][kslots], or [kslots][T] when slot_major).  splits: K splits of the down GEMM, whose fp32 planes hold
 // `rows` rows each.  Records events 2..6 of the timed variant.
 static int experts_and_combine(const moe_shape* s, const Layout& L, const moe::GemmPlan& pl,
                                const void* x, const void* A, const int32_t* a_rows, long a_nrows,
                                const void* w_gate, const void* w_up, const void* w_down,
                                const void* ws_gate, const void* ws_up, const void* ws_down,
                                int splits, long rows, const int32_t* rpos, const float* g,
-                               int kslots, void* y, void* ws, hipStream_t stream, hipEvent_t* ev) {
+                               int kslots, bool slot_major, void* y, void* ws, hipStream_t stream,
+                               hipEvent_t* ev) {
   const bool bf16 = s->dtype == MOE_DTYPE_BF16;
   const int T = (int)s->T, d = (int)s->d, dff = (int)s->d_ff;
   void* h = at<void>(ws, L.h);
@@ -480,7 +481,10 @@ static int experts_and_combine(const moe_shape* s, const Layout& L, const moe::G
     ysh = ys;
   }
   mark(5);
-  e = moe::launch_combine(bf16, yrows, splits, stride, rpos, g, ysh, T, kslots, d, y, stream);
+  e = slot_major ? moe::launch_combine_slot_major(bf16, yrows, splits, stride, rpos, g, ysh, T,
+                                                  kslots, d, y, stream)
+                 : moe::launch_combine(bf16, yrows, splits, stride, rpos, g, ysh, T, kslots, d, y,
+                                       stream);
   if (e != hipSuccess) return MOE_ERR_HIP;
   mark(6);
   return MOE_OK;
@@ -541,20 +545,23 @@ static int layer_forward_impl(const moe_shape* s, const void* x, const void* w_r
   if (choice) {
     // expert choice: logits, each expert's top-Ce tokens, then the shared
     // GEMM, shared-expert and combine stages below with one slot per expert
+    // the route table stays expert-major inside; the callers' [T][E] copies
+    // of the scores and the table are written only when asked for
     const int Ce = (int)ce_of(s);
-    float* sc = gates ? gates : at<float>(ws, L.ecs);
-    int32_t* ecpos = route_pos ? route_pos : at<int32_t>(ws, L.ecp);
+    uint32_t* keys = at<uint32_t>(ws, L.eck);
+    int32_t* pos_et = at<int32_t>(ws, L.ecp);
     int32_t* ecoff = at<int32_t>(ws, L.ecoff);
     hipError_t e = moe::launch_route(bf16, x, w_router, b_router, T, d, E, k, 0,
                                      at<float>(ws, L.logits), nullptr, nullptr, stream);
     if (e != hipSuccess) return MOE_ERR_HIP;
     mark(1);
-    e = moe::launch_expert_choice(at<float>(ws, L.logits), T, E, Ce, sc, at<uint32_t>(ws, L.eck),
-                                  ecpos, row_token, ecoff, stream);
+    e = moe::launch_expert_choice(at<float>(ws, L.logits), T, E, Ce, gates, keys, pos_et,
+                                  route_pos, row_token, ecoff, stream);
     if (e != hipSuccess) return MOE_ERR_HIP;
+    // gates: the score bits in the keys, read as floats, expert-major
     return experts_and_combine(s, L, choice_plan(s, ecoff), x, x, row_token, T, w_gate, w_up,
-                               w_down, ws_gate, ws_up, ws_down, L.splits_ec, (long)E * Ce, ecpos,
-                               sc, E, y, ws, stream, ev);
+                               w_down, ws_gate, ws_up, ws_down, L.splits_ec, (long)E * Ce, pos_et,
+                               reinterpret_cast<const float*>(keys), E, true, y, ws, stream, ev);
   }
   hipError_t e = moe::launch_route(bf16, x, w_router, b_router, T, d, E, k, s->renormalize,
                                    at<float>(ws, L.logits), ids, g, stream);
@@ -585,9 +592,9 @@ static int layer_forward_impl(const moe_shape* s, const void* x, const void* w_r
   if (padded)
     return experts_and_combine(s, L, pl, x, at<void>(ws, L.xpad), nullptr, Rpad, w_gate, w_up,
                                w_down, ws_gate, ws_up, ws_down, L.splits_pad, Rpad, ppos, g, k,
-                               y, ws, stream, ev);
+                               false, y, ws, stream, ev);
   return experts_and_combine(s, L, pl, x, x, row_token, T, w_gate, w_up, w_down, ws_gate, ws_up,
-                             ws_down, L.splits, Rmax, rpos, g, k, y, ws, stream, ev);
+                             ws_down, L.splits, Rmax, rpos, g, k, false, y, ws, stream, ev);
 }
 
 int moe_layer_forward(const moe_shape* s, const void* x, const void* w_router,
