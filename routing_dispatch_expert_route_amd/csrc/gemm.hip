@@ -569,12 +569,17 @@ static long row_tile_bound(const GemmPlan& pl, int BM) {
 //   L  256-row tiles, one workgroup per CU: best when K is long and every
 //      group has many rows (the K loop amortises the pipeline fill);
 //   M  128-row tiles, two per CU: the default;
+//   N  (gate/up only) 128-row tiles of 64 output columns with 64-wide K
+//      stages: every row segment a load fetches is a whole 128-byte line
+//      (32-wide stages fetch half lines, which the memory system serves at
+//      about two thirds of the rate); worth its extra activation re-reads
+//      up to about two rounds of M tiles;
 //   S  64-row tiles: fewer idle slots in the last round for small problems
 //      (the down projection below about two rounds of 128-row tiles, the
 //      gate/up projection only for a few hundred rows in all).
 // Tile counts are estimated from the row bound (each group wastes half a
 // tile on average).
-enum TileCfg { TILE_L, TILE_M, TILE_S };
+enum TileCfg { TILE_L, TILE_M, TILE_N, TILE_S };
 static long est_tiles(const GemmPlan& pl, int bm, int bno, int N) {
   const long mt = pl.grouped ? pl.R_max / bm + (pl.E + 1) / 2 : (pl.M_dense + bm - 1) / bm;
   return mt * ((N + bno - 1) / bno);
@@ -585,10 +590,12 @@ static TileCfg tile_cfg(const GemmPlan& pl, int N, int K, bool swiglu) {
   if (K >= 2048 && per_group >= 1024 && est_tiles(pl, 256, bno, N) >= 256) return TILE_L;
   // GEMM 1 keeps 128-row tiles unless the rows are very few (decode); the
   // down projection takes 64-row tiles below about two rounds
-  if (est_tiles(pl, 128, bno, N) > (swiglu ? 256 : 1024)) return TILE_M;
-  return TILE_S;
+  const long est_m = est_tiles(pl, 128, bno, N);
+  if (!swiglu) return est_m > 1024 ? TILE_M : TILE_S;
+  if (est_m > 1024) return TILE_M;
+  return est_m > 256 ? TILE_N : TILE_S;
 }
-static int cfg_bm(TileCfg c) { return c == TILE_L ? 256 : c == TILE_M ? 128 : 64; }
+static int cfg_bm(TileCfg c) { return c == TILE_L ? 256 : (c == TILE_M || c == TILE_N) ? 128 : 64; }
 
 template <int BM, int BNW, int WM, int WN, int BK, int NSX, int NSW, int OCC, bool SWIGLU,
           bool PARTIAL>
@@ -613,6 +620,9 @@ static hipError_t run_cfg(const GemmPlan& pl, GemmArgs a, hipStream_t st) {
   switch (tile_cfg(pl, a.N, a.K, SWIGLU)) {
     case TILE_L: return run_bf16<256, 256, 2, 2, 64, 2, 3, 1, SWIGLU, PARTIAL>(pl, a, st);
     case TILE_M: return run_bf16<128, 256, 2, 2, 32, 3, 3, 2, SWIGLU, PARTIAL>(pl, a, st);
+    case TILE_N:
+      if constexpr (SWIGLU) return run_bf16<128, 128, 2, 2, 64, 2, 3, 2, SWIGLU, PARTIAL>(pl, a, st);
+      else return hipErrorInvalidValue;  // gate/up only
     default:
       // a long K loop per tile wants the deeper ring; short ones two
       // workgroups per CU
