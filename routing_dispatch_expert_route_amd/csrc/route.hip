@@ -17,10 +17,21 @@
 //   topk_gates_kernel  one lane per token over an LDS copy of its logits:
 //       a single insertion pass keeps the k best by (logit desc, index asc),
 //       then the gates.
+#include <type_traits>
+
 #include "common.h"
 #include "launch.h"
 
 namespace moe {
+
+// Calls f(integral_constant<int, I>) for I = B .. E-1 (compile-time unrolled).
+template <int B, int E, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (B < E) {
+    f(std::integral_constant<int, B>{});
+    static_for<B + 1, E>(f);
+  }
+}
 
 // Router logits.  Block = 64 tokens x (4 * EPW) experts; lane = token, wave
 // w owns experts e0 + w*EPW + j.  The hidden dimension advances in chunks of
@@ -101,24 +112,57 @@ __global__ __launch_bounds__(256) void router_logits_kernel(
 #pragma unroll
   for (int j = 0; j < EPW; ++j) acc[j] = 0.0f;
   const float* xr = sx + lane * XS;
-  auto chain4 = [&](int kk) {
-    const f32x4_t xv = *reinterpret_cast<const f32x4_t*>(xr + kk);
+  // One k step = 4 hidden indices: this lane's x values and each expert's
+  // W values, then 4 FMAs per chain in increasing index.
+  struct Step {
+    f32x4_t x;
+    f32x4_t w[EPW];
+  };
+  auto read_step = [&](int kk, Step& q) {
+    q.x = *reinterpret_cast<const f32x4_t*>(xr + kk);
+#pragma unroll
+    for (int j = 0; j < EPW; ++j)
+      q.w[j] = *reinterpret_cast<const f32x4_t*>(sw + (wave * EPW + j) * RKC + kk);
+  };
+  auto fma_step = [&](const Step& q) {
 #pragma unroll
     for (int j = 0; j < EPW; ++j) {
-      const f32x4_t wv = *reinterpret_cast<const f32x4_t*>(sw + (wave * EPW + j) * RKC + kk);
-      acc[j] = __builtin_fmaf(xv[0], wv[0], acc[j]);
-      acc[j] = __builtin_fmaf(xv[1], wv[1], acc[j]);
-      acc[j] = __builtin_fmaf(xv[2], wv[2], acc[j]);
-      acc[j] = __builtin_fmaf(xv[3], wv[3], acc[j]);
+      acc[j] = __builtin_fmaf(q.x[0], q.w[j][0], acc[j]);
+      acc[j] = __builtin_fmaf(q.x[1], q.w[j][1], acc[j]);
+      acc[j] = __builtin_fmaf(q.x[2], q.w[j][2], acc[j]);
+      acc[j] = __builtin_fmaf(q.x[3], q.w[j][3], acc[j]);
     }
+  };
+  // A full chunk: the LDS reads run P steps ahead of the FMAs (a ring of P
+  // register sets), so their latency hides behind (P-1) steps of FMAs even
+  // with one or two waves per SIMD; the schedule keeps each step's FMAs
+  // before the refill it allows.
+  constexpr int P = EPW == 4 ? 3 : 8 / EPW;
+  constexpr int NSTEP = RKC / 4;
+  static_assert(P <= NSTEP, "read-ahead within a chunk");
+  auto consume_full = [&]() {
+    Step q[P];
+    static_for<0, P>([&](auto i) { read_step(decltype(i)::value * 4, q[decltype(i)::value]); });
+    static_for<0, NSTEP>([&](auto si) {
+      constexpr int st = decltype(si)::value;
+      fma_step(q[st % P]);
+      if constexpr (st + P < NSTEP) {
+        read_step((st + P) * 4, q[st % P]);
+        __builtin_amdgcn_sched_group_barrier(0x002, 4 * EPW, 0);  // the FMAs
+        __builtin_amdgcn_sched_group_barrier(0x100, 1 + EPW, 0);  // then the refill
+      }
+    });
   };
   auto consume = [&](int k0) {
     const int kc = min(RKC, d - k0);  // a multiple of 8
     if (kc == RKC) {
-#pragma unroll 8
-      for (int kk = 0; kk < RKC; kk += 4) chain4(kk);
+      consume_full();
     } else {
-      for (int kk = 0; kk < kc; kk += 4) chain4(kk);
+      for (int kk = 0; kk < kc; kk += 4) {
+        Step q;
+        read_step(kk, q);
+        fma_step(q);
+      }
     }
   };
   const int nc = (d + RKC - 1) / RKC;
