@@ -70,6 +70,29 @@ def gemm1_model(w, kept_rows, active_experts):
     return flops, byts
 
 
+def layer_model(w, kept_rows, active_experts):
+    """Algorithmic flops and bytes of the whole layer ("Measurement"):
+    F = kept*6*d*d_ff + T*6*d*d_ffs + 2*T*d*E (kept routes only, no padding);
+    B = active experts' weights + the shared expert's + router weights + x
+    read + y written + 12 bytes of route metadata per route."""
+    eb = 2 if w.dtype == "bf16" else 4
+    flops = (kept_rows * 6.0 * w.d * w.d_ff + w.T * 6.0 * w.d * w.d_ff_shared
+             + 2.0 * w.T * w.d * w.E)
+    byts = (active_experts * 3.0 * w.d * w.d_ff * eb + 3.0 * w.d * w.d_ff_shared * eb
+            + w.E * w.d * eb + 2.0 * w.T * w.d * eb + w.T * w.k * 12.0)
+    return flops, byts
+
+
+def _cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
 GEMM_SRC = os.path.join(ROOT, "routing_dispatch_expert_route_amd", "csrc", "gemm.hip")
 N_CAL = 3  # calibration copies at the end of a --copy-calibration run
 
@@ -172,7 +195,7 @@ def cpu_baseline(w, inp, seconds, choice=False):
             f"first {n} of {w.T} tokens of {w.name} (routing of all {w.T} tokens, "
             f"expert FFN + combine of the {n})")
     return {"value": n * reps / t, "unit": "tokens/s", "cores": cores, "kind": "oracle",
-            "sample": f"{what}, {t:.1f} s wall"}
+            "sample": f"{what}, {t:.1f} s wall", "cpu_model": _cpu_model()}
 
 
 def main():
@@ -301,6 +324,8 @@ def main():
 
     # per-stage times: a second pass with every stage boundary marked
     stages = None
+    step_pct = None
+    warm_ms = None
     if not args.no_stages:
         evs = new_events(K * 7)
         torch.cuda.synchronize()
@@ -313,12 +338,34 @@ def main():
                                     choice=args.choice)
         torch.cuda.synchronize()
         acc = [0.0] * 6
+        per_step = []
         for i in range(K):
             for j in range(6):
                 acc[j] += elapsed_us(evs[7 * i + j], evs[7 * i + j + 1])
+            per_step.append(elapsed_us(evs[7 * i], evs[7 * i + 6]))
         for e in evs:
             hip.hipEventDestroy(e)
         stages = {n: round(a / K, 2) for n, a in zip(STAGES, acc)}
+        per_step.sort()
+
+        def pct(q):
+            return round(per_step[min(len(per_step) - 1, int(q * len(per_step)))], 2)
+
+        step_pct = {"p10": pct(0.1), "p50": pct(0.5), "p90": pct(0.9)}
+
+        # warm caches: the same K steps on one weight set (MALL-resident
+        # when the weights fit), labelled as such
+        torch.cuda.synchronize()
+        tw0 = time.perf_counter()
+        for i in range(K):
+            p = sets[0]
+            moe.layer_forward_timed(s, p["x"], p["w_router"], p["b_router"], p["w_gate"],
+                                    p["w_up"], p["w_down"], p["ws_gate"], p["ws_up"],
+                                    p["ws_down"], y, ws, [None] * 7, stream=stream,
+                                    padded=args.padded, reroute=args.reroute,
+                                    choice=args.choice)
+        torch.cuda.synchronize()
+        warm_ms = (time.perf_counter() - tw0) * 1e3 / K
 
     # forward-only routing statistics of the bench batch: one extra pass over
     # the route outputs (router logits requested from moe_route)
@@ -377,6 +424,18 @@ def main():
         roof["traffic"] = (None if (args.padded or args.reroute or args.choice)
                            else traffic_from_profile(w.name))
 
+    layer_roof = None
+    if ms > 0:
+        lf, lb = layer_model(w, kept_rows, active)
+        peak_c = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_F32_TFLOPS
+        t = ms * 1e-3
+        fm = lf / t / (peak_c * 1e12)
+        fh = lb / t / (PEAK_HBM_GBS * 1e9)
+        layer_roof = {"algorithmic_flops": lf, "algorithmic_bytes": lb,
+                      "tflops": round(lf / t / 1e12, 1), "gbs": round(lb / t / 1e9, 1),
+                      "frac_mfma": round(fm, 4), "frac_hbm": round(fh, 4),
+                      "frac": round(max(fm, fh), 4)}
+
     cpu = None
     if not args.no_cpu:
         cpu = cpu_baseline(w, inp, args.cpu_seconds, choice=args.choice)
@@ -401,8 +460,14 @@ def main():
                    "overflow": "reroute" if args.reroute else "drop",
                    "routing": "expert choice" if args.choice else "token choice (top-k)",
                    "padded_rows": (w.E * C) if (args.padded and C > 0) else None,
+                   "capacity": C if C >= 0 else None,
+                   "dropped_routes": (w.T * w.k - kept_rows) if not args.choice else None,
+                   "fill": round(kept_rows / (w.E * C), 4) if C > 0 else None,
                    "parallelism": "single GPU"},
         "roofline": roof,
+        "layer_roofline": layer_roof,
+        "step_us_percentiles": step_pct,
+        "warm_ms_per_step": round(warm_ms, 5) if warm_ms else None,
         "cpu_baseline": cpu,
         "stages_us": stages,
         "routing_stats": rstats,

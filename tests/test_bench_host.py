@@ -68,3 +68,19 @@ def test_multi_gpu_refused():
                        text=True, timeout=120)
     assert r.returncode != 0
     assert "one GPU" in r.stderr
+
+
+def test_layer_model_matches_the_work_table():
+    # Mixtral decode: T=16, E=8, k=2, d=4096, d_ff=14336, bf16, all 32 routes
+    # kept on all 8 experts -> F = 11.3 GFLOP, B = 2.82 GB (the measurement
+    # table's algorithmic work: kept routes, active experts' weights)
+    from workloads import WORKLOADS
+    w = WORKLOADS["mixtral_decode"]
+    f, b = bench.layer_model(w, kept_rows=32, active_experts=8)
+    assert f == pytest.approx(32 * 6 * 4096 * 14336 + 2 * 16 * 4096 * 8)
+    assert f == pytest.approx(11.27e9, rel=1e-3)
+    assert b == pytest.approx(2.818e9, rel=1e-3)
+    # Granite T=16384 dropless: F = 413 GFLOP
+    g = WORKLOADS["granite_16384"]
+    f2, _ = bench.layer_model(g, kept_rows=16384 * 8, active_experts=32)
+    assert f2 == pytest.approx(413e9, rel=2e-3)
