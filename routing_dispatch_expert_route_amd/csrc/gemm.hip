@@ -138,7 +138,7 @@ __device__ __forceinline__ bool tile_of_block(const GemmArgs& a, int m_real, int
 }
 
 // ---------------------------------------------------------------------------
-// bf16 MFMA kernel, 256 threads = WM x WN waves.
+// bf16 MFMA kernel, WM x WN waves (four or eight).
 //
 // Operand roles.  The MFMA A operand is the weight tile (rows n), the B
 // operand the activation tile (rows m), so the accumulator holds D[n][m]:
@@ -146,22 +146,23 @@ __device__ __forceinline__ bool tile_of_block(const GemmArgs& a, int m_real, int
 // 4*(l/32) + v%4 -- four consecutive output columns of one token row per
 // group of four accumulator registers, written as one 8-byte store.
 //
-// Pipeline.  K advances in stages of BK = 32 through a ring of four LDS
-// stages filled by direct buffer->LDS loads (buffer_load_dwordx4 ... lds:
-// each wave-level load writes 1 KB = 16 rows of 64 bytes; no staging
-// registers; the K position is the scalar offset, so a lane's vector
-// offset never changes).  Three stages are in flight while one feeds the
-// MFMAs; a stage costs one s_waitcnt on the wave's own loads and one
-// workgroup barrier.  Each ring slot is its own LDS object and every access
-// names its slot statically (switch on kt % 4), so the compiler can tell a
-// load into one slot from a read of another and inserts no extra waits.
+// Pipeline.  K advances in stages of BK (32 or 64) through two LDS rings,
+// NSX slots for the activation tile and NSW >= NSX for the weight tile
+// (the weights, first touched in HBM, are fetched further ahead), filled by
+// direct buffer->LDS loads (buffer_load_dwordx4 ... lds: each wave-level load
+// writes 1 KB; no staging registers; the K position is the scalar offset, so
+// a lane's vector offset never changes).  A stage costs one counted
+// s_waitcnt on the wave's own loads and one workgroup barrier.  Each ring
+// slot is its own LDS object and the loop body is unrolled over every
+// combination of slots, so every access names its slot statically and the
+// compiler inserts no extra waits.  MFMA fragments are double-buffered in
+// registers and the schedule interleaves LDS reads, MFMAs and refills.
 //
-// LDS layout.  A row holds 4 chunks of 16 bytes; logical chunk c of row r
-// sits at c ^ f(r), f(r) = ((r >> 1) ^ (r >> 3)) & 3: the 8 or 16 lanes that
-// read one chunk column of consecutive rows visit distinct bank groups
-// whether the LDS has 32 or 64 four-byte banks.
+// LDS layout.  Logical 16-byte chunk c of row r sits at c ^ f(r) (swz<CH>),
+// so the lanes that read one chunk column of consecutive rows visit
+// distinct bank groups.
 //
-// K tail (K not a multiple of 32): a chunk past the end gets a vector
+// K tail (K not a multiple of BK): a chunk past the end gets a vector
 // offset beyond the buffer, which the buffer unit returns as zero.
 //
 // SWIGLU: the weight tile stacks BNW/2 gate rows over the matching BNW/2 up
@@ -202,7 +203,7 @@ constexpr int kBufFlags = 0x00020000;  // raw buffer, 32-bit data format
 
 template <int BM, int BNW, int WM, int WN, int BK, int NSX, int NSW, int OCC, bool SWIGLU,
           bool GATHER, bool PARTIAL>
-__global__ __launch_bounds__(256, OCC) void gemm_bf16_kernel(GemmArgs a) {
+__global__ __launch_bounds__(64 * WM * WN, OCC) void gemm_bf16_kernel(GemmArgs a) {
 #if defined(__HIP_DEVICE_COMPILE__)  // the host pass only emits the launch stub
   // BK: K elements per stage (32 or 64); NSX / NSW: ring slots of the
   // activation / weight tiles (2 to 4 each, NSW >= NSX: the weights, first
@@ -214,12 +215,13 @@ __global__ __launch_bounds__(256, OCC) void gemm_bf16_kernel(GemmArgs a) {
   constexpr int BNO = BNW / NREG;  // output columns per block
   constexpr int WTM = BM / WM, WTN = BNO / WN;
   constexpr int TM = WTM / 32, TN = WTN / 32;
-  constexpr int XS = BM / RPS / 4;   // activation loads per wave per stage
-  constexpr int WS = BNW / RPS / 4;  // weight loads per wave per stage
+  constexpr int NWV = WM * WN;          // waves per workgroup
+  constexpr int XS = BM / RPS / NWV;   // activation loads per wave per stage
+  constexpr int WS = BNW / RPS / NWV;  // weight loads per wave per stage
   constexpr int PER = XS + WS;
   constexpr int XSTAGE = BM * CH;   // 16-byte units per activation stage
   constexpr int WSTAGE = BNW * CH;  // 16-byte units per weight stage
-  static_assert(WM * WN == 4, "four waves");
+  static_assert(NWV == 4 || NWV == 8, "four or eight waves");
   static_assert(TM >= 1 && TN >= 1 && XS >= 1 && WS >= 1, "tile shape");
   static_assert(!(SWIGLU && PARTIAL), "SwiGLU needs the full K sum");
   static_assert(XS * (NSX - 1) + WS * (NSW - 1) < 64, "vmcnt range");
@@ -566,8 +568,10 @@ static long row_tile_bound(const GemmPlan& pl, int BM) {
 
 // Tile shape, from the shape alone (the routing is not known on the host;
 // the row counts are bounded by R_max).  Measured on MI355X:
-//   L  256-row tiles, one workgroup per CU: best when K is long and every
-//      group has many rows (the K loop amortises the pipeline fill);
+//   L  256-row tiles, one workgroup of eight waves per CU (two per SIMD,
+//      so one wave's waits overlap the other's MFMAs): best when K is long
+//      and every group has many rows (the K loop amortises the pipeline
+//      fill); the gate/up projection already from K = 1024;
 //   M  128-row tiles, two per CU: the default;
 //   N  (gate/up only) 128-row tiles of 64 output columns with 64-wide K
 //      stages: every row segment a load fetches is a whole 128-byte line
@@ -587,7 +591,8 @@ static long est_tiles(const GemmPlan& pl, int bm, int bno, int N) {
 static TileCfg tile_cfg(const GemmPlan& pl, int N, int K, bool swiglu) {
   const int bno = swiglu ? 128 : 256;
   const long per_group = pl.grouped ? pl.R_max / (pl.E > 0 ? pl.E : 1) : pl.M_dense;
-  if (K >= 2048 && per_group >= 1024 && est_tiles(pl, 256, bno, N) >= 256) return TILE_L;
+  if (K >= (swiglu ? 1024 : 2048) && per_group >= 1024 && est_tiles(pl, 256, bno, N) >= 256)
+    return TILE_L;
   // GEMM 1 keeps 128-row tiles unless the rows are very few (decode); the
   // down projection takes 64-row tiles below about two rounds
   const long est_m = est_tiles(pl, 128, bno, N);
@@ -615,17 +620,17 @@ static hipError_t run_bf16(const GemmPlan& pl, GemmArgs a, hipStream_t st) {
   if (blocks == 0) return hipSuccess;
   if (a.a_rows)
     hipLaunchKernelGGL((gemm_bf16_kernel<BM, BNW, WM, WN, BK, NSX, NSW, OCC, SWIGLU, true, PARTIAL>),
-                       dim3((unsigned)blocks), dim3(256), 0, st, a);
+                       dim3((unsigned)blocks), dim3(64 * WM * WN), 0, st, a);
   else
     hipLaunchKernelGGL((gemm_bf16_kernel<BM, BNW, WM, WN, BK, NSX, NSW, OCC, SWIGLU, false, PARTIAL>),
-                       dim3((unsigned)blocks), dim3(256), 0, st, a);
+                       dim3((unsigned)blocks), dim3(64 * WM * WN), 0, st, a);
   return hipGetLastError();
 }
 
 template <bool SWIGLU, bool PARTIAL>
 static hipError_t run_cfg(const GemmPlan& pl, GemmArgs a, hipStream_t st) {
   switch (tile_cfg(pl, a.N, a.K, SWIGLU)) {
-    case TILE_L: return run_bf16<256, 256, 2, 2, 64, 2, 3, 1, SWIGLU, PARTIAL>(pl, a, st);
+    case TILE_L: return run_bf16<256, 256, 4, 2, 64, 2, 3, 1, SWIGLU, PARTIAL>(pl, a, st);
     case TILE_M: return run_bf16<128, 256, 2, 2, 32, 3, 3, 2, SWIGLU, PARTIAL>(pl, a, st);
     case TILE_N:
       if constexpr (SWIGLU) return run_bf16<128, 128, 2, 2, 64, 2, 3, 2, SWIGLU, PARTIAL>(pl, a, st);

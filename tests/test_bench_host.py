@@ -12,7 +12,7 @@ import bench
 FIELDS = ["Dispatch_Id", "Kernel_Name", "Counter_Name", "Counter_Value"]
 G1 = "void moe::gemm_bf16_kernel<128, 256, 2, 2, 32, 3, 3, 2, true, true, false>(moe::GemmArgs)"
 G2 = "void moe::gemm_bf16_kernel<64, 256, 1, 4, 64, 2, 2, 2, false, false, true>(moe::GemmArgs)"
-SHARED1 = "void moe::gemm_bf16_kernel<256, 256, 2, 2, 64, 2, 3, 1, true, false, false>(moe::GemmArgs)"
+SHARED1 = "void moe::gemm_bf16_kernel<256, 256, 4, 2, 64, 2, 3, 1, true, false, false>(moe::GemmArgs)"
 COPY = "__amd_rocclr_copyBuffer"
 
 
