@@ -334,6 +334,30 @@ def test_layer_forward_edge_cases(moe, name):
     _layer_check(moe, w, make_inputs(w, seed=11))
 
 
+# Shapes that land on each grouped-GEMM tile with K tails (K not a multiple
+# of the tile's K stage) and ragged output widths; the tile each one takes
+# follows from the host heuristic in gemm.hip (shape only).
+TILES = {
+    # GEMM 1: 128x64-output tile (64-wide stages, K = 712 = 11*64 + 8); GEMM 2:
+    # the narrow 64x128 down tile (N = 712, K = 3000) split into fp32 planes
+    "narrow_tiles": Workload("narrow_tiles", T=2000, E=4, k=2, d=712, d_ff=3000, phi=1.1),
+    # GEMM 1: 128x256 tile with 32-wide stages (K = 776 = 24*32 + 8)
+    "m_tile_k_tail": Workload("m_tile_k_tail", T=8192, E=4, k=2, d=776, d_ff=1032),
+    # GEMM 1: eight-wave 256-row tile (K = 1032, N = 2056 ragged); GEMM 2: 64x256
+    "l_tile_gate_up": Workload("l_tile_gate_up", T=4096, E=2, k=1, d=1032, d_ff=2056,
+                               renorm=0, bias="normal"),
+    # both GEMMs on the eight-wave 256-row tile with K tails (4104, 2056)
+    "l_tile_both": Workload("l_tile_both", T=8192, E=2, k=1, d=4104, d_ff=2056, renorm=0),
+}
+
+
+@pytest.mark.parametrize("name", list(TILES))
+def test_layer_forward_tile_paths(moe, name):
+    w = TILES[name]
+    say(f"[layer tile path] {name}")
+    _layer_check(moe, w, make_inputs(w, seed=13), n_random=48)
+
+
 def test_forced_hot_expert_reaches_E_over_k(moe):
     say("[layer hot expert]")
     w = Workload("hot", T=512, E=32, k=8, d=64, d_ff=32, bias="normal")
