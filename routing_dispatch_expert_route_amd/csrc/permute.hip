@@ -494,6 +494,234 @@ __global__ __launch_bounds__(256) void reroute_rows_kernel(const int32_t* __rest
   row_token[p] = r / k;
 }
 
+// Top-1 routing (k = 1) in parallel.  A token then holds no other expert, so
+// the greedy above is a serial dictatorship: the dropped routes choose in
+// arrival order, and every expert in effect ranks routes by that one order.
+// When all experts share one priority order, deferred acceptance with the
+// routes proposing ends in exactly the assignment of the serial dictatorship
+// in that order, and each of its rounds is parallel: every unplaced route
+// proposes to its next preferred expert among those with a free seat after
+// the drop policy, each expert keeps the earliest routes it holds or was
+// proposed, up to its free seats, and rejects the rest, and the rejected
+// routes move one rank on.  It ends after a round without proposals (each
+// proposal moves a route's rank or places it, so that round comes).  Seats
+// follow arrival order among an expert's accepted routes, as in the walk.
+// One block of 1024 threads; the state sits in dynamic LDS, sized for R
+// routes (the bound on the dropped ones), W = ceil(R / 32):
+//   held  [E][W] uint32   bit j: dropped route j is held by / proposed to e
+//   drop  [R] uint16      route index of dropped route j (arrival order)
+//   pref  [R][E] uint8    expert at each preference rank of route j, or
+//                         kNoExpert where that expert had no free seat (after
+//                         the rounds the area holds [E][W] int seat prefixes)
+//   next  [R] uint8       next rank route j tries
+//   cur   [R] uint8       expert route j is proposed to or held by, or kNoExpert
+constexpr int kDaThreads = 1024;
+constexpr int kDaWaves = kDaThreads / kWave;
+constexpr uint8_t kNoExpert = 0xFF;
+constexpr long kDaMaxLds = 60L * 1024;  // with the static arrays, under 64 KB
+constexpr int kDaMaxR = 65535;          // route indices fit uint16
+
+struct DaLayout {
+  long held, drop, pref, next, cur, bytes;
+};
+__host__ __device__ inline DaLayout da_layout(int R, int E) {
+  const long W = (R + 31) / 32;
+  DaLayout L;
+  L.held = 0;
+  L.drop = (long)E * W * 4;
+  L.pref = L.drop + ((2L * R + 3) & ~3L);
+  const long pref_bytes = (long)R * E > (long)E * W * 4 ? (long)R * E : (long)E * W * 4;
+  L.next = L.pref + ((pref_bytes + 3) & ~3L);
+  L.cur = L.next + R;
+  L.bytes = L.cur + R;
+  return L;
+}
+
+__global__ __launch_bounds__(kDaThreads) void reroute_da_kernel(
+    const uint8_t* __restrict__ rank, const int32_t* __restrict__ ids_in,
+    const int32_t* __restrict__ route_pos0, const int32_t* __restrict__ offsets0,
+    const int32_t* __restrict__ kept, int R, int E, int C, int32_t* __restrict__ ids_out,
+    int32_t* __restrict__ slot, int32_t* __restrict__ offsets) {
+  extern __shared__ __attribute__((aligned(16))) uint32_t s_dyn[];
+  __shared__ int s_kept[kRerouteMaxE], s_free[kRerouteMaxE], s_new[kRerouteMaxE],
+      s_fill[kRerouteMaxE];
+  __shared__ int s_wsum[kDaWaves];
+  const int tid = threadIdx.x, lane = tid & (kWave - 1);
+  const int wv = __builtin_amdgcn_readfirstlane(tid / kWave);
+  const int W = (R + 31) / 32;
+  const DaLayout L = da_layout(R, E);
+  uint8_t* base = reinterpret_cast<uint8_t*>(s_dyn);
+  uint32_t* held = reinterpret_cast<uint32_t*>(base + L.held);
+  uint16_t* drop = reinterpret_cast<uint16_t*>(base + L.drop);
+  uint8_t* pref = base + L.pref;
+  uint8_t* next = base + L.next;
+  uint8_t* cur = base + L.cur;
+
+  if (tid < E) {
+    const int kp = kept[tid];
+    s_kept[tid] = kp;
+    s_free[tid] = C > kp ? C - kp : 0;
+    s_new[tid] = 0;
+  }
+  for (int i = tid; i < E * W; i += kDaThreads) held[i] = 0;
+
+  // dropped routes in arrival order (each thread a run of cpt routes; block
+  // scan of the run counts); kept routes keep expert and seat
+  const int cpt = (R + kDaThreads - 1) / kDaThreads;  // <= 64
+  const int r0 = tid * cpt, r1 = min(R, r0 + cpt);
+  int nd = 0;
+  uint64_t dmask = 0;
+  for (int r = r0; r < r1; ++r) {
+    const int p = route_pos0[r];
+    if (p < 0) {
+      dmask |= 1ull << (r - r0);
+      ++nd;
+    } else {
+      const int e = ids_in[r];
+      ids_out[r] = e;
+      slot[r] = p - offsets0[e];
+    }
+  }
+  const int incl = wave_incl_scan(nd, lane);
+  if (lane == kWave - 1) s_wsum[wv] = incl;
+  __syncthreads();
+  int at = incl - nd, rd = 0;
+  for (int w = 0; w < kDaWaves; ++w) {
+    const int s = s_wsum[w];
+    at += w < wv ? s : 0;
+    rd += s;
+  }
+  const int Rd = __builtin_amdgcn_readfirstlane(rd);
+  while (dmask) {
+    drop[at++] = (uint16_t)(r0 + __builtin_ctzll(dmask));
+    dmask &= dmask - 1;
+  }
+  __syncthreads();
+
+  // preference lists: pref[j][rank of e] = e when e has a free seat
+  for (int i = tid; i < Rd * E; i += kDaThreads) {
+    const int j = i / E, e = i - j * E;
+    const int rk = rank[(size_t)drop[j] * kRerouteMaxE + e];
+    pref[j * E + rk] = s_free[e] > 0 ? (uint8_t)e : kNoExpert;
+  }
+  for (int j = tid; j < Rd; j += kDaThreads) {
+    next[j] = 0;
+    cur[j] = kNoExpert;
+  }
+  __syncthreads();
+
+  // The round loop keeps every branch around its barriers wave-uniform: the
+  // per-route loops run the same trip count on every lane (a lane past Rd
+  // idles in the body), and the exit reads the block-wide OR as a scalar.
+  // With a per-lane loop bound (j = tid; j < Rd) the compiler may route the
+  // lanes that have no route straight from one round's barriers to the
+  // next's, and a wave holding both kinds of lane then meets the barriers
+  // out of step with the others.
+  for (;;) {
+    // proposals of the unplaced routes
+    int proposed = 0;
+    for (int j0 = 0; j0 < Rd; j0 += kDaThreads) {
+      const int j = j0 + tid;
+      if (j >= Rd || cur[j] != kNoExpert) continue;
+      const uint8_t* pj = pref + j * E;
+      int p = next[j];
+      while (p < E && pj[p] == kNoExpert) ++p;
+      next[j] = (uint8_t)p;
+      if (p < E) {
+        const int e = pj[p];
+        atomicOr(&held[e * W + (j >> 5)], 1u << (j & 31));
+        cur[j] = (uint8_t)e;
+        s_new[e] = 1;
+        proposed = 1;
+      }
+    }
+    if (!__builtin_amdgcn_readfirstlane(__syncthreads_or(proposed))) break;
+    // each expert with proposals keeps its earliest s_free[e] routes; lane i
+    // of the expert's wave owns words [i*wpl, (i+1)*wpl)
+    const int wpl = (W + kWave - 1) / kWave;
+    for (int e = wv; e < E; e += kDaWaves) {
+      if (!__builtin_amdgcn_readfirstlane(s_new[e])) continue;
+      uint32_t* row = held + e * W;
+      const int cap = s_free[e];
+      const int w0 = lane * wpl, w1 = min(W, w0 + wpl);
+      int c = 0;
+      for (int w = w0; w < w1; ++w) c += __popc(row[w]);
+      const int inc = wave_incl_scan(c, lane);
+      if (__shfl(inc, kWave - 1, kWave) > cap) {
+        int before = inc - c;
+        for (int w = w0; w < w1; ++w) {
+          uint32_t v = row[w];
+          const int pc = __popc(v);
+          if (before >= cap) {
+            v = 0;
+          } else if (before + pc > cap) {  // keep the lowest cap - before bits
+            uint32_t keep = 0;
+            for (int q = cap - before; q > 0; --q) {
+              const uint32_t low = v & (0u - v);
+              keep |= low;
+              v ^= low;
+            }
+            v = keep;
+          }
+          if (before + pc > cap) row[w] = v;
+          before += pc;
+        }
+      }
+      if (lane == 0) s_new[e] = 0;
+    }
+    __syncthreads();
+    // rejected routes (their bit cleared) move one rank on
+    for (int j0 = 0; j0 < Rd; j0 += kDaThreads) {
+      const int j = j0 + tid;
+      if (j >= Rd) continue;
+      const int e = cur[j];
+      if (e != kNoExpert && !((held[e * W + (j >> 5)] >> (j & 31)) & 1u)) {
+        cur[j] = kNoExpert;
+        next[j] = (uint8_t)(next[j] + 1);
+      }
+    }
+  }
+
+  // seats: per expert, the exclusive prefix of its words' popcounts (into
+  // the preference area, no longer read), then each route's rank among the
+  // accepted ones
+  int32_t* pre = reinterpret_cast<int32_t*>(pref);
+  {
+    const int wpl = (W + kWave - 1) / kWave;
+    for (int e = wv; e < E; e += kDaWaves) {
+      const uint32_t* row = held + e * W;
+      const int w0 = lane * wpl, w1 = min(W, w0 + wpl);
+      int c = 0;
+      for (int w = w0; w < w1; ++w) c += __popc(row[w]);
+      const int inc = wave_incl_scan(c, lane);
+      int before = inc - c;
+      for (int w = w0; w < w1; ++w) {
+        pre[e * W + w] = before;
+        before += __popc(row[w]);
+      }
+      if (lane == kWave - 1) s_fill[e] = s_kept[e] + inc;
+    }
+  }
+  __syncthreads();
+  for (int j = tid; j < Rd; j += kDaThreads) {
+    const int r = drop[j], e = cur[j];
+    if (e == kNoExpert) {  // no expert with room: dropped after all
+      ids_out[r] = ids_in[r];
+      slot[r] = -1;
+    } else {
+      const int w = j >> 5;
+      ids_out[r] = e;
+      slot[r] = s_kept[e] + pre[e * W + w] + __popc(held[e * W + w] & ((1u << (j & 31)) - 1u));
+    }
+  }
+  if (wv == 0) {
+    const int f = lane < E ? s_fill[lane] : 0;
+    const int inc = wave_incl_scan(f, lane);
+    if (lane == 0) offsets[0] = 0;
+    if (lane < E) offsets[lane + 1] = inc;
+  }
+}
+
 hipError_t launch_reroute(const float* logits, const int32_t* ids_in, const int32_t* route_pos0,
                           const int32_t* offsets0, const int32_t* kept, int T, int k, int E,
                           int C, int32_t* ids_out, int32_t* slot, int32_t* offsets,
@@ -507,8 +735,14 @@ hipError_t launch_reroute(const float* logits, const int32_t* ids_in, const int3
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
   }
-  hipLaunchKernelGGL(reroute_kernel, dim3(1), dim3(kWave), 0, st, pref, ids_in, route_pos0,
-                     offsets0, kept, T, k, E, C, ids_out, slot, offsets);
+  const long da_bytes = da_layout(R, E).bytes;
+  if (k == 1 && R <= kDaMaxR && da_bytes <= kDaMaxLds) {
+    hipLaunchKernelGGL(reroute_da_kernel, dim3(1), dim3(kDaThreads), (unsigned)da_bytes, st, pref,
+                       ids_in, route_pos0, offsets0, kept, R, E, C, ids_out, slot, offsets);
+  } else {
+    hipLaunchKernelGGL(reroute_kernel, dim3(1), dim3(kWave), 0, st, pref, ids_in, route_pos0,
+                       offsets0, kept, T, k, E, C, ids_out, slot, offsets);
+  }
   hipError_t err = hipGetLastError();
   if (err != hipSuccess || R == 0) return err;
   hipLaunchKernelGGL(reroute_rows_kernel, dim3(ceil_div(R, 256)), dim3(256), 0, st, ids_out, slot,
