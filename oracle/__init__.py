@@ -59,6 +59,8 @@ def lib():
         L.oracle_dispatch_padded.argtypes = [_i64, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _vp]
         L.oracle_dispatch_reroute.restype = None
         L.oracle_dispatch_reroute.argtypes = [_i64, _i64, _i64, _i64] + [_vp] * 9
+        L.oracle_dispatch_queue.restype = _i64
+        L.oracle_dispatch_queue.argtypes = [_i64] * 5 + [_vp] * 8
         L.oracle_expert_choice.restype = None
         L.oracle_expert_choice.argtypes = [_i64, _i64, _i64, _vp, _vp, _vp, _vp]
         L.oracle_layer_forward_expert_choice.restype = _int
@@ -181,6 +183,85 @@ def dispatch_reroute(logits, expert_ids, E, C):
     return dict(ids=ids_out, counts=counts, filled=filled, offsets=offsets,
                 route_pos=route_pos.reshape(T, k), row_token=row_token[:n].copy(),
                 n_rerouted=int(moved[0]))
+
+
+def dispatch_queue(expert_ids, E, C, q_ids=None):
+    """Queue-to-the-next-micro-batch dispatch (see oracle_dispatch_queue).
+    expert_ids [T, k] of this batch, q_ids [Q] of the routes queued before.
+    Returns dict(counts, kept, offsets, pos [Q + T*k] over the arrivals,
+    row_arrival [offsets[E]], out_arrival [n_out]) -- arrival a < Q is queued
+    route a, arrival Q + r is route r of this batch."""
+    ids = np.ascontiguousarray(expert_ids, dtype=np.int32)
+    T, k = ids.shape
+    qa = np.ascontiguousarray(np.zeros(0) if q_ids is None else q_ids, dtype=np.int32).reshape(-1)
+    Q = qa.shape[0]
+    N = Q + T * k
+    counts = np.empty(E, np.int32)
+    kept = np.empty(E, np.int32)
+    offsets = np.empty(E + 1, np.int32)
+    pos = np.empty(max(N, 1), np.int32)
+    row_arrival = np.full(max(N, 1), -1, np.int32)
+    out_arrival = np.empty(max(N, 1), np.int32)
+    n_out = lib().oracle_dispatch_queue(T, E, k, int(C), Q, _p(qa), _p(ids), _p(counts),
+                                        _p(kept), _p(offsets), _p(pos), _p(row_arrival),
+                                        _p(out_arrival))
+    n = int(offsets[E])
+    return dict(counts=counts, kept=kept, offsets=offsets, pos=pos[:N].copy(),
+                row_arrival=row_arrival[:n].copy(), out_arrival=out_arrival[:int(n_out)].copy())
+
+
+def layer_forward_queued(x, w_router, b_router, w_gate, w_up, w_down, k, renorm, phi,
+                         queue=None, tag_base=0, ws_gate=None, ws_up=None, ws_down=None):
+    """The layer under the queue policy, composed from the oracle's steps:
+    route this batch, dispatch the arrivals (queued routes first), run the
+    experts on the seated rows (a queued route's row is its own token row,
+    carried in the queue), combine this batch's routes (plus the shared
+    expert) into y, and each seated queued route into its own row of y_late
+    (gate times expert output; zero when it waits again).
+    queue: dict(x [Q, d], ids [Q], gates [Q], tags [Q]) or None.  The tag
+    of this batch's token t is tag_base + t.
+    Returns dict(y [T, d], y_late [Q, d] (float64), ids, gates, counts,
+    pos, out=dict(x, ids, gates, tags) in arrival order)."""
+    xa, dt = as_array(x)
+    T, d = xa.shape
+    L = router_logits(x, w_router, b_router)
+    E = L.shape[1]
+    ids, gates = topk_gates(L, k, renorm)
+    C = capacity(T, E, k, phi)
+    if queue is None:
+        qx = np.zeros((0, d), xa.dtype)
+        qids = np.zeros(0, np.int32)
+        qg = np.zeros(0, np.float32)
+        qt = np.zeros(0, np.int64)
+    else:
+        qx = as_array(queue["x"])[0].reshape(-1, d)
+        qids = np.ascontiguousarray(queue["ids"], np.int32).reshape(-1)
+        qg = np.ascontiguousarray(queue["gates"], np.float32).reshape(-1)
+        qt = np.ascontiguousarray(queue["tags"], np.int64).reshape(-1)
+    Q = qids.shape[0]
+    dq = dispatch_queue(ids, E, C, qids)
+    rows = np.concatenate([xa, qx.astype(xa.dtype)], axis=0)       # token rows, then queued rows
+    a = dq["row_arrival"].astype(np.int64)
+    src = np.where(a < Q, T + a, (a - Q) // k)
+    yp = expert_ffn(gather_rows(rows, src), dq["offsets"], w_gate, w_up, w_down)
+    ysh = None if ws_gate is None else swiglu_rows(x, ws_gate, ws_up, ws_down)
+    pos = dq["pos"]
+    y = combine(yp, pos[Q:].reshape(T, k), gates, ysh)
+    y_late = combine(yp, pos[:Q].reshape(Q, 1), qg.reshape(Q, 1)) if Q else np.zeros((0, d))
+    # the routes that wait again, in arrival order
+    n_out = dq["out_arrival"].shape[0]
+    out = dict(x=np.empty((n_out, d), xa.dtype), ids=np.empty(n_out, np.int32),
+               gates=np.empty(n_out, np.float32), tags=np.empty(n_out, np.int64))
+    for i, a in enumerate(dq["out_arrival"].tolist()):
+        if a < Q:
+            out["x"][i], out["ids"][i], out["gates"][i], out["tags"][i] = \
+                rows[T + a], qids[a], qg[a], qt[a]
+        else:
+            r = a - Q
+            out["x"][i], out["ids"][i], out["gates"][i], out["tags"][i] = \
+                rows[r // k], ids.reshape(-1)[r], gates.reshape(-1)[r], tag_base + r // k
+    return dict(y=y, y_late=y_late, ids=ids, gates=gates, counts=dq["counts"], pos=pos, C=C,
+                out=out)
 
 
 def expert_choice(logits, C):

@@ -230,6 +230,27 @@ void oracle_dispatch_reroute(int64_t T, int64_t E, int64_t k, int64_t C,
   free(slot);
 }
 
+/* Queue to the next micro-batch ("Session 19", "Overflow policies"): the
+ * drop policy over the arrival sequence (queued routes first, then the
+ * call's routes), with the routes past capacity listed for the next call
+ * instead of being lost. */
+int64_t oracle_dispatch_queue(int64_t T, int64_t E, int64_t k, int64_t C, int64_t Q,
+                              const int32_t* q_ids, const int32_t* ids, int32_t* counts,
+                              int32_t* kept, int32_t* offsets, int32_t* pos,
+                              int32_t* row_arrival, int32_t* out_arrival) {
+  int64_t N = Q + T * k;
+  int32_t* seq = (int32_t*)malloc((size_t)(N > 0 ? N : 1) * sizeof(int32_t));
+  for (int64_t a = 0; a < Q; a++) seq[a] = q_ids[a];
+  for (int64_t r = 0; r < T * k; r++) seq[Q + r] = ids[r];
+  /* one route per arrival: k = 1 over the sequence */
+  oracle_dispatch(N, E, 1, C, seq, counts, kept, offsets, pos, row_arrival);
+  int64_t n_out = 0;
+  for (int64_t a = 0; a < N; a++)
+    if (pos[a] < 0) out_arrival[n_out++] = (int32_t)a;
+  free(seq);
+  return n_out;
+}
+
 /* Expert-choice routing ("MoE Inference Visualized", "Why MoE Matters for
  * Infrastructure": against load imbalance the experts can pick the tokens
  * instead of the tokens picking experts).  The page names the idea only.

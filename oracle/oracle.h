@@ -139,6 +139,32 @@ void oracle_dispatch_reroute(int64_t T, int64_t E, int64_t k, int64_t C,
                              int32_t* offsets, int32_t* route_pos,
                              int32_t* row_token, int64_t* n_rerouted);
 
+/* Overflow policy "queue to the next micro-batch" ("Session 19", "Overflow
+ * policies": the overflowing route is processed in the next micro-batch, at
+ * the cost of an extra exchange and a saw-tooth latency).  Reading: a route
+ * that finds its expert full is neither lost nor moved; it waits, with its
+ * expert and its gate, for the next call.  In that call the waiting routes
+ * arrive first, in their queue order, and the call's own routes after them
+ * in the order r = t*k + j: arrival a = 0..Q-1 is queued route a, arrival
+ * a = Q + r is route r.  Each expert seats its first C arrivals (C of the
+ * call's own batch); every later arrival, queued or new, waits again, and
+ * the new queue lists them in arrival order.  That is the drop policy of
+ * oracle_dispatch over the arrival sequence, the drops kept.
+ *   q_ids[Q], ids[T*k]   experts of the queued routes and of the call's routes
+ *   counts[E], kept[E], offsets[E+1]   as oracle_dispatch, over the arrivals
+ *   pos[Q + T*k]         packed row of arrival a, -1 if it waits again
+ *   row_arrival[p]       the arrival seated in packed row p
+ *   out_arrival[]        the arrivals that wait again, in arrival order
+ * Returns their number.  Pinned by the trace (t6's route at E1 waits, then
+ * takes the first seat of E1 in the next batch), by invariants over a run of
+ * batches (each route seated once; queued routes ahead of new ones; no
+ * expert over C) and, through the layer, by a dense brute force over that
+ * run. */
+int64_t oracle_dispatch_queue(int64_t T, int64_t E, int64_t k, int64_t C, int64_t Q,
+                              const int32_t* q_ids, const int32_t* ids, int32_t* counts,
+                              int32_t* kept, int32_t* offsets, int32_t* pos,
+                              int32_t* row_arrival, int32_t* out_arrival);
+
 /* Expert-choice routing ("MoE Inference Visualized", "Why MoE Matters for
  * Infrastructure": the experts pick the tokens instead of the tokens picking
  * experts -- named only).  Reading: score[t][e] = full softmax probability

@@ -671,6 +671,143 @@ def test_reroute_without_overflow_is_the_drop_policy():
 
 
 # ---------------------------------------------------------------------------
+# Overflow policy "queue to the next micro-batch" ([SPK] "Overflow policies":
+# the overflowing route is processed in the next micro-batch).  Reading: it
+# waits with its expert and gate; in the next call the waiting routes arrive
+# before that call's routes and are seated first.
+
+def test_queue_trace_spk():
+    """The [SPK] trace (C = 5): t6's route at E1 is the one overflow; under the
+    queue policy it waits instead of being lost.  Next micro-batch (the same
+    eight assignments again): E1 now has 7 arrivals for 5 seats -- the waiting
+    t6 route takes the first seat, then t1..t4; the new t5 and t6 routes to E1
+    wait in their arrival order.  Derived by hand from the reading."""
+    g = G.load("spk_capacity_trace.txt")
+    ids = np.array(G.rows(g["assign"], int), np.int32)
+    T, E, k = 8, 4, 2
+    C = oracle.capacity(T, E, k, 1.25)
+    b1 = oracle.dispatch_queue(ids, E, C)
+    assert b1["out_arrival"].tolist() == [5 * k + 0]              # t6's first route (to E1)
+    assert b1["kept"].tolist() == [5, 4, 3, 3]
+    # batch 2: the queued E1 route arrives first
+    q = ids.reshape(-1)[b1["out_arrival"]]
+    assert q.tolist() == [0]
+    b2 = oracle.dispatch_queue(ids, E, C, q)
+    assert b2["counts"].tolist() == [7, 4, 3, 3]
+    assert b2["kept"].tolist() == [5, 4, 3, 3]
+    lo = int(b2["offsets"][0])
+    assert b2["row_arrival"][lo:lo + 5].tolist() == [0] + [1 + t * k for t in range(4)]
+    assert b2["pos"][0] == lo                                       # first seat of E1
+    assert b2["out_arrival"].tolist() == [1 + 4 * k, 1 + 5 * k]     # t5, t6 of batch 2 at E1
+
+
+def _queue_run(batches, E, k, phi):
+    """Dispatch a run of batches (lists of [T, k] ids) under the queue policy;
+    queued routes carry their (batch, route) name."""
+    names = np.zeros((0, 2), np.int64)
+    qids = np.zeros(0, np.int32)
+    runs = []
+    for b, ids in enumerate(batches):
+        T = ids.shape[0]
+        C = oracle.capacity(T, E, k, phi)
+        out = oracle.dispatch_queue(ids, E, C, qids)
+        Q = qids.shape[0]
+        arr_names = np.concatenate([names, np.stack([np.full(T * k, b), np.arange(T * k)], 1)])
+        arr_ids = np.concatenate([qids, ids.reshape(-1)]).astype(np.int32)
+        runs.append(dict(out=out, Q=Q, C=C, names=arr_names, ids=arr_ids))
+        names = arr_names[out["out_arrival"]]
+        qids = arr_ids[out["out_arrival"]]
+    return runs, names
+
+
+@pytest.mark.parametrize("k,phi,seed", [(1, 0.6, 0), (2, 0.5, 1), (2, 0.9, 2), (4, 0.4, 3)])
+def test_queue_run_invariants(k, phi, seed):
+    """Over a run of micro-batches: no expert seats more than C per batch;
+    each route is seated exactly once or is still waiting at the end; at each
+    expert every seated queued route is ahead of every seated new route, and
+    a new route is seated only when no queued route to that expert waits;
+    the queue keeps arrival order; no overflow leaves the drop policy."""
+    rng = np.random.default_rng(seed)
+    E = 6
+    batches = []
+    for b in range(5):
+        T = int(rng.integers(5, 40))
+        L = rng.standard_normal((T, E)).astype(np.float32)
+        L[:, 0] += 1.0
+        batches.append(oracle.topk_gates(L, k, 1)[0])
+    runs, left = _queue_run(batches, E, k, phi)
+    seen = {}
+    for b, run in enumerate(runs):
+        out, Q, C = run["out"], run["Q"], run["C"]
+        assert (out["kept"] <= C).all()
+        pos = out["pos"]
+        assert np.array_equal(np.bincount(run["ids"][pos >= 0], minlength=E), out["kept"])
+        for a in np.flatnonzero(pos >= 0):
+            key = tuple(run["names"][a])
+            assert key not in seen
+            seen[key] = b
+        for e in range(E):
+            arr = np.flatnonzero(run["ids"] == e)
+            seated = arr[pos[arr] >= 0]
+            waiting = arr[pos[arr] < 0]
+            # seats go to the earliest arrivals: queued ones first
+            assert (seated.size == 0 or waiting.size == 0) or seated.max() < waiting.min()
+            assert np.array_equal(pos[seated], out["offsets"][e] + np.arange(seated.size))
+        assert np.array_equal(out["out_arrival"], np.flatnonzero(pos < 0))
+    total = sum(ids.size for ids in batches)
+    assert len(seen) + left.shape[0] == total
+    for key in map(tuple, left):
+        assert key not in seen
+    # no overflow: every batch is the drop policy's, nothing waits
+    runs2, left2 = _queue_run(batches, E, k, 8.0)
+    assert left2.shape[0] == 0
+    for ids, run in zip(batches, runs2):
+        ref = oracle.dispatch(ids, E, run["C"])
+        assert np.array_equal(run["out"]["pos"], ref["route_pos"].reshape(-1))
+
+
+def test_queue_layer_run_against_dense_brute_force():
+    """A run of fp32 micro-batches with overflow, then one call with no batch
+    and no capacity that seats every waiting route.  Each token's output in
+    its own batch plus the late rows of its queued routes equals the dense
+    fp64 mixture of all its k routes (no capacity) plus the shared expert."""
+    rng = np.random.default_rng(11)
+    E, k, d, d_ff, d_ffs = 4, 2, 16, 24, 8
+    wr = rng.standard_normal((E, d)).astype(np.float32) * 0.5
+    br = np.array([1.5, 0.0, -0.5, -1.0], np.float32)
+    wg, wu = (rng.standard_normal((E, d_ff, d)).astype(np.float32) / 4 for _ in range(2))
+    wd = rng.standard_normal((E, d, d_ff)).astype(np.float32) / 5
+    sg, su = (rng.standard_normal((d_ffs, d)).astype(np.float32) / 4 for _ in range(2))
+    sd = rng.standard_normal((d, d_ffs)).astype(np.float32) / 3
+    xs = [rng.standard_normal((T, d)).astype(np.float32) for T in (12, 9, 15)] + \
+        [np.zeros((0, d), np.float32)]
+    total = {}
+    queue = None
+    for b, x in enumerate(xs):
+        last = b == len(xs) - 1
+        out = oracle.layer_forward_queued(x, wr, br, wg, wu, wd, k, 1, 0.0 if last else 0.6,
+                                          queue=queue, tag_base=1000 * b,
+                                          ws_gate=None if last else sg, ws_up=None if last else su,
+                                          ws_down=None if last else sd)
+        for t in range(x.shape[0]):
+            total[1000 * b + t] = out["y"][t].copy()
+        if queue is not None:
+            for q, tag in enumerate(queue["tags"].tolist()):
+                total[tag] += out["y_late"][q]
+        if not last:
+            assert out["out"]["ids"].size > 0 or b > 0    # the run does overflow
+        queue = out["out"]
+    assert queue["ids"].size == 0                       # the last call seats everyone
+    for b, x in enumerate(xs[:-1]):
+        ref = dense_mask_layer(torch.from_numpy(x), torch.from_numpy(wr), torch.from_numpy(br),
+                               torch.from_numpy(wg), torch.from_numpy(wu), torch.from_numpy(wd),
+                               k, 1, 0.0, torch.from_numpy(sg), torch.from_numpy(su),
+                               torch.from_numpy(sd))["y"].numpy()
+        got = np.stack([total[1000 * b + t] for t in range(x.shape[0])])
+        assert np.allclose(got, ref, rtol=1e-5, atol=1e-5), np.abs(got - ref).max()
+
+
+# ---------------------------------------------------------------------------
 # Expert-choice routing ([BEA] "Why MoE Matters for Infrastructure": experts
 # pick tokens).  Reading: score = full softmax probability, expert e keeps
 # its Ce = min(C, T) best tokens (lower index first on equal scores), gate =
