@@ -351,6 +351,63 @@ int moe_layer_forward_timed(const moe_shape* s, const void* x, const void* w_rou
                             const void* ws_down, void* y, void* ws, size_t ws_bytes,
                             hipStream_t stream, hipEvent_t* events /*host*/, int32_t layout);
 
+/* Overflow policy "queue to the next micro-batch" ("Session 19:
+ * Mixture-of-Experts: routing and capacity", "Overflow policies": the
+ * overflowing route is processed in the next micro-batch, at the price of an
+ * extra exchange and a saw-tooth latency).  A route that finds its expert
+ * full is neither lost nor moved: it waits, with its expert and gate, in a
+ * queue the caller keeps and passes to the next call.  In that call the
+ * waiting routes arrive first, in queue order, and the call's own routes
+ * after them in the order r = t*k + j (arrival a < q_n is queued route a,
+ * arrival q_n + r is route r).  Each expert seats its first C arrivals, C =
+ * ceil(phi*T*k/E) of this call's batch (no limit when phi <= 0); every
+ * later arrival, queued or new, joins the outgoing queue, in arrival order.
+ * The library keeps no state: the queue lives in the caller's buffers.
+ *   q_n          routes waiting from the previous call (host, >= 0)
+ *   q_x [q_n, d] their token rows (dtype); q_ids [q_n] int32 experts;
+ *   q_gates [q_n] fp32 gates; q_tags [q_n] int64 (opaque to the library,
+ *                returned with the route)
+ *   tag_base     tag of this batch's token t is tag_base + t
+ *   y [T, d]     this batch: its seated routes' gated expert outputs plus
+ *                the shared expert
+ *   y_late [q_n, d]  row a: queued route a's gate times its expert output
+ *                if it was seated in this call, else a zero row (the caller
+ *                adds it to the output of the token its tag names)
+ *   out_n        device int32: routes in the outgoing queue
+ *   out_x [q_n + T*k, d], out_ids, out_gates, out_tags: the outgoing queue
+ *                (first *out_n entries), same layout as the q_ arguments;
+ *                out_x must not alias q_x or x
+ *   expert_ids, gates [T, k], counts [E] (demand over all arrivals): optional
+ *   route_pos [q_n + T*k]: optional, packed row of every arrival, -1 if it
+ *                waits
+ * Workspace: moe_workspace_bytes_queued(s, q_n).  Errors as
+ * moe_layer_forward; MOE_ERR_UNSUPPORTED when q_n + T*k or the row buffer
+ * [T + q_n, d] leaves the 32-bit ranges. */
+int moe_workspace_bytes_queued(const moe_shape* s, int64_t q_n, size_t* bytes_out /*host*/);
+int moe_layer_forward_queued(const moe_shape* s, const void* x, const void* w_router,
+                             const float* b_router, const void* w_gate, const void* w_up,
+                             const void* w_down, const void* ws_gate, const void* ws_up,
+                             const void* ws_down, int64_t q_n, const void* q_x,
+                             const int32_t* q_ids, const float* q_gates, const int64_t* q_tags,
+                             int64_t tag_base, void* y, void* y_late, int32_t* out_n, void* out_x,
+                             int32_t* out_ids, float* out_gates, int64_t* out_tags,
+                             int32_t* expert_ids, float* gates, int32_t* counts,
+                             int32_t* route_pos, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* moe_layer_forward_queued (tag_base 0, no optional outputs) with the
+ * stage-boundary events of moe_layer_forward_timed (events[1] before the
+ * arrivals' dispatch and the outgoing queue; the late rows follow
+ * events[6]).  For measurement only. */
+int moe_layer_forward_queued_timed(const moe_shape* s, const void* x, const void* w_router,
+                                   const float* b_router, const void* w_gate, const void* w_up,
+                                   const void* w_down, const void* ws_gate, const void* ws_up,
+                                   const void* ws_down, int64_t q_n, const void* q_x,
+                                   const int32_t* q_ids, const float* q_gates,
+                                   const int64_t* q_tags, void* y, void* y_late, int32_t* out_n,
+                                   void* out_x, int32_t* out_ids, float* out_gates,
+                                   int64_t* out_tags, void* ws, size_t ws_bytes,
+                                   hipStream_t stream, hipEvent_t* events /*host*/);
+
 #ifdef __cplusplus
 }
 #endif

@@ -9,7 +9,8 @@ fails when libmoe.so has not been built.
 Entry points (same names as the C ABI, without the moe_ prefix):
     capacity, workspace_bytes, route, permute, expert_ffn, combine,
     layer_forward, layer_forward_timed, routing_stats, permute_padded,
-    permute_reroute, permute_expert_choice, layer_forward_expert_choice
+    permute_reroute, permute_expert_choice, layer_forward_expert_choice,
+    workspace_bytes_queued, layer_forward_queued, layer_forward_queued_timed
     (layer_forward takes padded= / reroute= for the other layouts)
 """
 import ctypes
@@ -34,7 +35,9 @@ EXPORTS = ("moe_status_string", "moe_capacity", "moe_workspace_bytes", "moe_rout
            "moe_permute", "moe_expert_ffn", "moe_combine", "moe_layer_forward",
            "moe_layer_forward_timed", "moe_routing_stats", "moe_permute_padded",
            "moe_layer_forward_padded", "moe_permute_reroute", "moe_layer_forward_reroute",
-           "moe_permute_expert_choice", "moe_layer_forward_expert_choice")
+           "moe_permute_expert_choice", "moe_layer_forward_expert_choice",
+           "moe_workspace_bytes_queued", "moe_layer_forward_queued",
+           "moe_layer_forward_queued_timed")
 
 
 class MoeShape(ctypes.Structure):
@@ -71,6 +74,12 @@ _lib.moe_permute_expert_choice.argtypes = [_SP] + [_vp] * 7 + [_vp, _sz, _vp]
 _lib.moe_layer_forward_expert_choice.argtypes = [_SP] + [_vp] * 12 + [_vp, _sz, _vp]
 _lib.moe_routing_stats.argtypes = [_SP, _vp, _vp, _vp, ctypes.c_double, ctypes.c_int32, _vp, _vp,
                                    _vp, _sz, _vp]
+_i64 = ctypes.c_int64
+_lib.moe_workspace_bytes_queued.argtypes = [_SP, _i64, ctypes.POINTER(_sz)]
+_lib.moe_layer_forward_queued.argtypes = [_SP] + [_vp] * 9 + [_i64] + [_vp] * 4 + [_i64] + \
+    [_vp] * 11 + [_vp, _sz, _vp]
+_lib.moe_layer_forward_queued_timed.argtypes = [_SP] + [_vp] * 9 + [_i64] + [_vp] * 4 + \
+    [_vp] * 7 + [_vp, _sz, _vp, _vp]
 for _n in EXPORTS[1:]:
     getattr(_lib, _n).restype = ctypes.c_int
 
@@ -434,3 +443,115 @@ def layer_forward_timed(s, x, w_router, b_router, w_gate, w_up, w_down, ws_gate,
         1 if padded else 2 if reroute else 3 if choice else 0),
         "moe_layer_forward_timed")
     return y
+
+
+def workspace_bytes_queued(s, q_n):
+    n = _sz()
+    _check(_lib.moe_workspace_bytes_queued(ctypes.byref(s), int(q_n), ctypes.byref(n)),
+           "moe_workspace_bytes_queued")
+    return n.value
+
+
+def queue_buffers(s, q_n, device="cuda"):
+    """Device buffers of one queued call with q_n waiting routes: y, y_late,
+    the outgoing queue (capacity q_n + T*k) and its length, and the
+    workspace."""
+    dt = _tdtype(s)
+    n = int(q_n) + s.T * s.k
+    return dict(y=torch.empty(s.T, s.d, dtype=dt, device=device),
+                y_late=torch.empty(int(q_n), s.d, dtype=dt, device=device),
+                out_n=torch.zeros(1, dtype=torch.int32, device=device),
+                out_x=torch.empty(n, s.d, dtype=dt, device=device),
+                out_ids=torch.empty(n, dtype=torch.int32, device=device),
+                out_gates=torch.empty(n, dtype=torch.float32, device=device),
+                out_tags=torch.empty(n, dtype=torch.int64, device=device),
+                ws=torch.empty(workspace_bytes_queued(s, q_n), dtype=torch.uint8, device=device))
+
+
+def _queue_args(s, queue, dt):
+    if queue is None:
+        return 0, None, None, None, None
+    qn = int(queue["ids"].shape[0])
+    return (qn, _ptr(queue["x"], "queue x", (qn, s.d), dt),
+            _ptr(queue["ids"], "queue ids", (qn,), torch.int32),
+            _ptr(queue["gates"], "queue gates", (qn,), torch.float32),
+            _ptr(queue["tags"], "queue tags", (qn,), torch.int64))
+
+
+def _layer_args(s, x, w_router, b_router, w_gate, w_up, w_down, ws_gate, ws_up, ws_down):
+    dt = _tdtype(s)
+    shp = s.d_ff_shared > 0
+    return [_ptr(x, "x", (s.T, s.d), dt), _ptr(w_router, "w_router", (s.E, s.d), dt),
+            _ptr(b_router, "b_router", (s.E,), torch.float32, optional=True),
+            _ptr(w_gate, "w_gate", (s.E, s.d_ff, s.d), dt),
+            _ptr(w_up, "w_up", (s.E, s.d_ff, s.d), dt),
+            _ptr(w_down, "w_down", (s.E, s.d, s.d_ff), dt),
+            _ptr(ws_gate, "ws_gate", (s.d_ff_shared, s.d), dt, optional=not shp),
+            _ptr(ws_up, "ws_up", (s.d_ff_shared, s.d), dt, optional=not shp),
+            _ptr(ws_down, "ws_down", (s.d, s.d_ff_shared), dt, optional=not shp)]
+
+
+def _out_args(s, b, qn, dt):
+    n = qn + s.T * s.k
+    return [_ptr(b["y"], "y", (s.T, s.d), dt), _ptr(b["y_late"], "y_late", (qn, s.d), dt),
+            _ptr(b["out_n"], "out_n", (1,), torch.int32),
+            _ptr(b["out_x"], "out_x", (n, s.d), dt),
+            _ptr(b["out_ids"], "out_ids", (n,), torch.int32),
+            _ptr(b["out_gates"], "out_gates", (n,), torch.float32),
+            _ptr(b["out_tags"], "out_tags", (n,), torch.int64)]
+
+
+def layer_forward_queued(s, x, w_router, b_router, w_gate, w_up, w_down, ws_gate=None,
+                         ws_up=None, ws_down=None, queue=None, tag_base=0, bufs=None,
+                         stream=None, return_routing=False, sync=True):
+    """moe_layer_forward_queued (overflow policy "queue to the next
+    micro-batch").  queue: dict(x [Q, d], ids [Q] int32, gates [Q] fp32,
+    tags [Q] int64) of the routes waiting from the previous call, or None.
+    Returns (y, y_late, out_queue) -- out_queue in the same form, cut to its
+    length (one host synchronisation; with sync=False the full buffers are
+    returned with out_queue["n"], a device int32) -- plus, with
+    return_routing, dict(expert_ids, gates, counts, route_pos [Q + T*k])."""
+    dt = _tdtype(s)
+    dev = x.device
+    qn, qx, qi, qg, qt = _queue_args(s, queue, dt)
+    if bufs is None:
+        bufs = queue_buffers(s, qn, dev)
+    routing = None
+    extra = [None] * 4
+    if return_routing:
+        routing = dict(expert_ids=torch.empty(s.T, s.k, dtype=torch.int32, device=dev),
+                       gates=torch.empty(s.T, s.k, dtype=torch.float32, device=dev),
+                       counts=torch.empty(s.E, dtype=torch.int32, device=dev),
+                       route_pos=torch.empty(qn + s.T * s.k, dtype=torch.int32, device=dev))
+        extra = [_ptr(routing[n], n) for n in ("expert_ids", "gates", "counts", "route_pos")]
+    ws = bufs["ws"]
+    _ptr(ws, "ws", dtype=torch.uint8)
+    args = _layer_args(s, x, w_router, b_router, w_gate, w_up, w_down, ws_gate, ws_up, ws_down)
+    _check(_lib.moe_layer_forward_queued(ctypes.byref(s), *args, qn, qx, qi, qg, qt,
+                                         int(tag_base), *_out_args(s, bufs, qn, dt), *extra,
+                                         ws.data_ptr(), ws.numel(), _stream(stream)),
+           "moe_layer_forward_queued")
+    out = dict(x=bufs["out_x"], ids=bufs["out_ids"], gates=bufs["out_gates"],
+               tags=bufs["out_tags"], n=bufs["out_n"])
+    if sync:
+        n = int(bufs["out_n"].item())
+        out = dict(x=out["x"][:n], ids=out["ids"][:n], gates=out["gates"][:n],
+                   tags=out["tags"][:n])
+    res = (bufs["y"], bufs["y_late"], out)
+    return res + (routing,) if return_routing else res
+
+
+def layer_forward_queued_timed(s, x, w_router, b_router, w_gate, w_up, w_down, ws_gate, ws_up,
+                               ws_down, queue, bufs, events, stream=None):
+    """moe_layer_forward_queued_timed: the queued layer with the 7
+    stage-boundary hipEvents of layer_forward_timed."""
+    dt = _tdtype(s)
+    qn, qx, qi, qg, qt = _queue_args(s, queue, dt)
+    arr = (ctypes.c_void_p * 7)(*[ctypes.c_void_p(e) for e in events])
+    ws = bufs["ws"]
+    args = _layer_args(s, x, w_router, b_router, w_gate, w_up, w_down, ws_gate, ws_up, ws_down)
+    _check(_lib.moe_layer_forward_queued_timed(ctypes.byref(s), *args, qn, qx, qi, qg, qt,
+                                               *_out_args(s, bufs, qn, dt), ws.data_ptr(),
+                                               ws.numel(), _stream(stream), arr),
+           "moe_layer_forward_queued_timed")
+    return bufs["y"]

@@ -68,6 +68,8 @@ int64_t rmax_of(const moe_shape* s, int64_t C) {
 struct Layout {
   size_t logits, ids, gates, cnt, counts, kept, offsets, route_pos, row_token, h, yp, part, hs,
       ys, spart, shist, xpad, opad, ppos, ids2, slot, offs2, rpos0, pref, eck, ecp, ecoff;
+  // queue policy: row buffer [x; queued rows], outgoing-queue scratch
+  size_t aall, qflags, qcnt, qmisc, qpos, qarr, qsrc;
   int splits;      // K splits of the routed down GEMM (fp32 partial planes when > 1)
   int splits_pad;  // the same for the fixed-shape [E, C] layout
   int splits_ec;   // the same for expert-choice rows
@@ -137,10 +139,35 @@ moe::GemmPlan choice_plan(const moe_shape* s, const int32_t* offsets_ec) {
                        (long)(s->E * Ce), (long)Ce};
 }
 
-Layout layout_of(const moe_shape* s) {
+// Queue policy ("queue to the next micro-batch"): Q routes waiting from the
+// previous call arrive ahead of this call's T*k routes, N = Q + T*k arrivals
+// of one route each.  Packed rows: at most E*C (C of this call), else N.
+int64_t rmax_queue(const moe_shape* s, int64_t Q) {
   const int64_t C = capacity_of(s);
-  const int64_t Rmax = rmax_of(s, C);
-  const size_t R = (size_t)(s->T * s->k);
+  const int64_t N = Q + s->T * s->k;
+  if (C < 0) return N;
+  const int64_t ec = s->E * C;
+  return ec < N ? ec : N;
+}
+
+// An expert seats at most C arrivals, and never more than every queued
+// route plus each token once.
+moe::GemmPlan queue_plan(const moe_shape* s, int64_t Q, const int32_t* offsets) {
+  const int64_t C = capacity_of(s);
+  const int64_t most = Q + s->T;
+  const long cap = (long)(C >= 0 && C < most ? C : most);
+  return moe::GemmPlan{s->dtype == MOE_DTYPE_BF16, true, offsets, (int)s->E, 0,
+                       (long)rmax_queue(s, Q), cap};
+}
+
+// Q >= 0: the queue policy's layout for Q waiting routes (route-sized
+// arrays span the N = Q + T*k arrivals; the other layouts' buffers are left
+// out).  Q < 0: the layout every other entry point uses.
+Layout layout_of(const moe_shape* s, int64_t Q = -1) {
+  const bool queued = Q >= 0;
+  const int64_t C = capacity_of(s);
+  const int64_t Rmax = queued ? rmax_queue(s, Q) : rmax_of(s, C);
+  const size_t R = (size_t)(s->T * s->k + (queued ? Q : 0));
   const size_t eb = (size_t)elem_bytes(s);
   const size_t nch = (size_t)moe::permute_nchunks((long)R);
   Layout L{};
@@ -161,12 +188,13 @@ Layout layout_of(const moe_shape* s) {
   // expert rows: the packed layout's R_max rows, or the fixed-shape
   // buffer's E*C rows when there is a capacity (the larger of the two;
   // expert choice's E*Ce rows are at most E*C)
-  const int64_t Rpad = rpad_of(s);
+  const int64_t Rpad = queued ? 0 : rpad_of(s);
   const size_t Rbig = (size_t)(Rpad > Rmax ? Rpad : Rmax);
   L.row_token = take(Rbig * sizeof(int32_t));
   L.h = take(Rbig * s->d_ff * eb);
   L.yp = take(Rbig * s->d * eb);
-  L.splits = moe::gemm_down_splits(routed_plan(s, nullptr, false), (int)s->d, (int)s->d_ff);
+  L.splits = moe::gemm_down_splits(queued ? queue_plan(s, Q, nullptr) : routed_plan(s, nullptr, false),
+                                   (int)s->d, (int)s->d_ff);
   L.splits_pad = Rpad > 0 ? moe::gemm_down_splits(padded_plan(s, nullptr), (int)s->d, (int)s->d_ff)
                           : 1;
   L.splits_ec = Rpad > 0 ? moe::gemm_down_splits(choice_plan(s, nullptr), (int)s->d, (int)s->d_ff)
@@ -180,15 +208,16 @@ Layout layout_of(const moe_shape* s) {
   L.part = take(part_max * s->d * sizeof(float));
   L.xpad = take((size_t)Rpad * s->d * eb);
   L.opad = take((size_t)(s->E + 1) * sizeof(int32_t));
-  L.ppos = take(R * sizeof(int32_t));
+  const size_t Ro = queued ? 0 : R;  // routes of the other layouts' buffers
+  L.ppos = take(Ro * sizeof(int32_t));
   // reroute policy: primary positions, final experts and seats
-  L.ids2 = take(R * sizeof(int32_t));
-  L.slot = take(R * sizeof(int32_t));
+  L.ids2 = take(Ro * sizeof(int32_t));
+  L.slot = take(Ro * sizeof(int32_t));
   L.offs2 = take((size_t)(s->E + 1) * sizeof(int32_t));
-  L.rpos0 = take(R * sizeof(int32_t));
-  L.pref = take(R * 64);  // preference lists of the dropped routes (E <= 64)
+  L.rpos0 = take(Ro * sizeof(int32_t));
+  L.pref = take(Ro * 64);  // preference lists of the dropped routes (E <= 64)
   // expert choice: expert-major keys (score bits) and route table, row groups
-  const size_t TE = (size_t)s->T * s->E;
+  const size_t TE = queued ? 0 : (size_t)s->T * s->E;
   L.eck = take(TE * sizeof(uint32_t));
   L.ecp = take(TE * sizeof(int32_t));
   L.ecoff = take((size_t)(s->E + 1) * sizeof(int32_t));
@@ -198,6 +227,17 @@ Layout layout_of(const moe_shape* s) {
   const size_t sblk = (size_t)moe::stats_blocks((long)s->T);
   L.spart = take(sblk * (size_t)(s->E + 3) * sizeof(float));
   L.shist = take(sblk * (size_t)moe::kMaxStatBins * sizeof(int32_t));
+  // queue policy: rows [x (T); queued (Q)], and the outgoing queue's
+  // counting sort (flags, chunk counts, n_out / kept / offsets, positions,
+  // arrivals, source rows)
+  const size_t Rq = queued ? R : 0;
+  L.aall = take(queued ? (size_t)(s->T + Q) * s->d * eb : 0);
+  L.qflags = take(Rq * sizeof(int32_t));
+  L.qcnt = take(queued ? (size_t)moe::permute_nchunks((long)R) * sizeof(int32_t) : 0);
+  L.qmisc = take(4 * sizeof(int32_t));
+  L.qpos = take(Rq * sizeof(int32_t));
+  L.qarr = take(Rq * sizeof(int32_t));
+  L.qsrc = take(Rq * sizeof(int32_t));
   L.total = o;
   return L;
 }
@@ -651,6 +691,148 @@ int moe_layer_forward_timed(const moe_shape* s, const void* x, const void* w_rou
   return layer_forward_impl(s, x, w_router, b_router, w_gate, w_up, w_down, ws_gate, ws_up,
                             ws_down, y, nullptr, nullptr, nullptr, nullptr, ws, ws_bytes, stream,
                             events, layout);
+}
+
+// Queue policy: the waiting routes of the previous call arrive first; the
+// drop policy runs over the arrivals (one route each); the routes past
+// capacity form the outgoing queue.  Expert rows come from [x; queued rows].
+static int layer_forward_queued_impl(
+    const moe_shape* s, const void* x, const void* w_router, const float* b_router,
+    const void* w_gate, const void* w_up, const void* w_down, const void* ws_gate,
+    const void* ws_up, const void* ws_down, int64_t q_n, const void* q_x, const int32_t* q_ids,
+    const float* q_gates, const int64_t* q_tags, int64_t tag_base, void* y, void* y_late,
+    int32_t* out_n, void* out_x, int32_t* out_ids, float* out_gates, int64_t* out_tags,
+    int32_t* expert_ids, float* gates, int32_t* counts, int32_t* route_pos, void* ws,
+    size_t ws_bytes, hipStream_t stream, hipEvent_t* ev) {
+  int v = validate(s);
+  if (v != MOE_OK) return v;
+  if (q_n < 0) return MOE_ERR_INVALID_ARG;
+  const int64_t Q = q_n, N = q_n + s->T * s->k;
+  const int64_t eb = elem_bytes(s);
+  const int64_t lim = int64_t(1) << 31;
+  const int64_t wide = s->d > s->d_ff ? s->d : s->d_ff;
+  if (N >= lim || (s->T + Q) * s->d * eb >= lim || rmax_queue(s, Q) * wide * eb >= lim)
+    return MOE_ERR_UNSUPPORTED;
+  if (!w_router || !w_gate || !w_up || !w_down || !out_n || (s->T > 0 && (!x || !y)) ||
+      (Q > 0 && (!q_x || !q_ids || !q_gates || !q_tags || !y_late)) ||
+      (N > 0 && (!out_x || !out_ids || !out_gates || !out_tags)))
+    return MOE_ERR_INVALID_ARG;
+  const bool shared = s->d_ff_shared > 0;
+  if (shared && (!ws_gate || !ws_up || !ws_down)) return MOE_ERR_INVALID_ARG;
+  if (!aligned16(x) || !aligned16(w_router) || !aligned16(w_gate) || !aligned16(w_up) ||
+      !aligned16(w_down) || !aligned16(y) || !aligned16(q_x) || !aligned16(y_late) ||
+      !aligned16(out_x))
+    return MOE_ERR_INVALID_ARG;
+  if (shared && (!aligned16(ws_gate) || !aligned16(ws_up) || !aligned16(ws_down)))
+    return MOE_ERR_INVALID_ARG;
+  if (!ws || reinterpret_cast<uintptr_t>(ws) % kAlign) return MOE_ERR_WORKSPACE;
+  const Layout L = layout_of(s, Q);
+  if (ws_bytes < L.total) return MOE_ERR_WORKSPACE;
+
+  const bool bf16 = s->dtype == MOE_DTYPE_BF16;
+  const int T = (int)s->T, d = (int)s->d, E = (int)s->E, k = (int)s->k;
+  const int64_t C = capacity_of(s);
+  const int64_t Rmax = rmax_queue(s, Q);
+  const size_t row_bytes = (size_t)d * eb;
+  int32_t* ids_all = at<int32_t>(ws, L.ids);  // [Q queued experts; T*k router choices]
+  float* g = gates ? gates : at<float>(ws, L.gates);
+  int32_t* cnts = counts ? counts : at<int32_t>(ws, L.counts);
+  int32_t* pos = route_pos ? route_pos : at<int32_t>(ws, L.route_pos);
+  int32_t* offsets = at<int32_t>(ws, L.offsets);
+  int32_t* row_token = at<int32_t>(ws, L.row_token);
+  void* rows = at<void>(ws, L.aall);
+  int32_t* misc = at<int32_t>(ws, L.qmisc);  // kept1, off1[2]
+  auto mark = [&](int i) {
+    if (ev && ev[i]) hipEventRecord(ev[i], stream);
+  };
+  mark(0);
+  // arrivals: the queued experts, then this batch's router choices
+  if (Q > 0 && hipMemcpyAsync(ids_all, q_ids, (size_t)Q * sizeof(int32_t),
+                              hipMemcpyDeviceToDevice, stream) != hipSuccess)
+    return MOE_ERR_HIP;
+  hipError_t e = moe::launch_route(bf16, x, w_router, b_router, T, d, E, k, s->renormalize,
+                                   at<float>(ws, L.logits), ids_all + Q, g, stream);
+  if (e != hipSuccess) return MOE_ERR_HIP;
+  mark(1);
+  if (expert_ids && T > 0 &&
+      hipMemcpyAsync(expert_ids, ids_all + Q, (size_t)T * k * sizeof(int32_t),
+                     hipMemcpyDeviceToDevice, stream) != hipSuccess)
+    return MOE_ERR_HIP;
+  // expert rows: [x; queued rows]
+  if (T > 0 && hipMemcpyAsync(rows, x, (size_t)T * row_bytes, hipMemcpyDeviceToDevice,
+                              stream) != hipSuccess)
+    return MOE_ERR_HIP;
+  if (Q > 0 && hipMemcpyAsync(static_cast<char*>(rows) + (size_t)T * row_bytes, q_x,
+                              (size_t)Q * row_bytes, hipMemcpyDeviceToDevice, stream) != hipSuccess)
+    return MOE_ERR_HIP;
+  // the drop policy over the arrivals, then packed rows -> source rows
+  e = moe::launch_permute_index(ids_all, (int)N, 1, E, (int)C, at<int32_t>(ws, L.cnt), cnts,
+                                at<int32_t>(ws, L.kept), offsets, pos, row_token, stream);
+  if (e != hipSuccess) return MOE_ERR_HIP;
+  e = moe::launch_queue_src(offsets, E, (int)Q, T, k, (long)Rmax, row_token, stream);
+  if (e != hipSuccess) return MOE_ERR_HIP;
+  // the outgoing queue: arrivals past capacity, in arrival order
+  int32_t* src = at<int32_t>(ws, L.qsrc);
+  e = moe::launch_queue_out(pos, (long)N, (int)Q, T, k, q_ids, q_gates, q_tags, ids_all + Q, g,
+                            tag_base, at<int32_t>(ws, L.qflags), at<int32_t>(ws, L.qcnt), out_n,
+                            misc, misc + 1, at<int32_t>(ws, L.qpos), at<int32_t>(ws, L.qarr),
+                            out_ids, out_gates, out_tags, src, stream);
+  if (e != hipSuccess) return MOE_ERR_HIP;
+  e = moe::launch_gather_rows(rows, src, misc + 1, 1, (long)N, (long)row_bytes, out_x, stream);
+  if (e != hipSuccess) return MOE_ERR_HIP;
+  // experts on the seated rows, shared expert, this batch's combine
+  const moe::GemmPlan pl = queue_plan(s, Q, offsets);
+  v = experts_and_combine(s, L, pl, x, rows, row_token, (long)(T + Q), w_gate, w_up, w_down,
+                          ws_gate, ws_up, ws_down, L.splits, (long)Rmax, pos + Q, g, k, false, y,
+                          ws, stream, ev);
+  if (v != MOE_OK) return v;
+  // late rows: each queued route's gated output (zero when it waits again)
+  if (Q > 0) {
+    const void* yrows = L.splits > 1 ? at<void>(ws, L.part) : at<void>(ws, L.yp);
+    e = moe::launch_combine(bf16, yrows, L.splits, (long)Rmax * d, pos, q_gates, nullptr, (int)Q,
+                            1, d, y_late, stream);
+    if (e != hipSuccess) return MOE_ERR_HIP;
+  }
+  return MOE_OK;
+}
+
+int moe_workspace_bytes_queued(const moe_shape* s, int64_t q_n, size_t* bytes_out) {
+  int v = validate(s);
+  if (v != MOE_OK) return v;
+  if (!bytes_out || q_n < 0) return MOE_ERR_INVALID_ARG;
+  *bytes_out = layout_of(s, q_n).total;
+  return MOE_OK;
+}
+
+int moe_layer_forward_queued(const moe_shape* s, const void* x, const void* w_router,
+                             const float* b_router, const void* w_gate, const void* w_up,
+                             const void* w_down, const void* ws_gate, const void* ws_up,
+                             const void* ws_down, int64_t q_n, const void* q_x,
+                             const int32_t* q_ids, const float* q_gates, const int64_t* q_tags,
+                             int64_t tag_base, void* y, void* y_late, int32_t* out_n, void* out_x,
+                             int32_t* out_ids, float* out_gates, int64_t* out_tags,
+                             int32_t* expert_ids, float* gates, int32_t* counts,
+                             int32_t* route_pos, void* ws, size_t ws_bytes, hipStream_t stream) {
+  return layer_forward_queued_impl(s, x, w_router, b_router, w_gate, w_up, w_down, ws_gate, ws_up,
+                                   ws_down, q_n, q_x, q_ids, q_gates, q_tags, tag_base, y, y_late,
+                                   out_n, out_x, out_ids, out_gates, out_tags, expert_ids, gates,
+                                   counts, route_pos, ws, ws_bytes, stream, nullptr);
+}
+
+int moe_layer_forward_queued_timed(const moe_shape* s, const void* x, const void* w_router,
+                                   const float* b_router, const void* w_gate, const void* w_up,
+                                   const void* w_down, const void* ws_gate, const void* ws_up,
+                                   const void* ws_down, int64_t q_n, const void* q_x,
+                                   const int32_t* q_ids, const float* q_gates,
+                                   const int64_t* q_tags, void* y, void* y_late, int32_t* out_n,
+                                   void* out_x, int32_t* out_ids, float* out_gates,
+                                   int64_t* out_tags, void* ws, size_t ws_bytes,
+                                   hipStream_t stream, hipEvent_t* events) {
+  if (!events) return MOE_ERR_INVALID_ARG;
+  return layer_forward_queued_impl(s, x, w_router, b_router, w_gate, w_up, w_down, ws_gate, ws_up,
+                                   ws_down, q_n, q_x, q_ids, q_gates, q_tags, 0, y, y_late, out_n,
+                                   out_x, out_ids, out_gates, out_tags, nullptr, nullptr, nullptr,
+                                   nullptr, ws, ws_bytes, stream, events);
 }
 
 }  // extern "C"

@@ -241,3 +241,47 @@ def test_expert_choice_rejected_before_launch():
     assert L.moe_layer_forward_timed(ctypes.byref(s), fake, fake, None, fake, fake, fake, None,
                                      None, None, fake, ws, moe.workspace_bytes(s), None, evs,
                                      4) == moe.MOE_ERR_INVALID_ARG
+
+
+def test_queue_entry_point_rejected_before_launch():
+    """moe_layer_forward_queued validates on the host: a negative queue
+    length, missing queue or output buffers, misalignment and a workspace
+    sized for a shorter queue are errors before any launch."""
+    moe = _moe()
+    L = moe._lib
+    s = moe.shape(16, 64, 4, 2, 64, phi=1.0)
+    by = ctypes.byref(s)
+    fake, ws = 4096, 1 << 20
+
+    def call(q_n, qx=fake, qi=fake, qg=fake, qt=fake, y_late=fake, out_n=fake, out_x=fake,
+             need=None, w=ws):
+        if need is None:
+            need = moe.workspace_bytes_queued(s, max(q_n, 0))
+        return L.moe_layer_forward_queued(by, fake, fake, None, fake, fake, fake, None, None, None,
+                                          q_n, qx, qi, qg, qt, 0, fake, y_late, out_n, out_x,
+                                          fake, fake, fake, None, None, None, None, w, need, None)
+
+    assert call(-1, need=1 << 30) == moe.MOE_ERR_INVALID_ARG
+    assert call(3, qx=None) == moe.MOE_ERR_INVALID_ARG
+    assert call(3, qt=None) == moe.MOE_ERR_INVALID_ARG
+    assert call(3, y_late=None) == moe.MOE_ERR_INVALID_ARG
+    assert call(0, out_n=None) == moe.MOE_ERR_INVALID_ARG
+    assert call(0, out_x=None) == moe.MOE_ERR_INVALID_ARG
+    assert call(3, qx=fake + 8) == moe.MOE_ERR_INVALID_ARG
+    assert call(3, w=ws + 16) == moe.MOE_ERR_WORKSPACE
+    assert call(4000, need=moe.workspace_bytes_queued(s, 100)) == moe.MOE_ERR_WORKSPACE
+    n = ctypes.c_size_t()
+    assert L.moe_workspace_bytes_queued(by, -1, ctypes.byref(n)) == moe.MOE_ERR_INVALID_ARG
+    assert moe.workspace_bytes_queued(s, 1000) > moe.workspace_bytes_queued(s, 0)
+    # the row buffer [T + q_n, d] must keep 32-bit offsets
+    big = moe.shape(16, 1 << 16, 4, 2, 64, phi=1.0)
+    assert L.moe_layer_forward_queued(ctypes.byref(big), fake, fake, None, fake, fake, fake, None,
+                                      None, None, 1 << 14, fake, fake, fake, fake, 0, fake, fake,
+                                      fake, fake, fake, fake, fake, None, None, None, None, ws,
+                                      1 << 40, None) == moe.MOE_ERR_UNSUPPORTED
+    evs = (ctypes.c_void_p * 7)()
+    assert L.moe_layer_forward_queued_timed(by, fake, fake, None, fake, fake, fake, None, None,
+                                            None, 0, None, None, None, None, fake, None, fake,
+                                            fake, fake, fake, fake, ws,
+                                            moe.workspace_bytes_queued(s, 0), None, None) \
+        == moe.MOE_ERR_INVALID_ARG

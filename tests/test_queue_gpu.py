@@ -1,0 +1,148 @@
+"""GPU parity of the overflow policy "queue to the next micro-batch"
+("Session 19", "Overflow policies") -- moe_layer_forward_queued -- against
+the CPU oracle, over runs of micro-batches.
+
+The GPU run and the oracle run each carry their own queue from call to call
+(the oracle's queue never comes from the GPU).  Per call: the arrival
+positions, the outgoing queue (length, experts, tags, gates) and its token
+rows are compared bit for bit; y and the late rows to the layer tolerances.
+A run ends with a call that has no batch and no capacity, which seats every
+waiting route."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from tests._gpu import bits, check_y, say
+from workloads import WORKLOADS, Workload, make_inputs
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def moe():
+    assert torch.cuda.is_available(), "GPU parity tests need a GPU"
+    import routing_dispatch_expert_route_amd as m
+    return m
+
+
+def _np(t):
+    return t.detach().cpu().numpy()
+
+
+RUNS = {
+    # name: (workload (weights, k, phi, bias), batch sizes, seed)
+    "switch_small": (Workload("q_switch", T=0, E=8, k=1, d=256, d_ff=512, renorm=0, phi=0.8,
+                              bias="normal"), (512, 384, 640), 3),
+    "f32_k3_ragged": (Workload("q_f32", T=0, E=5, k=3, d=40, d_ff=24, dtype="f32", phi=0.6,
+                               bias="normal"), (77, 50, 93), 4),
+    "e32_k8_shared_zipf": (Workload("q_e32", T=0, E=32, k=8, d=128, d_ff=64, d_ff_shared=96,
+                                    phi=0.5, bias="zipf"), (300, 200, 257), 5),
+    "chunked_permute": (Workload("q_chunk", T=0, E=16, k=2, d=64, d_ff=64, phi=0.7,
+                                 bias="normal"), (3000, 2600), 6),
+}
+
+
+def _weights(w, seed):
+    return make_inputs(w.with_(T=1), seed=seed)
+
+
+def _x(w, T, seed):
+    g = torch.Generator(device="cpu")
+    g.manual_seed(seed)
+    return torch.randn(T, w.d, generator=g, dtype=torch.float32).to(w.torch_dtype)
+
+
+def _compare_call(w, name, b, got, ref, Q):
+    y, y_late, qo, rt = got
+    pos = _np(rt["route_pos"])
+    assert np.array_equal(pos, ref["pos"]), f"{name} call {b}: arrival positions"
+    assert np.array_equal(_np(rt["counts"]), ref["counts"])
+    assert np.array_equal(_np(rt["expert_ids"]), ref["ids"])
+    assert np.max(np.abs(_np(rt["gates"]) - ref["gates"]), initial=0.0) <= 1e-6
+    ro = ref["out"]
+    assert qo["ids"].shape[0] == ro["ids"].shape[0], f"{name} call {b}: queue length"
+    assert np.array_equal(_np(qo["ids"]), ro["ids"])
+    assert np.array_equal(_np(qo["tags"]), ro["tags"])
+    # a gate travels with its route: queued gates are the router's, bit for bit
+    # on each side; across sides they agree to the routing tolerance
+    assert np.max(np.abs(_np(qo["gates"]) - ro["gates"]), initial=0.0) <= 1e-6
+    assert np.array_equal(bits(qo["x"]), oracle.as_array(ro["x"])[0].view(bits(qo["x"]).dtype))
+    check_y(y, ref["y"], w.dtype, f"{name} call {b} y")
+    if Q:
+        check_y(y_late, ref["y_late"], w.dtype, f"{name} call {b} y_late")
+
+
+@pytest.mark.parametrize("name", list(RUNS))
+def test_layer_forward_queued_run(moe, name):
+    w, sizes, seed = RUNS[name]
+    wts = _weights(w, seed)
+    dev = {k: (None if v is None else v.cuda()) for k, v in wts.items()}
+    shared = w.d_ff_shared > 0
+    q_gpu = None
+    q_ref = None
+    waited = 0
+    for b, T in enumerate(list(sizes) + [0]):
+        last = T == 0
+        phi = 0.0 if last else w.phi
+        wb = w.with_(T=T, phi=phi)
+        s = moe.shape_of(wb)
+        x = _x(w, T, 1000 * seed + b)
+        Q = 0 if q_gpu is None else int(q_gpu["ids"].shape[0])
+        say(f"[queue] {name} call {b}: T={T} Q={Q} phi={phi}")
+        got = moe.layer_forward_queued(
+            s, x.cuda(), dev["w_router"], dev["b_router"], dev["w_gate"], dev["w_up"],
+            dev["w_down"], dev["ws_gate"], dev["ws_up"], dev["ws_down"], queue=q_gpu,
+            tag_base=1000 * b, return_routing=True)
+        torch.cuda.synchronize()
+        ref = oracle.layer_forward_queued(
+            x, wts["w_router"], wts["b_router"], wts["w_gate"], wts["w_up"], wts["w_down"], w.k,
+            w.renorm, phi, queue=q_ref, tag_base=1000 * b,
+            ws_gate=wts["ws_gate"] if shared else None, ws_up=wts["ws_up"] if shared else None,
+            ws_down=wts["ws_down"] if shared else None)
+        _compare_call(w, name, b, got, ref, Q)
+        q_gpu = got[2]
+        q_ref = ref["out"]
+        waited = max(waited, int(q_gpu["ids"].shape[0]))
+        say(f"   {name} call {b}: {int(q_gpu['ids'].shape[0])} routes wait")
+    assert waited > 0, "the run never overflowed"
+    assert int(q_gpu["ids"].shape[0]) == 0
+
+
+def test_layer_forward_queued_switch_full_size(moe):
+    """The Switch top-1 shape at phi = 1.25 (T = 4096, E = 8, d = 768,
+    d_ff = 3072) with the queue of one earlier batch: arrival positions, the
+    outgoing queue and its rows in full, bit for bit (the expert outputs at
+    this size are covered by the layer tests of the other policies)."""
+    w = WORKLOADS["switch_phi125"]
+    wts = make_inputs(w, seed=0)
+    dev = {k: (None if v is None else v.cuda()) for k, v in wts.items()}
+    s = moe.shape_of(w)
+    q_gpu = None
+    q_ids = np.zeros(0, np.int32)
+    q_rows = np.zeros((0, w.d), np.int16)   # host copy of the waiting rows (oracle side)
+    for b in range(2):
+        x = wts["x"] if b == 0 else _x(w, w.T, 77)
+        say(f"[queue] switch_phi125 call {b}")
+        y, y_late, qo, rt = moe.layer_forward_queued(
+            s, x.cuda(), dev["w_router"], dev["b_router"], dev["w_gate"], dev["w_up"],
+            dev["w_down"], queue=q_gpu, tag_base=10000 * b, return_routing=True)
+        torch.cuda.synchronize()
+        L = oracle.router_logits(x, wts["w_router"], wts["b_router"])
+        ids, gates = oracle.topk_gates(L, w.k, w.renorm)
+        C = oracle.capacity(w.T, w.E, w.k, w.phi)
+        ref = oracle.dispatch_queue(ids, w.E, C, q_ids)
+        assert np.array_equal(_np(rt["route_pos"]), ref["pos"])
+        assert np.array_equal(_np(rt["counts"]), ref["counts"])
+        Q = q_ids.shape[0]
+        oa = ref["out_arrival"]
+        assert qo["ids"].shape[0] == oa.shape[0] > 0
+        arr_ids = np.concatenate([q_ids, ids.reshape(-1)])
+        assert np.array_equal(_np(qo["ids"]), arr_ids[oa])
+        # rows: a new route's token row, a queued route's carried row
+        src_rows = np.concatenate([bits(x), q_rows])
+        a = oa.astype(np.int64)
+        rows = src_rows[np.where(a < Q, w.T + a, (a - Q) // w.k)]
+        assert np.array_equal(bits(qo["x"]), rows)
+        say(f"   call {b}: {oa.shape[0]} routes wait, {Q} arrived queued")
+        q_gpu, q_ids, q_rows = qo, arr_ids[oa], rows
