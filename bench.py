@@ -216,6 +216,9 @@ def main():
     ap.add_argument("--choice", action="store_true",
                     help="expert-choice routing (each expert keeps its top-C tokens; full softmax "
                          "gates, capacity factor 1 when the workload has none)")
+    ap.add_argument("--queue", action="store_true",
+                    help="queue-to-the-next-micro-batch overflow policy: each step processes the "
+                         "batch plus the routes one earlier batch left waiting")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB")
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
     ap.add_argument("--traffic-out", default=None)
@@ -254,8 +257,31 @@ def main():
     y = torch.empty(w.T, w.d, dtype=w.torch_dtype, device=dev)
     stream = torch.cuda.current_stream()
 
+    # queue policy: the routes one earlier batch (the same tokens) left waiting
+    # arrive with every step's batch
+    queue = qbufs = None
+    if args.queue:
+        _, _, queue = moe.layer_forward_queued(s, d["x"], d["w_router"], d["b_router"],
+                                               d["w_gate"], d["w_up"], d["w_down"], d["ws_gate"],
+                                               d["ws_up"], d["ws_down"])
+        qbufs = moe.queue_buffers(s, queue["ids"].shape[0], dev)
+
+    def timed(p, events):
+        if args.queue:
+            moe.layer_forward_queued_timed(s, p["x"], p["w_router"], p["b_router"], p["w_gate"],
+                                           p["w_up"], p["w_down"], p["ws_gate"], p["ws_up"],
+                                           p["ws_down"], queue, qbufs, events, stream=stream)
+            return
+        moe.layer_forward_timed(s, p["x"], p["w_router"], p["b_router"], p["w_gate"], p["w_up"],
+                                p["w_down"], p["ws_gate"], p["ws_up"], p["ws_down"], y, ws,
+                                events, stream=stream, padded=args.padded, reroute=args.reroute,
+                                choice=args.choice)
+
     def step(i):
         p = sets[i % nsets]
+        if args.queue:
+            timed(p, [None] * 7)
+            return
         if args.choice:
             moe.layer_forward_expert_choice(s, p["x"], p["w_router"], p["b_router"], p["w_gate"],
                                             p["w_up"], p["w_down"], p["ws_gate"], p["ws_up"],
@@ -281,6 +307,15 @@ def main():
         kept = torch.bincount(rt_r["expert_ids"].cpu().flatten().long()[seated], minlength=w.E)
     if args.choice:  # every expert holds exactly Ce rows
         kept = torch.full((w.E,), moe.choice_capacity(s), dtype=torch.long)
+    n_wait = None
+    if args.queue:  # seated arrivals per expert (queued routes first)
+        _, _, q_out, rt_q = moe.layer_forward_queued(
+            s, d["x"], d["w_router"], d["b_router"], d["w_gate"], d["w_up"], d["w_down"],
+            d["ws_gate"], d["ws_up"], d["ws_down"], queue=queue, return_routing=True)
+        arr_ids = torch.cat([queue["ids"], rt_q["expert_ids"].flatten()]).cpu().long()
+        seated = rt_q["route_pos"].cpu() >= 0
+        kept = torch.bincount(arr_ids[seated], minlength=w.E)
+        n_wait = int(q_out["ids"].shape[0])
     kept_rows = int(kept.sum())
     active = int((kept > 0).sum())
 
@@ -308,12 +343,7 @@ def main():
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(K):
-        p = sets[i % nsets]
-        moe.layer_forward_timed(s, p["x"], p["w_router"], p["b_router"], p["w_gate"], p["w_up"],
-                                p["w_down"], p["ws_gate"], p["ws_up"], p["ws_down"], y, ws,
-                                [None, None, g1_ev[2 * i], g1_ev[2 * i + 1], None, None, None],
-                                stream=stream, padded=args.padded, reroute=args.reroute,
-                                choice=args.choice)
+        timed(sets[i % nsets], [None, None, g1_ev[2 * i], g1_ev[2 * i + 1], None, None, None])
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms = (t1 - t0) * 1e3 / K
@@ -330,12 +360,7 @@ def main():
         evs = new_events(K * 7)
         torch.cuda.synchronize()
         for i in range(K):
-            p = sets[i % nsets]
-            moe.layer_forward_timed(s, p["x"], p["w_router"], p["b_router"], p["w_gate"],
-                                    p["w_up"], p["w_down"], p["ws_gate"], p["ws_up"],
-                                    p["ws_down"], y, ws, evs[7 * i:7 * i + 7], stream=stream,
-                                    padded=args.padded, reroute=args.reroute,
-                                    choice=args.choice)
+            timed(sets[i % nsets], evs[7 * i:7 * i + 7])
         torch.cuda.synchronize()
         acc = [0.0] * 6
         per_step = []
@@ -358,12 +383,7 @@ def main():
         torch.cuda.synchronize()
         tw0 = time.perf_counter()
         for i in range(K):
-            p = sets[0]
-            moe.layer_forward_timed(s, p["x"], p["w_router"], p["b_router"], p["w_gate"],
-                                    p["w_up"], p["w_down"], p["ws_gate"], p["ws_up"],
-                                    p["ws_down"], y, ws, [None] * 7, stream=stream,
-                                    padded=args.padded, reroute=args.reroute,
-                                    choice=args.choice)
+            timed(sets[0], [None] * 7)
         torch.cuda.synchronize()
         warm_ms = (time.perf_counter() - tw0) * 1e3 / K
 
@@ -421,7 +441,7 @@ def main():
         roof["us_per_launch"] = round(g1_us, 2)
         roof["algorithmic_flops"] = flops
         roof["algorithmic_bytes"] = byts
-        roof["traffic"] = (None if (args.padded or args.reroute or args.choice)
+        roof["traffic"] = (None if (args.padded or args.reroute or args.choice or args.queue)
                            else traffic_from_profile(w.name))
 
     layer_roof = None
@@ -457,11 +477,15 @@ def main():
                    "d_ff_shared": w.d_ff_shared, "phi": w.phi, "renormalize": w.renorm,
                    "kept_routes": kept_rows, "weight_sets": nsets,
                    "layout": "padded [E, C, d]" if args.padded else "packed",
-                   "overflow": "reroute" if args.reroute else "drop",
+                   "overflow": ("reroute" if args.reroute else "queue to the next micro-batch"
+                                if args.queue else "drop"),
+                   "queued_in": int(queue["ids"].shape[0]) if args.queue else None,
+                   "queued_out": n_wait,
                    "routing": "expert choice" if args.choice else "token choice (top-k)",
                    "padded_rows": (w.E * C) if (args.padded and C > 0) else None,
                    "capacity": C if C >= 0 else None,
-                   "dropped_routes": (w.T * w.k - kept_rows) if not args.choice else None,
+                   "dropped_routes": ((w.T * w.k - kept_rows) if not (args.choice or args.queue)
+                                      else None),
                    "fill": round(kept_rows / (w.E * C), 4) if C > 0 else None,
                    "parallelism": "single GPU"},
         "roofline": roof,
