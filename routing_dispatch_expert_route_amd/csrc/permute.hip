@@ -494,68 +494,74 @@ __global__ __launch_bounds__(256) void reroute_rows_kernel(const int32_t* __rest
   row_token[p] = r / k;
 }
 
-// Top-1 routing (k = 1) in parallel.  A token then holds no other expert, so
-// the greedy above is a serial dictatorship: the dropped routes choose in
-// arrival order, and every expert in effect ranks routes by that one order.
-// When all experts share one priority order, deferred acceptance with the
-// routes proposing ends in exactly the assignment of the serial dictatorship
-// in that order, and each of its rounds is parallel: every unplaced route
-// proposes to its next preferred expert among those with a free seat after
-// the drop policy, each expert keeps the earliest routes it holds or was
-// proposed, up to its free seats, and rejects the rest, and the rejected
-// routes move one rank on.  It ends after a round without proposals (each
-// proposal moves a route's rank or places it, so that round comes).  Seats
-// follow arrival order among an expert's accepted routes, as in the walk.
-// One block of 1024 threads; the state sits in dynamic LDS, sized for R
-// routes (the bound on the dropped ones), W = ceil(R / 32):
-//   held  [E][W] uint32   bit j: dropped route j is held by / proposed to e
-//   drop  [R] uint16      route index of dropped route j (arrival order)
-//   pref  [R][E] uint8    expert at each preference rank of route j, or
-//                         kNoExpert where that expert had no free seat (after
-//                         the rounds the area holds [E][W] int seat prefixes)
-//   next  [R] uint8       next rank route j tries
-//   cur   [R] uint8       expert route j is proposed to or held by, or kNoExpert
+// The same result in parallel rounds.  A token's dropped routes are
+// consecutive in arrival order and must take distinct experts, so the walk is
+// a serial dictatorship over tokens: in token order, each token with n_t
+// dropped routes takes its n_t best experts that still have a seat (its own
+// experts excluded), its i-th dropped route the i-th best of them.  When every
+// expert ranks tokens by one common priority, deferred acceptance with the
+// tokens proposing ends in exactly that assignment (a standard property of
+// matching under a common priority), and each of its rounds is parallel:
+//   1. every token drops the experts that rejected it, then proposes along its
+//      preference list (experts it holds originally and experts without a
+//      free seat after the drop policy are skipped) until it holds n_t
+//      experts again or the list ends;
+//   2. every expert keeps the earliest tokens it holds, up to its free seats,
+//      and rejects the rest.
+// It ends after a round without proposals (each proposal moves a token's
+// list pointer, so that round comes).  Seats follow token order among an
+// expert's accepted routes, as in the walk.  One block of 1024 threads; the
+// state sits in a fixed LDS arena, laid out for T tokens (the bound on the
+// tokens with drops), W = ceil(T / 32):
+//   held  [E][W] uint32   bit a: token a holds (or is proposed to) expert e
+//   pre   [E][W] int32    exclusive prefix of held's word popcounts (seats)
+//   hold  [T] uint64      experts token a holds
+//   tok   [T] uint16      token index of token a (token order)
+//   need  [T] uint8       its dropped routes n_t
+//   next  [T] uint8       next position of its preference list
+//   pref  [T][E] uint8    its experts by preference, kNoExpert where skipped
 constexpr int kDaThreads = 1024;
 constexpr int kDaWaves = kDaThreads / kWave;
 constexpr uint8_t kNoExpert = 0xFF;
-constexpr long kDaMaxLds = 60L * 1024;  // with the static arrays, under 64 KB
-constexpr int kDaMaxR = 65535;          // route indices fit uint16
+constexpr long kDaArena = 144L * 1024;
 
 struct DaLayout {
-  long held, drop, pref, next, cur, bytes;
+  long held, pre, hold, tok, need, next, pref, bytes;
 };
-__host__ __device__ inline DaLayout da_layout(int R, int E) {
-  const long W = (R + 31) / 32;
+__host__ __device__ inline DaLayout da_layout(int T, int E) {
+  const long W = (T + 31) / 32;
   DaLayout L;
   L.held = 0;
-  L.drop = (long)E * W * 4;
-  L.pref = L.drop + ((2L * R + 3) & ~3L);
-  const long pref_bytes = (long)R * E > (long)E * W * 4 ? (long)R * E : (long)E * W * 4;
-  L.next = L.pref + ((pref_bytes + 3) & ~3L);
-  L.cur = L.next + R;
-  L.bytes = L.cur + R;
+  L.pre = L.held + (long)E * W * 4;
+  L.hold = L.pre + (long)E * W * 4;
+  L.tok = L.hold + 8L * T;
+  L.need = L.tok + ((2L * T + 3) & ~3L);
+  L.next = L.need + T;
+  L.pref = L.next + T;
+  L.bytes = L.pref + (long)T * E;
   return L;
 }
 
 __global__ __launch_bounds__(kDaThreads) void reroute_da_kernel(
     const uint8_t* __restrict__ rank, const int32_t* __restrict__ ids_in,
     const int32_t* __restrict__ route_pos0, const int32_t* __restrict__ offsets0,
-    const int32_t* __restrict__ kept, int R, int E, int C, int32_t* __restrict__ ids_out,
+    const int32_t* __restrict__ kept, int T, int k, int E, int C, int32_t* __restrict__ ids_out,
     int32_t* __restrict__ slot, int32_t* __restrict__ offsets) {
-  extern __shared__ __attribute__((aligned(16))) uint32_t s_dyn[];
+  __shared__ __attribute__((aligned(16))) uint8_t arena[kDaArena];
   __shared__ int s_kept[kRerouteMaxE], s_free[kRerouteMaxE], s_new[kRerouteMaxE],
       s_fill[kRerouteMaxE];
   __shared__ int s_wsum[kDaWaves];
   const int tid = threadIdx.x, lane = tid & (kWave - 1);
   const int wv = __builtin_amdgcn_readfirstlane(tid / kWave);
-  const int W = (R + 31) / 32;
-  const DaLayout L = da_layout(R, E);
-  uint8_t* base = reinterpret_cast<uint8_t*>(s_dyn);
-  uint32_t* held = reinterpret_cast<uint32_t*>(base + L.held);
-  uint16_t* drop = reinterpret_cast<uint16_t*>(base + L.drop);
-  uint8_t* pref = base + L.pref;
-  uint8_t* next = base + L.next;
-  uint8_t* cur = base + L.cur;
+  const int W = (T + 31) / 32;
+  const DaLayout L = da_layout(T, E);
+  uint32_t* held = reinterpret_cast<uint32_t*>(arena + L.held);
+  int32_t* pre = reinterpret_cast<int32_t*>(arena + L.pre);
+  uint64_t* hold = reinterpret_cast<uint64_t*>(arena + L.hold);
+  uint16_t* tok = reinterpret_cast<uint16_t*>(arena + L.tok);
+  uint8_t* need = arena + L.need;
+  uint8_t* next = arena + L.next;
+  uint8_t* pref = arena + L.pref;
 
   if (tid < E) {
     const int kp = kept[tid];
@@ -565,80 +571,111 @@ __global__ __launch_bounds__(kDaThreads) void reroute_da_kernel(
   }
   for (int i = tid; i < E * W; i += kDaThreads) held[i] = 0;
 
-  // dropped routes in arrival order (each thread a run of cpt routes; block
-  // scan of the run counts); kept routes keep expert and seat
-  const int cpt = (R + kDaThreads - 1) / kDaThreads;  // <= 64
-  const int r0 = tid * cpt, r1 = min(R, r0 + cpt);
-  int nd = 0;
-  uint64_t dmask = 0;
-  for (int r = r0; r < r1; ++r) {
-    const int p = route_pos0[r];
-    if (p < 0) {
-      dmask |= 1ull << (r - r0);
-      ++nd;
-    } else {
-      const int e = ids_in[r];
-      ids_out[r] = e;
-      slot[r] = p - offsets0[e];
+  // tokens with dropped routes in token order (each thread a run of cpt
+  // tokens; block scan of the run counts); kept routes keep expert and seat
+  const int cpt = (T + kDaThreads - 1) / kDaThreads;  // <= 64 (T <= 65535)
+  const int t0 = tid * cpt, t1 = min(T, t0 + cpt);
+  int na = 0;
+  uint64_t amask = 0;
+  for (int t = t0; t < t1; ++t) {
+    int nd = 0;
+    for (int j = 0; j < k; ++j) {
+      const int r = t * k + j;
+      const int p = route_pos0[r];
+      if (p < 0) {
+        ++nd;
+      } else {
+        const int e = ids_in[r];
+        ids_out[r] = e;
+        slot[r] = p - offsets0[e];
+      }
+    }
+    if (nd) {
+      amask |= 1ull << (t - t0);
+      ++na;
     }
   }
-  const int incl = wave_incl_scan(nd, lane);
+  const int incl = wave_incl_scan(na, lane);
   if (lane == kWave - 1) s_wsum[wv] = incl;
   __syncthreads();
-  int at = incl - nd, rd = 0;
+  int at = incl - na, an = 0;
   for (int w = 0; w < kDaWaves; ++w) {
     const int s = s_wsum[w];
     at += w < wv ? s : 0;
-    rd += s;
+    an += s;
   }
-  const int Rd = __builtin_amdgcn_readfirstlane(rd);
-  while (dmask) {
-    drop[at++] = (uint16_t)(r0 + __builtin_ctzll(dmask));
-    dmask &= dmask - 1;
-  }
-  __syncthreads();
-
-  // preference lists: pref[j][rank of e] = e when e has a free seat
-  for (int i = tid; i < Rd * E; i += kDaThreads) {
-    const int j = i / E, e = i - j * E;
-    const int rk = rank[(size_t)drop[j] * kRerouteMaxE + e];
-    pref[j * E + rk] = s_free[e] > 0 ? (uint8_t)e : kNoExpert;
-  }
-  for (int j = tid; j < Rd; j += kDaThreads) {
-    next[j] = 0;
-    cur[j] = kNoExpert;
+  const int A = __builtin_amdgcn_readfirstlane(an);
+  while (amask) {
+    tok[at++] = (uint16_t)(t0 + __builtin_ctzll(amask));
+    amask &= amask - 1;
   }
   __syncthreads();
 
-  // The round loop keeps every branch around its barriers wave-uniform: the
-  // per-route loops run the same trip count on every lane (a lane past Rd
-  // idles in the body), and the exit reads the block-wide OR as a scalar.
-  // With a per-lane loop bound (j = tid; j < Rd) the compiler may route the
-  // lanes that have no route straight from one round's barriers to the
-  // next's, and a wave holding both kinds of lane then meets the barriers
-  // out of step with the others.
+  // preference lists: one token per thread.  The rank row of the token's
+  // first dropped route (every route of a token shares the logits) places
+  // each expert; its own experts and the experts without a free seat are
+  // skipped.
+  for (int a0 = 0; a0 < A; a0 += kDaThreads) {
+    const int a = a0 + tid;
+    if (a >= A) continue;
+    const int t = tok[a];
+    uint64_t own = 0;
+    int nd = 0, rf = -1;
+    for (int j = 0; j < k; ++j) {
+      const int r = t * k + j;
+      own |= 1ull << ids_in[r];
+      if (route_pos0[r] < 0) {
+        if (rf < 0) rf = r;
+        ++nd;
+      }
+    }
+    const uint8_t* rr = rank + (size_t)rf * kRerouteMaxE;
+    uint8_t* pa = pref + (long)a * E;
+    for (int e = 0; e < E; ++e)
+      pa[rr[e]] = (s_free[e] > 0 && !((own >> e) & 1)) ? (uint8_t)e : kNoExpert;
+    need[a] = (uint8_t)nd;
+    next[a] = 0;
+    hold[a] = 0;
+  }
+  __syncthreads();
+
+  // Every branch around the round's barriers is wave-uniform: the per-token
+  // loops run the same trip count on every lane (a lane past A idles in the
+  // body), and the exit reads the block-wide OR as a scalar.  With per-lane
+  // loop bounds (a = tid; a < A) the compiler may route the lanes that have
+  // no token straight from one round's barriers to the next's, and a wave
+  // holding both kinds of lane then meets the barriers out of step.
+  const int wpl = (W + kWave - 1) / kWave;
   for (;;) {
-    // proposals of the unplaced routes
+    // rejections of the last round, then proposals up to n_t held experts
     int proposed = 0;
-    for (int j0 = 0; j0 < Rd; j0 += kDaThreads) {
-      const int j = j0 + tid;
-      if (j >= Rd || cur[j] != kNoExpert) continue;
-      const uint8_t* pj = pref + j * E;
-      int p = next[j];
-      while (p < E && pj[p] == kNoExpert) ++p;
-      next[j] = (uint8_t)p;
-      if (p < E) {
-        const int e = pj[p];
-        atomicOr(&held[e * W + (j >> 5)], 1u << (j & 31));
-        cur[j] = (uint8_t)e;
+    for (int a0 = 0; a0 < A; a0 += kDaThreads) {
+      const int a = a0 + tid;
+      if (a >= A) continue;
+      const int word = a >> 5;
+      const uint32_t bit = 1u << (a & 31);
+      uint64_t h = hold[a];
+      for (uint64_t m = h; m; m &= m - 1) {
+        const int e = __builtin_ctzll(m);
+        if (!(held[e * W + word] & bit)) h &= ~(1ull << e);
+      }
+      const int nd = need[a];
+      int p = next[a];
+      const uint8_t* pa = pref + (long)a * E;
+      while (__popcll(h) < nd && p < E) {
+        const int e = pa[p++];
+        if (e == kNoExpert) continue;
+        atomicOr(&held[e * W + word], bit);
+        h |= 1ull << e;
         s_new[e] = 1;
         proposed = 1;
       }
+      hold[a] = h;
+      next[a] = (uint8_t)p;
     }
     if (!__builtin_amdgcn_readfirstlane(__syncthreads_or(proposed))) break;
-    // each expert with proposals keeps its earliest s_free[e] routes; lane i
+    // each expert with proposals keeps its earliest s_free[e] tokens; lane i
     // of the expert's wave owns words [i*wpl, (i+1)*wpl)
-    const int wpl = (W + kWave - 1) / kWave;
     for (int e = wv; e < E; e += kDaWaves) {
       if (!__builtin_amdgcn_readfirstlane(s_new[e])) continue;
       uint32_t* row = held + e * W;
@@ -670,48 +707,52 @@ __global__ __launch_bounds__(kDaThreads) void reroute_da_kernel(
       if (lane == 0) s_new[e] = 0;
     }
     __syncthreads();
-    // rejected routes (their bit cleared) move one rank on
-    for (int j0 = 0; j0 < Rd; j0 += kDaThreads) {
-      const int j = j0 + tid;
-      if (j >= Rd) continue;
-      const int e = cur[j];
-      if (e != kNoExpert && !((held[e * W + (j >> 5)] >> (j & 31)) & 1u)) {
-        cur[j] = kNoExpert;
-        next[j] = (uint8_t)(next[j] + 1);
-      }
-    }
   }
 
-  // seats: per expert, the exclusive prefix of its words' popcounts (into
-  // the preference area, no longer read), then each route's rank among the
-  // accepted ones
-  int32_t* pre = reinterpret_cast<int32_t*>(pref);
-  {
-    const int wpl = (W + kWave - 1) / kWave;
-    for (int e = wv; e < E; e += kDaWaves) {
-      const uint32_t* row = held + e * W;
-      const int w0 = lane * wpl, w1 = min(W, w0 + wpl);
-      int c = 0;
-      for (int w = w0; w < w1; ++w) c += __popc(row[w]);
-      const int inc = wave_incl_scan(c, lane);
-      int before = inc - c;
-      for (int w = w0; w < w1; ++w) {
-        pre[e * W + w] = before;
-        before += __popc(row[w]);
-      }
-      if (lane == kWave - 1) s_fill[e] = s_kept[e] + inc;
+  // seats: per expert, the exclusive prefix of its words' popcounts; then
+  // each token's i-th dropped route takes the i-th best expert it holds
+  for (int e = wv; e < E; e += kDaWaves) {
+    const uint32_t* row = held + e * W;
+    const int w0 = lane * wpl, w1 = min(W, w0 + wpl);
+    int c = 0;
+    for (int w = w0; w < w1; ++w) c += __popc(row[w]);
+    const int inc = wave_incl_scan(c, lane);
+    int before = inc - c;
+    for (int w = w0; w < w1; ++w) {
+      pre[e * W + w] = before;
+      before += __popc(row[w]);
     }
+    if (lane == kWave - 1) s_fill[e] = s_kept[e] + inc;
   }
   __syncthreads();
-  for (int j = tid; j < Rd; j += kDaThreads) {
-    const int r = drop[j], e = cur[j];
-    if (e == kNoExpert) {  // no expert with room: dropped after all
-      ids_out[r] = ids_in[r];
-      slot[r] = -1;
-    } else {
-      const int w = j >> 5;
-      ids_out[r] = e;
-      slot[r] = s_kept[e] + pre[e * W + w] + __popc(held[e * W + w] & ((1u << (j & 31)) - 1u));
+  for (int a0 = 0; a0 < A; a0 += kDaThreads) {
+    const int a = a0 + tid;
+    if (a >= A) continue;
+    const int t = tok[a];
+    const int word = a >> 5;
+    const uint32_t below = (1u << (a & 31)) - 1u;
+    uint64_t h = hold[a];
+    const uint8_t* pa = pref + (long)a * E;
+    int p = 0;
+    for (int j = 0; j < k; ++j) {
+      const int r = t * k + j;
+      if (route_pos0[r] >= 0) continue;
+      int e = -1;
+      while (h && p < E) {  // the next best held expert
+        const int c = pa[p++];
+        if (c != kNoExpert && ((h >> c) & 1)) {
+          e = c;
+          h &= ~(1ull << c);
+          break;
+        }
+      }
+      if (e < 0) {  // no expert with room: dropped after all
+        ids_out[r] = ids_in[r];
+        slot[r] = -1;
+      } else {
+        ids_out[r] = e;
+        slot[r] = s_kept[e] + pre[e * W + word] + __popc(held[e * W + word] & below);
+      }
     }
   }
   if (wv == 0) {
@@ -735,10 +776,9 @@ hipError_t launch_reroute(const float* logits, const int32_t* ids_in, const int3
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
   }
-  const long da_bytes = da_layout(R, E).bytes;
-  if (k == 1 && R <= kDaMaxR && da_bytes <= kDaMaxLds) {
-    hipLaunchKernelGGL(reroute_da_kernel, dim3(1), dim3(kDaThreads), (unsigned)da_bytes, st, pref,
-                       ids_in, route_pos0, offsets0, kept, R, E, C, ids_out, slot, offsets);
+  if (da_layout(T, E).bytes <= kDaArena) {
+    hipLaunchKernelGGL(reroute_da_kernel, dim3(1), dim3(kDaThreads), 0, st, pref, ids_in,
+                       route_pos0, offsets0, kept, T, k, E, C, ids_out, slot, offsets);
   } else {
     hipLaunchKernelGGL(reroute_kernel, dim3(1), dim3(kWave), 0, st, pref, ids_in, route_pos0,
                        offsets0, kept, T, k, E, C, ids_out, slot, offsets);

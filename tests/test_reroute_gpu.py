@@ -36,13 +36,14 @@ CASES = {
                              renorm=0, phi=1.0, bias="zipf"),
     "granite_tight": WORKLOADS["granite_1412"].with_(name="granite_tight", phi=0.75, bias="normal"),
     "e64_k8_zipf": Workload("e64_k8", T=600, E=64, k=8, d=64, d_ff=32, phi=0.9, bias="zipf"),
-    # top-1 shapes on either side of the parallel (deferred acceptance)
-    # kernel's LDS bound: 700 routes over 64 experts fit, 6000 over 8 do not
-    # and take the sequential walk
+    # shapes on either side of the parallel (deferred acceptance) kernel's
+    # LDS bound (about T * (E + 12) bytes): the ones above fit, 8000 tokens
+    # over 8 experts and 3000 over 32 do not and take the sequential walk
     "k1_e64_zipf": Workload("k1_e64", T=700, E=64, k=1, d=64, d_ff=32, renorm=0, phi=0.5,
                             bias="zipf"),
-    "k1_walk": Workload("k1_walk", T=6000, E=8, k=1, d=64, d_ff=32, renorm=0, phi=1.0,
+    "k1_walk": Workload("k1_walk", T=8000, E=8, k=1, d=64, d_ff=32, renorm=0, phi=1.0,
                         bias="normal"),
+    "k8_walk": Workload("k8_walk", T=3000, E=32, k=8, d=64, d_ff=32, phi=0.75, bias="normal"),
 }
 
 
@@ -103,16 +104,17 @@ def test_layer_forward_reroute_parity(moe, name):
     say(f"   {name}: err {errs[0]:.3e} / {errs[1]:.3e}")
 
 
-@pytest.mark.parametrize("T,E,phi", [(2048, 16, 0.5), (700, 64, 0.4), (6000, 8, 0.5)])
-def test_permute_reroute_common_order(moe, T, E, phi):
+@pytest.mark.parametrize("T,E,k,phi", [(2048, 16, 1, 0.5), (700, 64, 1, 0.4), (8000, 8, 1, 0.5),
+                                       (1024, 16, 4, 0.5), (600, 64, 8, 0.3)])
+def test_permute_reroute_common_order(moe, T, E, k, phi):
     """Every token has the same preference order (identical rows of x), so the
     dropped routes fill the experts one after another in that order: the
-    longest chain of rejections the top-1 parallel kernel can meet (one round
-    per expert), and, at T=6000, the same inputs through the walk."""
-    w = Workload("common_order", T=T, E=E, k=1, d=64, d_ff=32, renorm=0, phi=phi, bias="zipf")
+    longest chain of rejections the parallel kernel can meet (about one round
+    per expert), and, at T=8000, the same inputs through the walk."""
+    w = Workload("common_order", T=T, E=E, k=k, d=64, d_ff=32, renorm=0, phi=phi, bias="zipf")
     inp = make_inputs(w, seed=5)
     inp["x"] = inp["x"][:1].repeat(T, 1).contiguous()
-    say(f"[permute reroute common order] T={T} E={E} phi={phi}")
+    say(f"[permute reroute common order] T={T} E={E} k={k} phi={phi}")
     d = to_dev(inp)
     s = moe.shape_of(w)
     ids, _, logits = moe.route(s, d["x"], d["w_router"], d["b_router"], want_logits=True)
@@ -124,5 +126,5 @@ def test_permute_reroute_common_order(moe, T, E, phi):
     assert np.array_equal(_np(out["route_pos"]), ref["route_pos"])
     n = int(ref["offsets"][-1])
     assert np.array_equal(_np(out["row_token"])[:n], ref["row_token"])
-    C = oracle.capacity(T, E, 1, phi)
-    assert n == min(T, C * E)  # every expert full, or every route seated
+    C = oracle.capacity(T, E, k, phi)
+    assert n == min(T * k, C * E)  # every expert full, or every route seated
