@@ -345,8 +345,9 @@ hipError_t launch_padded(const void* x, const int32_t* ids, const int32_t* route
 // ones.  reroute_da_kernel below reaches the same result in parallel rounds
 // when its state fits LDS; beyond that one wave walks the dropped routes one
 // by one.  Both read every dropped route's rank of each expert (one byte
-// each), written first by a parallel kernel.  The walk stages a 64-route chunk's rank rows in LDS (the next
-// chunk's are loaded while this one is walked); for a route, lane e reads
+// each), written first by a parallel kernel.  The walk stages a 64-route
+// chunk's rank rows in LDS (the next chunk's are loaded while this one is
+// walked); for a route, lane e reads
 // its expert's rank and the choice is the lowest rank among the lanes with
 // room that the token does not hold -- six ballots over the rank bits, no
 // branches; lane e keeps expert e's seat count (E <= 64).
