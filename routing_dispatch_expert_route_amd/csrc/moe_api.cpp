@@ -491,7 +491,8 @@ static int experts_and_combine(const moe_shape* s, const Layout& L, const moe::G
   void* h = at<void>(ws, L.h);
   void* yp = at<void>(ws, L.yp);
   auto mark = [&](int i) {
-    if (ev && ev[i]) hipEventRecord(ev[i], stream);
+    // a stage marker: a failed record loses a timing, never a result
+    if (ev && ev[i]) (void)hipEventRecord(ev[i], stream);
   };
   mark(2);
   hipError_t e = moe::launch_gemm_swiglu(pl, A, a_rows, a_nrows, w_gate, w_up, dff, d, h, stream);
@@ -579,7 +580,8 @@ static int layer_forward_impl(const moe_shape* s, const void* x, const void* w_r
   int32_t* row_token = at<int32_t>(ws, L.row_token);
 
   auto mark = [&](int i) {
-    if (ev && ev[i]) hipEventRecord(ev[i], stream);
+    // a stage marker: a failed record loses a timing, never a result
+    if (ev && ev[i]) (void)hipEventRecord(ev[i], stream);
   };
   mark(0);
   if (choice) {
@@ -743,7 +745,8 @@ static int layer_forward_queued_impl(
   void* rows = at<void>(ws, L.aall);
   int32_t* misc = at<int32_t>(ws, L.qmisc);  // kept1, off1[2]
   auto mark = [&](int i) {
-    if (ev && ev[i]) hipEventRecord(ev[i], stream);
+    // a stage marker: a failed record loses a timing, never a result
+    if (ev && ev[i]) (void)hipEventRecord(ev[i], stream);
   };
   mark(0);
   // arrivals: the queued experts, then this batch's router choices
