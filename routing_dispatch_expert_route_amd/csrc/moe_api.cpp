@@ -193,8 +193,8 @@ Layout layout_of(const moe_shape* s, int64_t Q = -1) {
   L.row_token = take(Rbig * sizeof(int32_t));
   L.h = take(Rbig * s->d_ff * eb);
   L.yp = take(Rbig * s->d * eb);
-  L.splits = moe::gemm_down_splits(queued ? queue_plan(s, Q, nullptr) : routed_plan(s, nullptr, false),
-                                   (int)s->d, (int)s->d_ff);
+  const moe::GemmPlan routed = queued ? queue_plan(s, Q, nullptr) : routed_plan(s, nullptr, false);
+  L.splits = moe::gemm_down_splits(routed, (int)s->d, (int)s->d_ff);
   L.splits_pad = Rpad > 0 ? moe::gemm_down_splits(padded_plan(s, nullptr), (int)s->d, (int)s->d_ff)
                           : 1;
   L.splits_ec = Rpad > 0 ? moe::gemm_down_splits(choice_plan(s, nullptr), (int)s->d, (int)s->d_ff)
@@ -477,8 +477,9 @@ int moe_routing_stats(const moe_shape* s, const float* logits, const float* gate
 // Expert GEMMs over the row groups of pl (activations A, gathered through
 // a_rows when non-null; a_nrows rows of A), the shared expert (on x), and the
 // combine over kslots slots per token (route table rpos, gates g, both
-// [T][kslots], or [kslots][T] when slot_major).  splits: K splits of the down GEMM, whose fp32 planes hold
-// `rows` rows each.  Records events 2..6 of the timed variant.
+// [T][kslots], or [kslots][T] when slot_major).  splits: K splits of the
+// down GEMM, whose fp32 planes hold `rows` rows each.  Records events 2..6 of
+// the timed variant.
 static int experts_and_combine(const moe_shape* s, const Layout& L, const moe::GemmPlan& pl,
                                const void* x, const void* A, const int32_t* a_rows, long a_nrows,
                                const void* w_gate, const void* w_up, const void* w_down,
