@@ -381,8 +381,8 @@ int moe_layer_forward_timed(const moe_shape* s, const void* x, const void* w_rou
  *   route_pos [q_n + T*k]: optional, packed row of every arrival, -1 if it
  *                waits
  * Workspace: moe_workspace_bytes_queued(s, q_n).  Errors as
- * moe_layer_forward; MOE_ERR_UNSUPPORTED when q_n + T*k or the row buffer
- * [T + q_n, d] leaves the 32-bit ranges. */
+ * moe_layer_forward; MOE_ERR_UNSUPPORTED when q_n + T*k, the queued rows
+ * [q_n, d] or the packed rows leave the 32-bit ranges. */
 int moe_workspace_bytes_queued(const moe_shape* s, int64_t q_n, size_t* bytes_out /*host*/);
 int moe_layer_forward_queued(const moe_shape* s, const void* x, const void* w_router,
                              const float* b_router, const void* w_gate, const void* w_up,

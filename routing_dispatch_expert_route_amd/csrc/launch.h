@@ -30,20 +30,19 @@ hipError_t launch_reroute(const float* logits, const int32_t* ids_in, const int3
                           hipStream_t st);
 // Queue policy ("queue to the next micro-batch"), after launch_permute_index
 // over the arrival sequence (Q queued routes, then T*k routes, one route per
-// arrival).  launch_queue_src maps packed rows p < offsets[E] from arrival
-// indices to rows of [x (T rows); queued rows].  launch_queue_out lists the
-// arrivals with pos < 0 in arrival order (n_out[0] of them; flags, cnt_ws,
-// kept1, off1[2], qpos and arr are scratch of N, permute_nchunks(N), 1, 2, N
-// and N ints) and writes their expert, gate, tag (queued: carried; new:
-// tag_base + token) and source row src[p].
-hipError_t launch_queue_src(const int32_t* offsets, int E, int Q, int T, int k, long R_max,
-                            int32_t* row_token, hipStream_t st);
-hipError_t launch_queue_out(const int32_t* pos, long N, int Q, int T, int k, const int32_t* q_ids,
-                            const float* q_gates, const int64_t* q_tags, const int32_t* ids,
-                            const float* gates, int64_t tag_base, int32_t* flags, int32_t* cnt_ws,
-                            int32_t* n_out, int32_t* kept1, int32_t* off1, int32_t* qpos,
-                            int32_t* arr, int32_t* out_ids, float* out_gates, int64_t* out_tags,
-                            int32_t* src, hipStream_t st);
+// arrival).  launch_queue_gather copies, for p < count[0] (at most max_rows),
+// the row of arrival arr[p] -- q_x[a] for a < Q, else x[(a - Q) / k] -- into
+// rows[p].  launch_queue_compact lists the arrivals with pos < 0 in arrival
+// order (n_out[0] of them, arrivals in arr) with their expert, gate and tag
+// (queued: carried; new: tag_base + token).
+hipError_t launch_queue_gather(const void* x, const void* q_x, const int32_t* arr,
+                               const int32_t* count, int Q, int k, long max_rows, long row_bytes,
+                               void* rows, hipStream_t st);
+hipError_t launch_queue_compact(const int32_t* pos, long N, int Q, int k, const int32_t* q_ids,
+                                const float* q_gates, const int64_t* q_tags, const int32_t* ids,
+                                const float* gates, int64_t tag_base, int32_t* n_out,
+                                int32_t* arr, int32_t* out_ids, float* out_gates,
+                                int64_t* out_tags, hipStream_t st);
 // seats[e] = offsets[e+1] - offsets[e]
 hipError_t launch_seats(const int32_t* offsets, int E, int32_t* seats, hipStream_t st);
 // Fixed-shape [E, C, d] buffer from a packed dispatch (needs C >= 1): padded

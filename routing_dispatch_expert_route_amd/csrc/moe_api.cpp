@@ -68,8 +68,8 @@ int64_t rmax_of(const moe_shape* s, int64_t C) {
 struct Layout {
   size_t logits, ids, gates, cnt, counts, kept, offsets, route_pos, row_token, h, yp, part, hs,
       ys, spart, shist, xpad, opad, ppos, ids2, slot, offs2, rpos0, pref, eck, ecp, ecoff;
-  // queue policy: row buffer [x; queued rows], outgoing-queue scratch
-  size_t aall, qflags, qcnt, qmisc, qpos, qarr, qsrc;
+  // queue policy: packed rows of the arrivals, the outgoing queue's arrivals
+  size_t xq, qarr;
   int splits;      // K splits of the routed down GEMM (fp32 partial planes when > 1)
   int splits_pad;  // the same for the fixed-shape [E, C] layout
   int splits_ec;   // the same for expert-choice rows
@@ -227,17 +227,10 @@ Layout layout_of(const moe_shape* s, int64_t Q = -1) {
   const size_t sblk = (size_t)moe::stats_blocks((long)s->T);
   L.spart = take(sblk * (size_t)(s->E + 3) * sizeof(float));
   L.shist = take(sblk * (size_t)moe::kMaxStatBins * sizeof(int32_t));
-  // queue policy: rows [x (T); queued (Q)], and the outgoing queue's
-  // counting sort (flags, chunk counts, n_out / kept / offsets, positions,
-  // arrivals, source rows)
-  const size_t Rq = queued ? R : 0;
-  L.aall = take(queued ? (size_t)(s->T + Q) * s->d * eb : 0);
-  L.qflags = take(Rq * sizeof(int32_t));
-  L.qcnt = take(queued ? (size_t)moe::permute_nchunks((long)R) * sizeof(int32_t) : 0);
-  L.qmisc = take(4 * sizeof(int32_t));
-  L.qpos = take(Rq * sizeof(int32_t));
-  L.qarr = take(Rq * sizeof(int32_t));
-  L.qsrc = take(Rq * sizeof(int32_t));
+  // queue policy: the seated arrivals' rows, packed (from x or the carried
+  // queued rows), and the arrivals of the outgoing queue
+  L.xq = take(queued ? (size_t)Rmax * s->d * eb : 0);
+  L.qarr = take(queued ? R * sizeof(int32_t) : 0);
   L.total = o;
   return L;
 }
@@ -698,7 +691,8 @@ int moe_layer_forward_timed(const moe_shape* s, const void* x, const void* w_rou
 
 // Queue policy: the waiting routes of the previous call arrive first; the
 // drop policy runs over the arrivals (one route each); the routes past
-// capacity form the outgoing queue.  Expert rows come from [x; queued rows].
+// capacity form the outgoing queue.  The seated rows are gathered from x and
+// the carried queued rows into packed rows.
 static int layer_forward_queued_impl(
     const moe_shape* s, const void* x, const void* w_router, const float* b_router,
     const void* w_gate, const void* w_up, const void* w_down, const void* ws_gate,
@@ -714,7 +708,7 @@ static int layer_forward_queued_impl(
   const int64_t eb = elem_bytes(s);
   const int64_t lim = int64_t(1) << 31;
   const int64_t wide = s->d > s->d_ff ? s->d : s->d_ff;
-  if (N >= lim || (s->T + Q) * s->d * eb >= lim || rmax_queue(s, Q) * wide * eb >= lim)
+  if (N >= lim || Q * s->d * eb >= lim || rmax_queue(s, Q) * wide * eb >= lim)
     return MOE_ERR_UNSUPPORTED;
   if (!w_router || !w_gate || !w_up || !w_down || !out_n || (s->T > 0 && (!x || !y)) ||
       (Q > 0 && (!q_x || !q_ids || !q_gates || !q_tags || !y_late)) ||
@@ -742,9 +736,8 @@ static int layer_forward_queued_impl(
   int32_t* cnts = counts ? counts : at<int32_t>(ws, L.counts);
   int32_t* pos = route_pos ? route_pos : at<int32_t>(ws, L.route_pos);
   int32_t* offsets = at<int32_t>(ws, L.offsets);
-  int32_t* row_token = at<int32_t>(ws, L.row_token);
-  void* rows = at<void>(ws, L.aall);
-  int32_t* misc = at<int32_t>(ws, L.qmisc);  // kept1, off1[2]
+  int32_t* row_token = at<int32_t>(ws, L.row_token);  // arrival of each packed row
+  void* xq = at<void>(ws, L.xq);
   auto mark = [&](int i) {
     // a stage marker: a failed record loses a timing, never a result
     if (ev && ev[i]) (void)hipEventRecord(ev[i], stream);
@@ -762,33 +755,26 @@ static int layer_forward_queued_impl(
       hipMemcpyAsync(expert_ids, ids_all + Q, (size_t)T * k * sizeof(int32_t),
                      hipMemcpyDeviceToDevice, stream) != hipSuccess)
     return MOE_ERR_HIP;
-  // expert rows: [x; queued rows]
-  if (T > 0 && hipMemcpyAsync(rows, x, (size_t)T * row_bytes, hipMemcpyDeviceToDevice,
-                              stream) != hipSuccess)
-    return MOE_ERR_HIP;
-  if (Q > 0 && hipMemcpyAsync(static_cast<char*>(rows) + (size_t)T * row_bytes, q_x,
-                              (size_t)Q * row_bytes, hipMemcpyDeviceToDevice, stream) != hipSuccess)
-    return MOE_ERR_HIP;
-  // the drop policy over the arrivals, then packed rows -> source rows
+  // the drop policy over the arrivals, then the seated rows, packed
   e = moe::launch_permute_index(ids_all, (int)N, 1, E, (int)C, at<int32_t>(ws, L.cnt), cnts,
                                 at<int32_t>(ws, L.kept), offsets, pos, row_token, stream);
   if (e != hipSuccess) return MOE_ERR_HIP;
-  e = moe::launch_queue_src(offsets, E, (int)Q, T, k, (long)Rmax, row_token, stream);
+  e = moe::launch_queue_gather(x, q_x, row_token, offsets + E, (int)Q, k, (long)Rmax,
+                               (long)row_bytes, xq, stream);
   if (e != hipSuccess) return MOE_ERR_HIP;
-  // the outgoing queue: arrivals past capacity, in arrival order
-  int32_t* src = at<int32_t>(ws, L.qsrc);
-  e = moe::launch_queue_out(pos, (long)N, (int)Q, T, k, q_ids, q_gates, q_tags, ids_all + Q, g,
-                            tag_base, at<int32_t>(ws, L.qflags), at<int32_t>(ws, L.qcnt), out_n,
-                            misc, misc + 1, at<int32_t>(ws, L.qpos), at<int32_t>(ws, L.qarr),
-                            out_ids, out_gates, out_tags, src, stream);
+  // the outgoing queue: arrivals past capacity, in arrival order, and their rows
+  int32_t* qarr = at<int32_t>(ws, L.qarr);
+  e = moe::launch_queue_compact(pos, (long)N, (int)Q, k, q_ids, q_gates, q_tags, ids_all + Q, g,
+                                tag_base, out_n, qarr, out_ids, out_gates, out_tags, stream);
   if (e != hipSuccess) return MOE_ERR_HIP;
-  e = moe::launch_gather_rows(rows, src, misc + 1, 1, (long)N, (long)row_bytes, out_x, stream);
+  e = moe::launch_queue_gather(x, q_x, qarr, out_n, (int)Q, k, (long)N, (long)row_bytes, out_x,
+                               stream);
   if (e != hipSuccess) return MOE_ERR_HIP;
   // experts on the seated rows, shared expert, this batch's combine
   const moe::GemmPlan pl = queue_plan(s, Q, offsets);
-  v = experts_and_combine(s, L, pl, x, rows, row_token, (long)(T + Q), w_gate, w_up, w_down,
-                          ws_gate, ws_up, ws_down, L.splits, (long)Rmax, pos + Q, g, k, false, y,
-                          ws, stream, ev);
+  v = experts_and_combine(s, L, pl, x, xq, nullptr, (long)Rmax, w_gate, w_up, w_down, ws_gate,
+                          ws_up, ws_down, L.splits, (long)Rmax, pos + Q, g, k, false, y, ws, stream,
+                          ev);
   if (v != MOE_OK) return v;
   // late rows: each queued route's gated output (zero when it waits again)
   if (Q > 0) {

@@ -808,80 +808,99 @@ hipError_t launch_seats(const int32_t* offsets, int E, int32_t* seats, hipStream
 // policies": the overflowing route is processed in the next micro-batch).
 // The dispatch is the drop policy over the arrival sequence -- the Q queued
 // routes first, then the call's T*k routes -- run by the counting sort above
-// with one route per arrival, so a packed row holds an arrival index a.
-// These kernels turn that into source rows of the row buffer [token rows;
-// queued rows] and build the outgoing queue.
+// with one route per arrival, so a packed row holds an arrival index a.  The
+// row of arrival a is its carried row q_x[a] (a < Q) or its token's row
+// x[(a - Q) / k].
 
-// row_token[p] = a  ->  the row of arrival a in [x (T rows); queued rows]
-__global__ __launch_bounds__(256) void queue_src_kernel(const int32_t* __restrict__ offsets, int E,
-                                                        int Q, int T, int k, long R_max,
-                                                        int32_t* __restrict__ row_token) {
-  const long p = (long)blockIdx.x * blockDim.x + threadIdx.x;
-  if (p >= R_max || p >= offsets[E]) return;
-  const int a = row_token[p];
-  row_token[p] = a < Q ? T + a : (a - Q) / k;
-}
-
-// flags[a] = 0 for an arrival that waits again (pos < 0), -1 (no key) else
-__global__ __launch_bounds__(256) void queue_flags_kernel(const int32_t* __restrict__ pos, long N,
-                                                          int32_t* __restrict__ flags) {
-  const long a = (long)blockIdx.x * blockDim.x + threadIdx.x;
-  if (a < N) flags[a] = pos[a] < 0 ? 0 : -1;
-}
-
-// Entry p < n_out of the outgoing queue from its arrival arr[p]: expert,
-// gate, tag and the source row of its token row.
-__global__ __launch_bounds__(256) void queue_out_kernel(
-    const int32_t* __restrict__ arr, const int32_t* __restrict__ n_out, long N, int Q, int T, int k,
-    const int32_t* __restrict__ q_ids, const float* __restrict__ q_gates,
-    const int64_t* __restrict__ q_tags, const int32_t* __restrict__ ids,
-    const float* __restrict__ gates, int64_t tag_base, int32_t* __restrict__ out_ids,
-    float* __restrict__ out_gates, int64_t* __restrict__ out_tags, int32_t* __restrict__ src) {
-  const long p = (long)blockIdx.x * blockDim.x + threadIdx.x;
-  if (p >= N || p >= n_out[0]) return;
-  const int a = arr[p];
-  if (a < Q) {
-    out_ids[p] = q_ids[a];
-    out_gates[p] = q_gates[a];
-    out_tags[p] = q_tags[a];
-    src[p] = T + a;
-  } else {
-    const int r = a - Q;
-    out_ids[p] = ids[r];
-    out_gates[p] = gates[r];
-    out_tags[p] = tag_base + r / k;
-    src[p] = r / k;
+// rows[p] = row of arrival arr[p] for p < count[0]; 16-byte chunks
+__global__ __launch_bounds__(256) void queue_gather_kernel(const u32x4_t* __restrict__ x,
+                                                           const u32x4_t* __restrict__ qx,
+                                                           const int32_t* __restrict__ arr,
+                                                           const int32_t* __restrict__ count,
+                                                           int Q, int k, int cpr, long total,
+                                                           u32x4_t* __restrict__ rows) {
+  const long n = (long)count[0] * cpr;
+  const long lim = n < total ? n : total;
+  for (long g = (long)blockIdx.x * blockDim.x + threadIdx.x; g < lim;
+       g += (long)gridDim.x * blockDim.x) {
+    const long p = g / cpr;
+    const int ch = (int)(g - p * cpr);
+    const int a = arr[p];
+    rows[g] = a < Q ? qx[(long)a * cpr + ch] : x[(long)((a - Q) / k) * cpr + ch];
   }
 }
 
-hipError_t launch_queue_src(const int32_t* offsets, int E, int Q, int T, int k, long R_max,
-                            int32_t* row_token, hipStream_t st) {
-  if (R_max <= 0) return hipSuccess;
-  hipLaunchKernelGGL(queue_src_kernel, dim3((unsigned)((R_max + 255) / 256)), dim3(256), 0, st,
-                     offsets, E, Q, T, k, R_max, row_token);
+// The outgoing queue: the arrivals with pos < 0, in arrival order, by a
+// stream compaction in one workgroup (ballots per wave, a prefix over the
+// waves, a running count over chunks of 1024 arrivals).  Writes n_out, each
+// entry's arrival, expert, gate and tag (queued: carried; new: tag_base +
+// token).
+__global__ __launch_bounds__(1024) void queue_compact_kernel(
+    const int32_t* __restrict__ pos, int N, int Q, int k, const int32_t* __restrict__ q_ids,
+    const float* __restrict__ q_gates, const int64_t* __restrict__ q_tags,
+    const int32_t* __restrict__ ids, const float* __restrict__ gates, int64_t tag_base,
+    int32_t* __restrict__ n_out, int32_t* __restrict__ arr, int32_t* __restrict__ out_ids,
+    float* __restrict__ out_gates, int64_t* __restrict__ out_tags) {
+  constexpr int NW = 1024 / kWave;
+  __shared__ int s_wsum[NW];
+  const int tid = threadIdx.x, lane = tid & (kWave - 1);
+  const int wv = __builtin_amdgcn_readfirstlane(tid / kWave);
+  const uint64_t lt = lane ? (~0ull >> (kWave - lane)) : 0ull;
+  int carry = 0;
+  for (int base = 0; base < N; base += 1024) {  // same trip count on every lane
+    const int a = base + tid;
+    const bool wait = a < N && pos[a] < 0;
+    const uint64_t m = __ballot(wait);
+    if (lane == 0) s_wsum[wv] = __popcll(m);
+    __syncthreads();
+    int before = carry, chunk = 0;
+    for (int w = 0; w < NW; ++w) {
+      const int c = s_wsum[w];
+      before += w < wv ? c : 0;
+      chunk += c;
+    }
+    if (wait) {
+      const int p = before + __popcll(m & lt);
+      arr[p] = a;
+      if (a < Q) {
+        out_ids[p] = q_ids[a];
+        out_gates[p] = q_gates[a];
+        out_tags[p] = q_tags[a];
+      } else {
+        const int r = a - Q;
+        out_ids[p] = ids[r];
+        out_gates[p] = gates[r];
+        out_tags[p] = tag_base + r / k;
+      }
+    }
+    carry += chunk;
+    __syncthreads();  // s_wsum is rewritten by the next chunk
+  }
+  if (tid == 0) n_out[0] = carry;
+}
+
+hipError_t launch_queue_gather(const void* x, const void* q_x, const int32_t* arr,
+                               const int32_t* count, int Q, int k, long max_rows, long row_bytes,
+                               void* rows, hipStream_t st) {
+  const int cpr = (int)(row_bytes / 16);
+  const long total = max_rows * cpr;
+  if (total == 0) return hipSuccess;
+  long blocks = (total + 255) / 256;
+  if (blocks > 8192) blocks = 8192;
+  hipLaunchKernelGGL(queue_gather_kernel, dim3((unsigned)blocks), dim3(256), 0, st,
+                     reinterpret_cast<const u32x4_t*>(x), reinterpret_cast<const u32x4_t*>(q_x),
+                     arr, count, Q, k, cpr, total, reinterpret_cast<u32x4_t*>(rows));
   return hipGetLastError();
 }
 
-hipError_t launch_queue_out(const int32_t* pos, long N, int Q, int T, int k, const int32_t* q_ids,
-                            const float* q_gates, const int64_t* q_tags, const int32_t* ids,
-                            const float* gates, int64_t tag_base, int32_t* flags, int32_t* cnt_ws,
-                            int32_t* n_out, int32_t* kept1, int32_t* off1, int32_t* qpos,
-                            int32_t* arr, int32_t* out_ids, float* out_gates, int64_t* out_tags,
-                            int32_t* src, hipStream_t st) {
-  if (N <= 0) {
-    // an empty arrival sequence still reports an empty queue
-    return launch_permute_index(flags, 0, 1, 1, -1, cnt_ws, n_out, kept1, off1, qpos, arr, st);
-  }
-  const unsigned blocks = (unsigned)((N + 255) / 256);
-  hipLaunchKernelGGL(queue_flags_kernel, dim3(blocks), dim3(256), 0, st, pos, N, flags);
-  hipError_t err = hipGetLastError();
-  if (err != hipSuccess) return err;
-  // one key: the waiting arrivals in arrival order (counting sort, no capacity)
-  err = launch_permute_index(flags, (int)N, 1, 1, -1, cnt_ws, n_out, kept1, off1, qpos, arr, st);
-  if (err != hipSuccess) return err;
-  hipLaunchKernelGGL(queue_out_kernel, dim3(blocks), dim3(256), 0, st, arr, n_out, N, Q, T, k,
-                     q_ids, q_gates, q_tags, ids, gates, tag_base, out_ids, out_gates, out_tags,
-                     src);
+hipError_t launch_queue_compact(const int32_t* pos, long N, int Q, int k, const int32_t* q_ids,
+                                const float* q_gates, const int64_t* q_tags, const int32_t* ids,
+                                const float* gates, int64_t tag_base, int32_t* n_out,
+                                int32_t* arr, int32_t* out_ids, float* out_gates,
+                                int64_t* out_tags, hipStream_t st) {
+  hipLaunchKernelGGL(queue_compact_kernel, dim3(1), dim3(1024), 0, st, pos, (int)N, Q, k, q_ids,
+                     q_gates, q_tags, ids, gates, tag_base, n_out, arr, out_ids, out_gates,
+                     out_tags);
   return hipGetLastError();
 }
 
