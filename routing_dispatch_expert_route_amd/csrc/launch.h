@@ -17,6 +17,15 @@ int permute_nchunks(long R);
 hipError_t launch_permute_index(const int32_t* ids, int T, int k, int E, int C, int32_t* cnt_ws,
                                 int32_t* counts, int32_t* kept, int32_t* offsets,
                                 int32_t* route_pos, int32_t* row_token, hipStream_t st);
+// Top-k (as launch_route's) and the counting-sort permute in one launch, from
+// router logits [T][E], when topk_permute_fused(T, k, E) (T <= 256, E <= 16):
+// ids and gates as launch_route writes them, then the outputs of
+// launch_permute_index.
+bool topk_permute_fused(int T, int k, int E);
+hipError_t launch_topk_permute(const float* logits, int T, int E, int k, int renorm, int C,
+                               int32_t* ids, float* gates, int32_t* counts, int32_t* kept,
+                               int32_t* offsets, int32_t* route_pos, int32_t* row_token,
+                               hipStream_t st);
 hipError_t launch_gather_rows(const void* x, const int32_t* row_token, const int32_t* offsets,
                               int E, long R_max, long row_bytes, void* x_packed, hipStream_t st);
 // Overflow policy "reroute" after a drop-policy dispatch (route_pos0,

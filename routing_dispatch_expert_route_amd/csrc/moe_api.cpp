@@ -599,13 +599,19 @@ static int layer_forward_impl(const moe_shape* s, const void* x, const void* w_r
                                w_down, ws_gate, ws_up, ws_down, L.splits_ec, (long)E * Ce, pos_et,
                                reinterpret_cast<const float*>(keys), E, true, y, ws, stream, ev);
   }
-  hipError_t e = moe::launch_route(bf16, x, w_router, b_router, T, d, E, k, s->renormalize,
-                                   at<float>(ws, L.logits), ids, g, stream);
+  // few tokens and experts: top-k runs inside the single-workgroup permute
+  // (one launch fewer; the route stage is then the projection alone)
+  const bool fused = moe::topk_permute_fused(T, k, E);
+  float* logits = at<float>(ws, L.logits);
+  hipError_t e = moe::launch_route(bf16, x, w_router, b_router, T, d, E, k, s->renormalize, logits,
+                                   fused ? nullptr : ids, g, stream);
   if (e != hipSuccess) return MOE_ERR_HIP;
   mark(1);
-  e = moe::launch_permute_index(ids, T, k, E, (int)C, at<int32_t>(ws, L.cnt), cnts,
-                                at<int32_t>(ws, L.kept), offsets,
-                                reroute ? at<int32_t>(ws, L.rpos0) : rpos, row_token, stream);
+  int32_t* rp = reroute ? at<int32_t>(ws, L.rpos0) : rpos;
+  e = fused ? moe::launch_topk_permute(logits, T, E, k, s->renormalize, (int)C, ids, g, cnts,
+                                       at<int32_t>(ws, L.kept), offsets, rp, row_token, stream)
+            : moe::launch_permute_index(ids, T, k, E, (int)C, at<int32_t>(ws, L.cnt), cnts,
+                                        at<int32_t>(ws, L.kept), offsets, rp, row_token, stream);
   if (e != hipSuccess) return MOE_ERR_HIP;
   if (reroute) {
     // the drop-policy seats stay; dropped routes move; packed rows follow

@@ -21,6 +21,7 @@
 // Expert ids outside [0, E) are treated as dropped routes (never counted).
 #include "common.h"
 #include "launch.h"
+#include "topk.h"
 
 namespace moe {
 
@@ -174,10 +175,14 @@ constexpr int kSmallThreads = 1024;
 constexpr int kSmallWaves = kSmallThreads / kWave;
 constexpr long kSmallMaxRoutes = 4096;
 
-__global__ __launch_bounds__(kSmallThreads) void permute_small_kernel(
-    const int32_t* __restrict__ ids, int R, int k, int E, int C, int32_t* __restrict__ counts,
-    int32_t* __restrict__ kept, int32_t* __restrict__ offsets, int32_t* __restrict__ route_pos,
-    int32_t* __restrict__ row_token) {
+// The body, over ids_at(r) = expert of route r (global or LDS).
+template <typename Ids>
+__device__ __forceinline__ void permute_small_body(Ids ids_at, int R, int k, int E, int C,
+                                                   int32_t* __restrict__ counts,
+                                                   int32_t* __restrict__ kept,
+                                                   int32_t* __restrict__ offsets,
+                                                   int32_t* __restrict__ route_pos,
+                                                   int32_t* __restrict__ row_token) {
   __shared__ int s_cnt[256];
   __shared__ int s_off[256];
   __shared__ int s_run[256];
@@ -191,7 +196,7 @@ __global__ __launch_bounds__(kSmallThreads) void permute_small_kernel(
   }
   __syncthreads();
   for (int r = tid; r < R; r += kSmallThreads) {
-    const int e = ids[r];
+    const int e = ids_at(r);
     if (e >= 0 && e < E) atomicAdd(&s_cnt[e], 1);
   }
   __syncthreads();
@@ -216,7 +221,7 @@ __global__ __launch_bounds__(kSmallThreads) void permute_small_kernel(
   for (int base = 0; base < R; base += kSmallThreads) {
     for (int e = lane; e < E; e += kWave) s_w[wave][e] = 0;
     const int r = base + tid;
-    const int e = r < R ? ids[r] : -1;
+    const int e = r < R ? ids_at(r) : -1;
     const bool valid = r < R && e >= 0 && e < E;
     uint64_t m = __ballot(valid);
 #pragma unroll
@@ -253,6 +258,75 @@ __global__ __launch_bounds__(kSmallThreads) void permute_small_kernel(
     }
     __syncthreads();  // s_w is reused by the next chunk
   }
+}
+
+__global__ __launch_bounds__(kSmallThreads) void permute_small_kernel(
+    const int32_t* __restrict__ ids, int R, int k, int E, int C, int32_t* __restrict__ counts,
+    int32_t* __restrict__ kept, int32_t* __restrict__ offsets, int32_t* __restrict__ route_pos,
+    int32_t* __restrict__ row_token) {
+  permute_small_body([&](int r) { return ids[r]; }, R, k, E, C, counts, kept, offsets, route_pos,
+                     row_token);
+}
+
+// Top-k and the whole permute in one workgroup, for few tokens (at most
+// kFusedMaxT; the top-k of many tokens is faster spread over many CUs, as
+// topk_gates_kernel does) and at most kFusedMaxE experts: the selection of
+// topk_gates_kernel (the same per-token arithmetic, so the same ids and
+// gates bit for bit) runs first, a thread per token, and leaves the ids in
+// LDS for the permute.  One launch and its gap fewer than top-k followed by
+// the permute: about 5 us of a decode step.
+constexpr int kFusedMaxE = 16;
+constexpr int kFusedMaxT = 256;
+
+template <int KMAX>
+__global__ __launch_bounds__(kSmallThreads) void topk_permute_small_kernel(
+    const float* __restrict__ logits, int T, int E, int k, int renorm, int C,
+    int32_t* __restrict__ ids, float* __restrict__ gates, int32_t* __restrict__ counts,
+    int32_t* __restrict__ kept, int32_t* __restrict__ offsets, int32_t* __restrict__ route_pos,
+    int32_t* __restrict__ row_token) {
+  static_assert(kFusedMaxT <= kSmallThreads, "a thread per token");
+  __shared__ int s_ids[kFusedMaxT * 8];
+  const int t = threadIdx.x;
+  if (t < T) {
+    float v[kFusedMaxE];
+    const float* lr = logits + (size_t)t * E;
+#pragma unroll
+    for (int e = 0; e < kFusedMaxE; ++e) v[e] = e < E ? lr[e] : 0.0f;
+    int bi[KMAX];
+    float gate[KMAX];
+    topk_token<KMAX, kFusedMaxE>([&](int e) { return v[e]; }, E, k, renorm, bi, gate);
+#pragma unroll
+    for (int j = 0; j < KMAX; ++j) {
+      if (j < k) {
+        ids[(size_t)t * k + j] = bi[j];
+        gates[(size_t)t * k + j] = gate[j];
+        s_ids[t * k + j] = bi[j];
+      }
+    }
+  }
+  __syncthreads();
+  permute_small_body([&](int r) { return s_ids[r]; }, T * k, k, E, C, counts, kept, offsets,
+                     route_pos, row_token);
+}
+
+bool topk_permute_fused(int T, int k, int E) {
+  return T <= kFusedMaxT && k <= 8 && E <= kFusedMaxE;
+}
+
+hipError_t launch_topk_permute(const float* logits, int T, int E, int k, int renorm, int C,
+                               int32_t* ids, float* gates, int32_t* counts, int32_t* kept,
+                               int32_t* offsets, int32_t* route_pos, int32_t* row_token,
+                               hipStream_t st) {
+  if (!topk_permute_fused(T, k, E)) return hipErrorInvalidValue;
+#define TP(KM)                                                                                 \
+  hipLaunchKernelGGL(topk_permute_small_kernel<KM>, dim3(1), dim3(kSmallThreads), 0, st, logits, \
+                     T, E, k, renorm, C, ids, gates, counts, kept, offsets, route_pos, row_token)
+  if (k <= 1) TP(1);
+  else if (k <= 2) TP(2);
+  else if (k <= 4) TP(4);
+  else TP(8);
+#undef TP
+  return hipGetLastError();
 }
 
 // x_packed[p][:] = x[row_token[p]][:] for p < offsets[E]; 16-byte chunks.

@@ -21,6 +21,7 @@
 
 #include "common.h"
 #include "launch.h"
+#include "topk.h"
 
 namespace moe {
 
@@ -194,12 +195,6 @@ __global__ __launch_bounds__(256) void router_logits_kernel(
   }
 }
 
-// (a, ia) precedes (b, ib) in the selection order: larger logit first, lower
-// expert index first among equal logits.
-__device__ __forceinline__ bool precedes(float a, int ia, float b, int ib) {
-  return a > b || (a == b && ia < ib);
-}
-
 // KMAX: slots kept by the insertion pass, the smallest power of two >= k
 template <int KMAX>
 __global__ __launch_bounds__(64) void topk_gates_kernel(const float* __restrict__ logits, int T,
@@ -230,47 +225,15 @@ __global__ __launch_bounds__(64) void topk_gates_kernel(const float* __restrict_
   __syncthreads();
   if (lane >= nt) return;
   const float* row = s_log + lane * stride;
-  float bv[KMAX];
   int bi[KMAX];
-#pragma unroll
-  for (int j = 0; j < KMAX; ++j) {
-    bv[j] = 0.0f;
-    bi[j] = 0;
-  }
-  int filled = 0;
-  for (int e = 0; e < E; ++e) {
-    float cv = row[e];
-    int ci = e;
-    // branch-free insertion: the displaced entry moves one slot down
-#pragma unroll
-    for (int j = 0; j < KMAX; ++j) {
-      const bool take = (j < k) & ((j >= filled) | precedes(cv, ci, bv[j], bi[j]));
-      const float ov = bv[j];
-      const int oi = bi[j];
-      bv[j] = take ? cv : ov;
-      bi[j] = take ? ci : oi;
-      cv = take ? ov : cv;
-      ci = take ? oi : ci;
-    }
-    filled = filled < k ? filled + 1 : k;
-  }
-  const float m = bv[0];
-  float ex[KMAX];
-  float denom = 0.0f;
-#pragma unroll
-  for (int j = 0; j < KMAX; ++j) {
-    ex[j] = j < k ? expf(bv[j] - m) : 0.0f;
-    if (renorm) denom += ex[j];
-  }
-  if (!renorm) {
-    for (int e = 0; e < E; ++e) denom += expf(row[e] - m);
-  }
+  float gate[KMAX];
+  topk_token<KMAX, 0>([&](int e) { return row[e]; }, E, k, renorm, bi, gate);
   const int t = t0 + lane;
 #pragma unroll
   for (int j = 0; j < KMAX; ++j) {
     if (j < k) {
       ids[(size_t)t * k + j] = bi[j];
-      gates[(size_t)t * k + j] = ex[j] / denom;
+      gates[(size_t)t * k + j] = gate[j];
     }
   }
 }
