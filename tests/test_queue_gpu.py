@@ -146,3 +146,62 @@ def test_layer_forward_queued_switch_full_size(moe):
         assert np.array_equal(bits(qo["x"]), rows)
         say(f"   call {b}: {oa.shape[0]} routes wait, {Q} arrived queued")
         q_gpu, q_ids, q_rows = qo, arr_ids[oa], rows
+
+
+def test_queue_calls_without_a_batch(moe):
+    """No batch and no queue: nothing to do, an empty outgoing queue.  No batch
+    but a waiting queue and phi > 0: C = ceil(phi*0) = 0 seats, so every route
+    waits again -- the same routes, rows, gates and tags, in the same order --
+    and its late rows are zero."""
+    w = Workload("q_empty", T=0, E=8, k=2, d=64, d_ff=64, phi=1.0, bias="normal")
+    wts = _weights(w, 9)
+    dev = {k: (None if v is None else v.cuda()) for k, v in wts.items()}
+    s = moe.shape_of(w)
+    x0 = torch.empty(0, w.d, dtype=w.torch_dtype, device="cuda")
+    say("[queue] no batch, no queue")
+    y, y_late, qo = moe.layer_forward_queued(s, x0, dev["w_router"], dev["b_router"],
+                                             dev["w_gate"], dev["w_up"], dev["w_down"])
+    torch.cuda.synchronize()
+    assert y.shape == (0, w.d) and y_late.shape == (0, w.d) and qo["ids"].shape[0] == 0
+    # a waiting queue made on the host: seeded rows, experts, gates and tags
+    n = 300
+    g = torch.Generator(device="cpu")
+    g.manual_seed(21)
+    q = dict(x=torch.randn(n, w.d, generator=g).to(w.torch_dtype).cuda(),
+             ids=torch.randint(0, w.E, (n,), generator=g, dtype=torch.int32).cuda(),
+             gates=torch.rand(n, generator=g).cuda(),
+             tags=(7000 + torch.arange(n, dtype=torch.int64)).cuda())
+    say(f"[queue] no batch, {n} routes waiting")
+    y, y_late, qo, rt = moe.layer_forward_queued(s, x0, dev["w_router"], dev["b_router"],
+                                                 dev["w_gate"], dev["w_up"], dev["w_down"],
+                                                 queue=q, return_routing=True)
+    torch.cuda.synchronize()
+    assert (_np(rt["route_pos"]) == -1).all()
+    assert np.array_equal(_np(qo["ids"]), _np(q["ids"]))
+    assert np.array_equal(_np(qo["tags"]), _np(q["tags"]))
+    assert np.array_equal(bits(qo["gates"]), bits(q["gates"]))
+    assert np.array_equal(bits(qo["x"]), bits(q["x"]))
+    assert not _np(y_late.float()).any()
+
+
+def test_queue_without_capacity_routes_like_the_layer(moe):
+    """No capacity (phi = 0) and no queue: every route is seated and nothing
+    waits; routing and output match the oracle's layer without capacity."""
+    w = Workload("q_nocap", T=500, E=16, k=4, d=128, d_ff=64, d_ff_shared=32, phi=0.0,
+                 bias="zipf")
+    inp = make_inputs(w, seed=12)
+    d = {k: (None if v is None else v.cuda()) for k, v in inp.items()}
+    s = moe.shape_of(w)
+    say("[queue] no capacity")
+    yq, y_late, qo, rt = moe.layer_forward_queued(
+        s, d["x"], d["w_router"], d["b_router"], d["w_gate"], d["w_up"], d["w_down"],
+        d["ws_gate"], d["ws_up"], d["ws_down"], return_routing=True)
+    torch.cuda.synchronize()
+    ref = oracle.layer_forward(inp["x"], inp["w_router"], inp["b_router"], inp["w_gate"],
+                               inp["w_up"], inp["w_down"], w.k, w.renorm, 0.0, inp["ws_gate"],
+                               inp["ws_up"], inp["ws_down"])
+    assert qo["ids"].shape[0] == 0 and y_late.shape[0] == 0
+    assert np.array_equal(_np(rt["expert_ids"]), ref["ids"])
+    assert np.array_equal(_np(rt["route_pos"]).reshape(w.T, w.k), ref["route_pos"])
+    assert np.array_equal(_np(rt["counts"]), ref["counts"])
+    check_y(yq, ref["y"], w.dtype, "queued layer without capacity")
