@@ -738,7 +738,7 @@ __global__ __launch_bounds__(kDaThreads) void reroute_da_kernel(
       const int nd = need[a];
       int p = next[a];
       const uint8_t* pa = pref + (long)a * E;
-      while (__popcll(h) < nd && p < E) {
+      while ((int)__popcll(h) < nd && p < E) {
         const int e = pa[p++];
         if (e == kNoExpert) continue;
         atomicOr(&held[e * W + word], bit);
