@@ -6,7 +6,7 @@
 
 namespace moe {
 
-// router_logits_kernel + topk_gates_kernel (the projection only when ids
+// router_logits_kernel + topk_rank_kernel (the projection only when ids
 // is null)
 hipError_t launch_route(bool bf16, const void* x, const void* w, const float* b, int T, int d,
                         int E, int k, int renorm, float* logits, int32_t* ids, float* gates,

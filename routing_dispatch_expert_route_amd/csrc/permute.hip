@@ -270,8 +270,8 @@ __global__ __launch_bounds__(kSmallThreads) void permute_small_kernel(
 
 // Top-k and the whole permute in one workgroup, for few tokens (at most
 // kFusedMaxT; the top-k of many tokens is faster spread over many CUs, as
-// topk_gates_kernel does) and at most kFusedMaxE experts: the selection of
-// topk_gates_kernel (the same per-token arithmetic, so the same ids and
+// topk_rank_kernel does) and at most kFusedMaxE experts: topk_token (the
+// same selection and gate sums as topk_rank_kernel, so the same ids and
 // gates bit for bit) runs first, a thread per token, and leaves the ids in
 // LDS for the permute.  One launch and its gap fewer than top-k followed by
 // the permute: about 5 us of a decode step.

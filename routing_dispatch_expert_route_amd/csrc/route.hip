@@ -14,14 +14,13 @@
 //       makes the logits -- and so the selected expert ids at near ties --
 //       bit-reproducible.  Token and expert rows are staged through LDS as
 //       fp32 tiles (see the kernel).
-//   topk_gates_kernel  one lane per token over an LDS copy of its logits:
-//       a single insertion pass keeps the k best by (logit desc, index asc),
+//   topk_rank_kernel  one lane per (token, expert): an expert's rank among
+//       its token's logits (logit desc, index asc) is its slot when below k;
 //       then the gates.
 #include <type_traits>
 
 #include "common.h"
 #include "launch.h"
-#include "topk.h"
 
 namespace moe {
 
@@ -195,46 +194,56 @@ __global__ __launch_bounds__(256) void router_logits_kernel(
   }
 }
 
-// KMAX: slots kept by the insertion pass, the smallest power of two >= k
-template <int KMAX>
-__global__ __launch_bounds__(64) void topk_gates_kernel(const float* __restrict__ logits, int T,
-                                                         int E, int k, int renorm,
-                                                         int32_t* __restrict__ ids,
-                                                         float* __restrict__ gates) {
-  extern __shared__ float s_log[];  // [blockDim.x][E+1]
-  const int lane = threadIdx.x;
-  const int tpb = blockDim.x;  // tokens per block
-  const int t0 = blockIdx.x * tpb;
-  const int nt = min(tpb, T - t0);
-  const int stride = E + 1;
-  // coalesced staging, eight loads in flight per lane
-  const int n = nt * E;
-  for (int base = 0; base < n; base += 8 * tpb) {
-    float v[8];
-#pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const int idx = base + u * tpb + lane;
-      v[u] = idx < n ? logits[(size_t)t0 * E + idx] : 0.0f;
+// Top-k by rank, one lane per (token, expert): expert e's rank is the number
+// of experts that precede it (larger logit, or an equal one at a lower
+// index); it is selected iff rank < k, into slot rank -- the same selection
+// as the insertion pass of topk_token, in E comparisons per lane instead of
+// E*k serial steps per token.  The gates are topk_token's too: exp(l - max)
+// summed in slot order (renormalised) or in expert order, then divided, so
+// the same bits.  EP: lanes per token, a power of two >= E.
+template <int EP>
+__global__ __launch_bounds__(256) void topk_rank_kernel(const float* __restrict__ logits, int T,
+                                                        int E, int k, int renorm,
+                                                        int32_t* __restrict__ ids,
+                                                        float* __restrict__ gates) {
+  constexpr int TPB = 256 / EP;  // tokens per block
+  __shared__ float s_l[TPB][EP + 1];
+  __shared__ float s_ex[TPB][EP + 1];
+  __shared__ float s_m[TPB];
+  const int tid = threadIdx.x;
+  const int tl = tid / EP, e = tid % EP;
+  const int t0 = blockIdx.x * TPB;
+  const int nt = min(TPB, T - t0);
+  // the block's logits are nt*E consecutive floats
+  for (int i = tid; i < nt * E; i += 256) s_l[i / E][i % E] = logits[(size_t)t0 * E + i];
+  __syncthreads();
+  const bool active = tl < nt && e < E;
+  float l = 0.0f;
+  int rank = E;
+  if (active) {
+    l = s_l[tl][e];
+    rank = 0;
+    for (int e2 = 0; e2 < E; ++e2) {
+      const float l2 = s_l[tl][e2];
+      rank += (l2 > l) | ((l2 == l) & (e2 < e));
     }
-#pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const int idx = base + u * tpb + lane;
-      if (idx < n) s_log[(idx / E) * stride + idx % E] = v[u];
-    }
+    if (rank == 0) s_m[tl] = l;
   }
   __syncthreads();
-  if (lane >= nt) return;
-  const float* row = s_log + lane * stride;
-  int bi[KMAX];
-  float gate[KMAX];
-  topk_token<KMAX, 0>([&](int e) { return row[e]; }, E, k, renorm, bi, gate);
-  const int t = t0 + lane;
-#pragma unroll
-  for (int j = 0; j < KMAX; ++j) {
-    if (j < k) {
-      ids[(size_t)t * k + j] = bi[j];
-      gates[(size_t)t * k + j] = gate[j];
-    }
+  float ex = 0.0f;
+  if (active) {
+    ex = expf(l - s_m[tl]);
+    if (!renorm) s_ex[tl][e] = ex;
+    else if (rank < k) s_ex[tl][rank] = ex;
+  }
+  __syncthreads();
+  if (active && rank < k) {
+    const int n = renorm ? k : E;
+    float denom = 0.0f;
+    for (int j = 0; j < n; ++j) denom += s_ex[tl][j];
+    const size_t o = (size_t)(t0 + tl) * k + rank;
+    ids[o] = e;
+    gates[o] = ex / denom;
   }
 }
 
@@ -265,17 +274,22 @@ hipError_t launch_route(bool bf16, const void* x, const void* w, const float* b,
 #undef RL
   hipError_t err = hipGetLastError();
   if (err != hipSuccess || !ids) return err;  // logits only
-  const int tpb = (E + 1) * 64 * (int)sizeof(float) <= 48 * 1024 ? 64 : 32;
-  const size_t lds = (size_t)tpb * (E + 1) * sizeof(float);
-  const dim3 tg(ceil_div(T, tpb)), tb(tpb);
-  if (k <= 1)
-    hipLaunchKernelGGL(topk_gates_kernel<1>, tg, tb, lds, st, logits, T, E, k, renorm, ids, gates);
-  else if (k <= 2)
-    hipLaunchKernelGGL(topk_gates_kernel<2>, tg, tb, lds, st, logits, T, E, k, renorm, ids, gates);
-  else if (k <= 4)
-    hipLaunchKernelGGL(topk_gates_kernel<4>, tg, tb, lds, st, logits, T, E, k, renorm, ids, gates);
-  else
-    hipLaunchKernelGGL(topk_gates_kernel<8>, tg, tb, lds, st, logits, T, E, k, renorm, ids, gates);
+  int ep = 4;
+  while (ep < E) ep *= 2;  // E <= 256
+  const dim3 tb(256);
+#define TR(EP_)                                                                        \
+  hipLaunchKernelGGL(topk_rank_kernel<EP_>, dim3(ceil_div(T, 256 / EP_)), tb, 0, st, logits, T, \
+                     E, k, renorm, ids, gates)
+  switch (ep) {
+    case 4: TR(4); break;
+    case 8: TR(8); break;
+    case 16: TR(16); break;
+    case 32: TR(32); break;
+    case 64: TR(64); break;
+    case 128: TR(128); break;
+    default: TR(256); break;
+  }
+#undef TR
   return hipGetLastError();
 }
 

@@ -1,5 +1,6 @@
-// topk.h -- one token's top-k and gates, shared by the kernels that select
-// experts (internal to libmoe).
+// topk.h -- one token's top-k and gates in one thread (internal to libmoe;
+// the fused top-k + permute kernel uses it, topk_rank_kernel computes the
+// same values with a lane per expert).
 //
 // "271,104 Routes", section 2: topk on the logits, then softmax over the k
 // selected logits (the renormalised gate); "MoE Inference Visualized",
