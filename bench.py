@@ -219,6 +219,8 @@ def main():
     ap.add_argument("--queue", action="store_true",
                     help="queue-to-the-next-micro-batch overflow policy: each step processes the "
                          "batch plus the routes one earlier batch left waiting")
+    ap.add_argument("--no-graph", action="store_true",
+                    help="skip the HIP-graph replay timing (graph_ms_per_step)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB")
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
     ap.add_argument("--traffic-out", default=None)
@@ -351,6 +353,31 @@ def main():
     g1_us = sum(elapsed_us(g1_ev[2 * i], g1_ev[2 * i + 1]) for i in range(K)) / K
     for e in g1_ev:
         hip.hipEventDestroy(e)
+
+    # the same steps replayed from a HIP graph (one captured step per weight
+    # set, replayed until K steps ran): the launch sequence without the host,
+    # reported beside the eager value
+    graph_ms = None
+    if not args.no_graph and not args.queue:
+        g = torch.cuda.CUDAGraph()
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            step(0)
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g):
+            for i in range(nsets):
+                step(i)
+        reps = max(1, -(-K // nsets))
+        g.replay()
+        torch.cuda.synchronize()
+        tg0 = time.perf_counter()
+        for _ in range(reps):
+            g.replay()
+        torch.cuda.synchronize()
+        graph_ms = (time.perf_counter() - tg0) * 1e3 / (reps * nsets)
+        del g
 
     # per-stage times: a second pass with every stage boundary marked
     stages = None
@@ -492,6 +519,7 @@ def main():
         "layer_roofline": layer_roof,
         "step_us_percentiles": step_pct,
         "warm_ms_per_step": round(warm_ms, 5) if warm_ms else None,
+        "graph_ms_per_step": round(graph_ms, 5) if graph_ms else None,
         "cpu_baseline": cpu,
         "stages_us": stages,
         "routing_stats": rstats,
