@@ -175,10 +175,13 @@ constexpr int kSmallThreads = 1024;
 constexpr int kSmallWaves = kSmallThreads / kWave;
 constexpr long kSmallMaxRoutes = 4096;
 
-// The body, over ids_at(r) = expert of route r (global or LDS).
-template <typename Ids>
-__device__ __forceinline__ void permute_small_body(Ids ids_at, int R, int k, int E, int C,
-                                                   int32_t* __restrict__ counts,
+constexpr int kSmallPerThread = kSmallMaxRoutes / kSmallThreads;
+
+// The body, over the routes' experts already in registers: thread tid holds
+// route q * kSmallThreads + tid in idv[q] (-1 past R), loaded together by
+// the caller, so neither pass waits on memory per chunk.
+__device__ __forceinline__ void permute_small_body(const int (&idv)[kSmallPerThread], int R, int k,
+                                                   int E, int C, int32_t* __restrict__ counts,
                                                    int32_t* __restrict__ kept,
                                                    int32_t* __restrict__ offsets,
                                                    int32_t* __restrict__ route_pos,
@@ -195,8 +198,9 @@ __device__ __forceinline__ void permute_small_body(Ids ids_at, int R, int k, int
     s_run[e] = 0;
   }
   __syncthreads();
-  for (int r = tid; r < R; r += kSmallThreads) {
-    const int e = ids_at(r);
+#pragma unroll
+  for (int q = 0; q < kSmallPerThread; ++q) {
+    const int e = idv[q];
     if (e >= 0 && e < E) atomicAdd(&s_cnt[e], 1);
   }
   __syncthreads();
@@ -218,10 +222,13 @@ __device__ __forceinline__ void permute_small_body(Ids ids_at, int R, int k, int
     }
   }
   const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (kWave - lane));
-  for (int base = 0; base < R; base += kSmallThreads) {
+#pragma unroll
+  for (int q = 0; q < kSmallPerThread; ++q) {
+    const int base = q * kSmallThreads;
+    if (base >= R) break;  // R is uniform: every wave leaves together
     for (int e = lane; e < E; e += kWave) s_w[wave][e] = 0;
     const int r = base + tid;
-    const int e = r < R ? ids_at(r) : -1;
+    const int e = idv[q];
     const bool valid = r < R && e >= 0 && e < E;
     uint64_t m = __ballot(valid);
 #pragma unroll
@@ -264,8 +271,13 @@ __global__ __launch_bounds__(kSmallThreads) void permute_small_kernel(
     const int32_t* __restrict__ ids, int R, int k, int E, int C, int32_t* __restrict__ counts,
     int32_t* __restrict__ kept, int32_t* __restrict__ offsets, int32_t* __restrict__ route_pos,
     int32_t* __restrict__ row_token) {
-  permute_small_body([&](int r) { return ids[r]; }, R, k, E, C, counts, kept, offsets, route_pos,
-                     row_token);
+  int idv[kSmallPerThread];
+#pragma unroll
+  for (int q = 0; q < kSmallPerThread; ++q) {
+    const int r = q * kSmallThreads + (int)threadIdx.x;
+    idv[q] = r < R ? ids[r] : -1;
+  }
+  permute_small_body(idv, R, k, E, C, counts, kept, offsets, route_pos, row_token);
 }
 
 // Top-k and the whole permute in one workgroup, for few tokens (at most
@@ -305,8 +317,13 @@ __global__ __launch_bounds__(kSmallThreads) void topk_permute_small_kernel(
     }
   }
   __syncthreads();
-  permute_small_body([&](int r) { return s_ids[r]; }, T * k, k, E, C, counts, kept, offsets,
-                     route_pos, row_token);
+  int idv[kSmallPerThread];
+#pragma unroll
+  for (int q = 0; q < kSmallPerThread; ++q) {
+    const int r = q * kSmallThreads + t;
+    idv[q] = r < T * k ? s_ids[r] : -1;
+  }
+  permute_small_body(idv, T * k, k, E, C, counts, kept, offsets, route_pos, row_token);
 }
 
 bool topk_permute_fused(int T, int k, int E) {
