@@ -31,12 +31,15 @@ hipError_t launch_gather_rows(const void* x, const int32_t* row_token, const int
 // Overflow policy "reroute" after a drop-policy dispatch (route_pos0,
 // offsets0, kept from launch_permute_index); E <= 64, k <= 8, C >= 0.
 // Writes the final experts, the packed positions and rows of the result.
-// pref: scratch of T*k*64 bytes (preference lists of the dropped routes).
+// pref: scratch of T*k*64 bytes (preference ranks of the dropped routes);
+// da_state: scratch of reroute_state_bytes(T, E) (per-token state of the
+// parallel kernel when it does not fit LDS).
+long reroute_state_bytes(int T, int E);
 hipError_t launch_reroute(const float* logits, const int32_t* ids_in, const int32_t* route_pos0,
                           const int32_t* offsets0, const int32_t* kept, int T, int k, int E,
                           int C, int32_t* ids_out, int32_t* slot, int32_t* offsets,
                           int32_t* route_pos, int32_t* row_token, uint8_t* pref,
-                          hipStream_t st);
+                          uint8_t* da_state, hipStream_t st);
 // Queue policy ("queue to the next micro-batch"), after launch_permute_index
 // over the arrival sequence (Q queued routes, then T*k routes, one route per
 // arrival).  launch_queue_gather copies, for p < count[0] (at most max_rows),

@@ -67,7 +67,7 @@ int64_t rmax_of(const moe_shape* s, int64_t C) {
 
 struct Layout {
   size_t logits, ids, gates, cnt, counts, kept, offsets, route_pos, row_token, h, yp, part, hs,
-      ys, spart, shist, xpad, opad, ppos, ids2, slot, offs2, rpos0, pref, eck, ecp, ecoff;
+      ys, spart, shist, xpad, opad, ppos, ids2, slot, offs2, rpos0, pref, dast, eck, ecp, ecoff;
   // queue policy: packed rows of the arrivals, the outgoing queue's arrivals
   size_t xq, qarr;
   int splits;      // K splits of the routed down GEMM (fp32 partial planes when > 1)
@@ -216,6 +216,8 @@ Layout layout_of(const moe_shape* s, int64_t Q = -1) {
   L.offs2 = take((size_t)(s->E + 1) * sizeof(int32_t));
   L.rpos0 = take(Ro * sizeof(int32_t));
   L.pref = take(Ro * 64);  // preference lists of the dropped routes (E <= 64)
+  // per-token state of the parallel reroute where it does not fit LDS
+  L.dast = take(queued || s->E > 64 ? 0 : (size_t)moe::reroute_state_bytes((int)s->T, (int)s->E));
   // expert choice: expert-major keys (score bits) and route table, row groups
   const size_t TE = queued ? 0 : (size_t)s->T * s->E;
   L.eck = take(TE * sizeof(uint32_t));
@@ -375,7 +377,7 @@ int moe_permute_reroute(const moe_shape* s, const void* x, const float* logits,
   // kept counts (in filled) seed the walk, which turns them into seats
   e = moe::launch_reroute(logits, expert_ids, at<int32_t>(ws, L.rpos0), offs0, filled, T, k, E,
                           (int)C, expert_ids_out, at<int32_t>(ws, L.slot), offsets, route_pos,
-                          row_token, at<uint8_t>(ws, L.pref), stream);
+                          row_token, at<uint8_t>(ws, L.pref), at<uint8_t>(ws, L.dast), stream);
   if (e != hipSuccess) return MOE_ERR_HIP;
   e = moe::launch_seats(offsets, E, filled, stream);
   if (e != hipSuccess) return MOE_ERR_HIP;
@@ -619,7 +621,7 @@ static int layer_forward_impl(const moe_shape* s, const void* x, const void* w_r
     e = moe::launch_reroute(at<float>(ws, L.logits), ids, at<int32_t>(ws, L.rpos0), offsets,
                             at<int32_t>(ws, L.kept), T, k, E, (int)C, ids_final,
                             at<int32_t>(ws, L.slot), at<int32_t>(ws, L.offs2), rpos, row_token,
-                            at<uint8_t>(ws, L.pref), stream);
+                            at<uint8_t>(ws, L.pref), at<uint8_t>(ws, L.dast), stream);
     if (e != hipSuccess) return MOE_ERR_HIP;
     offsets = at<int32_t>(ws, L.offs2);
   }

@@ -603,43 +603,54 @@ __global__ __launch_bounds__(256) void reroute_rows_kernel(const int32_t* __rest
 //      and rejects the rest.
 // It ends after a round without proposals (each proposal moves a token's
 // list pointer, so that round comes).  Seats follow token order among an
-// expert's accepted routes, as in the walk.  One block of 1024 threads; the
-// state sits in a fixed LDS arena, laid out for T tokens (the bound on the
-// tokens with drops), W = ceil(T / 32):
+// expert's accepted routes, as in the walk.  One block of 1024 threads, laid
+// out for T tokens (the bound on the tokens with drops), W = ceil(T / 32):
 //   held  [E][W] uint32   bit a: token a holds (or is proposed to) expert e
-//   pre   [E][W] int32    exclusive prefix of held's word popcounts (seats)
+//   pre   [E][W] uint16   exclusive prefix of held's word popcounts (seats)
+// in a fixed LDS arena, shared by every wave, and the per-token state
 //   hold  [T] uint64      experts token a holds
 //   tok   [T] uint16      token index of token a (token order)
 //   need  [T] uint8       its dropped routes n_t
 //   next  [T] uint8       next position of its preference list
 //   pref  [T][E] uint8    its experts by preference, kNoExpert where skipped
+// in the arena too when it fits (TOK_LDS), else in a global workspace region:
+// each token's state is read and written only by the thread that owns the
+// token, so it needs no sharing, only room.
 constexpr int kDaThreads = 1024;
 constexpr int kDaWaves = kDaThreads / kWave;
 constexpr uint8_t kNoExpert = 0xFF;
 constexpr long kDaArena = 144L * 1024;
+constexpr int kDaMaxT = 65535;  // token indices and seat prefixes fit uint16
 
+// held and pre from the arena's start; the per-token arrays from tok_base,
+// the arena's next byte (TOK_LDS) or 0 in the global region.  lds_bytes and
+// tok_bytes are the two footprints.
 struct DaLayout {
-  long held, pre, hold, tok, need, next, pref, bytes;
+  long held, pre, hold, tok, need, next, pref, lds_bytes, tok_bytes;
 };
-__host__ __device__ inline DaLayout da_layout(int T, int E) {
+__host__ __device__ inline DaLayout da_layout(int T, int E, bool tok_lds) {
   const long W = (T + 31) / 32;
   DaLayout L;
   L.held = 0;
   L.pre = L.held + (long)E * W * 4;
-  L.hold = L.pre + (long)E * W * 4;
+  const long pre_end = L.pre + (long)E * W * 2;
+  const long tb = tok_lds ? (pre_end + 7) & ~7L : 0;
+  L.hold = tb;
   L.tok = L.hold + 8L * T;
   L.need = L.tok + ((2L * T + 3) & ~3L);
   L.next = L.need + T;
   L.pref = L.next + T;
-  L.bytes = L.pref + (long)T * E;
+  L.tok_bytes = L.pref + (long)T * E - tb;
+  L.lds_bytes = tok_lds ? L.pref + (long)T * E : pre_end;
   return L;
 }
 
+template <bool TOK_LDS>
 __global__ __launch_bounds__(kDaThreads) void reroute_da_kernel(
     const uint8_t* __restrict__ rank, const int32_t* __restrict__ ids_in,
     const int32_t* __restrict__ route_pos0, const int32_t* __restrict__ offsets0,
     const int32_t* __restrict__ kept, int T, int k, int E, int C, int32_t* __restrict__ ids_out,
-    int32_t* __restrict__ slot, int32_t* __restrict__ offsets) {
+    int32_t* __restrict__ slot, int32_t* __restrict__ offsets, uint8_t* __restrict__ tok_state) {
   __shared__ __attribute__((aligned(16))) uint8_t arena[kDaArena];
   __shared__ int s_kept[kRerouteMaxE], s_free[kRerouteMaxE], s_new[kRerouteMaxE],
       s_fill[kRerouteMaxE];
@@ -647,14 +658,15 @@ __global__ __launch_bounds__(kDaThreads) void reroute_da_kernel(
   const int tid = threadIdx.x, lane = tid & (kWave - 1);
   const int wv = __builtin_amdgcn_readfirstlane(tid / kWave);
   const int W = (T + 31) / 32;
-  const DaLayout L = da_layout(T, E);
+  const DaLayout L = da_layout(T, E, TOK_LDS);
   uint32_t* held = reinterpret_cast<uint32_t*>(arena + L.held);
-  int32_t* pre = reinterpret_cast<int32_t*>(arena + L.pre);
-  uint64_t* hold = reinterpret_cast<uint64_t*>(arena + L.hold);
-  uint16_t* tok = reinterpret_cast<uint16_t*>(arena + L.tok);
-  uint8_t* need = arena + L.need;
-  uint8_t* next = arena + L.next;
-  uint8_t* pref = arena + L.pref;
+  uint16_t* pre = reinterpret_cast<uint16_t*>(arena + L.pre);
+  uint8_t* const tb = TOK_LDS ? arena : tok_state;
+  uint64_t* hold = reinterpret_cast<uint64_t*>(tb + L.hold);
+  uint16_t* tok = reinterpret_cast<uint16_t*>(tb + L.tok);
+  uint8_t* need = tb + L.need;
+  uint8_t* next = tb + L.next;
+  uint8_t* pref = tb + L.pref;
 
   if (tid < E) {
     const int kp = kept[tid];
@@ -812,7 +824,7 @@ __global__ __launch_bounds__(kDaThreads) void reroute_da_kernel(
     const int inc = wave_incl_scan(c, lane);
     int before = inc - c;
     for (int w = w0; w < w1; ++w) {
-      pre[e * W + w] = before;
+      pre[e * W + w] = (uint16_t)before;  // < T <= 65535
       before += __popc(row[w]);
     }
     if (lane == kWave - 1) s_fill[e] = s_kept[e] + inc;
@@ -856,11 +868,24 @@ __global__ __launch_bounds__(kDaThreads) void reroute_da_kernel(
   }
 }
 
+// The three reroute kernels by footprint: all state in LDS, the per-token
+// state in the workspace, or the serial walk.
+enum class RerouteKind { kDaLds, kDaGlobal, kWalk };
+static RerouteKind reroute_kind(int T, int E) {
+  if (T <= kDaMaxT && da_layout(T, E, true).lds_bytes <= kDaArena) return RerouteKind::kDaLds;
+  if (T <= kDaMaxT && da_layout(T, E, false).lds_bytes <= kDaArena) return RerouteKind::kDaGlobal;
+  return RerouteKind::kWalk;
+}
+
+long reroute_state_bytes(int T, int E) {
+  return reroute_kind(T, E) == RerouteKind::kDaGlobal ? da_layout(T, E, false).tok_bytes : 0;
+}
+
 hipError_t launch_reroute(const float* logits, const int32_t* ids_in, const int32_t* route_pos0,
                           const int32_t* offsets0, const int32_t* kept, int T, int k, int E,
                           int C, int32_t* ids_out, int32_t* slot, int32_t* offsets,
                           int32_t* route_pos, int32_t* row_token, uint8_t* pref,
-                          hipStream_t st) {
+                          uint8_t* da_state, hipStream_t st) {
   const int R = T * k;
   if (R > 0) {
     const long threads = (long)R * kRerouteMaxE;
@@ -869,9 +894,13 @@ hipError_t launch_reroute(const float* logits, const int32_t* ids_in, const int3
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
   }
-  if (da_layout(T, E).bytes <= kDaArena) {
-    hipLaunchKernelGGL(reroute_da_kernel, dim3(1), dim3(kDaThreads), 0, st, pref, ids_in,
-                       route_pos0, offsets0, kept, T, k, E, C, ids_out, slot, offsets);
+  const RerouteKind kind = reroute_kind(T, E);
+  if (kind == RerouteKind::kDaLds) {
+    hipLaunchKernelGGL(reroute_da_kernel<true>, dim3(1), dim3(kDaThreads), 0, st, pref, ids_in,
+                       route_pos0, offsets0, kept, T, k, E, C, ids_out, slot, offsets, nullptr);
+  } else if (kind == RerouteKind::kDaGlobal) {
+    hipLaunchKernelGGL(reroute_da_kernel<false>, dim3(1), dim3(kDaThreads), 0, st, pref, ids_in,
+                       route_pos0, offsets0, kept, T, k, E, C, ids_out, slot, offsets, da_state);
   } else {
     hipLaunchKernelGGL(reroute_kernel, dim3(1), dim3(kWave), 0, st, pref, ids_in, route_pos0,
                        offsets0, kept, T, k, E, C, ids_out, slot, offsets);

@@ -36,14 +36,22 @@ CASES = {
                              renorm=0, phi=1.0, bias="zipf"),
     "granite_tight": WORKLOADS["granite_1412"].with_(name="granite_tight", phi=0.75, bias="normal"),
     "e64_k8_zipf": Workload("e64_k8", T=600, E=64, k=8, d=64, d_ff=32, phi=0.9, bias="zipf"),
-    # shapes on either side of the parallel (deferred acceptance) kernel's
-    # LDS bound (about T * (E + 12) bytes): the ones above fit, 8000 tokens
-    # over 8 experts and 3000 over 32 do not and take the sequential walk
+    # the three reroute kernels: the parallel (deferred acceptance) kernel
+    # with all its state in LDS (about T * (E + 12) + 3 * E * T / 16 bytes
+    # <= 144 KiB: the shapes above and k1_e64), the same kernel with its
+    # per-token state in the workspace (3 * E * T / 16 bytes of bitmaps and
+    # seat prefixes <= 144 KiB, T <= 65535), and the sequential walk beyond
     "k1_e64_zipf": Workload("k1_e64", T=700, E=64, k=1, d=64, d_ff=32, renorm=0, phi=0.5,
                             bias="zipf"),
-    "k1_walk": Workload("k1_walk", T=8000, E=8, k=1, d=64, d_ff=32, renorm=0, phi=1.0,
-                        bias="normal"),
-    "k8_walk": Workload("k8_walk", T=3000, E=32, k=8, d=64, d_ff=32, phi=0.75, bias="normal"),
+    "k1_state_ws": Workload("k1_ws", T=8000, E=8, k=1, d=64, d_ff=32, renorm=0, phi=1.0,
+                            bias="normal"),
+    "k8_state_ws": Workload("k8_ws", T=3000, E=32, k=8, d=64, d_ff=32, phi=0.75, bias="normal"),
+    "k8_e40_t16384_ws": Workload("k8_e40_big", T=16384, E=40, k=8, d=64, d_ff=32, phi=0.75,
+                                 bias="zipf"),
+    "k1_t60000_ws": Workload("k1_t60000", T=60000, E=8, k=1, d=64, d_ff=32, renorm=0, phi=1.0,
+                             bias="normal"),
+    "k2_e64_walk": Workload("k2_walk", T=13000, E=64, k=2, d=64, d_ff=32, phi=0.8,
+                            bias="normal"),
 }
 
 
@@ -105,12 +113,15 @@ def test_layer_forward_reroute_parity(moe, name):
 
 
 @pytest.mark.parametrize("T,E,k,phi", [(2048, 16, 1, 0.5), (700, 64, 1, 0.4), (8000, 8, 1, 0.5),
-                                       (1024, 16, 4, 0.5), (600, 64, 8, 0.3)])
+                                       (1024, 16, 4, 0.5), (600, 64, 8, 0.3),
+                                       (16384, 40, 8, 0.5), (13000, 64, 1, 0.5)])
 def test_permute_reroute_common_order(moe, T, E, k, phi):
     """Every token has the same preference order (identical rows of x), so the
     dropped routes fill the experts one after another in that order: the
     longest chain of rejections the parallel kernel can meet (about one round
-    per expert), and, at T=8000, the same inputs through the walk."""
+    per expert), with its per-token state in LDS or (T=8000, 16384) in the
+    workspace, and, at T=13000 over 64 experts, the same inputs through the
+    walk."""
     w = Workload("common_order", T=T, E=E, k=k, d=64, d_ff=32, renorm=0, phi=phi, bias="zipf")
     inp = make_inputs(w, seed=5)
     inp["x"] = inp["x"][:1].repeat(T, 1).contiguous()
