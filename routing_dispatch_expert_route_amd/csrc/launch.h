@@ -31,7 +31,8 @@ hipError_t launch_gather_rows(const void* x, const int32_t* row_token, const int
 // Overflow policy "reroute" after a drop-policy dispatch (route_pos0,
 // offsets0, kept from launch_permute_index); E <= 64, k <= 8, C >= 0.
 // Writes the final experts, the packed positions and rows of the result.
-// pref: scratch of T*k*64 bytes (preference ranks of the dropped routes);
+// pref: scratch of T*k*64 bytes (per dropped route, its experts' ranks or
+// its experts in preference order);
 // da_state: scratch of reroute_state_bytes(T, E) (per-token state of the
 // parallel kernel when it does not fit LDS).
 long reroute_state_bytes(int T, int E);

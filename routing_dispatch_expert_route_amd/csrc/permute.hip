@@ -434,9 +434,10 @@ hipError_t launch_padded(const void* x, const int32_t* ids, const int32_t* route
 // lower index first) that the token does not hold and that still has room.
 // That is a greedy in arrival order -- every choice depends on the earlier
 // ones.  reroute_da_kernel below reaches the same result in parallel rounds
-// when its state fits LDS; beyond that one wave walks the dropped routes one
-// by one.  Both read every dropped route's rank of each expert (one byte
-// each), written first by a parallel kernel.  The walk stages a 64-route
+// while its per-expert bitmaps fit LDS; beyond that one wave walks the dropped
+// routes one by one.  A parallel kernel first writes, for every dropped
+// route, the rank of each expert (one byte each; the walk) or the experts
+// in preference order (the parallel rounds).  The walk stages a 64-route
 // chunk's rank rows in LDS (the next chunk's are loaded while this one is
 // walked); for a route, lane e reads
 // its expert's rank and the choice is the lowest rank among the lanes with
@@ -446,9 +447,11 @@ hipError_t launch_padded(const void* x, const int32_t* ids, const int32_t* route
 //   offsets   exclusive prefix of the seats used per expert
 constexpr int kRerouteMaxE = 64;
 
-// rank[r][e] = rank of expert e in dropped route r's preference order
-// (experts ahead: larger logit, or equal logit and lower index); one thread
-// per (r, e)
+// The rank of expert e in dropped route r's preference order (experts
+// ahead: larger logit, or equal logit and lower index), one thread per
+// (r, e), stored as rank[r][e] (the walk) or inverted, order[r][rank] = e
+// (ORDER: the parallel rounds read the experts in preference order).
+template <bool ORDER>
 __global__ __launch_bounds__(256) void reroute_rank_kernel(const float* __restrict__ logits,
                                                            const int32_t* __restrict__ route_pos0,
                                                            int R, int k, int E,
@@ -463,7 +466,10 @@ __global__ __launch_bounds__(256) void reroute_rank_kernel(const float* __restri
     const float l2 = l[e2];
     rk += (l2 > le) | ((l2 == le) & (e2 < e));
   }
-  rank[(size_t)r * kRerouteMaxE + e] = (uint8_t)rk;
+  if (ORDER)
+    rank[(size_t)r * kRerouteMaxE + rk] = (uint8_t)e;
+  else
+    rank[(size_t)r * kRerouteMaxE + e] = (uint8_t)rk;
 }
 
 __global__ __launch_bounds__(64) void reroute_kernel(
@@ -609,16 +615,19 @@ __global__ __launch_bounds__(256) void reroute_rows_kernel(const int32_t* __rest
 //   pre   [E][W] uint16   exclusive prefix of held's word popcounts (seats)
 // in a fixed LDS arena, shared by every wave, and the per-token state
 //   hold  [T] uint64      experts token a holds
+//   own   [T] uint64      experts token a had from the router (skipped)
+//   first [T] int32       its first dropped route (its preference list is
+//                         that route's row of experts in preference order)
 //   tok   [T] uint16      token index of token a (token order)
 //   need  [T] uint8       its dropped routes n_t
 //   next  [T] uint8       next position of its preference list
-//   pref  [T][E] uint8    its experts by preference, kNoExpert where skipped
 // in the arena too when it fits (TOK_LDS), else in a global workspace region:
 // each token's state is read and written only by the thread that owns the
-// token, so it needs no sharing, only room.
+// token, so it needs no sharing, only room.  Preference rows are read 16
+// bytes at a time (a row is 64 bytes, 64-byte aligned); experts the token
+// had and experts without a free seat are skipped as they come up.
 constexpr int kDaThreads = 1024;
 constexpr int kDaWaves = kDaThreads / kWave;
-constexpr uint8_t kNoExpert = 0xFF;
 constexpr long kDaArena = 144L * 1024;
 constexpr int kDaMaxT = 65535;  // token indices and seat prefixes fit uint16
 
@@ -626,28 +635,38 @@ constexpr int kDaMaxT = 65535;  // token indices and seat prefixes fit uint16
 // the arena's next byte (TOK_LDS) or 0 in the global region.  lds_bytes and
 // tok_bytes are the two footprints.
 struct DaLayout {
-  long held, pre, hold, tok, need, next, pref, lds_bytes, tok_bytes;
+  long held, pre, hold, own, first, tok, need, next, lds_bytes, tok_bytes;
 };
 __host__ __device__ inline DaLayout da_layout(int T, int E, bool tok_lds) {
   const long W = (T + 31) / 32;
   DaLayout L;
   L.held = 0;
   L.pre = L.held + (long)E * W * 4;
-  const long pre_end = L.pre + (long)E * W * 2;
+  // pre doubles as the rounds' dirty bitmap (W words)
+  const long pre_end = L.pre + ((long)E * W * 2 > 4L * W ? (long)E * W * 2 : 4L * W);
   const long tb = tok_lds ? (pre_end + 7) & ~7L : 0;
   L.hold = tb;
-  L.tok = L.hold + 8L * T;
+  L.own = L.hold + 8L * T;
+  L.first = L.own + 8L * T;
+  L.tok = L.first + 4L * T;
   L.need = L.tok + ((2L * T + 3) & ~3L);
   L.next = L.need + T;
-  L.pref = L.next + T;
-  L.tok_bytes = L.pref + (long)T * E - tb;
-  L.lds_bytes = tok_lds ? L.pref + (long)T * E : pre_end;
+  const long end = L.next + T;
+  L.tok_bytes = end - tb;
+  L.lds_bytes = tok_lds ? end : pre_end;
   return L;
+}
+
+// byte p of a 16-byte chunk
+__device__ __forceinline__ int chunk_byte(const u32x4_t& c, int p) {
+  const int q = (p >> 2) & 3;
+  const uint32_t w = q == 0 ? c[0] : q == 1 ? c[1] : q == 2 ? c[2] : c[3];
+  return (int)((w >> ((p & 3) * 8)) & 0xFFu);
 }
 
 template <bool TOK_LDS>
 __global__ __launch_bounds__(kDaThreads) void reroute_da_kernel(
-    const uint8_t* __restrict__ rank, const int32_t* __restrict__ ids_in,
+    const uint8_t* __restrict__ order, const int32_t* __restrict__ ids_in,
     const int32_t* __restrict__ route_pos0, const int32_t* __restrict__ offsets0,
     const int32_t* __restrict__ kept, int T, int k, int E, int C, int32_t* __restrict__ ids_out,
     int32_t* __restrict__ slot, int32_t* __restrict__ offsets, uint8_t* __restrict__ tok_state) {
@@ -661,12 +680,17 @@ __global__ __launch_bounds__(kDaThreads) void reroute_da_kernel(
   const DaLayout L = da_layout(T, E, TOK_LDS);
   uint32_t* held = reinterpret_cast<uint32_t*>(arena + L.held);
   uint16_t* pre = reinterpret_cast<uint16_t*>(arena + L.pre);
+  // bit a: token a lost an expert in the last cut (or the rounds just began);
+  // the others have nothing to do (they hold n_t experts or their list ran
+  // out) -- the seats' prefix replaces it after the rounds
+  uint32_t* dirty = reinterpret_cast<uint32_t*>(arena + L.pre);
   uint8_t* const tb = TOK_LDS ? arena : tok_state;
   uint64_t* hold = reinterpret_cast<uint64_t*>(tb + L.hold);
+  uint64_t* own = reinterpret_cast<uint64_t*>(tb + L.own);
+  int32_t* first = reinterpret_cast<int32_t*>(tb + L.first);
   uint16_t* tok = reinterpret_cast<uint16_t*>(tb + L.tok);
   uint8_t* need = tb + L.need;
   uint8_t* next = tb + L.next;
-  uint8_t* pref = tb + L.pref;
 
   if (tid < E) {
     const int kp = kept[tid];
@@ -675,6 +699,7 @@ __global__ __launch_bounds__(kDaThreads) void reroute_da_kernel(
     s_new[tid] = 0;
   }
   for (int i = tid; i < E * W; i += kDaThreads) held[i] = 0;
+  for (int i = tid; i < W; i += kDaThreads) dirty[i] = ~0u;
 
   // tokens with dropped routes in token order (each thread a run of cpt
   // tokens; block scan of the run counts); kept routes keep expert and seat
@@ -716,28 +741,25 @@ __global__ __launch_bounds__(kDaThreads) void reroute_da_kernel(
   }
   __syncthreads();
 
-  // preference lists: one token per thread.  The rank row of the token's
-  // first dropped route (every route of a token shares the logits) places
-  // each expert; its own experts and the experts without a free seat are
-  // skipped.
+  // per token: the experts it had, its first dropped route (every route of
+  // a token shares the logits, so that route's order row is the token's
+  // preference list) and n_t
   for (int a0 = 0; a0 < A; a0 += kDaThreads) {
     const int a = a0 + tid;
     if (a >= A) continue;
     const int t = tok[a];
-    uint64_t own = 0;
+    uint64_t om = 0;
     int nd = 0, rf = -1;
     for (int j = 0; j < k; ++j) {
       const int r = t * k + j;
-      own |= 1ull << ids_in[r];
+      om |= 1ull << ids_in[r];
       if (route_pos0[r] < 0) {
         if (rf < 0) rf = r;
         ++nd;
       }
     }
-    const uint8_t* rr = rank + (size_t)rf * kRerouteMaxE;
-    uint8_t* pa = pref + (long)a * E;
-    for (int e = 0; e < E; ++e)
-      pa[rr[e]] = (s_free[e] > 0 && !((own >> e) & 1)) ? (uint8_t)e : kNoExpert;
+    own[a] = om;
+    first[a] = rf;
     need[a] = (uint8_t)nd;
     next[a] = 0;
     hold[a] = 0;
@@ -759,6 +781,8 @@ __global__ __launch_bounds__(kDaThreads) void reroute_da_kernel(
       if (a >= A) continue;
       const int word = a >> 5;
       const uint32_t bit = 1u << (a & 31);
+      if (!(dirty[word] & bit)) continue;
+      atomicAnd(&dirty[word], ~bit);
       uint64_t h = hold[a];
       for (uint64_t m = h; m; m &= m - 1) {
         const int e = __builtin_ctzll(m);
@@ -766,10 +790,17 @@ __global__ __launch_bounds__(kDaThreads) void reroute_da_kernel(
       }
       const int nd = need[a];
       int p = next[a];
-      const uint8_t* pa = pref + (long)a * E;
+      const uint8_t* pa = order + (size_t)first[a] * kRerouteMaxE;
+      const uint64_t om = own[a];
+      u32x4_t c = {0u, 0u, 0u, 0u};
+      int cbase = -1;
       while ((int)__popcll(h) < nd && p < E) {
-        const int e = pa[p++];
-        if (e == kNoExpert) continue;
+        if ((p & ~15) != cbase) {
+          cbase = p & ~15;
+          c = *reinterpret_cast<const u32x4_t*>(pa + cbase);
+        }
+        const int e = chunk_byte(c, p++);
+        if (((om >> e) & 1) || s_free[e] <= 0) continue;  // had it, or no seat
         atomicOr(&held[e * W + word], bit);
         h |= 1ull << e;
         s_new[e] = 1;
@@ -805,7 +836,11 @@ __global__ __launch_bounds__(kDaThreads) void reroute_da_kernel(
             }
             v = keep;
           }
-          if (before + pc > cap) row[w] = v;
+          if (before + pc > cap) {
+            const uint32_t cut = row[w] & ~v;
+            row[w] = v;
+            if (cut) atomicOr(&dirty[w], cut);  // these tokens propose again
+          }
           before += pc;
         }
       }
@@ -837,17 +872,23 @@ __global__ __launch_bounds__(kDaThreads) void reroute_da_kernel(
     const int word = a >> 5;
     const uint32_t below = (1u << (a & 31)) - 1u;
     uint64_t h = hold[a];
-    const uint8_t* pa = pref + (long)a * E;
+    const uint8_t* pa = order + (size_t)first[a] * kRerouteMaxE;
+    u32x4_t c = {0u, 0u, 0u, 0u};
+    int cbase = -1;
     int p = 0;
     for (int j = 0; j < k; ++j) {
       const int r = t * k + j;
       if (route_pos0[r] >= 0) continue;
       int e = -1;
       while (h && p < E) {  // the next best held expert
-        const int c = pa[p++];
-        if (c != kNoExpert && ((h >> c) & 1)) {
-          e = c;
-          h &= ~(1ull << c);
+        if ((p & ~15) != cbase) {
+          cbase = p & ~15;
+          c = *reinterpret_cast<const u32x4_t*>(pa + cbase);
+        }
+        const int x = chunk_byte(c, p++);
+        if ((h >> x) & 1) {
+          e = x;
+          h &= ~(1ull << x);
           break;
         }
       }
@@ -887,14 +928,19 @@ hipError_t launch_reroute(const float* logits, const int32_t* ids_in, const int3
                           int32_t* route_pos, int32_t* row_token, uint8_t* pref,
                           uint8_t* da_state, hipStream_t st) {
   const int R = T * k;
+  const RerouteKind kind = reroute_kind(T, E);
   if (R > 0) {
     const long threads = (long)R * kRerouteMaxE;
-    hipLaunchKernelGGL(reroute_rank_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0,
-                       st, logits, route_pos0, R, k, E, pref);
+    const dim3 grid((unsigned)((threads + 255) / 256));
+    if (kind == RerouteKind::kWalk)
+      hipLaunchKernelGGL(reroute_rank_kernel<false>, grid, dim3(256), 0, st, logits, route_pos0, R,
+                         k, E, pref);
+    else
+      hipLaunchKernelGGL(reroute_rank_kernel<true>, grid, dim3(256), 0, st, logits, route_pos0, R,
+                         k, E, pref);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
   }
-  const RerouteKind kind = reroute_kind(T, E);
   if (kind == RerouteKind::kDaLds) {
     hipLaunchKernelGGL(reroute_da_kernel<true>, dim3(1), dim3(kDaThreads), 0, st, pref, ids_in,
                        route_pos0, offsets0, kept, T, k, E, C, ids_out, slot, offsets, nullptr);

@@ -37,15 +37,16 @@ CASES = {
     "granite_tight": WORKLOADS["granite_1412"].with_(name="granite_tight", phi=0.75, bias="normal"),
     "e64_k8_zipf": Workload("e64_k8", T=600, E=64, k=8, d=64, d_ff=32, phi=0.9, bias="zipf"),
     # the three reroute kernels: the parallel (deferred acceptance) kernel
-    # with all its state in LDS (about T * (E + 12) + 3 * E * T / 16 bytes
-    # <= 144 KiB: the shapes above and k1_e64), the same kernel with its
+    # with all its state in LDS (about 24 * T + 3 * E * T / 16 bytes <= 144
+    # KiB: the shapes above, k1_e64 and k8_e32_t3000), the same kernel with its
     # per-token state in the workspace (3 * E * T / 16 bytes of bitmaps and
     # seat prefixes <= 144 KiB, T <= 65535), and the sequential walk beyond
     "k1_e64_zipf": Workload("k1_e64", T=700, E=64, k=1, d=64, d_ff=32, renorm=0, phi=0.5,
                             bias="zipf"),
     "k1_state_ws": Workload("k1_ws", T=8000, E=8, k=1, d=64, d_ff=32, renorm=0, phi=1.0,
                             bias="normal"),
-    "k8_state_ws": Workload("k8_ws", T=3000, E=32, k=8, d=64, d_ff=32, phi=0.75, bias="normal"),
+    "k8_e32_t3000": Workload("k8_t3000", T=3000, E=32, k=8, d=64, d_ff=32, phi=0.75,
+                             bias="normal"),
     "k8_e40_t16384_ws": Workload("k8_e40_big", T=16384, E=40, k=8, d=64, d_ff=32, phi=0.75,
                                  bias="zipf"),
     "k1_t60000_ws": Workload("k1_t60000", T=60000, E=8, k=1, d=64, d_ff=32, renorm=0, phi=1.0,
