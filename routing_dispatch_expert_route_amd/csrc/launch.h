@@ -33,8 +33,9 @@ hipError_t launch_gather_rows(const void* x, const int32_t* row_token, const int
 // Writes the final experts, the packed positions and rows of the result.
 // pref: scratch of T*k*64 bytes (per dropped route, its experts' ranks or
 // its experts in preference order);
-// da_state: scratch of reroute_state_bytes(T, E) (per-token state of the
-// parallel kernel when it does not fit LDS).
+// da_state: scratch of reroute_state_bytes(T, E) bytes, 16-byte aligned (the
+// parallel kernel's token arrays, final bitmaps and, when it does not fit
+// LDS, its per-token state; 0 bytes where the walk runs).
 long reroute_state_bytes(int T, int E);
 hipError_t launch_reroute(const float* logits, const int32_t* ids_in, const int32_t* route_pos0,
                           const int32_t* offsets0, const int32_t* kept, int T, int k, int E,

@@ -612,7 +612,7 @@ __global__ __launch_bounds__(256) void reroute_rows_kernel(const int32_t* __rest
 // expert's accepted routes, as in the walk.  One block of 1024 threads, laid
 // out for T tokens (the bound on the tokens with drops), W = ceil(T / 32):
 //   held  [E][W] uint32   bit a: token a holds (or is proposed to) expert e
-//   pre   [E][W] uint16   exclusive prefix of held's word popcounts (seats)
+//   dirty [W] uint32      bit a: token a was cut in the last round
 // in a fixed LDS arena, shared by every wave, and the per-token state
 //   hold  [T] uint64      experts token a holds
 //   own   [T] uint64      experts token a had from the router (skipped)
@@ -631,20 +631,19 @@ constexpr int kDaWaves = kDaThreads / kWave;
 constexpr long kDaArena = 144L * 1024;
 constexpr int kDaMaxT = 65535;  // token indices and seat prefixes fit uint16
 
-// held and pre from the arena's start; the per-token arrays from tok_base,
-// the arena's next byte (TOK_LDS) or 0 in the global region.  lds_bytes and
+// held and dirty from the arena's start; the per-token arrays from the
+// arena's next byte (TOK_LDS) or from 0 in a global region.  lds_bytes and
 // tok_bytes are the two footprints.
 struct DaLayout {
-  long held, pre, hold, own, first, tok, need, next, lds_bytes, tok_bytes;
+  long held, dirty, hold, own, first, tok, need, next, lds_bytes, tok_bytes;
 };
 __host__ __device__ inline DaLayout da_layout(int T, int E, bool tok_lds) {
   const long W = (T + 31) / 32;
   DaLayout L;
   L.held = 0;
-  L.pre = L.held + (long)E * W * 4;
-  // pre doubles as the rounds' dirty bitmap (W words)
-  const long pre_end = L.pre + ((long)E * W * 2 > 4L * W ? (long)E * W * 2 : 4L * W);
-  const long tb = tok_lds ? (pre_end + 7) & ~7L : 0;
+  L.dirty = L.held + (long)E * W * 4;
+  const long shared_end = L.dirty + 4L * W;
+  const long tb = tok_lds ? (shared_end + 7) & ~7L : 0;
   L.hold = tb;
   L.own = L.hold + 8L * T;
   L.first = L.own + 8L * T;
@@ -653,7 +652,32 @@ __host__ __device__ inline DaLayout da_layout(int T, int E, bool tok_lds) {
   L.next = L.need + T;
   const long end = L.next + T;
   L.tok_bytes = end - tb;
-  L.lds_bytes = tok_lds ? end : pre_end;
+  L.lds_bytes = tok_lds ? end : shared_end;
+  return L;
+}
+
+// The parallel reroute's workspace region: token-indexed arrays written by
+// reroute_tok_kernel (tneed: dropped routes of token t, 0 for none; town:
+// the experts the router gave it; tfirst: its first dropped route) and by
+// reroute_da_kernel (tidx: its index among the tokens with drops; thold: the
+// experts it holds at the end; gheld / gpre: the final per-expert bitmaps and
+// seat prefixes), which reroute_seat_kernel reads; then, when the per-token
+// state of the rounds does not fit LDS, that state (tok_bytes of da_layout).
+struct RrLayout {
+  long town, thold, tfirst, tidx, tneed, gheld, gpre, state, bytes;
+};
+__host__ __device__ inline RrLayout rr_layout(int T, int E, bool tok_lds) {
+  const long W = (T + 31) / 32;
+  RrLayout L;
+  L.tneed = 0;  // read 16 bytes at a time
+  L.town = (T + 15L) & ~15L;
+  L.thold = L.town + 8L * T;
+  L.tfirst = L.thold + 8L * T;
+  L.tidx = L.tfirst + 4L * T;
+  L.gheld = (L.tidx + 4L * T + 15) & ~15L;
+  L.gpre = L.gheld + 4L * E * W;
+  L.state = (L.gpre + 2L * E * W + 15) & ~15L;
+  L.bytes = L.state + (tok_lds ? 0 : da_layout(T, E, false).tok_bytes);
   return L;
 }
 
@@ -666,10 +690,8 @@ __device__ __forceinline__ int chunk_byte(const u32x4_t& c, int p) {
 
 template <bool TOK_LDS>
 __global__ __launch_bounds__(kDaThreads) void reroute_da_kernel(
-    const uint8_t* __restrict__ order, const int32_t* __restrict__ ids_in,
-    const int32_t* __restrict__ route_pos0, const int32_t* __restrict__ offsets0,
-    const int32_t* __restrict__ kept, int T, int k, int E, int C, int32_t* __restrict__ ids_out,
-    int32_t* __restrict__ slot, int32_t* __restrict__ offsets, uint8_t* __restrict__ tok_state) {
+    const uint8_t* __restrict__ order, const int32_t* __restrict__ kept, int T, int E, int C,
+    int32_t* __restrict__ offsets, uint8_t* __restrict__ region) {
   __shared__ __attribute__((aligned(16))) uint8_t arena[kDaArena];
   __shared__ int s_kept[kRerouteMaxE], s_free[kRerouteMaxE], s_new[kRerouteMaxE],
       s_fill[kRerouteMaxE];
@@ -678,12 +700,20 @@ __global__ __launch_bounds__(kDaThreads) void reroute_da_kernel(
   const int wv = __builtin_amdgcn_readfirstlane(tid / kWave);
   const int W = (T + 31) / 32;
   const DaLayout L = da_layout(T, E, TOK_LDS);
+  const RrLayout G = rr_layout(T, E, TOK_LDS);
+  const uint8_t* tneed = region + G.tneed;
+  const uint64_t* town = reinterpret_cast<const uint64_t*>(region + G.town);
+  const int32_t* tfirst = reinterpret_cast<const int32_t*>(region + G.tfirst);
+  uint64_t* thold = reinterpret_cast<uint64_t*>(region + G.thold);
+  int32_t* tidx = reinterpret_cast<int32_t*>(region + G.tidx);
+  uint32_t* gheld = reinterpret_cast<uint32_t*>(region + G.gheld);
+  uint16_t* gpre = reinterpret_cast<uint16_t*>(region + G.gpre);
+  uint8_t* tok_state = region + G.state;
   uint32_t* held = reinterpret_cast<uint32_t*>(arena + L.held);
-  uint16_t* pre = reinterpret_cast<uint16_t*>(arena + L.pre);
   // bit a: token a lost an expert in the last cut (or the rounds just began);
   // the others have nothing to do (they hold n_t experts or their list ran
-  // out) -- the seats' prefix replaces it after the rounds
-  uint32_t* dirty = reinterpret_cast<uint32_t*>(arena + L.pre);
+  // out)
+  uint32_t* dirty = reinterpret_cast<uint32_t*>(arena + L.dirty);
   uint8_t* const tb = TOK_LDS ? arena : tok_state;
   uint64_t* hold = reinterpret_cast<uint64_t*>(tb + L.hold);
   uint64_t* own = reinterpret_cast<uint64_t*>(tb + L.own);
@@ -701,30 +731,20 @@ __global__ __launch_bounds__(kDaThreads) void reroute_da_kernel(
   for (int i = tid; i < E * W; i += kDaThreads) held[i] = 0;
   for (int i = tid; i < W; i += kDaThreads) dirty[i] = ~0u;
 
-  // tokens with dropped routes in token order (each thread a run of cpt
-  // tokens; block scan of the run counts); kept routes keep expert and seat
-  const int cpt = (T + kDaThreads - 1) / kDaThreads;  // <= 64 (T <= 65535)
-  const int t0 = tid * cpt, t1 = min(T, t0 + cpt);
-  int na = 0;
+  // tokens with dropped routes in token order: each thread a run of cpt
+  // tokens (a multiple of 16, <= 64 as T <= 65535) read as 16-byte chunks of
+  // tneed; a block scan of the run counts places them
+  const int cpt = ((T + kDaThreads - 1) / kDaThreads + 15) & ~15;
+  const int t0 = tid * cpt;
   uint64_t amask = 0;
-  for (int t = t0; t < t1; ++t) {
-    int nd = 0;
-    for (int j = 0; j < k; ++j) {
-      const int r = t * k + j;
-      const int p = route_pos0[r];
-      if (p < 0) {
-        ++nd;
-      } else {
-        const int e = ids_in[r];
-        ids_out[r] = e;
-        slot[r] = p - offsets0[e];
-      }
-    }
-    if (nd) {
-      amask |= 1ull << (t - t0);
-      ++na;
-    }
+  for (int q = 0; q < cpt; q += 16) {
+    if (t0 + q >= T) break;
+    const u32x4_t c = *reinterpret_cast<const u32x4_t*>(tneed + t0 + q);
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+      if (chunk_byte(c, i) && t0 + q + i < T) amask |= 1ull << (q + i);
   }
+  const int na = __popcll(amask);
   const int incl = wave_incl_scan(na, lane);
   if (lane == kWave - 1) s_wsum[wv] = incl;
   __syncthreads();
@@ -736,31 +756,23 @@ __global__ __launch_bounds__(kDaThreads) void reroute_da_kernel(
   }
   const int A = __builtin_amdgcn_readfirstlane(an);
   while (amask) {
-    tok[at++] = (uint16_t)(t0 + __builtin_ctzll(amask));
+    const int t = t0 + __builtin_ctzll(amask);
+    tok[at] = (uint16_t)t;
+    tidx[t] = at++;
     amask &= amask - 1;
   }
   __syncthreads();
 
   // per token: the experts it had, its first dropped route (every route of
   // a token shares the logits, so that route's order row is the token's
-  // preference list) and n_t
+  // preference list) and n_t, from the token-indexed arrays
   for (int a0 = 0; a0 < A; a0 += kDaThreads) {
     const int a = a0 + tid;
     if (a >= A) continue;
     const int t = tok[a];
-    uint64_t om = 0;
-    int nd = 0, rf = -1;
-    for (int j = 0; j < k; ++j) {
-      const int r = t * k + j;
-      om |= 1ull << ids_in[r];
-      if (route_pos0[r] < 0) {
-        if (rf < 0) rf = r;
-        ++nd;
-      }
-    }
-    own[a] = om;
-    first[a] = rf;
-    need[a] = (uint8_t)nd;
+    own[a] = town[t];
+    first[a] = tfirst[t];
+    need[a] = tneed[t];
     next[a] = 0;
     hold[a] = 0;
   }
@@ -849,8 +861,8 @@ __global__ __launch_bounds__(kDaThreads) void reroute_da_kernel(
     __syncthreads();
   }
 
-  // seats: per expert, the exclusive prefix of its words' popcounts; then
-  // each token's i-th dropped route takes the i-th best expert it holds
+  // seats: per expert, the exclusive prefix of its words' popcounts; the
+  // bitmaps, prefixes and final holdings go out to reroute_seat_kernel
   for (int e = wv; e < E; e += kDaWaves) {
     const uint32_t* row = held + e * W;
     const int w0 = lane * wpl, w1 = min(W, w0 + wpl);
@@ -859,53 +871,103 @@ __global__ __launch_bounds__(kDaThreads) void reroute_da_kernel(
     const int inc = wave_incl_scan(c, lane);
     int before = inc - c;
     for (int w = w0; w < w1; ++w) {
-      pre[e * W + w] = (uint16_t)before;  // < T <= 65535
-      before += __popc(row[w]);
+      const uint32_t v = row[w];
+      gheld[e * W + w] = v;
+      gpre[e * W + w] = (uint16_t)before;  // < T <= 65535
+      before += __popc(v);
     }
     if (lane == kWave - 1) s_fill[e] = s_kept[e] + inc;
   }
-  __syncthreads();
   for (int a0 = 0; a0 < A; a0 += kDaThreads) {
     const int a = a0 + tid;
-    if (a >= A) continue;
-    const int t = tok[a];
-    const int word = a >> 5;
-    const uint32_t below = (1u << (a & 31)) - 1u;
-    uint64_t h = hold[a];
-    const uint8_t* pa = order + (size_t)first[a] * kRerouteMaxE;
-    u32x4_t c = {0u, 0u, 0u, 0u};
-    int cbase = -1;
-    int p = 0;
-    for (int j = 0; j < k; ++j) {
-      const int r = t * k + j;
-      if (route_pos0[r] >= 0) continue;
-      int e = -1;
-      while (h && p < E) {  // the next best held expert
-        if ((p & ~15) != cbase) {
-          cbase = p & ~15;
-          c = *reinterpret_cast<const u32x4_t*>(pa + cbase);
-        }
-        const int x = chunk_byte(c, p++);
-        if ((h >> x) & 1) {
-          e = x;
-          h &= ~(1ull << x);
-          break;
-        }
-      }
-      if (e < 0) {  // no expert with room: dropped after all
-        ids_out[r] = ids_in[r];
-        slot[r] = -1;
-      } else {
-        ids_out[r] = e;
-        slot[r] = s_kept[e] + pre[e * W + word] + __popc(held[e * W + word] & below);
-      }
-    }
+    if (a < A) thold[tok[a]] = hold[a];
   }
+  __syncthreads();
   if (wv == 0) {
     const int f = lane < E ? s_fill[lane] : 0;
     const int inc = wave_incl_scan(f, lane);
     if (lane == 0) offsets[0] = 0;
     if (lane < E) offsets[lane + 1] = inc;
+  }
+}
+
+// One thread per token, before the rounds: its kept routes keep expert and
+// seat; its dropped routes are counted, its first one and its router
+// experts noted (the rounds' input, token-indexed).
+__global__ __launch_bounds__(256) void reroute_tok_kernel(
+    const int32_t* __restrict__ ids_in, const int32_t* __restrict__ route_pos0,
+    const int32_t* __restrict__ offsets0, int T, int k, int E, int32_t* __restrict__ ids_out,
+    int32_t* __restrict__ slot, uint8_t* __restrict__ region) {
+  const int t = blockIdx.x * blockDim.x + threadIdx.x;
+  if (t >= T) return;
+  const RrLayout G = rr_layout(T, E, true);
+  uint64_t om = 0;
+  int nd = 0, rf = -1;
+  for (int j = 0; j < k; ++j) {
+    const int r = t * k + j;
+    const int p = route_pos0[r];
+    const int e = ids_in[r];
+    om |= 1ull << e;
+    if (p >= 0) {
+      ids_out[r] = e;
+      slot[r] = p - offsets0[e];
+    } else {
+      if (rf < 0) rf = r;
+      ++nd;
+    }
+  }
+  region[G.tneed + t] = (uint8_t)nd;
+  reinterpret_cast<uint64_t*>(region + G.town)[t] = om;
+  reinterpret_cast<int32_t*>(region + G.tfirst)[t] = rf;
+}
+
+// One thread per token with drops, after the rounds: its i-th dropped route
+// takes the i-th best expert it holds, at seat kept[e] + the number of
+// accepted tokens before it (token order); with none left it stays dropped.
+__global__ __launch_bounds__(256) void reroute_seat_kernel(
+    const uint8_t* __restrict__ order, const int32_t* __restrict__ ids_in,
+    const int32_t* __restrict__ route_pos0, const int32_t* __restrict__ kept, int T, int k, int E,
+    int32_t* __restrict__ ids_out, int32_t* __restrict__ slot,
+    const uint8_t* __restrict__ region) {
+  const int t = blockIdx.x * blockDim.x + threadIdx.x;
+  if (t >= T) return;
+  const RrLayout G = rr_layout(T, E, true);
+  if (region[G.tneed + t] == 0) return;
+  const int W = (T + 31) / 32;
+  const int a = reinterpret_cast<const int32_t*>(region + G.tidx)[t];
+  uint64_t h = reinterpret_cast<const uint64_t*>(region + G.thold)[t];
+  const int rf = reinterpret_cast<const int32_t*>(region + G.tfirst)[t];
+  const uint32_t* gheld = reinterpret_cast<const uint32_t*>(region + G.gheld);
+  const uint16_t* gpre = reinterpret_cast<const uint16_t*>(region + G.gpre);
+  const int word = a >> 5;
+  const uint32_t below = (1u << (a & 31)) - 1u;
+  const uint8_t* pa = order + (size_t)rf * kRerouteMaxE;
+  u32x4_t c = {0u, 0u, 0u, 0u};
+  int cbase = -1;
+  int p = 0;
+  for (int j = 0; j < k; ++j) {
+    const int r = t * k + j;
+    if (route_pos0[r] >= 0) continue;
+    int e = -1;
+    while (h && p < E) {  // the next best held expert
+      if ((p & ~15) != cbase) {
+        cbase = p & ~15;
+        c = *reinterpret_cast<const u32x4_t*>(pa + cbase);
+      }
+      const int x = chunk_byte(c, p++);
+      if ((h >> x) & 1) {
+        e = x;
+        h &= ~(1ull << x);
+        break;
+      }
+    }
+    if (e < 0) {  // no expert with room: dropped after all
+      ids_out[r] = ids_in[r];
+      slot[r] = -1;
+    } else {
+      ids_out[r] = e;
+      slot[r] = kept[e] + gpre[e * W + word] + __popc(gheld[e * W + word] & below);
+    }
   }
 }
 
@@ -919,7 +981,8 @@ static RerouteKind reroute_kind(int T, int E) {
 }
 
 long reroute_state_bytes(int T, int E) {
-  return reroute_kind(T, E) == RerouteKind::kDaGlobal ? da_layout(T, E, false).tok_bytes : 0;
+  const RerouteKind kind = reroute_kind(T, E);
+  return kind == RerouteKind::kWalk ? 0 : rr_layout(T, E, kind == RerouteKind::kDaLds).bytes;
 }
 
 hipError_t launch_reroute(const float* logits, const int32_t* ids_in, const int32_t* route_pos0,
@@ -941,15 +1004,24 @@ hipError_t launch_reroute(const float* logits, const int32_t* ids_in, const int3
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
   }
-  if (kind == RerouteKind::kDaLds) {
-    hipLaunchKernelGGL(reroute_da_kernel<true>, dim3(1), dim3(kDaThreads), 0, st, pref, ids_in,
-                       route_pos0, offsets0, kept, T, k, E, C, ids_out, slot, offsets, nullptr);
-  } else if (kind == RerouteKind::kDaGlobal) {
-    hipLaunchKernelGGL(reroute_da_kernel<false>, dim3(1), dim3(kDaThreads), 0, st, pref, ids_in,
-                       route_pos0, offsets0, kept, T, k, E, C, ids_out, slot, offsets, da_state);
-  } else {
+  if (kind == RerouteKind::kWalk) {
     hipLaunchKernelGGL(reroute_kernel, dim3(1), dim3(kWave), 0, st, pref, ids_in, route_pos0,
                        offsets0, kept, T, k, E, C, ids_out, slot, offsets);
+  } else {
+    // token set-up, the rounds in one workgroup, then the seats
+    const dim3 tgrid(ceil_div(T, 256));
+    if (T > 0)
+      hipLaunchKernelGGL(reroute_tok_kernel, tgrid, dim3(256), 0, st, ids_in, route_pos0, offsets0,
+                         T, k, E, ids_out, slot, da_state);
+    if (kind == RerouteKind::kDaLds)
+      hipLaunchKernelGGL(reroute_da_kernel<true>, dim3(1), dim3(kDaThreads), 0, st, pref, kept, T,
+                         E, C, offsets, da_state);
+    else
+      hipLaunchKernelGGL(reroute_da_kernel<false>, dim3(1), dim3(kDaThreads), 0, st, pref, kept, T,
+                         E, C, offsets, da_state);
+    if (T > 0)
+      hipLaunchKernelGGL(reroute_seat_kernel, tgrid, dim3(256), 0, st, pref, ids_in, route_pos0,
+                         kept, T, k, E, ids_out, slot, da_state);
   }
   hipError_t err = hipGetLastError();
   if (err != hipSuccess || R == 0) return err;

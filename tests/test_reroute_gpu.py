@@ -37,10 +37,10 @@ CASES = {
     "granite_tight": WORKLOADS["granite_1412"].with_(name="granite_tight", phi=0.75, bias="normal"),
     "e64_k8_zipf": Workload("e64_k8", T=600, E=64, k=8, d=64, d_ff=32, phi=0.9, bias="zipf"),
     # the three reroute kernels: the parallel (deferred acceptance) kernel
-    # with all its state in LDS (about 24 * T + 3 * E * T / 16 bytes <= 144
+    # with all its state in LDS (about 24 * T + (E + 1) * T / 8 bytes <= 144
     # KiB: the shapes above, k1_e64 and k8_e32_t3000), the same kernel with its
-    # per-token state in the workspace (3 * E * T / 16 bytes of bitmaps and
-    # seat prefixes <= 144 KiB, T <= 65535), and the sequential walk beyond
+    # per-token state in the workspace ((E + 1) * T / 8 bytes of bitmaps <= 144
+    # KiB, T <= 65535), and the sequential walk beyond
     "k1_e64_zipf": Workload("k1_e64", T=700, E=64, k=1, d=64, d_ff=32, renorm=0, phi=0.5,
                             bias="zipf"),
     "k1_state_ws": Workload("k1_ws", T=8000, E=8, k=1, d=64, d_ff=32, renorm=0, phi=1.0,
@@ -51,7 +51,9 @@ CASES = {
                                  bias="zipf"),
     "k1_t60000_ws": Workload("k1_t60000", T=60000, E=8, k=1, d=64, d_ff=32, renorm=0, phi=1.0,
                              bias="normal"),
-    "k2_e64_walk": Workload("k2_walk", T=13000, E=64, k=2, d=64, d_ff=32, phi=0.8,
+    "k2_e64_t13000_ws": Workload("k2_t13000", T=13000, E=64, k=2, d=64, d_ff=32, phi=0.8,
+                                 bias="normal"),
+    "k2_e64_walk": Workload("k2_walk", T=20000, E=64, k=2, d=64, d_ff=32, phi=0.8,
                             bias="normal"),
 }
 
@@ -115,14 +117,15 @@ def test_layer_forward_reroute_parity(moe, name):
 
 @pytest.mark.parametrize("T,E,k,phi", [(2048, 16, 1, 0.5), (700, 64, 1, 0.4), (8000, 8, 1, 0.5),
                                        (1024, 16, 4, 0.5), (600, 64, 8, 0.3),
-                                       (16384, 40, 8, 0.5), (13000, 64, 1, 0.5)])
+                                       (16384, 40, 8, 0.5), (13000, 64, 1, 0.5),
+                                       (20000, 64, 1, 0.5)])
 def test_permute_reroute_common_order(moe, T, E, k, phi):
     """Every token has the same preference order (identical rows of x), so the
     dropped routes fill the experts one after another in that order: the
     longest chain of rejections the parallel kernel can meet (about one round
-    per expert), with its per-token state in LDS or (T=8000, 16384) in the
-    workspace, and, at T=13000 over 64 experts, the same inputs through the
-    walk."""
+    per expert), with its per-token state in LDS or (T = 8000, 16384, 13000)
+    in the workspace, and, at T = 20000 over 64 experts, the same inputs
+    through the walk."""
     w = Workload("common_order", T=T, E=E, k=k, d=64, d_ff=32, renorm=0, phi=phi, bias="zipf")
     inp = make_inputs(w, seed=5)
     inp["x"] = inp["x"][:1].repeat(T, 1).contiguous()
