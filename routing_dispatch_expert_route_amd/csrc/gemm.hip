@@ -42,7 +42,37 @@ struct GemmArgs {
   int splits;         // K splits (partial-plane output when > 1)
   int k_chunk;        // K elements per split, a multiple of 64
   unsigned a_bytes;   // extent of A in bytes (< 2^31; buffer range of the activation loads)
+  // Combine fused into the down projection (one route per token, no shared
+  // expert; y_tok != nullptr): output row p is token y_tok[p]'s, scaled by
+  // its gate y_gate[token] and written to row y_tok[p] of C ([T][N]) -- the
+  // rounding of the separate combine kept: the row is rounded to bf16 first,
+  // then gate * value (an FMA onto +0) is rounded again.  Workgroups from
+  // main_blocks on write the zero rows of the tokens whose route was dropped
+  // (y_pos[t] < 0).
+  const int32_t* y_tok;
+  const float* y_gate;
+  const int32_t* y_pos;
+  int y_T;
+  int main_blocks;
 };
+
+// Tokens per zero-row workgroup of the fused combine.
+constexpr int kZeroTok = 16;
+
+// The zero rows of workgroup z of the fused combine: tokens [z*kZeroTok,
+// (z+1)*kZeroTok) whose route was dropped, 16 bytes per thread and store.
+__device__ __forceinline__ void zero_dropped_rows(const GemmArgs& a, int z) {
+  const int cpr = a.N / 8;  // 16-byte chunks per row (N % 8 == 0)
+  const int t0 = z * kZeroTok;
+  const int nt = min(kZeroTok, a.y_T - t0);
+  const u32x4_t zero = {0u, 0u, 0u, 0u};
+  for (int i = threadIdx.x; i < nt * cpr; i += blockDim.x) {
+    const int t = t0 + i / cpr;
+    if (a.y_pos[t] < 0)
+      *reinterpret_cast<u32x4_t*>(reinterpret_cast<bf16_t*>(a.C) + (size_t)t * a.N +
+                                  (size_t)(i % cpr) * 8) = zero;
+  }
+}
 
 // Find the (expert, first row, row count) of row-tile mt.  Executed by one
 // wave; the lane that owns the tile writes the result to info[0..2]
@@ -242,6 +272,12 @@ __global__ __launch_bounds__(64 * WM * WN, OCC) void gemm_bf16_kernel(GemmArgs a
   // feed buffer descriptors and LDS load destinations, which must be scalar
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave / WN, wn = wave % WN;
+  if constexpr (!SWIGLU && !PARTIAL) {
+    if (a.y_tok && (int)blockIdx.x >= a.main_blocks) {  // whole workgroup, before any barrier
+      zero_dropped_rows(a, (int)blockIdx.x - a.main_blocks);
+      return;
+    }
+  }
   if (wave == 0) {
     int mt0 = 0, nt0 = 0, ks0 = 0;
     if (tile_of_block(a, count_row_tiles<BM>(a, lane), mt0, nt0, ks0)) {
@@ -508,6 +544,14 @@ __global__ __launch_bounds__(64 * WM * WN, OCC) void gemm_bf16_kernel(GemmArgs a
           float* Cp = reinterpret_cast<float*>(a.C) + (size_t)ks * a.split_stride;
           f32x4_t v = {o[0], o[1], o[2], o[3]};
           *reinterpret_cast<f32x4_t*>(Cp + p * N + n) = v;
+        } else if (!SWIGLU && a.y_tok) {
+          const int tk = a.y_tok[p];
+          const float g = a.y_gate[tk];
+          const uint32_t r0 = pack_bf16x2(o[0], o[1]), r1 = pack_bf16x2(o[2], o[3]);
+          uint2 v;
+          v.x = pack_bf16x2(__builtin_fmaf(g, bf16lo(r0), 0.0f), __builtin_fmaf(g, bf16hi(r0), 0.0f));
+          v.y = pack_bf16x2(__builtin_fmaf(g, bf16lo(r1), 0.0f), __builtin_fmaf(g, bf16hi(r1), 0.0f));
+          *reinterpret_cast<uint2*>(reinterpret_cast<bf16_t*>(a.C) + (size_t)tk * N + n) = v;
         } else {
           bf16_t* Cp = reinterpret_cast<bf16_t*>(a.C);
           uint2 v;
@@ -617,13 +661,15 @@ static hipError_t run_bf16(const GemmPlan& pl, GemmArgs a, hipStream_t st) {
   a.m_tiles = (int)row_tile_bound(pl, BM);
   // an upper bound on the tiles, rounded up to whole rounds of the 8 XCDs
   const long blocks = ((long)a.m_tiles * a.n_tiles * a.splits + 7) / 8 * 8;
-  if (blocks == 0) return hipSuccess;
+  a.main_blocks = (int)blocks;
+  const long grid = blocks + (a.y_tok ? (a.y_T + kZeroTok - 1) / kZeroTok : 0);
+  if (grid == 0) return hipSuccess;
   if (a.a_rows)
     hipLaunchKernelGGL((gemm_bf16_kernel<BM, BNW, WM, WN, BK, NSX, NSW, OCC, SWIGLU, true, PARTIAL>),
-                       dim3((unsigned)blocks), dim3(64 * WM * WN), 0, st, a);
+                       dim3((unsigned)grid), dim3(64 * WM * WN), 0, st, a);
   else
     hipLaunchKernelGGL((gemm_bf16_kernel<BM, BNW, WM, WN, BK, NSX, NSW, OCC, SWIGLU, false, PARTIAL>),
-                       dim3((unsigned)blocks), dim3(64 * WM * WN), 0, st, a);
+                       dim3((unsigned)grid), dim3(64 * WM * WN), 0, st, a);
   return hipGetLastError();
 }
 
@@ -687,6 +733,16 @@ hipError_t launch_gemm_swiglu(const GemmPlan& pl, const void* A, const int32_t* 
              (unsigned)(a_nrows * K * 2)};
   if (!pl.bf16) return run_f32<true>(pl, a, st);
   return run_cfg<true, false>(pl, a, st);
+}
+
+hipError_t launch_gemm_down_combine(const GemmPlan& pl, const void* H, const void* Wd, int N,
+                                    int K, const int32_t* row_token, const float* gates,
+                                    const int32_t* route_pos, int T, void* y, hipStream_t st) {
+  if (!pl.bf16 || N % 8) return hipErrorInvalidValue;
+  const long h_rows = pl.grouped ? pl.R_max : pl.M_dense;
+  GemmArgs a{H, nullptr, pl.offsets, pl.E, pl.M_dense, Wd, nullptr, N, K, y, 0, 0, 0,
+             1, K, (unsigned)(h_rows * K * 2), row_token, gates, route_pos, T, 0};
+  return run_cfg<false, false>(pl, a, st);
 }
 
 hipError_t launch_gemm_down(const GemmPlan& pl, const void* H, const void* Wd, int N, int K,

@@ -98,6 +98,14 @@ hipError_t launch_gemm_swiglu(const GemmPlan& pl, const void* A, const int32_t* 
 int gemm_down_splits(const GemmPlan& pl, int N, int K);
 hipError_t launch_gemm_down(const GemmPlan& pl, const void* H, const void* Wd, int N, int K,
                             void* Y, int splits, long split_stride, hipStream_t st);
+// The down GEMM with the combine of one route per token (no shared expert,
+// no K split, bf16, N % 8 == 0) fused: packed row p, of token row_token[p],
+// is scaled by gates[token] and written to row token of y [T][N]; tokens
+// with route_pos[t] < 0 get zero rows.  Bit-identical to launch_gemm_down
+// followed by launch_combine with k = 1.
+hipError_t launch_gemm_down_combine(const GemmPlan& pl, const void* H, const void* Wd, int N,
+                                    int K, const int32_t* row_token, const float* gates,
+                                    const int32_t* route_pos, int T, void* y, hipStream_t st);
 
 // y_packed is dtype rows (splits == 1) or fp32 partial planes (splits > 1,
 // plane stride split_stride elements).

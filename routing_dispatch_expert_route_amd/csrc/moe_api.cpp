@@ -494,6 +494,15 @@ static int experts_and_combine(const moe_shape* s, const Layout& L, const moe::G
   hipError_t e = moe::launch_gemm_swiglu(pl, A, a_rows, a_nrows, w_gate, w_up, dff, d, h, stream);
   if (e != hipSuccess) return MOE_ERR_HIP;
   mark(3);
+  if (bf16 && splits <= 1 && s->d_ff_shared == 0 && kslots == 1 && !slot_major && a_rows) {
+    // one route per token and nothing to add: the down GEMM writes y itself
+    e = moe::launch_gemm_down_combine(pl, h, w_down, d, dff, a_rows, g, rpos, T, y, stream);
+    if (e != hipSuccess) return MOE_ERR_HIP;
+    mark(4);
+    mark(5);
+    mark(6);
+    return MOE_OK;
+  }
   const void* yrows = yp;
   const long stride = rows * d;
   if (splits > 1) {

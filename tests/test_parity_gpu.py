@@ -405,3 +405,38 @@ def test_layer_dropped_route_keeps_only_other_gate(moe):
     y = _layer_check(moe, w, inp)
     e2 = oracle.swiglu_rows(x[5:6], inp["w_gate"][1], inp["w_up"][1], inp["w_down"][1])[0]
     assert np.allclose(_np(y[5]), 0.4256 * e2, rtol=2e-3, atol=1e-6)
+
+
+FUSED = {
+    "switch_phi125": WORKLOADS["switch_phi125"],
+    "switch_phi1": WORKLOADS["switch_phi1"],
+    "k1_ragged_drops": Workload("k1_ragged", T=515, E=6, k=1, d=72, d_ff=40, renorm=0, phi=0.7,
+                                bias="normal"),
+}
+
+
+@pytest.mark.parametrize("name,reroute", [(n, False) for n in FUSED] + [("switch_phi125", True)])
+def test_top1_layer_equals_its_pieces(moe, name, reroute):
+    """With one route per token and no shared expert the layer's down GEMM
+    writes y itself (gate-scaled rows, zero rows for dropped tokens).  Its
+    output is the separate entry points' -- permute, expert_ffn, combine on
+    the same routing -- bit for bit, and a dropped token's row is zero."""
+    w = FUSED[name]
+    inp = host_inputs(name) if name in WORKLOADS else make_inputs(w, seed=21)
+    say(f"[top-1 layer vs pieces] {name} reroute={reroute}")
+    d = to_dev(inp)
+    s = moe.shape_of(w)
+    y, rt = moe.layer_forward(s, d["x"], d["w_router"], d["b_router"], d["w_gate"], d["w_up"],
+                              d["w_down"], return_routing=True, reroute=reroute)
+    ids, gates, logits = moe.route(s, d["x"], d["w_router"], d["b_router"], want_logits=True)
+    logits = logits.clone()
+    out = (moe.permute_reroute(s, d["x"], logits, ids) if reroute
+           else moe.permute(s, d["x"], ids))
+    yp = moe.expert_ffn(s, out["x_packed"], out["offsets"], d["w_gate"], d["w_up"], d["w_down"])
+    y2 = moe.combine(s, yp, out["route_pos"], gates)
+    torch.cuda.synchronize()
+    assert np.array_equal(_np(rt["route_pos"]), _np(out["route_pos"]))
+    assert np.array_equal(bits(y), bits(y2)), f"{name}: fused layer differs from its pieces"
+    dropped = _np(out["route_pos"]).reshape(-1) < 0
+    assert not bits(y)[dropped].any()
+    say(f"   {name}: {int(dropped.sum())} dropped tokens, bit-identical")
