@@ -420,7 +420,8 @@ def test_top1_layer_equals_its_pieces(moe, name, reroute):
     """With one route per token and no shared expert the layer's down GEMM
     writes y itself (gate-scaled rows, zero rows for dropped tokens).  Its
     output is the separate entry points' -- permute, expert_ffn, combine on
-    the same routing -- bit for bit, and a dropped token's row is zero."""
+    the same routing -- bit for bit, a dropped token's row is zero, and the
+    layer agrees with the oracle to the layer tolerance."""
     w = FUSED[name]
     inp = host_inputs(name) if name in WORKLOADS else make_inputs(w, seed=21)
     say(f"[top-1 layer vs pieces] {name} reroute={reroute}")
@@ -439,4 +440,14 @@ def test_top1_layer_equals_its_pieces(moe, name, reroute):
     assert np.array_equal(bits(y), bits(y2)), f"{name}: fused layer differs from its pieces"
     dropped = _np(out["route_pos"]).reshape(-1) < 0
     assert not bits(y)[dropped].any()
+    if not reroute:
+        # and the layer itself against the oracle (all tokens of the small
+        # case, sampled tokens at full size)
+        sel = None if w.T <= 1024 else sample_tokens(w.T, _np(out["route_pos"]),
+                                                     _np(out["offsets"]), _np(out["row_token"]),
+                                                     n_random=32)
+        ref = oracle.layer_forward(inp["x"], inp["w_router"], inp["b_router"], inp["w_gate"],
+                                   inp["w_up"], inp["w_down"], w.k, w.renorm, w.phi, sel=sel)
+        got = y if sel is None else y[torch.from_numpy(sel).long().cuda()]
+        check_y(got, ref["y"], w.dtype, f"top-1 layer {name}")
     say(f"   {name}: {int(dropped.sum())} dropped tokens, bit-identical")
