@@ -219,6 +219,9 @@ def main():
     ap.add_argument("--queue", action="store_true",
                     help="queue-to-the-next-micro-batch overflow policy: each step processes the "
                          "batch plus the routes one earlier batch left waiting")
+    ap.add_argument("--phi", type=float, default=None,
+                    help="override the workload's capacity factor (0: no capacity); the line's "
+                         "config names the value, and no committed traffic figure applies")
     ap.add_argument("--no-graph", action="store_true",
                     help="skip the HIP-graph replay timing (graph_ms_per_step)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB")
@@ -242,6 +245,8 @@ def main():
     from workloads import WORKLOADS, make_inputs
 
     w = WORKLOADS[args.workload]
+    if args.phi is not None:
+        w = w.with_(phi=args.phi)
     if args.choice:  # expert choice needs a capacity and full softmax gates
         w = w.with_(renorm=0, phi=w.phi if w.phi > 0 else 1.0)
     dev = torch.device("cuda:0")
@@ -468,7 +473,8 @@ def main():
         roof["us_per_launch"] = round(g1_us, 2)
         roof["algorithmic_flops"] = flops
         roof["algorithmic_bytes"] = byts
-        roof["traffic"] = (None if (args.padded or args.reroute or args.choice or args.queue)
+        roof["traffic"] = (None if (args.padded or args.reroute or args.choice or args.queue
+                                    or args.phi is not None)
                            else traffic_from_profile(w.name))
 
     layer_roof = None
