@@ -454,11 +454,13 @@ constexpr int kRerouteMaxE = 64;
 template <bool ORDER>
 __global__ __launch_bounds__(256) void reroute_rank_kernel(const float* __restrict__ logits,
                                                            const int32_t* __restrict__ route_pos0,
-                                                           int R, int k, int E,
+                                                           const int32_t* __restrict__ offsets0,
+                                                           int R, int k, int E, int C,
                                                            uint8_t* __restrict__ rank) {
   const long g = (long)blockIdx.x * blockDim.x + threadIdx.x;
   const int r = (int)(g / kRerouteMaxE), e = (int)(g % kRerouteMaxE);
   if (r >= R || e >= E || route_pos0[r] >= 0) return;
+  if (ORDER && offsets0[E] >= (long)E * C) return;  // every seat taken: nothing moves
   const float* l = logits + (size_t)(r / k) * E;
   const float le = l[e];
   int rk = 0;
@@ -690,8 +692,9 @@ __device__ __forceinline__ int chunk_byte(const u32x4_t& c, int p) {
 
 template <bool TOK_LDS>
 __global__ __launch_bounds__(kDaThreads) void reroute_da_kernel(
-    const uint8_t* __restrict__ order, const int32_t* __restrict__ kept, int T, int E, int C,
-    int32_t* __restrict__ offsets, uint8_t* __restrict__ region) {
+    const uint8_t* __restrict__ order, const int32_t* __restrict__ offsets0,
+    const int32_t* __restrict__ kept, int T, int E, int C, int32_t* __restrict__ offsets,
+    uint8_t* __restrict__ region) {
   __shared__ __attribute__((aligned(16))) uint8_t arena[kDaArena];
   __shared__ int s_kept[kRerouteMaxE], s_free[kRerouteMaxE], s_new[kRerouteMaxE],
       s_fill[kRerouteMaxE];
@@ -722,6 +725,14 @@ __global__ __launch_bounds__(kDaThreads) void reroute_da_kernel(
   uint8_t* need = tb + L.need;
   uint8_t* next = tb + L.next;
 
+  if (offsets0[E] >= (long)E * C) {  // every seat taken: the seats stay the drop policy's
+    if (wv == 0) {
+      const int inc = wave_incl_scan(lane < E ? kept[lane] : 0, lane);
+      if (lane == 0) offsets[0] = 0;
+      if (lane < E) offsets[lane + 1] = inc;
+    }
+    return;
+  }
   if (tid < E) {
     const int kp = kept[tid];
     s_kept[tid] = kp;
@@ -926,16 +937,18 @@ __global__ __launch_bounds__(256) void reroute_tok_kernel(
 // accepted tokens before it (token order); with none left it stays dropped.
 __global__ __launch_bounds__(256) void reroute_seat_kernel(
     const uint8_t* __restrict__ order, const int32_t* __restrict__ ids_in,
-    const int32_t* __restrict__ route_pos0, const int32_t* __restrict__ kept, int T, int k, int E,
-    int32_t* __restrict__ ids_out, int32_t* __restrict__ slot,
-    const uint8_t* __restrict__ region) {
+    const int32_t* __restrict__ route_pos0, const int32_t* __restrict__ offsets0,
+    const int32_t* __restrict__ kept, int T, int k, int E, int C, int32_t* __restrict__ ids_out,
+    int32_t* __restrict__ slot, const uint8_t* __restrict__ region) {
   const int t = blockIdx.x * blockDim.x + threadIdx.x;
   if (t >= T) return;
   const RrLayout G = rr_layout(T, E, true);
   if (region[G.tneed + t] == 0) return;
   const int W = (T + 31) / 32;
-  const int a = reinterpret_cast<const int32_t*>(region + G.tidx)[t];
-  uint64_t h = reinterpret_cast<const uint64_t*>(region + G.thold)[t];
+  // every seat taken: the rounds wrote nothing and every dropped route stays
+  const bool full = offsets0[E] >= (long)E * C;
+  const int a = full ? 0 : reinterpret_cast<const int32_t*>(region + G.tidx)[t];
+  uint64_t h = full ? 0 : reinterpret_cast<const uint64_t*>(region + G.thold)[t];
   const int rf = reinterpret_cast<const int32_t*>(region + G.tfirst)[t];
   const uint32_t* gheld = reinterpret_cast<const uint32_t*>(region + G.gheld);
   const uint16_t* gpre = reinterpret_cast<const uint16_t*>(region + G.gpre);
@@ -996,11 +1009,11 @@ hipError_t launch_reroute(const float* logits, const int32_t* ids_in, const int3
     const long threads = (long)R * kRerouteMaxE;
     const dim3 grid((unsigned)((threads + 255) / 256));
     if (kind == RerouteKind::kWalk)
-      hipLaunchKernelGGL(reroute_rank_kernel<false>, grid, dim3(256), 0, st, logits, route_pos0, R,
-                         k, E, pref);
+      hipLaunchKernelGGL(reroute_rank_kernel<false>, grid, dim3(256), 0, st, logits, route_pos0,
+                         offsets0, R, k, E, C, pref);
     else
-      hipLaunchKernelGGL(reroute_rank_kernel<true>, grid, dim3(256), 0, st, logits, route_pos0, R,
-                         k, E, pref);
+      hipLaunchKernelGGL(reroute_rank_kernel<true>, grid, dim3(256), 0, st, logits, route_pos0,
+                         offsets0, R, k, E, C, pref);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
   }
@@ -1014,14 +1027,14 @@ hipError_t launch_reroute(const float* logits, const int32_t* ids_in, const int3
       hipLaunchKernelGGL(reroute_tok_kernel, tgrid, dim3(256), 0, st, ids_in, route_pos0, offsets0,
                          T, k, E, ids_out, slot, da_state);
     if (kind == RerouteKind::kDaLds)
-      hipLaunchKernelGGL(reroute_da_kernel<true>, dim3(1), dim3(kDaThreads), 0, st, pref, kept, T,
-                         E, C, offsets, da_state);
+      hipLaunchKernelGGL(reroute_da_kernel<true>, dim3(1), dim3(kDaThreads), 0, st, pref, offsets0,
+                         kept, T, E, C, offsets, da_state);
     else
-      hipLaunchKernelGGL(reroute_da_kernel<false>, dim3(1), dim3(kDaThreads), 0, st, pref, kept, T,
-                         E, C, offsets, da_state);
+      hipLaunchKernelGGL(reroute_da_kernel<false>, dim3(1), dim3(kDaThreads), 0, st, pref,
+                         offsets0, kept, T, E, C, offsets, da_state);
     if (T > 0)
       hipLaunchKernelGGL(reroute_seat_kernel, tgrid, dim3(256), 0, st, pref, ids_in, route_pos0,
-                         kept, T, k, E, ids_out, slot, da_state);
+                         offsets0, kept, T, k, E, C, ids_out, slot, da_state);
   }
   hipError_t err = hipGetLastError();
   if (err != hipSuccess || R == 0) return err;
