@@ -595,6 +595,40 @@ def test_reroute_trace_spk():
     assert out["row_token"][lo:lo + 4].tolist() == G.nums(g[f"slots_E{third}"], int) + [5]
 
 
+def test_reroute_ties_take_lowest_index():
+    """Ties in the reroute: among free experts with equal logits a dropped
+    route takes the lowest index ("Session 19", "Overflow policies": the
+    overflowing route goes to the token's next-best expert; ties broken by
+    the lowest expert index, as in the router's own top-k).  Expected values
+    derived by hand.
+
+    Top-1, E = 4, T = 3, C = ceil(1.0 * 3 / 4) = 1, every token's logits
+    [3, 1, 1, 0]: t0 takes E0; t1 overflows E0, E1 and E2 tie -> E1; t2
+    overflows E0, E1 is now full -> E2 (its tie partner); E3 stays empty.
+    Top-2, E = 5, T = 2, C = ceil(0.5 * 4 / 5) = 1, logits [4, 3, 1, 1, 1]:
+    t0 holds E0, E1; t1 loses both, E2..E4 tie -> E2 then E3."""
+    L = np.array([[3, 1, 1, 0]] * 3, np.float32)
+    ids, _ = oracle.topk_gates(L, 1, 0)
+    assert ids[:, 0].tolist() == [0, 0, 0]
+    C = oracle.capacity(3, 4, 1, 1.0)
+    assert C == 1
+    out = oracle.dispatch_reroute(L, ids, 4, C)
+    assert out["ids"][:, 0].tolist() == [0, 1, 2]
+    assert out["filled"].tolist() == [1, 1, 1, 0]
+    assert out["route_pos"][:, 0].tolist() == [0, 1, 2]
+    assert out["n_rerouted"] == 2
+
+    L2 = np.array([[4, 3, 1, 1, 1]] * 2, np.float32)
+    ids2, _ = oracle.topk_gates(L2, 2, 1)
+    assert ids2.tolist() == [[0, 1], [0, 1]]
+    C2 = oracle.capacity(2, 5, 2, 0.5)
+    assert C2 == 1
+    out2 = oracle.dispatch_reroute(L2, ids2, 5, C2)
+    assert out2["ids"].tolist() == [[0, 1], [2, 3]]
+    assert out2["filled"].tolist() == [1, 1, 1, 1, 0]
+    assert out2["route_pos"].tolist() == [[0, 1], [2, 3]]
+
+
 def _reroute_invariants(L, ids, E, C, out, ref):
     T, k = ids.shape
     fids, rp = out["ids"], out["route_pos"]
