@@ -8,7 +8,11 @@ several device copies of the expert weights (enough copies to exceed the
 weights are read cold from HBM every step.
 
 Prints ONE JSON line:
-  value          whole-step tokens/s (T / step time)
+  value          whole-step tokens/s: T / (wall time of the K timed steps / K),
+                 the steps bracketed by device synchronisations
+  step_us        p10 / median / p90 of the same K steps' GPU time, from
+                 hipEvents recorded on the library's stream at the start and
+                 end of every timed step
   roofline       dominant kernel (grouped GEMM 1, gate+up+SwiGLU) against
                  the MI355X bf16 dense MFMA peak or the HBM peak, timed with
                  hipEvents recorded on the library's stream around it in
@@ -17,6 +21,7 @@ Prints ONE JSON line:
                  taken on another version of the GEMM source)
   cpu_baseline   the CPU oracle on a bounded sample of the same workload
   stages_us      mean per-stage times of a second, fully event-marked pass
+                 (stage_step_us_percentiles: that pass's per-step times)
   routing_stats  forward-only routing statistics of the batch (Switch
                  aux-loss value with alpha 1e-2, demand imbalance, ...) and
                  the time of one moe_routing_stats call
@@ -47,7 +52,10 @@ PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_F32_TFLOPS = 157.3     # MI355X fp32 (vector)
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 MALL_BYTES = 256 << 20
-DEFAULT_WORKLOAD = "switch_phi125"
+# The largest configuration that fits one GPU: Mixtral-like prefill (E=8,
+# top-2, d=4096, d_ff=14336, T=8192; 5.77 TFLOP per step, MFMA-bound).
+DEFAULT_WORKLOAD = "mixtral_prefill"
+METRIC = "MoE layer tokens/s at 1 GPU; % of MFMA peak (large T) / HBM BW (small T)"
 STAGES = ["route", "permute", "gemm1_gate_up_swiglu", "gemm2_down", "shared_expert", "combine"]
 
 
@@ -181,11 +189,20 @@ def cpu_baseline(w, inp, seconds, choice=False):
                                  inp["ws_up"], inp["ws_down"], sel=sel)
         return time.perf_counter() - t0
 
-    n0 = min(w.T, max(1, cores))
-    t_route = run(1)                      # routing of all T tokens + one token's FFN
-    t0 = max(run(n0) - t_route, 1e-3)     # per-token FFN cost from n0 tokens
-    n = int(min(w.T, max(n0, n0 * (seconds - t_route) / t0)))
-    t = run(n)
+    t_route = run(0)                      # routing of all T tokens, no FFN
+    # grow the FFN sample geometrically until it takes a quarter of the
+    # budget, then extrapolate to the budget (the whole run stays within
+    # about 1.5x the budget however slow a token is)
+    n = min(w.T, max(1, cores))
+    while True:
+        t = run(n)
+        if n == w.T or t >= seconds / 4:
+            break
+        n = min(w.T, 4 * n)
+    grow = (seconds - t_route) / max(t - t_route, 1e-3)
+    if grow > 1.25 and n < w.T:
+        n = int(min(w.T, n * grow))
+        t = run(n)
     reps = 1
     if n == w.T:                          # the whole workload fits: repeat it
         while t < seconds:
@@ -196,6 +213,53 @@ def cpu_baseline(w, inp, seconds, choice=False):
             f"expert FFN + combine of the {n})")
     return {"value": n * reps / t, "unit": "tokens/s", "cores": cores, "kind": "oracle",
             "sample": f"{what}, {t:.1f} s wall", "cpu_model": _cpu_model()}
+
+
+def blas_reference(w, kept, steps, dev):
+    """The expert GEMMs' shapes on the vendor library (torch.nn.functional.linear
+    in bf16, i.e. hipBLASLt): for every active expert e, its m_e rows times
+    [W_gate; W_up][e]^T (one GEMM of 2*d_ff outputs), then m_e rows times
+    W_down[e]^T.  A dense-GEMM reference for this GPU's reachable MFMA rate on
+    the same per-expert shapes -- no SwiGLU, no gather, one launch per expert
+    -- timed with events around the gate/up and the down launches of each
+    pass.  Not part of the MoE path."""
+    import torch
+    import torch.nn.functional as F
+    g = torch.Generator(device="cpu").manual_seed(1)
+    act = [int(m) for m in kept.tolist() if m > 0]
+    wgu = [torch.randn(2 * w.d_ff, w.d, generator=g).to(torch.bfloat16).to(dev) for _ in act]
+    wd = [torch.randn(w.d, w.d_ff, generator=g).to(torch.bfloat16).to(dev) for _ in act]
+    xs = [torch.randn(m, w.d, generator=g).to(torch.bfloat16).to(dev) for m in act]
+    hs = [torch.randn(m, w.d_ff, generator=g).to(torch.bfloat16).to(dev) for m in act]
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(3 * steps)]
+
+    def one_pass():
+        for x_, wg_ in zip(xs, wgu):
+            F.linear(x_, wg_)
+
+    def down_pass():
+        for h_, wd_ in zip(hs, wd):
+            F.linear(h_, wd_)
+
+    for _ in range(2):
+        one_pass()
+        down_pass()
+    torch.cuda.synchronize()
+    for i in range(steps):
+        ev[3 * i].record()
+        one_pass()
+        ev[3 * i + 1].record()
+        down_pass()
+        ev[3 * i + 2].record()
+    torch.cuda.synchronize()
+    t1 = sorted(ev[3 * i].elapsed_time(ev[3 * i + 1]) for i in range(steps))[steps // 2]
+    t2 = sorted(ev[3 * i + 1].elapsed_time(ev[3 * i + 2]) for i in range(steps))[steps // 2]
+    rows = sum(act)
+    f1 = 2.0 * rows * w.d * 2 * w.d_ff
+    f2 = 2.0 * rows * w.d_ff * w.d
+    return {"library": "torch.nn.functional.linear bf16 (hipBLASLt)", "experts": len(act),
+            "rows": rows, "gate_up_ms": round(t1, 4), "gate_up_tflops": round(f1 / t1 / 1e9, 1),
+            "down_ms": round(t2, 4), "down_tflops": round(f2 / t2 / 1e9, 1)}
 
 
 def main():
@@ -224,6 +288,9 @@ def main():
                          "config names the value, and no committed traffic figure applies")
     ap.add_argument("--no-graph", action="store_true",
                     help="skip the HIP-graph replay timing (graph_ms_per_step)")
+    ap.add_argument("--blas-reference", action="store_true",
+                    help="also time the expert GEMMs' per-expert shapes on hipBLASLt "
+                         "(blas_reference: a dense-GEMM reference, not the MoE path)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB")
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
     ap.add_argument("--traffic-out", default=None)
@@ -341,23 +408,31 @@ def main():
         assert hip.hipEventElapsedTime(ctypes.byref(f), a, b) == 0
         return f.value * 1e3
 
-    # timed region: K steps, GEMM 1 bracketed by hipEvents on the library's
-    # stream in every step (the other stage boundaries are not marked here)
+    # timed region: K steps, each bracketed by hipEvents on the library's
+    # stream, and GEMM 1 inside it too (the other stage boundaries are not
+    # marked here)
     K = args.steps
-    g1_ev = new_events(2 * K)
+    ev = new_events(4 * K)
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(K):
-        timed(sets[i % nsets], [None, None, g1_ev[2 * i], g1_ev[2 * i + 1], None, None, None])
+        e4 = ev[4 * i:4 * i + 4]
+        timed(sets[i % nsets], [e4[0], None, e4[1], e4[2], None, None, e4[3]])
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms = (t1 - t0) * 1e3 / K
     value = w.T / (ms / 1e3)
-    g1_us = sum(elapsed_us(g1_ev[2 * i], g1_ev[2 * i + 1]) for i in range(K)) / K
-    for e in g1_ev:
+    g1_us = sum(elapsed_us(ev[4 * i + 1], ev[4 * i + 2]) for i in range(K)) / K
+    step_us = sorted(elapsed_us(ev[4 * i], ev[4 * i + 3]) for i in range(K))
+    for e in ev:
         hip.hipEventDestroy(e)
+
+    def pct(v, q):
+        return round(v[min(len(v) - 1, int(q * len(v)))], 2)
+
+    step_ev = {"p10": pct(step_us, 0.1), "median": pct(step_us, 0.5), "p90": pct(step_us, 0.9)}
 
     # the same steps replayed from a HIP graph (one captured step per weight
     # set, replayed until K steps ran): the launch sequence without the host,
@@ -404,11 +479,8 @@ def main():
             hip.hipEventDestroy(e)
         stages = {n: round(a / K, 2) for n, a in zip(STAGES, acc)}
         per_step.sort()
-
-        def pct(q):
-            return round(per_step[min(len(per_step) - 1, int(q * len(per_step)))], 2)
-
-        step_pct = {"p10": pct(0.1), "p50": pct(0.5), "p90": pct(0.9)}
+        step_pct = {"p10": pct(per_step, 0.1), "p50": pct(per_step, 0.5),
+                    "p90": pct(per_step, 0.9)}
 
         # warm caches: the same K steps on one weight set (MALL-resident
         # when the weights fit), labelled as such
@@ -489,12 +561,16 @@ def main():
                       "frac_mfma": round(fm, 4), "frac_hbm": round(fh, 4),
                       "frac": round(max(fm, fh), 4)}
 
+    blas = None
+    if args.blas_reference and w.dtype == "bf16":
+        blas = blas_reference(w, kept, max(5, min(K, 20)), dev)
+
     cpu = None
     if not args.no_cpu:
         cpu = cpu_baseline(w, inp, args.cpu_seconds, choice=args.choice)
 
     out = {
-        "metric": "MoE layer forward tokens/s at 1 GPU",
+        "metric": METRIC,
         "value": round(value, 1),
         "unit": "tokens/s",
         "n_gpus": 1,
@@ -523,13 +599,16 @@ def main():
                    "parallelism": "single GPU"},
         "roofline": roof,
         "layer_roofline": layer_roof,
-        "step_us_percentiles": step_pct,
+        "step_us": step_ev,
+        "stage_step_us_percentiles": step_pct,
         "warm_ms_per_step": round(warm_ms, 5) if warm_ms else None,
         "graph_ms_per_step": round(graph_ms, 5) if graph_ms else None,
         "cpu_baseline": cpu,
         "stages_us": stages,
         "routing_stats": rstats,
     }
+    if blas is not None:
+        out["blas_reference"] = blas
     print(json.dumps(out), flush=True)
 
 

@@ -65,6 +65,12 @@ CASES = {
     "t16384_e32": (Workload("t16384", T=16384, E=32, k=8, d=64, d_ff=32, phi=1.0, renorm=0), None),
     "t32768_max": (Workload("t32768", T=32768, E=8, k=2, d=32, d_ff=16, phi=0.7, renorm=0,
                             bias="normal"), None),
+    # the full-size MFMA-bound shapes under expert choice (the layer is
+    # checked on sampled tokens)
+    "granite_16384": (WORKLOADS["granite_16384"].with_(name="granite16k_ec", renorm=0, phi=1.0),
+                      None),
+    "mixtral_prefill": (WORKLOADS["mixtral_prefill"].with_(name="mixtral_ec", renorm=0, phi=1.0),
+                        None),
 }
 
 
@@ -151,11 +157,15 @@ def test_layer_forward_expert_choice_parity(moe, name):
         rows[e * Ce:(e + 1) * Ce] = np.flatnonzero(P[:, e] >= 0)
     differ = _check_choice(w, rt["scores"], rt["route_pos"], rows, ref, name)
     rng = np.random.default_rng(3)
-    if w.T <= 400:
+    # every token when the oracle's FFN work is small; else 512 seeded
+    # tokens, the first and last, and every expert's first and last token
+    if 6.0 * (w.E * Ce * w.d * w.d_ff + w.T * w.d * w.d_ff_shared) <= 100e9:
         sel = np.arange(w.T)
     else:
-        sel = np.unique(np.concatenate([[0, w.T - 1], rng.choice(w.T, 96, replace=False),
-                                        ref["row_token"][::max(1, Ce)][:64]]))
+        firsts = np.concatenate([ref["row_token"][e * Ce:(e + 1) * Ce][[0, -1]]
+                                 for e in range(w.E) if Ce > 0])
+        sel = np.unique(np.concatenate([[0, w.T - 1], rng.choice(w.T, 512, replace=False),
+                                        firsts]))
     sel = np.array([t for t in sel if t not in differ], np.int32)
     yref = oracle.layer_forward_expert_choice(inp["x"], inp["w_router"], inp["b_router"],
                                               inp["w_gate"], inp["w_up"], inp["w_down"], C,

@@ -143,3 +143,46 @@ def test_permute_reroute_common_order(moe, T, E, k, phi):
     assert np.array_equal(_np(out["row_token"])[:n], ref["row_token"])
     C = oracle.capacity(T, E, k, phi)
     assert n == min(T * k, C * E)  # every expert full, or every route seated
+
+
+@pytest.mark.parametrize("T,E,k,phi", [(300, 8, 1, 1.0), (500, 16, 2, 1.0), (400, 32, 8, 1.0),
+                                       (8000, 8, 1, 1.25), (3000, 64, 2, 1.0),
+                                       (20000, 64, 2, 1.0)])
+def test_permute_reroute_exact_ties(moe, T, E, k, phi):
+    """Integer-valued x and router rows in {-1, 0, 1} (and a bias of 3 on
+    the first quarter of the experts, so they overflow) give integer logits,
+    so many of a dropped route's free experts tie exactly: the reroute must
+    take the lowest index among them ("Session 19", "Overflow policies", with
+    the router's tie rule), on every reroute kernel (state in LDS, in the
+    workspace at T = 8000, and the walk at T = 20000 over 64 experts)."""
+    say(f"[permute reroute ties] T={T} E={E} k={k} phi={phi}")
+    w = Workload("reroute_ties", T=T, E=E, k=k, d=64, d_ff=16, phi=phi)
+    g = torch.Generator().manual_seed(T + E + k)
+    x = torch.randint(-1, 2, (T, 64), generator=g).to(torch.bfloat16)
+    wr = torch.randint(-1, 2, (E, 64), generator=g).to(torch.bfloat16)
+    b = torch.zeros(E)
+    b[:E // 4] = 3.0
+    s = moe.shape_of(w)
+    xd = x.cuda()
+    ids, _, logits = moe.route(s, xd, wr.cuda(), b.cuda(), want_logits=True)
+    out = moe.permute_reroute(s, xd, logits, ids)
+    torch.cuda.synchronize()
+    L = oracle.router_logits(x, wr, b)
+    oids, _ = oracle.topk_gates(L, k, 1)
+    assert np.array_equal(_np(logits), L) and np.array_equal(_np(ids), oids)
+    ref = oracle.dispatch_reroute(L, oids, E, oracle.capacity(T, E, k, phi))
+    assert np.array_equal(_np(out["expert_ids"]), ref["ids"])
+    assert np.array_equal(_np(out["filled"]), ref["filled"])
+    assert np.array_equal(_np(out["offsets"]), ref["offsets"])
+    assert np.array_equal(_np(out["route_pos"]), ref["route_pos"])
+    n = int(ref["offsets"][-1])
+    assert np.array_equal(_np(out["row_token"])[:n], ref["row_token"])
+    # the inputs really exercise the rule: count rerouted routes whose expert
+    # tied with a higher-indexed expert the token did not hold
+    tied = 0
+    for t, j in zip(*np.nonzero(ref["ids"] != oids)):
+        e1 = ref["ids"][t, j]
+        held = set(ref["ids"][t].tolist())
+        tied += any(L[t, e] == L[t, e1] and e not in held for e in range(e1 + 1, E))
+    assert tied > 0, "no tie was broken"
+    say(f"   {ref['n_rerouted']} rerouted, {tied} of them chosen among tied experts")
