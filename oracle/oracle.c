@@ -49,16 +49,26 @@ void oracle_router_logits(int64_t T, int64_t d, int64_t E, int dtype,
                           const void* x, const void* w, const float* b,
                           float* logits) {
   /* [INT8] section 1: scores = x @ W_router + b_router, W stored [E][d].
-   * fp32 accumulation ([MML] section 4 casts the router logits to float);
-   * sequential fused multiply-add in increasing i, then the bias. */
+   * fp32 accumulation ([MML] section 4 casts the router logits to float)
+   * in the fixed order of oracle.h ("R64"): the hidden index i belongs to
+   * granule i / 8 and granule q to partial sum q mod 64; each partial sum
+   * is a chain of fmaf in increasing i from +0; the 64 partial sums are
+   * folded by halving (sum l += sum l+s for l < s, s = 32, 16, ..., 1);
+   * the bias is added to the result. */
 #pragma omp parallel for schedule(static)
   for (int64_t t = 0; t < T; t++) {
     for (int64_t e = 0; e < E; e++) {
-      float acc = 0.0f;
+      float part[64];
+      for (int l = 0; l < 64; l++) part[l] = 0.0f;
       for (int64_t i = 0; i < d; i++) {
-        acc = fmaf(elem_f(x, dtype, t * d + i), elem_f(w, dtype, e * d + i),
-                   acc);
+        const int l = (int)((i / 8) % 64);
+        part[l] = fmaf(elem_f(x, dtype, t * d + i), elem_f(w, dtype, e * d + i),
+                       part[l]);
       }
+      for (int s = 32; s >= 1; s /= 2) {
+        for (int l = 0; l < s; l++) part[l] = part[l] + part[l + s];
+      }
+      float acc = part[0];
       if (b) acc = acc + b[e];
       logits[t * E + e] = acc;
     }

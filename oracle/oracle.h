@@ -23,11 +23,10 @@
  *          "The maths": the gate, capacity and load-imbalance formulas.
  *
  * Precision.  Router logits are fp32 (the [MML] Granite experiment casts the
- * router logits to float before top-k), accumulated by a plain sequential
- * fused multiply-add over the hidden dimension in increasing index order;
- * that order is a reading of ours, because the pages leave it open and the
- * selected expert ids depend on it at near ties.  Gates, expert FFNs and the
- * combine are computed in double precision.
+ * router logits to float before top-k), accumulated in one fixed order, R64
+ * (see oracle_router_logits); that order is a reading of ours, because the
+ * pages leave it open and the selected expert ids depend on it at near ties.
+ * Gates, expert FFNs and the combine are computed in double precision.
  *
  * Element types: dtype 0 = IEEE binary32, dtype 1 = bfloat16 (raw 16-bit
  * patterns, the upper half of a binary32).  All arrays are row-major and
@@ -55,11 +54,18 @@ extern "C" {
  * the [INT8] overflow case (C = 2). */
 int64_t oracle_capacity(int64_t T, int64_t E, int64_t k, double phi);
 
-/* Router logits, fp32: logits[t][e] = sum_i x[t][i] * w[e][i] (+ b[e]),
- * accumulated with fmaf in increasing i, bias added after the sum
+/* Router logits, fp32: logits[t][e] = sum_i x[t][i] * w[e][i] (+ b[e])
  * ([INT8] section 1: x @ W_router + b_router; [BEA] "The Router": one
  * 768-wide dot product per expert row).  b may be NULL.
- * Pinned against fp64 dot products within the fp32 error bound. */
+ * Summation order R64: hidden index i lies in granule q = i / 8 (eight
+ * consecutive elements); granule q is accumulated into partial sum
+ * l = q mod 64, each partial sum a chain of fmaf over its elements in
+ * increasing i, starting from +0; then for s = 32, 16, 8, 4, 2, 1 the
+ * partial sums are folded, p[l] = p[l] + p[l + s] for l < s; the logit is
+ * p[0], and the bias is added last.
+ * Pinned against fp64 dot products within the fp32 error bound, and by
+ * hand-derived sums whose rounding depends on the order (a 2^24 term with
+ * unit terms in chosen granules). */
 void oracle_router_logits(int64_t T, int64_t d, int64_t E, int dtype,
                           const void* x, const void* w, const float* b,
                           float* logits);

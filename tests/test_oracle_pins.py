@@ -133,11 +133,58 @@ def test_router_logits_within_fp32_bound(dtype):
     Wr = inp["w_router"].double().numpy()
     ref = X @ Wr.T + inp["b_router"].double().numpy()
     assert np.allclose(L64, ref, rtol=0, atol=1e-12)
-    # sequential fp32 summation: |err| <= gamma_d * sum|x_i w_i| + bias rounding
+    # R64 order: every term passes through at most 8*ceil(d/512) fused
+    # multiply-adds of its partial sum and 6 folds, so |err| <= gamma_n *
+    # sum|x_i w_i| with n = 8*ceil(d/512) + 6, plus the bias rounding
     u = 2.0 ** -24
-    gam = w.d * u / (1 - w.d * u)
+    n = 8 * -(-w.d // 512) + 6
+    gam = n * u / (1 - n * u)
     bound = gam * (np.abs(X) @ np.abs(Wr).T) + 2 * u * (np.abs(ref) + 1)
     assert np.all(np.abs(L.astype(np.float64) - ref) <= bound)
+
+
+# Hand-derived R64 sums.  x is 1 at the listed hidden indices (0 elsewhere)
+# and the router row holds the listed weight there, so each product is one
+# exact weight; 2^24 = 16777216 is where fp32 spacing becomes 2, so adding 1
+# to it rounds (ties to even) and the result depends on the order.  Values:
+#   A  d=512: 2^24 at i=0 and 1 at i=8l for l=1..63 (one unit in every other
+#      partial sum).  Folds: s=32 2^24+1 -> 2^24, the rest 2; then +2, +4,
+#      +8, +16, +32 exactly: 2^24 + 62 (exact sum 2^24+63; a sequential sum
+#      gives 2^24).
+#   B  d=512: 2^24 at i=0, 1 at i=256 and i=384 (partial sums 32 and 48), bias
+#      2.  s=32: 2^24+1 -> 2^24 and p16 = 1; s=16: 2^24+1 -> 2^24; bias last:
+#      2^24 + 2 (folding s=1 first gives 2^24+2 before the bias; the bias
+#      added first gives 2^24+4).
+#   C  d=1024: 2^24 at i=0, 1 at i=7 and i=512 (granules 0 and 64, both
+#      partial sum 0), 1 at i=8 and i=520 (granules 1 and 65, partial sum 1).
+#      p0: 2^24, +1 -> 2^24, +1 -> 2^24; p1 = 2; fold: 2^24 + 2 (granules of
+#      one element instead of eight give 2^24+4, a sequential sum 2^24).
+R64_CASES = {
+    "A": (512, [(0, 2.0 ** 24)] + [(8 * l, 1.0) for l in range(1, 64)], None, 2 ** 24 + 62),
+    "B": (512, [(0, 2.0 ** 24), (256, 1.0), (384, 1.0)], 2.0, 2 ** 24 + 2),
+    "C": (1024, [(0, 2.0 ** 24), (7, 1.0), (512, 1.0), (8, 1.0), (520, 1.0)], None, 2 ** 24 + 2),
+}
+
+
+def r64_case(name, dtype):
+    """(x [1, d], w_router [1, d], bias [1] or None, expected logit)."""
+    d, terms, bias, want = R64_CASES[name]
+    x = torch.zeros(1, d)
+    w = torch.zeros(1, d)
+    for i, v in terms:
+        x[0, i] = 1.0
+        w[0, i] = v
+    dt = torch.float32 if dtype == "f32" else torch.bfloat16
+    b = None if bias is None else torch.tensor([bias], dtype=torch.float32)
+    return x.to(dt), w.to(dt), b, float(want)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("name", list(R64_CASES))
+def test_router_r64_order_hand_sums(name, dtype):
+    x, w, b, want = r64_case(name, dtype)
+    L = oracle.router_logits(x, w, b)
+    assert float(L[0, 0]) == want, (name, float(L[0, 0]), want)
 
 
 # -------------------------------------------------------------- dispatch ---
