@@ -106,9 +106,12 @@ int moe_capacity(const moe_shape* s, int64_t* C_out /*host*/, int64_t* R_max_out
 int moe_workspace_bytes(const moe_shape* s, size_t* bytes_out /*host*/);
 
 /* Route: logits = x W_router^T + b ("Mixture of Experts: Routing, Dispatch,
- * and Load Balancing", section 1), fp32, each dot product accumulated by a
- * sequential fused multiply-add in increasing hidden index, bias added
- * after; top-k by (logit descending, expert index ascending) ("271,104
+ * and Load Balancing", section 1), fp32, each dot product summed in the
+ * fixed order R64 (the pages leave the order open): hidden index i belongs
+ * to granule i/8, granule q to partial sum q mod 64, each partial sum a
+ * chain of fused multiply-adds in increasing i from +0; the 64 partial sums
+ * are folded by halving, p[l] += p[l+s] for l < s, s = 32, ..., 1; the bias
+ * is added last.  top-k by (logit descending, expert index ascending) ("271,104
  * Routes", section 2); gates per shape->renormalize (see moe_shape).
  *   x           [T, d]   dtype
  *   w_router    [E, d]   dtype

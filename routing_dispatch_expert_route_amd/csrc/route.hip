@@ -8,12 +8,11 @@
 // softmax probability (no renormalisation).
 //
 // Two kernels:
-//   router_logits_kernel  one lane per (token, expert) chain: each logit is a
-//       sequential fp32 fused multiply-add over the hidden index in
-//       increasing order, bias added after the sum.  That fixed order is what
-//       makes the logits -- and so the selected expert ids at near ties --
-//       bit-reproducible.  Token and expert rows are staged through LDS as
-//       fp32 tiles (see the kernel).
+//   router_r64_kernel  a wave per (tokens, experts) group: each logit is a
+//       dot product in the fixed fp32 order R64 (partial sums over
+//       granules of eight elements, one per lane, folded by halving; bias
+//       added last).  That fixed order is what makes the logits -- and so
+//       the selected expert ids at near ties -- bit-reproducible.
 //   topk_rank_kernel  one lane per (token, expert): an expert's rank among
 //       its token's logits (logit desc, index asc) is its slot when below k;
 //       then the gates.
@@ -33,161 +32,125 @@ __device__ __forceinline__ void static_for(F&& f) {
   }
 }
 
-// Router logits.  Block = 64 tokens x (4 * EPW) experts; lane = token, wave
-// w owns experts e0 + w*EPW + j.  The hidden dimension advances in chunks of
-// RKC (128 when the chains are few and latency-bound, 64 when many blocks
-// share a CU): the block stages the x tile [64][RKC] and the W tile
-// [4*EPW][RKC] in LDS as fp32 (converted once per element), then every lane
-// runs its EPW fused-multiply-add chains in increasing hidden index, reading
-// its own x row and broadcast W rows.  Chunks are prefetched two ahead into
-// two register sets while the current one is consumed.
-template <bool BF16, int EPW, int RKC>
-__global__ __launch_bounds__(256) void router_logits_kernel(
-    const void* __restrict__ x, const void* __restrict__ w, const float* __restrict__ b, int T,
-    int d, int E, float* __restrict__ logits) {
-  constexpr int EB = 4 * EPW;             // experts per block
-  constexpr int G = BF16 ? 8 : 4;         // elements per 16-byte chunk
-  constexpr int CPR = RKC / G;            // 16-byte chunks per tile row
-  constexpr int XPT = 64 * CPR / 256;     // x chunks per thread
-  constexpr int WPT = (EB * CPR + 255) / 256;  // W chunks per thread (upper bound)
-  constexpr int XS = RKC + 4;             // padded fp32 row (conflict-free b128 reads)
-  __shared__ __attribute__((aligned(16))) float sx[64 * XS];
-  __shared__ __attribute__((aligned(16))) float sw[EB * RKC];
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const int t0 = blockIdx.x * 64;
-  const int e0 = blockIdx.y * EB;
-  const char* xb = reinterpret_cast<const char*>(x);
-  const char* wb = reinterpret_cast<const char*>(w);
-  constexpr int esz = BF16 ? 2 : 4;
-  const u32x4_t zero = {0u, 0u, 0u, 0u};
-
-  u32x4_t rx[2][XPT], rw[2][WPT];
-  auto fetch = [&](int set, int k0) {
+// Router logits in the fixed summation order R64: hidden index i lies in
+// granule i / 8 (eight consecutive elements, one 16-byte load in bf16) and
+// granule q belongs to partial sum q mod 64 -- lane q mod 64 of a wave, which
+// runs a chain of fused multiply-adds over its granules' elements in
+// increasing i from +0.  The 64 partial sums of a dot product are then
+// folded by halving, p[l] = p[l] + p[l + s] for l < s, s = 32, ..., 1, and
+// the bias is added to p[0].  Each wave-level load covers 64 consecutive
+// granules (1 KiB of a row), so a row is read once, coalesced.
+//
+// One wave computes TPW tokens x EPW experts (C = TPW*EPW dot products, each
+// lane holding C partial sums); weights are reused across the TPW tokens and
+// token rows across the EPW experts.  The fold works on all C dot products
+// at once: at each halving step the two lanes of a pair (l, l ^ s) each keep
+// half of their dot products and exchange the other half, so each step
+// moves half as many values as the last and every lane finishes with the
+// result of dot product lane / (64 / C) -- the same sums as the fold above
+// (a pair's sum is p[l] + p[l + s], and fp32 addition commutes).
+template <int C>
+__device__ __forceinline__ void r64_fold(float (&v)[C], int lane) {
+  static_for<0, 6>([&](auto L) {
+    constexpr int lev = decltype(L)::value;
+    constexpr int s = 32 >> lev;
+    constexpr int n = (C >> lev) > 1 ? (C >> lev) : 1;  // dot products held
+    constexpr int half = n / 2;
+    const bool up = (lane & s) != 0;  // this lane holds partial sum l + s
+    if constexpr (half >= 1) {
 #pragma unroll
-    for (int q = 0; q < XPT; ++q) {
-      const int c = q * 256 + tid;
-      const int row = c / CPR, col = (c % CPR) * G;
-      const int t = min(t0 + row, T - 1);
-      rx[set][q] = (k0 + col < d)
-                       ? *reinterpret_cast<const u32x4_t*>(xb + ((size_t)t * d + k0 + col) * esz)
-                       : zero;
-    }
-#pragma unroll
-    for (int q = 0; q < WPT; ++q) {
-      const int c = q * 256 + tid;
-      const int row = c / CPR, col = (c % CPR) * G;
-      const int e = min(e0 + row, E - 1);
-      rw[set][q] = (c < EB * CPR && k0 + col < d)
-                       ? *reinterpret_cast<const u32x4_t*>(wb + ((size_t)e * d + k0 + col) * esz)
-                       : zero;
-    }
-  };
-  auto put = [&](float* dst, const u32x4_t v) {
-    if constexpr (BF16) {
-      f32x4_t lo = {bf16lo(v[0]), bf16hi(v[0]), bf16lo(v[1]), bf16hi(v[1])};
-      f32x4_t hi = {bf16lo(v[2]), bf16hi(v[2]), bf16lo(v[3]), bf16hi(v[3])};
-      *reinterpret_cast<f32x4_t*>(dst) = lo;
-      *reinterpret_cast<f32x4_t*>(dst + 4) = hi;
-    } else {
-      *reinterpret_cast<u32x4_t*>(dst) = v;
-    }
-  };
-  auto stage = [&](int set) {
-#pragma unroll
-    for (int q = 0; q < XPT; ++q) {
-      const int c = q * 256 + tid;
-      put(sx + (c / CPR) * XS + (c % CPR) * G, rx[set][q]);
-    }
-#pragma unroll
-    for (int q = 0; q < WPT; ++q) {
-      const int c = q * 256 + tid;
-      if (c < EB * CPR) put(sw + (c / CPR) * RKC + (c % CPR) * G, rw[set][q]);
-    }
-  };
-
-  float acc[EPW];
-#pragma unroll
-  for (int j = 0; j < EPW; ++j) acc[j] = 0.0f;
-  const float* xr = sx + lane * XS;
-  // One k step = 4 hidden indices: this lane's x values and each expert's
-  // W values, then 4 FMAs per chain in increasing index.
-  struct Step {
-    f32x4_t x;
-    f32x4_t w[EPW];
-  };
-  auto read_step = [&](int kk, Step& q) {
-    q.x = *reinterpret_cast<const f32x4_t*>(xr + kk);
-#pragma unroll
-    for (int j = 0; j < EPW; ++j)
-      q.w[j] = *reinterpret_cast<const f32x4_t*>(sw + (wave * EPW + j) * RKC + kk);
-  };
-  auto fma_step = [&](const Step& q) {
-#pragma unroll
-    for (int j = 0; j < EPW; ++j) {
-      acc[j] = __builtin_fmaf(q.x[0], q.w[j][0], acc[j]);
-      acc[j] = __builtin_fmaf(q.x[1], q.w[j][1], acc[j]);
-      acc[j] = __builtin_fmaf(q.x[2], q.w[j][2], acc[j]);
-      acc[j] = __builtin_fmaf(q.x[3], q.w[j][3], acc[j]);
-    }
-  };
-  // A full chunk: the LDS reads run P steps ahead of the FMAs (a ring of P
-  // register sets), so their latency hides behind (P-1) steps of FMAs even
-  // with one or two waves per SIMD; the schedule keeps each step's FMAs
-  // before the refill it allows.
-  constexpr int P = EPW == 4 ? 3 : 8 / EPW;
-  constexpr int NSTEP = RKC / 4;
-  static_assert(P <= NSTEP, "read-ahead within a chunk");
-  auto consume_full = [&]() {
-    Step q[P];
-    static_for<0, P>([&](auto i) { read_step(decltype(i)::value * 4, q[decltype(i)::value]); });
-    static_for<0, NSTEP>([&](auto si) {
-      constexpr int st = decltype(si)::value;
-      fma_step(q[st % P]);
-      if constexpr (st + P < NSTEP) {
-        read_step((st + P) * 4, q[st % P]);
-        __builtin_amdgcn_sched_group_barrier(0x002, 4 * EPW, 0);  // the FMAs
-        __builtin_amdgcn_sched_group_barrier(0x100, 1 + EPW, 0);  // then the refill
+      for (int i = 0; i < half; ++i) {
+        const float keep = up ? v[half + i] : v[i];
+        const float send = up ? v[i] : v[half + i];
+        v[i] = keep + __shfl_xor(send, s, kWave);
       }
-    });
-  };
-  auto consume = [&](int k0) {
-    const int kc = min(RKC, d - k0);  // a multiple of 8
-    if (kc == RKC) {
-      consume_full();
     } else {
-      for (int kk = 0; kk < kc; kk += 4) {
-        Step q;
-        read_step(kk, q);
-        fma_step(q);
+      v[0] = v[0] + __shfl_xor(v[0], s, kWave);
+    }
+  });
+}
+
+template <bool BF16, int TPW, int EPW>
+__global__ __launch_bounds__(64) void router_r64_kernel(const void* __restrict__ x,
+                                                        const void* __restrict__ w,
+                                                        const float* __restrict__ b, int T, int d,
+                                                        int E, float* __restrict__ logits) {
+  constexpr int C = TPW * EPW;
+  static_assert(C >= 1 && C <= 64 && (C & (C - 1)) == 0, "a power of two up to 64");
+  constexpr int NL = BF16 ? 1 : 2;  // 16-byte loads per granule
+  const int lane = threadIdx.x;
+  const int n_eg = (E + EPW - 1) / EPW;
+  const int eg = blockIdx.x % n_eg;
+  const int t0 = (blockIdx.x / n_eg) * TPW, e0 = eg * EPW;
+  const int Q = d / 8;
+  const size_t rowb = (size_t)d * (BF16 ? 2 : 4);
+  const char* xr[TPW];
+  const char* wr[EPW];
+#pragma unroll
+  for (int t = 0; t < TPW; ++t)
+    xr[t] = reinterpret_cast<const char*>(x) + (size_t)min(t0 + t, T - 1) * rowb;
+#pragma unroll
+  for (int e = 0; e < EPW; ++e)
+    wr[e] = reinterpret_cast<const char*>(w) + (size_t)min(e0 + e, E - 1) * rowb;
+
+  struct Granule {
+    u32x4_t x[TPW][NL];
+    u32x4_t w[EPW][NL];
+  };
+  auto load = [&](int q, Granule& g) {
+    const size_t o = (size_t)q * 16 * NL;
+#pragma unroll
+    for (int t = 0; t < TPW; ++t)
+#pragma unroll
+      for (int h = 0; h < NL; ++h) g.x[t][h] = *reinterpret_cast<const u32x4_t*>(xr[t] + o + 16 * h);
+#pragma unroll
+    for (int e = 0; e < EPW; ++e)
+#pragma unroll
+      for (int h = 0; h < NL; ++h) g.w[e][h] = *reinterpret_cast<const u32x4_t*>(wr[e] + o + 16 * h);
+  };
+  // element j (0..7) of a granule as fp32
+  auto elem = [&](const u32x4_t (&v)[NL], int j) -> float {
+    if constexpr (BF16) return (j & 1) ? bf16hi(v[0][j >> 1]) : bf16lo(v[0][j >> 1]);
+    else return __uint_as_float(v[j >> 2][j & 3]);
+  };
+  float acc[C];
+#pragma unroll
+  for (int c = 0; c < C; ++c) acc[c] = 0.0f;
+  auto consume = [&](const Granule& g) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      float xv[TPW];
+#pragma unroll
+      for (int t = 0; t < TPW; ++t) xv[t] = elem(g.x[t], j);
+#pragma unroll
+      for (int e = 0; e < EPW; ++e) {
+        const float wv = elem(g.w[e], j);
+#pragma unroll
+        for (int t = 0; t < TPW; ++t) acc[t * EPW + e] = __builtin_fmaf(xv[t], wv, acc[t * EPW + e]);
       }
     }
   };
-  const int nc = (d + RKC - 1) / RKC;
-  fetch(0, 0);
-  if (nc > 1) fetch(1, RKC);
-  for (int c = 0; c < nc; c += 2) {
-    __syncthreads();  // previous chunk fully consumed
-    stage(0);
-    if (c + 2 < nc) fetch(0, (c + 2) * RKC);
-    __syncthreads();
-    consume(c * RKC);
-    if (c + 1 >= nc) break;
-    __syncthreads();
-    stage(1);
-    if (c + 3 < nc) fetch(1, (c + 3) * RKC);
-    __syncthreads();
-    consume((c + 1) * RKC);
+  // a lane's granules q = lane, lane + 64, ... (in increasing i), the next
+  // granule's loads in flight while the current one is consumed
+  Granule g0, g1;
+  int q = lane;
+  if (q < Q) load(q, g0);
+  while (q < Q) {
+    if (q + 64 < Q) load(q + 64, g1);
+    consume(g0);
+    q += 64;
+    if (q >= Q) break;
+    if (q + 64 < Q) load(q + 64, g0);
+    consume(g1);
+    q += 64;
   }
-  const int t = t0 + lane;
-  if (t >= T) return;
-#pragma unroll
-  for (int j = 0; j < EPW; ++j) {
-    const int e = e0 + wave * EPW + j;
-    if (e < E) {
-      float v = acc[j];
+  r64_fold<C>(acc, lane);
+  constexpr int LPC = 64 / C;  // lanes holding each result
+  if (lane % LPC == 0) {
+    const int c = lane / LPC;
+    const int t = t0 + c / EPW, e = e0 + c % EPW;
+    if (t < T && e < E) {
+      float v = acc[0];
       if (b) v = v + b[e];
       logits[(size_t)t * E + e] = v;
     }
@@ -251,26 +214,28 @@ hipError_t launch_route(bool bf16, const void* x, const void* w, const float* b,
                         int E, int k, int renorm, float* logits, int32_t* ids, float* gates,
                         hipStream_t st) {
   if (T == 0) return hipSuccess;
-  // experts per wave: the most register reuse that still leaves about
-  // 2048 waves (two per SIMD) of independent chains
-  const long waves_at1 = (long)ceil_div(T, kWave) * E;
+  // a wave per TPW tokens x EPW experts: the most reuse (up to 4 tokens x 16
+  // experts) that still leaves about 2048 waves, fewer tokens first, then
+  // fewer experts
   int EPW = 1;
-  if (waves_at1 >= 8192) EPW = 4;
-  else if (waves_at1 >= 4096) EPW = 2;
-  dim3 grid(ceil_div(T, kWave), ceil_div(E, 4 * EPW));
-  dim3 block(256);
-#define RL(BF, EPW_)                                                                            \
-  hipLaunchKernelGGL((router_logits_kernel<BF, EPW_, (EPW_ == 4 ? 64 : 128)>), grid, block, 0, st, \
-                     x, w, b, T, d, E, logits)
+  while (EPW < E && EPW < 16) EPW *= 2;
+  int TPW = 4;
+  auto waves = [&](int tpw, int epw) { return (long)ceil_div(T, tpw) * ceil_div(E, epw); };
+  while (TPW > 1 && waves(TPW, EPW) < 2048) TPW /= 2;
+  while (EPW > 1 && waves(TPW, EPW) < 2048) EPW /= 2;
+  const dim3 grid((unsigned)waves(TPW, EPW)), block(64);
+#define RL(BF, TP, EP)                                                                        \
+  if (TPW == TP && EPW == EP)                                                                 \
+  hipLaunchKernelGGL((router_r64_kernel<BF, TP, EP>), grid, block, 0, st, x, w, b, T, d, E, \
+                     logits)
+#define RL_E(BF, TP) \
+  RL(BF, TP, 1); RL(BF, TP, 2); RL(BF, TP, 4); RL(BF, TP, 8); RL(BF, TP, 16)
   if (bf16) {
-    if (EPW == 1) RL(true, 1);
-    else if (EPW == 2) RL(true, 2);
-    else RL(true, 4);
+    RL_E(true, 1); RL_E(true, 2); RL_E(true, 4);
   } else {
-    if (EPW == 1) RL(false, 1);
-    else if (EPW == 2) RL(false, 2);
-    else RL(false, 4);
+    RL_E(false, 1); RL_E(false, 2); RL_E(false, 4);
   }
+#undef RL_E
 #undef RL
   hipError_t err = hipGetLastError();
   if (err != hipSuccess || !ids) return err;  // logits only

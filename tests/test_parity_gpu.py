@@ -2,8 +2,9 @@
 
 Integer outputs (expert ids, counts, offsets, route positions, row tokens,
 drop masks) and byte copies (packed rows) must match bit for bit; router
-logits too (both sides accumulate each dot product by sequential fp32
-fused multiply-add).  Floating outputs are held to 1e-4 absolute (fp32) or
+logits too (both sides sum each dot product in the same fixed fp32 order,
+R64: fused multiply-add chains over granules of eight elements, 64 partial
+sums folded by halving, bias last).  Floating outputs are held to 1e-4 absolute (fp32) or
 2e-2 relative (bf16).  Full-size workloads compare every routing output in
 full; the layer output is compared on every token wherever the oracle's
 FFN work is at most 1e11 flops (every workload but Granite T=16384, Mixtral
@@ -93,6 +94,35 @@ def test_route_worked_example(moe, dtype):
     ids2, g2, _ = moe.route(s2, x.cuda(), wr.cuda())
     assert np.allclose(_np(g2)[0], [0.574, 0.426], atol=tol)
     assert sorted(_np(ids2)[1].tolist()) == [0, 2]
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("case", ["A", "B", "C"])
+def test_route_r64_hand_sums(moe, case, dtype):
+    """Logits whose rounding depends on the summation order (a 2^24 term
+    and unit terms in chosen granules; values derived by hand in
+    tests/test_oracle_pins.py): the kernel's logit equals the hand value."""
+    from tests.test_oracle_pins import r64_case
+    say(f"[route R64 hand sums] {case} {dtype}")
+    x, wr, b, want = r64_case(case, dtype)
+    d = x.shape[1]
+    s = moe.shape(1, d, 1, 1, 8, dtype=dtype, renorm=1)
+    _, _, logits = moe.route(s, x.cuda(), wr.cuda(), None if b is None else b.cuda(),
+                             want_logits=True)
+    torch.cuda.synchronize()
+    assert float(_np(logits)[0, 0]) == want
+    # the same dot products among 70 tokens x 3 experts (other lanes and
+    # groups of the launch): token 5, expert 1 carries the case
+    xt = torch.zeros(70, d, dtype=x.dtype)
+    xt[5] = x[0]
+    wt = torch.zeros(3, d, dtype=x.dtype)
+    wt[1] = wr[0]
+    bt = None if b is None else torch.tensor([0.0, float(b[0]), 0.0])
+    s3 = moe.shape(70, d, 3, 1, 8, dtype=dtype, renorm=1)
+    _, _, L3 = moe.route(s3, xt.cuda(), wt.cuda(), None if bt is None else bt.cuda(),
+                         want_logits=True)
+    torch.cuda.synchronize()
+    assert float(_np(L3)[5, 1]) == want
 
 
 def test_route_ties_take_lowest_index(moe):
