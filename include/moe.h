@@ -197,6 +197,31 @@ int moe_layer_forward(const moe_shape* s, const void* x, const void* w_router,
                       int32_t* counts, int32_t* route_pos, void* ws, size_t ws_bytes,
                       hipStream_t stream);
 
+/* moe_layer_forward without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc).  Same arguments, semantics and output
+ * bits as moe_layer_forward (the same kernels run); the workspace is a
+ * fixed array of MOE_NOALLOC_SCRATCH_BYTES inside the library, one per GPU,
+ * held from the library's load until the process ends.  The call allocates
+ * nothing.
+ *   - Shapes whose moe_workspace_bytes exceeds MOE_NOALLOC_SCRATCH_BYTES
+ *     (64 MiB: enough for, e.g., Switch T=4096 d=768 d_ff=3072, Granite
+ *     T=1412 k=8 of 32 experts d=1024, Mixtral decode T=16 d=4096
+ *     d_ff=14336) return MOE_ERR_UNSUPPORTED before any launch.
+ *   - The array's address on the current device is looked up on the first
+ *     call there (MOE_ERR_HIP if that fails).
+ *   - Every call on one GPU shares that GPU's array: calls that overlap on
+ *     one GPU (on different streams, or from different threads without
+ *     ordering) race and give wrong results.  Calls ordered on one stream
+ *     are safe.  The layer needs no part of the array cleared between
+ *     calls (every value it reads there it wrote earlier in the same call). */
+#define MOE_NOALLOC_SCRATCH_BYTES (64u << 20)
+int moe_layer_forward_noalloc(const moe_shape* s, const void* x, const void* w_router,
+                              const float* b_router, const void* w_gate, const void* w_up,
+                              const void* w_down, const void* ws_gate, const void* ws_up,
+                              const void* ws_down, void* y, int32_t* expert_ids, float* gates,
+                              int32_t* counts, int32_t* route_pos, hipStream_t stream);
+
 /* Fixed-shape dispatch buffer [E, C, d] ("Session 19: Mixture-of-Experts:
  * routing and capacity", "Capacity": capacity is a tensor dimension, and the
  * slot table of "Visual support -- Capacity"; "271,104 Routes", section 3

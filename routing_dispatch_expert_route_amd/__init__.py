@@ -10,7 +10,8 @@ Entry points (same names as the C ABI, without the moe_ prefix):
     capacity, workspace_bytes, route, permute, expert_ffn, combine,
     layer_forward, layer_forward_timed, routing_stats, permute_padded,
     permute_reroute, permute_expert_choice, layer_forward_expert_choice,
-    workspace_bytes_queued, layer_forward_queued, layer_forward_queued_timed
+    workspace_bytes_queued, layer_forward_queued, layer_forward_queued_timed,
+    layer_forward_noalloc
     (layer_forward takes padded= / reroute= for the other layouts)
 """
 import ctypes
@@ -37,7 +38,7 @@ EXPORTS = ("moe_status_string", "moe_capacity", "moe_workspace_bytes", "moe_rout
            "moe_layer_forward_padded", "moe_permute_reroute", "moe_layer_forward_reroute",
            "moe_permute_expert_choice", "moe_layer_forward_expert_choice",
            "moe_workspace_bytes_queued", "moe_layer_forward_queued",
-           "moe_layer_forward_queued_timed")
+           "moe_layer_forward_queued_timed", "moe_layer_forward_noalloc")
 
 
 class MoeShape(ctypes.Structure):
@@ -65,6 +66,7 @@ _lib.moe_permute.argtypes = [_SP] + [_vp] * 8 + [_vp, _sz, _vp]
 _lib.moe_expert_ffn.argtypes = [_SP] + [_vp] * 6 + [_vp, _sz, _vp]
 _lib.moe_combine.argtypes = [_SP] + [_vp] * 5 + [_vp]
 _lib.moe_layer_forward.argtypes = [_SP] + [_vp] * 14 + [_vp, _sz, _vp]
+_lib.moe_layer_forward_noalloc.argtypes = [_SP] + [_vp] * 14 + [_vp]
 _lib.moe_layer_forward_timed.argtypes = [_SP] + [_vp] * 10 + [_vp, _sz, _vp, _vp, ctypes.c_int32]
 _lib.moe_permute_padded.argtypes = [_SP] + [_vp] * 6 + [_vp, _sz, _vp]
 _lib.moe_layer_forward_padded.argtypes = [_SP] + [_vp] * 14 + [_vp, _sz, _vp]
@@ -422,6 +424,33 @@ def layer_forward(s, x, w_router, b_router, w_gate, w_up, w_down, ws_gate=None, 
     return (y, routing) if return_routing else y
 
 
+NOALLOC_SCRATCH_BYTES = 64 << 20
+
+
+def layer_forward_noalloc(s, x, w_router, b_router, w_gate, w_up, w_down, ws_gate=None,
+                          ws_up=None, ws_down=None, y=None, stream=None, return_routing=False):
+    """moe_layer_forward_noalloc: the layer with the library's fixed device
+    array as its workspace (no workspace tensor; calls overlapping on one
+    GPU race).  Outputs as layer_forward; y may be passed in."""
+    dt = _tdtype(s)
+    dev = x.device
+    args = _layer_args(s, x, w_router, b_router, w_gate, w_up, w_down, ws_gate, ws_up, ws_down)
+    if y is None:
+        y = torch.empty(s.T, s.d, dtype=dt, device=dev)
+    yo = _ptr(y, "y", (s.T, s.d), dt)
+    routing = None
+    extra = [None] * 4
+    if return_routing:
+        routing = dict(expert_ids=torch.empty(s.T, s.k, dtype=torch.int32, device=dev),
+                       gates=torch.empty(s.T, s.k, dtype=torch.float32, device=dev),
+                       counts=torch.empty(s.E, dtype=torch.int32, device=dev),
+                       route_pos=torch.empty(s.T, s.k, dtype=torch.int32, device=dev))
+        extra = [_ptr(routing[n], n) for n in ("expert_ids", "gates", "counts", "route_pos")]
+    _check(_lib.moe_layer_forward_noalloc(ctypes.byref(s), *args, yo, *extra, _stream(stream)),
+           "moe_layer_forward_noalloc")
+    return (y, routing) if return_routing else y
+
+
 def layer_forward_timed(s, x, w_router, b_router, w_gate, w_up, w_down, ws_gate, ws_up, ws_down,
                         y, ws, events, stream=None, padded=False, reroute=False, choice=False):
     """moe_layer_forward_timed: records the 7 stage-boundary hipEvents
@@ -553,5 +582,5 @@ def layer_forward_queued_timed(s, x, w_router, b_router, w_gate, w_up, w_down, w
     _check(_lib.moe_layer_forward_queued_timed(ctypes.byref(s), *args, qn, qx, qi, qg, qt,
                                                *_out_args(s, bufs, qn, dt), ws.data_ptr(),
                                                ws.numel(), _stream(stream), arr),
-           "moe_layer_forward_queued_timed")
+           "moe_layer_forward_queued_timed", "moe_layer_forward_noalloc")
     return bufs["y"]

@@ -6,7 +6,15 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "launch.h"
+
+// Workspace of moe_layer_forward_noalloc: one fixed array per GPU, part of
+// the library's code object (each device holds its copy from module load
+// until the process ends).  Host code never names it after set-up: its
+// device address comes from hipGetSymbolAddress, per device.
+static __device__ __align__(256) unsigned char scratch[MOE_NOALLOC_SCRATCH_BYTES];
 
 namespace {
 
@@ -250,6 +258,25 @@ T* at(void* ws, size_t off) {
 }
 
 int hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
+
+// Device address of `scratch` on the current device, looked up once per
+// device with that device current (the first noalloc call there); nullptr
+// when the lookup fails.
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+void* scratch_on_current_device() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess) return nullptr;
+    g_scratch_ptr[dev] = p;
+  }
+  return g_scratch_ptr[dev];
+}
 
 }  // namespace
 
@@ -659,6 +686,23 @@ int moe_layer_forward(const moe_shape* s, const void* x, const void* w_router,
   return layer_forward_impl(s, x, w_router, b_router, w_gate, w_up, w_down, ws_gate, ws_up,
                             ws_down, y, expert_ids, gates, counts, route_pos, ws, ws_bytes,
                             stream, nullptr, 0);
+}
+
+int moe_layer_forward_noalloc(const moe_shape* s, const void* x, const void* w_router,
+                              const float* b_router, const void* w_gate, const void* w_up,
+                              const void* w_down, const void* ws_gate, const void* ws_up,
+                              const void* ws_down, void* y, int32_t* expert_ids, float* gates,
+                              int32_t* counts, int32_t* route_pos, hipStream_t stream) {
+  const int v = validate(s);
+  if (v != MOE_OK) return v;
+  // the layout moe_layer_forward would take from the caller's workspace
+  // must fit the fixed array; checked before anything touches the device
+  if (layout_of(s).total > (size_t)MOE_NOALLOC_SCRATCH_BYTES) return MOE_ERR_UNSUPPORTED;
+  void* ws = scratch_on_current_device();
+  if (!ws) return MOE_ERR_HIP;
+  return layer_forward_impl(s, x, w_router, b_router, w_gate, w_up, w_down, ws_gate, ws_up,
+                            ws_down, y, expert_ids, gates, counts, route_pos, ws,
+                            (size_t)MOE_NOALLOC_SCRATCH_BYTES, stream, nullptr, 0);
 }
 
 int moe_layer_forward_padded(const moe_shape* s, const void* x, const void* w_router,

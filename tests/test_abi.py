@@ -285,3 +285,19 @@ def test_queue_entry_point_rejected_before_launch():
                                             fake, fake, fake, fake, ws,
                                             moe.workspace_bytes_queued(s, 0), None, None) \
         == moe.MOE_ERR_INVALID_ARG
+
+
+def test_noalloc_entry_point_rejected_before_launch():
+    """moe_layer_forward_noalloc validates on the host before it touches the
+    device: an invalid shape, and a shape whose workspace exceeds the fixed
+    array (MOE_ERR_UNSUPPORTED)."""
+    moe = _moe()
+    L = moe._lib
+    fake = 4096
+    bad = moe.shape(16, 60, 4, 2, 64)  # d not a multiple of 8
+    args = [fake, fake, None, fake, fake, fake, None, None, None, fake, None, None, None, None,
+            None]
+    assert L.moe_layer_forward_noalloc(ctypes.byref(bad), *args) == moe.MOE_ERR_INVALID_ARG
+    big = moe.shape(8192, 4096, 8, 2, 14336)
+    assert moe.workspace_bytes(big) > moe.NOALLOC_SCRATCH_BYTES
+    assert L.moe_layer_forward_noalloc(ctypes.byref(big), *args) == moe.MOE_ERR_UNSUPPORTED
