@@ -45,7 +45,11 @@
  *    kernels surface at the caller's next synchronisation.  No C++
  *    exception crosses this interface.
  *  - Supported range: T >= 0, T*k < 2^31, 1 <= E <= 256, 1 <= k <= min(E, 8),
- *    d, d_ff (and d_ff_shared when non-zero) positive multiples of 8.
+ *    d, d_ff (and d_ff_shared when non-zero) positive multiples of 8 and
+ *    below 2^22; x [T, d] and each expert's (and the shared expert's) weight
+ *    matrix below 2^31 bytes; packed, hidden and output rows of any count
+ *    (beyond these, MOE_ERR_UNSUPPORTED).  The fixed-shape buffer, expert
+ *    choice and the queue policy add limits of their own (below).
  *    NaN or infinite inputs give unspecified (but memory-safe) results.
  */
 #ifndef MOE_H

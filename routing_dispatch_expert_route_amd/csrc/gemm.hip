@@ -41,7 +41,9 @@ struct GemmArgs {
   int m_tiles;        // row tiles (an upper bound, host side; the kernel counts the real ones)
   int splits;         // K splits (partial-plane output when > 1)
   int k_chunk;        // K elements per split, a multiple of 64
-  unsigned a_bytes;   // extent of A in bytes (< 2^31; buffer range of the activation loads)
+  long a_bytes;       // extent of A in bytes (gathered rows: < 2^31, the buffer range of
+                      // the activation loads; packed rows: any size, the range starts at
+                      // each tile's first row)
   // Combine fused into the down projection (one route per token, no shared
   // expert; y_tok != nullptr): output row p is token y_tok[p]'s, scaled by
   // its gate y_gate[token] and written to row y_tok[p] of C ([T][N]) -- the
@@ -303,8 +305,17 @@ __global__ __launch_bounds__(64 * WM * WN, OCC) void gemm_bf16_kernel(GemmArgs a
   const int klen = min(K, kb + a.k_chunk) - kb;
 
   // Buffer resources: activations, and the expert's gate/up or down rows.
-  const __amdgpu_buffer_rsrc_t rx =
-      __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(a.A), (short)0, (int)a.a_bytes, kBufFlags);
+  // Packed rows are addressed from the tile's first row (64-bit base), so
+  // the 32-bit offsets of a tile stay below BM*K*2 however many rows the
+  // buffer holds; gathered token rows keep the buffer's own base.
+  const char* abase = reinterpret_cast<const char*>(a.A);
+  long aext = a.a_bytes;
+  if constexpr (!GATHER) {
+    abase += (size_t)row0 * K * 2;
+    aext -= (long)row0 * K * 2;
+  }
+  const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<char*>(abase), (short)0, (int)(aext < 0x7fffffff ? aext : 0x7fffffff), kBufFlags);
   __amdgpu_buffer_rsrc_t rw[NREG];
   const size_t wexp = (size_t)e * N * K * 2;
   rw[0] = __builtin_amdgcn_make_buffer_rsrc(
@@ -324,8 +335,8 @@ __global__ __launch_bounds__(64 * WM * WN, OCC) void gemm_bf16_kernel(GemmArgs a
   for (int q = 0; q < XS; ++q) {
     const int r = (wave * XS + q) * RPS + lane / CH;
     xc[q] = (lane % CH) ^ swz<CH>(r);
-    const int p = row0 + (r < rows ? r : rows - 1);
-    const int src = GATHER ? a.a_rows[p] : p;
+    const int rr = r < rows ? r : rows - 1;
+    const int src = GATHER ? a.a_rows[row0 + rr] : rr;
     xo[q] = ((unsigned)src * (unsigned)K + (unsigned)(kb + xc[q] * 8)) * 2u;
   }
   unsigned wo[WS];
@@ -340,7 +351,7 @@ __global__ __launch_bounds__(64 * WM * WN, OCC) void gemm_bf16_kernel(GemmArgs a
   }
 
   // one stage of the activation tile (BM rows) / of the weight tile (BNW rows)
-  auto issue_x = [&](u32x4_t* xs, int kt) {
+  auto issue_x = [&](u32x4_t* xs, int kt) __attribute__((always_inline)) {
     const int k0 = kt * BK;
     const int soff = k0 * 2;
     const bool tail = k0 + BK > klen;  // includes padding stages past K
@@ -352,7 +363,7 @@ __global__ __launch_bounds__(64 * WM * WN, OCC) void gemm_bf16_kernel(GemmArgs a
                                                soff, 0, 0);
     }
   };
-  auto issue_w = [&](u32x4_t* wsl, int kt) {
+  auto issue_w = [&](u32x4_t* wsl, int kt) __attribute__((always_inline)) {
     const int k0 = kt * BK;
     const int soff = k0 * 2;
     const bool tail = k0 + BK > klen;
@@ -396,7 +407,7 @@ __global__ __launch_bounds__(64 * WM * WN, OCC) void gemm_bf16_kernel(GemmArgs a
     bf16x8_t bx[TM];
     bf16x8_t aw[NREG][TN];
   };
-  auto read_frags = [&](const u32x4_t* xs, const u32x4_t* wsl, int kk, Frag& F) {
+  auto read_frags = [&](const u32x4_t* xs, const u32x4_t* wsl, int kk, Frag& F) __attribute__((always_inline)) {
     // opaque copies: keeps the compiler from hoisting one set of addresses
     // per (ring slot, k step) out of the loop (which would not fit in
     // registers)
@@ -413,7 +424,7 @@ __global__ __launch_bounds__(64 * WM * WN, OCC) void gemm_bf16_kernel(GemmArgs a
       for (int j = 0; j < TN; ++j)
         F.aw[g][j] = *reinterpret_cast<const bf16x8_t*>(wb + wo + (g * BNO + j * 32) * CH * 16);
   };
-  auto mma = [&](const Frag& F) {
+  auto mma = [&](const Frag& F) __attribute__((always_inline)) {
 #pragma unroll
     for (int g = 0; g < NREG; ++g)
 #pragma unroll
@@ -423,15 +434,20 @@ __global__ __launch_bounds__(64 * WM * WN, OCC) void gemm_bf16_kernel(GemmArgs a
           acc[g][j][i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(F.aw[g][j], F.bx[i], acc[g][j][i], 0, 0, 0);
   };
 
-  // Stage count padded to a whole number of loop bodies (every combination
-  // of the two rings' slots); stages past K (the padding, and the refills
-  // issued during the last stages) read zeros -- every chunk offset is past
-  // the buffer -- so the loop body is straight line and every refill is
-  // unconditional.  (A conditional refill makes the compiler wait for all
-  // loads in flight before the next LDS read, which would serialise the
-  // ring.)
+  // The K loop runs whole loop bodies (every combination of the two rings'
+  // slots, LB stages) and then the remaining stages of one more body, each
+  // behind a wave-uniform branch.  Refills issued for stages past K read
+  // zeros -- every chunk offset is past the buffer -- so the loop body is
+  // straight line and every refill is unconditional.  (A conditional refill
+  // makes the compiler wait for all loads in flight before the next LDS
+  // read, which would serialise the ring.)
   constexpr int LB = NSX * NSW / (NSX == NSW ? NSX : (NSW % NSX == 0 ? NSX : 1));  // lcm
-  const int nk = ((klen + BK - 1) / BK + LB - 1) / LB * LB;
+  const int nk = (klen + BK - 1) / BK;
+  // Waves whose rows all lie past the tile's last row (the last tile of an
+  // expert) issue their share of the loads and take part in every barrier,
+  // but read no fragments and run no MFMAs: the SIMDs they share with busy
+  // waves spend that time on the busy ones.
+  const bool active = wm * WTM < rows;
   // The transition into stage t+1 (at the end of stage t) refills the
   // slots of stage t with x(t+NSX) and w(t+NSW), in that order.  Entering
   // it, x(t+1) and w(t+1) must have landed: the loads issued after x(t+1)
@@ -442,10 +458,10 @@ __global__ __launch_bounds__(64 * WM * WN, OCC) void gemm_bf16_kernel(GemmArgs a
   constexpr int VM = (NSW > NSX ? WS : 0) + (NSX - 2) * PER;
   constexpr int WAIT = 0x0070 | (VM & 15) | ((VM >> 4) << 14);   // vmcnt(VM) lgkmcnt(0)
   constexpr int WAIT0 = 0x0F70 | (VM & 15) | ((VM >> 4) << 14);  // vmcnt(VM)
-  auto xslot = [&](auto i) -> u32x4_t* {
+  auto xslot = [&](auto i) __attribute__((always_inline)) -> u32x4_t* {
     return lds_slot<decltype(i)::value % NSX, XSTAGE>();
   };
-  auto wslot = [&](auto i) -> u32x4_t* {
+  auto wslot = [&](auto i) __attribute__((always_inline)) -> u32x4_t* {
     return lds_slot<4 + decltype(i)::value % NSW, WSTAGE>();
   };
   Frag F0, F1;
@@ -455,14 +471,14 @@ __global__ __launch_bounds__(64 * WM * WN, OCC) void gemm_bf16_kernel(GemmArgs a
   // one refill load per MFMA as well.
   constexpr int NDS = TM + NREG * TN;  // LDS reads per k step
   constexpr int NMF = NREG * TN * TM;  // MFMAs per k step
-  auto order_kstep = [&]() {
+  auto order_kstep = [&]() __attribute__((always_inline)) {
 #pragma unroll
     for (int u = 0; u < NMF; ++u) {
       if (u < NDS) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);               // MFMA
     }
   };
-  auto order_transition = [&]() {
+  auto order_transition = [&]() __attribute__((always_inline)) {
 #pragma unroll
     for (int u = 0; u < (NMF > PER ? NMF : PER); ++u) {
       if (u < PER) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // global load
@@ -472,11 +488,19 @@ __global__ __launch_bounds__(64 * WM * WN, OCC) void gemm_bf16_kernel(GemmArgs a
   };
   // Stage S of the loop body (kt = its stage index): k steps 0 .. KS-2 read
   // the next step's fragments first; the last step moves to the next stage
-  // before its MFMAs, which only need registers.
-  auto stage = [&](auto S, int kt) {
+  // before its MFMAs, which only need registers.  ACT false: an inactive
+  // wave's stage (the wait, the barrier and the refills only).
+  auto stage = [&](auto S, auto ACT, int kt) __attribute__((always_inline)) {
     constexpr int s = decltype(S)::value;
     u32x4_t* xc_ = xslot(std::integral_constant<int, s>{});
     u32x4_t* wc_ = wslot(std::integral_constant<int, s>{});
+    if constexpr (!decltype(ACT)::value) {
+      __builtin_amdgcn_s_waitcnt(WAIT);
+      __builtin_amdgcn_s_barrier();
+      issue_x(xc_, kt + NSX);
+      issue_w(wc_, kt + NSW);
+      return;
+    }
 #pragma unroll
     for (int kk = 0; kk < KS - 1; ++kk) {
       if (kk % 2 == 0) {
@@ -501,7 +525,7 @@ __global__ __launch_bounds__(64 * WM * WN, OCC) void gemm_bf16_kernel(GemmArgs a
   static_assert(BK / 16 % 2 == 0, "even number of k steps per stage");
   // prologue: the transitions before stage 0 (t = -NSW .. -1), the wait of
   // the last one in between
-  static_for<0, NSW - 1>([&](auto tt) {
+  static_for<0, NSW - 1>([&](auto tt) __attribute__((always_inline)) {
     constexpr int t = decltype(tt)::value - NSW;
     if constexpr (t + NSX >= 0) issue_x(xslot(std::integral_constant<int, t + NSX>{}), t + NSX);
     issue_w(wslot(std::integral_constant<int, t + NSW>{}), t + NSW);
@@ -510,12 +534,22 @@ __global__ __launch_bounds__(64 * WM * WN, OCC) void gemm_bf16_kernel(GemmArgs a
   __builtin_amdgcn_s_barrier();
   issue_x(xslot(std::integral_constant<int, NSX - 1>{}), NSX - 1);
   issue_w(wslot(std::integral_constant<int, NSW - 1>{}), NSW - 1);
-  read_frags(X0, W0, 0, F0);
-  for (int kt = 0; kt < nk; kt += LB)
-    static_for<0, LB>([&](auto S) { stage(S, kt + decltype(S)::value); });
+  auto k_loop = [&](auto ACT) __attribute__((always_inline)) {
+    if constexpr (decltype(ACT)::value) read_frags(X0, W0, 0, F0);
+    int kt = 0;
+    for (; kt + LB <= nk; kt += LB)
+      static_for<0, LB>([&](auto S) __attribute__((always_inline)) { stage(S, ACT, kt + decltype(S)::value); });
+    const int rest = nk - kt;  // < LB stages of one more body
+    static_for<0, LB - 1>([&](auto S) __attribute__((always_inline)) {
+      if (decltype(S)::value < rest) stage(S, ACT, kt + decltype(S)::value);
+    });
+  };
+  if (active) k_loop(std::true_type{});
+  else k_loop(std::false_type{});
   // the zero-reading refills past the end must land before the workgroup's
   // LDS is released
   __builtin_amdgcn_s_waitcnt(0x0F70);
+  if (!active) return;
 
   // epilogue: four consecutive columns per store
 #pragma unroll
@@ -730,7 +764,7 @@ hipError_t launch_gemm_swiglu(const GemmPlan& pl, const void* A, const int32_t* 
                               long a_nrows, const void* Wg, const void* Wu, int N, int K, void* H,
                               hipStream_t st) {
   GemmArgs a{A, a_rows, pl.offsets, pl.E, pl.M_dense, Wg, Wu, N, K, H, 0, 0, 0, 1, K,
-             (unsigned)(a_nrows * K * 2)};
+             a_nrows * K * 2};
   if (!pl.bf16) return run_f32<true>(pl, a, st);
   return run_cfg<true, false>(pl, a, st);
 }
@@ -741,7 +775,7 @@ hipError_t launch_gemm_down_combine(const GemmPlan& pl, const void* H, const voi
   if (!pl.bf16 || N % 8) return hipErrorInvalidValue;
   const long h_rows = pl.grouped ? pl.R_max : pl.M_dense;
   GemmArgs a{H, nullptr, pl.offsets, pl.E, pl.M_dense, Wd, nullptr, N, K, y, 0, 0, 0,
-             1, K, (unsigned)(h_rows * K * 2), row_token, gates, route_pos, T, 0};
+             1, K, h_rows * K * 2, row_token, gates, route_pos, T, 0};
   return run_cfg<false, false>(pl, a, st);
 }
 
@@ -749,7 +783,7 @@ hipError_t launch_gemm_down(const GemmPlan& pl, const void* H, const void* Wd, i
                             void* Y, int splits, long split_stride, hipStream_t st) {
   const long h_rows = pl.grouped ? pl.R_max : pl.M_dense;
   GemmArgs a{H, nullptr, pl.offsets, pl.E, pl.M_dense, Wd, nullptr, N, K, Y, split_stride, 0, 0,
-             1, K, (unsigned)(h_rows * K * 2)};
+             1, K, h_rows * K * 2};
   if (!pl.bf16) return run_f32<false>(pl, a, st);
   if (splits <= 1) return run_cfg<false, false>(pl, a, st);
   a.splits = splits;

@@ -43,17 +43,18 @@ int validate(const moe_shape* s) {
   if (s->tie_break != MOE_TIE_LOWEST_INDEX) return MOE_ERR_UNSUPPORTED;
   if (s->E > kMaxE || s->k > kMaxK) return MOE_ERR_UNSUPPORTED;
   if (s->T * s->k >= (int64_t(1) << 31)) return MOE_ERR_UNSUPPORTED;
-  if (s->d >= (int64_t(1) << 24) || s->d_ff >= (int64_t(1) << 24) ||
-      s->d_ff_shared >= (int64_t(1) << 24))
+  // a GEMM tile's rows (at most 256) must span less than 2^31 bytes: the
+  // packed-row operands are addressed with 32-bit offsets from each tile's
+  // first row, so their total size is free
+  if (s->d >= (int64_t(1) << 22) || s->d_ff >= (int64_t(1) << 22) ||
+      s->d_ff_shared >= (int64_t(1) << 22))
     return MOE_ERR_UNSUPPORTED;
-  // every activation, hidden and per-expert weight buffer the GEMMs read
-  // must span less than 2^31 bytes (32-bit buffer offsets)
+  // token rows gathered by the first GEMM (x) and each expert's weight
+  // matrices are addressed from their own base: each must span less than
+  // 2^31 bytes
   const int64_t eb = s->dtype == MOE_DTYPE_BF16 ? 2 : 4;
   const int64_t lim = int64_t(1) << 31;
-  const int64_t R = s->T * s->k;
-  const int64_t wide = s->d > s->d_ff ? s->d : s->d_ff;
-  if (s->T * s->d * eb >= lim || R * wide * eb >= lim || s->d * s->d_ff * eb >= lim ||
-      s->T * s->d_ff_shared * eb >= lim || s->d * s->d_ff_shared * eb >= lim)
+  if (s->T * s->d * eb >= lim || s->d * s->d_ff * eb >= lim || s->d * s->d_ff_shared * eb >= lim)
     return MOE_ERR_UNSUPPORTED;
   return MOE_OK;
 }

@@ -75,8 +75,19 @@ BAD_SHAPES = [
     (dict(T=-1), 1), (dict(d=0), 1), (dict(d=12), 1), (dict(d_ff=20), 1), (dict(k=5), 1),
     (dict(E=0), 1), (dict(d_ff_shared=12), 1), (dict(renorm=2), 1), (dict(phi=float("nan")), 1),
     (dict(E=300, k=2), 2), (dict(k=9, E=16), 2), (dict(dtype=7), 2), (dict(tie=1), 2),
-    (dict(T=2**29, k=8, E=16), 2),
+    (dict(T=2**29, k=8, E=16), 2), (dict(d=2**22), 2), (dict(T=2**18, d=4096), 2),
+    (dict(d=4096, d_ff=2**18), 2),
 ]
+
+
+def test_packed_rows_beyond_2gib_accepted():
+    """Packed, hidden and output rows may exceed 2^31 bytes (the GEMMs
+    address them from each tile's first row): Mixtral-shape prefill of 65536
+    tokens has 3.8 GB of hidden rows; the workspace covers them."""
+    moe = _moe()
+    s = moe.shape(65536, 4096, 8, 2, 14336)
+    assert moe.capacity(s) == (-1, 131072)
+    assert moe.workspace_bytes(s) >= 131072 * (14336 + 4096) * 2
 
 
 @pytest.mark.parametrize("bad,status", BAD_SHAPES)

@@ -401,6 +401,17 @@ def test_layer_forward_tile_paths(moe, name):
     _layer_check(moe, w, make_inputs(w, seed=13))
 
 
+def test_layer_forward_packed_rows_beyond_2gib(moe):
+    """Mixtral shape with T = 65536: 131072 packed rows, 3.8 GB of hidden
+    rows and 1.1 GB of expert outputs, beyond 32-bit byte offsets (each GEMM
+    tile addresses its rows from its own first row).  Routing outputs in
+    full, the layer on 256 seeded tokens plus each expert's first and last
+    row owners."""
+    w = Workload("mixtral_t65536", T=65536, E=8, k=2, d=4096, d_ff=14336)
+    say("[layer packed rows > 2 GiB] mixtral T=65536")
+    _layer_check(moe, w, make_inputs(w, seed=29), n_random=256)
+
+
 def test_forced_hot_expert_reaches_E_over_k(moe):
     say("[layer hot expert]")
     w = Workload("hot", T=512, E=32, k=8, d=64, d_ff=32, bias="normal")
