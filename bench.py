@@ -126,9 +126,12 @@ def traffic_from_profile(workload):
 
 
 def _is_gemm1(name):
-    # gemm_bf16_kernel<tile and pipeline sizes..., SWIGLU, GATHER, PARTIAL>:
-    # GEMM 1 of the whole-layer path is the SwiGLU instance that gathers
-    # token rows
+    # gemm_bf16_kernel<tile and pipeline sizes..., SWIGLU, GATHER, PARTIAL> or
+    # gemm_pp_kernel<SWIGLU, GATHER>: GEMM 1 of the whole-layer path is the
+    # SwiGLU instance that gathers token rows
+    if "gemm_pp_kernel<" in name:
+        args = [a.strip() for a in name.split("<", 1)[1].split(">", 1)[0].split(",")]
+        return args == ["true", "true"]
     if "gemm_bf16_kernel<" not in name:
         return False
     args = [a.strip() for a in name.split("<", 1)[1].split(">", 1)[0].split(",")]
@@ -541,7 +544,7 @@ def main():
             ach = byts / (g1_us * 1e-6) / 1e9
             roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBS,
                     "unit": "GB/s", "frac": round(ach / PEAK_HBM_GBS, 4)}
-        roof["kernel"] = "gemm_bf16_kernel (grouped GEMM 1: gate+up+SwiGLU)"
+        roof["kernel"] = "grouped GEMM 1 (gate+up+SwiGLU)"
         roof["us_per_launch"] = round(g1_us, 2)
         roof["algorithmic_flops"] = flops
         roof["algorithmic_bytes"] = byts

@@ -233,6 +233,62 @@ __device__ __forceinline__ u32x4_t* lds_slot() {
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 constexpr int kBufFlags = 0x00020000;  // raw buffer, 32-bit data format
 
+// Epilogue of a tile: the wave's accumulators (rows wm*WTM.., output
+// columns nt*BNO + wn*WTN..) to C, four consecutive columns per store:
+// SiLU(gate)*up rounded to bf16 (SWIGLU), fp32 into the K split's partial
+// plane (PARTIAL), gate-scaled rows scattered to their tokens (the down
+// projection with the combine fused, a.y_tok set), else bf16 rows.
+template <int NREG, int TN, int TM, int BNO, int WTM, int WTN, bool SWIGLU, bool PARTIAL>
+__device__ __forceinline__ void store_tile(const GemmArgs& a, const f32x16_t (&acc)[NREG][TN][TM],
+                                           int row0, int rows, int nt, int ks, int wm, int wn,
+                                           int lrow, int lk) {
+  const int N = a.N;
+#pragma unroll
+  for (int j = 0; j < TN; ++j) {
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+      const int m = wm * WTM + i * 32 + lrow;
+      if (m >= rows) continue;
+      const size_t p = (size_t)(row0 + m);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int n = nt * BNO + wn * WTN + j * 32 + 8 * q + 4 * lk;
+        if (n >= N) continue;
+        float o[4];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          if constexpr (SWIGLU) {
+            const float gv = acc[0][j][i][4 * q + t];
+            const float uv = acc[1][j][i][4 * q + t];
+            o[t] = __fdividef(gv, 1.0f + __expf(-gv)) * uv;
+          } else {
+            o[t] = acc[0][j][i][4 * q + t];
+          }
+        }
+        if constexpr (PARTIAL) {
+          float* Cp = reinterpret_cast<float*>(a.C) + (size_t)ks * a.split_stride;
+          f32x4_t v = {o[0], o[1], o[2], o[3]};
+          *reinterpret_cast<f32x4_t*>(Cp + p * N + n) = v;
+        } else if (!SWIGLU && a.y_tok) {
+          const int tk = a.y_tok[p];
+          const float g = a.y_gate[tk];
+          const uint32_t r0 = pack_bf16x2(o[0], o[1]), r1 = pack_bf16x2(o[2], o[3]);
+          uint2 v;
+          v.x = pack_bf16x2(__builtin_fmaf(g, bf16lo(r0), 0.0f), __builtin_fmaf(g, bf16hi(r0), 0.0f));
+          v.y = pack_bf16x2(__builtin_fmaf(g, bf16lo(r1), 0.0f), __builtin_fmaf(g, bf16hi(r1), 0.0f));
+          *reinterpret_cast<uint2*>(reinterpret_cast<bf16_t*>(a.C) + (size_t)tk * N + n) = v;
+        } else {
+          bf16_t* Cp = reinterpret_cast<bf16_t*>(a.C);
+          uint2 v;
+          v.x = pack_bf16x2(o[0], o[1]);
+          v.y = pack_bf16x2(o[2], o[3]);
+          *reinterpret_cast<uint2*>(Cp + p * N + n) = v;
+        }
+      }
+    }
+  }
+}
+
 template <int BM, int BNW, int WM, int WN, int BK, int NSX, int NSW, int OCC, bool SWIGLU,
           bool GATHER, bool PARTIAL>
 __global__ __launch_bounds__(64 * WM * WN, OCC) void gemm_bf16_kernel(GemmArgs a) {
@@ -551,51 +607,281 @@ __global__ __launch_bounds__(64 * WM * WN, OCC) void gemm_bf16_kernel(GemmArgs a
   __builtin_amdgcn_s_waitcnt(0x0F70);
   if (!active) return;
 
-  // epilogue: four consecutive columns per store
-#pragma unroll
-  for (int j = 0; j < TN; ++j) {
-#pragma unroll
-    for (int i = 0; i < TM; ++i) {
-      const int m = wm * WTM + i * 32 + lrow;
-      if (m >= rows) continue;
-      const size_t p = (size_t)(row0 + m);
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int n = nt * BNO + wn * WTN + j * 32 + 8 * q + 4 * lk;
-        if (n >= N) continue;
-        float o[4];
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
-          if constexpr (SWIGLU) {
-            const float gv = acc[0][j][i][4 * q + t];
-            const float uv = acc[1][j][i][4 * q + t];
-            o[t] = __fdividef(gv, 1.0f + __expf(-gv)) * uv;
-          } else {
-            o[t] = acc[0][j][i][4 * q + t];
-          }
-        }
-        if constexpr (PARTIAL) {
-          float* Cp = reinterpret_cast<float*>(a.C) + (size_t)ks * a.split_stride;
-          f32x4_t v = {o[0], o[1], o[2], o[3]};
-          *reinterpret_cast<f32x4_t*>(Cp + p * N + n) = v;
-        } else if (!SWIGLU && a.y_tok) {
-          const int tk = a.y_tok[p];
-          const float g = a.y_gate[tk];
-          const uint32_t r0 = pack_bf16x2(o[0], o[1]), r1 = pack_bf16x2(o[2], o[3]);
-          uint2 v;
-          v.x = pack_bf16x2(__builtin_fmaf(g, bf16lo(r0), 0.0f), __builtin_fmaf(g, bf16hi(r0), 0.0f));
-          v.y = pack_bf16x2(__builtin_fmaf(g, bf16lo(r1), 0.0f), __builtin_fmaf(g, bf16hi(r1), 0.0f));
-          *reinterpret_cast<uint2*>(reinterpret_cast<bf16_t*>(a.C) + (size_t)tk * N + n) = v;
-        } else {
-          bf16_t* Cp = reinterpret_cast<bf16_t*>(a.C);
-          uint2 v;
-          v.x = pack_bf16x2(o[0], o[1]);
-          v.y = pack_bf16x2(o[2], o[3]);
-          *reinterpret_cast<uint2*>(Cp + p * N + n) = v;
-        }
-      }
+  store_tile<NREG, TN, TM, BNO, WTM, WTN, SWIGLU, PARTIAL>(a, acc, row0, rows, nt, ks, wm, wn, lrow,
+                                                          lk);
+#endif
+}
+
+// ---------------------------------------------------------------------------
+// bf16 MFMA kernel, ping-pong schedule: 256x256 tiles, eight waves in two
+// groups of four (one wave of each group per SIMD).  Each group alternates
+// between a load phase -- its share of the global->LDS refills, then every
+// MFMA fragment of one K stage from LDS into registers -- and a compute
+// phase of 32 MFMAs from registers; the groups are one phase apart, so on
+// each SIMD one wave feeds the MFMA pipe while the other loads.  One
+// workgroup barrier ends every phase.
+//
+// Group 0 (tile rows 0..127) loads the activation tile (two LDS slots),
+// group 1 (rows 128..255) the weight tile (three slots).  Stage t is read by
+// group 0 in phase 2t and by group 1 in phase 2t+1; group 0 refills the
+// activation slot of stage t-1 with stage t+1 during phase 2t and waits
+// for it at the end of phase 2t+1; group 1 refills the weight slot of
+// stage t-1 with stage t+2 during phase 2t+1 and waits for it at the end
+// of phase 2t+3.  Every accumulator sums its K steps in increasing order,
+// as in gemm_bf16_kernel, so both kernels give the same bits.
+// ---------------------------------------------------------------------------
+template <bool SWIGLU, bool GATHER>
+__global__ __launch_bounds__(512, 1) void gemm_pp_kernel(GemmArgs a) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  constexpr int BM = 256, BNW = 256, BK = 64, CH = 8, RPS = 8, KS = 4;
+  constexpr int NSX = 2, NSW = 3;
+  constexpr int NREG = SWIGLU ? 2 : 1;
+  constexpr int BNO = BNW / NREG;
+  constexpr int WTM = 64, WTN = BNO / 2;
+  constexpr int TM = WTM / 32, TN = WTN / 32;
+  constexpr int NL = BM / RPS / 4;  // loads per wave per stage (x by group 0, w by group 1)
+  static_assert(BM == BNW, "both groups issue the same number of loads");
+  constexpr int XSTAGE = BM * CH, WSTAGE = BNW * CH;
+
+  u32x4_t* const X0 = lds_slot<0, XSTAGE>();
+  int* s_info = reinterpret_cast<int*>(X0);
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int grp = wave >> 2, wi = wave & 3;
+  const int wm = wave >> 1, wn = wave & 1;
+  if constexpr (!SWIGLU) {
+    if (a.y_tok && (int)blockIdx.x >= a.main_blocks) {  // whole workgroup, before any barrier
+      zero_dropped_rows(a, (int)blockIdx.x - a.main_blocks);
+      return;
     }
   }
+  if (wave == 0) {
+    int mt0 = 0, nt0 = 0, ks0 = 0;
+    if (tile_of_block(a, count_row_tiles<BM>(a, lane), mt0, nt0, ks0)) {
+      find_row_tile<BM>(a, mt0, lane, s_info);
+      if (lane == 0) {
+        s_info[3] = nt0;
+        s_info[4] = ks0;
+      }
+    } else if (lane == 0) {
+      s_info[0] = -1;
+    }
+  }
+  __syncthreads();
+  const int e = __builtin_amdgcn_readfirstlane(s_info[0]);
+  if (e < 0) return;
+  const int row0 = __builtin_amdgcn_readfirstlane(s_info[1]);
+  const int rows = __builtin_amdgcn_readfirstlane(s_info[2]);
+  const int nt = __builtin_amdgcn_readfirstlane(s_info[3]);
+  __syncthreads();  // every wave has its tile before X0 is refilled
+  const int K = a.K, N = a.N;
+  const int klen = K;
+
+  // This wave's loads: group 0 the activation rows (wi*NL + q)*RPS + lane/CH,
+  // group 1 the weight rows of the same numbers; lane i of a wave-level load
+  // fetches logical chunk (i%CH) ^ f(row) of its row.  A load's first row is
+  // a multiple of RPS, so the chunk depends on the lane and on q's parity
+  // only; packed activation rows and weight rows are then a wave-uniform
+  // base (the scalar offset) plus a lane offset, and only gathered token
+  // rows need an offset per load.  Weight rows past N get offsets past the
+  // buffer, which read zero.
+  const int lrow_ld = lane / CH;
+  int chk[2];
+  unsigned lo[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) chk[h] = (lane % CH) ^ swz<CH>(h * RPS + lrow_ld);
+  constexpr bool GOFF = GATHER;  // group 0 needs an offset per load
+  unsigned goff[GOFF ? NL : 1];
+  unsigned ubase;  // wave-uniform byte offset of row (wi*NL)*RPS
+  __amdgpu_buffer_rsrc_t rsrc[NREG];
+  if (grp == 0) {
+    const char* abase = reinterpret_cast<const char*>(a.A);
+    long aext = a.a_bytes;
+    if constexpr (!GATHER) {
+      abase += (size_t)row0 * K * 2;
+      aext -= (long)row0 * K * 2;
+    }
+    rsrc[0] = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<char*>(abase), (short)0, (int)(aext < 0x7fffffff ? aext : 0x7fffffff), kBufFlags);
+    if constexpr (NREG > 1) rsrc[1] = rsrc[0];
+    if constexpr (GATHER) {
+      ubase = 0;
+#pragma unroll
+      for (int q = 0; q < NL; ++q) {
+        const int r = (wi * NL + q) * RPS + lrow_ld;
+        const int rr = r < rows ? r : rows - 1;
+        goff[q] = ((unsigned)a.a_rows[row0 + rr] * (unsigned)K + (unsigned)(chk[q & 1] * 8)) * 2u;
+      }
+    } else {
+      // rows past the tile's last row read rows of the next tile (or past the
+      // buffer): harmless, their results are never stored
+      ubase = (unsigned)(wi * NL * RPS) * (unsigned)K * 2u;
+#pragma unroll
+      for (int h = 0; h < 2; ++h) lo[h] = ((unsigned)lrow_ld * (unsigned)K + (unsigned)(chk[h] * 8)) * 2u;
+    }
+  } else {
+    const size_t wexp = (size_t)e * N * K * 2;
+    rsrc[0] = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<char*>(reinterpret_cast<const char*>(a.B0) + wexp), (short)0, N * K * 2, kBufFlags);
+    if constexpr (SWIGLU)
+      rsrc[NREG - 1] = __builtin_amdgcn_make_buffer_rsrc(
+          const_cast<char*>(reinterpret_cast<const char*>(a.B1) + wexp), (short)0, N * K * 2,
+          kBufFlags);
+    ubase = (unsigned)(nt * BNO) * (unsigned)K * 2u;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) lo[h] = ((unsigned)lrow_ld * (unsigned)K + (unsigned)(chk[h] * 8)) * 2u;
+  }
+  // stage kt of this wave's operand into ring slot dst (stages past K, and
+  // chunks past K in the last stage, read zero: their offsets lie past the
+  // buffer)
+  auto issue = [&](u32x4_t* dst, int kt) __attribute__((always_inline)) {
+    const int k0 = kt * BK;
+    const bool tail = k0 + BK > klen;
+#pragma unroll
+    for (int q = 0; q < NL; ++q) {
+      const int row = (wi * NL + q) * RPS;  // the load's first row in the tile
+      int reg = 0;
+      unsigned vo, so;
+      if (grp == 0 && GOFF) {
+        vo = goff[GOFF ? q : 0];
+        so = (unsigned)(k0 * 2);
+      } else if (grp == 0) {
+        vo = lo[q & 1];
+        so = ubase + (unsigned)(q * RPS) * (unsigned)K * 2u + (unsigned)(k0 * 2);
+      } else {
+        reg = row / BNO;
+        vo = lo[q & 1];
+        so = ubase + (unsigned)(row % BNO) * (unsigned)K * 2u + (unsigned)(k0 * 2);
+      }
+      if (tail && chk[q & 1] * 8 >= klen - k0) vo = 0x80000000u;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc[reg], (lds_ptr_t)(dst + (wi * NL + q) * 64), 16,
+                                               vo, (int)so, 0, 0);
+    }
+  };
+  auto xslot = [&](auto i) __attribute__((always_inline)) -> u32x4_t* {
+    return lds_slot<decltype(i)::value % NSX, XSTAGE>();
+  };
+  auto wslot = [&](auto i) __attribute__((always_inline)) -> u32x4_t* {
+    return lds_slot<4 + decltype(i)::value % NSW, WSTAGE>();
+  };
+
+  f32x16_t acc[NREG][TN][TM];
+#pragma unroll
+  for (int g = 0; g < NREG; ++g)
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) acc[g][j][i][v] = 0.0f;
+  const int lrow = lane & 31;
+  const int lk = lane >> 5;
+  struct Frag {
+    bf16x8_t bx[TM];
+    bf16x8_t aw[NREG][TN];
+  };
+  Frag F[KS];
+  // every fragment of one stage (from slots xs, wsl) into F
+  auto read_stage = [&](const u32x4_t* xs, const u32x4_t* wsl) __attribute__((always_inline)) {
+    const char* xb = reinterpret_cast<const char*>(xs);
+    const char* wb = reinterpret_cast<const char*>(wsl);
+#pragma unroll
+    for (int kk = 0; kk < KS; ++kk) {
+      const int chunk = ((kk * 2 + lk) ^ swz<CH>(lrow)) * 16;
+      const int xo = (wm * WTM + lrow) * CH * 16 + chunk;
+      const int wo = (wn * WTN + lrow) * CH * 16 + chunk;
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+        F[kk].bx[i] = *reinterpret_cast<const bf16x8_t*>(xb + xo + i * 32 * CH * 16);
+#pragma unroll
+      for (int g = 0; g < NREG; ++g)
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+          F[kk].aw[g][j] = *reinterpret_cast<const bf16x8_t*>(wb + wo + (g * BNO + j * 32) * CH * 16);
+    }
+  };
+  // the stage's MFMAs from F, k steps in increasing order
+  auto compute = [&]() __attribute__((always_inline)) {
+#pragma unroll
+    for (int kk = 0; kk < KS; ++kk)
+#pragma unroll
+      for (int g = 0; g < NREG; ++g)
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+#pragma unroll
+          for (int i = 0; i < TM; ++i)
+            acc[g][j][i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(F[kk].aw[g][j], F[kk].bx[i],
+                                                                  acc[g][j][i], 0, 0, 0);
+  };
+  constexpr int LB = NSX * NSW;  // slot combinations repeat every 6 stages
+  const int nk = (klen + BK - 1) / BK;
+  // prologue: activation stage 0 (group 0), weight stages 0 and 1 (group 1)
+  if (grp == 0) {
+    issue(xslot(std::integral_constant<int, 0>{}), 0);
+  } else {
+    issue(wslot(std::integral_constant<int, 0>{}), 0);
+    issue(wslot(std::integral_constant<int, 1>{}), 1);
+  }
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+  __builtin_amdgcn_s_barrier();
+  constexpr int WAIT_ALL = 0x0070;                                  // vmcnt(0) lgkmcnt(0)
+  constexpr int WAIT_NL = 0x0070 | (NL & 15) | ((NL >> 4) << 14);  // vmcnt(NL) lgkmcnt(0)
+  // stage kt (slot index S = kt % LB): group 0's two phases, or group 1's
+  auto stage0 = [&](auto S, int kt) __attribute__((always_inline)) {
+    constexpr int s = decltype(S)::value;
+    // phase 2kt: refill, read
+    issue(xslot(std::integral_constant<int, s + 1>{}), kt + 1);
+    read_stage(xslot(std::integral_constant<int, s>{}), wslot(std::integral_constant<int, s>{}));
+    __builtin_amdgcn_s_waitcnt(WAIT_NL);  // fragments in registers
+    __builtin_amdgcn_s_barrier();
+    // phase 2kt+1: compute, then the refill must have landed
+    __builtin_amdgcn_s_setprio(1);
+    compute();
+    __builtin_amdgcn_s_setprio(0);
+    __builtin_amdgcn_s_waitcnt(WAIT_ALL);
+    __builtin_amdgcn_s_barrier();
+  };
+  auto stage1 = [&](auto S, int kt) __attribute__((always_inline)) {
+    constexpr int s = decltype(S)::value;
+    // phase 2kt: compute the previous stage
+    if (kt > 0) {
+      __builtin_amdgcn_s_setprio(1);
+      compute();
+      __builtin_amdgcn_s_setprio(0);
+    }
+    __builtin_amdgcn_s_barrier();
+    // phase 2kt+1: refill, read; the previous refill must have landed
+    issue(wslot(std::integral_constant<int, s + 2>{}), kt + 2);
+    read_stage(xslot(std::integral_constant<int, s>{}), wslot(std::integral_constant<int, s>{}));
+    __builtin_amdgcn_s_waitcnt(WAIT_NL);
+    __builtin_amdgcn_s_barrier();
+  };
+  auto run = [&](auto G) __attribute__((always_inline)) {
+    int kt = 0;
+    for (; kt + LB <= nk; kt += LB)
+      static_for<0, LB>([&](auto S) __attribute__((always_inline)) {
+        if constexpr (decltype(G)::value == 0) stage0(S, kt + decltype(S)::value);
+        else stage1(S, kt + decltype(S)::value);
+      });
+    const int rest = nk - kt;
+    static_for<0, LB - 1>([&](auto S) __attribute__((always_inline)) {
+      if (decltype(S)::value < rest) {
+        if constexpr (decltype(G)::value == 0) stage0(S, kt + decltype(S)::value);
+        else stage1(S, kt + decltype(S)::value);
+      }
+    });
+  };
+  if (grp == 0) {
+    run(std::integral_constant<int, 0>{});
+  } else {
+    run(std::integral_constant<int, 1>{});
+    compute();  // the last stage (group 0 has left the loop; no barrier follows)
+  }
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // the refills past the end have landed
+  if (wm * WTM >= rows) return;
+  store_tile<NREG, TN, TM, BNO, WTM, WTN, SWIGLU, false>(a, acc, row0, rows, nt, 0, wm, wn, lrow,
+                                                        lk);
 #endif
 }
 
@@ -646,10 +932,12 @@ static long row_tile_bound(const GemmPlan& pl, int BM) {
 
 // Tile shape, from the shape alone (the routing is not known on the host;
 // the row counts are bounded by R_max).  Measured on MI355X:
-//   L  256-row tiles, one workgroup of eight waves per CU (two per SIMD,
-//      so one wave's waits overlap the other's MFMAs): best when K is long
-//      and every group has many rows (the K loop amortises the pipeline
-//      fill); the gate/up projection already from K = 1024;
+//   L  256x256 tiles on the ping-pong kernel, one workgroup of eight waves
+//      per CU: best when every group has many rows and K is at least 512
+//      (the gate/up projection from K = 1024) -- Mixtral prefill gate/up
+//      3.32 -> 3.16 ms and down 1.86 -> 1.76 ms against the same tile on
+//      gemm_bf16_kernel, the Granite T = 16384 down projection (K = 512)
+//      269 -> 250 us against the M tile;
 //   M  128-row tiles, two per CU: the default;
 //   N  (gate/up only) 128-row tiles of 64 output columns with 64-wide K
 //      stages: every row segment a load fetches is a whole 128-byte line
@@ -669,7 +957,7 @@ static long est_tiles(const GemmPlan& pl, int bm, int bno, int N) {
 static TileCfg tile_cfg(const GemmPlan& pl, int N, int K, bool swiglu) {
   const int bno = swiglu ? 128 : 256;
   const long per_group = pl.grouped ? pl.R_max / (pl.E > 0 ? pl.E : 1) : pl.M_dense;
-  if (K >= (swiglu ? 1024 : 2048) && per_group >= 1024 && est_tiles(pl, 256, bno, N) >= 256)
+  if (K >= (swiglu ? 1024 : 512) && per_group >= 1024 && est_tiles(pl, 256, bno, N) >= 256)
     return TILE_L;
   // GEMM 1 keeps 128-row tiles unless the rows are very few (decode); the
   // down projection takes 64-row tiles below about two rounds
@@ -707,10 +995,30 @@ static hipError_t run_bf16(const GemmPlan& pl, GemmArgs a, hipStream_t st) {
   return hipGetLastError();
 }
 
+// The 256x256 tile on the ping-pong kernel (no K split: the L tile is only
+// chosen when the tiles fill the chip, where no split is planned).
+template <bool SWIGLU>
+static hipError_t run_pp(const GemmPlan& pl, GemmArgs a, hipStream_t st) {
+  constexpr int BNO = SWIGLU ? 128 : 256;
+  a.n_tiles = (a.N + BNO - 1) / BNO;
+  a.m_tiles = (int)row_tile_bound(pl, 256);
+  const long blocks = ((long)a.m_tiles * a.n_tiles + 7) / 8 * 8;
+  a.main_blocks = (int)blocks;
+  const long grid = blocks + (a.y_tok ? (a.y_T + kZeroTok - 1) / kZeroTok : 0);
+  if (grid == 0) return hipSuccess;
+  if (a.a_rows)
+    hipLaunchKernelGGL((gemm_pp_kernel<SWIGLU, true>), dim3((unsigned)grid), dim3(512), 0, st, a);
+  else
+    hipLaunchKernelGGL((gemm_pp_kernel<SWIGLU, false>), dim3((unsigned)grid), dim3(512), 0, st, a);
+  return hipGetLastError();
+}
+
 template <bool SWIGLU, bool PARTIAL>
 static hipError_t run_cfg(const GemmPlan& pl, GemmArgs a, hipStream_t st) {
   switch (tile_cfg(pl, a.N, a.K, SWIGLU)) {
-    case TILE_L: return run_bf16<256, 256, 4, 2, 64, 2, 3, 1, SWIGLU, PARTIAL>(pl, a, st);
+    case TILE_L:
+      if constexpr (!PARTIAL) return run_pp<SWIGLU>(pl, a, st);
+      else return run_bf16<256, 256, 4, 2, 64, 2, 3, 1, SWIGLU, PARTIAL>(pl, a, st);
     case TILE_M: return run_bf16<128, 256, 2, 2, 32, 3, 3, 2, SWIGLU, PARTIAL>(pl, a, st);
     case TILE_N:
       if constexpr (SWIGLU) return run_bf16<128, 128, 2, 2, 64, 2, 3, 2, SWIGLU, PARTIAL>(pl, a, st);

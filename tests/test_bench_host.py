@@ -16,7 +16,14 @@ SHARED1 = "void moe::gemm_bf16_kernel<256, 256, 4, 2, 64, 2, 3, 1, true, false, 
 COPY = "__amd_rocclr_copyBuffer"
 
 
+PP1 = "void moe::gemm_pp_kernel<true, true>(moe::GemmArgs)"
+PP2 = "void moe::gemm_pp_kernel<false, false>(moe::GemmArgs)"
+PPS = "void moe::gemm_pp_kernel<true, false>(moe::GemmArgs)"
+
+
 def test_gemm1_filter():
+    assert bench._is_gemm1(PP1)
+    assert not bench._is_gemm1(PP2) and not bench._is_gemm1(PPS)
     assert bench._is_gemm1(G1)
     assert not bench._is_gemm1(G2)
     assert not bench._is_gemm1(SHARED1)  # the shared expert's GEMM 1 reads x directly
