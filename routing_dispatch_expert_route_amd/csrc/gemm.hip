@@ -56,7 +56,47 @@ struct GemmArgs {
   const int32_t* y_pos;
   int y_T;
   int main_blocks;
+  // Down projection on 256x256 tiles: when the real tiles leave the last
+  // round of 256 workgroups at most half full, its tiles are split into q
+  // K pieces (q <= 4, r*q <= 256 for r such tiles); piece unit u writes its
+  // fp32 tile to tail + u*65536 and tail_fixup_kernel sums the pieces.
+  float* tail;
 };
+
+constexpr int kTailCUs = 256;  // workgroups per round of the 256x256 tile
+constexpr int kTailMaxSplit = 4;
+constexpr long kTailTileFloats = 256 * 256;
+
+constexpr int kTailMinStages = 16;  // 64-wide K stages per piece, at least
+
+// The tail split of n_real tiles with nk K stages each: tiles [0, full)
+// whole, tiles [full, n_real) in q pieces each.  A piece keeps at least
+// kTailMinStages stages: below that its own start-up and the fp32 round
+// trip cost more than the idle CUs it fills (Granite's down projection, K
+// = 512: 230 -> 286 us when split four ways).
+__host__ __device__ __forceinline__ void tail_plan(int n_real, int nk, int& full, int& q) {
+  full = n_real / kTailCUs * kTailCUs;
+  const int r = n_real - full;
+  q = r > 0 ? kTailCUs / r : 1;
+  if (q > kTailMaxSplit) q = kTailMaxSplit;
+  if (q > nk / kTailMinStages) q = nk / kTailMinStages;
+  if (q < 2) {
+    full = n_real;
+    q = 1;
+  }
+}
+
+// Tile l of m_real row tiles x n_tiles column tiles: groups of GM row tiles,
+// the column tile slowest inside a group.
+__device__ __forceinline__ void tile_mn(int l, int m_real, int n_tiles, int& mt, int& nt) {
+  constexpr int GM = 8;
+  const int group = l / (GM * n_tiles);
+  const int first = group * GM;
+  const int gsize = min(GM, m_real - first);
+  const int within = l - group * GM * n_tiles;
+  mt = first + within % gsize;
+  nt = within / gsize;
+}
 
 // Tokens per zero-row workgroup of the fused combine.
 constexpr int kZeroTok = 16;
@@ -657,12 +697,35 @@ __global__ __launch_bounds__(512, 1) void gemm_pp_kernel(GemmArgs a) {
     }
   }
   if (wave == 0) {
-    int mt0 = 0, nt0 = 0, ks0 = 0;
-    if (tile_of_block(a, count_row_tiles<BM>(a, lane), mt0, nt0, ks0)) {
+    int mt0 = 0, nt0 = 0, ks0 = 0, piece = 0, q = 1, unit = -1;
+    bool have;
+    const int m_real = count_row_tiles<BM>(a, lane);
+    int full = 0;
+    if (!SWIGLU && a.tail) tail_plan(m_real * a.n_tiles, (a.K + 63) / 64, full, q);
+    if (q > 1) {
+      // whole tiles first (XCD-aware over them; full is a multiple of 256),
+      // then the K pieces of the last round's tiles
+      const int n_real = m_real * a.n_tiles;
+      const int b = blockIdx.x;
+      have = b < full + (n_real - full) * q;
+      if (have && b < full) {
+        const int chunk = full / 8;
+        tile_mn((b % 8) * chunk + b / 8, m_real, a.n_tiles, mt0, nt0);
+      } else if (have) {
+        unit = b - full;
+        piece = unit % q;
+        tile_mn(full + unit / q, m_real, a.n_tiles, mt0, nt0);
+      }
+    } else {
+      have = tile_of_block(a, m_real, mt0, nt0, ks0);
+    }
+    if (have) {
       find_row_tile<BM>(a, mt0, lane, s_info);
       if (lane == 0) {
         s_info[3] = nt0;
-        s_info[4] = ks0;
+        s_info[4] = piece;
+        s_info[5] = unit >= 0 ? q : 1;  // a whole tile takes all of K
+        s_info[6] = unit;
       }
     } else if (lane == 0) {
       s_info[0] = -1;
@@ -674,9 +737,15 @@ __global__ __launch_bounds__(512, 1) void gemm_pp_kernel(GemmArgs a) {
   const int row0 = __builtin_amdgcn_readfirstlane(s_info[1]);
   const int rows = __builtin_amdgcn_readfirstlane(s_info[2]);
   const int nt = __builtin_amdgcn_readfirstlane(s_info[3]);
+  const int piece = __builtin_amdgcn_readfirstlane(s_info[4]);
+  const int npiece = __builtin_amdgcn_readfirstlane(s_info[5]);
+  const int unit = __builtin_amdgcn_readfirstlane(s_info[6]);
   __syncthreads();  // every wave has its tile before X0 is refilled
   const int K = a.K, N = a.N;
-  const int klen = K;
+  // K range of this workgroup: all of K, or piece `piece` of npiece
+  const int kc = ((K + BK - 1) / BK + npiece - 1) / npiece * BK;
+  const int kb = piece * kc;
+  const int klen = min(K, kb + kc) - kb;
 
   // This wave's loads: group 0 the activation rows (wi*NL + q)*RPS + lane/CH,
   // group 1 the weight rows of the same numbers; lane i of a wave-level load
@@ -743,16 +812,17 @@ __global__ __launch_bounds__(512, 1) void gemm_pp_kernel(GemmArgs a) {
       const int row = (wi * NL + q) * RPS;  // the load's first row in the tile
       int reg = 0;
       unsigned vo, so;
+      const unsigned kofs = (unsigned)((kb + k0) * 2);
       if (grp == 0 && GOFF) {
         vo = goff[GOFF ? q : 0];
-        so = (unsigned)(k0 * 2);
+        so = kofs;
       } else if (grp == 0) {
         vo = lo[q & 1];
-        so = ubase + (unsigned)(q * RPS) * (unsigned)K * 2u + (unsigned)(k0 * 2);
+        so = ubase + (unsigned)(q * RPS) * (unsigned)K * 2u + kofs;
       } else {
         reg = row / BNO;
         vo = lo[q & 1];
-        so = ubase + (unsigned)(row % BNO) * (unsigned)K * 2u + (unsigned)(k0 * 2);
+        so = ubase + (unsigned)(row % BNO) * (unsigned)K * 2u + kofs;
       }
       if (tail && chk[q & 1] * 8 >= klen - k0) vo = 0x80000000u;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc[reg], (lds_ptr_t)(dst + (wi * NL + q) * 64), 16,
@@ -880,9 +950,87 @@ __global__ __launch_bounds__(512, 1) void gemm_pp_kernel(GemmArgs a) {
   }
   __builtin_amdgcn_s_waitcnt(0x0F70);  // the refills past the end have landed
   if (wm * WTM >= rows) return;
+  if constexpr (!SWIGLU) {
+    if (unit >= 0) {  // a K piece: the fp32 tile, all 256x256 of it
+      float* T = a.tail + (size_t)unit * kTailTileFloats;
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int m = wm * WTM + i * 32 + lrow;
+            const int n = wn * WTN + j * 32 + 8 * q + 4 * lk;
+            f32x4_t v = {acc[0][j][i][4 * q], acc[0][j][i][4 * q + 1], acc[0][j][i][4 * q + 2],
+                         acc[0][j][i][4 * q + 3]};
+            *reinterpret_cast<f32x4_t*>(T + m * 256 + n) = v;
+          }
+      return;
+    }
+  }
   store_tile<NREG, TN, TM, BNO, WTM, WTN, SWIGLU, false>(a, acc, row0, rows, nt, 0, wm, wn, lrow,
                                                         lk);
 #endif
+}
+
+// Sum of the K pieces of the down GEMM's split tiles (see GemmArgs::tail):
+// workgroup t takes split tile full + t, adds its q pieces in piece order in
+// fp32, rounds once to bf16 and writes the tile's rows of C (or, with the
+// fused combine, each row gate-scaled to its token's row).
+__global__ __launch_bounds__(256) void tail_fixup_kernel(GemmArgs a) {
+  __shared__ int s_info[8];
+  const int tid = threadIdx.x;
+  if (tid < 64) {
+    const int m_real = count_row_tiles<256>(a, tid);
+    const int n_real = m_real * a.n_tiles;
+    int full, q;
+    tail_plan(n_real, (a.K + 63) / 64, full, q);
+    const int t = blockIdx.x;
+    if (q > 1 && full + t < n_real) {
+      int mt, nt;
+      tile_mn(full + t, m_real, a.n_tiles, mt, nt);
+      find_row_tile<256>(a, mt, tid, s_info);
+      if (tid == 0) {
+        s_info[3] = nt;
+        s_info[4] = q;
+      }
+    } else if (tid == 0) {
+      s_info[0] = -1;
+    }
+  }
+  __syncthreads();
+  if (s_info[0] < 0) return;
+  const int row0 = s_info[1], rows = s_info[2], nt = s_info[3], q = s_info[4];
+  const int N = a.N;
+  const float* P = a.tail + (size_t)blockIdx.x * q * kTailTileFloats;
+  // 4 columns per thread and step: 64 column groups x 4 rows per pass
+  for (int idx = tid; idx < 256 * 64; idx += 256) {
+    const int m = idx / 64, c4 = (idx % 64) * 4;
+    const int n = nt * 256 + c4;
+    if (m >= rows || n >= N) continue;
+    f32x4_t s = *reinterpret_cast<const f32x4_t*>(P + m * 256 + c4);
+    for (int p = 1; p < q; ++p) {
+      const f32x4_t v = *reinterpret_cast<const f32x4_t*>(P + (size_t)p * kTailTileFloats + m * 256 + c4);
+      s[0] += v[0];
+      s[1] += v[1];
+      s[2] += v[2];
+      s[3] += v[3];
+    }
+    const size_t pr = (size_t)(row0 + m);
+    uint2 w;
+    if (a.y_tok) {
+      const int tk = a.y_tok[pr];
+      const float g = a.y_gate[tk];
+      const uint32_t r0 = pack_bf16x2(s[0], s[1]), r1 = pack_bf16x2(s[2], s[3]);
+      w.x = pack_bf16x2(__builtin_fmaf(g, bf16lo(r0), 0.0f), __builtin_fmaf(g, bf16hi(r0), 0.0f));
+      w.y = pack_bf16x2(__builtin_fmaf(g, bf16lo(r1), 0.0f), __builtin_fmaf(g, bf16hi(r1), 0.0f));
+      *reinterpret_cast<uint2*>(reinterpret_cast<bf16_t*>(a.C) + (size_t)tk * N + n) = w;
+    } else {
+      w.x = pack_bf16x2(s[0], s[1]);
+      w.y = pack_bf16x2(s[2], s[3]);
+      *reinterpret_cast<uint2*>(reinterpret_cast<bf16_t*>(a.C) + pr * N + n) = w;
+    }
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -1002,7 +1150,10 @@ static hipError_t run_pp(const GemmPlan& pl, GemmArgs a, hipStream_t st) {
   constexpr int BNO = SWIGLU ? 128 : 256;
   a.n_tiles = (a.N + BNO - 1) / BNO;
   a.m_tiles = (int)row_tile_bound(pl, 256);
-  const long blocks = ((long)a.m_tiles * a.n_tiles + 7) / 8 * 8;
+  a.tail = SWIGLU ? nullptr : pl.tail;
+  long blocks = ((long)a.m_tiles * a.n_tiles + 7) / 8 * 8;
+  // room for the K pieces of a last round (r tiles become r*q <= 256 units)
+  if (a.tail) blocks += kTailCUs;
   a.main_blocks = (int)blocks;
   const long grid = blocks + (a.y_tok ? (a.y_T + kZeroTok - 1) / kZeroTok : 0);
   if (grid == 0) return hipSuccess;
@@ -1010,7 +1161,16 @@ static hipError_t run_pp(const GemmPlan& pl, GemmArgs a, hipStream_t st) {
     hipLaunchKernelGGL((gemm_pp_kernel<SWIGLU, true>), dim3((unsigned)grid), dim3(512), 0, st, a);
   else
     hipLaunchKernelGGL((gemm_pp_kernel<SWIGLU, false>), dim3((unsigned)grid), dim3(512), 0, st, a);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess || !a.tail) return err;
+  hipLaunchKernelGGL(tail_fixup_kernel, dim3(kTailCUs), dim3(256), 0, st, a);
   return hipGetLastError();
+}
+
+long gemm_tail_floats(const GemmPlan& pl, int N, int K) {
+  if (!pl.bf16 || tile_cfg(pl, N, K, false) != TILE_L) return 0;
+  if ((K + 63) / 64 < 2 * kTailMinStages) return 0;  // never split
+  return (long)kTailCUs * kTailTileFloats;
 }
 
 template <bool SWIGLU, bool PARTIAL>

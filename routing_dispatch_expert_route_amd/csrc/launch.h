@@ -86,7 +86,13 @@ struct GemmPlan {
   int M_dense;
   long R_max;  // bound on offsets[E]
   long m_cap;  // bound on any one group's rows
+  // fp32 scratch of gemm_tail_floats(plan, N, K) floats for the down GEMM's
+  // last-round tiles split along K (nullptr: no split)
+  float* tail = nullptr;
 };
+// fp32 scratch the down GEMM of this plan uses to split its last round of
+// 256x256 tiles along K (0 when it does not): a pure function of the plan.
+long gemm_tail_floats(const GemmPlan& pl, int N, int K);
 // a_nrows: rows of A (its byte extent bounds the activation loads)
 hipError_t launch_gemm_swiglu(const GemmPlan& pl, const void* A, const int32_t* a_rows,
                               long a_nrows, const void* Wg, const void* Wu, int N, int K, void* H,

@@ -79,6 +79,10 @@ struct Layout {
       ys, spart, shist, xpad, opad, ppos, ids2, slot, offs2, rpos0, pref, dast, eck, ecp, ecoff;
   // queue policy: packed rows of the arrivals, the outgoing queue's arrivals
   size_t xq, qarr;
+  // fp32 scratch of the down GEMM's split last round (0 bytes when no plan
+  // of this shape splits)
+  size_t tail;
+  long tail_floats;
   int splits;      // K splits of the routed down GEMM (fp32 partial planes when > 1)
   int splits_pad;  // the same for the fixed-shape [E, C] layout
   int splits_ec;   // the same for expert-choice rows
@@ -242,6 +246,21 @@ Layout layout_of(const moe_shape* s, int64_t Q = -1) {
   // queued rows), and the arrivals of the outgoing queue
   L.xq = take(queued ? (size_t)Rmax * s->d * eb : 0);
   L.qarr = take(queued ? R * sizeof(int32_t) : 0);
+  long tf = moe::gemm_tail_floats(routed, (int)s->d, (int)s->d_ff);
+  if (Rpad > 0) {
+    const long tp = moe::gemm_tail_floats(padded_plan(s, nullptr), (int)s->d, (int)s->d_ff);
+    const long tc = moe::gemm_tail_floats(choice_plan(s, nullptr), (int)s->d, (int)s->d_ff);
+    tf = tp > tf ? tp : tf;
+    tf = tc > tf ? tc : tf;
+  }
+  if (s->d_ff_shared > 0) {
+    const moe::GemmPlan ps{s->dtype == MOE_DTYPE_BF16, false, nullptr, 1, (int)s->T, (long)s->T,
+                           (long)s->T};
+    const long ts = moe::gemm_tail_floats(ps, (int)s->d, (int)s->d_ff_shared);
+    tf = ts > tf ? ts : tf;
+  }
+  L.tail_floats = tf;
+  L.tail = take((size_t)tf * sizeof(float));
   L.total = o;
   return L;
 }
@@ -259,6 +278,14 @@ T* at(void* ws, size_t off) {
 }
 
 int hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
+
+// The plan with the workspace's tail scratch attached, for a down GEMM of
+// width N over K that splits its last round.
+moe::GemmPlan with_tail(moe::GemmPlan pl, const Layout& L, void* ws, int N, int K) {
+  const long need = moe::gemm_tail_floats(pl, N, K);
+  pl.tail = (need > 0 && need <= L.tail_floats) ? at<float>(ws, L.tail) : nullptr;
+  return pl;
+}
 
 // Device address of `scratch` on the current device, looked up once per
 // device with that device current (the first noalloc call there); nullptr
@@ -451,7 +478,7 @@ int moe_expert_ffn(const moe_shape* s, const void* x_packed, const int32_t* offs
   v = check_ws(s, ws, ws_bytes);
   if (v != MOE_OK) return v;
   const Layout L = layout_of(s);
-  const moe::GemmPlan pl = routed_plan(s, offsets, false);
+  const moe::GemmPlan pl = with_tail(routed_plan(s, offsets, false), L, ws, (int)s->d, (int)s->d_ff);
   const bool bf16 = s->dtype == MOE_DTYPE_BF16;
   void* h = at<void>(ws, L.h);
   hipError_t e = moe::launch_gemm_swiglu(pl, x_packed, nullptr, pl.R_max, w_gate, w_up,
@@ -503,7 +530,7 @@ int moe_routing_stats(const moe_shape* s, const float* logits, const float* gate
 // [T][kslots], or [kslots][T] when slot_major).  splits: K splits of the
 // down GEMM, whose fp32 planes hold `rows` rows each.  Records events 2..6 of
 // the timed variant.
-static int experts_and_combine(const moe_shape* s, const Layout& L, const moe::GemmPlan& pl,
+static int experts_and_combine(const moe_shape* s, const Layout& L, const moe::GemmPlan& pl_in,
                                const void* x, const void* A, const int32_t* a_rows, long a_nrows,
                                const void* w_gate, const void* w_up, const void* w_down,
                                const void* ws_gate, const void* ws_up, const void* ws_down,
@@ -512,6 +539,7 @@ static int experts_and_combine(const moe_shape* s, const Layout& L, const moe::G
                                hipEvent_t* ev) {
   const bool bf16 = s->dtype == MOE_DTYPE_BF16;
   const int T = (int)s->T, d = (int)s->d, dff = (int)s->d_ff;
+  const moe::GemmPlan pl = with_tail(pl_in, L, ws, d, dff);
   void* h = at<void>(ws, L.h);
   void* yp = at<void>(ws, L.yp);
   auto mark = [&](int i) {
@@ -544,7 +572,8 @@ static int experts_and_combine(const moe_shape* s, const Layout& L, const moe::G
   mark(4);
   const void* ysh = nullptr;
   if (s->d_ff_shared > 0) {
-    moe::GemmPlan ps{bf16, false, nullptr, 1, T, (long)T, (long)T};
+    const moe::GemmPlan ps = with_tail(moe::GemmPlan{bf16, false, nullptr, 1, T, (long)T, (long)T},
+                                       L, ws, d, (int)s->d_ff_shared);
     void* hs = at<void>(ws, L.hs);
     void* ys = at<void>(ws, L.ys);
     e = moe::launch_gemm_swiglu(ps, x, nullptr, T, ws_gate, ws_up, (int)s->d_ff_shared, d, hs,
