@@ -582,5 +582,5 @@ def layer_forward_queued_timed(s, x, w_router, b_router, w_gate, w_up, w_down, w
     _check(_lib.moe_layer_forward_queued_timed(ctypes.byref(s), *args, qn, qx, qi, qg, qt,
                                                *_out_args(s, bufs, qn, dt), ws.data_ptr(),
                                                ws.numel(), _stream(stream), arr),
-           "moe_layer_forward_queued_timed", "moe_layer_forward_noalloc")
+           "moe_layer_forward_queued_timed")
     return bufs["y"]

@@ -974,9 +974,11 @@ __global__ __launch_bounds__(512, 1) void gemm_pp_kernel(GemmArgs a) {
 }
 
 // Sum of the K pieces of the down GEMM's split tiles (see GemmArgs::tail):
-// workgroup t takes split tile full + t, adds its q pieces in piece order in
-// fp32, rounds once to bf16 and writes the tile's rows of C (or, with the
-// fused combine, each row gate-scaled to its token's row).
+// the kTailFixSlices workgroups of split tile full + t each take 256 /
+// kTailFixSlices of its rows, add the rows' q pieces in piece order in fp32,
+// round once to bf16 and write the rows of C (or, with the fused combine,
+// each row gate-scaled to its token's row).
+constexpr int kTailFixSlices = 16;
 __global__ __launch_bounds__(256) void tail_fixup_kernel(GemmArgs a) {
   __shared__ int s_info[8];
   const int tid = threadIdx.x;
@@ -985,7 +987,7 @@ __global__ __launch_bounds__(256) void tail_fixup_kernel(GemmArgs a) {
     const int n_real = m_real * a.n_tiles;
     int full, q;
     tail_plan(n_real, (a.K + 63) / 64, full, q);
-    const int t = blockIdx.x;
+    const int t = blockIdx.x / kTailFixSlices;
     if (q > 1 && full + t < n_real) {
       int mt, nt;
       tile_mn(full + t, m_real, a.n_tiles, mt, nt);
@@ -1002,10 +1004,12 @@ __global__ __launch_bounds__(256) void tail_fixup_kernel(GemmArgs a) {
   if (s_info[0] < 0) return;
   const int row0 = s_info[1], rows = s_info[2], nt = s_info[3], q = s_info[4];
   const int N = a.N;
-  const float* P = a.tail + (size_t)blockIdx.x * q * kTailTileFloats;
+  const float* P = a.tail + (size_t)(blockIdx.x / kTailFixSlices) * q * kTailTileFloats;
+  constexpr int SR = 256 / kTailFixSlices;  // rows of this workgroup's slice
+  const int m0 = (blockIdx.x % kTailFixSlices) * SR;
   // 4 columns per thread and step: 64 column groups x 4 rows per pass
-  for (int idx = tid; idx < 256 * 64; idx += 256) {
-    const int m = idx / 64, c4 = (idx % 64) * 4;
+  for (int idx = tid; idx < SR * 64; idx += 256) {
+    const int m = m0 + idx / 64, c4 = (idx % 64) * 4;
     const int n = nt * 256 + c4;
     if (m >= rows || n >= N) continue;
     f32x4_t s = *reinterpret_cast<const f32x4_t*>(P + m * 256 + c4);
@@ -1163,7 +1167,7 @@ static hipError_t run_pp(const GemmPlan& pl, GemmArgs a, hipStream_t st) {
     hipLaunchKernelGGL((gemm_pp_kernel<SWIGLU, false>), dim3((unsigned)grid), dim3(512), 0, st, a);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess || !a.tail) return err;
-  hipLaunchKernelGGL(tail_fixup_kernel, dim3(kTailCUs), dim3(256), 0, st, a);
+  hipLaunchKernelGGL(tail_fixup_kernel, dim3(kTailCUs * kTailFixSlices), dim3(256), 0, st, a);
   return hipGetLastError();
 }
 

@@ -205,3 +205,49 @@ def test_queue_without_capacity_routes_like_the_layer(moe):
     assert np.array_equal(_np(rt["route_pos"]).reshape(w.T, w.k), ref["route_pos"])
     assert np.array_equal(_np(rt["counts"]), ref["counts"])
     check_y(yq, ref["y"], w.dtype, "queued layer without capacity")
+
+
+def test_layer_forward_queued_timed_matches_untimed(moe):
+    """moe_layer_forward_queued_timed (the queued layer with its 7 stage
+    events, what bench.py --queue times) gives the untimed call's outputs bit
+    for bit: y, the late rows and the outgoing queue, for a call that both
+    receives and leaves routes waiting."""
+    import ctypes
+    hip = ctypes.CDLL("libamdhip64.so")
+    hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+    hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                        ctypes.c_void_p]
+    hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+    w, _, seed = RUNS["e32_k8_shared_zipf"]
+    wts = _weights(w, seed)
+    dev = {k: (None if v is None else v.cuda()) for k, v in wts.items()}
+    args = (dev["w_router"], dev["b_router"], dev["w_gate"], dev["w_up"], dev["w_down"],
+            dev["ws_gate"], dev["ws_up"], dev["ws_down"])
+    s0 = moe.shape_of(w.with_(T=300))
+    _, _, q = moe.layer_forward_queued(s0, _x(w, 300, 1).cuda(), *args)
+    Q = int(q["ids"].shape[0])
+    assert Q > 0, "the first call left no route waiting"
+    s = moe.shape_of(w.with_(T=257))
+    x = _x(w, 257, 2).cuda()
+    y, y_late, qo = moe.layer_forward_queued(s, x, *args, queue=q)
+    say(f"[queue timed] T=257 Q={Q}: {int(qo['ids'].shape[0])} routes leave")
+    bufs = moe.queue_buffers(s, Q)
+    evs = []
+    for _ in range(7):
+        e = ctypes.c_void_p()
+        assert hip.hipEventCreate(ctypes.byref(e)) == 0
+        evs.append(e.value)
+    y2 = moe.layer_forward_queued_timed(s, x, *args, q, bufs, evs)
+    torch.cuda.synchronize()
+    n = int(bufs["out_n"].item())
+    assert np.array_equal(bits(y), bits(y2))
+    assert np.array_equal(bits(y_late), bits(bufs["y_late"]))
+    assert n == int(qo["ids"].shape[0])
+    assert np.array_equal(_np(qo["ids"]), _np(bufs["out_ids"][:n]))
+    assert np.array_equal(_np(qo["tags"]), _np(bufs["out_tags"][:n]))
+    assert np.array_equal(bits(qo["x"]), bits(bufs["out_x"][:n]))
+    f = ctypes.c_float()
+    assert hip.hipEventElapsedTime(ctypes.byref(f), evs[0], evs[6]) == 0
+    assert f.value > 0.0
+    for e in evs:
+        hip.hipEventDestroy(e)
