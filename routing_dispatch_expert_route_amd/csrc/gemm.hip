@@ -86,17 +86,6 @@ __host__ __device__ __forceinline__ void tail_plan(int n_real, int nk, int& full
   }
 }
 
-// Tile l of m_real row tiles x n_tiles column tiles: groups of GM row tiles,
-// the column tile slowest inside a group.
-__device__ __forceinline__ void tile_mn(int l, int m_real, int n_tiles, int& mt, int& nt) {
-  constexpr int GM = 8;
-  const int group = l / (GM * n_tiles);
-  const int first = group * GM;
-  const int gsize = min(GM, m_real - first);
-  const int within = l - group * GM * n_tiles;
-  mt = first + within % gsize;
-  nt = within / gsize;
-}
 
 // Tokens per zero-row workgroup of the fused combine.
 constexpr int kZeroTok = 16;
@@ -178,6 +167,64 @@ __device__ __forceinline__ int count_row_tiles(const GemmArgs& a, int lane) {
   return total;
 }
 
+// The linear order of the tiles: group (expert) after group; a group's rt
+// row tiles in ceil(rt / 8) bands of equal height (the last shorter), and
+// inside a band the column tile slowest.  The workgroups that run together
+// on one XCD then share a band's activation tiles and its expert's weight
+// tiles in the XCD's L2, and no band mixes two experts, whose weight tiles
+// would both be fetched.  Tile l -> info[0..3] = group, first packed row,
+// rows, column tile (written by the one lane that finds it; info[0] = -1 by
+// lane 0 when l is past the tiles).  Called by one whole wave.
+constexpr int kBandMax = 8;
+template <int BM>
+__device__ __forceinline__ void tile_at(const GemmArgs& a, int l, int lane, int* info) {
+  const bool dense = a.offsets == nullptr;
+  const int G = dense ? 1 : a.E;
+  const int nt_all = a.n_tiles;
+  int carry = 0;
+  for (int e0 = 0; e0 < G; e0 += kWave) {
+    const int e = e0 + lane;
+    int m = 0, off = 0;
+    if (e < G) {
+      if (dense) {
+        m = a.M_dense;
+      } else {
+        off = a.offsets[e];
+        m = a.offsets[e + 1] - off;
+      }
+    }
+    const int rt = (m + BM - 1) / BM;
+    const int tiles = rt * nt_all;
+    int incl = tiles;
+#pragma unroll
+    for (int s = 1; s < kWave; s <<= 1) {
+      const int o = __shfl_up(incl, s, kWave);
+      if (lane >= s) incl += o;
+    }
+    const int excl = carry + incl - tiles;
+    const bool mine = e < G && l >= excl && l < excl + tiles;
+    if (__ballot(mine)) {
+      if (mine) {
+        const int local = l - excl;
+        const int bands = (rt + kBandMax - 1) / kBandMax;
+        const int bh = (rt + bands - 1) / bands;  // band height
+        const int band = local / (bh * nt_all);
+        const int first = band * bh;
+        const int bsize = min(bh, rt - first);
+        const int within = local - band * bh * nt_all;
+        const int mtl = first + within % bsize;
+        info[0] = e;
+        info[1] = off + mtl * BM;
+        info[2] = min(BM, m - mtl * BM);
+        info[3] = within / bsize;
+      }
+      return;
+    }
+    carry += __shfl(incl, kWave - 1, kWave);
+  }
+  if (lane == 0) info[0] = -1;
+}
+
 // Block -> (row tile, column tile, K split) over the tiles that exist.  The
 // grid is an upper bound (a multiple of 8) on the tile count; the real count
 // comes from the device offsets.  Workgroups are dispatched round-robin over
@@ -187,25 +234,18 @@ __device__ __forceinline__ int count_row_tiles(const GemmArgs& a, int lane) {
 // groups of GM row tiles, column tile slowest inside a group, so the
 // workgroups that run together on one XCD share their weight and activation
 // tiles.  Returns false for a block with no tile.
-__device__ __forceinline__ bool tile_of_block(const GemmArgs& a, int m_real, int& mt, int& nt,
-                                              int& ks) {
-  constexpr int NXCD = 8, GM = 8;
+__device__ __forceinline__ bool tile_index(const GemmArgs& a, int m_real, int& l, int& ks) {
+  constexpr int NXCD = 8;
   const int bid = blockIdx.x;
   const int xcd = bid % NXCD, local = bid / NXCD;
   const int tiles = m_real * a.n_tiles;
   const int n_real = tiles * a.splits;
   const int chunk = (n_real + NXCD - 1) / NXCD;
   if (local >= chunk) return false;
-  int l = xcd * chunk + local;
+  l = xcd * chunk + local;
   if (l >= n_real) return false;
   ks = l / tiles;
   l -= ks * tiles;
-  const int group = l / (GM * a.n_tiles);
-  const int first = group * GM;
-  const int gsize = min(GM, m_real - first);
-  const int within = l - group * GM * a.n_tiles;
-  mt = first + within % gsize;
-  nt = within / gsize;
   return true;
 }
 
@@ -377,13 +417,10 @@ __global__ __launch_bounds__(64 * WM * WN, OCC) void gemm_bf16_kernel(GemmArgs a
     }
   }
   if (wave == 0) {
-    int mt0 = 0, nt0 = 0, ks0 = 0;
-    if (tile_of_block(a, count_row_tiles<BM>(a, lane), mt0, nt0, ks0)) {
-      find_row_tile<BM>(a, mt0, lane, s_info);
-      if (lane == 0) {
-        s_info[3] = nt0;
-        s_info[4] = ks0;
-      }
+    int l0 = 0, ks0 = 0;
+    if (tile_index(a, count_row_tiles<BM>(a, lane), l0, ks0)) {
+      tile_at<BM>(a, l0, lane, s_info);
+      if (lane == 0) s_info[4] = ks0;
     } else if (lane == 0) {
       s_info[0] = -1;
     }
@@ -697,7 +734,7 @@ __global__ __launch_bounds__(512, 1) void gemm_pp_kernel(GemmArgs a) {
     }
   }
   if (wave == 0) {
-    int mt0 = 0, nt0 = 0, ks0 = 0, piece = 0, q = 1, unit = -1;
+    int l0 = 0, ks0 = 0, piece = 0, q = 1, unit = -1;
     bool have;
     const int m_real = count_row_tiles<BM>(a, lane);
     int full = 0;
@@ -710,19 +747,18 @@ __global__ __launch_bounds__(512, 1) void gemm_pp_kernel(GemmArgs a) {
       have = b < full + (n_real - full) * q;
       if (have && b < full) {
         const int chunk = full / 8;
-        tile_mn((b % 8) * chunk + b / 8, m_real, a.n_tiles, mt0, nt0);
+        l0 = (b % 8) * chunk + b / 8;
       } else if (have) {
         unit = b - full;
         piece = unit % q;
-        tile_mn(full + unit / q, m_real, a.n_tiles, mt0, nt0);
+        l0 = full + unit / q;
       }
     } else {
-      have = tile_of_block(a, m_real, mt0, nt0, ks0);
+      have = tile_index(a, m_real, l0, ks0);
     }
     if (have) {
-      find_row_tile<BM>(a, mt0, lane, s_info);
+      tile_at<BM>(a, l0, lane, s_info);
       if (lane == 0) {
-        s_info[3] = nt0;
         s_info[4] = piece;
         s_info[5] = unit >= 0 ? q : 1;  // a whole tile takes all of K
         s_info[6] = unit;
@@ -912,10 +948,14 @@ __global__ __launch_bounds__(512, 1) void gemm_pp_kernel(GemmArgs a) {
     __builtin_amdgcn_s_waitcnt(WAIT_ALL);
     __builtin_amdgcn_s_barrier();
   };
+  // group 1 holds tile rows 128..255: with 128 rows or fewer (an expert's
+  // last, partial row tile) its MFMAs would only fill rows that are never
+  // stored, and skipping them shortens every other phase
+  const bool act1 = rows > 128;
   auto stage1 = [&](auto S, int kt) __attribute__((always_inline)) {
     constexpr int s = decltype(S)::value;
     // phase 2kt: compute the previous stage
-    if (kt > 0) {
+    if (kt > 0 && act1) {
       __builtin_amdgcn_s_setprio(1);
       compute();
       __builtin_amdgcn_s_setprio(0);
@@ -946,7 +986,7 @@ __global__ __launch_bounds__(512, 1) void gemm_pp_kernel(GemmArgs a) {
     run(std::integral_constant<int, 0>{});
   } else {
     run(std::integral_constant<int, 1>{});
-    compute();  // the last stage (group 0 has left the loop; no barrier follows)
+    if (act1) compute();  // the last stage (group 0 has left the loop; no barrier follows)
   }
   __builtin_amdgcn_s_waitcnt(0x0F70);  // the refills past the end have landed
   if (wm * WTM >= rows) return;
@@ -989,13 +1029,8 @@ __global__ __launch_bounds__(256) void tail_fixup_kernel(GemmArgs a) {
     tail_plan(n_real, (a.K + 63) / 64, full, q);
     const int t = blockIdx.x / kTailFixSlices;
     if (q > 1 && full + t < n_real) {
-      int mt, nt;
-      tile_mn(full + t, m_real, a.n_tiles, mt, nt);
-      find_row_tile<256>(a, mt, tid, s_info);
-      if (tid == 0) {
-        s_info[3] = nt;
-        s_info[4] = q;
-      }
+      tile_at<256>(a, full + t, tid, s_info);
+      if (tid == 0) s_info[4] = q;
     } else if (tid == 0) {
       s_info[0] = -1;
     }
