@@ -466,6 +466,14 @@ FUSED = {
     "switch_phi1": WORKLOADS["switch_phi1"],
     "k1_ragged_drops": Workload("k1_ragged", T=515, E=6, k=1, d=72, d_ff=40, renorm=0, phi=0.7,
                                 bias="normal"),
+    # the 256x256 down tile with a partial last round (about 300 tiles) and
+    # K = 2048: that round is split along K into fp32 pieces, and the fix-up
+    # kernel writes the gate-scaled token rows (and, with drops, the zero rows
+    # come from the appended workgroups)
+    "k1_tail_split": Workload("k1_tail", T=18432, E=8, k=1, d=1024, d_ff=2048, renorm=0,
+                              bias="normal"),
+    "k1_tail_split_drops": Workload("k1_tail_drops", T=18432, E=8, k=1, d=1024, d_ff=2048,
+                                    renorm=0, phi=0.9),
 }
 
 
