@@ -922,14 +922,18 @@ __global__ __launch_bounds__(512, 1) void gemm_pp_kernel(GemmArgs a) {
   };
   constexpr int LB = NSX * NSW;  // slot combinations repeat every 6 stages
   const int nk = (klen + BK - 1) / BK;
-  // prologue: activation stage 0 (group 0), weight stages 0 and 1 (group 1)
+  // prologue: activation stage 0 (group 0), weight stages 0 and 1 (group 1);
+  // only stage 0 must land before the first barrier -- group 1's stage-1
+  // loads (its last NL) are waited for by its counted wait in phase 1, as
+  // every later refill is
   if (grp == 0) {
     issue(xslot(std::integral_constant<int, 0>{}), 0);
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
   } else {
     issue(wslot(std::integral_constant<int, 0>{}), 0);
     issue(wslot(std::integral_constant<int, 1>{}), 1);
+    __builtin_amdgcn_s_waitcnt(0x0F70 | (NL & 15) | ((NL >> 4) << 14));  // vmcnt(NL)
   }
-  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
   __builtin_amdgcn_s_barrier();
   constexpr int WAIT_ALL = 0x0070;                                  // vmcnt(0) lgkmcnt(0)
   constexpr int WAIT_NL = 0x0070 | (NL & 15) | ((NL >> 4) << 14);  // vmcnt(NL) lgkmcnt(0)
