@@ -125,13 +125,15 @@ def traffic_from_profile(workload):
     return rec["traffic_bytes_per_launch"]
 
 
-def _is_gemm1(name):
+def _is_gemm1(name, shared=False):
     # gemm_bf16_kernel<tile and pipeline sizes..., SWIGLU, GATHER, PARTIAL> or
     # gemm_pp_kernel<SWIGLU, GATHER>: GEMM 1 of the whole-layer path is the
-    # SwiGLU instance that gathers token rows
+    # SwiGLU instance that gathers token rows -- or, on the 256x256 tile with
+    # a wide d_ff, the one that reads the rows packed first (the same name as
+    # a shared expert's GEMM 1 on that tile, so only without a shared expert)
     if "gemm_pp_kernel<" in name:
         args = [a.strip() for a in name.split("<", 1)[1].split(">", 1)[0].split(",")]
-        return args == ["true", "true"]
+        return args == ["true", "true"] or (args == ["true", "false"] and not shared)
     if "gemm_bf16_kernel<" not in name:
         return False
     args = [a.strip() for a in name.split("<", 1)[1].split(">", 1)[0].split(",")]
@@ -153,11 +155,13 @@ def _counter_rows(folder, counter):
 def traffic_summary(fetch_dir, write_dir, workload, cal_mib, out_path):
     """Per-launch HBM bytes of GEMM 1 from two counter passes, each counter
     scaled by what it reads for the calibration copies (known bytes)."""
+    from workloads import WORKLOADS
     res = {"workload": workload, "gemm_hip_sha256": _gemm_sha(), "calibration_mib": cal_mib}
     known = cal_mib * 1024.0  # KiB read (and written) by one calibration copy
     for key, folder, counter in (("fetch", fetch_dir, "FETCH_SIZE"), ("write", write_dir, "WRITE_SIZE")):
         rows = _counter_rows(folder, counter)
-        g1 = [float(r["Counter_Value"]) for r in rows if _is_gemm1(r["Kernel_Name"])]
+        shared = WORKLOADS[workload].d_ff_shared > 0 if workload in WORKLOADS else True
+        g1 = [float(r["Counter_Value"]) for r in rows if _is_gemm1(r["Kernel_Name"], shared)]
         cal = [float(r["Counter_Value"]) for r in rows if "copyBuffer" in r["Kernel_Name"]][-N_CAL:]
         if not g1 or len(cal) < N_CAL:
             raise SystemExit(f"{counter}: {len(g1)} GEMM-1 and {len(cal)} calibration dispatches")

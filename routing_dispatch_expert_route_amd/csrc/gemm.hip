@@ -1210,6 +1210,15 @@ static hipError_t run_pp(const GemmPlan& pl, GemmArgs a, hipStream_t st) {
   return hipGetLastError();
 }
 
+// Packing the rows first costs about 2*K*2 bytes of copy per row against
+// GEMM 1's 4*K*N flops per row, and gains a few per cent of GEMM 1: worth
+// it from a wide d_ff (N) on.  Same box, alternating builds: Mixtral prefill
+// (N = 14336) 4.82 -> 4.79-4.80 ms per step, with expert choice 4.55-4.57
+// -> 4.52; Granite T = 16384 (N = 512) 0.68 -> 0.75 ms, hence the bound.
+bool gemm_swiglu_prefers_packed(const GemmPlan& pl, int N, int K) {
+  return pl.bf16 && N >= 4096 && tile_cfg(pl, N, K, true) == TILE_L;
+}
+
 long gemm_tail_floats(const GemmPlan& pl, int N, int K) {
   if (!pl.bf16 || tile_cfg(pl, N, K, false) != TILE_L) return 0;
   if ((K + 63) / 64 < 2 * kTailMinStages) return 0;  // never split

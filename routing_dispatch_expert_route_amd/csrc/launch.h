@@ -90,6 +90,10 @@ struct GemmPlan {
   // last-round tiles split along K (nullptr: no split)
   float* tail = nullptr;
 };
+// True when GEMM 1 of this plan should read packed rows rather than gather
+// token rows: the 256x256 tile with a wide output (a pure function of the
+// plan and shape).
+bool gemm_swiglu_prefers_packed(const GemmPlan& pl, int N, int K);
 // fp32 scratch the down GEMM of this plan uses to split its last round of
 // 256x256 tiles along K (0 when it does not): a pure function of the plan.
 long gemm_tail_floats(const GemmPlan& pl, int N, int K);

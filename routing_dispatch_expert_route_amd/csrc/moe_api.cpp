@@ -546,8 +546,22 @@ static int experts_and_combine(const moe_shape* s, const Layout& L, const moe::G
     // a stage marker: a failed record loses a timing, never a result
     if (ev && ev[i]) (void)hipEventRecord(ev[i], stream);
   };
-  mark(2);
-  hipError_t e = moe::launch_gemm_swiglu(pl, A, a_rows, a_nrows, w_gate, w_up, dff, d, h, stream);
+  hipError_t e;
+  if (a_rows && moe::gemm_swiglu_prefers_packed(pl, dff, d)) {
+    // The 256x256 GEMM 1 tile streams packed rows faster than it gathers
+    // token rows (each of a tile's loads then takes a wave-uniform base), by
+    // more than the gather costs at a wide d_ff: the dispatch packs the rows
+    // (the pack of the permute step, before GEMM 1's stage marker) into
+    // y_packed, which is free until the down GEMM writes it.
+    e = moe::launch_gather_rows(A, a_rows, pl.offsets, pl.E, pl.R_max, (long)d * elem_bytes(s), yp,
+                                stream);
+    if (e != hipSuccess) return MOE_ERR_HIP;
+    mark(2);
+    e = moe::launch_gemm_swiglu(pl, yp, nullptr, pl.R_max, w_gate, w_up, dff, d, h, stream);
+  } else {
+    mark(2);
+    e = moe::launch_gemm_swiglu(pl, A, a_rows, a_nrows, w_gate, w_up, dff, d, h, stream);
+  }
   if (e != hipSuccess) return MOE_ERR_HIP;
   mark(3);
   if (bf16 && splits <= 1 && s->d_ff_shared == 0 && kslots == 1 && !slot_major && a_rows) {
