@@ -391,6 +391,11 @@ TILES = {
                                renorm=0, bias="normal"),
     # both GEMMs on the eight-wave 256-row tile with K tails (4104, 2056)
     "l_tile_both": Workload("l_tile_both", T=8192, E=2, k=1, d=4104, d_ff=2056, renorm=0),
+    # a wide d_ff on the 256-row tile with capacity drops: the dispatch packs
+    # the rows before GEMM 1 (K = 1032 tail, N = 4104 ragged), and the down
+    # GEMM (K = 4104) splits its partial last round along K
+    "l_tile_packed_drops": Workload("l_tile_packed_drops", T=16384, E=8, k=2, d=1032, d_ff=4104,
+                                    phi=0.9),
 }
 
 
