@@ -1154,6 +1154,12 @@ static TileCfg tile_cfg(const GemmPlan& pl, int N, int K, bool swiglu) {
   // down projection takes 64-row tiles below about two rounds
   const long est_m = est_tiles(pl, 128, bno, N);
   if (!swiglu) return est_m > 1024 ? TILE_M : TILE_S;
+  // decode: fewer rows per group than even the 64-row tile holds, so every
+  // tile streams weights for a handful of rows; the 64x256 tile streams
+  // twice the weight rows per workgroup of the 128x128 one (Mixtral decode
+  // GEMM 1 319 -> 309 us; at 350-500 rows per group, Switch and Granite
+  // T = 1412, it is slower)
+  if (per_group < 64) return TILE_S;
   if (est_m > 1024) return TILE_M;
   return est_m > 256 ? TILE_N : TILE_S;
 }
