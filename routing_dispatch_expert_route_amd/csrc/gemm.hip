@@ -328,42 +328,69 @@ __device__ __forceinline__ void store_tile(const GemmArgs& a, const f32x16_t (&a
 #pragma unroll
     for (int i = 0; i < TM; ++i) {
       const int m = wm * WTM + i * 32 + lrow;
-      if (m >= rows) continue;
+      const bool live = m < rows;
       const size_t p = (size_t)(row0 + m);
+      float o[4][4];
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int n = nt * BNO + wn * WTN + j * 32 + 8 * q + 4 * lk;
-        if (n >= N) continue;
-        float o[4];
+      for (int q = 0; q < 4; ++q)
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
           if constexpr (SWIGLU) {
             const float gv = acc[0][j][i][4 * q + t];
             const float uv = acc[1][j][i][4 * q + t];
-            o[t] = __fdividef(gv, 1.0f + __expf(-gv)) * uv;
+            o[q][t] = __fdividef(gv, 1.0f + __expf(-gv)) * uv;
           } else {
-            o[t] = acc[0][j][i][4 * q + t];
+            o[q][t] = acc[0][j][i][4 * q + t];
           }
         }
-        if constexpr (PARTIAL) {
-          float* Cp = reinterpret_cast<float*>(a.C) + (size_t)ks * a.split_stride;
-          f32x4_t v = {o[0], o[1], o[2], o[3]};
+      if constexpr (PARTIAL) {
+        if (!live) continue;
+        float* Cp = reinterpret_cast<float*>(a.C) + (size_t)ks * a.split_stride;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int n = nt * BNO + wn * WTN + j * 32 + 8 * q + 4 * lk;
+          if (n >= N) continue;
+          f32x4_t v = {o[q][0], o[q][1], o[q][2], o[q][3]};
           *reinterpret_cast<f32x4_t*>(Cp + p * N + n) = v;
-        } else if (!SWIGLU && a.y_tok) {
-          const int tk = a.y_tok[p];
-          const float g = a.y_gate[tk];
-          const uint32_t r0 = pack_bf16x2(o[0], o[1]), r1 = pack_bf16x2(o[2], o[3]);
-          uint2 v;
-          v.x = pack_bf16x2(__builtin_fmaf(g, bf16lo(r0), 0.0f), __builtin_fmaf(g, bf16hi(r0), 0.0f));
-          v.y = pack_bf16x2(__builtin_fmaf(g, bf16lo(r1), 0.0f), __builtin_fmaf(g, bf16hi(r1), 0.0f));
-          *reinterpret_cast<uint2*>(reinterpret_cast<bf16_t*>(a.C) + (size_t)tk * N + n) = v;
-        } else {
-          bf16_t* Cp = reinterpret_cast<bf16_t*>(a.C);
-          uint2 v;
-          v.x = pack_bf16x2(o[0], o[1]);
-          v.y = pack_bf16x2(o[2], o[3]);
-          *reinterpret_cast<uint2*>(Cp + p * N + n) = v;
         }
+        continue;
+      }
+      // bf16 rows: lane (r, h) of the 32x32 block holds columns 8q + 4h ..
+      // 8q + 4h + 3 of row r.  Each pair of column groups (q = 2u, 2u+1) is
+      // exchanged between the two halves of the wave, so that one lane holds
+      // 8 consecutive columns and stores them with one 16-byte write (lanes
+      // 0-31 columns 16u .. 16u+7, lanes 32-63 the next 8).
+      size_t drow = p;
+      float g = 1.0f;
+      if constexpr (!SWIGLU) {
+        if (a.y_tok) {
+          const int tk = live ? a.y_tok[p] : 0;
+          g = live ? a.y_gate[tk] : 0.0f;
+          drow = (size_t)tk;
+        }
+      }
+      uint32_t pk[4][2];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const uint32_t r0 = pack_bf16x2(o[q][0], o[q][1]), r1 = pack_bf16x2(o[q][2], o[q][3]);
+        if (!SWIGLU && a.y_tok) {  // the gate scales the rounded row (as the combine does)
+          pk[q][0] = pack_bf16x2(__builtin_fmaf(g, bf16lo(r0), 0.0f), __builtin_fmaf(g, bf16hi(r0), 0.0f));
+          pk[q][1] = pack_bf16x2(__builtin_fmaf(g, bf16lo(r1), 0.0f), __builtin_fmaf(g, bf16hi(r1), 0.0f));
+        } else {
+          pk[q][0] = r0;
+          pk[q][1] = r1;
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        // v_permlane32_swap: lanes 32-63 of the first operand trade places
+        // with lanes 0-31 of the second
+        const auto s0 = __builtin_amdgcn_permlane32_swap(pk[2 * u][0], pk[2 * u + 1][0], false, false);
+        const auto s1 = __builtin_amdgcn_permlane32_swap(pk[2 * u][1], pk[2 * u + 1][1], false, false);
+        const int n = nt * BNO + wn * WTN + j * 32 + 16 * u + 8 * lk;
+        if (!live || n >= N) continue;  // N is a multiple of 8
+        u32x4_t v = {s0[0], s1[0], s0[1], s1[1]};
+        *reinterpret_cast<u32x4_t*>(reinterpret_cast<bf16_t*>(a.C) + drow * N + n) = v;
       }
     }
   }
