@@ -23,15 +23,15 @@ __device__ __forceinline__ float bf16_to_f32(uint32_t h) {
 __device__ __forceinline__ float bf16lo(uint32_t p) { return __uint_as_float(p << 16); }
 __device__ __forceinline__ float bf16hi(uint32_t p) { return __uint_as_float(p & 0xffff0000u); }
 
-// fp32 -> bf16, round to nearest even (NaN kept quiet).
-__device__ __forceinline__ uint32_t f32_to_bf16(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0u;
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return u >> 16;
-}
+// Two fp32 values -> packed bf16 pair (lo in bits 0-15), round to nearest
+// even: one v_cvt_pk_bf16_f32.  For every finite or infinite input it gives
+// the bits of the integer rounding (u + 0x7fff + lsb) >> 16 (checked over all
+// 2^32 patterns on gfx950); a NaN stays a NaN.
+typedef __bf16 bf16x2_v __attribute__((ext_vector_type(2)));
+typedef float f32x2_v __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  return f32_to_bf16(lo) | (f32_to_bf16(hi) << 16);
+  const f32x2_v f = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2_v));
 }
 
 template <typename T>

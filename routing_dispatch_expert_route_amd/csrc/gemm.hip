@@ -256,7 +256,8 @@ __device__ __forceinline__ bool tile_index(const GemmArgs& a, int m_real, int& l
 // operand the activation tile (rows m), so the accumulator holds D[n][m]:
 // lane l of a 32x32 tile owns column m = l%32 and rows n = 8*(v/4) +
 // 4*(l/32) + v%4 -- four consecutive output columns of one token row per
-// group of four accumulator registers, written as one 8-byte store.
+// group of four accumulator registers (the epilogue pairs groups across
+// the two halves of the wave into 16-byte stores).
 //
 // Pipeline.  K advances in stages of BK (32 or 64) through two LDS rings,
 // NSX slots for the activation tile and NSW >= NSX for the weight tile
@@ -336,9 +337,12 @@ __device__ __forceinline__ void store_tile(const GemmArgs& a, const f32x16_t (&a
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
           if constexpr (SWIGLU) {
+            // SiLU(g) = g / (1 + e^-g) with the hardware reciprocal (about
+            // 1 ulp in fp32; an IEEE division costs ten VALU instructions
+            // per output, a third of the epilogue)
             const float gv = acc[0][j][i][4 * q + t];
             const float uv = acc[1][j][i][4 * q + t];
-            o[q][t] = __fdividef(gv, 1.0f + __expf(-gv)) * uv;
+            o[q][t] = gv * __builtin_amdgcn_rcpf(1.0f + __expf(-gv)) * uv;
           } else {
             o[q][t] = acc[0][j][i][4 * q + t];
           }
