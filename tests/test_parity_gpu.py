@@ -479,6 +479,13 @@ FUSED = {
                               bias="normal"),
     "k1_tail_split_drops": Workload("k1_tail_drops", T=18432, E=8, k=1, d=1024, d_ff=2048,
                                     renorm=0, phi=0.9),
+    # the 256x256 down tile over whole K (K = 1024, 16 stages: no split) in
+    # two rounds or more: its epilogue writes the gate-scaled token rows
+    # (with drops, the appended workgroups write the zero rows)
+    "k1_whole_k": Workload("k1_whole_k", T=16384, E=8, k=1, d=2048, d_ff=1024, renorm=0,
+                           bias="normal"),
+    "k1_whole_k_drops": Workload("k1_whole_k_drops", T=16384, E=8, k=1, d=2048, d_ff=1024,
+                                 renorm=0, phi=0.9),
 }
 
 
