@@ -264,9 +264,32 @@ def blas_reference(w, kept, steps, dev):
     rows = sum(act)
     f1 = 2.0 * rows * w.d * 2 * w.d_ff
     f2 = 2.0 * rows * w.d_ff * w.d
+
+    # The gate/up shapes again with nothing in between: the per-expert passes
+    # back to back, and one dense GEMM over all the rows (one weight matrix)
+    # back to back -- what the library sustains when the MFMA units stay busy
+    # for milliseconds, as the grouped GEMM 1 does.
+    def back_to_back(fn):
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+        fn()
+        torch.cuda.synchronize()
+        evs[0].record()
+        for i in range(steps):
+            fn()
+            evs[i + 1].record()
+        torch.cuda.synchronize()
+        return sorted(evs[i].elapsed_time(evs[i + 1]) for i in range(steps))[steps // 2]
+
+    t_seq = back_to_back(one_pass)
+    x_all = torch.cat(xs)
+    t_dense = back_to_back(lambda: F.linear(x_all, wgu[0]))
     return {"library": "torch.nn.functional.linear bf16 (hipBLASLt)", "experts": len(act),
             "rows": rows, "gate_up_ms": round(t1, 4), "gate_up_tflops": round(f1 / t1 / 1e9, 1),
-            "down_ms": round(t2, 4), "down_tflops": round(f2 / t2 / 1e9, 1)}
+            "down_ms": round(t2, 4), "down_tflops": round(f2 / t2 / 1e9, 1),
+            "gate_up_back_to_back_ms": round(t_seq, 4),
+            "gate_up_back_to_back_tflops": round(f1 / t_seq / 1e9, 1),
+            "gate_up_dense_ms": round(t_dense, 4),
+            "gate_up_dense_tflops": round(f1 / t_dense / 1e9, 1)}
 
 
 def main():
