@@ -923,11 +923,19 @@ __global__ __launch_bounds__(512, 1) void gemm_pp_kernel(GemmArgs a) {
   auto read_stage = [&](const u32x4_t* xs, const u32x4_t* wsl) __attribute__((always_inline)) {
     const char* xb = reinterpret_cast<const char*>(xs);
     const char* wb = reinterpret_cast<const char*>(wsl);
+    // With gathered rows (8 row offsets per lane live through the K loop)
+    // the fragment addresses are recomputed in every stage, a few VALU
+    // instructions, instead of being kept live: kept, they pushed 28
+    // registers per lane to scratch memory around the K loop (Granite
+    // T = 16384 GEMM 1 282 -> 267 us, shared64 286 -> 277 us).  On packed
+    // rows they fit, and recomputing them costs about 1 %.
+    int lr = lrow, lq = lk;
+    if constexpr (GATHER) asm volatile("" : "+v"(lr), "+v"(lq));
 #pragma unroll
     for (int kk = 0; kk < KS; ++kk) {
-      const int chunk = ((kk * 2 + lk) ^ swz<CH>(lrow)) * 16;
-      const int xo = (wm * WTM + lrow) * CH * 16 + chunk;
-      const int wo = (wn * WTN + lrow) * CH * 16 + chunk;
+      const int chunk = ((kk * 2 + lq) ^ swz<CH>(lr)) * 16;
+      const int xo = (wm * WTM + lr) * CH * 16 + chunk;
+      const int wo = (wn * WTN + lr) * CH * 16 + chunk;
 #pragma unroll
       for (int i = 0; i < TM; ++i)
         F[kk].bx[i] = *reinterpret_cast<const bf16x8_t*>(xb + xo + i * 32 * CH * 16);
