@@ -946,8 +946,9 @@ __global__ __launch_bounds__(512, 1) void gemm_pp_kernel(GemmArgs a) {
           F[kk].aw[g][j] = *reinterpret_cast<const bf16x8_t*>(wb + wo + (g * BNO + j * 32) * CH * 16);
     }
   };
-  // the stage's MFMAs from F, k steps in increasing order
-  auto compute = [&]() __attribute__((always_inline)) {
+  // the stage's MFMAs from F for the first NB of the wave's 32-row blocks,
+  // k steps in increasing order
+  auto compute_blocks = [&](auto NB) __attribute__((always_inline)) {
 #pragma unroll
     for (int kk = 0; kk < KS; ++kk)
 #pragma unroll
@@ -955,10 +956,19 @@ __global__ __launch_bounds__(512, 1) void gemm_pp_kernel(GemmArgs a) {
 #pragma unroll
         for (int j = 0; j < TN; ++j)
 #pragma unroll
-          for (int i = 0; i < TM; ++i)
+          for (int i = 0; i < decltype(NB)::value; ++i)
             acc[g][j][i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(F[kk].aw[g][j], F[kk].bx[i],
                                                                   acc[g][j][i], 0, 0, 0);
   };
+  // A 32-row block of the wave's 64 rows that holds no row of the tile (an
+  // expert with a handful of rows, or the end of its last row tile) is
+  // never stored, so its MFMAs are skipped: with at most 32 rows the busy
+  // waves run half of theirs and every compute phase is half as long.  The
+  // K loop is instantiated per block count, so each instance is straight
+  // line (a branch per MFMA group spills the accumulators).
+  static_assert(TM == 2, "two 32-row blocks per wave");
+  const int wrows = rows - wm * WTM;
+  const int nblk = wrows > 32 ? 2 : (wrows > 0 ? 1 : 0);
   constexpr int LB = NSX * NSW;  // slot combinations repeat every 6 stages
   const int nk = (klen + BK - 1) / BK;
   // prologue: activation stage 0 (group 0), weight stages 0 and 1 (group 1);
@@ -977,7 +987,7 @@ __global__ __launch_bounds__(512, 1) void gemm_pp_kernel(GemmArgs a) {
   constexpr int WAIT_ALL = 0x0070;                                  // vmcnt(0) lgkmcnt(0)
   constexpr int WAIT_NL = 0x0070 | (NL & 15) | ((NL >> 4) << 14);  // vmcnt(NL) lgkmcnt(0)
   // stage kt (slot index S = kt % LB): group 0's two phases, or group 1's
-  auto stage0 = [&](auto S, int kt) __attribute__((always_inline)) {
+  auto stage0 = [&](auto S, auto NB, int kt) __attribute__((always_inline)) {
     constexpr int s = decltype(S)::value;
     // phase 2kt: refill, read
     issue(xslot(std::integral_constant<int, s + 1>{}), kt + 1);
@@ -986,7 +996,7 @@ __global__ __launch_bounds__(512, 1) void gemm_pp_kernel(GemmArgs a) {
     __builtin_amdgcn_s_barrier();
     // phase 2kt+1: compute, then the refill must have landed
     __builtin_amdgcn_s_setprio(1);
-    compute();
+    compute_blocks(NB);
     __builtin_amdgcn_s_setprio(0);
     __builtin_amdgcn_s_waitcnt(WAIT_ALL);
     __builtin_amdgcn_s_barrier();
@@ -995,12 +1005,12 @@ __global__ __launch_bounds__(512, 1) void gemm_pp_kernel(GemmArgs a) {
   // last, partial row tile) its MFMAs would only fill rows that are never
   // stored, and skipping them shortens every other phase
   const bool act1 = rows > 128;
-  auto stage1 = [&](auto S, int kt) __attribute__((always_inline)) {
+  auto stage1 = [&](auto S, auto NB, int kt) __attribute__((always_inline)) {
     constexpr int s = decltype(S)::value;
     // phase 2kt: compute the previous stage
     if (kt > 0 && act1) {
       __builtin_amdgcn_s_setprio(1);
-      compute();
+      compute_blocks(NB);
       __builtin_amdgcn_s_setprio(0);
     }
     __builtin_amdgcn_s_barrier();
@@ -1010,27 +1020,31 @@ __global__ __launch_bounds__(512, 1) void gemm_pp_kernel(GemmArgs a) {
     __builtin_amdgcn_s_waitcnt(WAIT_NL);
     __builtin_amdgcn_s_barrier();
   };
-  auto run = [&](auto G) __attribute__((always_inline)) {
+  auto run = [&](auto G, auto NB) __attribute__((always_inline)) {
     int kt = 0;
     for (; kt + LB <= nk; kt += LB)
       static_for<0, LB>([&](auto S) __attribute__((always_inline)) {
-        if constexpr (decltype(G)::value == 0) stage0(S, kt + decltype(S)::value);
-        else stage1(S, kt + decltype(S)::value);
+        if constexpr (decltype(G)::value == 0) stage0(S, NB, kt + decltype(S)::value);
+        else stage1(S, NB, kt + decltype(S)::value);
       });
     const int rest = nk - kt;
     static_for<0, LB - 1>([&](auto S) __attribute__((always_inline)) {
       if (decltype(S)::value < rest) {
-        if constexpr (decltype(G)::value == 0) stage0(S, kt + decltype(S)::value);
-        else stage1(S, kt + decltype(S)::value);
+        if constexpr (decltype(G)::value == 0) stage0(S, NB, kt + decltype(S)::value);
+        else stage1(S, NB, kt + decltype(S)::value);
       }
     });
+    // group 1: the last stage (group 0 has left the loop; no barrier follows)
+    if constexpr (decltype(G)::value == 1)
+      if (act1) compute_blocks(NB);
   };
-  if (grp == 0) {
-    run(std::integral_constant<int, 0>{});
-  } else {
-    run(std::integral_constant<int, 1>{});
-    if (act1) compute();  // the last stage (group 0 has left the loop; no barrier follows)
-  }
+  auto run_blocks = [&](auto G) __attribute__((always_inline)) {
+    if (nblk == 2) run(G, std::integral_constant<int, 2>{});
+    else if (nblk == 1) run(G, std::integral_constant<int, 1>{});
+    else run(G, std::integral_constant<int, 0>{});
+  };
+  if (grp == 0) run_blocks(std::integral_constant<int, 0>{});
+  else run_blocks(std::integral_constant<int, 1>{});
   __builtin_amdgcn_s_waitcnt(0x0F70);  // the refills past the end have landed
   if (wm * WTM >= rows) return;
   if constexpr (!SWIGLU) {
