@@ -346,7 +346,8 @@ int moe_routing_stats(const moe_shape* s, const float* logits, const float* gate
  *   row_token   [E*Ce] int32: source token of every row
  *   x_packed    [E*Ce][d]: x_packed[r] = x[row_token[r]]
  * shape->k only sets C = ceil(phi*T*k/E).  Needs phi > 0 and renormalize = 0
- * (else MOE_ERR_INVALID_ARG) and T <= 32768 (else MOE_ERR_UNSUPPORTED).
+ * (else MOE_ERR_INVALID_ARG) and E*T < 2^29 (the [E][T] key and route
+ * tables below 2 GiB; else MOE_ERR_UNSUPPORTED).
  * Uses the workspace of moe_workspace_bytes. */
 int moe_permute_expert_choice(const moe_shape* s, const void* x, const float* logits,
                               float* scores, int32_t* route_pos, int32_t* offsets,

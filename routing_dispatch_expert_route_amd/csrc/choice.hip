@@ -27,6 +27,8 @@
 //                   increasing index; the route table is written
 //                   expert-major [E][T] (coalesced).  No atomics: the result
 //                   is unique.
+// ec_select_long_kernel  the same choice for columns beyond the registers
+//                   (T > 32768): radix passes over the column in memory.
 // ec_transpose_kernel  the [T][E] route table for callers that ask for it.
 #include "common.h"
 #include "launch.h"
@@ -234,6 +236,115 @@ __global__ __launch_bounds__(NT) void ec_select_kernel(const uint32_t* __restric
   }
 }
 
+// Columns longer than the register-resident kernel holds (T > 32768): one
+// block of NT threads per expert, the column read from memory in every pass.
+// The Ce-th largest key comes from four radix passes of 8 bits (largest
+// digit first): each pass counts, in an LDS histogram, the digit of the keys
+// that match the digits chosen so far (integer atomics: exact counts), and
+// one wave picks the digit where the count of keys at or above it reaches
+// the keys still needed.  Seating gives each wave a contiguous range of
+// tokens: one pass counts every wave's keys above and equal to thr, one
+// barrier, and a second pass walks each range 64 tokens at a time with
+// running counts (ballots), so rows follow token order as in
+// ec_select_kernel and the result is the same.
+template <int NT>
+__global__ __launch_bounds__(NT) void ec_select_long_kernel(const uint32_t* __restrict__ keys,
+                                                            int T, int E, int Ce,
+                                                            int32_t* __restrict__ pos_et,
+                                                            int32_t* __restrict__ row_token,
+                                                            int32_t* __restrict__ offsets) {
+  constexpr int NW = NT / 64;
+  __shared__ uint32_t s_h[256];
+  __shared__ int s_sel[2];
+  __shared__ uint32_t s_tot[NW][2];
+  const int e = blockIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const uint32_t* col = keys + (size_t)e * T;
+  uint32_t prefix = 0, pmask = 0;
+  int need = Ce;  // keys still to take among those matching prefix under pmask
+  for (int shift = 24; shift >= 0; shift -= 8) {
+    for (int i = tid; i < 256; i += NT) s_h[i] = 0u;
+    __syncthreads();
+    for (int t = tid; t < T; t += NT) {
+      const uint32_t k = col[t];
+      if ((k & pmask) == prefix) atomicAdd(&s_h[(k >> shift) & 255u], 1u);
+    }
+    __syncthreads();
+    if (wid == 0) {
+      // lane l holds digits 4l .. 4l+3; above = keys with a digit past them
+      uint32_t b[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) b[q] = s_h[4 * lane + q];
+      const uint32_t lsum = b[0] + b[1] + b[2] + b[3];
+      uint32_t sfx = lsum;  // sum over lanes >= this one
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const uint32_t v = __shfl_down(sfx, o, 64);
+        if (lane + o < 64) sfx += v;
+      }
+      uint32_t ge = sfx - lsum;  // count of keys with a digit above 4l+3
+      // the digit d with count(>= d) >= need and (d = 255 or count(> d) <
+      // need): unique, since count(>= d) grows as d falls
+#pragma unroll
+      for (int q = 3; q >= 0; --q) {
+        const uint32_t gt = ge;
+        ge += b[q];
+        const int d = 4 * lane + q;
+        if ((int)ge >= need && (d == 255 || (int)gt < need)) {
+          s_sel[0] = d;
+          s_sel[1] = need - (int)gt;
+        }
+      }
+    }
+    __syncthreads();
+    prefix |= (uint32_t)s_sel[0] << shift;
+    pmask |= 255u << shift;
+    need = s_sel[1];
+  }
+  const uint32_t thr = prefix;  // the Ce-th largest key (Ce > 0)
+  // need = keys equal to thr to seat, in token order
+  const int per = ((T + NW - 1) / NW + 63) / 64 * 64;
+  const int w0 = min(T, wid * per), w1 = min(T, w0 + per);
+  uint32_t cgt = 0, ceq = 0;
+  for (int t0 = w0; t0 < w1; t0 += 64) {
+    const int t = t0 + lane;
+    const bool valid = t < w1;
+    const uint32_t k = valid ? col[t] : 0u;
+    cgt += (uint32_t)__popcll(__ballot(valid && k > thr));
+    ceq += (uint32_t)__popcll(__ballot(valid && k == thr));
+  }
+  if (lane == 0) {
+    s_tot[wid][0] = cgt;
+    s_tot[wid][1] = ceq;
+  }
+  __syncthreads();
+  int bgt = 0, beq = 0;  // keys above / equal to thr before this wave's range
+  for (int w = 0; w < wid; ++w) {
+    bgt += (int)s_tot[w][0];
+    beq += (int)s_tot[w][1];
+  }
+  const uint64_t below = (1ull << lane) - 1ull;
+  for (int t0 = w0; t0 < w1; t0 += 64) {
+    const int t = t0 + lane;
+    const bool valid = t < w1;
+    const uint32_t k = valid ? col[t] : 0u;
+    const bool gt = valid && k > thr, eq = valid && k == thr;
+    const uint64_t mg = __ballot(gt), me = __ballot(eq);
+    const int gb = bgt + __popcll(mg & below);
+    const int eb = beq + __popcll(me & below);
+    const int pos = gb + min(eb, need);
+    const bool sel = (gt || (eq && eb < need)) && pos < Ce;
+    if (valid) pos_et[(size_t)e * T + t] = sel ? e * Ce + pos : -1;
+    if (sel) row_token[e * Ce + pos] = t;
+    bgt += __popcll(mg);
+    beq += __popcll(me);
+  }
+  if (tid == 0) {
+    offsets[e] = e * Ce;
+    if (e == E - 1) offsets[E] = E * Ce;
+  }
+}
+
 // route_pos[t][e] = pos_et[e][t], through a tile of kTrTok tokens in LDS
 // (E * (kTrTok + 1) ints: 33 KiB at E = 256).
 constexpr int kTrTok = 32;
@@ -277,7 +388,9 @@ hipError_t launch_expert_choice(const float* logits, int T, int E, int Ce, float
   else if (T <= 8192) SEL(1024, 8);
   else if (T <= 16384) SEL(1024, 16);
   else if (T <= 32768) SEL(1024, 32);
-  else return hipErrorInvalidValue;
+  else
+    hipLaunchKernelGGL((ec_select_long_kernel<1024>), dim3(E), dim3(1024), 0, st, keys, T, E, Ce,
+                       pos_et, row_token, offsets);
 #undef SEL
   hipError_t err = hipGetLastError();
   if (err != hipSuccess || !route_pos || T == 0) return err;

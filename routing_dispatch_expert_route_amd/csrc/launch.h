@@ -70,8 +70,8 @@ hipError_t launch_padded(const void* x, const int32_t* ids, const int32_t* route
 // Expert-choice routing from router logits [T][E]: scores [T][E] (softmax;
 // may be null), keys [E][T] (the scores' bits, expert-major), pos_et [E][T]
 // (row e*Ce + i or -1), route_pos [T][E] (the same table token-major; may be
-// null), row_token [E*Ce] and offsets[e] = e*Ce.  Needs T <= 32768 and
-// 1 <= Ce <= T (Ce = 0 when T = 0).
+// null), row_token [E*Ce] and offsets[e] = e*Ce.  Needs 1 <= Ce <= T (Ce =
+// 0 when T = 0) and E*T < 2^29.
 hipError_t launch_expert_choice(const float* logits, int T, int E, int Ce, float* scores,
                                 uint32_t* keys, int32_t* pos_et, int32_t* route_pos,
                                 int32_t* row_token, int32_t* offsets, hipStream_t st);

@@ -21,7 +21,6 @@ namespace {
 constexpr int64_t kMaxE = 256;
 constexpr int64_t kMaxK = 8;
 constexpr int64_t kMaxRerouteE = 64;  // the reroute walk keeps one expert per lane
-constexpr int64_t kMaxChoiceT = 32768;  // expert choice keeps a column in registers
 constexpr size_t kAlign = 256;
 
 size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
@@ -135,10 +134,11 @@ int64_t ce_of(const moe_shape* s) {
 // Expert choice needs a capacity (its rows are the fixed E*Ce; their extent
 // is bounded like the fixed-shape buffer's), full softmax gates (a token's
 // number of experts is not fixed, so there is no set to renormalise over)
-// and T within the register-resident selection.
+// and its expert-major key and route tables ([E][T], 4 bytes each) below
+// 2^31 bytes.
 int validate_choice(const moe_shape* s) {
   if (!(s->phi > 0.0) || s->renormalize != 0) return MOE_ERR_INVALID_ARG;
-  if (s->T > kMaxChoiceT) return MOE_ERR_UNSUPPORTED;
+  if (s->E * s->T >= (int64_t(1) << 29)) return MOE_ERR_UNSUPPORTED;
   const int64_t eb = elem_bytes(s);
   const int64_t wide = s->d > s->d_ff ? s->d : s->d_ff;
   if (s->E * ce_of(s) * wide * eb >= (int64_t(1) << 31)) return MOE_ERR_UNSUPPORTED;

@@ -243,8 +243,8 @@ def test_expert_choice_rejected_before_launch():
     assert both(moe.shape(16, 64, 4, 2, 64, renorm=0)) == (moe.MOE_ERR_INVALID_ARG,) * 2
     # renormalised gates: a token's set of experts is not fixed
     assert both(moe.shape(16, 64, 4, 2, 64, renorm=1, phi=1.0)) == (moe.MOE_ERR_INVALID_ARG,) * 2
-    # beyond the register-resident selection
-    assert both(moe.shape(32769, 64, 4, 1, 64, renorm=0, phi=1.0)) == \
+    # the [E][T] key and route tables would reach 2 GiB (the expert rows stay small)
+    assert both(moe.shape(1 << 23, 8, 64, 1, 8, renorm=0, phi=1.0)) == \
         (moe.MOE_ERR_UNSUPPORTED,) * 2
     # the timed variant knows layouts 0..3 only
     s = moe.shape(16, 64, 4, 2, 64, renorm=0, phi=1.0)
