@@ -1298,12 +1298,13 @@ static hipError_t run_cfg(const GemmPlan& pl, GemmArgs a, hipStream_t st) {
       if constexpr (SWIGLU) return run_bf16<128, 128, 2, 2, 64, 2, 3, 2, SWIGLU, PARTIAL>(pl, a, st);
       else return hipErrorInvalidValue;  // gate/up only
     default:
-      // a long K loop per tile wants the deeper ring; short ones two
-      // workgroups per CU
+      // two workgroups per CU with two-slot rings; the down projection's K
+      // splits make about two per CU, so at decode every split runs in one
+      // round (Mixtral decode down GEMM 164.7 -> 160.4 us against one
+      // workgroup per CU with three-slot rings, same box)
       if constexpr (!SWIGLU) {
         if (down_narrow(a.N, a.K)) return run_bf16<64, 128, 1, 4, 64, 2, 3, 2, SWIGLU, PARTIAL>(pl, a, st);
       }
-      if (!SWIGLU && a.k_chunk >= 2048) return run_bf16<64, 256, 1, 4, 64, 3, 3, 1, SWIGLU, PARTIAL>(pl, a, st);
       return run_bf16<64, 256, 1, 4, 64, 2, 2, 2, SWIGLU, PARTIAL>(pl, a, st);
   }
 }
