@@ -273,13 +273,14 @@ int moe_layer_forward_padded(const moe_shape* s, const void* x, const void* w_ro
  *   [T][k] packed row (an expert's kept routes first, then its rerouted
  *   ones, each in arrival order), -1 if dropped; row_token [R_max];
  *   x_packed [R_max][d] as in moe_permute.
- * E <= 64 (else MOE_ERR_UNSUPPORTED); expert_ids must lie in [0, E), as
- * moe_route writes them.  The dropped routes are placed by parallel rounds
- * (deferred acceptance under token-order priority, which ends in the same
- * assignment as the arrival-order greedy) while the per-expert token bitmaps
- * fit 144 KiB of LDS (T <= 65535 at E <= 16, T <= 35744 at E = 32,
- * T <= 18144 at E = 64), else by one wave walking them in arrival order.
- * The workspace of moe_workspace_bytes covers either. */
+ * expert_ids must lie in [0, E), as moe_route writes them.  Up to 64
+ * experts the dropped routes are placed by parallel rounds (deferred
+ * acceptance under token-order priority, which ends in the same assignment
+ * as the arrival-order greedy) while the per-expert token bitmaps fit 144
+ * KiB of LDS (T <= 65535 at E <= 16, T <= 35744 at E = 32, T <= 18144 at
+ * E = 64), else by one wave walking them in arrival order; beyond 64
+ * experts always by the walk (four experts per lane).  The workspace of
+ * moe_workspace_bytes covers each. */
 int moe_permute_reroute(const moe_shape* s, const void* x, const float* logits,
                         const int32_t* expert_ids, int32_t* expert_ids_out, int32_t* counts,
                         int32_t* filled, int32_t* offsets, int32_t* route_pos,
@@ -289,7 +290,7 @@ int moe_permute_reroute(const moe_shape* s, const void* x, const float* logits,
 /* moe_layer_forward with the reroute overflow policy (moe_permute_reroute
  * in place of moe_permute).  expert_ids receives the experts after
  * rerouting, counts the demand of the router's choices, route_pos the
- * rerouted packed rows.  E <= 64. */
+ * rerouted packed rows. */
 int moe_layer_forward_reroute(const moe_shape* s, const void* x, const void* w_router,
                               const float* b_router, const void* w_gate, const void* w_up,
                               const void* w_down, const void* ws_gate, const void* ws_up,

@@ -20,7 +20,6 @@ namespace {
 
 constexpr int64_t kMaxE = 256;
 constexpr int64_t kMaxK = 8;
-constexpr int64_t kMaxRerouteE = 64;  // the reroute walk keeps one expert per lane
 constexpr size_t kAlign = 256;
 
 size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
@@ -228,7 +227,9 @@ Layout layout_of(const moe_shape* s, int64_t Q = -1) {
   L.slot = take(Ro * sizeof(int32_t));
   L.offs2 = take((size_t)(s->E + 1) * sizeof(int32_t));
   L.rpos0 = take(Ro * sizeof(int32_t));
-  L.pref = take(Ro * 64);  // preference lists of the dropped routes (E <= 64)
+  // preference ranks of the dropped routes: a 64-byte row per route up to
+  // 64 experts, a 256-byte row for the wide walk beyond
+  L.pref = take(Ro * (s->E > 64 ? 256 : 64));
   // per-token state of the parallel reroute where it does not fit LDS
   L.dast = take(queued || s->E > 64 ? 0 : (size_t)moe::reroute_state_bytes((int)s->T, (int)s->E));
   // expert choice: expert-major keys (score bits) and route table, row groups
@@ -412,7 +413,6 @@ int moe_permute_reroute(const moe_shape* s, const void* x, const float* logits,
                         hipStream_t stream) {
   int v = validate(s);
   if (v != MOE_OK) return v;
-  if (s->E > kMaxRerouteE) return MOE_ERR_UNSUPPORTED;
   const bool tok = s->T > 0;
   if (!counts || !filled || !offsets ||
       (tok && (!x || !logits || !expert_ids || !expert_ids_out || !route_pos || !row_token ||
@@ -622,7 +622,6 @@ static int layer_forward_impl(const moe_shape* s, const void* x, const void* w_r
   int v = validate(s);
   if (v != MOE_OK) return v;
   if (padded && (v = validate_padded(s)) != MOE_OK) return v;
-  if (reroute && s->E > kMaxRerouteE) return MOE_ERR_UNSUPPORTED;
   if (choice && (v = validate_choice(s)) != MOE_OK) return v;
   if (!w_router || !w_gate || !w_up || !w_down || (s->T > 0 && (!x || !y)))
     return MOE_ERR_INVALID_ARG;

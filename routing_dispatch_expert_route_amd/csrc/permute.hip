@@ -451,14 +451,15 @@ constexpr int kRerouteMaxE = 64;
 // ahead: larger logit, or equal logit and lower index), one thread per
 // (r, e), stored as rank[r][e] (the walk) or inverted, order[r][rank] = e
 // (ORDER: the parallel rounds read the experts in preference order).
-template <bool ORDER>
+// RS: bytes per route (64, or 256 for the wide walk).
+template <bool ORDER, int RS>
 __global__ __launch_bounds__(256) void reroute_rank_kernel(const float* __restrict__ logits,
                                                            const int32_t* __restrict__ route_pos0,
                                                            const int32_t* __restrict__ offsets0,
                                                            int R, int k, int E, int C,
                                                            uint8_t* __restrict__ rank) {
   const long g = (long)blockIdx.x * blockDim.x + threadIdx.x;
-  const int r = (int)(g / kRerouteMaxE), e = (int)(g % kRerouteMaxE);
+  const int r = (int)(g / RS), e = (int)(g % RS);
   if (r >= R || e >= E || route_pos0[r] >= 0) return;
   if (ORDER && offsets0[E] >= (long)E * C) return;  // every seat taken: nothing moves
   const float* l = logits + (size_t)(r / k) * E;
@@ -469,9 +470,9 @@ __global__ __launch_bounds__(256) void reroute_rank_kernel(const float* __restri
     rk += (l2 > le) | ((l2 == le) & (e2 < e));
   }
   if (ORDER)
-    rank[(size_t)r * kRerouteMaxE + rk] = (uint8_t)e;
+    rank[(size_t)r * RS + rk] = (uint8_t)e;
   else
-    rank[(size_t)r * kRerouteMaxE + e] = (uint8_t)rk;
+    rank[(size_t)r * RS + e] = (uint8_t)rk;
 }
 
 __global__ __launch_bounds__(64) void reroute_kernel(
@@ -573,6 +574,128 @@ __global__ __launch_bounds__(64) void reroute_kernel(
   const int incl = wave_incl_scan(f, lane);
   if (lane == 0) offsets[0] = 0;
   if (lane < E) offsets[lane + 1] = incl;
+}
+
+// The walk for 64 < E <= 256: lane l keeps the seat counts of experts l,
+// l + 64, l + 128 and l + 192, and a dropped route takes the smallest
+// (rank, expert) key among the experts with room that its token does not
+// hold -- a wave minimum in place of reroute_kernel's ballots over one
+// expert per lane.  Ranks are distinct, so the key names one expert: the
+// same choice as the walk above, one route at a time in arrival order.
+constexpr int kRerouteWideE = 256;
+__global__ __launch_bounds__(64) void reroute_wide_kernel(
+    const uint8_t* __restrict__ rank, const int32_t* __restrict__ ids_in,
+    const int32_t* __restrict__ route_pos0, const int32_t* __restrict__ offsets0,
+    const int32_t* __restrict__ kept, int T, int k, int E, int C, int32_t* __restrict__ ids_out,
+    int32_t* __restrict__ slot, int32_t* __restrict__ offsets) {
+  constexpr int G = kRerouteWideE / kWave;  // experts per lane
+  constexpr int NW = kRerouteWideE / 16;    // 16-byte words of a rank row
+  __shared__ __attribute__((aligned(16))) uint8_t s_rank[kWave][kRerouteWideE];
+  const int lane = threadIdx.x;
+  const int R = T * k;
+  int fill[G];  // seats used at expert lane + 64 * g
+#pragma unroll
+  for (int g = 0; g < G; ++g) fill[g] = lane + kWave * g < E ? kept[lane + kWave * g] : 0;
+  int cur_t = -1;
+  int cur_e[8];  // final experts of token cur_t's slots (wave-uniform)
+#pragma unroll
+  for (int jj = 0; jj < 8; ++jj) cur_e[jj] = -1;
+  int p0, e0, tid[8];
+  uint4 rw[NW];
+  auto load = [&](int base) {
+    const int rr = base + lane;
+    p0 = rr < R ? route_pos0[rr] : 0;
+    e0 = rr < R ? ids_in[rr] : 0;
+    const bool drop = rr < R && p0 < 0;
+    const uint4* src = reinterpret_cast<const uint4*>(rank + (size_t)(drop ? rr : 0) * kRerouteWideE);
+#pragma unroll
+    for (int w = 0; w < NW; ++w) rw[w] = (drop && 16 * w < E) ? src[w] : uint4{0u, 0u, 0u, 0u};
+    const int t = drop ? rr / k : 0;
+#pragma unroll
+    for (int jj = 0; jj < 8; ++jj) tid[jj] = (drop && jj < k) ? ids_in[t * k + jj] : 0;
+  };
+  load(0);
+  for (int base = 0; base < R; base += kWave) {
+    const int cp0 = p0, ce0 = e0;
+    int ctid[8];
+#pragma unroll
+    for (int jj = 0; jj < 8; ++jj) ctid[jj] = tid[jj];
+    __syncthreads();  // the previous chunk's rank rows are no longer read
+#pragma unroll
+    for (int w = 0; w < NW; ++w) *reinterpret_cast<uint4*>(&s_rank[lane][16 * w]) = rw[w];
+    __syncthreads();
+    if (base + kWave < R) load(base + kWave);  // in flight during this chunk's walk
+    const int rr = base + lane;
+    if (rr < R && cp0 >= 0) {  // kept by the drop policy: same expert, same seat
+      ids_out[rr] = ce0;
+      slot[rr] = cp0 - offsets0[ce0];
+    }
+    uint64_t m = __ballot(rr < R && cp0 < 0);
+    while (m) {
+      const int b = __builtin_amdgcn_readfirstlane(__builtin_ctzll(m));
+      m &= m - 1;
+      const int r = base + b;
+      const int t = r / k, j = r - t * k;
+      if (t != cur_t) {
+        cur_t = t;
+#pragma unroll
+        for (int jj = 0; jj < 8; ++jj)
+          cur_e[jj] = jj < k ? __builtin_amdgcn_readlane(ctid[jj], b) : -1;
+      }
+      uint32_t key = 0xffffffffu;
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+        const int e = lane + kWave * g;
+        bool ok = e < E && fill[g] < C;
+#pragma unroll
+        for (int jj = 0; jj < 8; ++jj) ok = ok && !(jj != j && cur_e[jj] == e);
+        const uint32_t kk = ((uint32_t)s_rank[b][e] << 8) | (uint32_t)e;
+        if (ok && kk < key) key = kk;
+      }
+#pragma unroll
+      for (int o = kWave / 2; o >= 1; o >>= 1) {
+        const uint32_t other = (uint32_t)__shfl_xor((int)key, o, kWave);
+        key = other < key ? other : key;
+      }
+      key = (uint32_t)__builtin_amdgcn_readfirstlane((int)key);
+      if (key != 0xffffffffu) {
+        const int best = (int)(key & 255u);
+        const int owner = best % kWave, gb = best / kWave;
+        int mine = fill[0];
+#pragma unroll
+        for (int g = 1; g < G; ++g) mine = g == gb ? fill[g] : mine;
+        const int seat = __builtin_amdgcn_readlane(mine, owner);
+        if (lane == owner) {
+#pragma unroll
+          for (int g = 0; g < G; ++g)
+            if (g == gb) fill[g] = seat + 1;
+        }
+        if (lane == 0) {
+          slot[r] = seat;
+          ids_out[r] = best;
+        }
+#pragma unroll
+        for (int jj = 0; jj < 8; ++jj)
+          if (jj == j) cur_e[jj] = best;
+      } else {  // no expert with room: dropped after all (lane b's own expert)
+        const int orig = __builtin_amdgcn_readlane(ce0, b);
+        if (lane == 0) {
+          ids_out[r] = orig;
+          slot[r] = -1;
+        }
+      }
+    }
+  }
+  int carry = 0;
+  if (lane == 0) offsets[0] = 0;
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    const int e = lane + kWave * g;
+    const int f = e < E ? fill[g] : 0;
+    const int incl = wave_incl_scan(f, lane);
+    if (e < E) offsets[e + 1] = carry + incl;
+    carry += __shfl(incl, kWave - 1, kWave);
+  }
 }
 
 // Packed rows of the rerouted dispatch: route_pos[r] = offsets[ids[r]] +
@@ -1004,16 +1127,33 @@ hipError_t launch_reroute(const float* logits, const int32_t* ids_in, const int3
                           int32_t* route_pos, int32_t* row_token, uint8_t* pref,
                           uint8_t* da_state, hipStream_t st) {
   const int R = T * k;
+  if (E > kRerouteMaxE) {  // beyond one expert per lane: the wide walk
+    if (R > 0) {
+      const long threads = (long)R * kRerouteWideE;
+      hipLaunchKernelGGL((reroute_rank_kernel<false, kRerouteWideE>),
+                         dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, st, logits,
+                         route_pos0, offsets0, R, k, E, C, pref);
+      hipError_t err = hipGetLastError();
+      if (err != hipSuccess) return err;
+    }
+    hipLaunchKernelGGL(reroute_wide_kernel, dim3(1), dim3(kWave), 0, st, pref, ids_in, route_pos0,
+                       offsets0, kept, T, k, E, C, ids_out, slot, offsets);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess || R == 0) return err;
+    hipLaunchKernelGGL(reroute_rows_kernel, dim3(ceil_div(R, 256)), dim3(256), 0, st, ids_out,
+                       slot, offsets, R, k, route_pos, row_token);
+    return hipGetLastError();
+  }
   const RerouteKind kind = reroute_kind(T, E);
   if (R > 0) {
     const long threads = (long)R * kRerouteMaxE;
     const dim3 grid((unsigned)((threads + 255) / 256));
     if (kind == RerouteKind::kWalk)
-      hipLaunchKernelGGL(reroute_rank_kernel<false>, grid, dim3(256), 0, st, logits, route_pos0,
-                         offsets0, R, k, E, C, pref);
+      hipLaunchKernelGGL((reroute_rank_kernel<false, kRerouteMaxE>), grid, dim3(256), 0, st,
+                         logits, route_pos0, offsets0, R, k, E, C, pref);
     else
-      hipLaunchKernelGGL(reroute_rank_kernel<true>, grid, dim3(256), 0, st, logits, route_pos0,
-                         offsets0, R, k, E, C, pref);
+      hipLaunchKernelGGL((reroute_rank_kernel<true, kRerouteMaxE>), grid, dim3(256), 0, st, logits,
+                         route_pos0, offsets0, R, k, E, C, pref);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
   }

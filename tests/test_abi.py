@@ -211,13 +211,16 @@ def test_padded_entry_points_need_a_capacity():
     assert moe.workspace_bytes(sc) >= moe.workspace_bytes(s)
 
 
-def test_reroute_needs_at_most_64_experts():
+def test_reroute_expert_limit_is_the_library_one():
+    """Reroute runs for every E the library takes (up to 256 experts; beyond
+    64 the walk with four experts per lane) and rejects E = 257 before any
+    launch, like every entry point."""
     moe = _moe()
-    s = moe.shape(16, 64, 65, 2, 64, phi=1.0)
-    by = ctypes.byref(s)
     L = moe._lib
     fake, ws = 4096, 1 << 20
-    need = moe.workspace_bytes(s)
+    s = moe.shape(16, 64, 257, 2, 64, phi=1.0)
+    by = ctypes.byref(s)
+    need = 1 << 20
     assert L.moe_permute_reroute(by, fake, fake, fake, fake, fake, fake, fake, fake, fake, fake,
                                  ws, need, None) == moe.MOE_ERR_UNSUPPORTED
     assert L.moe_layer_forward_reroute(by, fake, fake, None, fake, fake, fake, None, None, None,

@@ -86,6 +86,8 @@ CASES = {
     # few rows, long d_ff: the down projection splits K into fp32 planes
     "bf16_split": Workload("bf16_split", T=16, E=8, k=2, d=256, d_ff=2048, phi=1.0),
     "f32": Workload("f32", T=77, E=5, k=3, d=40, d_ff=24, dtype="f32", phi=0.8, bias="normal"),
+    # beyond 64 experts (the reroute's wide walk, 256-byte rank rows)
+    "bf16_e160": Workload("bf16_e160", T=400, E=160, k=4, d=64, d_ff=32, phi=0.8, bias="zipf"),
 }
 
 

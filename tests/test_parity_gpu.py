@@ -123,6 +123,16 @@ def test_route_r64_hand_sums(moe, case, dtype):
                          want_logits=True)
     torch.cuda.synchronize()
     assert float(_np(L3)[5, 1]) == want
+    if dtype == "bf16":
+        # among 8192 tokens x 3 experts (a full-size launch: 2048 waves of 4
+        # tokens each): token 5000, expert 1 carries the case
+        xt = torch.zeros(8192, d, dtype=x.dtype)
+        xt[5000] = x[0]
+        sL = moe.shape(8192, d, 3, 1, 8, dtype=dtype, renorm=1)
+        _, _, LL = moe.route(sL, xt.cuda(), wt.cuda(), None if bt is None else bt.cuda(),
+                             want_logits=True)
+        torch.cuda.synchronize()
+        assert float(_np(LL)[5000, 1]) == want
 
 
 def test_route_ties_take_lowest_index(moe):

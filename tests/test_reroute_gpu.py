@@ -55,6 +55,13 @@ CASES = {
                                  bias="normal"),
     "k2_e64_walk": Workload("k2_walk", T=20000, E=64, k=2, d=64, d_ff=32, phi=0.8,
                             bias="normal"),
+    # beyond 64 experts: the walk with four experts per lane
+    "e128_k8_zipf_wide": Workload("e128_k8", T=600, E=128, k=8, d=64, d_ff=32, phi=0.9,
+                                  bias="zipf"),
+    "e256_k2_wide": Workload("e256_k2", T=3000, E=256, k=2, d=64, d_ff=32, phi=0.7,
+                             bias="normal"),
+    "e65_k1_wide": Workload("e65_k1", T=900, E=65, k=1, d=64, d_ff=32, renorm=0, phi=0.6,
+                            bias="zipf"),
 }
 
 
@@ -118,14 +125,14 @@ def test_layer_forward_reroute_parity(moe, name):
 @pytest.mark.parametrize("T,E,k,phi", [(2048, 16, 1, 0.5), (700, 64, 1, 0.4), (8000, 8, 1, 0.5),
                                        (1024, 16, 4, 0.5), (600, 64, 8, 0.3),
                                        (16384, 40, 8, 0.5), (13000, 64, 1, 0.5),
-                                       (20000, 64, 1, 0.5)])
+                                       (20000, 64, 1, 0.5), (1500, 200, 4, 0.5)])
 def test_permute_reroute_common_order(moe, T, E, k, phi):
     """Every token has the same preference order (identical rows of x), so the
     dropped routes fill the experts one after another in that order: the
     longest chain of rejections the parallel kernel can meet (about one round
     per expert), with its per-token state in LDS or (T = 8000, 16384, 13000)
     in the workspace, and, at T = 20000 over 64 experts, the same inputs
-    through the walk."""
+    through the walk; over 200 experts, the wide walk."""
     w = Workload("common_order", T=T, E=E, k=k, d=64, d_ff=32, renorm=0, phi=phi, bias="zipf")
     inp = make_inputs(w, seed=5)
     inp["x"] = inp["x"][:1].repeat(T, 1).contiguous()
@@ -147,14 +154,16 @@ def test_permute_reroute_common_order(moe, T, E, k, phi):
 
 @pytest.mark.parametrize("T,E,k,phi", [(300, 8, 1, 1.0), (500, 16, 2, 1.0), (400, 32, 8, 1.0),
                                        (8000, 8, 1, 1.25), (3000, 64, 2, 1.0),
-                                       (20000, 64, 2, 1.0)])
+                                       (20000, 64, 2, 1.0), (2000, 128, 4, 1.0),
+                                       (1000, 256, 8, 1.0)])
 def test_permute_reroute_exact_ties(moe, T, E, k, phi):
     """Integer-valued x and router rows in {-1, 0, 1} (and a bias of 3 on
     the first quarter of the experts, so they overflow) give integer logits,
     so many of a dropped route's free experts tie exactly: the reroute must
     take the lowest index among them ("Session 19", "Overflow policies", with
     the router's tie rule), on every reroute kernel (state in LDS, in the
-    workspace at T = 8000, and the walk at T = 20000 over 64 experts)."""
+    workspace at T = 8000, the walk at T = 20000 over 64 experts, and the
+    wide walk over 128 and 256 experts)."""
     say(f"[permute reroute ties] T={T} E={E} k={k} phi={phi}")
     w = Workload("reroute_ties", T=T, E=E, k=k, d=64, d_ff=16, phi=phi)
     g = torch.Generator().manual_seed(T + E + k)
