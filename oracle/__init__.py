@@ -19,7 +19,9 @@ import os
 import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+# MOE_ORACLE_LIB names another build of oracle.c (the mutation check of the
+# pins loads deliberately broken copies through it)
+_LIB_PATH = os.environ.get("MOE_ORACLE_LIB") or os.path.join(_HERE, "liboracle.so")
 _lib = None
 
 F32, BF16, F64 = 0, 1, 2
