@@ -118,6 +118,60 @@ __global__ __launch_bounds__(256) void combine_kernel(const void* __restrict__ y
   store_out<BF16>(y, (size_t)t * d + col, acc);
 }
 
+// The same sum for direct rows and k <= KS slots (KS = 2, 4 or 8): a wave
+// holds one token, so its route positions are wave-uniform and the KS rows
+// load without a branch -- a dropped slot loads the token's first kept row
+// and adds nothing -- all in flight before the first sum, which keeps slot
+// order (the kernel above issues one row at a time behind its branches).
+template <bool BF16, int KS>
+__global__ __launch_bounds__(256) void combine_rows_kernel(const void* __restrict__ yp,
+                                                           const int32_t* __restrict__ route_pos,
+                                                           const float* __restrict__ gates,
+                                                           const void* __restrict__ ysh, int T,
+                                                           int k, int d, void* __restrict__ y) {
+  constexpr int G = BF16 ? 8 : 4;  // output elements per 16-byte chunk
+  const int lane = threadIdx.x & 63;
+  const int t = blockIdx.x * (blockDim.x / 64) + (threadIdx.x >> 6);
+  const int col = (blockIdx.y * 64 + lane) * G;
+  if (t >= T || col >= d) return;
+  int pos[KS];
+  float g[KS];
+#pragma unroll
+  for (int j = 0; j < KS; ++j) {  // all of the token's slots in flight together
+    const size_t at = (size_t)t * k + (j < k ? j : 0);
+    pos[j] = route_pos[at];
+    g[j] = gates[at];
+  }
+  int any = -1;
+#pragma unroll
+  for (int j = 0; j < KS; ++j) {
+    pos[j] = j < k ? __builtin_amdgcn_readfirstlane(pos[j]) : -1;
+    if (any < 0 && pos[j] >= 0) any = pos[j];
+  }
+  float acc[G];
+#pragma unroll
+  for (int q = 0; q < G; ++q) acc[q] = 0.0f;
+  if (any >= 0) {
+    float v[KS][G];
+#pragma unroll
+    for (int j = 0; j < KS; ++j)
+      load_row<BF16, false, G>(yp, 1, 0, (size_t)(pos[j] >= 0 ? pos[j] : any), d, col, v[j]);
+#pragma unroll
+    for (int j = 0; j < KS; ++j) {
+      if (pos[j] < 0) continue;
+#pragma unroll
+      for (int q = 0; q < G; ++q) acc[q] = __builtin_fmaf(g[j], v[j][q], acc[q]);
+    }
+  }
+  if (ysh) {
+    float v[G];
+    load_row<BF16, false, G>(ysh, 1, 0, (size_t)t, d, col, v);
+#pragma unroll
+    for (int q = 0; q < G; ++q) acc[q] += v[q];
+  }
+  store_out<BF16>(y, (size_t)t * d + col, acc);
+}
+
 // y[p][:] = sum_s parts[s][p][:] for the valid rows, rounded once.
 template <bool BF16>
 __global__ __launch_bounds__(256) void reduce_splits_kernel(const float* __restrict__ parts,
@@ -163,6 +217,24 @@ static hipError_t combine_strided(bool bf16, const void* y_packed, int splits, l
 hipError_t launch_combine(bool bf16, const void* y_packed, int splits, long split_stride,
                           const int32_t* route_pos, const float* gates, const void* y_shared,
                           int T, int k, int d, void* y, hipStream_t st) {
+  if (splits <= 1 && k <= 8 && T > 0) {
+    dim3 grid(ceil_div(T, 4), ceil_div(d, 64 * (bf16 ? 8 : 4))), block(256);
+#define CR(B, K)                                                                                \
+  hipLaunchKernelGGL((combine_rows_kernel<B, K>), grid, block, 0, st, y_packed, route_pos, gates, \
+                     y_shared, T, k, d, y)
+    const int ks = k <= 2 ? 2 : (k <= 4 ? 4 : 8);
+    if (bf16) {
+      if (ks == 2) CR(true, 2);
+      else if (ks == 4) CR(true, 4);
+      else CR(true, 8);
+    } else {
+      if (ks == 2) CR(false, 2);
+      else if (ks == 4) CR(false, 4);
+      else CR(false, 8);
+    }
+#undef CR
+    return hipGetLastError();
+  }
   return combine_strided(bf16, y_packed, splits, split_stride, route_pos, gates, k, 1, y_shared,
                          T, k, d, y, st);
 }
