@@ -172,6 +172,67 @@ __global__ __launch_bounds__(256) void combine_rows_kernel(const void* __restric
   store_out<BF16>(y, (size_t)t * d + col, acc);
 }
 
+// Slot-major route tables (expert choice: slot e of token t at e*T + t, one
+// slot per expert, a handful of them taken): a wave holds one token and its
+// lanes read 64 slots at once; the taken ones (a ballot, in increasing e)
+// are summed in batches of up to 8 rows, each batch's rows in flight
+// together, in slot order -- the generic kernel's sums, without reading the
+// E slots eight at a time.
+template <bool BF16>
+__global__ __launch_bounds__(256) void combine_slots_kernel(const void* __restrict__ yp,
+                                                            const int32_t* __restrict__ route_pos,
+                                                            const float* __restrict__ gates,
+                                                            const void* __restrict__ ysh, int T,
+                                                            int E, int d, void* __restrict__ y) {
+  constexpr int G = BF16 ? 8 : 4;  // output elements per 16-byte chunk
+  const int lane = threadIdx.x & 63;
+  const int t = blockIdx.x * (blockDim.x / 64) + (threadIdx.x >> 6);
+  const int col = (blockIdx.y * 64 + lane) * G;
+  if (t >= T) return;  // whole waves: the column test comes after the ballots
+  const bool colok = col < d;
+  float acc[G];
+#pragma unroll
+  for (int q = 0; q < G; ++q) acc[q] = 0.0f;
+  for (int e0 = 0; e0 < E; e0 += 64) {
+    const int e = e0 + lane;
+    const int p = e < E ? route_pos[(size_t)e * T + t] : -1;
+    const float gv = e < E ? gates[(size_t)e * T + t] : 0.0f;
+    uint64_t m = __ballot(p >= 0);
+    while (m) {  // wave-uniform
+      constexpr int B = 8;
+      int pos[B];
+      float g[B];
+#pragma unroll
+      for (int j = 0; j < B; ++j) {  // the next (up to) B taken slots, in order
+        const int src = m ? __builtin_ctzll(m) : 0;
+        pos[j] = m ? __builtin_amdgcn_readlane(p, src) : -1;
+        g[j] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(gv), src));
+        m &= m - 1;  // 0 stays 0
+      }
+      if (colok) {
+        float v[B][G];
+#pragma unroll
+        for (int j = 0; j < B; ++j)
+          load_row<BF16, false, G>(yp, 1, 0, (size_t)(pos[j] >= 0 ? pos[j] : pos[0]), d, col, v[j]);
+#pragma unroll
+        for (int j = 0; j < B; ++j) {
+          if (pos[j] < 0) continue;
+#pragma unroll
+          for (int q = 0; q < G; ++q) acc[q] = __builtin_fmaf(g[j], v[j][q], acc[q]);
+        }
+      }
+    }
+  }
+  if (!colok) return;
+  if (ysh) {
+    float v[G];
+    load_row<BF16, false, G>(ysh, 1, 0, (size_t)t, d, col, v);
+#pragma unroll
+    for (int q = 0; q < G; ++q) acc[q] += v[q];
+  }
+  store_out<BF16>(y, (size_t)t * d + col, acc);
+}
+
 // y[p][:] = sum_s parts[s][p][:] for the valid rows, rounded once.
 template <bool BF16>
 __global__ __launch_bounds__(256) void reduce_splits_kernel(const float* __restrict__ parts,
@@ -243,6 +304,16 @@ hipError_t launch_combine_slot_major(bool bf16, const void* y_packed, int splits
                                      long split_stride, const int32_t* route_pos,
                                      const float* gates, const void* y_shared, int T, int k,
                                      int d, void* y, hipStream_t st) {
+  if (splits <= 1 && T > 0) {
+    dim3 grid(ceil_div(T, 4), ceil_div(d, 64 * (bf16 ? 8 : 4))), block(256);
+    if (bf16)
+      hipLaunchKernelGGL(combine_slots_kernel<true>, grid, block, 0, st, y_packed, route_pos, gates,
+                         y_shared, T, k, d, y);
+    else
+      hipLaunchKernelGGL(combine_slots_kernel<false>, grid, block, 0, st, y_packed, route_pos,
+                         gates, y_shared, T, k, d, y);
+    return hipGetLastError();
+  }
   return combine_strided(bf16, y_packed, splits, split_stride, route_pos, gates, 1, T, y_shared,
                          T, k, d, y, st);
 }
