@@ -65,8 +65,8 @@ CASES = {
     "t16384_e32": (Workload("t16384", T=16384, E=32, k=8, d=64, d_ff=32, phi=1.0, renorm=0), None),
     "t32768_max": (Workload("t32768", T=32768, E=8, k=2, d=32, d_ff=16, phi=0.7, renorm=0,
                             bias="normal"), None),
-    # columns beyond the register-resident select (radix passes over memory):
-    # the first such T (ragged), exact ties at the boundary, a long column
+    # long columns for the radix select: a ragged T, exact ties at the
+    # boundary, a column of 131072 tokens
     "t32769_long": (Workload("t32769", T=32769, E=8, k=1, d=32, d_ff=16, phi=0.9, renorm=0,
                              bias="normal"), None),
     "dup_rows_long": (Workload("dup_long", T=40000, E=8, k=2, d=64, d_ff=32, phi=1.0, renorm=0),
