@@ -29,10 +29,10 @@ hipError_t launch_topk_permute(const float* logits, int T, int E, int k, int ren
 hipError_t launch_gather_rows(const void* x, const int32_t* row_token, const int32_t* offsets,
                               int E, long R_max, long row_bytes, void* x_packed, hipStream_t st);
 // Overflow policy "reroute" after a drop-policy dispatch (route_pos0,
-// offsets0, kept from launch_permute_index); E <= 64, k <= 8, C >= 0.
+// offsets0, kept from launch_permute_index); E <= 256, k <= 8, C >= 0.
 // Writes the final experts, the packed positions and rows of the result.
-// pref: scratch of T*k*64 bytes (per dropped route, its experts' ranks or
-// its experts in preference order);
+// pref: scratch of T*k*64 bytes, T*k*256 when E > 64 (per dropped route,
+// its experts' ranks or its experts in preference order);
 // da_state: scratch of reroute_state_bytes(T, E) bytes, 16-byte aligned (the
 // parallel kernel's token arrays, final bitmaps and, when it does not fit
 // LDS, its per-token state; 0 bytes where the walk runs).

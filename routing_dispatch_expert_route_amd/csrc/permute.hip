@@ -433,9 +433,10 @@ hipError_t launch_padded(const void* x, const int32_t* ids, const int32_t* route
 // order, each take the best-ranked expert of their token (logit descending,
 // lower index first) that the token does not hold and that still has room.
 // That is a greedy in arrival order -- every choice depends on the earlier
-// ones.  reroute_da_kernel below reaches the same result in parallel rounds
-// while its per-expert bitmaps fit LDS; beyond that one wave walks the dropped
-// routes one by one.  A parallel kernel first writes, for every dropped
+// ones.  Up to 64 experts, reroute_da_kernel below reaches the same result
+// in parallel rounds while its per-expert bitmaps fit LDS; beyond that one
+// wave walks the dropped routes one by one (reroute_kernel here, or
+// reroute_wide_kernel, four experts per lane, past 64 experts).  A parallel kernel first writes, for every dropped
 // route, the rank of each expert (one byte each; the walk) or the experts
 // in preference order (the parallel rounds).  The walk stages a 64-route
 // chunk's rank rows in LDS (the next chunk's are loaded while this one is
