@@ -454,12 +454,10 @@ constexpr int kRerouteMaxE = 64;
 // (ORDER: the parallel rounds read the experts in preference order).
 // RS: bytes per route (64, or 256 for the wide walk).
 template <bool ORDER, int RS>
-__global__ __launch_bounds__(256) void reroute_rank_kernel(const float* __restrict__ logits,
-                                                           const int32_t* __restrict__ route_pos0,
-                                                           const int32_t* __restrict__ offsets0,
-                                                           int R, int k, int E, int C,
-                                                           uint8_t* __restrict__ rank) {
-  const long g = (long)blockIdx.x * blockDim.x + threadIdx.x;
+__device__ __forceinline__ void reroute_rank_at(long g, const float* __restrict__ logits,
+                                                const int32_t* __restrict__ route_pos0,
+                                                const int32_t* __restrict__ offsets0, int R,
+                                                int k, int E, int C, uint8_t* __restrict__ rank) {
   const int r = (int)(g / RS), e = (int)(g % RS);
   if (r >= R || e >= E || route_pos0[r] >= 0) return;
   if (ORDER && offsets0[E] >= (long)E * C) return;  // every seat taken: nothing moves
@@ -474,6 +472,15 @@ __global__ __launch_bounds__(256) void reroute_rank_kernel(const float* __restri
     rank[(size_t)r * RS + rk] = (uint8_t)e;
   else
     rank[(size_t)r * RS + e] = (uint8_t)rk;
+}
+template <bool ORDER, int RS>
+__global__ __launch_bounds__(256) void reroute_rank_kernel(const float* __restrict__ logits,
+                                                           const int32_t* __restrict__ route_pos0,
+                                                           const int32_t* __restrict__ offsets0,
+                                                           int R, int k, int E, int C,
+                                                           uint8_t* __restrict__ rank) {
+  reroute_rank_at<ORDER, RS>((long)blockIdx.x * blockDim.x + threadIdx.x, logits, route_pos0,
+                             offsets0, R, k, E, C, rank);
 }
 
 __global__ __launch_bounds__(64) void reroute_kernel(
@@ -783,7 +790,7 @@ __host__ __device__ inline DaLayout da_layout(int T, int E, bool tok_lds) {
 }
 
 // The parallel reroute's workspace region: token-indexed arrays written by
-// reroute_tok_kernel (tneed: dropped routes of token t, 0 for none; town:
+// reroute_tok_at (tneed: dropped routes of token t, 0 for none; town:
 // the experts the router gave it; tfirst: its first dropped route) and by
 // reroute_da_kernel (tidx: its index among the tokens with drops; thold: the
 // experts it holds at the end; gheld / gpre: the final per-expert bitmaps and
@@ -1029,11 +1036,10 @@ __global__ __launch_bounds__(kDaThreads) void reroute_da_kernel(
 // One thread per token, before the rounds: its kept routes keep expert and
 // seat; its dropped routes are counted, its first one and its router
 // experts noted (the rounds' input, token-indexed).
-__global__ __launch_bounds__(256) void reroute_tok_kernel(
-    const int32_t* __restrict__ ids_in, const int32_t* __restrict__ route_pos0,
+__device__ __forceinline__ void reroute_tok_at(
+    int t, const int32_t* __restrict__ ids_in, const int32_t* __restrict__ route_pos0,
     const int32_t* __restrict__ offsets0, int T, int k, int E, int32_t* __restrict__ ids_out,
     int32_t* __restrict__ slot, uint8_t* __restrict__ region) {
-  const int t = blockIdx.x * blockDim.x + threadIdx.x;
   if (t >= T) return;
   const RrLayout G = rr_layout(T, E, true);
   uint64_t om = 0;
@@ -1056,18 +1062,60 @@ __global__ __launch_bounds__(256) void reroute_tok_kernel(
   reinterpret_cast<int32_t*>(region + G.tfirst)[t] = rf;
 }
 
-// One thread per token with drops, after the rounds: its i-th dropped route
-// takes the i-th best expert it holds, at seat kept[e] + the number of
-// accepted tokens before it (token order); with none left it stays dropped.
+// The set-up before the rounds, in one launch: blocks below n_rank write the
+// dropped routes' experts in preference order (reroute_rank_at), the rest
+// the token arrays (reroute_tok_at); the two read only the dispatch.
+__global__ __launch_bounds__(256) void reroute_prep_kernel(
+    int n_rank, const float* __restrict__ logits, const int32_t* __restrict__ ids_in,
+    const int32_t* __restrict__ route_pos0, const int32_t* __restrict__ offsets0, int T, int k,
+    int E, int C, uint8_t* __restrict__ order, int32_t* __restrict__ ids_out,
+    int32_t* __restrict__ slot, uint8_t* __restrict__ region) {
+  const int b = blockIdx.x;
+  if (b < n_rank)
+    reroute_rank_at<true, kRerouteMaxE>((long)b * blockDim.x + threadIdx.x, logits, route_pos0,
+                                        offsets0, T * k, k, E, C, order);
+  else
+    reroute_tok_at((b - n_rank) * blockDim.x + threadIdx.x, ids_in, route_pos0, offsets0, T, k, E,
+                   ids_out, slot, region);
+}
+
+// One thread per token, after the rounds: a token with drops gives its i-th
+// dropped route the i-th best expert it holds, at seat kept[e] + the number
+// of accepted tokens before it (token order), or leaves it dropped when none
+// is left.  With route_pos set, every route of the token also gets its
+// packed row, route_pos[r] = offsets[e] + seat, and row_token of that row
+// (reroute_rows_kernel's work, done per token: one launch fewer, worth it
+// for a route or two per token; with k = 8 the per-thread stores of 8
+// consecutive positions cost more than the launch).
 __global__ __launch_bounds__(256) void reroute_seat_kernel(
     const uint8_t* __restrict__ order, const int32_t* __restrict__ ids_in,
     const int32_t* __restrict__ route_pos0, const int32_t* __restrict__ offsets0,
     const int32_t* __restrict__ kept, int T, int k, int E, int C, int32_t* __restrict__ ids_out,
-    int32_t* __restrict__ slot, const uint8_t* __restrict__ region) {
+    int32_t* __restrict__ slot, const uint8_t* __restrict__ region,
+    const int32_t* __restrict__ offsets, int32_t* __restrict__ route_pos,
+    int32_t* __restrict__ row_token) {
   const int t = blockIdx.x * blockDim.x + threadIdx.x;
   if (t >= T) return;
   const RrLayout G = rr_layout(T, E, true);
-  if (region[G.tneed + t] == 0) return;
+  auto place = [&](int r, int e, int sl) {
+    if (!route_pos) return;
+    if (sl < 0) {
+      route_pos[r] = -1;
+      return;
+    }
+    const int p = offsets[e] + sl;
+    route_pos[r] = p;
+    row_token[p] = t;
+  };
+  if (region[G.tneed + t] == 0) {  // every route kept: the seats of the drop policy
+    if (!route_pos) return;
+    for (int j = 0; j < k; ++j) {
+      const int r = t * k + j;
+      const int e = ids_in[r];
+      place(r, e, route_pos0[r] - offsets0[e]);
+    }
+    return;
+  }
   const int W = (T + 31) / 32;
   // every seat taken: the rounds wrote nothing and every dropped route stays
   const bool full = offsets0[E] >= (long)E * C;
@@ -1084,7 +1132,12 @@ __global__ __launch_bounds__(256) void reroute_seat_kernel(
   int p = 0;
   for (int j = 0; j < k; ++j) {
     const int r = t * k + j;
-    if (route_pos0[r] >= 0) continue;
+    const int p0 = route_pos0[r];
+    if (p0 >= 0) {  // kept by the drop policy
+      const int e0 = ids_in[r];
+      place(r, e0, p0 - offsets0[e0]);
+      continue;
+    }
     int e = -1;
     while (h && p < E) {  // the next best held expert
       if ((p & ~15) != cbase) {
@@ -1101,9 +1154,12 @@ __global__ __launch_bounds__(256) void reroute_seat_kernel(
     if (e < 0) {  // no expert with room: dropped after all
       ids_out[r] = ids_in[r];
       slot[r] = -1;
+      place(r, 0, -1);
     } else {
+      const int sl = kept[e] + gpre[e * W + word] + __popc(gheld[e * W + word] & below);
       ids_out[r] = e;
-      slot[r] = kept[e] + gpre[e * W + word] + __popc(gheld[e * W + word] & below);
+      slot[r] = sl;
+      place(r, e, sl);
     }
   }
 }
@@ -1146,39 +1202,45 @@ hipError_t launch_reroute(const float* logits, const int32_t* ids_in, const int3
     return hipGetLastError();
   }
   const RerouteKind kind = reroute_kind(T, E);
-  if (R > 0) {
-    const long threads = (long)R * kRerouteMaxE;
-    const dim3 grid((unsigned)((threads + 255) / 256));
-    if (kind == RerouteKind::kWalk)
-      hipLaunchKernelGGL((reroute_rank_kernel<false, kRerouteMaxE>), grid, dim3(256), 0, st,
-                         logits, route_pos0, offsets0, R, k, E, C, pref);
-    else
-      hipLaunchKernelGGL((reroute_rank_kernel<true, kRerouteMaxE>), grid, dim3(256), 0, st, logits,
-                         route_pos0, offsets0, R, k, E, C, pref);
-    hipError_t err = hipGetLastError();
-    if (err != hipSuccess) return err;
-  }
   if (kind == RerouteKind::kWalk) {
+    if (R > 0) {
+      const long threads = (long)R * kRerouteMaxE;
+      hipLaunchKernelGGL((reroute_rank_kernel<false, kRerouteMaxE>),
+                         dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, st, logits,
+                         route_pos0, offsets0, R, k, E, C, pref);
+      hipError_t err = hipGetLastError();
+      if (err != hipSuccess) return err;
+    }
     hipLaunchKernelGGL(reroute_kernel, dim3(1), dim3(kWave), 0, st, pref, ids_in, route_pos0,
                        offsets0, kept, T, k, E, C, ids_out, slot, offsets);
-  } else {
-    // token set-up, the rounds in one workgroup, then the seats
-    const dim3 tgrid(ceil_div(T, 256));
-    if (T > 0)
-      hipLaunchKernelGGL(reroute_tok_kernel, tgrid, dim3(256), 0, st, ids_in, route_pos0, offsets0,
-                         T, k, E, ids_out, slot, da_state);
-    if (kind == RerouteKind::kDaLds)
-      hipLaunchKernelGGL(reroute_da_kernel<true>, dim3(1), dim3(kDaThreads), 0, st, pref, offsets0,
-                         kept, T, E, C, offsets, da_state);
-    else
-      hipLaunchKernelGGL(reroute_da_kernel<false>, dim3(1), dim3(kDaThreads), 0, st, pref,
-                         offsets0, kept, T, E, C, offsets, da_state);
-    if (T > 0)
-      hipLaunchKernelGGL(reroute_seat_kernel, tgrid, dim3(256), 0, st, pref, ids_in, route_pos0,
-                         offsets0, kept, T, k, E, C, ids_out, slot, da_state);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess || R == 0) return err;
+    hipLaunchKernelGGL(reroute_rows_kernel, dim3(ceil_div(R, 256)), dim3(256), 0, st, ids_out,
+                       slot, offsets, R, k, route_pos, row_token);
+    return hipGetLastError();
   }
+  // preference lists and token set-up in one launch, the rounds in one
+  // workgroup, then the seats and packed rows per token
+  const dim3 tgrid(ceil_div(T, 256));
+  if (T > 0) {
+    const int n_rank = (int)(((long)R * kRerouteMaxE + 255) / 256);
+    hipLaunchKernelGGL(reroute_prep_kernel, dim3((unsigned)(n_rank + ceil_div(T, 256))),
+                       dim3(256), 0, st, n_rank, logits, ids_in, route_pos0, offsets0, T, k, E, C,
+                       pref, ids_out, slot, da_state);
+  }
+  if (kind == RerouteKind::kDaLds)
+    hipLaunchKernelGGL(reroute_da_kernel<true>, dim3(1), dim3(kDaThreads), 0, st, pref, offsets0,
+                       kept, T, E, C, offsets, da_state);
+  else
+    hipLaunchKernelGGL(reroute_da_kernel<false>, dim3(1), dim3(kDaThreads), 0, st, pref,
+                       offsets0, kept, T, E, C, offsets, da_state);
+  const bool rows_here = k <= 2;  // see reroute_seat_kernel
+  if (T > 0)
+    hipLaunchKernelGGL(reroute_seat_kernel, tgrid, dim3(256), 0, st, pref, ids_in, route_pos0,
+                       offsets0, kept, T, k, E, C, ids_out, slot, da_state, offsets,
+                       rows_here ? route_pos : nullptr, row_token);
   hipError_t err = hipGetLastError();
-  if (err != hipSuccess || R == 0) return err;
+  if (err != hipSuccess || R == 0 || rows_here) return err;
   hipLaunchKernelGGL(reroute_rows_kernel, dim3(ceil_div(R, 256)), dim3(256), 0, st, ids_out, slot,
                      offsets, R, k, route_pos, row_token);
   return hipGetLastError();
