@@ -366,35 +366,29 @@ __global__ __launch_bounds__(256) void gather_rows_kernel(const u32x4_t* __restr
 // is a tensor dimension; slot table of "Visual support -- Capacity").  From
 // the packed dispatch: a kept route r of expert e at packed row p sits in
 // slot p - offsets[e] of e, i.e. row e*C + slot of the buffer.
-__global__ __launch_bounds__(256) void padded_index_kernel(const int32_t* __restrict__ route_pos,
-                                                           const int32_t* __restrict__ ids,
-                                                           const int32_t* __restrict__ offsets,
-                                                           int R, int C,
-                                                           int32_t* __restrict__ pad_pos) {
-  const int r = blockIdx.x * blockDim.x + threadIdx.x;
-  if (r >= R) return;
-  const int p = route_pos[r];
-  if (p < 0) {
-    pad_pos[r] = -1;
-    return;
-  }
-  const int e = ids[r];
-  pad_pos[r] = e * C + (p - offsets[e]);
-}
-
 // x_pad[e*C + c] = x[row_token[offsets[e] + c]] for c < kept[e], zero rows
-// for the empty slots; offsets_pad[e] = e*C (the buffer's row groups).
+// for the empty slots; offsets_pad[e] = e*C (the buffer's row groups); and,
+// in the same launch, every route's pad_pos = e*C + slot, or -1 when dropped
+// (both read only the packed dispatch).
 __global__ __launch_bounds__(256) void fill_padded_kernel(const u32x4_t* __restrict__ x,
                                                           const int32_t* __restrict__ row_token,
                                                           const int32_t* __restrict__ offsets,
                                                           const int32_t* __restrict__ kept, int E,
                                                           int C, int cpr, long total,
                                                           u32x4_t* __restrict__ x_pad,
-                                                          int32_t* __restrict__ offsets_pad) {
+                                                          int32_t* __restrict__ offsets_pad,
+                                                          const int32_t* __restrict__ route_pos,
+                                                          const int32_t* __restrict__ ids, int R,
+                                                          int32_t* __restrict__ pad_pos) {
   const long g0 = (long)blockIdx.x * blockDim.x + threadIdx.x;
+  const long stride = (long)gridDim.x * blockDim.x;
   if (g0 <= E) offsets_pad[g0] = (int32_t)(g0 * C);
+  for (long r = g0; r < R; r += stride) {
+    const int p = route_pos[r];
+    pad_pos[r] = p < 0 ? -1 : ids[r] * C + (p - offsets[ids[r]]);
+  }
   const u32x4_t zero = {0u, 0u, 0u, 0u};
-  for (long g = g0; g < total; g += (long)gridDim.x * blockDim.x) {
+  for (long g = g0; g < total; g += stride) {
     const long p = g / cpr;
     const int ch = (int)(g - p * cpr);
     const int e = (int)(p / C);
@@ -408,12 +402,6 @@ hipError_t launch_padded(const void* x, const int32_t* ids, const int32_t* route
                          int T, int k, int E, int C, long row_bytes, int32_t* pad_pos,
                          void* x_pad, int32_t* offsets_pad, hipStream_t st) {
   const int R = T * k;
-  if (R > 0) {
-    hipLaunchKernelGGL(padded_index_kernel, dim3(ceil_div(R, 256)), dim3(256), 0, st, route_pos,
-                       ids, offsets, R, C, pad_pos);
-    hipError_t err = hipGetLastError();
-    if (err != hipSuccess) return err;
-  }
   const int cpr = (int)(row_bytes / 16);
   const long total = (long)E * C * cpr;
   long blocks = (total + 255) / 256;
@@ -423,7 +411,7 @@ hipError_t launch_padded(const void* x, const int32_t* ids, const int32_t* route
   if (blocks < (E + 256) / 256) blocks = (E + 256) / 256;
   hipLaunchKernelGGL(fill_padded_kernel, dim3((unsigned)blocks), dim3(256), 0, st,
                      reinterpret_cast<const u32x4_t*>(x), row_token, offsets, kept, E, C, cpr, total,
-                     reinterpret_cast<u32x4_t*>(x_pad), offsets_pad);
+                     reinterpret_cast<u32x4_t*>(x_pad), offsets_pad, route_pos, ids, R, pad_pos);
   return hipGetLastError();
 }
 
