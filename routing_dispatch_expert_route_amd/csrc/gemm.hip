@@ -1194,21 +1194,22 @@ static long row_tile_bound(const GemmPlan& pl, int BM) {
 // Tile counts are estimated from the row bound (each group wastes half a
 // tile on average).
 enum TileCfg { TILE_L, TILE_M, TILE_N, TILE_S };
-static long est_tiles(const GemmPlan& pl, int bm, int bno, int N) {
-  const long mt = pl.grouped ? pl.R_max / bm + (pl.E + 1) / 2 : (pl.M_dense + bm - 1) / bm;
+static long est_tiles(const GemmPlan& pl, long rows, int bm, int bno, int N) {
+  const long mt = pl.grouped ? rows / bm + (pl.E + 1) / 2 : (pl.M_dense + bm - 1) / bm;
   return mt * ((N + bno - 1) / bno);
 }
 static TileCfg tile_cfg(const GemmPlan& pl, int N, int K, bool swiglu) {
   const int bno = swiglu ? 128 : 256;
-  const long per_group = pl.grouped ? pl.R_max / (pl.E > 0 ? pl.E : 1) : pl.M_dense;
+  const long rows = swiglu && pl.R_tile > 0 ? pl.R_tile : pl.R_max;
+  const long per_group = pl.grouped ? rows / (pl.E > 0 ? pl.E : 1) : pl.M_dense;
   // the 256x256 tile from 256 rows per group on (one row tile per expert
   // reads each weight tile once; shared64's 256-row experts: GEMM 1 323 ->
   // 308 us, GEMM 2 194 -> 186 us against the 128-row tiles)
-  if (K >= (swiglu ? 1024 : 512) && per_group >= 256 && est_tiles(pl, 256, bno, N) >= 256)
+  if (K >= (swiglu ? 1024 : 512) && per_group >= 256 && est_tiles(pl, rows, 256, bno, N) >= 256)
     return TILE_L;
   // GEMM 1 keeps 128-row tiles unless the rows are very few (decode); the
   // down projection takes 64-row tiles below about two rounds
-  const long est_m = est_tiles(pl, 128, bno, N);
+  const long est_m = est_tiles(pl, rows, 128, bno, N);
   if (!swiglu) return est_m > 1024 ? TILE_M : TILE_S;
   // decode: fewer rows per group than even the 64-row tile holds, so every
   // tile streams weights for a handful of rows; the 64x256 tile streams

@@ -89,6 +89,10 @@ struct GemmPlan {
   // fp32 scratch of gemm_tail_floats(plan, N, K) floats for the down GEMM's
   // last-round tiles split along K (nullptr: no split)
   float* tail = nullptr;
+  // rows GEMM 1's tile shape is chosen for, when R_max overstates them
+  // (the queue policy: E*C bounds its seats, T*k routes arrive per call);
+  // 0: R_max.  The grid still covers R_max rows.
+  long R_tile = 0;
 };
 // True when GEMM 1 of this plan should read packed rows rather than gather
 // token rows: the 256x256 tile with a wide output (a pure function of the

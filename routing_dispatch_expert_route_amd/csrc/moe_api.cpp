@@ -168,8 +168,13 @@ moe::GemmPlan queue_plan(const moe_shape* s, int64_t Q, const int32_t* offsets) 
   const int64_t C = capacity_of(s);
   const int64_t most = Q + s->T;
   const long cap = (long)(C >= 0 && C < most ? C : most);
-  return moe::GemmPlan{s->dtype == MOE_DTYPE_BF16, true, offsets, (int)s->E, 0,
-                       (long)rmax_queue(s, Q), cap};
+  moe::GemmPlan pl{s->dtype == MOE_DTYPE_BF16, true, offsets, (int)s->E, 0,
+                   (long)rmax_queue(s, Q), cap};
+  // GEMM 1's tile for the rows a call seats in steady state, the drop
+  // policy's bound min(T*k, E*C), not E*C (Switch phi 1.25: the 128x256
+  // tile for E*C = 5120 rows against 2505 seated)
+  pl.R_tile = (long)rmax_of(s, C);
+  return pl;
 }
 
 // Q >= 0: the queue policy's layout for Q waiting routes (route-sized
