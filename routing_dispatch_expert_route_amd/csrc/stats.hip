@@ -14,8 +14,9 @@
 //       logits (sequential over experts), its confidence bin, largest gate
 //       and gate entropy; then per expert the block's sum of probabilities
 //       over its tokens in token order.  Writes one partial row per block.
-//   stats_final_kernel    one block: sums the partial rows in block order
-//       and forms the statistics.
+//   stats_final_kernel    one block: sums the partial rows (each column's
+//       rows in interleaved slices, each slice in row order, then the slices
+//       in order) and forms the statistics.
 #include "common.h"
 #include "launch.h"
 
@@ -89,19 +90,45 @@ __global__ __launch_bounds__(256) void stats_partial_kernel(const float* __restr
   for (int b = tid; b < n_bins; b += 256) hpart[(size_t)blockIdx.x * n_bins + b] = s_hist[b];
 }
 
-// Sum of column c over nblk rows of a row-major [nblk][ld] array, rows in
-// order, sixteen loads in flight (a fixed order: repeat calls agree).
+// Column sums of a row-major [nblk][ld] array, columns 0 .. nc-1, into
+// out[0 .. nc).  Row r belongs to slice r mod S; one thread sums a column's
+// slice in row order with sixteen loads in flight, then the S slice sums are
+// added in slice order -- a fixed order, so repeat calls agree.  The fewer
+// the columns, the more slices (up to 8), so that a few columns still keep
+// the block's 256 threads loading.  Every thread of the block calls it.
 template <typename V>
-__device__ __forceinline__ V column_sum(const V* __restrict__ a, int nblk, int ld, int c) {
-  V acc = 0;
-  for (int b0 = 0; b0 < nblk; b0 += 16) {
-    V v[16];
+__device__ void block_column_sums(const V* __restrict__ a, int nblk, int ld, int nc,
+                                  V* __restrict__ out, V* __restrict__ s_scr /*[256]*/) {
+  int w = 1;
+  while (w < nc && w < 256) w *= 2;
+  const int S = 256 / w < 8 ? 256 / w : 8;  // slices
+  const int G = 256 / S;                    // columns per pass
+  const int tid = threadIdx.x;
+  const int cl = tid % G, sl = tid / G;
+  for (int c0 = 0; c0 < nc; c0 += G) {
+    const int c = c0 + cl;
+    V acc = 0;
+    if (c < nc) {
+      for (int r0 = sl; r0 < nblk; r0 += 16 * S) {
+        V v[16];
 #pragma unroll
-    for (int u = 0; u < 16; ++u) v[u] = b0 + u < nblk ? a[(size_t)(b0 + u) * ld + c] : V(0);
+        for (int u = 0; u < 16; ++u) {
+          const int r = r0 + u * S;
+          v[u] = r < nblk ? a[(size_t)r * ld + c] : V(0);
+        }
 #pragma unroll
-    for (int u = 0; u < 16; ++u) acc += v[u];
+        for (int u = 0; u < 16; ++u) acc += v[u];
+      }
+    }
+    s_scr[tid] = acc;
+    __syncthreads();
+    if (sl == 0 && c < nc) {
+      V t = s_scr[cl];
+      for (int j = 1; j < S; ++j) t += s_scr[j * G + cl];
+      out[c] = t;
+    }
+    __syncthreads();
   }
-  return acc;
 }
 
 // stats: [0] aux loss, [1] load imbalance, [2] mean largest gate, [3] mean
@@ -114,20 +141,22 @@ __global__ __launch_bounds__(256) void stats_final_kernel(const float* __restric
                                                           float alpha, float* __restrict__ stats,
                                                           int32_t* __restrict__ hist) {
   __shared__ float s_f[256], s_p[256];
-  __shared__ float s_tok[3];
+  __shared__ float s_col[256 + 3];
+  __shared__ float s_scrf[256];
+  __shared__ int32_t s_scri[256];
   const int tid = threadIdx.x;
   const float inv_t = T > 0 ? 1.0f / (float)T : 0.0f;
   const float R = (float)T * (float)k;
+  block_column_sums(part, nblk, E + 3, E + 3, s_col, s_scrf);
+  block_column_sums(hpart, nblk, n_bins, n_bins, hist, s_scri);
   for (int e = tid; e < E; e += 256) {
-    const float p = column_sum(part, nblk, E + 3, e) * inv_t;
+    const float p = s_col[e] * inv_t;
     const float f = T > 0 ? (float)counts[e] / R : 0.0f;
     s_f[e] = f;
     s_p[e] = p;
     stats[6 + e] = f;
     stats[6 + E + e] = p;
   }
-  if (tid < 3) s_tok[tid] = column_sum(part, nblk, E + 3, E + tid) * inv_t;
-  for (int b = tid; b < n_bins; b += 256) hist[b] = column_sum(hpart, nblk, n_bins, b);
   __syncthreads();
   if (tid == 0) {
     float aux = 0.0f, cmax = 0.0f, js = 0.0f;
@@ -142,10 +171,10 @@ __global__ __launch_bounds__(256) void stats_final_kernel(const float* __restric
     const bool any = T > 0;
     stats[0] = any ? alpha * (float)E * aux : 0.0f;
     stats[1] = any ? cmax / (R / (float)E) : 0.0f;
-    stats[2] = s_tok[0];
-    stats[3] = s_tok[1];
+    stats[2] = s_col[E] * inv_t;
+    stats[3] = s_col[E + 1] * inv_t;
     stats[4] = any ? sqrtf(fmaxf(js, 0.0f)) : 0.0f;
-    stats[5] = s_tok[2];
+    stats[5] = s_col[E + 2] * inv_t;
   }
 }
 
