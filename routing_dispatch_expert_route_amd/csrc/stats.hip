@@ -32,6 +32,7 @@ __global__ __launch_bounds__(256) void stats_partial_kernel(const float* __restr
   __shared__ float s_l[kStatTok * 257];  // the block's logits, row stride E + 1
   __shared__ float s_m[kStatTok], s_iz[kStatTok];
   __shared__ float s_tok[3][kStatTok];
+  __shared__ float s_scr[256];
   __shared__ int s_hist[kMaxStatBins];
   const int tid = threadIdx.x;
   const int t0 = blockIdx.x * kStatTok;
@@ -77,10 +78,29 @@ __global__ __launch_bounds__(256) void stats_partial_kernel(const float* __restr
   }
   __syncthreads();
   const size_t row = (size_t)blockIdx.x * (E + 3);
-  for (int e = tid; e < E; e += 256) {
-    float acc = 0.0f;
-    for (int t = 0; t < nt; ++t) acc += __expf(s_l[t * ls + e] - s_m[t]) * s_iz[t];
-    part[row + e] = acc;
+  {
+    // per expert, its probabilities summed over the block's tokens: token t
+    // in slice t mod S, one thread per (expert, slice) in token order, then
+    // the slices in order (up to 8 slices when the experts are few)
+    int w = 1;
+    while (w < E && w < 256) w *= 2;
+    const int S = 256 / w < 8 ? 256 / w : 8;
+    const int G = 256 / S;
+    const int cl = tid % G, sl = tid / G;
+    for (int e0 = 0; e0 < E; e0 += G) {
+      const int e = e0 + cl;
+      float acc = 0.0f;
+      if (e < E)
+        for (int t = sl; t < nt; t += S) acc += __expf(s_l[t * ls + e] - s_m[t]) * s_iz[t];
+      s_scr[tid] = acc;
+      __syncthreads();
+      if (sl == 0 && e < E) {
+        float v = s_scr[cl];
+        for (int j = 1; j < S; ++j) v += s_scr[j * G + cl];
+        part[row + e] = v;
+      }
+      __syncthreads();
+    }
   }
   if (tid < 3) {
     float acc = 0.0f;
@@ -158,23 +178,32 @@ __global__ __launch_bounds__(256) void stats_final_kernel(const float* __restric
     stats[6 + E + e] = p;
   }
   __syncthreads();
-  if (tid == 0) {
+  if (tid < kWave) {
+    // wave 0: lane l takes experts l, l + 64, ... in order, then the lanes'
+    // terms are folded by halving (a fixed order)
     float aux = 0.0f, cmax = 0.0f, js = 0.0f;
     const float u = 1.0f / (float)E;
-    for (int e = 0; e < E; ++e) {
+    for (int e = tid; e < E; e += kWave) {
       aux += s_f[e] * s_p[e];
       cmax = fmaxf(cmax, (float)counts[e]);
       const float mid = 0.5f * (s_f[e] + u);
       if (s_f[e] > 0.0f) js += 0.5f * s_f[e] * __log2f(s_f[e] / mid);
       js += 0.5f * u * __log2f(u / mid);
     }
-    const bool any = T > 0;
-    stats[0] = any ? alpha * (float)E * aux : 0.0f;
-    stats[1] = any ? cmax / (R / (float)E) : 0.0f;
-    stats[2] = s_col[E] * inv_t;
-    stats[3] = s_col[E + 1] * inv_t;
-    stats[4] = any ? sqrtf(fmaxf(js, 0.0f)) : 0.0f;
-    stats[5] = s_col[E + 2] * inv_t;
+    for (int sh = kWave / 2; sh >= 1; sh /= 2) {
+      aux += __shfl_xor(aux, sh, kWave);
+      js += __shfl_xor(js, sh, kWave);
+      cmax = fmaxf(cmax, __shfl_xor(cmax, sh, kWave));
+    }
+    if (tid == 0) {
+      const bool any = T > 0;
+      stats[0] = any ? alpha * (float)E * aux : 0.0f;
+      stats[1] = any ? cmax / (R / (float)E) : 0.0f;
+      stats[2] = s_col[E] * inv_t;
+      stats[3] = s_col[E + 1] * inv_t;
+      stats[4] = any ? sqrtf(fmaxf(js, 0.0f)) : 0.0f;
+      stats[5] = s_col[E + 2] * inv_t;
+    }
   }
 }
 
