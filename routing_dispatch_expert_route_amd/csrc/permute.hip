@@ -67,30 +67,47 @@ __global__ __launch_bounds__(1024) void scan_kernel(int32_t* __restrict__ cnt, i
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = threadIdx.x / kWave;
   const int nwaves = blockDim.x / kWave;
-  for (int e = wave; e < E; e += nwaves) {
-    int32_t* row = cnt + (size_t)e * nchunks;
-    int carry = 0;
-    constexpr int NB = 8;  // groups of 64 chunks loaded together
-    for (int c1 = 0; c1 < nchunks; c1 += NB * kWave) {
-      int v[NB];
+  // wave w scans experts w, w + nwaves, ...; NE of them and NB groups of 64
+  // chunks each are loaded together, so their loads are in flight at once
+  constexpr int NE = 4, NB = 4;
+  for (int e0 = wave; e0 < E; e0 += NE * nwaves) {
+    int carry[NE];
 #pragma unroll
-      for (int q = 0; q < NB; ++q) {
-        const int c = c1 + q * kWave + lane;
-        v[q] = c < nchunks ? row[c] : 0;
+    for (int j = 0; j < NE; ++j) carry[j] = 0;
+    for (int c1 = 0; c1 < nchunks; c1 += NB * kWave) {
+      int v[NE][NB];
+#pragma unroll
+      for (int j = 0; j < NE; ++j) {
+        const int e = e0 + j * nwaves;
+#pragma unroll
+        for (int q = 0; q < NB; ++q) {
+          const int c = c1 + q * kWave + lane;
+          v[j][q] = e < E && c < nchunks ? cnt[(size_t)e * nchunks + c] : 0;
+        }
       }
 #pragma unroll
-      for (int q = 0; q < NB; ++q) {
-        const int c = c1 + q * kWave + lane;
-        const int incl = wave_incl_scan(v[q], lane);
-        if (c < nchunks) row[c] = carry + incl - v[q];
-        carry += __shfl(incl, kWave - 1, kWave);
+      for (int j = 0; j < NE; ++j) {
+        const int e = e0 + j * nwaves;  // the same in every lane
+        if (e >= E) break;
+#pragma unroll
+        for (int q = 0; q < NB; ++q) {
+          if (c1 + q * kWave >= nchunks) break;  // the same in every lane
+          const int c = c1 + q * kWave + lane;
+          const int incl = wave_incl_scan(v[j][q], lane);
+          if (c < nchunks) cnt[(size_t)e * nchunks + c] = carry[j] + incl - v[j][q];
+          carry[j] += __shfl(incl, kWave - 1, kWave);
+        }
       }
     }
-    if (lane == 0) {
-      const int m = (C < 0 || carry <= C) ? carry : C;
-      counts[e] = carry;
-      kept[e] = m;
-      s_kept[e] = m;
+#pragma unroll
+    for (int j = 0; j < NE; ++j) {
+      const int e = e0 + j * nwaves;
+      if (lane == 0 && e < E) {
+        const int m = (C < 0 || carry[j] <= C) ? carry[j] : C;
+        counts[e] = carry[j];
+        kept[e] = m;
+        s_kept[e] = m;
+      }
     }
   }
   __syncthreads();
