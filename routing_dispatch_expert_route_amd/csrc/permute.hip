@@ -182,43 +182,68 @@ __global__ __launch_bounds__(64) void scatter_kernel(const int32_t* __restrict__
 
 // Whole permute in one workgroup of 1024 threads (16 waves), for route counts
 // small enough that one CU finishes them faster than three dependent
-// launches: histogram by LDS atomics, capacity and the exclusive prefix by
-// one wave, then the routes in chunks of 1024 in route order -- the rank of
-// a route is the running count of its expert before the chunk, plus the
-// routes of the same expert in earlier waves of the chunk, plus its rank
-// among the lanes of its own wave (ballots).  Same result as the chunked
-// kernels above, bit for bit.
+// launches.  Route r = q * 1024 + tid lies in group (q, wave): the groups
+// in route order are g = q * 16 + wave, 64 of them.  The ballots on the
+// expert-id bits give each route its rank among the lanes of its wave and
+// each group its size per expert; one wave per expert then scans the 64
+// group sizes, which gives every group its expert's running count before it
+// and the expert's demand; one wave clips the demands to the capacity and
+// forms the offsets.  A route's slot is its group's running count plus its
+// rank -- the number of routes of its expert before it, as the chunked
+// kernels above count them, so the same result bit for bit.
 constexpr int kSmallThreads = 1024;
 constexpr int kSmallWaves = kSmallThreads / kWave;
 constexpr long kSmallMaxRoutes = 4096;
 
 constexpr int kSmallPerThread = kSmallMaxRoutes / kSmallThreads;
+static_assert(kSmallPerThread * kSmallWaves <= kWave, "one lane per group in the per-expert scan");
 
 // The body, over the routes' experts already in registers: thread tid holds
 // route q * kSmallThreads + tid in idv[q] (-1 past R), loaded together by
-// the caller, so neither pass waits on memory per chunk.
-__device__ __forceinline__ void permute_small_body(const int (&idv)[kSmallPerThread], int R, int k,
+// the caller, so no pass waits on memory.  PT: routes per thread the caller
+// covers (R <= PT * 1024), which sizes the group table.
+template <int PT>
+__device__ __forceinline__ void permute_small_body(const int (&idv)[PT], int R, int k,
                                                    int E, int C, int32_t* __restrict__ counts,
                                                    int32_t* __restrict__ kept,
                                                    int32_t* __restrict__ offsets,
                                                    int32_t* __restrict__ route_pos,
                                                    int32_t* __restrict__ row_token) {
-  __shared__ int s_cnt[256];
+  static_assert(PT >= 1 && PT <= kSmallPerThread, "at most 4096 routes");
+  constexpr int kGroups = PT * kSmallWaves;
   __shared__ int s_off[256];
-  __shared__ int s_run[256];
-  __shared__ int s_w[kSmallWaves][256];  // per-wave counts of the chunk, then their prefix
+  __shared__ int s_g[kGroups][256];  // group sizes per expert, then their prefix
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
   const int wave = tid / kWave;
-  for (int e = tid; e < E; e += kSmallThreads) {
-    s_cnt[e] = 0;
-    s_run[e] = 0;
+  for (int i = tid; i < kGroups * E; i += kSmallThreads) s_g[i / E][i % E] = 0;
+  __syncthreads();
+  const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (kWave - lane));
+  int rank[PT];
+#pragma unroll
+  for (int q = 0; q < PT; ++q) {
+    const int r = q * kSmallThreads + tid;
+    const int e = idv[q];
+    const bool valid = r < R && e >= 0 && e < E;
+    // lanes holding the same expert id: match on all 8 bits (E <= 256)
+    uint64_t m = __ballot(valid);
+#pragma unroll
+    for (int bit = 0; bit < 8; ++bit) {
+      const bool on = (e >> bit) & 1;
+      const uint64_t bb = __ballot(on);
+      m &= on ? bb : ~bb;
+    }
+    rank[q] = __popcll(m & lt_mask);
+    // the first lane of each expert's lanes records the group's size
+    if (valid && rank[q] == 0) s_g[q * kSmallWaves + wave][e] = __popcll(m);
   }
   __syncthreads();
-#pragma unroll
-  for (int q = 0; q < kSmallPerThread; ++q) {
-    const int e = idv[q];
-    if (e >= 0 && e < E) atomicAdd(&s_cnt[e], 1);
+  // per expert (a wave each): exclusive prefix over the groups in route order
+  for (int e = wave; e < E; e += kSmallWaves) {
+    const int c = lane < kGroups ? s_g[lane][e] : 0;
+    const int incl = wave_incl_scan(c, lane);
+    if (lane < kGroups) s_g[lane][e] = incl - c;
+    if (lane == kWave - 1) s_off[e] = incl;  // the expert's demand, for now
   }
   __syncthreads();
   if (wave == 0) {
@@ -226,7 +251,7 @@ __device__ __forceinline__ void permute_small_body(const int (&idv)[kSmallPerThr
     if (lane == 0) offsets[0] = 0;
     for (int e0 = 0; e0 < E; e0 += kWave) {
       const int e = e0 + lane;
-      const int n = e < E ? s_cnt[e] : 0;
+      const int n = e < E ? s_off[e] : 0;
       const int m = (C < 0 || n <= C) ? n : C;
       const int incl = wave_incl_scan(m, lane);
       if (e < E) {
@@ -238,40 +263,14 @@ __device__ __forceinline__ void permute_small_body(const int (&idv)[kSmallPerThr
       carry += __shfl(incl, kWave - 1, kWave);
     }
   }
-  const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (kWave - lane));
+  __syncthreads();
 #pragma unroll
-  for (int q = 0; q < kSmallPerThread; ++q) {
-    const int base = q * kSmallThreads;
-    if (base >= R) break;  // R is uniform: every wave leaves together
-    for (int e = lane; e < E; e += kWave) s_w[wave][e] = 0;
-    const int r = base + tid;
-    const int e = idv[q];
-    const bool valid = r < R && e >= 0 && e < E;
-    uint64_t m = __ballot(valid);
-#pragma unroll
-    for (int bit = 0; bit < 8; ++bit) {
-      const bool on = (e >> bit) & 1;
-      const uint64_t bb = __ballot(on);
-      m &= on ? bb : ~bb;
-    }
-    const int rank = __popcll(m & lt_mask);
-    __syncthreads();  // s_w cleared (and s_off written, first chunk)
-    // the first lane of each expert group records the group's size
-    if (valid && rank == 0) s_w[wave][e] = __popcll(m);
-    __syncthreads();
-    // per expert: exclusive prefix over the waves, and the running count
-    for (int x = tid; x < E; x += kSmallThreads) {
-      int acc = s_run[x];
-      for (int w = 0; w < kSmallWaves; ++w) {
-        const int c = s_w[w][x];
-        s_w[w][x] = acc;
-        acc += c;
-      }
-      s_run[x] = acc;
-    }
-    __syncthreads();
+  for (int q = 0; q < PT; ++q) {
+    const int r = q * kSmallThreads + tid;
     if (r < R) {
-      const int slot = valid ? s_w[wave][e] + rank : 0;
+      const int e = idv[q];
+      const bool valid = e >= 0 && e < E;
+      const int slot = valid ? s_g[q * kSmallWaves + wave][e] + rank[q] : 0;
       if (valid && (C < 0 || slot < C)) {
         const int p = s_off[e] + slot;
         route_pos[r] = p;
@@ -280,17 +279,17 @@ __device__ __forceinline__ void permute_small_body(const int (&idv)[kSmallPerThr
         route_pos[r] = -1;
       }
     }
-    __syncthreads();  // s_w is reused by the next chunk
   }
 }
 
+template <int PT>
 __global__ __launch_bounds__(kSmallThreads) void permute_small_kernel(
     const int32_t* __restrict__ ids, int R, int k, int E, int C, int32_t* __restrict__ counts,
     int32_t* __restrict__ kept, int32_t* __restrict__ offsets, int32_t* __restrict__ route_pos,
     int32_t* __restrict__ row_token) {
-  int idv[kSmallPerThread];
+  int idv[PT];
 #pragma unroll
-  for (int q = 0; q < kSmallPerThread; ++q) {
+  for (int q = 0; q < PT; ++q) {
     const int r = q * kSmallThreads + (int)threadIdx.x;
     idv[q] = r < R ? ids[r] : -1;
   }
@@ -334,9 +333,11 @@ __global__ __launch_bounds__(kSmallThreads) void topk_permute_small_kernel(
     }
   }
   __syncthreads();
-  int idv[kSmallPerThread];
+  constexpr int PT = kFusedMaxT * KMAX <= kSmallThreads ? 1 : 2;
+  static_assert(kFusedMaxT * KMAX <= PT * kSmallThreads, "every route in a thread");
+  int idv[PT];
 #pragma unroll
-  for (int q = 0; q < kSmallPerThread; ++q) {
+  for (int q = 0; q < PT; ++q) {
     const int r = q * kSmallThreads + t;
     idv[q] = r < T * k ? s_ids[r] : -1;
   }
@@ -1370,8 +1371,13 @@ hipError_t launch_permute_index(const int32_t* ids, int T, int k, int E, int C, 
                                 int32_t* route_pos, int32_t* row_token, hipStream_t st) {
   const int R = T * k;
   if (R <= kSmallMaxRoutes) {
-    hipLaunchKernelGGL(permute_small_kernel, dim3(1), dim3(kSmallThreads), 0, st, ids, R, k, E, C,
-                       counts, kept, offsets, route_pos, row_token);
+#define PS(PT)                                                                                \
+  hipLaunchKernelGGL(permute_small_kernel<PT>, dim3(1), dim3(kSmallThreads), 0, st, ids, R, k, E, \
+                     C, counts, kept, offsets, route_pos, row_token)
+    if (R <= kSmallThreads) PS(1);
+    else if (R <= 2 * kSmallThreads) PS(2);
+    else PS(4);
+#undef PS
     return hipGetLastError();
   }
   const int nch = permute_nchunks(R);
